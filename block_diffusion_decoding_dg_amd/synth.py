@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs: workload shapes, random-init weights and prompts.
+
+This module is shared by the GPU tests, the CPU oracle's callers and the
+bench.  It holds none of the decoder's arithmetic: it only draws numbers.
+
+Workloads (the pages give one real configuration, DiffusionGemma 26B A4B: a
+mixture of experts with 128 experts, 8 routed plus 1 shared active, 25.2B
+total / 3.8B active parameters, 256-token canvases, batch 1, 4096 input /
+1024 output tokens -- "DiffusionGemma hits ~1,500 TPS on one H100", section
+"The specs that matter for serving"; "DiffusionGemma Hits 1,000 Tokens per
+Second", section "The speed numbers and the hardware they require").  The
+pages' own runs use real prompts and trained weights; here every matrix is
+N(0, 0.02), norm gains are 1 and prompts are uniform random token ids.
+
+Generators: torch's seeded normal generator (CPU or GPU device) per tensor,
+seed = hash of (workload seed, tensor index); fp32 then round-to-nearest-even
+bf16 for the bf16 workloads.  Prompts: numpy PCG64 uniform integers.
+"""
+from dataclasses import dataclass, asdict
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "f32" or "bf16"
+    vocab: int
+    d_model: int
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_experts: int
+    top_k: int
+    expert_hidden: int
+    shared_hidden: int
+    prompt_len: int
+    n_out: int            # output tokens per request
+    n_requests: int
+    tau: float
+    max_steps: int
+    canvas_len: int = 256
+    rope_theta: float = 10000.0
+    rms_eps: float = 1e-6
+    init_std: float = 0.02
+
+    @property
+    def n_blocks(self):
+        return -(-self.n_out // self.canvas_len)
+
+    @property
+    def max_ctx(self):
+        return self.prompt_len + self.n_blocks * self.canvas_len
+
+    def model_dict(self):
+        keys = ("vocab", "d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "n_experts",
+                "top_k", "expert_hidden", "shared_hidden", "canvas_len", "rope_theta", "rms_eps")
+        return {k: getattr(self, k) for k in keys}
+
+    def param_count(self):
+        d, hd = self.d_model, self.head_dim
+        per_layer = ((self.n_q_heads + 2 * self.n_kv_heads) * hd * d + self.n_q_heads * hd * d
+                     + self.n_experts * d + self.n_experts * 3 * d * self.expert_hidden
+                     + 3 * d * self.shared_hidden + 2 * d)
+        return self.n_layers * per_layer + self.vocab * d + d
+
+
+# The five workloads.  The tiny one leaves the shared-expert width unstated;
+# it is taken equal to the routed experts' width.
+WORKLOADS = {
+    "tiny": Workload("tiny", "f32", vocab=512, d_model=64, n_layers=2, n_q_heads=4, n_kv_heads=2,
+                     head_dim=16, n_experts=8, top_k=2, expert_hidden=128, shared_hidden=128,
+                     prompt_len=64, n_out=256, n_requests=1, tau=0.5, max_steps=64),
+    "mid": Workload("mid", "bf16", vocab=32768, d_model=1024, n_layers=8, n_q_heads=16,
+                    n_kv_heads=4, head_dim=64, n_experts=32, top_k=4, expert_hidden=512,
+                    shared_hidden=1536, prompt_len=1024, n_out=512, n_requests=1, tau=1.0,
+                    max_steps=256),
+    "full": Workload("full", "bf16", vocab=262144, d_model=2816, n_layers=30, n_q_heads=16,
+                     n_kv_heads=8, head_dim=256, n_experts=128, top_k=8, expert_hidden=704,
+                     shared_hidden=2112, prompt_len=4096, n_out=1024, n_requests=1, tau=1.0,
+                     max_steps=256),
+    "full_x8": Workload("full_x8", "bf16", vocab=262144, d_model=2816, n_layers=30, n_q_heads=16,
+                        n_kv_heads=8, head_dim=256, n_experts=128, top_k=8, expert_hidden=704,
+                        shared_hidden=2112, prompt_len=4096, n_out=1024, n_requests=8, tau=1.0,
+                        max_steps=256),
+    "full_long": Workload("full_long", "bf16", vocab=262144, d_model=2816, n_layers=30,
+                          n_q_heads=16, n_kv_heads=8, head_dim=256, n_experts=128, top_k=8,
+                          expert_hidden=704, shared_hidden=2112, prompt_len=131072, n_out=512,
+                          n_requests=1, tau=1.0, max_steps=256),
+}
+
+LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router",
+                 "w1", "w3", "w2", "sw1", "sw3", "sw2")
+
+
+def layer_shapes(w: Workload):
+    d, hd, E = w.d_model, w.head_dim, w.n_experts
+    return {
+        "attn_norm": (d,), "wq": (w.n_q_heads * hd, d), "wk": (w.n_kv_heads * hd, d),
+        "wv": (w.n_kv_heads * hd, d), "wo": (d, w.n_q_heads * hd), "ffn_norm": (d,),
+        "router": (E, d), "w1": (E, w.expert_hidden, d), "w3": (E, w.expert_hidden, d),
+        "w2": (E, d, w.expert_hidden), "sw1": (w.shared_hidden, d), "sw3": (w.shared_hidden, d),
+        "sw2": (d, w.shared_hidden),
+    }
+
+
+def torch_dtype(w: Workload):
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def _tensor_seed(seed: int, index: int) -> int:
+    return (seed * 1_000_003 + index * 7_919 + 12_345) % (2 ** 63)
+
+
+def _normal(shape, std, seed, index, device, dtype):
+    g = torch.Generator(device=device)
+    g.manual_seed(_tensor_seed(seed, index))
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    t.mul_(std)
+    return t.to(dtype)
+
+
+def make_weights(w: Workload, seed: int = 0, device="cpu", layers: Optional[List[int]] = None):
+    """Random-init weights as torch tensors on `device`, in the workload dtype.
+
+    Returns {"embed": [V, d], "final_norm": [d], "layers": [ {name: tensor} ]}.
+    `layers` restricts generation to the listed layer indices (others None);
+    the values of a layer do not depend on which others are generated."""
+    dt = torch_dtype(w)
+    out = {"embed": _normal((w.vocab, w.d_model), w.init_std, seed, 0, device, dt),
+           "final_norm": torch.ones(w.d_model, device=device, dtype=dt), "layers": []}
+    shapes = layer_shapes(w)
+    for l in range(w.n_layers):
+        if layers is not None and l not in layers:
+            out["layers"].append(None)
+            continue
+        lt = {}
+        for i, name in enumerate(LAYER_TENSORS):
+            if name.endswith("norm"):
+                lt[name] = torch.ones(shapes[name], device=device, dtype=dt)
+            else:
+                lt[name] = _normal(shapes[name], w.init_std, seed, 1 + l * 64 + i, device, dt)
+        out["layers"].append(lt)
+    return out
+
+
+def make_prompt(w: Workload, seed: int = 0, length: Optional[int] = None):
+    n = w.prompt_len if length is None else length
+    rng = np.random.Generator(np.random.PCG64(seed + 0x5EED))
+    return rng.integers(0, w.vocab, size=n, dtype=np.int64).astype(np.int32)
+
+
+def make_normal(shape, seed, std=1.0, device="cpu", dtype=torch.float32):
+    """Seeded N(0, std) tensor for op-level test inputs (activations, caches)."""
+    return _normal(shape, std, seed, 0x7FFF, device, dtype)
+
+
+def make_uniform_ints(n, high, seed):
+    rng = np.random.Generator(np.random.PCG64(seed + 0xA11))
+    return rng.integers(0, high, size=n, dtype=np.int64).astype(np.int32)

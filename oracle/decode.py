@@ -1,0 +1,223 @@
+"""Prefill, denoising step, entropy-bound sampler and block commit (oracle side).
+
+Test infrastructure: only the tests, the package's smoke check and the bench's
+CPU-baseline leg use this package; the GPU library never imports or links it.
+
+The decoding loop follows "DiffusionGemma hits ~1,500 TPS on one H100",
+sections "What DiffusionGemma is" and "How the sampler actually works", and
+"DiffusionGemma Hits 1,000 Tokens per Second", section "How diffusion text
+generation changes the bottleneck":
+
+1. a 256-token canvas starts filled with random tokens;
+2. each step runs the decoder bidirectionally over the whole canvas, with the
+   committed prefix in the KV cache visible to every canvas position;
+3. a candidate is chosen at every position, confident positions are accepted
+   and the rest are re-randomized for the next step;
+4. the loop ends when the block has converged or at the step cap;
+5. a finished block is committed to the KV cache and the next canvas is
+   conditioned on it; nothing of the canvas enters the cache before that.
+
+The pages leave the acceptance rule open (the budget sampler of the second
+page is described only in words).  Rule implemented, a stated reading: the
+candidate is the argmax token; among open positions, accept those whose
+softmax entropy is strictly below tau, and always the single open position of
+lowest entropy (ties to the lower position); accepted positions never change.
+At the step cap every position still open is forced to its argmax.  The
+committed K/V of a block are those of one more forward over the final canvas.
+Prompt positions attend causally (the parent model is autoregressive).
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from .model import (ModelConfig, Weights, Precision, layer_forward, lm_head_stats)
+from .philox import draw_tokens
+
+
+@dataclass
+class SamplerConfig:
+    tau: float
+    max_steps: int  # step cap per block
+
+
+@dataclass
+class RequestState:
+    seed: int
+    max_ctx: int
+    cache_k: List[np.ndarray] = field(default_factory=list)  # per layer [max_ctx, Hkv, hd]
+    cache_v: List[np.ndarray] = field(default_factory=list)
+    P: int = 0              # committed length (prompt + committed blocks)
+    block: int = 0          # index of the current / next canvas
+    step: int = 0           # denoising steps taken on the current canvas
+    active: bool = False
+    ids: Optional[np.ndarray] = None       # [C] int64 canvas token ids
+    accepted: Optional[np.ndarray] = None  # [C] bool
+
+
+@dataclass
+class StepResult:
+    entropy: np.ndarray      # [C] float64 (every row, open or not)
+    argmax: np.ndarray       # [C] int64
+    lse: np.ndarray          # [C]
+    accept_entropy: np.ndarray  # [C] bool: accepted this step by the entropy rule
+    accept_forced: np.ndarray   # [C] bool: forced at the step cap
+    redrawn: np.ndarray      # [C] bool: re-randomized this step
+    ids_before: np.ndarray
+    accepted_before: np.ndarray
+    ids_after: np.ndarray
+    accepted_after: np.ndarray
+    n_open: int
+    done: bool
+    layers: list             # per-layer LayerTrace (router decisions etc.)
+    logits: Optional[np.ndarray] = None
+    hidden: Optional[np.ndarray] = None
+
+
+def new_request(cfg: ModelConfig, seed: int, max_ctx: int) -> RequestState:
+    st = RequestState(seed=seed, max_ctx=max_ctx)
+    for _ in range(cfg.n_layers):
+        st.cache_k.append(np.zeros((max_ctx, cfg.n_kv_heads, cfg.head_dim)))
+        st.cache_v.append(np.zeros((max_ctx, cfg.n_kv_heads, cfg.head_dim)))
+    return st
+
+
+def prefill(st: RequestState, prompt, cfg: ModelConfig, w: Weights, prec: Precision):
+    """Causal forward over the prompt; stores post-RoPE K/V at [0, n)."""
+    prompt = np.asarray(prompt, dtype=np.int64)
+    n = prompt.shape[0]
+    if n > st.max_ctx:
+        raise ValueError("prompt longer than max_ctx")
+    x = w.embed[prompt]
+    pos = np.arange(n)
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    empty = np.zeros((0, cfg.n_kv_heads, cfg.head_dim))
+    for l, lw in enumerate(w.layers):
+        x, tr = layer_forward(x, pos, lw, cfg, prec, empty, empty, mask=mask,
+                              skip_ffn=(l == cfg.n_layers - 1))
+        st.cache_k[l][:n] = tr.k
+        st.cache_v[l][:n] = tr.v
+    st.P = n
+    st.block = 0
+    st.active = False
+    return x
+
+
+def start_canvas(st: RequestState, cfg: ModelConfig):
+    """Canvas initialisation: step index 0 of the current block."""
+    c = cfg.canvas_len
+    st.ids = draw_tokens(st.seed, st.block, 0, np.arange(c), cfg.vocab)
+    st.accepted = np.zeros(c, dtype=bool)
+    st.step = 0
+    st.active = True
+
+
+def canvas_forward(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision,
+                   for_commit=False):
+    """Bidirectional forward of the canvas over [committed prefix ; canvas]."""
+    c = cfg.canvas_len
+    P = st.P
+    if P + c > st.max_ctx:
+        raise ValueError("canvas does not fit in max_ctx")
+    x = w.embed[st.ids]
+    pos = P + np.arange(c)
+    traces = []
+    for l, lw in enumerate(w.layers):
+        last = l == cfg.n_layers - 1
+        x, tr = layer_forward(x, pos, lw, cfg, prec, st.cache_k[l][:P], st.cache_v[l][:P],
+                              mask=None, skip_ffn=(for_commit and last))
+        traces.append(tr)
+    return x, traces
+
+
+def sampler_decide(entropy, argmax, accepted, tau, step, max_steps):
+    """Entropy-bound accept rule on one canvas (pure function).
+
+    entropy, argmax: per position; accepted: bool mask before the step; step:
+    the 1-based index of this denoising step.  Decisions are taken on float32
+    entropies.  Returns (accept_entropy, accept_forced) bool masks."""
+    open_ = ~np.asarray(accepted, dtype=bool)
+    h32 = np.asarray(entropy, dtype=np.float32)
+    acc = open_ & (h32 < np.float32(tau))
+    if open_.any():
+        cand = np.where(open_, h32, np.float32(np.inf))
+        lowest = int(np.argmin(cand))  # first minimum = lowest position
+        acc[lowest] = True
+    forced = np.zeros_like(acc)
+    if step >= max_steps:
+        forced = open_ & ~acc
+    return acc, forced
+
+
+def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Weights,
+                 prec: Precision, keep_logits=False) -> StepResult:
+    if not st.active:
+        start_canvas(st, cfg)
+    x, traces = canvas_forward(st, cfg, w, prec)
+    stats = lm_head_stats(x, w.embed, w.final_norm, cfg, prec, keep_logits=keep_logits)
+    s = st.step + 1
+    ids_before = st.ids.copy()
+    acc_before = st.accepted.copy()
+    acc_e, acc_f = sampler_decide(stats["entropy"], stats["argmax"], st.accepted, scfg.tau, s,
+                                  scfg.max_steps)
+    take = acc_e | acc_f
+    ids = st.ids.copy()
+    ids[take] = stats["argmax"][take]
+    accepted = st.accepted | take
+    redraw = ~accepted
+    if redraw.any():
+        pos = np.nonzero(redraw)[0]
+        ids[pos] = draw_tokens(st.seed, st.block, s, pos, cfg.vocab)
+    st.ids, st.accepted, st.step = ids, accepted, s
+    n_open = int((~accepted).sum())
+    return StepResult(entropy=stats["entropy"], argmax=stats["argmax"], lse=stats["lse"],
+                      accept_entropy=acc_e, accept_forced=acc_f, redrawn=redraw,
+                      ids_before=ids_before, accepted_before=acc_before,
+                      ids_after=ids.copy(), accepted_after=accepted.copy(),
+                      n_open=n_open, done=(n_open == 0), layers=traces,
+                      logits=stats.get("logits"), hidden=x)
+
+
+def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision):
+    """Write the K/V of a forward over the final canvas to [P, P + C); P += C."""
+    if not st.active or not st.accepted.all():
+        raise ValueError("commit before the canvas is done")
+    _, traces = canvas_forward(st, cfg, w, prec, for_commit=True)
+    c = cfg.canvas_len
+    for l, tr in enumerate(traces):
+        st.cache_k[l][st.P:st.P + c] = tr.k
+        st.cache_v[l][st.P:st.P + c] = tr.v
+    out = st.ids.copy()
+    st.P += c
+    st.block += 1
+    st.active = False
+    st.ids = None
+    st.accepted = None
+    return out
+
+
+def generate(prompt, n_out, seed, cfg: ModelConfig, scfg: SamplerConfig, w: Weights,
+             prec: Precision, max_ctx=None, on_step=None):
+    """Whole generation for one request: prefill, then block after block.
+
+    Output length n_out is rounded up to whole canvases and truncated."""
+    c = cfg.canvas_len
+    n_blocks = -(-n_out // c)
+    if max_ctx is None:
+        max_ctx = len(prompt) + n_blocks * c
+    st = new_request(cfg, seed, max_ctx)
+    prefill(st, prompt, cfg, w, prec)
+    out = []
+    steps = []
+    for b in range(n_blocks):
+        n = 0
+        while True:
+            r = denoise_step(st, cfg, scfg, w, prec)
+            n += 1
+            if on_step is not None:
+                on_step(b, n, r, st)
+            if r.done:
+                break
+        steps.append(n)
+        out.append(commit_block(st, cfg, w, prec))
+    return np.concatenate(out)[:n_out], steps, st
