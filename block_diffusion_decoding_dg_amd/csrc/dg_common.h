@@ -1,0 +1,121 @@
+// Device-side building blocks shared by the kernels of libdg (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+#define DG_WAVE 64
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// Matrix-core step on 16-byte per-lane fragments.
+//
+// A 16x16 output tile with a "k-chunk" of 64 bytes per row: bf16 -> 32 k values
+// (one v_mfma_f32_16x16x32_bf16), f32 -> 16 k values (four v_mfma_f32_16x16x4f32).
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, taking the 16 bytes
+// at byte offset 16 * (l / 16) of the 64-byte chunk.  For f32 the four MFMAs use
+// element j of every lane, i.e. k = 4 * (l / 16) + j: the same permutation of k on
+// both operands, so the sum over the chunk is unchanged.
+// Output: lane l holds D[4 * (l / 16) + i][l % 16], i = 0..3.
+template <typename T> struct MF;
+
+template <> struct MF<bf16_t> {
+  typedef v8s frag;
+  static constexpr int KC = 32;
+  static __device__ __forceinline__ void mma(v4f& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+};
+
+template <> struct MF<float> {
+  typedef v4f frag;
+  static constexpr int KC = 16;
+  static __device__ __forceinline__ void mma(v4f& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+  }
+};
+
+template <typename F> __device__ __forceinline__ F load_frag(const char* p) {
+  return *reinterpret_cast<const F*>(p);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// Softmax-statistics triple over a set of logits z: m = max z,
+// s = sum exp(z - m), t = sum exp(z - m) * (z - m).  Entropy = log s - t / s,
+// log-sum-exp = m + log s.  Two triples merge exactly (up to rounding):
+// with M = max(m1, m2), s = s1 e^(m1-M) + s2 e^(m2-M) and
+// t = e^(m1-M) (t1 + (m1 - M) s1) + e^(m2-M) (t2 + (m2 - M) s2).
+struct SoftStats {
+  float m, s, t;
+};
+__device__ __forceinline__ SoftStats soft_merge(SoftStats a, SoftStats b) {
+  if (a.s == 0.f) return b;
+  if (b.s == 0.f) return a;
+  float M = fmaxf(a.m, b.m);
+  float ea = __expf(a.m - M), eb = __expf(b.m - M);
+  SoftStats r;
+  r.m = M;
+  r.s = a.s * ea + b.s * eb;
+  r.t = ea * (a.t + (a.m - M) * a.s) + eb * (b.t + (b.m - M) * b.s);
+  return r;
+}
+
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds of
+// (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)),
+// key advanced by the Weyl increments before every round after the first.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += W0; k1 += W1; }
+    uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+    uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+  }
+}
+
+// Uniform token in [0, vocab): high 64 bits of r0 * vocab, r0 the first Philox word of
+// counter (position, step, block, 0) under key (seed, 0).
+__device__ __forceinline__ int32_t draw_token(uint64_t seed, uint32_t block, uint32_t step, uint32_t pos,
+                                              uint32_t vocab) {
+  uint64_t c[4] = {(uint64_t)pos, (uint64_t)step, (uint64_t)block, 0ull};
+  philox4x64_10(c, seed, 0ull);
+  return (int32_t)__umul64hi(c[0], (uint64_t)vocab);
+}

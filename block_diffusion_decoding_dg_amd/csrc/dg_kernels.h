@@ -1,0 +1,85 @@
+// Host-side launchers of the libdg kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DG_MAX_SEGS 16
+
+// One request's share of a batch of rows: rows [row0, row0 + n) of the batch sit at
+// absolute positions pos0 .. pos0 + n - 1 and attend to keys [0, nkeys) of the
+// request's cache of the current layer (K: [Hkv][max_ctx][hd], V: [Hkv][hd][max_ctx]).
+struct DgSeg {
+  void* k;
+  void* vt;
+  int32_t row0, n, pos0, nkeys;
+};
+struct DgSegs {
+  DgSeg s[DG_MAX_SEGS];
+  int32_t count;
+  int32_t causal;
+};
+
+struct DgShape {
+  int32_t d, hq, hkv, hd, max_ctx, vocab;
+};
+
+// dtype: 0 = f32, 1 = bf16 (weights, activations and cache).
+void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, float* x, hipStream_t s);
+struct DgSampleArgs;
+void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, int d, float* x, hipStream_t s);
+void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
+                       const void* gain, float eps, void* out, hipStream_t s);
+// y = A W^T; mode 0: store in dtype, 1: store fp32, 2: add into fp32 out.
+void dg_launch_gemm(int dtype, int mode, const void* A, int M, int K, const void* W, int N, void* out, int ldo,
+                    hipStream_t s);
+void dg_launch_qkv(int dtype, const void* A, int M, const DgShape& sh, const void* wq, const void* wk, const void* wv,
+                   const DgSegs& segs, const double* inv_freq, void* q_out, hipStream_t s);
+void dg_launch_swiglu(int dtype, const void* A, int M, int K, const void* w1, const void* w3, int N, void* h_out,
+                      hipStream_t s);
+// Attention: q [rows][hq*hd] (dtype), output o [rows][hq*hd] (dtype).  Uses the
+// split-KV partial buffers (fp32): opart [nsplit][rows*hq][hd], mlpart [nsplit][rows*hq][2].
+int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits);
+void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSegs& segs, int nsplit, float* opart,
+                         float* mlpart, void* o, int rows, hipStream_t s);
+// Router top-k: logits [rows][E] fp32 -> ids [rows][k], gates [rows][k].
+void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s);
+// Permutation: counts[E], offsets[E], perm[rows*k] (pair index t*k + j, token order per expert).
+void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       hipStream_t s);
+// Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
+void dg_launch_expert_up(int dtype, const void* b, int rows, int d, int E, int k, int eh, const void* w1,
+                         const void* w3, const int32_t* counts, const int32_t* offsets, const int32_t* perm, void* h,
+                         hipStream_t s);
+void dg_launch_expert_down(int dtype, const void* h, int rows, int d, int E, int k, int eh, const void* w2,
+                           const int32_t* counts, const int32_t* offsets, const int32_t* perm, float* y,
+                           hipStream_t s);
+// x[t] += sum_j gates[t][j] * y[t*k + j]
+void dg_launch_combine(float* x, const float* y, const float* gates, int rows, int d, int k, hipStream_t s);
+// LM head over rows of hn [n][d] (dtype), n from n_dev (<= max_rows): partials then merge.
+void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_rows, int d, const void* embed,
+                       int vocab, float* part, int32_t* part_arg, float* ent, float* lse, int32_t* amax,
+                       const int32_t* row_idx, hipStream_t s);
+int dg_lm_head_tiles(int vocab);
+// Sampler over a batch of canvases (one per slot).
+struct DgSampleSlot {
+  int32_t* ids;       // canvas ids [C]
+  uint8_t* accepted;  // [C]
+  uint64_t seed;
+  int32_t block, step, row0;
+};
+struct DgSampleArgs {
+  DgSampleSlot s[DG_MAX_SEGS];
+  int32_t count, C, vocab, max_steps;
+  float tau;
+};
+// ent/amax indexed by batch row (slot * C + pos).  info [count][4]: accepted, forced, open, done.
+// open_rows/n_open_rows: compacted list of batch rows still open after the step.
+void dg_launch_sample(const DgSampleArgs& a, const float* ent, const int32_t* amax, int32_t* info,
+                      int32_t* open_rows, int32_t* n_open_rows, hipStream_t s);
+// Canvas start: draw every position at step 0, clear accepted; also builds the open-row list.
+void dg_launch_canvas_init(const DgSampleArgs& a, int32_t* open_rows, int32_t* n_open_rows, hipStream_t s);
+// Open-row list from the accepted flags (used after state injection).
+void dg_launch_open_rows(const DgSampleArgs& a, int32_t* open_rows, int32_t* n_open_rows, hipStream_t s);
+void dg_launch_philox_tokens(uint64_t seed, int block, int step, int n, int vocab, int32_t* out, hipStream_t s);
+// Gather rows by index list into a compact fp32 buffer (used by the logits tap).
+void dg_launch_gather_rows(const float* x, const int32_t* idx, int n, int d, float* out, hipStream_t s);

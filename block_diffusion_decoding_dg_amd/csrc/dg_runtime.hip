@@ -1,0 +1,760 @@
+// libdg runtime: the C ABI of include/dg.h on top of the kernels.
+//
+// The context borrows caller-owned device memory (weights, KV cache, scratch) and
+// a HIP stream, keeps the per-request state machine on the host, and queues the
+// kernels of prefill, denoising step and block commit.  The only host<->device
+// traffic per denoising step is the queue of launches and one small read-back of
+// the per-request step counters.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dg.h"
+#include "dg_kernels.h"
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct Request {
+  bool prefilled = false;
+  bool active = false;
+  bool done = false;
+  int32_t P = 0;
+  int32_t block = 0;
+  int32_t step = 0;
+  uint64_t seed = 0;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <typename P> P* take(size_t bytes) {
+    off = align_up(off, 256);
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+}  // namespace
+
+struct dg_ctx {
+  dg_model_config cfg;
+  dg_sampler_config scfg;
+  int dtype = 0;
+  size_t esz = 4;
+  const void* embed = nullptr;
+  const void* final_norm = nullptr;
+  std::vector<dg_layer_weights> layers;
+  char* kv = nullptr;
+  hipStream_t stream = nullptr;
+  int C = 256;
+  int rows_step = 0;   // max_requests * C
+  int rows_max = 0;    // max(rows_step, prefill_chunk)
+  int prefill_chunk = 2048;
+  int lm_tiles = 0;
+  size_t attn_cap = 0;  // partial rows (split x row x q-head) the attention buffers hold, / hq
+
+  // scratch
+  float* x = nullptr;
+  void* xn = nullptr;
+  void* q = nullptr;
+  void* ao = nullptr;
+  float* opart = nullptr;
+  float* mlpart = nullptr;
+  float* rlogits = nullptr;
+  int32_t* rids = nullptr;
+  float* rgates = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* perm = nullptr;
+  void* hbuf = nullptr;
+  void* hs = nullptr;
+  float* ybuf = nullptr;
+  void* hn = nullptr;
+  float* lpart = nullptr;
+  int32_t* lpart_arg = nullptr;
+  float* ent = nullptr;
+  float* lse = nullptr;
+  int32_t* amax = nullptr;
+  int32_t* open_rows = nullptr;
+  int32_t* n_open_rows = nullptr;
+  int32_t* canvas_ids = nullptr;
+  uint8_t* canvas_acc = nullptr;
+  int32_t* info_dev = nullptr;
+  int32_t* tap_ids = nullptr;
+  float* tap_gates = nullptr;
+  double* inv_freq = nullptr;
+  int32_t* ids_stage = nullptr;
+  float* xg = nullptr;  // gathered rows for the logits tap [rows_step][d]
+
+  int32_t* info_host = nullptr;  // pinned [max_requests][4]
+
+  std::vector<Request> req;
+  std::vector<int> last_slots;  // request of each slot in the last step
+  int last_rows = 0;
+  std::string err;
+};
+
+namespace {
+
+dg_status fail(dg_ctx* c, dg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  else g_create_error = buf;
+  return st;
+}
+
+#define HIPCK(ctx, call)                                                                              \
+  do {                                                                                                \
+    hipError_t e_ = (call);                                                                           \
+    if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));     \
+  } while (0)
+
+#define LAUNCHCK(ctx)                                                                                  \
+  do {                                                                                                 \
+    hipError_t e_ = hipGetLastError();                                                                 \
+    if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+int kc_of(int dtype) { return dtype == DG_BF16 ? 32 : 16; }
+
+// Validation of shapes against what the kernels implement.  Returns a message or null.
+const char* check_config(const dg_model_config* c) {
+  if (!c) return "null config";
+  if (c->dtype != DG_F32 && c->dtype != DG_BF16) return "dtype must be DG_F32 or DG_BF16";
+  if (c->vocab <= 0 || c->d_model <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->expert_hidden <= 0 || c->shared_hidden <= 0 ||
+      c->max_ctx <= 0 || c->max_requests <= 0)
+    return "every size must be positive";
+  if (c->canvas_len != 256) return "canvas_len must be 256";
+  if (c->max_requests > DG_MAX_SEGS) return "max_requests must be <= 16";
+  if (c->n_q_heads % c->n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+  const int kc = kc_of(c->dtype);
+  const int hd = c->head_dim;
+  if (!(hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256)) return "head_dim must be 16, 32, 64, 128 or 256";
+  if (c->dtype == DG_BF16 && hd < 32) return "bf16 head_dim must be >= 32";
+  if (((c->n_q_heads + 2 * c->n_kv_heads) * hd / 2) % 16) return "(Hq + 2 Hkv) * head_dim / 2 must be a multiple of 16";
+  if (c->d_model % 64 || c->d_model % kc) return "d_model must be a multiple of 64";
+  if ((c->n_q_heads * hd) % kc) return "n_q_heads * head_dim must be a multiple of the k-chunk";
+  if (c->expert_hidden % 64) return "expert_hidden must be a multiple of 64";
+  if (c->shared_hidden % 16 || c->shared_hidden % kc) return "shared_hidden must be a multiple of 16 and the k-chunk";
+  if (c->vocab % 128) return "vocab must be a multiple of 128";
+  if (c->n_experts > 256) return "n_experts must be <= 256";
+  if (c->top_k > 16 || c->top_k > c->n_experts) return "top_k must be <= 16 and <= n_experts";
+  if (c->max_ctx % 64) return "max_ctx must be a multiple of 64";
+  if (c->max_ctx < c->canvas_len) return "max_ctx must hold at least one canvas";
+  if (c->prefill_chunk < 0) return "prefill_chunk must be >= 0";
+  return nullptr;
+}
+
+struct Plan {
+  size_t kv_bytes = 0, scratch_bytes = 0;
+};
+
+// Carves the scratch (base may be null to only size it).
+size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
+  Carve cv{base};
+  const size_t es = m.dtype == DG_BF16 ? 2 : 4;
+  const int C = m.canvas_len;
+  const int Rs = m.max_requests * C;
+  const int pc = m.prefill_chunk > 0 ? m.prefill_chunk : 2048;
+  const int Tm = std::max(Rs, pc);
+  const size_t d = m.d_model, qd = (size_t)m.n_q_heads * m.head_dim;
+  const size_t k = m.top_k, E = m.n_experts;
+  const size_t attn_cap = std::max((size_t)32 * Rs, (size_t)4 * Tm);
+  const int tiles = dg_lm_head_tiles(m.vocab);
+  c->x = cv.take<float>(Tm * d * 4);
+  c->xn = cv.take<void>(Tm * d * es);
+  c->q = cv.take<void>(Tm * qd * es);
+  c->ao = cv.take<void>(Tm * qd * es);
+  c->opart = cv.take<float>(attn_cap * m.n_q_heads * m.head_dim * 4);
+  c->mlpart = cv.take<float>(attn_cap * m.n_q_heads * 2 * 4);
+  c->rlogits = cv.take<float>(Tm * E * 4);
+  c->rids = cv.take<int32_t>(Tm * k * 4);
+  c->rgates = cv.take<float>(Tm * k * 4);
+  c->counts = cv.take<int32_t>(E * 4);
+  c->offsets = cv.take<int32_t>(E * 4);
+  c->perm = cv.take<int32_t>(Tm * k * 4);
+  c->hbuf = cv.take<void>(Tm * k * m.expert_hidden * es);
+  c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
+  c->ybuf = cv.take<float>(Tm * k * d * 4);
+  c->hn = cv.take<void>(Rs * d * es);
+  c->lpart = cv.take<float>((size_t)Rs * tiles * 3 * 4);
+  c->lpart_arg = cv.take<int32_t>((size_t)Rs * tiles * 4);
+  c->ent = cv.take<float>(Rs * 4);
+  c->lse = cv.take<float>(Rs * 4);
+  c->amax = cv.take<int32_t>(Rs * 4);
+  c->open_rows = cv.take<int32_t>(Rs * 4);
+  c->n_open_rows = cv.take<int32_t>(4);
+  c->canvas_ids = cv.take<int32_t>(Rs * 4);
+  c->canvas_acc = cv.take<uint8_t>(Rs);
+  c->info_dev = cv.take<int32_t>(m.max_requests * 4 * 4);
+  c->tap_ids = cv.take<int32_t>((size_t)m.n_layers * Rs * k * 4);
+  c->tap_gates = cv.take<float>((size_t)m.n_layers * Rs * k * 4);
+  c->inv_freq = cv.take<double>(m.head_dim / 2 * 8);
+  c->ids_stage = cv.take<int32_t>(Tm * 4);
+  c->xg = cv.take<float>(Rs * d * 4);
+  c->attn_cap = attn_cap;
+  return align_up(cv.off, 256);
+}
+
+size_t kv_size(const dg_model_config& m) {
+  const size_t es = m.dtype == DG_BF16 ? 2 : 4;
+  return (size_t)m.max_requests * m.n_layers * 2 * m.n_kv_heads * (size_t)m.max_ctx * m.head_dim * es;
+}
+
+DgShape shape_of(const dg_ctx* c) {
+  DgShape s;
+  s.d = c->cfg.d_model;
+  s.hq = c->cfg.n_q_heads;
+  s.hkv = c->cfg.n_kv_heads;
+  s.hd = c->cfg.head_dim;
+  s.max_ctx = c->cfg.max_ctx;
+  s.vocab = c->cfg.vocab;
+  return s;
+}
+
+void* kv_ptr(const dg_ctx* c, int r, int l, int which) {
+  const size_t per = (size_t)c->cfg.n_kv_heads * c->cfg.max_ctx * c->cfg.head_dim * c->esz;
+  return c->kv + (((size_t)r * c->cfg.n_layers + l) * 2 + which) * per;
+}
+
+// Segments (one per slot) for layer l.  rows of slot s: [s*n, (s+1)*n).
+struct SlotRow {
+  int req, pos0, n;
+};
+
+DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool causal) {
+  DgSegs sg;
+  memset(&sg, 0, sizeof sg);
+  int row = 0;
+  for (size_t i = 0; i < slots.size(); ++i) {
+    sg.s[i].k = kv_ptr(c, slots[i].req, l, 0);
+    sg.s[i].vt = kv_ptr(c, slots[i].req, l, 1);
+    sg.s[i].row0 = row;
+    sg.s[i].n = slots[i].n;
+    sg.s[i].pos0 = slots[i].pos0;
+    sg.s[i].nkeys = slots[i].pos0 + slots[i].n;
+    row += slots[i].n;
+  }
+  sg.count = (int)slots.size();
+  sg.causal = causal ? 1 : 0;
+  return sg;
+}
+
+// Attention half of layer l over `rows` rows in c->x.
+void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal) {
+  const dg_model_config& m = c->cfg;
+  const dg_layer_weights& w = c->layers[l];
+  hipStream_t s = c->stream;
+  const DgShape sh = shape_of(c);
+  const DgSegs sg = make_segs(c, slots, l, causal);
+  dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, s);
+  dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, s);
+  const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
+  const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
+  dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s);
+  dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x, m.d_model, s);
+}
+
+// FFN half of layer l over `rows` rows in c->x; routing written to ids/gates.
+void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates) {
+  const dg_model_config& m = c->cfg;
+  const dg_layer_weights& w = c->layers[l];
+  hipStream_t s = c->stream;
+  dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, s);
+  dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, c->rlogits, m.n_experts, s);
+  dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s);
+  dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s);
+  dg_launch_expert_up(c->dtype, c->xn, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w1, w.w3,
+                      c->counts, c->offsets, c->perm, c->hbuf, s);
+  dg_launch_expert_down(c->dtype, c->hbuf, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w2, c->counts,
+                        c->offsets, c->perm, c->ybuf, s);
+  dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s);
+  dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s);
+  dg_launch_combine(c->x, c->ybuf, gates, rows, m.d_model, m.top_k, s);
+}
+
+// Forward of the rows in c->x through all layers.  kv_only: the last layer only
+// writes its K/V (commit and prefill need nothing else from it).
+void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool causal, bool kv_only, bool tap) {
+  const dg_model_config& m = c->cfg;
+  for (int l = 0; l < m.n_layers; ++l) {
+    const bool last = l == m.n_layers - 1;
+    if (last && kv_only) {
+      const DgShape sh = shape_of(c);
+      const DgSegs sg = make_segs(c, slots, l, causal);
+      const dg_layer_weights& w = c->layers[l];
+      dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, c->stream);
+      dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, c->stream);
+      break;
+    }
+    attn_half(c, l, slots, rows, causal);
+    int32_t* ids = tap ? c->tap_ids + (size_t)l * c->rows_step * m.top_k : c->rids;
+    float* gates = tap ? c->tap_gates + (size_t)l * c->rows_step * m.top_k : c->rgates;
+    ffn_half(c, l, rows, ids, gates);
+  }
+}
+
+DgSampleArgs sample_args(const dg_ctx* c, const std::vector<int>& slot_req) {
+  DgSampleArgs a;
+  memset(&a, 0, sizeof a);
+  for (size_t i = 0; i < slot_req.size(); ++i) {
+    const int r = slot_req[i];
+    a.s[i].ids = c->canvas_ids + (size_t)r * c->C;
+    a.s[i].accepted = c->canvas_acc + (size_t)r * c->C;
+    a.s[i].seed = c->req[r].seed;
+    a.s[i].block = c->req[r].block;
+    a.s[i].step = c->req[r].step + 1;
+    a.s[i].row0 = (int)i * c->C;
+  }
+  a.count = (int)slot_req.size();
+  a.C = c->C;
+  a.vocab = c->cfg.vocab;
+  a.max_steps = c->scfg.max_steps > 0 ? c->scfg.max_steps : c->C;
+  a.tau = c->scfg.tau;
+  return a;
+}
+
+dg_status check_req(dg_ctx* c, int32_t req) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (req < 0 || req >= c->cfg.max_requests)
+    return fail(c, DG_ERR_CAPACITY, "request %d outside [0, %d)", req, c->cfg.max_requests);
+  return DG_OK;
+}
+
+double now_ms() {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_workspace_size(const dg_model_config* cfg, size_t* kv_bytes, size_t* scratch_bytes) {
+  const char* msg = check_config(cfg);
+  if (msg) return fail(nullptr, DG_ERR_INVALID_ARG, "%s", msg);
+  if (!kv_bytes || !scratch_bytes) return fail(nullptr, DG_ERR_INVALID_ARG, "null output pointer");
+  dg_ctx tmp;
+  *kv_bytes = kv_size(*cfg);
+  *scratch_bytes = carve(&tmp, *cfg, nullptr);
+  return DG_OK;
+}
+
+dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, const dg_weights* weights,
+                    void* kv_dev, size_t kv_bytes, void* scratch_dev, size_t scratch_bytes, void* stream,
+                    dg_ctx** out) {
+  if (out) *out = nullptr;
+  if (!out) return fail(nullptr, DG_ERR_INVALID_ARG, "null output pointer");
+  const char* msg = check_config(cfg);
+  if (msg) return fail(nullptr, DG_ERR_INVALID_ARG, "%s", msg);
+  if (!scfg) return fail(nullptr, DG_ERR_INVALID_ARG, "null sampler config");
+  if (!(scfg->tau >= 0.f)) return fail(nullptr, DG_ERR_INVALID_ARG, "tau must be >= 0");
+  if (!weights || !weights->embed || !weights->final_norm || !weights->layers)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "null weights");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dg_layer_weights& w = weights->layers[l];
+    const void* ps[] = {w.attn_norm, w.wq, w.wk, w.wv, w.wo, w.ffn_norm, w.router, w.w1, w.w3, w.w2, w.sw1, w.sw3, w.sw2};
+    for (const void* p : ps)
+      if (!p) return fail(nullptr, DG_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
+  }
+  if (!kv_dev || !scratch_dev) return fail(nullptr, DG_ERR_INVALID_ARG, "null kv or scratch buffer");
+  dg_model_config m = *cfg;
+  if (m.prefill_chunk == 0) m.prefill_chunk = 2048;
+  size_t need_kv = 0, need_scratch = 0;
+  dg_workspace_size(&m, &need_kv, &need_scratch);
+  if (kv_bytes < need_kv || scratch_bytes < need_scratch)
+    return fail(nullptr, DG_ERR_WORKSPACE, "workspace too small: kv %zu < %zu or scratch %zu < %zu", kv_bytes,
+                need_kv, scratch_bytes, need_scratch);
+
+  dg_ctx* c = new dg_ctx();
+  c->cfg = m;
+  c->scfg = *scfg;
+  c->dtype = m.dtype;
+  c->esz = m.dtype == DG_BF16 ? 2 : 4;
+  c->embed = weights->embed;
+  c->final_norm = weights->final_norm;
+  c->layers.assign(weights->layers, weights->layers + m.n_layers);
+  c->kv = (char*)kv_dev;
+  c->stream = (hipStream_t)stream;
+  c->C = m.canvas_len;
+  c->rows_step = m.max_requests * m.canvas_len;
+  c->prefill_chunk = m.prefill_chunk;
+  c->rows_max = std::max(c->rows_step, c->prefill_chunk);
+  c->lm_tiles = dg_lm_head_tiles(m.vocab);
+  c->req.resize(m.max_requests);
+  carve(c, m, (char*)scratch_dev);
+
+  std::vector<double> inv(m.head_dim / 2);
+  for (int j = 0; j < m.head_dim / 2; ++j) inv[j] = std::pow((double)m.rope_theta, -2.0 * j / m.head_dim);
+  hipError_t e = hipMemcpyAsync(c->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice, c->stream);
+  // Keys past a request's length are read (with zero weight) by the attention
+  // tiles; zeroing the cache once keeps those reads finite.
+  if (e == hipSuccess) e = hipMemsetAsync(c->kv, 0, need_kv, c->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->canvas_acc, 1, c->rows_step, c->stream);
+  if (e == hipSuccess) e = hipHostMalloc((void**)&c->info_host, m.max_requests * 4 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    fail(nullptr, DG_ERR_HIP, "create: %s", hipGetErrorString(e));
+    if (c->info_host) hipHostFree(c->info_host);
+    delete c;
+    return DG_ERR_HIP;
+  }
+  *out = c;
+  return DG_OK;
+}
+
+void dg_destroy(dg_ctx* ctx) {
+  if (!ctx) return;
+  hipStreamSynchronize(ctx->stream);
+  if (ctx->info_host) hipHostFree(ctx->info_host);
+  delete ctx;
+}
+
+const char* dg_last_error(const dg_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
+
+dg_status dg_prefill(dg_ctx* c, int32_t req, const int32_t* prompt_ids, int32_t n, uint64_t seed) {
+  dg_status st = check_req(c, req);
+  if (st != DG_OK) return st;
+  if (n < 0 || (n > 0 && !prompt_ids)) return fail(c, DG_ERR_INVALID_ARG, "bad prompt");
+  if (n + c->C > c->cfg.max_ctx)
+    return fail(c, DG_ERR_CAPACITY, "prompt of %d tokens plus one canvas exceeds max_ctx %d", n, c->cfg.max_ctx);
+  for (int i = 0; i < n; ++i)
+    if (prompt_ids[i] < 0 || prompt_ids[i] >= c->cfg.vocab)
+      return fail(c, DG_ERR_INVALID_ARG, "prompt id %d at %d out of range", prompt_ids[i], i);
+  for (int c0 = 0; c0 < n; c0 += c->prefill_chunk) {
+    const int cn = std::min(c->prefill_chunk, n - c0);
+    HIPCK(c, hipMemcpyAsync(c->ids_stage, prompt_ids + c0, cn * 4, hipMemcpyHostToDevice, c->stream));
+    dg_launch_embed(c->dtype, c->ids_stage, cn, c->embed, c->cfg.d_model, c->x, c->stream);
+    std::vector<SlotRow> slots{{req, c0, cn}};
+    forward_layers(c, slots, cn, true, true, false);
+    LAUNCHCK(c);
+    // the staging buffer is reused by the next chunk
+    HIPCK(c, hipStreamSynchronize(c->stream));
+  }
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  Request& r = c->req[req];
+  r = Request();
+  r.prefilled = true;
+  r.P = n;
+  r.seed = seed;
+  return DG_OK;
+}
+
+dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
+  if (!c || !info) return fail(c, DG_ERR_INVALID_ARG, "null argument");
+  const int R = c->cfg.max_requests;
+  std::vector<int> slot_req, fresh;
+  for (int r = 0; r < R; ++r) {
+    Request& q = c->req[r];
+    info[r] = dg_step_info{0, q.block, q.step, 0, 0, 0, q.done ? 1 : 0};
+    if (!q.prefilled) continue;
+    if (q.active && q.done) continue;
+    if (!q.active && q.P + c->C > c->cfg.max_ctx) continue;
+    slot_req.push_back(r);
+    if (!q.active) fresh.push_back(r);
+  }
+  if (slot_req.empty()) return fail(c, DG_ERR_STATE, "no request can take a denoising step");
+  hipStream_t s = c->stream;
+  if (!fresh.empty()) {
+    for (int r : fresh) {
+      c->req[r].active = true;
+      c->req[r].done = false;
+      c->req[r].step = 0;
+    }
+    DgSampleArgs ia = sample_args(c, fresh);
+    dg_launch_canvas_init(ia, c->open_rows, c->n_open_rows, s);
+  }
+  const DgSampleArgs a = sample_args(c, slot_req);
+  const int rows = a.count * c->C;
+  std::vector<SlotRow> slots;
+  for (int r : slot_req) slots.push_back({r, c->req[r].P, c->C});
+  dg_launch_open_rows(a, c->open_rows, c->n_open_rows, s);
+  dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s);
+  forward_layers(c, slots, rows, false, false, true);
+  dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
+                    c->cfg.rms_eps, c->hn, s);
+  dg_launch_lm_head(c->dtype, c->hn, c->n_open_rows, rows, c->cfg.d_model, c->embed, c->cfg.vocab, c->lpart,
+                    c->lpart_arg, c->ent, c->lse, c->amax, c->open_rows, s);
+  dg_launch_sample(a, c->ent, c->amax, c->info_dev, nullptr, nullptr, s);
+  LAUNCHCK(c);
+  HIPCK(c, hipMemcpyAsync(c->info_host, c->info_dev, a.count * 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  HIPCK(c, hipStreamSynchronize(s));
+  for (size_t i = 0; i < slot_req.size(); ++i) {
+    const int r = slot_req[i];
+    Request& q = c->req[r];
+    q.step += 1;
+    q.done = c->info_host[i * 4 + 3] != 0;
+    info[r] = dg_step_info{1, q.block, q.step, c->info_host[i * 4 + 0], c->info_host[i * 4 + 1],
+                           c->info_host[i * 4 + 2], q.done ? 1 : 0};
+  }
+  c->last_slots = slot_req;
+  c->last_rows = rows;
+  return DG_OK;
+}
+
+dg_status dg_commit_block(dg_ctx* c, int32_t req, int32_t* out_ids) {
+  dg_status st = check_req(c, req);
+  if (st != DG_OK) return st;
+  Request& q = c->req[req];
+  if (!q.active || !q.done) return fail(c, DG_ERR_STATE, "request %d has no finished canvas", req);
+  hipStream_t s = c->stream;
+  std::vector<int> one{req};
+  const DgSampleArgs a = sample_args(c, one);
+  dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s);
+  std::vector<SlotRow> slots{{req, q.P, c->C}};
+  forward_layers(c, slots, c->C, false, true, false);
+  LAUNCHCK(c);
+  if (out_ids)
+    HIPCK(c, hipMemcpyAsync(out_ids, c->canvas_ids + (size_t)req * c->C, c->C * 4, hipMemcpyDeviceToHost, s));
+  HIPCK(c, hipStreamSynchronize(s));
+  q.P += c->C;
+  q.block += 1;
+  q.step = 0;
+  q.active = false;
+  q.done = false;
+  return DG_OK;
+}
+
+dg_status dg_generate(dg_ctx* c, int32_t n_req, const int32_t* const* prompts, const int32_t* n_prompt,
+                      int32_t n_out, const uint64_t* seeds, int32_t* const* out_ids, dg_stats* stats) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (n_req <= 0 || n_req > c->cfg.max_requests)
+    return fail(c, DG_ERR_CAPACITY, "n_req %d outside [1, %d]", n_req, c->cfg.max_requests);
+  if (!prompts || !n_prompt || !seeds || !out_ids || n_out <= 0) return fail(c, DG_ERR_INVALID_ARG, "bad argument");
+  const int C = c->C;
+  const int n_blocks = (n_out + C - 1) / C;
+  for (int r = 0; r < n_req; ++r) {
+    if (!out_ids[r]) return fail(c, DG_ERR_INVALID_ARG, "null output of request %d", r);
+    if (n_prompt[r] + (int64_t)n_blocks * C > c->cfg.max_ctx)
+      return fail(c, DG_ERR_CAPACITY, "request %d: prompt %d + %d blocks exceeds max_ctx", r, n_prompt[r], n_blocks);
+  }
+  dg_stats stt{};
+  // requests beyond n_req take no part
+  for (int r = n_req; r < c->cfg.max_requests; ++r) c->req[r] = Request();
+  double t0 = now_ms();
+  for (int r = 0; r < n_req; ++r) {
+    dg_status st = dg_prefill(c, r, prompts[r], n_prompt[r], seeds[r]);
+    if (st != DG_OK) return st;
+  }
+  stt.prefill_ms = now_ms() - t0;
+  std::vector<dg_step_info> info(c->cfg.max_requests);
+  std::vector<int32_t> blk(C);
+  for (int b = 0; b < n_blocks; ++b) {
+    while (true) {
+      t0 = now_ms();
+      dg_status st = dg_denoise_step(c, info.data());
+      if (st != DG_OK) return st;
+      stt.decode_ms += now_ms() - t0;
+      stt.steps += 1;
+      bool all_done = true;
+      for (int r = 0; r < n_req; ++r) {
+        if (info[r].active) stt.tokens += info[r].n_accepted + info[r].n_forced;
+        all_done = all_done && c->req[r].done;
+      }
+      if (all_done) break;
+    }
+    t0 = now_ms();
+    for (int r = 0; r < n_req; ++r) {
+      dg_status st = dg_commit_block(c, r, blk.data());
+      if (st != DG_OK) return st;
+      const int take = std::min(C, n_out - b * C);
+      memcpy(out_ids[r] + b * C, blk.data(), take * sizeof(int32_t));
+    }
+    stt.commit_ms += now_ms() - t0;
+  }
+  if (stats) *stats = stt;
+  return DG_OK;
+}
+
+dg_status dg_get_request(dg_ctx* c, int32_t req, dg_request_state* st) {
+  dg_status s = check_req(c, req);
+  if (s != DG_OK) return s;
+  if (!st) return fail(c, DG_ERR_INVALID_ARG, "null output");
+  const Request& q = c->req[req];
+  *st = dg_request_state{q.prefilled, q.P, q.block, q.step, q.active, q.done, q.seed};
+  return DG_OK;
+}
+
+dg_status dg_get_canvas(dg_ctx* c, int32_t req, int32_t* ids, uint8_t* accepted) {
+  dg_status s = check_req(c, req);
+  if (s != DG_OK) return s;
+  if (!c->req[req].active) return fail(c, DG_ERR_STATE, "request %d has no canvas", req);
+  if (ids) HIPCK(c, hipMemcpyAsync(ids, c->canvas_ids + (size_t)req * c->C, c->C * 4, hipMemcpyDeviceToHost, c->stream));
+  if (accepted)
+    HIPCK(c, hipMemcpyAsync(accepted, c->canvas_acc + (size_t)req * c->C, c->C, hipMemcpyDeviceToHost, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  return DG_OK;
+}
+
+dg_status dg_set_canvas(dg_ctx* c, int32_t req, const int32_t* ids, const uint8_t* accepted, int32_t step,
+                        int32_t block) {
+  dg_status s = check_req(c, req);
+  if (s != DG_OK) return s;
+  Request& q = c->req[req];
+  if (!q.prefilled) return fail(c, DG_ERR_STATE, "request %d is not prefilled", req);
+  if (!ids || !accepted || step < 0 || block < 0) return fail(c, DG_ERR_INVALID_ARG, "bad canvas state");
+  if (q.P + c->C > c->cfg.max_ctx) return fail(c, DG_ERR_CAPACITY, "no room for a canvas");
+  int open = 0;
+  for (int i = 0; i < c->C; ++i) {
+    if (ids[i] < 0 || ids[i] >= c->cfg.vocab) return fail(c, DG_ERR_INVALID_ARG, "canvas id out of range");
+    if (accepted[i] > 1) return fail(c, DG_ERR_INVALID_ARG, "accepted flags must be 0 or 1");
+    open += accepted[i] == 0;
+  }
+  HIPCK(c, hipMemcpyAsync(c->canvas_ids + (size_t)req * c->C, ids, c->C * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCK(c, hipMemcpyAsync(c->canvas_acc + (size_t)req * c->C, accepted, c->C, hipMemcpyHostToDevice, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  q.active = true;
+  q.done = open == 0;
+  q.step = step;
+  q.block = block;
+  return DG_OK;
+}
+
+dg_status dg_set_committed(dg_ctx* c, int32_t req, int32_t committed, uint64_t seed) {
+  dg_status s = check_req(c, req);
+  if (s != DG_OK) return s;
+  if (committed < 0 || committed + c->C > c->cfg.max_ctx)
+    return fail(c, DG_ERR_CAPACITY, "committed length %d leaves no room for a canvas", committed);
+  Request& q = c->req[req];
+  q = Request();
+  q.prefilled = true;
+  q.P = committed;
+  q.seed = seed;
+  return DG_OK;
+}
+
+dg_status dg_last_step_rows(dg_ctx* c, int32_t* n_rows, float* entropy, float* lse, int32_t* argmax,
+                            int32_t* router_ids, float* router_gates) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
+  const int rows = c->last_rows;
+  const int k = c->cfg.top_k;
+  if (n_rows) *n_rows = rows;
+  hipStream_t s = c->stream;
+  if (entropy) HIPCK(c, hipMemcpyAsync(entropy, c->ent, rows * 4, hipMemcpyDeviceToHost, s));
+  if (lse) HIPCK(c, hipMemcpyAsync(lse, c->lse, rows * 4, hipMemcpyDeviceToHost, s));
+  if (argmax) HIPCK(c, hipMemcpyAsync(argmax, c->amax, rows * 4, hipMemcpyDeviceToHost, s));
+  for (int l = 0; l < c->cfg.n_layers; ++l) {
+    const size_t src = (size_t)l * c->rows_step * k, dst = (size_t)l * rows * k;
+    if (router_ids)
+      HIPCK(c, hipMemcpyAsync(router_ids + dst, c->tap_ids + src, (size_t)rows * k * 4, hipMemcpyDeviceToHost, s));
+    if (router_gates)
+      HIPCK(c, hipMemcpyAsync(router_gates + dst, c->tap_gates + src, (size_t)rows * k * 4, hipMemcpyDeviceToHost, s));
+  }
+  HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_last_step_logits(dg_ctx* c, const int32_t* rows_list, int32_t n, float* logits_dev) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
+  if (n <= 0 || n > c->rows_step || !rows_list || !logits_dev) return fail(c, DG_ERR_INVALID_ARG, "bad row list");
+  for (int i = 0; i < n; ++i)
+    if (rows_list[i] < 0 || rows_list[i] >= c->last_rows) return fail(c, DG_ERR_INVALID_ARG, "row out of range");
+  hipStream_t s = c->stream;
+  HIPCK(c, hipMemcpyAsync(c->ids_stage, rows_list, n * 4, hipMemcpyHostToDevice, s));
+  dg_launch_rmsnorm(c->dtype, c->x, c->ids_stage, nullptr, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn, s);
+  dg_launch_gemm(c->dtype, 1, c->hn, n, c->cfg.d_model, c->embed, c->cfg.vocab, logits_dev, c->cfg.vocab, s);
+  LAUNCHCK(c);
+  HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_op_attention(dg_ctx* c, int32_t req, int32_t layer, float* x_dev, int32_t t, int32_t pos0,
+                          int32_t causal) {
+  dg_status st = check_req(c, req);
+  if (st != DG_OK) return st;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, DG_ERR_INVALID_ARG, "bad layer");
+  if (!x_dev || t <= 0 || t > c->rows_max || pos0 < 0 || pos0 + t > c->cfg.max_ctx)
+    return fail(c, DG_ERR_INVALID_ARG, "bad rows");
+  const size_t bytes = (size_t)t * c->cfg.d_model * 4;
+  HIPCK(c, hipMemcpyAsync(c->x, x_dev, bytes, hipMemcpyDeviceToDevice, c->stream));
+  std::vector<SlotRow> slots{{req, pos0, t}};
+  attn_half(c, layer, slots, t, causal != 0);
+  LAUNCHCK(c);
+  HIPCK(c, hipMemcpyAsync(x_dev, c->x, bytes, hipMemcpyDeviceToDevice, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  return DG_OK;
+}
+
+dg_status dg_op_moe(dg_ctx* c, int32_t layer, float* x_dev, int32_t t, int32_t* ids_dev, float* gates_dev) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, DG_ERR_INVALID_ARG, "bad layer");
+  if (!x_dev || t <= 0 || t > c->rows_max) return fail(c, DG_ERR_INVALID_ARG, "bad rows");
+  const size_t bytes = (size_t)t * c->cfg.d_model * 4;
+  HIPCK(c, hipMemcpyAsync(c->x, x_dev, bytes, hipMemcpyDeviceToDevice, c->stream));
+  ffn_half(c, layer, t, c->rids, c->rgates);
+  LAUNCHCK(c);
+  HIPCK(c, hipMemcpyAsync(x_dev, c->x, bytes, hipMemcpyDeviceToDevice, c->stream));
+  const size_t kb = (size_t)t * c->cfg.top_k * 4;
+  if (ids_dev) HIPCK(c, hipMemcpyAsync(ids_dev, c->rids, kb, hipMemcpyDeviceToDevice, c->stream));
+  if (gates_dev) HIPCK(c, hipMemcpyAsync(gates_dev, c->rgates, kb, hipMemcpyDeviceToDevice, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  return DG_OK;
+}
+
+dg_status dg_op_lm_head(dg_ctx* c, const float* h_dev, int32_t n, float* entropy_dev, float* lse_dev,
+                        int32_t* argmax_dev) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (!h_dev || n <= 0 || n > c->rows_step || !entropy_dev || !lse_dev || !argmax_dev)
+    return fail(c, DG_ERR_INVALID_ARG, "bad arguments");
+  hipStream_t s = c->stream;
+  HIPCK(c, hipMemcpyAsync(c->n_open_rows, &n, 4, hipMemcpyHostToDevice, s));
+  dg_launch_rmsnorm(c->dtype, h_dev, nullptr, c->n_open_rows, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn,
+                    s);
+  dg_launch_lm_head(c->dtype, c->hn, c->n_open_rows, n, c->cfg.d_model, c->embed, c->cfg.vocab, c->lpart,
+                    c->lpart_arg, entropy_dev, lse_dev, argmax_dev, nullptr, s);
+  LAUNCHCK(c);
+  HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_op_sample(dg_ctx* c, int32_t req, const float* entropy_dev, const int32_t* argmax_dev, int32_t step,
+                       dg_step_info* info) {
+  dg_status st = check_req(c, req);
+  if (st != DG_OK) return st;
+  Request& q = c->req[req];
+  if (!q.active) return fail(c, DG_ERR_STATE, "request %d has no canvas", req);
+  if (!entropy_dev || !argmax_dev || !info || step < 1) return fail(c, DG_ERR_INVALID_ARG, "bad arguments");
+  std::vector<int> one{req};
+  DgSampleArgs a = sample_args(c, one);
+  a.s[0].step = step;
+  dg_launch_sample(a, entropy_dev, argmax_dev, c->info_dev, nullptr, nullptr, c->stream);
+  LAUNCHCK(c);
+  HIPCK(c, hipMemcpyAsync(c->info_host, c->info_dev, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  q.step = step;
+  q.done = c->info_host[3] != 0;
+  *info = dg_step_info{1, q.block, step, c->info_host[0], c->info_host[1], c->info_host[2], q.done ? 1 : 0};
+  return DG_OK;
+}
+
+dg_status dg_philox_tokens(uint64_t seed, int32_t block, int32_t step, int32_t n, int32_t vocab, int32_t* out_dev,
+                           void* stream) {
+  if (n < 0 || vocab <= 0 || block < 0 || step < 0 || (n > 0 && !out_dev))
+    return fail(nullptr, DG_ERR_INVALID_ARG, "bad arguments");
+  hipStream_t s = (hipStream_t)stream;
+  dg_launch_philox_tokens(seed, block, step, n, vocab, out_dev, s);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(nullptr, DG_ERR_HIP, "philox: %s", hipGetErrorString(e));
+  return DG_OK;
+}
+
+}  // extern "C"

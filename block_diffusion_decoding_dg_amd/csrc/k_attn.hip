@@ -1,0 +1,255 @@
+// Bidirectional (or causal, for the prompt) grouped-query attention of a batch of
+// rows over their request's KV cache, split over keys (flash-decoding style) and
+// merged with the log-sum-exp rule.
+//
+// Every canvas position sees the whole committed prefix and the whole canvas
+// ("Google open-sources DiffusionGemma", section "26B MoE Architecture, but Only
+// 3.8B Activated": bidirectional attention, every token sees all others in its
+// context; "DiffusionGemma hits ~1,500 TPS on one H100", section "How the sampler
+// actually works": the decoder runs bidirectionally over the full canvas).
+//
+// Layout of the work: a block takes one kv-head h of one request, 128 "query
+// rows" (pairs of (q-head of h's group, canvas row), head-major) and one key
+// range.  Each wave owns 32 query rows.  Scores are formed transposed,
+// S^T = K Q^T, so that lane l holds, for query column l % 16, keys 4*(l/16)+i:
+// exactly the B-operand layout of O^T = V^T P^T on the matrix cores.  With V
+// stored transposed in the cache ([hd][position]) both operands of both
+// products are plain row loads; P never leaves registers.
+#include "dg_common.h"
+#include "dg_kernels.h"
+
+#define ATTN_QROWS 128  // query rows per block (4 waves x 32)
+
+template <typename T, int HD>
+__global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape sh, DgSegs sg, int nqb, int nsplit,
+                                              float* __restrict__ opart, float* __restrict__ mlpart, int rows_total) {
+  typedef typename MF<T>::frag F;
+  constexpr int KC = MF<T>::KC;
+  constexpr int NKK = HD / KC;  // k-chunks over the head dimension
+  constexpr int NHT = HD / 16;  // 16-row tiles of O^T
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+
+  int bid = blockIdx.x;
+  const int split = bid % nsplit;
+  bid /= nsplit;
+  const int qb = bid % nqb;
+  bid /= nqb;
+  const int h = bid % sh.hkv;
+  const int si = bid / sh.hkv;
+  if (si >= sg.count) return;
+  const DgSeg seg = sg.s[si];
+  const int G = sh.hq / sh.hkv;
+  const int nq = G * seg.n;
+  const int qr0 = qb * ATTN_QROWS + wave * 32;
+  if (qb * ATTN_QROWS >= nq) return;  // uniform over the block
+
+  // This lane's two query rows (one per 16-wide query tile).
+  int qrow[2], qhead[2], trow[2], qpos[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qr = qr0 + qt * 16 + c16;
+    qvalid[qt] = qr < nq;
+    const int qrc = qvalid[qt] ? qr : nq - 1;
+    const int hg = qrc / seg.n, i = qrc - hg * seg.n;
+    qrow[qt] = qrc;
+    qhead[qt] = h * G + hg;
+    trow[qt] = seg.row0 + i;
+    qpos[qt] = seg.pos0 + i;
+  }
+  // Key range of this split; causal rows see keys <= their own position.
+  const int nkeys = seg.nkeys;
+  const int chunk = ((nkeys + nsplit - 1) / nsplit + 31) / 32 * 32;
+  const int k_lo = split * chunk;
+  int k_hi = min(nkeys, k_lo + chunk);
+  if (sg.causal) {
+    int mp = max(qvalid[0] ? qpos[0] : -1, qvalid[1] ? qpos[1] : -1);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mp = max(mp, __shfl_xor(mp, o, 64));
+    k_hi = min(k_hi, mp + 1);
+  }
+
+  F qf[2][NKK];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const char* qp = (const char*)(q + (size_t)trow[qt] * (sh.hq * HD) + qhead[qt] * HD) + g4 * 16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[qt][kk] = load_frag<F>(qp + kk * 64);
+  }
+
+  const T* kbase = (const T*)seg.k + (size_t)h * sh.max_ctx * HD;
+  const T* vbase = (const T*)seg.vt + (size_t)h * HD * sh.max_ctx;
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
+
+  v4f oacc[NHT][2];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) oacc[ht][0] = oacc[ht][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+  for (int kb = k_lo; kb < k_hi; kb += 32) {
+    v4f st[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      st[kt][0] = st[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+      const int key = min(kb + kt * 16 + c16, nkeys - 1);
+      const char* kp = (const char*)(kbase + (size_t)key * HD) + g4 * 16;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const F kf = load_frag<F>(kp + kk * 64);
+        MF<T>::mma(st[kt][0], kf, qf[0][kk]);
+        MF<T>::mma(st[kt][1], kf, qf[1][kk]);
+      }
+    }
+    // Scale, mask, online softmax per query column.
+    float p[2][2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + kt * 16 + g4 * 4 + i;
+          float s = st[kt][qt][i] * scale;
+          if (key >= k_hi || (sg.causal && key > qpos[qt])) s = -INFINITY;
+          p[kt][qt][i] = s;
+          tmax = fmaxf(tmax, s);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun[qt], tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun[qt] - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = (mnew == -INFINITY) ? 0.f : exp2f(p[kt][qt][i] - mnew);
+          p[kt][qt][i] = e;
+          psum += e;
+        }
+      lrun[qt] = lrun[qt] * alpha + psum;
+      mrun[qt] = mnew;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] *= alpha;
+    }
+    // O^T += V^T P^T over the 32 keys of this tile.
+    if constexpr (sizeof(T) == 2) {
+      F pf[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pf[qt][i] = (short)f2bf(p[0][qt][i]);
+          pf[qt][4 + i] = (short)f2bf(p[1][qt][i]);
+        }
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const T* vr = vbase + (size_t)(ht * 16 + c16) * sh.max_ctx + kb + g4 * 4;
+        const uint2 lo = *(const uint2*)vr;
+        const uint2 hi = *(const uint2*)(vr + 16);
+        F vf;
+        vf[0] = (short)(lo.x & 0xffff); vf[1] = (short)(lo.x >> 16);
+        vf[2] = (short)(lo.y & 0xffff); vf[3] = (short)(lo.y >> 16);
+        vf[4] = (short)(hi.x & 0xffff); vf[5] = (short)(hi.x >> 16);
+        vf[6] = (short)(hi.y & 0xffff); vf[7] = (short)(hi.y >> 16);
+        MF<T>::mma(oacc[ht][0], vf, pf[0]);
+        MF<T>::mma(oacc[ht][1], vf, pf[1]);
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        F pf0 = {p[kt][0][0], p[kt][0][1], p[kt][0][2], p[kt][0][3]};
+        F pf1 = {p[kt][1][0], p[kt][1][1], p[kt][1][2], p[kt][1][3]};
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          const T* vr = vbase + (size_t)(ht * 16 + c16) * sh.max_ctx + kb + kt * 16 + g4 * 4;
+          const F vf = *(const F*)vr;
+          MF<T>::mma(oacc[ht][0], vf, pf0);
+          MF<T>::mma(oacc[ht][1], vf, pf1);
+        }
+      }
+    }
+  }
+  // Row sums across the four lane groups, then the partial results of this split.
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
+    lrun[qt] += __shfl_xor(lrun[qt], 32, 64);
+    if (!qvalid[qt]) continue;
+    const size_t qi = (size_t)trow[qt] * sh.hq + qhead[qt];
+    float* op = opart + ((size_t)split * rows_total * sh.hq + qi) * HD;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) *(v4f*)(op + ht * 16 + g4 * 4) = oacc[ht][qt];
+    if (g4 == 0) {
+      float* ml = mlpart + ((size_t)split * rows_total * sh.hq + qi) * 2;
+      ml[0] = mrun[qt];
+      ml[1] = lrun[qt];
+    }
+  }
+}
+
+// Merge the splits of each (row, q-head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+template <typename T>
+__global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opart, const float* __restrict__ mlpart,
+                                                   int nsplit, int rows_total, int hq, int hd, T* __restrict__ o) {
+  const size_t qi = blockIdx.x;  // row * hq + qhead
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mlpart[((size_t)s * rows_total * hq + qi) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* ml = mlpart + ((size_t)s * rows_total * hq + qi) * 2;
+    if (ml[1] > 0.f) L += exp2f(ml[0] - M) * ml[1];
+  }
+  const float invL = 1.f / L;
+  for (int c = threadIdx.x; c < hd; c += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float* ml = mlpart + ((size_t)s * rows_total * hq + qi) * 2;
+      if (ml[1] > 0.f) acc += exp2f(ml[0] - M) * opart[((size_t)s * rows_total * hq + qi) * hd + c];
+    }
+    o[qi * hd + c] = from_f<T>(acc * invL);
+  }
+}
+
+int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits) {
+  int base = 0, maxkeys = 0;
+  const int G = sh.hq / sh.hkv;
+  for (int i = 0; i < segs.count; ++i) {
+    base += sh.hkv * ((G * segs.s[i].n + ATTN_QROWS - 1) / ATTN_QROWS);
+    maxkeys = maxkeys > segs.s[i].nkeys ? maxkeys : segs.s[i].nkeys;
+  }
+  int ns = (512 + base - 1) / (base > 0 ? base : 1);
+  const int by_keys = (maxkeys + 127) / 128;
+  if (ns > by_keys) ns = by_keys;
+  if (ns > max_splits) ns = max_splits;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSegs& segs, int nsplit, float* opart,
+                         float* mlpart, void* o, int rows, hipStream_t s) {
+  if (rows <= 0) return;
+  const int G = sh.hq / sh.hkv;
+  int nmax = 0;
+  for (int i = 0; i < segs.count; ++i) nmax = nmax > segs.s[i].n ? nmax : segs.s[i].n;
+  const int nqb = (G * nmax + ATTN_QROWS - 1) / ATTN_QROWS;
+  const int blocks = segs.count * sh.hkv * nqb * nsplit;
+#define DG_ATTN(TT, HDV)                                                                                     \
+  k_attn<TT, HDV><<<blocks, 256, 0, s>>>((const TT*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);         \
+  k_attn_merge<TT><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (TT*)o)
+  if (dtype == 1) {
+    if (sh.hd == 256) { DG_ATTN(bf16_t, 256); }
+    else if (sh.hd == 128) { DG_ATTN(bf16_t, 128); }
+    else if (sh.hd == 64) { DG_ATTN(bf16_t, 64); }
+    else { DG_ATTN(bf16_t, 32); }
+  } else {
+    if (sh.hd == 256) { DG_ATTN(float, 256); }
+    else if (sh.hd == 128) { DG_ATTN(float, 128); }
+    else if (sh.hd == 64) { DG_ATTN(float, 64); }
+    else if (sh.hd == 32) { DG_ATTN(float, 32); }
+    else { DG_ATTN(float, 16); }
+  }
+#undef DG_ATTN
+}

@@ -88,6 +88,11 @@ def prefill(st: RequestState, prompt, cfg: ModelConfig, w: Weights, prec: Precis
     n = prompt.shape[0]
     if n > st.max_ctx:
         raise ValueError("prompt longer than max_ctx")
+    st.P = n
+    st.block = 0
+    st.active = False
+    if n == 0:
+        return np.zeros((0, cfg.d_model))
     x = w.embed[prompt]
     pos = np.arange(n)
     mask = np.tril(np.ones((n, n), dtype=bool))
@@ -97,9 +102,6 @@ def prefill(st: RequestState, prompt, cfg: ModelConfig, w: Weights, prec: Precis
                               skip_ffn=(l == cfg.n_layers - 1))
         st.cache_k[l][:n] = tr.k
         st.cache_v[l][:n] = tr.v
-    st.P = n
-    st.block = 0
-    st.active = False
     return x
 
 
