@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Denoising-step benchmark: output tok/s at batch 1 and ms per 256-token step.
+
+Workload (default "full"): a 30-layer, 25.2B-parameter (3.8B active) bf16 MoE
+decoder with the shape the pages give for DiffusionGemma 26B A4B (128 experts,
+8 routed + 1 shared, bidirectional attention over 256-token canvases; "DiffusionGemma
+hits ~1,500 TPS on one H100", section "The specs that matter for serving").
+Weights are random N(0, 0.02), and the prompt is 4096 uniform random ids.
+1024 output tokens are produced as 4 canvases of 256.  The timed region is
+`--steps` denoising steps (1024 by default = the whole 4096-in / 1024-out
+generation) together with every block commit that falls inside it.  Weights
+and the prompt's KV cache are resident in HBM before timing starts.
+
+The JSON line carries:
+  value        output tokens / timed seconds (tokens accepted by the sampler);
+  ms_per_step  timed ms / steps;
+  roofline     the dominant kernel (routed-expert W1/W3 projection) measured
+               with HIP events on the library's stream: algorithmic bytes per
+               launch / mean launch time against 8 TB/s;
+  step_roofline  the whole step: algorithmic bytes and FLOPs per step against
+               max(bytes / 8 TB/s, FLOPs / 2.5 PFLOP/s);
+  cpu_baseline the CPU oracle on a bounded sample (one layer + LM head),
+               scaled to a whole step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+MFMA_F32_TFLOPS = 157.3
+
+# Routed-expert W1/W3 kernel: the largest single kernel of the step (2/3 of the
+# routed expert bytes, which are ~89% of the step's bytes at the full shape).
+DOMINANT = "expert_up"
+
+
+def esize(w):
+    return 2 if w.dtype == "bf16" else 4
+
+
+def expert_up_bytes(w, touched, rows):
+    """Algorithmic HBM bytes of one routed W1/W3 launch: the touched experts' W1 and
+    W3 once, the normalised rows once, the SwiGLU output once."""
+    es = esize(w)
+    return (touched * 2 * w.expert_hidden * w.d_model * es + rows * w.d_model * es
+            + rows * w.top_k * w.expert_hidden * es)
+
+
+def step_bytes(w, P, rows, touched_per_layer):
+    """Algorithmic HBM bytes of one denoising step over `rows` canvas rows whose
+    request has committed length P: every weight the step needs once (routed
+    experts: only those touched), the KV prefix once, the canvas K/V written once."""
+    es = esize(w)
+    d, hd = w.d_model, w.head_dim
+    dense = ((w.n_q_heads + 2 * w.n_kv_heads) * hd * d + w.n_q_heads * hd * d + w.n_experts * d
+             + 3 * d * w.shared_hidden)
+    total = 0
+    for t in touched_per_layer:
+        total += (dense + t * 3 * d * w.expert_hidden) * es
+    kv = w.n_layers * 2 * w.n_kv_heads * hd * es
+    total += P * kv + rows * kv          # prefix read + canvas K/V write
+    total += w.vocab * d * es            # LM head
+    return total
+
+
+def step_flops(w, P, rows, n_open):
+    d, hd = w.d_model, w.head_dim
+    per_tok = ((w.n_q_heads + 2 * w.n_kv_heads) * hd * d + w.n_q_heads * hd * d + w.n_experts * d
+               + 3 * d * w.shared_hidden + w.top_k * 3 * d * w.expert_hidden)
+    f = 2 * rows * w.n_layers * per_tok
+    f += 4 * w.n_layers * w.n_q_heads * hd * rows * (P + rows)
+    f += 2 * n_open * d * w.vocab
+    return f
+
+
+def cpu_baseline(w, tokens_per_step):
+    """Time the CPU oracle on a bounded sample of one denoising step of the same
+    workload: layer 0 at its real shapes (256 canvas rows over a prompt-length KV
+    prefix) and the LM head over 128 rows (the mean number of open rows of a
+    block), scaled to n_layers layers."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    from block_diffusion_decoding_dg_amd import synth
+
+    tw = synth.make_weights(w, seed=0, device="cpu", layers=[0])
+
+    def f64(t):
+        return t.float().numpy().astype(np.float64)
+
+    cfg = oracle.ModelConfig(**w.model_dict())
+    lw = oracle.LayerWeights(**{k: f64(v) for k, v in tw["layers"][0].items()})
+    embed = f64(tw["embed"])
+    fnorm = f64(tw["final_norm"])
+    del tw
+    prec = oracle.Precision(bf16_points=(w.dtype == "bf16"))
+    C = w.canvas_len
+    P = w.prompt_len
+    rng = np.random.default_rng(1)
+    kpre = rng.standard_normal((P, w.n_kv_heads, w.head_dim))
+    vpre = rng.standard_normal((P, w.n_kv_heads, w.head_dim))
+    ids = rng.integers(0, w.vocab, C)
+    x = embed[ids]
+    pos = P + np.arange(C)
+    n_open = C // 2
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    t0 = time.perf_counter()
+    h, _ = oracle.layer_forward(x, pos, lw, cfg, prec, kpre, vpre)
+    t1 = time.perf_counter()
+    oracle.lm_head_stats(h[:n_open], embed, fnorm, cfg, prec)
+    t2 = time.perf_counter()
+    step_s = w.n_layers * (t1 - t0) + (t2 - t1)
+    return {"value": tokens_per_step / step_s, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": ("float64 numpy oracle, one layer (256 canvas rows over a %d-row KV prefix) timed at "
+                       "%.2f s and the LM head over %d rows at %.2f s, scaled to %d layers: %.1f s per step, "
+                       "at the GPU's %.2f tokens per step" % (P, t1 - t0, n_open, t2 - t1, w.n_layers, step_s,
+                                                              tokens_per_step)),
+            "ms_per_step": step_s * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", default=DOMINANT, help="kernel family timed with HIP events")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no sharding, no collectives); --gpus %d is not "
+              "supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from block_diffusion_decoding_dg_amd import dg, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    C = w.canvas_len
+    R = w.n_requests
+    K, W = args.steps, args.warmup
+    n_blocks = max(1, -(-K // C))
+    max_ctx = w.prompt_len + n_blocks * C
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    log("bench: generating %s weights on the GPU" % w.name)
+    tw = synth.make_weights(w, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    cfg = dg.model_config(w, max_ctx=max_ctx)
+    dec = dg.Decoder(cfg, w.tau, w.max_steps, tw)
+    prompts = [synth.make_prompt(w, seed=args.seed + r) for r in range(R)]
+    seeds = [args.seed + r for r in range(R)]
+
+    def prefill_all():
+        t0 = time.perf_counter()
+        for r in range(R):
+            dec.dg_prefill(r, prompts[r], seeds[r])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    log("bench: prefill %d x %d tokens" % (R, w.prompt_len))
+    prefill_ms = prefill_all()
+    log("bench: prefill %.1f ms; warmup %d steps" % (prefill_ms, W))
+    for _ in range(W):
+        dec.dg_denoise_step()
+    prefill_ms = prefill_all()  # reset to block 0, step 0
+
+    dec.dg_kernel_timer(args.kernel)
+    torch.cuda.synchronize()
+    log("bench: timing %d steps" % K)
+    trace = []  # (P, open rows before the step) per request per step
+    tokens = 0
+    commits = 0
+    t0 = time.perf_counter()
+    for i in range(K):
+        infos = dec.dg_denoise_step()
+        for r in range(R):
+            inf = infos[r]
+            if not inf["active"]:
+                continue
+            tokens += inf["n_accepted"] + inf["n_forced"]
+            trace.append((inf["block"], inf["step"], inf["n_accepted"] + inf["n_forced"]))
+        if all(infos[r]["done"] or not infos[r]["active"] for r in range(R)):
+            for r in range(R):
+                if infos[r]["active"] and infos[r]["done"]:
+                    dec.dg_commit_block(r)
+                    commits += 1
+        if (i + 1) % 128 == 0:
+            log("bench: %d steps, %.1f s" % (i + 1, time.perf_counter() - t0))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt_ms, kt_n = dec.dg_kernel_timer_read()
+    elapsed = t1 - t0
+
+    # touched experts per layer of the last step (random-init routers touch all of them)
+    rows_info = dec.dg_last_step_rows()
+    rids = rows_info["router_ids"]
+    touched = [int(np.unique(rids[l]).size) for l in range(w.n_layers)]
+    dec.close()
+
+    # Algorithmic bytes and FLOPs of every timed step, from its block and its open rows.
+    tot_bytes = 0
+    tot_flops = 0
+    for blk, step, _ in trace:
+        P = w.prompt_len + blk * C
+        n_open = C - (step - 1)  # one acceptance per step before this one (checked below)
+        tot_bytes += step_bytes(w, P, C, touched)
+        tot_flops += step_flops(w, P, C, n_open)
+    mean_bytes = tot_bytes / max(1, len(trace)) * R
+    mean_flops = tot_flops / max(1, len(trace)) * R
+    ms_per_step = elapsed * 1e3 / K
+    roof_ms = max(mean_bytes / (HBM_PEAK_GBS * 1e9), mean_flops / (MFMA_BF16_TFLOPS * 1e12)) * 1e3
+    tok_per_step = tokens / K
+
+    launch_ms = kt_ms / max(1, kt_n)
+    rows_step = R * C
+    bpl = expert_up_bytes(w, sum(touched) / len(touched), rows_step)
+    achieved = bpl / (launch_ms * 1e-3) / 1e9 if kt_n else None
+
+    out = {
+        "metric": "output tok/s at bs=1, 4096-in/1024-out; ms per 256-token denoise step",
+        "value": tokens / elapsed,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: random N(0,0.02) weights, uniform random prompt ids",
+        "config": {"workload": "%s: vocab %d, d_model %d, %d layers, %d/%d heads x %d, %d experts top-%d + 1 "
+                               "shared, expert hidden %d, shared hidden %d; %d requests x %d-token prompt, "
+                               "%d timed steps (%d canvases of %d)" % (
+                                   w.name, w.vocab, w.d_model, w.n_layers, w.n_q_heads, w.n_kv_heads,
+                                   w.head_dim, w.n_experts, w.top_k, w.expert_hidden, w.shared_hidden, R,
+                                   w.prompt_len, K, n_blocks, C),
+                   "global_batch": R, "seq_len": w.prompt_len, "parallelism": "none"},
+        "tokens_per_step": tok_per_step,
+        "commits": commits,
+        "prefill_ms": prefill_ms,
+        "roofline": {"bound": "hbm", "kernel": args.kernel,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+                     "launch_ms": launch_ms, "launches": kt_n, "bytes_per_launch": bpl},
+        "step_roofline": {"bytes_per_step": mean_bytes, "flops_per_step": mean_flops,
+                          "roofline_ms": roof_ms, "frac": roof_ms / ms_per_step,
+                          "touched_experts_per_layer": sum(touched) / len(touched)},
+    }
+    if args.kernel != DOMINANT:
+        out["roofline"]["achieved"] = None
+        out["roofline"]["frac"] = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        del tw
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, tok_per_step)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -100,6 +100,13 @@ struct dg_ctx {
 
   int32_t* info_host = nullptr;  // pinned [max_requests][4]
 
+  // Kernel timer: HIP event pairs around every launch of one kernel family.
+  int kt_family = 0;
+  std::vector<hipEvent_t> kt_ev;  // 2 per recorded launch
+  size_t kt_used = 0;
+  double kt_ms = 0.0;
+  int64_t kt_launches = 0;
+
   std::vector<Request> req;
   std::vector<int> last_slots;  // request of each slot in the last step
   int last_rows = 0;
@@ -129,6 +136,39 @@ dg_status fail(dg_ctx* c, dg_status st, const char* fmt, ...) {
   do {                                                                                                 \
     hipError_t e_ = hipGetLastError();                                                                 \
     if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+// Kernel timer.  kt_begin/kt_end bracket one launch of family f; the events are
+// read back (and the pairs reused) by kt_collect after the stream has synchronised.
+void kt_begin(dg_ctx* c, int f) {
+  if (c->kt_family != f) return;
+  while (c->kt_ev.size() < c->kt_used + 2) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) { c->kt_family = 0; return; }
+    c->kt_ev.push_back(e);
+  }
+  hipEventRecord(c->kt_ev[c->kt_used], c->stream);
+}
+void kt_end(dg_ctx* c, int f) {
+  if (c->kt_family != f) return;
+  hipEventRecord(c->kt_ev[c->kt_used + 1], c->stream);
+  c->kt_used += 2;
+}
+void kt_collect(dg_ctx* c) {
+  for (size_t i = 0; i + 1 < c->kt_used; i += 2) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->kt_ev[i], c->kt_ev[i + 1]) == hipSuccess) {
+      c->kt_ms += ms;
+      c->kt_launches += 1;
+    }
+  }
+  c->kt_used = 0;
+}
+#define KT(c, fam, launch) \
+  do {                     \
+    kt_begin((c), (fam));  \
+    launch;                \
+    kt_end((c), (fam));    \
   } while (0)
 
 int kc_of(int dtype) { return dtype == DG_BF16 ? 32 : 16; }
@@ -264,12 +304,12 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
   hipStream_t s = c->stream;
   const DgShape sh = shape_of(c);
   const DgSegs sg = make_segs(c, slots, l, causal);
-  dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, s);
-  dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, s);
+  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, s));
+  KT(c, DG_KF_QKV, dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, s));
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
   const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
-  dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s);
-  dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x, m.d_model, s);
+  KT(c, DG_KF_ATTENTION, dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s));
+  KT(c, DG_KF_OUT_PROJ, dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x, m.d_model, s));
 }
 
 // FFN half of layer l over `rows` rows in c->x; routing written to ids/gates.
@@ -277,17 +317,17 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates) {
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
-  dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, s);
-  dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, c->rlogits, m.n_experts, s);
-  dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s);
-  dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s);
-  dg_launch_expert_up(c->dtype, c->xn, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w1, w.w3,
-                      c->counts, c->offsets, c->perm, c->hbuf, s);
-  dg_launch_expert_down(c->dtype, c->hbuf, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w2, c->counts,
-                        c->offsets, c->perm, c->ybuf, s);
-  dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s);
-  dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s);
-  dg_launch_combine(c->x, c->ybuf, gates, rows, m.d_model, m.top_k, s);
+  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, s));
+  KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, c->rlogits, m.n_experts, s);
+                          dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s));
+  KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s));
+  KT(c, DG_KF_EXPERT_UP, dg_launch_expert_up(c->dtype, c->xn, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w1, w.w3,
+                      c->counts, c->offsets, c->perm, c->hbuf, s));
+  KT(c, DG_KF_EXPERT_DOWN, dg_launch_expert_down(c->dtype, c->hbuf, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w2, c->counts,
+                        c->offsets, c->perm, c->ybuf, s));
+  KT(c, DG_KF_SHARED_UP, dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s));
+  KT(c, DG_KF_SHARED_DOWN, dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s));
+  KT(c, DG_KF_COMBINE, dg_launch_combine(c->x, c->ybuf, gates, rows, m.d_model, m.top_k, s));
 }
 
 // Forward of the rows in c->x through all layers.  kv_only: the last layer only
@@ -300,8 +340,8 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
       const DgShape sh = shape_of(c);
       const DgSegs sg = make_segs(c, slots, l, causal);
       const dg_layer_weights& w = c->layers[l];
-      dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, c->stream);
-      dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, c->stream);
+      KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, c->stream));
+      KT(c, DG_KF_QKV, dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, c->stream));
       break;
     }
     attn_half(c, l, slots, rows, causal);
@@ -341,6 +381,7 @@ dg_status check_req(dg_ctx* c, int32_t req) {
 double now_ms() {
   return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now().time_since_epoch()).count();
 }
+
 
 }  // namespace
 
@@ -422,6 +463,7 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
 void dg_destroy(dg_ctx* ctx) {
   if (!ctx) return;
   hipStreamSynchronize(ctx->stream);
+  for (hipEvent_t e : ctx->kt_ev) hipEventDestroy(e);
   if (ctx->info_host) hipHostFree(ctx->info_host);
   delete ctx;
 }
@@ -485,16 +527,17 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
   std::vector<SlotRow> slots;
   for (int r : slot_req) slots.push_back({r, c->req[r].P, c->C});
   dg_launch_open_rows(a, c->open_rows, c->n_open_rows, s);
-  dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s);
+  KT(c, DG_KF_EMBED, dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s));
   forward_layers(c, slots, rows, false, false, true);
-  dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
-                    c->cfg.rms_eps, c->hn, s);
-  dg_launch_lm_head(c->dtype, c->hn, c->n_open_rows, rows, c->cfg.d_model, c->embed, c->cfg.vocab, c->lpart,
-                    c->lpart_arg, c->ent, c->lse, c->amax, c->open_rows, s);
-  dg_launch_sample(a, c->ent, c->amax, c->info_dev, nullptr, nullptr, s);
+  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
+                                         c->cfg.rms_eps, c->hn, s));
+  KT(c, DG_KF_LM_HEAD, dg_launch_lm_head(c->dtype, c->hn, c->n_open_rows, rows, c->cfg.d_model, c->embed, c->cfg.vocab, c->lpart,
+                                         c->lpart_arg, c->ent, c->lse, c->amax, c->open_rows, s));
+  KT(c, DG_KF_SAMPLE, dg_launch_sample(a, c->ent, c->amax, c->info_dev, nullptr, nullptr, s));
   LAUNCHCK(c);
   HIPCK(c, hipMemcpyAsync(c->info_host, c->info_dev, a.count * 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
   HIPCK(c, hipStreamSynchronize(s));
+  kt_collect(c);
   for (size_t i = 0; i < slot_req.size(); ++i) {
     const int r = slot_req[i];
     Request& q = c->req[r];
@@ -523,6 +566,7 @@ dg_status dg_commit_block(dg_ctx* c, int32_t req, int32_t* out_ids) {
   if (out_ids)
     HIPCK(c, hipMemcpyAsync(out_ids, c->canvas_ids + (size_t)req * c->C, c->C * 4, hipMemcpyDeviceToHost, s));
   HIPCK(c, hipStreamSynchronize(s));
+  kt_collect(c);
   q.P += c->C;
   q.block += 1;
   q.step = 0;
@@ -754,6 +798,26 @@ dg_status dg_philox_tokens(uint64_t seed, int32_t block, int32_t step, int32_t n
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(nullptr, DG_ERR_HIP, "philox: %s", hipGetErrorString(e));
+  return DG_OK;
+}
+
+dg_status dg_kernel_timer(dg_ctx* c, int32_t family) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (family < 0 || family >= DG_KF_COUNT) return fail(c, DG_ERR_INVALID_ARG, "unknown kernel family %d", family);
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  kt_collect(c);
+  c->kt_family = family;
+  c->kt_ms = 0.0;
+  c->kt_launches = 0;
+  return DG_OK;
+}
+
+dg_status dg_kernel_timer_read(dg_ctx* c, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return fail(c, DG_ERR_INVALID_ARG, "null argument");
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  kt_collect(c);
+  *total_ms = c->kt_ms;
+  *launches = c->kt_launches;
   return DG_OK;
 }
 

@@ -18,7 +18,11 @@ DG_F32, DG_BF16 = 0, 1
 EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "dg_commit_block", "dg_generate",
            "dg_destroy", "dg_last_error", "dg_get_request", "dg_get_canvas", "dg_set_canvas", "dg_set_committed",
            "dg_last_step_rows", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
-           "dg_op_sample", "dg_philox_tokens")
+           "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read")
+
+KERNEL_FAMILIES = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "out_proj": 5, "router": 6, "permute": 7,
+                   "expert_up": 8, "expert_down": 9, "shared_up": 10, "shared_down": 11, "combine": 12,
+                   "lm_head": 13, "sample": 14}
 
 
 class DgError(RuntimeError):
@@ -99,6 +103,8 @@ def load():
         "dg_op_lm_head": [P, P, I32, P, P, P],
         "dg_op_sample": [P, I32, P, P, I32, ctypes.POINTER(StepInfo)],
         "dg_philox_tokens": [U64, I32, I32, I32, I32, P, P],
+        "dg_kernel_timer": [P, I32],
+        "dg_kernel_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -286,6 +292,16 @@ class Decoder:
         info = StepInfo()
         self._check(self.lib.dg_op_sample(self.ctx, req, _ptr(entropy), _ptr(argmax), step, ctypes.byref(info)))
         return info.as_dict()
+
+    # --- kernel timer ----------------------------------------------------------
+    def dg_kernel_timer(self, family):
+        f = KERNEL_FAMILIES[family] if isinstance(family, str) else int(family)
+        self._check(self.lib.dg_kernel_timer(self.ctx, f))
+
+    def dg_kernel_timer_read(self):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        self._check(self.lib.dg_kernel_timer_read(self.ctx, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     def kv_views(self, req, layer):
         """(K [Hkv][max_ctx][hd], Vt [Hkv][hd][max_ctx]) views of the caller-owned cache."""

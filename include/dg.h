@@ -325,6 +325,44 @@ dg_status dg_op_sample(dg_ctx* ctx, int32_t req, const float* entropy_dev,
 dg_status dg_philox_tokens(uint64_t seed, int32_t block, int32_t step, int32_t n, int32_t vocab,
                            int32_t* out_dev, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Kernel timer, for measurement.                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Kernel families of a denoising step.  The timer brackets every launch of one
+ * family with a pair of HIP events on the context's stream; a family made of
+ * two launches (the LM head and its tile merge, attention and its split merge,
+ * router logits and top-k) is timed as one unit.
+ */
+typedef enum dg_kernel_family {
+  DG_KF_NONE = 0,
+  DG_KF_EMBED = 1,
+  DG_KF_RMSNORM = 2,
+  DG_KF_QKV = 3,          /* q/k/v projection + RoPE + K/V cache write */
+  DG_KF_ATTENTION = 4,    /* split-KV attention + merge */
+  DG_KF_OUT_PROJ = 5,     /* output projection + residual */
+  DG_KF_ROUTER = 6,       /* router logits + top-k gates */
+  DG_KF_PERMUTE = 7,      /* expert histogram, offsets, token permutation */
+  DG_KF_EXPERT_UP = 8,    /* routed experts, W1/W3 with SwiGLU */
+  DG_KF_EXPERT_DOWN = 9,  /* routed experts, W2 */
+  DG_KF_SHARED_UP = 10,   /* shared expert, W1/W3 with SwiGLU */
+  DG_KF_SHARED_DOWN = 11, /* shared expert, W2 + residual */
+  DG_KF_COMBINE = 12,     /* gate-weighted sum of the routed outputs + residual */
+  DG_KF_LM_HEAD = 13,     /* fused LM head + softmax statistics + tile merge */
+  DG_KF_SAMPLE = 14,      /* entropy-bound sampler */
+  DG_KF_COUNT = 15
+} dg_kernel_family;
+
+/* Start timing `family` (DG_KF_NONE stops) on every later denoising step and
+ * block commit; resets the totals.  Synchronizes the stream.
+ * Errors: DG_ERR_INVALID_ARG for an unknown family. */
+dg_status dg_kernel_timer(dg_ctx* ctx, int32_t family);
+
+/* Total GPU time (ms, from the event pairs) and number of timed launches since
+ * dg_kernel_timer.  Synchronizes the stream. */
+dg_status dg_kernel_timer_read(dg_ctx* ctx, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

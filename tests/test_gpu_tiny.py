@@ -177,6 +177,7 @@ def test_tiny_lm_head_crafted_rows(setup):
     toks[:8] = 17
     toks[8:16] = 5
     mix = rng.uniform(0.0, 1.0, n) ** 2
+    mix[:16] = 0.0  # the tie rows point exactly along E[17] / E[5]
     e = owc.embed[toks]
     e = e / np.linalg.norm(e, axis=1, keepdims=True)
     u = rng.standard_normal((n, ocfg.d_model))
