@@ -90,10 +90,14 @@ def cpu_baseline(w, tokens_per_step):
     import oracle
     from block_diffusion_decoding_dg_amd import synth
 
-    tw = synth.make_weights(w, seed=0, device="cpu", layers=[0])
+    import torch
+    # The seeded generator runs on the GPU when there is one (much faster than
+    # torch's CPU generator); the values are copied to host memory for the oracle.
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    tw = synth.make_weights(w, seed=0, device=dev, layers=[0])
 
     def f64(t):
-        return t.float().numpy().astype(np.float64)
+        return t.float().cpu().numpy().astype(np.float64)
 
     cfg = oracle.ModelConfig(**w.model_dict())
     lw = oracle.LayerWeights(**{k: f64(v) for k, v in tw["layers"][0].items()})

@@ -83,3 +83,43 @@ void dg_launch_open_rows(const DgSampleArgs& a, int32_t* open_rows, int32_t* n_o
 void dg_launch_philox_tokens(uint64_t seed, int block, int step, int n, int vocab, int32_t* out, hipStream_t s);
 // Gather rows by index list into a compact fp32 buffer (used by the logits tap).
 void dg_launch_gather_rows(const float* x, const int32_t* idx, int n, int d, float* out, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Weight-streaming GEMM (bf16 only): out = A W^T per group, 64 weight rows per
+// block and every activation row of the group (256 per pass over the weights).
+enum {
+  WS_EPI_STORE_BF16 = 0,  // out bf16 [rows][ldo]
+  WS_EPI_STORE_F32 = 1,   // out fp32 [rows][ldo]
+  WS_EPI_ADD_F32 = 2,     // out fp32 [rows][ldo] +=
+  WS_EPI_SWIGLU = 3,      // W0 = W1, W1 = W3; 32 hidden columns per block; out bf16 silu(x W1^T) * (x W3^T)
+  WS_EPI_ROPE_QKV = 4     // W0/W1/W2 = wq/wk/wv; RoPE on q and k; q to out, k and v to the cache of segs
+};
+
+struct WsArgs {
+  const void* A;          // activation rows, bf16, row stride lda elements
+  int lda;
+  const void* W0;         // weight matrices, row-major [rows][K]
+  const void* W1;
+  const void* W2;
+  size_t wgs;             // elements between the matrices of consecutive groups
+  int K;                  // reduction length, multiple of 64
+  int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it
+  int M;                  // rows of the single group when counts is null
+  const int32_t* counts;  // grouped: rows per group
+  const int32_t* offsets; // grouped: first position of each group in perm
+  const int32_t* perm;    // grouped: pair index of each row; activation row = pair / kdiv, output row = pair
+  int kdiv;
+  const int32_t* units;   // grouped: work list (group << 16 | n-block), length *n_units
+  const int32_t* n_units;
+  void* out;
+  int ldo;
+  // q/k/v epilogue
+  int hd, hq, hkv, max_ctx;
+  const double* inv_freq;
+  DgSegs segs;
+};
+
+void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);
+// Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b).
+void dg_launch_ws_units(const int32_t* counts, int E, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
+                        int32_t* units_b, int32_t* n_b, hipStream_t s);

@@ -78,6 +78,9 @@ struct dg_ctx {
   int32_t* counts = nullptr;
   int32_t* offsets = nullptr;
   int32_t* perm = nullptr;
+  int32_t* units_up = nullptr;   // routed work lists (group << 16 | n-block)
+  int32_t* units_dn = nullptr;
+  int32_t* n_units = nullptr;    // [2]: lengths of the two lists
   void* hbuf = nullptr;
   void* hs = nullptr;
   float* ybuf = nullptr;
@@ -187,7 +190,9 @@ const char* check_config(const dg_model_config* c) {
   const int kc = kc_of(c->dtype);
   const int hd = c->head_dim;
   if (!(hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256)) return "head_dim must be 16, 32, 64, 128 or 256";
-  if (c->dtype == DG_BF16 && hd < 32) return "bf16 head_dim must be >= 32";
+  if (c->dtype == DG_BF16 && hd < 64) return "bf16 head_dim must be >= 64";
+  if (c->dtype == DG_BF16 && ((c->n_q_heads * hd) % 64 || c->shared_hidden % 64))
+    return "bf16: n_q_heads * head_dim and shared_hidden must be multiples of 64";
   if (((c->n_q_heads + 2 * c->n_kv_heads) * hd / 2) % 16) return "(Hq + 2 Hkv) * head_dim / 2 must be a multiple of 16";
   if (c->d_model % 64 || c->d_model % kc) return "d_model must be a multiple of 64";
   if ((c->n_q_heads * hd) % kc) return "n_q_heads * head_dim must be a multiple of the k-chunk";
@@ -230,6 +235,9 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->counts = cv.take<int32_t>(E * 4);
   c->offsets = cv.take<int32_t>(E * 4);
   c->perm = cv.take<int32_t>(Tm * k * 4);
+  c->units_up = cv.take<int32_t>(E * ((m.expert_hidden + 31) / 32) * 4);
+  c->units_dn = cv.take<int32_t>(E * ((m.d_model + 63) / 64) * 4);
+  c->n_units = cv.take<int32_t>(2 * 4);
   c->hbuf = cv.take<void>(Tm * k * m.expert_hidden * es);
   c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
   c->ybuf = cv.take<float>(Tm * k * d * 4);
@@ -297,6 +305,76 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
   return sg;
 }
 
+// Launch helpers.  bf16 models run the weight-streaming kernel (k_ws.hip); the
+// fp32 model keeps the plain matrix-core kernels.
+void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W0, const void* W1, int N, void* out,
+                  int ldo) {
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = A;
+  a.lda = K;
+  a.W0 = W0;
+  a.W1 = W1;
+  a.K = K;
+  a.N = N;
+  a.M = M;
+  a.kdiv = 1;
+  a.out = out;
+  a.ldo = ldo;
+  const int grid = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
+  dg_launch_ws(epi, a, grid, c->stream);
+}
+
+void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, const void* W1, size_t wgs, int K, int N,
+                   int kdiv, const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo) {
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = A;
+  a.lda = lda;
+  a.W0 = W0;
+  a.W1 = W1;
+  a.wgs = wgs;
+  a.K = K;
+  a.N = N;
+  a.counts = c->counts;
+  a.offsets = c->offsets;
+  a.perm = c->perm;
+  a.kdiv = kdiv;
+  a.units = units;
+  a.n_units = n_units;
+  a.out = out;
+  a.ldo = ldo;
+  dg_launch_ws(epi, a, c->cfg.n_experts * nblk, c->stream);
+}
+
+void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg) {
+  const dg_model_config& m = c->cfg;
+  if (c->dtype == DG_F32) {
+    dg_launch_qkv(c->dtype, c->xn, rows, shape_of(c), w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, c->stream);
+    return;
+  }
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = c->xn;
+  a.lda = m.d_model;
+  a.W0 = w.wq;
+  a.W1 = w.wk;
+  a.W2 = w.wv;
+  a.K = m.d_model;
+  a.N = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim;
+  a.M = rows;
+  a.kdiv = 1;
+  a.out = c->q;
+  a.ldo = m.n_q_heads * m.head_dim;
+  a.hd = m.head_dim;
+  a.hq = m.n_q_heads;
+  a.hkv = m.n_kv_heads;
+  a.max_ctx = m.max_ctx;
+  a.inv_freq = c->inv_freq;
+  a.segs = sg;
+  dg_launch_ws(WS_EPI_ROPE_QKV, a, (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64, c->stream);
+}
+
 // Attention half of layer l over `rows` rows in c->x.
 void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal) {
   const dg_model_config& m = c->cfg;
@@ -305,11 +383,11 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
   const DgShape sh = shape_of(c);
   const DgSegs sg = make_segs(c, slots, l, causal);
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, s));
-  KT(c, DG_KF_QKV, dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, s));
+  KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
   const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
   KT(c, DG_KF_ATTENTION, dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s));
-  KT(c, DG_KF_OUT_PROJ, dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x, m.d_model, s));
+  KT(c, DG_KF_OUT_PROJ, launch_dense(c, WS_EPI_ADD_F32, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, nullptr, m.d_model, c->x, m.d_model));
 }
 
 // FFN half of layer l over `rows` rows in c->x; routing written to ids/gates.
@@ -318,15 +396,35 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates) {
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, s));
-  KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, c->rlogits, m.n_experts, s);
-                          dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s));
-  KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s));
-  KT(c, DG_KF_EXPERT_UP, dg_launch_expert_up(c->dtype, c->xn, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w1, w.w3,
-                      c->counts, c->offsets, c->perm, c->hbuf, s));
-  KT(c, DG_KF_EXPERT_DOWN, dg_launch_expert_down(c->dtype, c->hbuf, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w2, c->counts,
-                        c->offsets, c->perm, c->ybuf, s));
-  KT(c, DG_KF_SHARED_UP, dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s));
-  KT(c, DG_KF_SHARED_DOWN, dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s));
+  if (c->dtype == DG_F32) {
+    KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, c->rlogits, m.n_experts, s);
+                            dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s));
+    KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s));
+    KT(c, DG_KF_EXPERT_UP, dg_launch_expert_up(c->dtype, c->xn, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w1, w.w3,
+                                               c->counts, c->offsets, c->perm, c->hbuf, s));
+    KT(c, DG_KF_EXPERT_DOWN, dg_launch_expert_down(c->dtype, c->hbuf, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w2,
+                                                   c->counts, c->offsets, c->perm, c->ybuf, s));
+    KT(c, DG_KF_SHARED_UP, dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s));
+    KT(c, DG_KF_SHARED_DOWN, dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s));
+  } else {
+    KT(c, DG_KF_ROUTER, launch_dense(c, WS_EPI_STORE_F32, c->xn, rows, m.d_model, w.router, nullptr, m.n_experts, c->rlogits,
+                                     m.n_experts);
+                            dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s));
+    const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
+    KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s);
+                             dg_launch_ws_units(c->counts, m.n_experts, nb_up, c->units_up, c->n_units, nb_dn, c->units_dn,
+                                                c->n_units + 1, s));
+    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xn, m.d_model, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
+                                         m.d_model, m.expert_hidden, m.top_k, c->units_up, c->n_units, nb_up, c->hbuf,
+                                         m.expert_hidden));
+    KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, m.expert_hidden, w.w2, nullptr,
+                                           (size_t)m.d_model * m.expert_hidden, m.expert_hidden, m.d_model, 1, c->units_dn,
+                                           c->n_units + 1, nb_dn, c->ybuf, m.d_model));
+    KT(c, DG_KF_SHARED_UP, launch_dense(c, WS_EPI_SWIGLU, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs,
+                                        m.shared_hidden));
+    KT(c, DG_KF_SHARED_DOWN, launch_dense(c, WS_EPI_ADD_F32, c->hs, rows, m.shared_hidden, w.sw2, nullptr, m.d_model, c->x,
+                                          m.d_model));
+  }
   KT(c, DG_KF_COMBINE, dg_launch_combine(c->x, c->ybuf, gates, rows, m.d_model, m.top_k, s));
 }
 
@@ -341,7 +439,7 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
       const DgSegs sg = make_segs(c, slots, l, causal);
       const dg_layer_weights& w = c->layers[l];
       KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, c->stream));
-      KT(c, DG_KF_QKV, dg_launch_qkv(c->dtype, c->xn, rows, sh, w.wq, w.wk, w.wv, sg, c->inv_freq, c->q, c->stream));
+      KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
       break;
     }
     attn_half(c, l, slots, rows, causal);

@@ -134,15 +134,24 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] *= alpha;
     }
-    // O^T += V^T P^T over the 32 keys of this tile.
+    // O^T += V^T P^T over the 32 keys of this tile.  In bf16, P enters the matrix
+    // cores as a high and a low bf16 part (p = hi + lo to ~2^-16 relative), two
+    // products against the same V tile: a single bf16 P would carry a relative
+    // error of ~2^-9 into the output, which for nearly uniform weights averaging
+    // over many keys does not shrink.
     if constexpr (sizeof(T) == 2) {
-      F pf[2];
+      F pf[2], pl[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pf[qt][i] = (short)f2bf(p[0][qt][i]);
-          pf[qt][4 + i] = (short)f2bf(p[1][qt][i]);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const float v = p[kt][qt][i];
+            const bf16_t h = f2bf(v);
+            pf[qt][kt * 4 + i] = (short)h;
+            pl[qt][kt * 4 + i] = (short)f2bf(v - bf2f(h));
+          }
         }
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
@@ -156,6 +165,8 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
         vf[6] = (short)(hi.y & 0xffff); vf[7] = (short)(hi.y >> 16);
         MF<T>::mma(oacc[ht][0], vf, pf[0]);
         MF<T>::mma(oacc[ht][1], vf, pf[1]);
+        MF<T>::mma(oacc[ht][0], vf, pl[0]);
+        MF<T>::mma(oacc[ht][1], vf, pl[1]);
       }
     } else {
 #pragma unroll

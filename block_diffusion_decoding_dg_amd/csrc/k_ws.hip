@@ -1,0 +1,287 @@
+// Weight-streaming GEMM on the bf16 matrix cores, for the shapes of the denoising
+// step: a few hundred activation rows against large weight matrices, so that the
+// step's time is set by how fast the weights stream from HBM.  Used for the routed
+// experts (grouped by expert, rows gathered through the token permutation), the
+// shared expert and the dense projections.
+//
+// A block owns 64 consecutive weight rows ("n-block") of one group and every
+// activation row of that group, up to 256 per pass over the weights (a group with
+// more rows takes several passes).  Each weight byte therefore crosses HBM once
+// per 256 rows, whatever the routing.  The weight tile streams through a
+// two-stage LDS buffer in chunks of 64 reduction elements (128 bytes per row),
+// fed by a four-deep register prefetch ring (8 KB per chunk per block, one
+// 16-byte segment per thread, four chunks in flight); the eight waves split the
+// activation rows (m-tile i goes to wave i % 8) and read their own activation
+// fragments straight from global memory one chunk ahead.  The LDS rows are XOR-swizzled in 16-byte units so that
+// both the cooperative stores and the fragment reads are free of bank conflicts.
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16): lane l supplies activation row
+// l % 16 and weight row l % 16, each with reduction elements 8 (l / 16) .. +7 of a
+// 32-element step, and receives D[4 (l / 16) + i][l % 16], i = 0..3.
+#include "dg_common.h"
+#include "dg_kernels.h"
+
+#include <type_traits>
+
+namespace {
+
+constexpr int BN = 64;    // weight rows per block
+constexpr int BK = 64;    // reduction elements per chunk
+constexpr int NWAVE = 8;  // waves per block
+constexpr int NT = 64 * NWAVE;
+constexpr int MTW = 2;    // m-tiles per wave per pass
+constexpr int RING = 4;   // weight chunks in flight per thread
+constexpr int PASS_ROWS = NWAVE * MTW * 16;
+
+__device__ __forceinline__ int lds_slot(int row, int seg) { return row * 8 + (seg ^ (row & 7)); }
+
+// Weight row `r` (0..63) of n-block nb of group g, per epilogue.
+template <int EPI>
+__device__ __forceinline__ const bf16_t* weight_row(const WsArgs& a, int g, int nb, int r) {
+  if constexpr (EPI == WS_EPI_SWIGLU) {
+    // rows 0..31: W1 rows, rows 32..63: W3 rows, of the same 32 hidden columns
+    const bf16_t* W = (const bf16_t*)(r < 32 ? a.W0 : a.W1) + (size_t)g * a.wgs;
+    const int n = nb * 32 + (r & 31);
+    return W + (size_t)min(n, a.N - 1) * a.K;
+  } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
+    // rows 0..31: columns j0 .. j0+31 of one head's first half, rows 32..63: the
+    // matching columns of its second half (RoPE pairs j, j + hd/2)
+    const int half = a.hd / 2, per_head = half / 32;
+    const int head = nb / per_head, j = (nb - head * per_head) * 32 + (r & 31) + (r < 32 ? 0 : half);
+    const bf16_t* W;
+    int hl;
+    if (head < a.hq) { W = (const bf16_t*)a.W0; hl = head; }
+    else if (head < a.hq + a.hkv) { W = (const bf16_t*)a.W1; hl = head - a.hq; }
+    else { W = (const bf16_t*)a.W2; hl = head - a.hq - a.hkv; }
+    return W + (size_t)(hl * a.hd + j) * a.K;
+  } else {
+    const bf16_t* W = (const bf16_t*)a.W0 + (size_t)g * a.wgs;
+    const int n = nb * BN + r;
+    return W + (size_t)min(n, a.N - 1) * a.K;
+  }
+}
+
+__device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
+  int s = 0;
+  for (int i = 1; i < sg.count; ++i)
+    if (r >= sg.s[i].row0) s = i;
+  return s;
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
+  __shared__ uint4 sW[2][BN * 8];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int g = 0, nb = blockIdx.x;
+  if (a.units) {
+    if ((int)blockIdx.x >= *a.n_units) return;
+    const int code = a.units[blockIdx.x];
+    g = code >> 16;
+    nb = code & 0xffff;
+  }
+  const int cnt = a.counts ? a.counts[g] : a.M;
+  if (cnt <= 0) return;  // uniform over the block
+  const int off = a.counts ? a.offsets[g] : 0;
+  const int nk = a.K / BK;
+
+  // This thread's 16-byte segment of every weight chunk.
+  const int wr = tid >> 3, wc = tid & 7;
+  const char* gsrc = (const char*)weight_row<EPI>(a, g, nb, wr) + wc * 16;
+  const int slot = lds_slot(wr, wc);
+
+  const int npass = (cnt + PASS_ROWS - 1) / PASS_ROWS;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int pbase = pass * PASS_ROWS;
+    // Activation rows of this wave's m-tiles.
+    int mt_act = 0;
+    const char* ap[MTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const int t0 = pbase + (wave + NWAVE * j) * 16;
+      if (t0 < cnt) mt_act = j + 1;
+      const int r = min(t0 + (lane & 15), cnt - 1);
+      int arow;
+      if (a.counts) arow = a.perm[off + r] / a.kdiv;
+      else arow = r;
+      ap[j] = (const char*)((const bf16_t*)a.A + (size_t)arow * a.lda) + (lane >> 4) * 16;
+    }
+
+    v4f acc[MTW][4];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Register prefetch ring (four named registers: chunk c lives in ring slot c % 4)
+    // and double-buffered activation fragments (chunk c in afr[c % 2]).  Refills
+    // past the last chunk re-read the last chunk (a harmless cached load) so that
+    // every refill is unconditional.
+    uint4 r0, r1, r2, r3;
+    r0 = *(const uint4*)(gsrc + min(0, nk - 1) * 128);
+    r1 = *(const uint4*)(gsrc + min(1, nk - 1) * 128);
+    r2 = *(const uint4*)(gsrc + min(2, nk - 1) * 128);
+    r3 = *(const uint4*)(gsrc + min(3, nk - 1) * 128);
+    v8s af0[MTW][2], af1[MTW][2];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j)
+      if (j < mt_act) {
+        af0[j][0] = *(const v8s*)(ap[j]);
+        af0[j][1] = *(const v8s*)(ap[j] + 64);
+      }
+
+    auto chunk = [&](auto JR, uint4& R, int c) {
+      constexpr int jr = decltype(JR)::value;
+      constexpr int st = jr & 1;  // LDS stage == c & 1 (c0 is a multiple of 4)
+      v8s(&acur)[MTW][2] = (jr & 1) ? af1 : af0;
+      v8s(&anxt)[MTW][2] = (jr & 1) ? af0 : af1;
+      sW[st][slot] = R;
+      __syncthreads();
+      R = *(const uint4*)(gsrc + min(c + RING, nk - 1) * 128);
+      if (c + 1 < nk) {
+#pragma unroll
+        for (int j = 0; j < MTW; ++j)
+          if (j < mt_act) {
+            anxt[j][0] = *(const v8s*)(ap[j] + (c + 1) * 128);
+            anxt[j][1] = *(const v8s*)(ap[j] + (c + 1) * 128 + 64);
+          }
+      }
+      if (mt_act > 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          v8s wf[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const uint4 u = sW[st][lds_slot(n * 16 + (lane & 15), s * 4 + (lane >> 4))];
+            wf[n] = *reinterpret_cast<const v8s*>(&u);
+          }
+#pragma unroll
+          for (int j = 0; j < MTW; ++j)
+            if (j < mt_act) {
+#pragma unroll
+              for (int n = 0; n < 4; ++n)
+                acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[j][s], wf[n], acc[j][n], 0, 0, 0);
+            }
+        }
+      }
+    };
+    for (int c0 = 0; c0 < nk; c0 += RING) {
+      chunk(std::integral_constant<int, 0>{}, r0, c0);
+      if (c0 + 1 < nk) chunk(std::integral_constant<int, 1>{}, r1, c0 + 1);
+      if (c0 + 2 < nk) chunk(std::integral_constant<int, 2>{}, r2, c0 + 2);
+      if (c0 + 3 < nk) chunk(std::integral_constant<int, 3>{}, r3, c0 + 3);
+    }
+
+    // Epilogue.
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      if (j >= mt_act) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
+        if (r >= cnt) continue;
+        const int orow = a.counts ? a.perm[off + r] : r;
+        if constexpr (EPI == WS_EPI_SWIGLU) {
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const int col = nb * 32 + n * 16 + (lane & 15);
+            if (col < a.N)
+              ((bf16_t*)a.out)[(size_t)orow * a.ldo + col] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + 2][i]);
+          }
+        } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
+          const int half = a.hd / 2, per_head = half / 32;
+          const int head = nb / per_head;
+          const int si = seg_index(a.segs, r);
+          const int pos = a.segs.s[si].pos0 + (r - a.segs.s[si].row0);
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const int jj = (nb - head * per_head) * 32 + n * 16 + (lane & 15);
+            float x1 = acc[j][n][i], x2 = acc[j][n + 2][i];
+            if (head < a.hq + a.hkv) {
+              double ang = (double)pos * a.inv_freq[jj];
+              const double two_pi = 6.283185307179586476925286766559;
+              ang -= two_pi * rint(ang / two_pi);
+              float sn, cs;
+              sincosf((float)ang, &sn, &cs);
+              const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+              x1 = y1;
+              x2 = y2;
+            }
+            if (head < a.hq) {
+              bf16_t* q = (bf16_t*)a.out + (size_t)r * a.ldo + head * a.hd;
+              q[jj] = f2bf(x1);
+              q[jj + half] = f2bf(x2);
+            } else if (head < a.hq + a.hkv) {
+              const int hl = head - a.hq;
+              bf16_t* k = (bf16_t*)a.segs.s[si].k + ((size_t)hl * a.max_ctx + pos) * a.hd;
+              k[jj] = f2bf(x1);
+              k[jj + half] = f2bf(x2);
+            } else {
+              const int hl = head - a.hq - a.hkv;
+              bf16_t* vt = (bf16_t*)a.segs.s[si].vt + (size_t)hl * a.hd * a.max_ctx;
+              vt[(size_t)jj * a.max_ctx + pos] = f2bf(x1);
+              vt[(size_t)(jj + half) * a.max_ctx + pos] = f2bf(x2);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const int col = nb * BN + n * 16 + (lane & 15);
+            if (col >= a.N) continue;
+            const size_t o = (size_t)orow * a.ldo + col;
+            if constexpr (EPI == WS_EPI_STORE_BF16) ((bf16_t*)a.out)[o] = f2bf(acc[j][n][i]);
+            else if constexpr (EPI == WS_EPI_STORE_F32) ((float*)a.out)[o] = acc[j][n][i];
+            else ((float*)a.out)[o] += acc[j][n][i];
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next pass reuses the LDS stages
+  }
+}
+
+// Work list of the grouped launches: every (group, n-block) of the groups that
+// received rows, groups in increasing order.  One block; E <= 256.
+__global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ counts, int E, int nblk_a,
+                                                  int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
+                                                  int nblk_b, int32_t* __restrict__ units_b,
+                                                  int32_t* __restrict__ n_b) {
+  __shared__ int s_scan[256];
+  const int e = threadIdx.x;
+  const int touched = (e < E && counts[e] > 0) ? 1 : 0;
+  s_scan[e] = touched;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = e >= o ? s_scan[e - o] : 0;
+    __syncthreads();
+    s_scan[e] += v;
+    __syncthreads();
+  }
+  const int before = s_scan[e] - touched;  // exclusive prefix
+  if (touched) {
+    for (int b = 0; b < nblk_a; ++b) units_a[before * nblk_a + b] = (e << 16) | b;
+    for (int b = 0; b < nblk_b; ++b) units_b[before * nblk_b + b] = (e << 16) | b;
+  }
+  if (e == 255) {
+    *n_a = s_scan[255] * nblk_a;
+    *n_b = s_scan[255] * nblk_b;
+  }
+}
+
+}  // namespace
+
+void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return;
+  switch (epi) {
+    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV><<<grid, NT, 0, s>>>(a); break;
+    default: break;
+  }
+}
+
+void dg_launch_ws_units(const int32_t* counts, int E, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
+                        int32_t* units_b, int32_t* n_b, hipStream_t s) {
+  k_ws_units<<<1, 256, 0, s>>>(counts, E, nblk_a, units_a, n_a, nblk_b, units_b, n_b);
+}

@@ -67,6 +67,16 @@ class Workload:
                      + 3 * d * self.shared_hidden + 2 * d)
         return self.n_layers * per_layer + self.vocab * d + d
 
+    def active_param_count(self):
+        """Parameters one token touches in a forward pass: attention, router, its
+        top_k routed experts, the shared expert, norms, and the tied embedding /
+        LM head counted once."""
+        d, hd = self.d_model, self.head_dim
+        per_layer = ((self.n_q_heads + 2 * self.n_kv_heads) * hd * d + self.n_q_heads * hd * d
+                     + self.n_experts * d + self.top_k * 3 * d * self.expert_hidden
+                     + 3 * d * self.shared_hidden + 2 * d)
+        return self.n_layers * per_layer + self.vocab * d + d
+
 
 # The five workloads.  The tiny one leaves the shared-expert width unstated;
 # it is taken equal to the routed experts' width.

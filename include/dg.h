@@ -66,10 +66,11 @@ typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  * W2 (silu(W1 b) * W3 b) weighted by the gates, plus one shared SwiGLU expert
  * with weight 1.  The embedding is not scaled and serves as the LM head (tied).
  *
- * Supported shapes: head_dim even and a multiple of 16; d_model,
- * n_q_heads*head_dim, expert_hidden and shared_hidden multiples of 32 (bf16)
- * or 16 (f32); vocab a multiple of 256 (bf16) or 16 (f32); top_k <= 16;
- * n_experts <= 256; canvas_len == 256.
+ * Supported shapes: head_dim 16, 32, 64, 128 or 256 (bf16: at least 64);
+ * d_model and expert_hidden multiples of 64; n_q_heads*head_dim and
+ * shared_hidden multiples of 64 (bf16) or 16 (f32); vocab a multiple of 128;
+ * top_k <= 16; n_experts <= 256; max_requests <= 16; max_ctx a multiple of 64;
+ * canvas_len == 256.
  */
 typedef struct dg_model_config {
   int32_t vocab;

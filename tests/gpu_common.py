@@ -75,56 +75,101 @@ def compare_router(gpu_ids, gpu_gates, tr, k, gate_tol):
     return flips
 
 
+def rule_on(H, accepted, tau, step, cap):
+    """Positions the sampler rule takes at 1-based step `step`, given entropies H
+    (fp32) and the accepted mask before the step: open positions with H < tau, the
+    open position of lowest H (lowest index on ties), and at the cap every open
+    position.  Used as a property check of the GPU's decision on its own H."""
+    H = np.asarray(H, dtype=np.float32)
+    open_ = ~np.asarray(accepted, dtype=bool)
+    take = open_ & (H < np.float32(tau))
+    if open_.any():
+        idx = np.nonzero(open_)[0]
+        take[idx[np.argmin(H[idx])]] = True
+    if step >= cap:
+        take |= open_
+    return take
+
+
 def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows=8, check_router=True,
-               req=0, rng=None):
+               req=0, rng=None, stats=None):
     """Run one GPU step and the oracle step from the same state; compare.
 
-    Returns (oracle StepResult, resynced: bool)."""
+    Continuous values (entropy, log-sum-exp, sampled logits) are compared on the
+    open rows whose routing agreed with the oracle's in every layer; a row whose
+    expert set differs in some layer (allowed only inside the router's near-tie
+    band) is left out of them.  Integer decisions:
+      * argmax: equal unless the oracle's top-1 - top-2 gap is < GAP;
+      * sampler: the GPU's accept set must be the rule applied to the GPU's own
+        entropies (exact); where it differs from the oracle's, the difference must
+        lie in the tau band, or be the choice of the lowest-entropy position whose
+        oracle entropy is within 2 x (measured max entropy error) of the oracle's
+        minimum, the only way an error that small can move that choice;
+      * Philox re-draws: bit-exact.
+    After a permitted difference the GPU is re-synchronised to the oracle's state.
+    Returns (oracle StepResult, resynced, GPU step info)."""
     ids_g0, acc_g0 = dec.dg_get_canvas(req) if dec.dg_get_request(req)["active"] else (None, None)
     if ids_g0 is not None and st.active:
         assert np.array_equal(ids_g0, st.ids) and np.array_equal(acc_g0, st.accepted), "states diverged before step"
     info = dec.dg_denoise_step()[req]
     rows = dec.dg_last_step_rows()
     r = oracle.denoise_step(st, ocfg, scfg, ow, prec, keep_logits=True)
+    C = ocfg.canvas_len
+    row0 = 0
     open_b = ~r.accepted_before
-    # per-row statistics of open rows
-    He = r.entropy[open_b]
-    Hg = rows["entropy"][open_b].astype(np.float64)
-    err_h = np.abs(Hg - He)
-    assert np.all(err_h <= ent_tol(He)), ("entropy", float(err_h.max()))
-    lse_err = np.abs(rows["lse"][open_b] - r.lse[open_b])
-    assert np.all(lse_err <= ent_tol(np.abs(r.lse[open_b]))), ("lse", float(lse_err.max()))
-    gap = topk_gap(r.logits.astype(np.float32), 1)
-    am_diff = np.nonzero(open_b & (rows["argmax"] != r.argmax))[0]
-    for i in am_diff:
-        assert gap[i] < GAP, ("argmax differs outside the near-tie band", int(i), rows["argmax"][i], r.argmax[i],
-                              gap[i])
-    # logits of a sample of open rows
-    cand = np.nonzero(open_b)[0]
-    rng = rng or np.random.default_rng(0)
-    pick = np.sort(rng.choice(cand, size=min(sample_rows, len(cand)), replace=False))
-    lg = dec.dg_last_step_logits(pick).cpu().numpy()
-    logit_tol(lg, r.logits[pick])
     # router decisions of every layer
+    flipped = np.zeros(C, dtype=bool)
     if check_router:
         for l, tr in enumerate(r.layers):
-            compare_router(rows["router_ids"][l], rows["router_gates"][l], tr, ocfg.top_k,
-                           gate_tol=1e-4 if w.dtype == "f32" else 2e-2)
-    # sampler decisions
+            fl = compare_router(rows["router_ids"][l][row0:row0 + C], rows["router_gates"][l][row0:row0 + C], tr,
+                                ocfg.top_k, gate_tol=1e-4 if w.dtype == "f32" else 2e-2)
+            flipped[fl] = True
+    cmp = open_b & ~flipped
+    He = r.entropy[cmp]
+    Hg = rows["entropy"][row0:row0 + C][cmp].astype(np.float64)
+    err_h = np.abs(Hg - He)
+    assert np.all(err_h <= ent_tol(He)), ("entropy", float(err_h.max()))
+    lse_err = np.abs(rows["lse"][row0:row0 + C][cmp] - r.lse[cmp])
+    assert np.all(lse_err <= ent_tol(np.abs(r.lse[cmp]))), ("lse", float(lse_err.max()))
+    gap = topk_gap(r.logits.astype(np.float32), 1)
+    am_g = rows["argmax"][row0:row0 + C]
+    am_diff = np.nonzero(cmp & (am_g != r.argmax))[0]
+    for i in am_diff:
+        assert gap[i] < GAP, ("argmax differs outside the near-tie band", int(i), am_g[i], r.argmax[i], gap[i])
+    # logits of a sample of compared rows
+    cand = np.nonzero(cmp)[0]
+    rng = rng or np.random.default_rng(0)
+    pick = np.sort(rng.choice(cand, size=min(sample_rows, len(cand)), replace=False))
+    lg = dec.dg_last_step_logits(pick + row0).cpu().numpy()
+    logit_tol(lg, r.logits[pick])
+    if stats is not None:
+        stats.setdefault("ent_err", []).append(float(err_h.max()) if err_h.size else 0.0)
+        stats.setdefault("router_flip_rows", []).append(int(flipped.sum()))
+        stats.setdefault("argmax_flips", []).append(int(len(am_diff)))
+    # sampler: the GPU's accept set is the rule applied to its own (H, argmax)
     ids_g, acc_g = dec.dg_get_canvas(req)
+    Hg_all = rows["entropy"][row0:row0 + C]
+    take_g = rule_on(Hg_all, r.accepted_before, scfg.tau, st.step, scfg.max_steps)
+    assert np.array_equal(acc_g, r.accepted_before | take_g), "GPU accept set is not the rule on its own entropies"
+    exp_ids = r.ids_before.copy()
+    exp_ids[take_g] = am_g[take_g]
+    still = ~(r.accepted_before | take_g)
+    from oracle import philox
+    exp_ids[still] = philox.draw_tokens(st.seed, st.block, st.step, np.nonzero(still)[0], ocfg.vocab)
+    assert np.array_equal(ids_g, exp_ids), "GPU canvas is not accepted argmax + Philox re-draws"
     resync = False
     if not (np.array_equal(ids_g, r.ids_after) and np.array_equal(acc_g, r.accepted_after)):
-        # every difference must come from an exempt near-tie of the oracle
         newly_o = r.accepted_after & ~r.accepted_before
         newly_g = acc_g & ~r.accepted_before
-        h32 = r.entropy.astype(np.float32)
-        open_h = np.sort(h32[open_b])
-        lowest_tie = len(open_h) > 1 and (open_h[1] - open_h[0]) < DELTA_H[w.dtype]
+        eps = float(np.max(np.abs(Hg_all[open_b].astype(np.float64) - r.entropy[open_b])))
+        h_o_min = float(np.min(r.entropy[open_b]))
         for i in np.nonzero(newly_o != newly_g)[0]:
             near_tau = abs(r.entropy[i] - scfg.tau) < TAU_BAND
-            assert near_tau or lowest_tie, ("accept decision differs outside the bands", int(i))
+            lowest_choice = r.entropy[i] - h_o_min <= 2 * eps + 1e-12
+            assert near_tau or lowest_choice or flipped[i], ("accept decision differs outside the bands", int(i),
+                                                             r.entropy[i] - h_o_min, eps)
         for i in np.nonzero(newly_o & newly_g & (ids_g != r.ids_after))[0]:
-            assert gap[i] < GAP, ("accepted token differs outside the argmax band", int(i))
+            assert gap[i] < GAP or flipped[i], ("accepted token differs outside the argmax band", int(i))
         dec.dg_set_canvas(req, st.ids, st.accepted, st.step, st.block)
         resync = True
         log("  resync at block %d step %d" % (st.block, st.step))
