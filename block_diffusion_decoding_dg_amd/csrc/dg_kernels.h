@@ -24,7 +24,8 @@ struct DgShape {
 };
 
 // dtype: 0 = f32, 1 = bf16 (weights, activations and cache).
-void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, float* x, hipStream_t s);
+void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, int vocab, float* x,
+                     hipStream_t s);
 struct DgSampleArgs;
 void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, int d, float* x, hipStream_t s);
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
@@ -60,6 +61,9 @@ void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_
                        int vocab, float* part, int32_t* part_arg, float* ent, float* lse, int32_t* amax,
                        const int32_t* row_idx, hipStream_t s);
 int dg_lm_head_tiles(int vocab);
+// Tile merge of the LM-head partials alone (part [rows][n_tiles][3], part_arg [rows][n_tiles]).
+void dg_launch_lm_merge(const float* part, const int32_t* part_arg, const int32_t* n_dev, int max_rows, int n_tiles,
+                        const int32_t* row_idx, float* ent, float* lse, int32_t* amax, hipStream_t s);
 // Sampler over a batch of canvases (one per slot).
 struct DgSampleSlot {
   int32_t* ids;       // canvas ids [C]
@@ -92,7 +96,9 @@ enum {
   WS_EPI_STORE_F32 = 1,   // out fp32 [rows][ldo]
   WS_EPI_ADD_F32 = 2,     // out fp32 [rows][ldo] +=
   WS_EPI_SWIGLU = 3,      // W0 = W1, W1 = W3; 32 hidden columns per block; out bf16 silu(x W1^T) * (x W3^T)
-  WS_EPI_ROPE_QKV = 4     // W0/W1/W2 = wq/wk/wv; RoPE on q and k; q to out, k and v to the cache of segs
+  WS_EPI_ROPE_QKV = 4,    // W0/W1/W2 = wq/wk/wv; RoPE on q and k; q to out, k and v to the cache of segs
+  WS_EPI_LM_STATS = 5     // 128 vocabulary rows per block; per (row, block): (max, sum exp, sum exp * z) to out
+                          // fp32 [rows][ldo][3] and the argmax to part_arg [rows][ldo] (ldo = vocab / 128)
 };
 
 struct WsArgs {
@@ -105,6 +111,7 @@ struct WsArgs {
   int K;                  // reduction length, multiple of 64
   int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it
   int M;                  // rows of the single group when counts is null
+  const int32_t* M_dev;   // if set (and counts null): the row count, read on the device
   const int32_t* counts;  // grouped: rows per group
   const int32_t* offsets; // grouped: first position of each group in perm
   const int32_t* perm;    // grouped: pair index of each row; activation row = pair / kdiv, output row = pair
@@ -113,6 +120,7 @@ struct WsArgs {
   const int32_t* n_units;
   void* out;
   int ldo;
+  int32_t* part_arg;      // LM-head argmax partials
   // q/k/v epilogue
   int hd, hq, hkv, max_ctx;
   const double* inv_freq;

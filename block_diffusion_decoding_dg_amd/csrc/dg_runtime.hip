@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -309,6 +310,7 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
 // fp32 model keeps the plain matrix-core kernels.
 void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W0, const void* W1, int N, void* out,
                   int ldo) {
+  if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
@@ -327,6 +329,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 
 void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, const void* W1, size_t wgs, int K, int N,
                    int kdiv, const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo) {
+  if (c->dtype != DG_BF16) abort();  // bf16-only kernel
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
@@ -375,6 +378,33 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   dg_launch_ws(WS_EPI_ROPE_QKV, a, (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64, c->stream);
 }
 
+// Fused LM head over the rows of c->hn (count *n_dev <= max_rows): per-row
+// softmax statistics and argmax written at row_idx[row] (or row).
+void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t* row_idx, float* ent, float* lse,
+                    int32_t* amax) {
+  const dg_model_config& m = c->cfg;
+  if (c->dtype == DG_F32) {
+    dg_launch_lm_head(c->dtype, c->hn, n_dev, max_rows, m.d_model, c->embed, m.vocab, c->lpart, c->lpart_arg, ent, lse,
+                      amax, row_idx, c->stream);
+    return;
+  }
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = c->hn;
+  a.lda = m.d_model;
+  a.W0 = c->embed;
+  a.K = m.d_model;
+  a.N = m.vocab;
+  a.M = max_rows;
+  a.M_dev = n_dev;
+  a.kdiv = 1;
+  a.out = c->lpart;
+  a.ldo = c->lm_tiles;
+  a.part_arg = c->lpart_arg;
+  dg_launch_ws(WS_EPI_LM_STATS, a, c->lm_tiles, c->stream);
+  dg_launch_lm_merge(c->lpart, c->lpart_arg, n_dev, max_rows, c->lm_tiles, row_idx, ent, lse, amax, c->stream);
+}
+
 // Attention half of layer l over `rows` rows in c->x.
 void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal) {
   const dg_model_config& m = c->cfg;
@@ -387,7 +417,12 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
   const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
   KT(c, DG_KF_ATTENTION, dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s));
-  KT(c, DG_KF_OUT_PROJ, launch_dense(c, WS_EPI_ADD_F32, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, nullptr, m.d_model, c->x, m.d_model));
+  if (c->dtype == DG_F32)
+    KT(c, DG_KF_OUT_PROJ, dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x,
+                                         m.d_model, s));
+  else
+    KT(c, DG_KF_OUT_PROJ, launch_dense(c, WS_EPI_ADD_F32, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, nullptr,
+                                       m.d_model, c->x, m.d_model));
 }
 
 // FFN half of layer l over `rows` rows in c->x; routing written to ids/gates.
@@ -580,7 +615,7 @@ dg_status dg_prefill(dg_ctx* c, int32_t req, const int32_t* prompt_ids, int32_t 
   for (int c0 = 0; c0 < n; c0 += c->prefill_chunk) {
     const int cn = std::min(c->prefill_chunk, n - c0);
     HIPCK(c, hipMemcpyAsync(c->ids_stage, prompt_ids + c0, cn * 4, hipMemcpyHostToDevice, c->stream));
-    dg_launch_embed(c->dtype, c->ids_stage, cn, c->embed, c->cfg.d_model, c->x, c->stream);
+    dg_launch_embed(c->dtype, c->ids_stage, cn, c->embed, c->cfg.d_model, c->cfg.vocab, c->x, c->stream);
     std::vector<SlotRow> slots{{req, c0, cn}};
     forward_layers(c, slots, cn, true, true, false);
     LAUNCHCK(c);
@@ -629,8 +664,7 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
   forward_layers(c, slots, rows, false, false, true);
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
                                          c->cfg.rms_eps, c->hn, s));
-  KT(c, DG_KF_LM_HEAD, dg_launch_lm_head(c->dtype, c->hn, c->n_open_rows, rows, c->cfg.d_model, c->embed, c->cfg.vocab, c->lpart,
-                                         c->lpart_arg, c->ent, c->lse, c->amax, c->open_rows, s));
+  KT(c, DG_KF_LM_HEAD, launch_lm_head(c, c->n_open_rows, rows, c->open_rows, c->ent, c->lse, c->amax));
   KT(c, DG_KF_SAMPLE, dg_launch_sample(a, c->ent, c->amax, c->info_dev, nullptr, nullptr, s));
   LAUNCHCK(c);
   HIPCK(c, hipMemcpyAsync(c->info_host, c->info_dev, a.count * 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
@@ -860,8 +894,7 @@ dg_status dg_op_lm_head(dg_ctx* c, const float* h_dev, int32_t n, float* entropy
   HIPCK(c, hipMemcpyAsync(c->n_open_rows, &n, 4, hipMemcpyHostToDevice, s));
   dg_launch_rmsnorm(c->dtype, h_dev, nullptr, c->n_open_rows, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn,
                     s);
-  dg_launch_lm_head(c->dtype, c->hn, c->n_open_rows, n, c->cfg.d_model, c->embed, c->cfg.vocab, c->lpart,
-                    c->lpart_arg, entropy_dev, lse_dev, argmax_dev, nullptr, s);
+  launch_lm_head(c, c->n_open_rows, n, nullptr, entropy_dev, lse_dev, argmax_dev);
   LAUNCHCK(c);
   HIPCK(c, hipStreamSynchronize(s));
   return DG_OK;

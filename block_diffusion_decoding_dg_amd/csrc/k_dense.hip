@@ -10,19 +10,23 @@
 // Embedding: x[r] = E[ids[r]] (no scaling), fp32 residual stream.
 template <typename T>
 __global__ void __launch_bounds__(256) k_embed(const int32_t* __restrict__ ids, const T* __restrict__ E, int d,
-                                               float* __restrict__ x) {
+                                               int vocab, float* __restrict__ x) {
   const int r = blockIdx.x;
-  const T* src = E + (size_t)ids[r] * d;
+  // Ids are validated where they enter (host prompts, the sampler's argmax and
+  // Philox draws); the clamp only keeps a corrupted id from reading outside the table.
+  const int id = min(max(ids[r], 0), vocab - 1);
+  const T* src = E + (size_t)id * d;
   float* dst = x + (size_t)r * d;
   for (int c = threadIdx.x; c < d; c += blockDim.x) dst[c] = to_f(src[c]);
 }
 
-void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, float* x, hipStream_t s) {
+void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, int vocab, float* x,
+                     hipStream_t s) {
   if (rows <= 0) return;
   if (dtype == 1)
-    k_embed<bf16_t><<<rows, 256, 0, s>>>(ids, (const bf16_t*)embed, d, x);
+    k_embed<bf16_t><<<rows, 256, 0, s>>>(ids, (const bf16_t*)embed, d, vocab, x);
   else
-    k_embed<float><<<rows, 256, 0, s>>>(ids, (const float*)embed, d, x);
+    k_embed<float><<<rows, 256, 0, s>>>(ids, (const float*)embed, d, vocab, x);
 }
 
 // Same, reading the ids of batch row r from canvas slot r / C, position r % C.
@@ -30,7 +34,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_embed_slots(DgSampleArgs a, const T* __restrict__ E, int d,
                                                      float* __restrict__ x) {
   const int r = blockIdx.x;
-  const int id = a.s[r / a.C].ids[r % a.C];
+  const int id = min(max(a.s[r / a.C].ids[r % a.C], 0), a.vocab - 1);  // see k_embed
   const T* src = E + (size_t)id * d;
   float* dst = x + (size_t)r * d;
   for (int c = threadIdx.x; c < d; c += blockDim.x) dst[c] = to_f(src[c]);
@@ -441,7 +445,9 @@ __global__ void __launch_bounds__(64) k_lm_merge(const float* __restrict__ part,
     SoftStats o{part[pi * 3], part[pi * 3 + 1], part[pi * 3 + 2]};
     st = soft_merge(st, o);
     const int a = part_arg[pi];
-    if (o.m > best || (o.m == best && a < barg)) { best = o.m; barg = a; }
+    // A NaN maximum ranks lowest, so the winner is always a real column.
+    const float om = o.m == o.m ? o.m : -INFINITY;
+    if (om > best || (om == best && a < barg)) { best = om; barg = a; }
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -477,5 +483,11 @@ void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_
   else
     k_lm_head<float, MT, NS, WM, WN><<<grid, 64 * WM * WN, 0, s>>>((const float*)hn, n_dev, d, (const float*)embed,
                                                                   n_tiles, part, part_arg);
+  k_lm_merge<<<max_rows, 64, 0, s>>>(part, part_arg, n_dev, n_tiles, row_idx, ent, lse, amax);
+}
+
+void dg_launch_lm_merge(const float* part, const int32_t* part_arg, const int32_t* n_dev, int max_rows, int n_tiles,
+                        const int32_t* row_idx, float* ent, float* lse, int32_t* amax, hipStream_t s) {
+  if (max_rows <= 0) return;
   k_lm_merge<<<max_rows, 64, 0, s>>>(part, part_arg, n_dev, n_tiles, row_idx, ent, lse, amax);
 }

@@ -23,17 +23,19 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? logits[(size_t)r * E + e] : -INFINITY;
+    const float x = e < E ? logits[(size_t)r * E + e] : -INFINITY;
+    v[i] = x == x ? x : -INFINITY;  // a NaN logit ranks lowest
   }
   float sel[16];
   int sid[16];
+  unsigned taken = 0;  // entries of this lane already selected
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+      if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -42,10 +44,10 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
     sel[j] = bv;
-    sid[j] = bi;
+    sid[j] = bi;  // k <= E: some untaken entry always exists, so bi is a real expert
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
+      if (lane + 64 * i == bi) taken |= 1u << i;
   }
   if (lane == 0) {
     float s = 0.f;

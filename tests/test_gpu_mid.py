@@ -23,6 +23,13 @@ STEPS = 4
 # oracle; entropies and log-sum-exp within 1e-2 nats.
 LOGIT_RL2 = 1e-2
 ENT_ABS = 1e-2
+# K/V cache rows after several layers.  Both sides round to bf16 at the same
+# points, but once their pre-rounding values differ by a fraction of an ulp some
+# roundings flip, and each flip seeds larger differences downstream: the
+# per-element difference grows until it saturates near one bf16 ulp (2^-8
+# relative).  Rows are held to a median of 1e-2 and a 2e-2 tail (~5 ulp) for at
+# most 5% of rows; the step's own bound is on the logits.
+CACHE_ROW_TAIL = 2e-2
 
 
 def _ent_tol(h):
@@ -57,7 +64,8 @@ def _cache_rows(dec, st, ocfg, lo, hi, req=0):
         ko = st.cache_k[l][lo:hi].reshape(hi - lo, -1)
         vo = st.cache_v[l][lo:hi].reshape(hi - lo, -1)
         rows = np.array([max(rel_l2(kg[i], ko[i]), rel_l2(vg[i], vo[i])) for i in range(hi - lo)])
-        out.append((max(rel_l2(kg, ko), rel_l2(vg, vo)), float(np.mean(rows > LOGIT_RL2)), float(np.median(rows))))
+        out.append((max(rel_l2(kg, ko), rel_l2(vg, vo)), float(np.mean(rows > CACHE_ROW_TAIL)),
+                    float(np.median(rows))))
     return out
 
 
@@ -65,8 +73,9 @@ def _check_cache(dec, st, ocfg, lo, hi, what):
     stats = _cache_rows(dec, st, ocfg, lo, hi)
     for l, (tot, frac, med) in enumerate(stats):
         log("mid: %s layer %d: rel L2 %.2e, median row %.2e, rows over %.0e: %.1f%%"
-            % (what, l, tot, med, LOGIT_RL2, 100 * frac))
-    assert all(frac <= 0.05 for _, frac, _ in stats), stats
+            % (what, l, tot, med, CACHE_ROW_TAIL, 100 * frac))
+    assert stats[0][0] < 1e-3, stats[0]     # layer 0 sees only exact inputs (embeddings)
+    assert all(med <= 1e-2 and frac <= 0.05 for _, frac, med in stats), stats
 
 
 def test_mid_prefill_steps_commit(setup):
