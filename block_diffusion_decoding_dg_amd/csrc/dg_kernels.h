@@ -112,6 +112,8 @@ struct WsArgs {
   int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it
   int M;                  // rows of the single group when counts is null
   const int32_t* M_dev;   // if set (and counts null): the row count, read on the device
+  int msplit;             // dense launches: row ranges per n-block (grid = nblk * msplit); 0 or 1 = none
+  int nblk;               // dense launches: number of n-blocks
   const int32_t* counts;  // grouped: rows per group
   const int32_t* offsets; // grouped: first position of each group in perm
   const int32_t* perm;    // grouped: pair index of each row; activation row = pair / kdiv, output row = pair

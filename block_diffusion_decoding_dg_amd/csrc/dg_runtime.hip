@@ -308,6 +308,15 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
 
 // Launch helpers.  bf16 models run the weight-streaming kernel (k_ws.hip); the
 // fp32 model keeps the plain matrix-core kernels.
+
+// Row ranges per weight tile for a dense launch with nblk tiles over M rows: enough
+// blocks to give every CU one (256), at least 16 rows per block.  The extra reads
+// of a tile come from L2 (see the row split in k_ws).
+int dense_msplit(int nblk, int M) {
+  int ms = (256 + nblk - 1) / nblk;
+  ms = std::min(ms, std::max(1, M / 16));
+  return std::max(ms, 1);
+}
 void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W0, const void* W1, int N, void* out,
                   int ldo) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
@@ -323,8 +332,10 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   a.kdiv = 1;
   a.out = out;
   a.ldo = ldo;
-  const int grid = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
-  dg_launch_ws(epi, a, grid, c->stream);
+  const int nblk = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
+  a.nblk = nblk;
+  a.msplit = dense_msplit(nblk, M);
+  dg_launch_ws(epi, a, nblk * a.msplit, c->stream);
 }
 
 void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, const void* W1, size_t wgs, int K, int N,
@@ -375,7 +386,10 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   a.max_ctx = m.max_ctx;
   a.inv_freq = c->inv_freq;
   a.segs = sg;
-  dg_launch_ws(WS_EPI_ROPE_QKV, a, (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64, c->stream);
+  const int nblk = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64;
+  a.nblk = nblk;
+  a.msplit = dense_msplit(nblk, rows);
+  dg_launch_ws(WS_EPI_ROPE_QKV, a, nblk * a.msplit, c->stream);
 }
 
 // Fused LM head over the rows of c->hn (count *n_dev <= max_rows): per-row

@@ -201,6 +201,220 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
   }
 }
 
+// bf16 attention with the K and V^T tiles of 32 keys staged in LDS once per
+// block and shared by its four waves (the kernel above reads them once per wave).
+// The next tile is prefetched into registers while the current one is used, and
+// written to the other of two LDS stages.  K rows are XOR-swizzled in 16-byte
+// units (key & 7); each V^T row holds its 32 keys in the order the score tiles
+// deliver them (lane group g of the matrix core covers keys 4g..4g+3 and
+// 16+4g..16+4g+3) and is swizzled by ((row >> 1) & 3), so every fragment read
+// is one conflict-free 16-byte LDS load.  All waves of a block walk the same
+// key tiles; the key range is cut at the largest position among the block's
+// rows when the mask is causal.
+template <int HD>
+__global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
+                                                     int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
+                                                     int rows_total) {
+  typedef v8s F;
+  constexpr int NKK = HD / 32;
+  constexpr int NHT = HD / 16;
+  constexpr int KSEG = HD / 8;            // 16-byte segments per key row
+  constexpr int SEGS_K = 32 * KSEG;       // per tile
+  constexpr int SEGS_V = HD * 4;          // per tile (HD rows of 32 keys)
+  constexpr int LK = SEGS_K / 256, LV = SEGS_V / 256;
+  static_assert(LK >= 1 && LV >= 1, "head_dim >= 64");
+  __shared__ uint4 sK[2][SEGS_K];
+  __shared__ uint4 sV[2][SEGS_V];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+
+  int bid = blockIdx.x;
+  const int split = bid % nsplit;
+  bid /= nsplit;
+  const int qb = bid % nqb;
+  bid /= nqb;
+  const int h = bid % sh.hkv;
+  const int si = bid / sh.hkv;
+  if (si >= sg.count) return;
+  const DgSeg seg = sg.s[si];
+  const int G = sh.hq / sh.hkv;
+  const int nq = G * seg.n;
+  if (qb * ATTN_QROWS >= nq) return;  // uniform over the block
+  const int qr0 = qb * ATTN_QROWS + wave * 32;
+  const bool wave_active = qr0 < nq;
+
+  int qhead[2], trow[2], qpos[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qr = qr0 + qt * 16 + c16;
+    qvalid[qt] = qr < nq;
+    const int qrc = qvalid[qt] ? qr : nq - 1;
+    const int hg = qrc / seg.n, i = qrc - hg * seg.n;
+    qhead[qt] = h * G + hg;
+    trow[qt] = seg.row0 + i;
+    qpos[qt] = seg.pos0 + i;
+  }
+  const int nkeys = seg.nkeys;
+  const int chunk = ((nkeys + nsplit - 1) / nsplit + 31) / 32 * 32;
+  const int k_lo = split * chunk;
+  int k_hi = min(nkeys, k_lo + chunk);
+  if (sg.causal) {
+    // largest position among the block's rows (block-uniform)
+    const int first = qb * ATTN_QROWS, last = min(first + ATTN_QROWS, nq) - 1;
+    const int max_i = (first / seg.n == last / seg.n) ? last % seg.n : seg.n - 1;
+    k_hi = min(k_hi, seg.pos0 + max_i + 1);
+  }
+
+  F qf[2][NKK];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const char* qp = (const char*)(q + (size_t)trow[qt] * (sh.hq * HD) + qhead[qt] * HD) + g4 * 16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[qt][kk] = *(const F*)(qp + kk * 64);
+  }
+
+  const bf16_t* kbase = (const bf16_t*)seg.k + (size_t)h * sh.max_ctx * HD;
+  const bf16_t* vbase = (const bf16_t*)seg.vt + (size_t)h * HD * sh.max_ctx;
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+
+  // This thread's segments of a tile.
+  auto load_tile = [&](int kb, uint4 (&rk)[LK], uint4 (&rv)[LV]) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int sid = tid + 256 * i, key = sid / KSEG, sgi = sid % KSEG;
+      const int gk = min(kb + key, nkeys - 1);
+      rk[i] = *(const uint4*)(kbase + (size_t)gk * HD + sgi * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int sid = tid + 256 * i, d = sid >> 2, s4 = sid & 3;
+      rv[i] = *(const uint4*)(vbase + (size_t)d * sh.max_ctx + kb + s4 * 8);
+    }
+  };
+  auto store_tile = [&](int stg, const uint4 (&rk)[LK], const uint4 (&rv)[LV]) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int sid = tid + 256 * i, key = sid / KSEG, sgi = sid % KSEG;
+      sK[stg][key * KSEG + (sgi ^ (key & 7))] = rk[i];
+    }
+    uint2* v8 = reinterpret_cast<uint2*>(sV[stg]);
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int sid = tid + 256 * i, d = sid >> 2, s4 = sid & 3;
+      const int kt = s4 >> 1, g0 = (s4 & 1) * 2, sw = (d >> 1) & 3;
+      v8[d * 8 + (g0 ^ sw) * 2 + kt] = make_uint2(rv[i].x, rv[i].y);        // keys 8 s4 .. +3
+      v8[d * 8 + ((g0 + 1) ^ sw) * 2 + kt] = make_uint2(rv[i].z, rv[i].w);  // keys 8 s4 + 4 .. +7
+    }
+  };
+
+  v4f oacc[NHT][2];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) oacc[ht][0] = oacc[ht][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+  uint4 rk[LK], rv[LV];
+  if (k_lo < k_hi) {
+    load_tile(k_lo, rk, rv);
+    store_tile(0, rk, rv);
+  }
+  __syncthreads();
+  int stg = 0;
+  for (int kb = k_lo; kb < k_hi; kb += 32) {
+    const bool more = kb + 32 < k_hi;
+    load_tile(more ? kb + 32 : kb, rk, rv);
+    if (wave_active) {
+      v4f st[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        st[kt][0] = st[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+        const int key = kt * 16 + c16;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & 7))];
+          const F kf = *reinterpret_cast<const F*>(&u);
+          st[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], st[kt][0], 0, 0, 0);
+          st[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], st[kt][1], 0, 0, 0);
+        }
+      }
+      float p[2][2][4];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + kt * 16 + g4 * 4 + i;
+            float sc = st[kt][qt][i] * scale;
+            if (key >= k_hi || (sg.causal && key > qpos[qt])) sc = -INFINITY;
+            p[kt][qt][i] = sc;
+            tmax = fmaxf(tmax, sc);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mnew = fmaxf(mrun[qt], tmax);
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun[qt] - mnew);
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = (mnew == -INFINITY) ? 0.f : exp2f(p[kt][qt][i] - mnew);
+            p[kt][qt][i] = e;
+            psum += e;
+          }
+        lrun[qt] = lrun[qt] * alpha + psum;
+        mrun[qt] = mnew;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] *= alpha;
+      }
+      // P as bf16 high + low parts (see k_attn).
+      F pf[2], pl[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = p[kt][qt][i];
+            const bf16_t hb = f2bf(v);
+            pf[qt][kt * 4 + i] = (short)hb;
+            pl[qt][kt * 4 + i] = (short)f2bf(v - bf2f(hb));
+          }
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const int d = ht * 16 + c16;
+        const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
+        const F vf = *reinterpret_cast<const F*>(&u);
+        oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], oacc[ht][0], 0, 0, 0);
+        oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], oacc[ht][1], 0, 0, 0);
+        oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[0], oacc[ht][0], 0, 0, 0);
+        oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[1], oacc[ht][1], 0, 0, 0);
+      }
+    }
+    store_tile(stg ^ 1, rk, rv);
+    __syncthreads();
+    stg ^= 1;
+  }
+  if (!wave_active) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
+    lrun[qt] += __shfl_xor(lrun[qt], 32, 64);
+    if (!qvalid[qt]) continue;
+    const size_t qi = (size_t)trow[qt] * sh.hq + qhead[qt];
+    float* op = opart + ((size_t)split * rows_total * sh.hq + qi) * HD;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) *(v4f*)(op + ht * 16 + g4 * 4) = oacc[ht][qt];
+    if (g4 == 0) {
+      float* ml = mlpart + ((size_t)split * rows_total * sh.hq + qi) * 2;
+      ml[0] = mrun[qt];
+      ml[1] = lrun[qt];
+    }
+  }
+}
+
 // Merge the splits of each (row, q-head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 template <typename T>
 __global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opart, const float* __restrict__ mlpart,
@@ -231,8 +445,10 @@ int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits) {
     base += sh.hkv * ((G * segs.s[i].n + ATTN_QROWS - 1) / ATTN_QROWS);
     maxkeys = maxkeys > segs.s[i].nkeys ? maxkeys : segs.s[i].nkeys;
   }
-  int ns = (512 + base - 1) / (base > 0 ? base : 1);
-  const int by_keys = (maxkeys + 127) / 128;
+  // One block per CU at the full head size: aim at 256 blocks, each split at
+  // least 8 key tiles long (fewer splits also means fewer partials to merge).
+  int ns = (256 + base - 1) / (base > 0 ? base : 1);
+  const int by_keys = (maxkeys + 255) / 256;
   if (ns > by_keys) ns = by_keys;
   if (ns > max_splits) ns = max_splits;
   if (ns < 1) ns = 1;
@@ -250,10 +466,13 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #define DG_ATTN(TT, HDV)                                                                                     \
   k_attn<TT, HDV><<<blocks, 256, 0, s>>>((const TT*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);         \
   k_attn_merge<TT><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (TT*)o)
+#define DG_ATTN_LDS(HDV)                                                                                    \
+  k_attn_lds<HDV><<<blocks, 256, 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);        \
+  k_attn_merge<bf16_t><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (bf16_t*)o)
   if (dtype == 1) {
-    if (sh.hd == 256) { DG_ATTN(bf16_t, 256); }
-    else if (sh.hd == 128) { DG_ATTN(bf16_t, 128); }
-    else if (sh.hd == 64) { DG_ATTN(bf16_t, 64); }
+    if (sh.hd == 256) { DG_ATTN_LDS(256); }
+    else if (sh.hd == 128) { DG_ATTN_LDS(128); }
+    else if (sh.hd == 64) { DG_ATTN_LDS(64); }
     else { DG_ATTN(bf16_t, 32); }
   } else {
     if (sh.hd == 256) { DG_ATTN(float, 256); }
@@ -263,4 +482,5 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
     else { DG_ATTN(float, 16); }
   }
 #undef DG_ATTN
+#undef DG_ATTN_LDS
 }

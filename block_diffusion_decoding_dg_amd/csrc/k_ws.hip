@@ -2,18 +2,19 @@
 // step: a few hundred activation rows against large weight matrices, so that the
 // step's time is set by how fast the weights stream from HBM.  Used for the routed
 // experts (grouped by expert, rows gathered through the token permutation), the
-// shared expert and the dense projections.
+// shared expert, the dense projections and the LM head.
 //
-// A block owns 64 consecutive weight rows ("n-block") of one group and every
-// activation row of that group, up to 256 per pass over the weights (a group with
-// more rows takes several passes).  Each weight byte therefore crosses HBM once
-// per 256 rows, whatever the routing.  The weight tile streams through a
-// two-stage LDS buffer in chunks of 64 reduction elements (128 bytes per row),
-// fed by a four-deep register prefetch ring (8 KB per chunk per block, one
-// 16-byte segment per thread, four chunks in flight); the eight waves split the
-// activation rows (m-tile i goes to wave i % 8) and read their own activation
-// fragments straight from global memory one chunk ahead.  The LDS rows are XOR-swizzled in 16-byte units so that
-// both the cooperative stores and the fragment reads are free of bank conflicts.
+// A block owns BN = 16 * NTN consecutive weight rows ("n-block") of one group and
+// every activation row of that group, up to 256 per pass over the weights (a group
+// with more rows takes several passes).  Each weight byte therefore crosses HBM
+// once per 256 rows, whatever the routing.  The weight tile streams through a
+// two-stage LDS buffer in chunks of 64 reduction elements (128 bytes per row), fed
+// by a four-deep register prefetch ring (NTN / 4 16-byte segments per thread per
+// chunk, four chunks in flight); the eight waves split the activation rows (m-tile
+// i goes to wave i % 8) and read their own activation fragments straight from
+// global memory one chunk ahead.  The LDS rows are XOR-swizzled in 16-byte units so
+// that both the cooperative stores and the fragment reads are free of bank
+// conflicts.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16): lane l supplies activation row
 // l % 16 and weight row l % 16, each with reduction elements 8 (l / 16) .. +7 of a
@@ -25,7 +26,6 @@
 
 namespace {
 
-constexpr int BN = 64;    // weight rows per block
 constexpr int BK = 64;    // reduction elements per chunk
 constexpr int NWAVE = 8;  // waves per block
 constexpr int NT = 64 * NWAVE;
@@ -35,8 +35,8 @@ constexpr int PASS_ROWS = NWAVE * MTW * 16;
 
 __device__ __forceinline__ int lds_slot(int row, int seg) { return row * 8 + (seg ^ (row & 7)); }
 
-// Weight row `r` (0..63) of n-block nb of group g, per epilogue.
-template <int EPI>
+// Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue.
+template <int EPI, int NTN>
 __device__ __forceinline__ const bf16_t* weight_row(const WsArgs& a, int g, int nb, int r) {
   if constexpr (EPI == WS_EPI_SWIGLU) {
     // rows 0..31: W1 rows, rows 32..63: W3 rows, of the same 32 hidden columns
@@ -56,7 +56,7 @@ __device__ __forceinline__ const bf16_t* weight_row(const WsArgs& a, int g, int 
     return W + (size_t)(hl * a.hd + j) * a.K;
   } else {
     const bf16_t* W = (const bf16_t*)a.W0 + (size_t)g * a.wgs;
-    const int n = nb * BN + r;
+    const int n = nb * (16 * NTN) + r;
     return W + (size_t)min(n, a.N - 1) * a.K;
   }
 }
@@ -68,169 +68,269 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
   return s;
 }
 
-template <int EPI>
+// Streams the weight tile of one pass through LDS and accumulates this wave's MA
+// active m-tiles (0, 1 or 2).  The loop body is branch-free: the chunk count is
+// padded to a multiple of the ring depth, chunks past the end put zeros in LDS
+// (their products add nothing) and every load address is clamped to valid
+// memory, so the number of loads in flight is the same in every iteration and the
+// compiler can wait for exactly the oldest one.  All variants execute the same
+// barriers.
+template <int NTN, int MA>
+__device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8], const char* gsrc0, const char* gsrc1, int slot0,
+                                          int slot1, const char* const (&ap)[MTW], int nk, int lane,
+                                          v4f (&acc)[MTW][NTN]) {
+  constexpr int NL = NTN / 4;
+  uint4 r0a, r0b, r1a, r1b, r2a, r2b, r3a, r3b;
+  r0a = *(const uint4*)(gsrc0 + min(0, nk - 1) * 128);
+  r1a = *(const uint4*)(gsrc0 + min(1, nk - 1) * 128);
+  r2a = *(const uint4*)(gsrc0 + min(2, nk - 1) * 128);
+  r3a = *(const uint4*)(gsrc0 + min(3, nk - 1) * 128);
+  if constexpr (NL == 2) {
+    r0b = *(const uint4*)(gsrc1 + min(0, nk - 1) * 128);
+    r1b = *(const uint4*)(gsrc1 + min(1, nk - 1) * 128);
+    r2b = *(const uint4*)(gsrc1 + min(2, nk - 1) * 128);
+    r3b = *(const uint4*)(gsrc1 + min(3, nk - 1) * 128);
+  }
+  v8s af0[MTW][2], af1[MTW][2];
+#pragma unroll
+  for (int j = 0; j < MA; ++j) {
+    af0[j][0] = *(const v8s*)(ap[j]);
+    af0[j][1] = *(const v8s*)(ap[j] + 64);
+  }
+  auto chunk = [&](auto JR, uint4& Ra, uint4& Rb, int c) {
+    constexpr int jr = decltype(JR)::value;
+    constexpr int st = jr & 1;  // LDS stage == c & 1 (c0 is a multiple of 4)
+    v8s(&acur)[MTW][2] = (jr & 1) ? af1 : af0;
+    v8s(&anxt)[MTW][2] = (jr & 1) ? af0 : af1;
+    // Chunks past the end store zeros: a mask on the values (a conditional between
+    // two lvalues would make the compiler select between their addresses and keep
+    // the ring in scratch memory).
+    const uint32_t live = c < nk ? 0xffffffffu : 0u;
+    sW[st][slot0] = make_uint4(Ra.x & live, Ra.y & live, Ra.z & live, Ra.w & live);
+    if constexpr (NL == 2) sW[st][slot1] = make_uint4(Rb.x & live, Rb.y & live, Rb.z & live, Rb.w & live);
+    __syncthreads();
+    const int cr = min(c + RING, nk - 1);
+    Ra = *(const uint4*)(gsrc0 + cr * 128);
+    if constexpr (NL == 2) Rb = *(const uint4*)(gsrc1 + cr * 128);
+    const int cn = min(c + 1, nk - 1);
+#pragma unroll
+    for (int j = 0; j < MA; ++j) {
+      anxt[j][0] = *(const v8s*)(ap[j] + cn * 128);
+      anxt[j][1] = *(const v8s*)(ap[j] + cn * 128 + 64);
+    }
+    if constexpr (MA > 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        v8s wf[NTN];
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+          const uint4 u = sW[st][lds_slot(n * 16 + (lane & 15), s * 4 + (lane >> 4))];
+          wf[n] = *reinterpret_cast<const v8s*>(&u);
+        }
+#pragma unroll
+        for (int j = 0; j < MA; ++j)
+#pragma unroll
+          for (int n = 0; n < NTN; ++n)
+            acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[j][s], wf[n], acc[j][n], 0, 0, 0);
+      }
+    }
+  };
+  for (int c0 = 0; c0 < nk; c0 += RING) {
+    chunk(std::integral_constant<int, 0>{}, r0a, r0b, c0);
+    chunk(std::integral_constant<int, 1>{}, r1a, r1b, c0 + 1);
+    chunk(std::integral_constant<int, 2>{}, r2a, r2b, c0 + 2);
+    chunk(std::integral_constant<int, 3>{}, r3a, r3b, c0 + 3);
+  }
+}
+
+template <int EPI, int NTN>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
+  constexpr int BN = 16 * NTN;
+  constexpr int NL = NTN / 4;  // 16-byte segments per thread per chunk
   __shared__ uint4 sW[2][BN * 8];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int g = 0, nb = blockIdx.x;
+  int g = 0, nb = blockIdx.x, ms = 0;
   if (a.units) {
     if ((int)blockIdx.x >= *a.n_units) return;
     const int code = a.units[blockIdx.x];
     g = code >> 16;
     nb = code & 0xffff;
+  } else if (a.msplit > 1) {
+    // Row split of a dense launch.  When the n-blocks come in groups of 8, the
+    // blocks sharing a weight tile are 8 launch slots apart, i.e. on the same XCD
+    // (work-groups are dealt to the 8 XCDs in turn) and started close together,
+    // so the tile crosses HBM once and the other row ranges read it from L2.
+    const int b = blockIdx.x;
+    if (a.nblk % 8 == 0) {
+      const int lo = b % 8, rest = b / 8;
+      ms = rest % a.msplit;
+      nb = (rest / a.msplit) * 8 + lo;
+    } else {
+      ms = b % a.msplit;
+      nb = b / a.msplit;
+    }
   }
-  const int cnt = a.counts ? a.counts[g] : a.M;
+  int cnt = a.counts ? a.counts[g] : (a.M_dev ? *a.M_dev : a.M);
+  int row0 = 0;
+  if (a.msplit > 1 && !a.counts) {
+    const int per = ((cnt + a.msplit - 1) / a.msplit + 15) / 16 * 16;
+    row0 = ms * per;
+    cnt = min(cnt - row0, per);
+  }
   if (cnt <= 0) return;  // uniform over the block
   const int off = a.counts ? a.offsets[g] : 0;
   const int nk = a.K / BK;
 
-  // This thread's 16-byte segment of every weight chunk.
-  const int wr = tid >> 3, wc = tid & 7;
-  const char* gsrc = (const char*)weight_row<EPI>(a, g, nb, wr) + wc * 16;
-  const int slot = lds_slot(wr, wc);
+  // This thread's 16-byte segments of every weight chunk (the second only when
+  // NTN == 8).  Named scalars rather than arrays keep them in registers.
+  const char* gsrc0 = (const char*)weight_row<EPI, NTN>(a, g, nb, tid >> 3) + (tid & 7) * 16;
+  const int slot0 = lds_slot(tid >> 3, tid & 7);
+  const char* gsrc1 = gsrc0;
+  int slot1 = slot0;
+  if constexpr (NL == 2) {
+    const int sid = tid + NT;
+    gsrc1 = (const char*)weight_row<EPI, NTN>(a, g, nb, sid >> 3) + (sid & 7) * 16;
+    slot1 = lds_slot(sid >> 3, sid & 7);
+  }
 
   const int npass = (cnt + PASS_ROWS - 1) / PASS_ROWS;
   for (int pass = 0; pass < npass; ++pass) {
     const int pbase = pass * PASS_ROWS;
-    // Activation rows of this wave's m-tiles.
+    // Activation rows of this wave's m-tiles (rows row0 + pbase + ... of the group).
     int mt_act = 0;
     const char* ap[MTW];
 #pragma unroll
     for (int j = 0; j < MTW; ++j) {
       const int t0 = pbase + (wave + NWAVE * j) * 16;
       if (t0 < cnt) mt_act = j + 1;
-      const int r = min(t0 + (lane & 15), cnt - 1);
+      const int r = row0 + min(t0 + (lane & 15), cnt - 1);
       int arow;
       if (a.counts) arow = a.perm[off + r] / a.kdiv;
       else arow = r;
       ap[j] = (const char*)((const bf16_t*)a.A + (size_t)arow * a.lda) + (lane >> 4) * 16;
     }
 
-    v4f acc[MTW][4];
+    v4f acc[MTW][NTN];
 #pragma unroll
     for (int j = 0; j < MTW; ++j)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Register prefetch ring (four named registers: chunk c lives in ring slot c % 4)
-    // and double-buffered activation fragments (chunk c in afr[c % 2]).  Refills
-    // past the last chunk re-read the last chunk (a harmless cached load) so that
-    // every refill is unconditional.
-    uint4 r0, r1, r2, r3;
-    r0 = *(const uint4*)(gsrc + min(0, nk - 1) * 128);
-    r1 = *(const uint4*)(gsrc + min(1, nk - 1) * 128);
-    r2 = *(const uint4*)(gsrc + min(2, nk - 1) * 128);
-    r3 = *(const uint4*)(gsrc + min(3, nk - 1) * 128);
-    v8s af0[MTW][2], af1[MTW][2];
-#pragma unroll
-    for (int j = 0; j < MTW; ++j)
-      if (j < mt_act) {
-        af0[j][0] = *(const v8s*)(ap[j]);
-        af0[j][1] = *(const v8s*)(ap[j] + 64);
-      }
-
-    auto chunk = [&](auto JR, uint4& R, int c) {
-      constexpr int jr = decltype(JR)::value;
-      constexpr int st = jr & 1;  // LDS stage == c & 1 (c0 is a multiple of 4)
-      v8s(&acur)[MTW][2] = (jr & 1) ? af1 : af0;
-      v8s(&anxt)[MTW][2] = (jr & 1) ? af0 : af1;
-      sW[st][slot] = R;
-      __syncthreads();
-      R = *(const uint4*)(gsrc + min(c + RING, nk - 1) * 128);
-      if (c + 1 < nk) {
-#pragma unroll
-        for (int j = 0; j < MTW; ++j)
-          if (j < mt_act) {
-            anxt[j][0] = *(const v8s*)(ap[j] + (c + 1) * 128);
-            anxt[j][1] = *(const v8s*)(ap[j] + (c + 1) * 128 + 64);
-          }
-      }
-      if (mt_act > 0) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          v8s wf[4];
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const uint4 u = sW[st][lds_slot(n * 16 + (lane & 15), s * 4 + (lane >> 4))];
-            wf[n] = *reinterpret_cast<const v8s*>(&u);
-          }
-#pragma unroll
-          for (int j = 0; j < MTW; ++j)
-            if (j < mt_act) {
-#pragma unroll
-              for (int n = 0; n < 4; ++n)
-                acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[j][s], wf[n], acc[j][n], 0, 0, 0);
-            }
-        }
-      }
-    };
-    for (int c0 = 0; c0 < nk; c0 += RING) {
-      chunk(std::integral_constant<int, 0>{}, r0, c0);
-      if (c0 + 1 < nk) chunk(std::integral_constant<int, 1>{}, r1, c0 + 1);
-      if (c0 + 2 < nk) chunk(std::integral_constant<int, 2>{}, r2, c0 + 2);
-      if (c0 + 3 < nk) chunk(std::integral_constant<int, 3>{}, r3, c0 + 3);
-    }
+    if (mt_act == 0) ws_stream<NTN, 0>(sW, gsrc0, gsrc1, slot0, slot1, ap, nk, lane, acc);
+    else if (mt_act == 1) ws_stream<NTN, 1>(sW, gsrc0, gsrc1, slot0, slot1, ap, nk, lane, acc);
+    else ws_stream<NTN, 2>(sW, gsrc0, gsrc1, slot0, slot1, ap, nk, lane, acc);
 
     // Epilogue.
+    if constexpr (EPI == WS_EPI_LM_STATS) {
+      // Per row over this block's BN vocabulary columns: max, sum exp(z - max),
+      // sum exp(z - max) (z - max), and the argmax (lowest column among equal
+      // maxima).  Lane holds columns n * 16 + lane % 16 of rows 4 (lane / 16) + i.
 #pragma unroll
-    for (int j = 0; j < MTW; ++j) {
-      if (j >= mt_act) break;
+      for (int j = 0; j < MTW; ++j) {
+        if (j >= mt_act) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
-        if (r >= cnt) continue;
-        const int orow = a.counts ? a.perm[off + r] : r;
-        if constexpr (EPI == WS_EPI_SWIGLU) {
+        for (int i = 0; i < 4; ++i) {
+          float m = acc[j][0][i];
+          int am = nb * BN + (lane & 15);
 #pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            const int col = nb * 32 + n * 16 + (lane & 15);
-            if (col < a.N)
-              ((bf16_t*)a.out)[(size_t)orow * a.ldo + col] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + 2][i]);
-          }
-        } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
-          const int half = a.hd / 2, per_head = half / 32;
-          const int head = nb / per_head;
-          const int si = seg_index(a.segs, r);
-          const int pos = a.segs.s[si].pos0 + (r - a.segs.s[si].row0);
-#pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            const int jj = (nb - head * per_head) * 32 + n * 16 + (lane & 15);
-            float x1 = acc[j][n][i], x2 = acc[j][n + 2][i];
-            if (head < a.hq + a.hkv) {
-              double ang = (double)pos * a.inv_freq[jj];
-              const double two_pi = 6.283185307179586476925286766559;
-              ang -= two_pi * rint(ang / two_pi);
-              float sn, cs;
-              sincosf((float)ang, &sn, &cs);
-              const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-              x1 = y1;
-              x2 = y2;
+          for (int n = 1; n < NTN; ++n)
+            if (acc[j][n][i] > m) {
+              m = acc[j][n][i];
+              am = nb * BN + n * 16 + (lane & 15);
             }
-            if (head < a.hq) {
-              bf16_t* q = (bf16_t*)a.out + (size_t)r * a.ldo + head * a.hd;
-              q[jj] = f2bf(x1);
-              q[jj + half] = f2bf(x2);
-            } else if (head < a.hq + a.hkv) {
-              const int hl = head - a.hq;
-              bf16_t* k = (bf16_t*)a.segs.s[si].k + ((size_t)hl * a.max_ctx + pos) * a.hd;
-              k[jj] = f2bf(x1);
-              k[jj + half] = f2bf(x2);
-            } else {
-              const int hl = head - a.hq - a.hkv;
-              bf16_t* vt = (bf16_t*)a.segs.s[si].vt + (size_t)hl * a.hd * a.max_ctx;
-              vt[(size_t)jj * a.max_ctx + pos] = f2bf(x1);
-              vt[(size_t)(jj + half) * a.max_ctx + pos] = f2bf(x2);
-            }
-          }
-        } else {
 #pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int col = nb * BN + n * 16 + (lane & 15);
-            if (col >= a.N) continue;
-            const size_t o = (size_t)orow * a.ldo + col;
-            if constexpr (EPI == WS_EPI_STORE_BF16) ((bf16_t*)a.out)[o] = f2bf(acc[j][n][i]);
-            else if constexpr (EPI == WS_EPI_STORE_F32) ((float*)a.out)[o] = acc[j][n][i];
-            else ((float*)a.out)[o] += acc[j][n][i];
+          for (int o = 1; o < 16; o <<= 1) {
+            const float om = __shfl_xor(m, o, 64);
+            const int oa = __shfl_xor(am, o, 64);
+            if (om > m || (om == m && oa < am)) { m = om; am = oa; }
+          }
+          float s = 0.f, t = 0.f;
+#pragma unroll
+          for (int n = 0; n < NTN; ++n) {
+            const float z = acc[j][n][i] - m;
+            const float e = __expf(z);
+            s += e;
+            t += e * z;
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            s += __shfl_xor(s, o, 64);
+            t += __shfl_xor(t, o, 64);
+          }
+          const int rl = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
+          const int r = row0 + rl;
+          if ((lane & 15) == 0 && rl < cnt) {
+            const size_t pi = (size_t)r * a.ldo + nb;  // ldo = number of vocabulary tiles
+            float* pp = (float*)a.out + pi * 3;
+            pp[0] = m;
+            pp[1] = s;
+            pp[2] = t;
+            a.part_arg[pi] = am;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+        if (j >= mt_act) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
+          if (rl >= cnt) continue;
+          const int r = row0 + rl;
+          const int orow = a.counts ? a.perm[off + r] : r;
+          if constexpr (EPI == WS_EPI_SWIGLU) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              const int col = nb * 32 + n * 16 + (lane & 15);
+              if (col < a.N)
+                ((bf16_t*)a.out)[(size_t)orow * a.ldo + col] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + 2][i]);
+            }
+          } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
+            const int half = a.hd / 2, per_head = half / 32;
+            const int head = nb / per_head;
+            const int si = seg_index(a.segs, r);
+            const int pos = a.segs.s[si].pos0 + (r - a.segs.s[si].row0);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              const int jj = (nb - head * per_head) * 32 + n * 16 + (lane & 15);
+              float x1 = acc[j][n][i], x2 = acc[j][n + 2][i];
+              if (head < a.hq + a.hkv) {
+                double ang = (double)pos * a.inv_freq[jj];
+                const double two_pi = 6.283185307179586476925286766559;
+                ang -= two_pi * rint(ang / two_pi);
+                float sn, cs;
+                sincosf((float)ang, &sn, &cs);
+                const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+                x1 = y1;
+                x2 = y2;
+              }
+              if (head < a.hq) {
+                bf16_t* qd = (bf16_t*)a.out + (size_t)r * a.ldo + head * a.hd;
+                qd[jj] = f2bf(x1);
+                qd[jj + half] = f2bf(x2);
+              } else if (head < a.hq + a.hkv) {
+                const int hl = head - a.hq;
+                bf16_t* k = (bf16_t*)a.segs.s[si].k + ((size_t)hl * a.max_ctx + pos) * a.hd;
+                k[jj] = f2bf(x1);
+                k[jj + half] = f2bf(x2);
+              } else {
+                const int hl = head - a.hq - a.hkv;
+                bf16_t* vt = (bf16_t*)a.segs.s[si].vt + (size_t)hl * a.hd * a.max_ctx;
+                vt[(size_t)jj * a.max_ctx + pos] = f2bf(x1);
+                vt[(size_t)(jj + half) * a.max_ctx + pos] = f2bf(x2);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) {
+              const int col = nb * BN + n * 16 + (lane & 15);
+              if (col >= a.N) continue;
+              const size_t o = (size_t)orow * a.ldo + col;
+              if constexpr (EPI == WS_EPI_STORE_BF16) ((bf16_t*)a.out)[o] = f2bf(acc[j][n][i]);
+              else if constexpr (EPI == WS_EPI_STORE_F32) ((float*)a.out)[o] = acc[j][n][i];
+              else ((float*)a.out)[o] += acc[j][n][i];
+            }
           }
         }
       }
@@ -272,11 +372,12 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
   switch (epi) {
-    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8><<<grid, NT, 0, s>>>(a); break;
     default: break;
   }
 }

@@ -82,8 +82,9 @@ def new_request(cfg: ModelConfig, seed: int, max_ctx: int) -> RequestState:
     return st
 
 
-def prefill(st: RequestState, prompt, cfg: ModelConfig, w: Weights, prec: Precision):
-    """Causal forward over the prompt; stores post-RoPE K/V at [0, n)."""
+def prefill(st: RequestState, prompt, cfg: ModelConfig, w: Weights, prec: Precision, keep_traces=False):
+    """Causal forward over the prompt; stores post-RoPE K/V at [0, n).
+    Returns the final rows, and with keep_traces also the per-layer traces."""
     prompt = np.asarray(prompt, dtype=np.int64)
     n = prompt.shape[0]
     if n > st.max_ctx:
@@ -92,17 +93,20 @@ def prefill(st: RequestState, prompt, cfg: ModelConfig, w: Weights, prec: Precis
     st.block = 0
     st.active = False
     if n == 0:
-        return np.zeros((0, cfg.d_model))
+        x = np.zeros((0, cfg.d_model))
+        return (x, []) if keep_traces else x
     x = w.embed[prompt]
     pos = np.arange(n)
     mask = np.tril(np.ones((n, n), dtype=bool))
     empty = np.zeros((0, cfg.n_kv_heads, cfg.head_dim))
+    traces = []
     for l, lw in enumerate(w.layers):
         x, tr = layer_forward(x, pos, lw, cfg, prec, empty, empty, mask=mask,
                               skip_ffn=(l == cfg.n_layers - 1))
         st.cache_k[l][:n] = tr.k
         st.cache_v[l][:n] = tr.v
-    return x
+        traces.append(tr)
+    return (x, traces) if keep_traces else x
 
 
 def start_canvas(st: RequestState, cfg: ModelConfig):
@@ -180,8 +184,9 @@ def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Wei
                       logits=stats.get("logits"), hidden=x)
 
 
-def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision):
-    """Write the K/V of a forward over the final canvas to [P, P + C); P += C."""
+def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision, keep_traces=False):
+    """Write the K/V of a forward over the final canvas to [P, P + C); P += C.
+    Returns the block's ids, and with keep_traces also the per-layer traces."""
     if not st.active or not st.accepted.all():
         raise ValueError("commit before the canvas is done")
     _, traces = canvas_forward(st, cfg, w, prec, for_commit=True)
@@ -195,7 +200,7 @@ def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision
     st.active = False
     st.ids = None
     st.accepted = None
-    return out
+    return (out, traces) if keep_traces else out
 
 
 def generate(prompt, n_out, seed, cfg: ModelConfig, scfg: SamplerConfig, w: Weights,

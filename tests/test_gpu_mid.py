@@ -12,7 +12,7 @@ import torch
 import oracle
 from block_diffusion_decoding_dg_amd import synth
 from tests import helpers
-from tests.gpu_common import check_step, log, make_decoder, rel_l2
+from tests.gpu_common import check_step, log, make_decoder, rel_l2, topk_gap
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,12 @@ STEPS = 4
 # oracle; entropies and log-sum-exp within 1e-2 nats.
 LOGIT_RL2 = 1e-2
 ENT_ABS = 1e-2
+# Near-tie band of the step-level decisions (router sets, argmax).  The spec's
+# 1e-3 applies to a decision taken from the same input, which the op-level tests
+# check; here the step runs on the library's own prefill cache and eight layers,
+# so its inputs carry the saturated ~1-ulp bf16 difference and router logits of
+# size ~0.6 differ by a few 1e-3.  The band is set from that error.
+STEP_BAND = 1e-2
 # K/V cache rows after several layers.  Both sides round to bf16 at the same
 # points, but once their pre-rounding values differ by a fraction of an ulp some
 # roundings flip, and each flip seeds larger differences downstream: the
@@ -30,6 +36,7 @@ ENT_ABS = 1e-2
 # relative).  Rows are held to a median of 1e-2 and a 2e-2 tail (~5 ulp) for at
 # most 5% of rows; the step's own bound is on the logits.
 CACHE_ROW_TAIL = 2e-2
+NEAR_TIE = 1e-2
 
 
 def _ent_tol(h):
@@ -56,7 +63,7 @@ def _cache_rows(dec, st, ocfg, lo, hi, req=0):
     exceeds the bf16 tolerance).  A position whose routing flipped at a near-tie
     in some layer carries a legitimately different hidden state (and K/V) from
     then on, so the check is per position, not an aggregate norm."""
-    out = []
+    out, over = [], []
     for l in range(ocfg.n_layers):
         k, vt = dec.kv_views(req, l)
         kg = k[:, lo:hi, :].float().cpu().numpy().transpose(1, 0, 2).reshape(hi - lo, -1)
@@ -66,16 +73,31 @@ def _cache_rows(dec, st, ocfg, lo, hi, req=0):
         rows = np.array([max(rel_l2(kg[i], ko[i]), rel_l2(vg[i], vo[i])) for i in range(hi - lo)])
         out.append((max(rel_l2(kg, ko), rel_l2(vg, vo)), float(np.mean(rows > CACHE_ROW_TAIL)),
                     float(np.median(rows))))
-    return out
+        over.append(rows > CACHE_ROW_TAIL)
+    return out, over
 
 
-def _check_cache(dec, st, ocfg, lo, hi, what):
-    stats = _cache_rows(dec, st, ocfg, lo, hi)
+def _check_cache(dec, st, ocfg, lo, hi, what, traces=None):
+    """Median row error <= 1e-2 in every layer.  Rows beyond CACHE_ROW_TAIL at
+    layer l must be explained: with the oracle's traces, by a router near-tie
+    (k-th - (k+1)-th logit gap < NEAR_TIE) of that row in an earlier layer (its
+    expert set may legitimately differ, and with it everything after); at most
+    0.5% of rows may be unexplained.  Without traces, at most 5% of rows."""
+    stats, over = _cache_rows(dec, st, ocfg, lo, hi)
+    flagged = np.zeros(hi - lo, dtype=bool)
     for l, (tot, frac, med) in enumerate(stats):
-        log("mid: %s layer %d: rel L2 %.2e, median row %.2e, rows over %.0e: %.1f%%"
-            % (what, l, tot, med, CACHE_ROW_TAIL, 100 * frac))
+        unexplained = over[l] & ~flagged
+        log("mid: %s layer %d: rel L2 %.2e, median row %.2e, rows over %.0e: %.1f%% (%d not after a near-tie)"
+            % (what, l, tot, med, CACHE_ROW_TAIL, 100 * frac, int(unexplained.sum())))
+        assert med <= 1e-2, (l, med)
+        if traces is not None:
+            assert unexplained.mean() <= 0.005, (l, int(unexplained.sum()))
+            if traces[l].router_logits is not None:   # the last layer's FFN is skipped
+                gap = topk_gap(traces[l].router_logits.astype(np.float32), ocfg.top_k)
+                flagged |= gap < NEAR_TIE
+        else:
+            assert frac <= 0.05, (l, frac)
     assert stats[0][0] < 1e-3, stats[0]     # layer 0 sees only exact inputs (embeddings)
-    assert all(med <= 1e-2 and frac <= 0.05 for _, frac, med in stats), stats
 
 
 def test_mid_prefill_steps_commit(setup):
@@ -86,13 +108,13 @@ def test_mid_prefill_steps_commit(setup):
     log("mid: prefill %d tokens" % len(prompt))
     dec.dg_prefill(0, prompt, seed)
     st = oracle.new_request(ocfg, seed, W.max_ctx)
-    oracle.prefill(st, prompt, ocfg, ow, prec)
-    _check_cache(dec, st, ocfg, 0, len(prompt), "prefill")
+    _, traces = oracle.prefill(st, prompt, ocfg, ow, prec, keep_traces=True)
+    _check_cache(dec, st, ocfg, 0, len(prompt), "prefill", traces)
     scfg = oracle.SamplerConfig(W.tau, W.max_steps)
     stats = {}
     for s in range(STEPS):
         r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16,
-                                     stats=stats)
+                                     stats=stats, band=STEP_BAND)
         assert info["n_accepted"] == 1 and info["n_open"] == 255 - s   # random weights: H >> tau
         log("mid: step %d ok (resync %s)" % (s + 1, resync))
     log("mid: per-step max entropy error %s, router-flip rows %s, argmax flips %s"
@@ -102,11 +124,12 @@ def test_mid_prefill_steps_commit(setup):
     dec.dg_set_canvas(0, st.ids, st.accepted, st.step, st.block)
     ids_g = dec.dg_commit_block(0)
     P = st.P
-    ids_o = oracle.commit_block(st, ocfg, ow, prec)
+    ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
     assert np.array_equal(ids_g, ids_o)
-    _check_cache(dec, st, ocfg, P, P + 256, "commit")
+    _check_cache(dec, st, ocfg, P, P + 256, "commit", ctraces)
     assert dec.dg_get_request(0)["committed"] == P + 256
     # First step of block 1: a fresh canvas drawn at (seed, block 1, step 0).
-    r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16)
+    r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16,
+                                 band=STEP_BAND)
     assert info["block"] == 1 and info["step"] == 1
     dec.close()
