@@ -98,6 +98,7 @@ struct dg_ctx {
   int32_t* info_dev = nullptr;
   int32_t* tap_ids = nullptr;
   float* tap_gates = nullptr;
+  float* tap_logits = nullptr;  // router logits of every layer of the last step [L][rows_step][E]
   double* inv_freq = nullptr;
   int32_t* ids_stage = nullptr;
   float* xg = nullptr;  // gathered rows for the logits tap [rows_step][d]
@@ -255,6 +256,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->info_dev = cv.take<int32_t>(m.max_requests * 4 * 4);
   c->tap_ids = cv.take<int32_t>((size_t)m.n_layers * Rs * k * 4);
   c->tap_gates = cv.take<float>((size_t)m.n_layers * Rs * k * 4);
+  c->tap_logits = cv.take<float>((size_t)m.n_layers * Rs * E * 4);
   c->inv_freq = cv.take<double>(m.head_dim / 2 * 8);
   c->ids_stage = cv.take<int32_t>(Tm * 4);
   c->xg = cv.take<float>(Rs * d * 4);
@@ -312,11 +314,19 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
 // Row ranges per weight tile for a dense launch with nblk tiles over M rows: enough
 // blocks to give every CU one (256), at least 16 rows per block.  The extra reads
 // of a tile come from L2 (see the row split in k_ws).
+#ifndef DG_DENSE_BLOCKS
+#define DG_DENSE_BLOCKS 256
+#endif
 int dense_msplit(int nblk, int M) {
-  int ms = (256 + nblk - 1) / nblk;
+  const int padded = (nblk + 7) / 8 * 8;
+  int ms = (DG_DENSE_BLOCKS + padded - 1) / padded;
   ms = std::min(ms, std::max(1, M / 16));
   return std::max(ms, 1);
 }
+
+// Grid of a dense launch: with a row split, tiles are dealt to XCDs in groups of
+// 8 (see k_ws), so the tile count is padded to a multiple of 8.
+int dense_grid(int nblk, int msplit) { return msplit > 1 ? (nblk + 7) / 8 * 8 * msplit : nblk; }
 void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W0, const void* W1, int N, void* out,
                   int ldo) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
@@ -335,7 +345,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   const int nblk = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, M);
-  dg_launch_ws(epi, a, nblk * a.msplit, c->stream);
+  dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), c->stream);
 }
 
 void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, const void* W1, size_t wgs, int K, int N,
@@ -389,7 +399,7 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   const int nblk = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64;
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, rows);
-  dg_launch_ws(WS_EPI_ROPE_QKV, a, nblk * a.msplit, c->stream);
+  dg_launch_ws(WS_EPI_ROPE_QKV, a, dense_grid(nblk, a.msplit), c->stream);
 }
 
 // Fused LM head over the rows of c->hn (count *n_dev <= max_rows): per-row
@@ -439,15 +449,16 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
                                        m.d_model, c->x, m.d_model));
 }
 
-// FFN half of layer l over `rows` rows in c->x; routing written to ids/gates.
-void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates) {
+// FFN half of layer l over `rows` rows in c->x; routing written to ids/gates,
+// router logits to rlog ([rows][E] fp32).
+void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlog) {
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, s));
   if (c->dtype == DG_F32) {
-    KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, c->rlogits, m.n_experts, s);
-                            dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s));
+    KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, rlog, m.n_experts, s);
+                            dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s));
     KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s));
     KT(c, DG_KF_EXPERT_UP, dg_launch_expert_up(c->dtype, c->xn, rows, m.d_model, m.n_experts, m.top_k, m.expert_hidden, w.w1, w.w3,
                                                c->counts, c->offsets, c->perm, c->hbuf, s));
@@ -456,9 +467,9 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates) {
     KT(c, DG_KF_SHARED_UP, dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s));
     KT(c, DG_KF_SHARED_DOWN, dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s));
   } else {
-    KT(c, DG_KF_ROUTER, launch_dense(c, WS_EPI_STORE_F32, c->xn, rows, m.d_model, w.router, nullptr, m.n_experts, c->rlogits,
+    KT(c, DG_KF_ROUTER, launch_dense(c, WS_EPI_STORE_F32, c->xn, rows, m.d_model, w.router, nullptr, m.n_experts, rlog,
                                      m.n_experts);
-                            dg_launch_topk(c->rlogits, rows, m.n_experts, m.top_k, ids, gates, s));
+                            dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
     KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s);
                              dg_launch_ws_units(c->counts, m.n_experts, nb_up, c->units_up, c->n_units, nb_dn, c->units_dn,
@@ -494,7 +505,8 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
     attn_half(c, l, slots, rows, causal);
     int32_t* ids = tap ? c->tap_ids + (size_t)l * c->rows_step * m.top_k : c->rids;
     float* gates = tap ? c->tap_gates + (size_t)l * c->rows_step * m.top_k : c->rgates;
-    ffn_half(c, l, rows, ids, gates);
+    float* rlog = tap ? c->tap_logits + (size_t)l * c->rows_step * m.n_experts : c->rlogits;
+    ffn_half(c, l, rows, ids, gates, rlog);
   }
 }
 
@@ -851,6 +863,17 @@ dg_status dg_last_step_rows(dg_ctx* c, int32_t* n_rows, float* entropy, float* l
   return DG_OK;
 }
 
+dg_status dg_last_step_router_logits(dg_ctx* c, float* logits) {
+  if (!c || !logits) return fail(c, DG_ERR_INVALID_ARG, "null argument");
+  if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
+  const size_t per = (size_t)c->last_rows * c->cfg.n_experts;
+  for (int l = 0; l < c->cfg.n_layers; ++l)
+    HIPCK(c, hipMemcpyAsync(logits + l * per, c->tap_logits + (size_t)l * c->rows_step * c->cfg.n_experts, per * 4,
+                            hipMemcpyDeviceToHost, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  return DG_OK;
+}
+
 dg_status dg_last_step_logits(dg_ctx* c, const int32_t* rows_list, int32_t n, float* logits_dev) {
   if (!c) return DG_ERR_INVALID_ARG;
   if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
@@ -889,7 +912,7 @@ dg_status dg_op_moe(dg_ctx* c, int32_t layer, float* x_dev, int32_t t, int32_t* 
   if (!x_dev || t <= 0 || t > c->rows_max) return fail(c, DG_ERR_INVALID_ARG, "bad rows");
   const size_t bytes = (size_t)t * c->cfg.d_model * 4;
   HIPCK(c, hipMemcpyAsync(c->x, x_dev, bytes, hipMemcpyDeviceToDevice, c->stream));
-  ffn_half(c, layer, t, c->rids, c->rgates);
+  ffn_half(c, layer, t, c->rids, c->rgates, c->rlogits);
   LAUNCHCK(c);
   HIPCK(c, hipMemcpyAsync(x_dev, c->x, bytes, hipMemcpyDeviceToDevice, c->stream));
   const size_t kb = (size_t)t * c->cfg.top_k * 4;

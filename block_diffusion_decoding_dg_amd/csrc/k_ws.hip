@@ -26,14 +26,34 @@
 
 namespace {
 
-constexpr int BK = 64;    // reduction elements per chunk
+#ifndef DG_WS_KSUB
+#define DG_WS_KSUB 1
+#endif
 constexpr int NWAVE = 8;  // waves per block
 constexpr int NT = 64 * NWAVE;
 constexpr int MTW = 2;    // m-tiles per wave per pass
-constexpr int RING = 4;   // weight chunks in flight per thread
 constexpr int PASS_ROWS = NWAVE * MTW * 16;
+// A chunk is KSUB sub-chunks of 64 reduction elements (128 bytes of each weight
+// row per sub-chunk); one barrier per chunk.  ring_depth(KSUB) chunks are in
+// flight per thread.
+constexpr int KSUB_PROJ = DG_WS_KSUB;  // projections and experts
+constexpr int KSUB_LM = DG_WS_KSUB < 2 ? DG_WS_KSUB : 2;  // LM head (128 weight rows per block)
+#ifndef DG_WS_RING1
+#define DG_WS_RING1 4
+#endif
+constexpr int ring_depth(int ksub) { return ksub == 1 ? DG_WS_RING1 : 2; }
 
-__device__ __forceinline__ int lds_slot(int row, int seg) { return row * 8 + (seg ^ (row & 7)); }
+// LDS slot (16-byte units) of segment `seg` (0 .. 8 KSUB - 1) of weight row `row`:
+// XOR swizzle of the segment within each 128-byte sub-row.
+template <int KSUB>
+__device__ __forceinline__ int lds_slot(int row, int seg) {
+  return row * (8 * KSUB) + (seg & ~7) + ((seg & 7) ^ (row & 7));
+}
+
+template <int N>
+struct Segs {
+  uint4 v[N];
+};
 
 // Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue.
 template <int EPI, int NTN>
@@ -70,84 +90,106 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
 
 // Streams the weight tile of one pass through LDS and accumulates this wave's MA
 // active m-tiles (0, 1 or 2).  The loop body is branch-free: the chunk count is
-// padded to a multiple of the ring depth, chunks past the end put zeros in LDS
-// (their products add nothing) and every load address is clamped to valid
+// padded to a multiple of the ring depth, sub-chunks past the end put zeros in
+// LDS (their products add nothing) and every load address is clamped to valid
 // memory, so the number of loads in flight is the same in every iteration and the
 // compiler can wait for exactly the oldest one.  All variants execute the same
 // barriers.
-template <int NTN, int MA>
-__device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8], const char* gsrc0, const char* gsrc1, int slot0,
-                                          int slot1, const char* const (&ap)[MTW], int nk, int lane,
-                                          v4f (&acc)[MTW][NTN]) {
-  constexpr int NL = NTN / 4;
-  uint4 r0a, r0b, r1a, r1b, r2a, r2b, r3a, r3b;
-  r0a = *(const uint4*)(gsrc0 + min(0, nk - 1) * 128);
-  r1a = *(const uint4*)(gsrc0 + min(1, nk - 1) * 128);
-  r2a = *(const uint4*)(gsrc0 + min(2, nk - 1) * 128);
-  r3a = *(const uint4*)(gsrc0 + min(3, nk - 1) * 128);
-  if constexpr (NL == 2) {
-    r0b = *(const uint4*)(gsrc1 + min(0, nk - 1) * 128);
-    r1b = *(const uint4*)(gsrc1 + min(1, nk - 1) * 128);
-    r2b = *(const uint4*)(gsrc1 + min(2, nk - 1) * 128);
-    r3b = *(const uint4*)(gsrc1 + min(3, nk - 1) * 128);
-  }
-  v8s af0[MTW][2], af1[MTW][2];
+template <int NTN, int KSUB, int MA>
+__device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], const char* const (&gsrc)[NTN * KSUB / 4],
+                                          const int (&slot)[NTN * KSUB / 4], const int (&sub)[NTN * KSUB / 4],
+                                          const char* const (&ap)[MTW], int nk64, int lane, v4f (&acc)[MTW][NTN]) {
+  constexpr int NSEG = NTN * KSUB / 4;  // 16-byte weight segments per thread per chunk
+  constexpr int RING = ring_depth(KSUB);
+  const int nchunk = (nk64 + KSUB - 1) / KSUB;
+  // Ring slots; slot q holds chunk c with c % RING == q.
+  static_assert(RING == 2 || RING == 4 || RING == 8, "ring depth");
+  Segs<NSEG> R0, R1, R2, R3, R4, R5, R6, R7;
+  auto fetch = [&](Segs<NSEG>& R, int c) {
 #pragma unroll
-  for (int j = 0; j < MA; ++j) {
-    af0[j][0] = *(const v8s*)(ap[j]);
-    af0[j][1] = *(const v8s*)(ap[j] + 64);
-  }
-  auto chunk = [&](auto JR, uint4& Ra, uint4& Rb, int c) {
-    constexpr int jr = decltype(JR)::value;
-    constexpr int st = jr & 1;  // LDS stage == c & 1 (c0 is a multiple of 4)
-    v8s(&acur)[MTW][2] = (jr & 1) ? af1 : af0;
-    v8s(&anxt)[MTW][2] = (jr & 1) ? af0 : af1;
-    // Chunks past the end store zeros: a mask on the values (a conditional between
-    // two lvalues would make the compiler select between their addresses and keep
-    // the ring in scratch memory).
-    const uint32_t live = c < nk ? 0xffffffffu : 0u;
-    sW[st][slot0] = make_uint4(Ra.x & live, Ra.y & live, Ra.z & live, Ra.w & live);
-    if constexpr (NL == 2) sW[st][slot1] = make_uint4(Rb.x & live, Rb.y & live, Rb.z & live, Rb.w & live);
-    __syncthreads();
-    const int cr = min(c + RING, nk - 1);
-    Ra = *(const uint4*)(gsrc0 + cr * 128);
-    if constexpr (NL == 2) Rb = *(const uint4*)(gsrc1 + cr * 128);
-    const int cn = min(c + 1, nk - 1);
-#pragma unroll
-    for (int j = 0; j < MA; ++j) {
-      anxt[j][0] = *(const v8s*)(ap[j] + cn * 128);
-      anxt[j][1] = *(const v8s*)(ap[j] + cn * 128 + 64);
+    for (int i = 0; i < NSEG; ++i) {
+      const int kc = min(c * KSUB + sub[i], nk64 - 1);
+      R.v[i] = *(const uint4*)(gsrc[i] + kc * 128);
     }
+  };
+  fetch(R0, 0);
+  fetch(R1, 1);
+  if constexpr (RING >= 4) {
+    fetch(R2, 2);
+    fetch(R3, 3);
+  }
+  if constexpr (RING == 8) {
+    fetch(R4, 4);
+    fetch(R5, 5);
+    fetch(R6, 6);
+    fetch(R7, 7);
+  }
+  // Activation fragments, double-buffered by chunk parity.
+  v8s af0[MTW][2 * KSUB], af1[MTW][2 * KSUB];
+  auto fetch_a = [&](v8s (&A)[MTW][2 * KSUB], int c) {
+#pragma unroll
+    for (int j = 0; j < MA; ++j)
+#pragma unroll
+      for (int q = 0; q < 2 * KSUB; ++q) {
+        const int kc = min(c * KSUB + q / 2, nk64 - 1);
+        A[j][q] = *(const v8s*)(ap[j] + kc * 128 + (q & 1) * 64);
+      }
+  };
+  fetch_a(af0, 0);
+  auto chunk = [&](auto JR, Segs<NSEG>& R, int c) {
+    constexpr int jr = decltype(JR)::value;
+    constexpr int st = jr & 1;  // LDS stage == c & 1 (c0 is a multiple of RING, which is even)
+    v8s(&acur)[MTW][2 * KSUB] = (jr & 1) ? af1 : af0;
+    v8s(&anxt)[MTW][2 * KSUB] = (jr & 1) ? af0 : af1;
+    // Sub-chunks past the end store zeros: a mask on the values (a conditional
+    // between two lvalues would make the compiler select between their addresses
+    // and keep the ring in scratch memory).
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      const uint32_t live = c * KSUB + sub[i] < nk64 ? 0xffffffffu : 0u;
+      sW[st][slot[i]] = make_uint4(R.v[i].x & live, R.v[i].y & live, R.v[i].z & live, R.v[i].w & live);
+    }
+    __syncthreads();
+    fetch(R, c + RING);
+    fetch_a(anxt, c + 1);
     if constexpr (MA > 0) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int q = 0; q < 2 * KSUB; ++q) {
         v8s wf[NTN];
 #pragma unroll
         for (int n = 0; n < NTN; ++n) {
-          const uint4 u = sW[st][lds_slot(n * 16 + (lane & 15), s * 4 + (lane >> 4))];
+          const uint4 u = sW[st][lds_slot<KSUB>(n * 16 + (lane & 15), q * 4 + (lane >> 4))];
           wf[n] = *reinterpret_cast<const v8s*>(&u);
         }
 #pragma unroll
         for (int j = 0; j < MA; ++j)
 #pragma unroll
           for (int n = 0; n < NTN; ++n)
-            acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[j][s], wf[n], acc[j][n], 0, 0, 0);
+            acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[j][q], wf[n], acc[j][n], 0, 0, 0);
       }
     }
   };
-  for (int c0 = 0; c0 < nk; c0 += RING) {
-    chunk(std::integral_constant<int, 0>{}, r0a, r0b, c0);
-    chunk(std::integral_constant<int, 1>{}, r1a, r1b, c0 + 1);
-    chunk(std::integral_constant<int, 2>{}, r2a, r2b, c0 + 2);
-    chunk(std::integral_constant<int, 3>{}, r3a, r3b, c0 + 3);
+  for (int c0 = 0; c0 < nchunk; c0 += RING) {
+    chunk(std::integral_constant<int, 0>{}, R0, c0);
+    chunk(std::integral_constant<int, 1>{}, R1, c0 + 1);
+    if constexpr (RING >= 4) {
+      chunk(std::integral_constant<int, 2>{}, R2, c0 + 2);
+      chunk(std::integral_constant<int, 3>{}, R3, c0 + 3);
+    }
+    if constexpr (RING == 8) {
+      chunk(std::integral_constant<int, 4>{}, R4, c0 + 4);
+      chunk(std::integral_constant<int, 5>{}, R5, c0 + 5);
+      chunk(std::integral_constant<int, 6>{}, R6, c0 + 6);
+      chunk(std::integral_constant<int, 7>{}, R7, c0 + 7);
+    }
   }
 }
 
-template <int EPI, int NTN>
+template <int EPI, int NTN, int KSUB>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   constexpr int BN = 16 * NTN;
-  constexpr int NL = NTN / 4;  // 16-byte segments per thread per chunk
-  __shared__ uint4 sW[2][BN * 8];
+  constexpr int NSEG = NTN * KSUB / 4;  // 16-byte segments per thread per chunk
+  __shared__ uint4 sW[2][BN * 8 * KSUB];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int g = 0, nb = blockIdx.x, ms = 0;
   if (a.units) {
@@ -156,19 +198,15 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
     g = code >> 16;
     nb = code & 0xffff;
   } else if (a.msplit > 1) {
-    // Row split of a dense launch.  When the n-blocks come in groups of 8, the
-    // blocks sharing a weight tile are 8 launch slots apart, i.e. on the same XCD
-    // (work-groups are dealt to the 8 XCDs in turn) and started close together,
-    // so the tile crosses HBM once and the other row ranges read it from L2.
-    const int b = blockIdx.x;
-    if (a.nblk % 8 == 0) {
-      const int lo = b % 8, rest = b / 8;
-      ms = rest % a.msplit;
-      nb = (rest / a.msplit) * 8 + lo;
-    } else {
-      ms = b % a.msplit;
-      nb = b / a.msplit;
-    }
+    // Row split of a dense launch.  Work-groups are dealt to the 8 XCDs in turn
+    // (block b runs on XCD b % 8), so tile nb is given to XCD nb % 8 and its
+    // msplit row ranges to consecutive slots of that XCD: they start together and
+    // share that XCD's L2, and the tile crosses HBM once.  The grid is padded to
+    // 8 * ceil(nblk / 8) * msplit; padding blocks exit at once.
+    const int b = blockIdx.x, x = b % 8, j = b / 8;
+    ms = j % a.msplit;
+    nb = x + 8 * (j / a.msplit);
+    if (nb >= a.nblk) return;
   }
   int cnt = a.counts ? a.counts[g] : (a.M_dev ? *a.M_dev : a.M);
   int row0 = 0;
@@ -179,18 +217,19 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   }
   if (cnt <= 0) return;  // uniform over the block
   const int off = a.counts ? a.offsets[g] : 0;
-  const int nk = a.K / BK;
+  const int nk64 = a.K / 64;  // 64-element sub-chunks of the reduction
 
-  // This thread's 16-byte segments of every weight chunk (the second only when
-  // NTN == 8).  Named scalars rather than arrays keep them in registers.
-  const char* gsrc0 = (const char*)weight_row<EPI, NTN>(a, g, nb, tid >> 3) + (tid & 7) * 16;
-  const int slot0 = lds_slot(tid >> 3, tid & 7);
-  const char* gsrc1 = gsrc0;
-  int slot1 = slot0;
-  if constexpr (NL == 2) {
-    const int sid = tid + NT;
-    gsrc1 = (const char*)weight_row<EPI, NTN>(a, g, nb, sid >> 3) + (sid & 7) * 16;
-    slot1 = lds_slot(sid >> 3, sid & 7);
+  // This thread's 16-byte segments of every weight chunk: segment id
+  // tid + NT i -> weight row id / (8 KSUB), segment id % (8 KSUB) within the
+  // chunk's KSUB * 128 bytes of that row (sub-chunk segment / 8).
+  const char* gsrc[NSEG];
+  int slot[NSEG], sub[NSEG];
+#pragma unroll
+  for (int i = 0; i < NSEG; ++i) {
+    const int sid = tid + NT * i, wr = sid / (8 * KSUB), sg = sid % (8 * KSUB);
+    gsrc[i] = (const char*)weight_row<EPI, NTN>(a, g, nb, wr) + (sg & 7) * 16;
+    slot[i] = lds_slot<KSUB>(wr, sg);
+    sub[i] = sg >> 3;
   }
 
   const int npass = (cnt + PASS_ROWS - 1) / PASS_ROWS;
@@ -216,9 +255,9 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
       for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (mt_act == 0) ws_stream<NTN, 0>(sW, gsrc0, gsrc1, slot0, slot1, ap, nk, lane, acc);
-    else if (mt_act == 1) ws_stream<NTN, 1>(sW, gsrc0, gsrc1, slot0, slot1, ap, nk, lane, acc);
-    else ws_stream<NTN, 2>(sW, gsrc0, gsrc1, slot0, slot1, ap, nk, lane, acc);
+    if (mt_act == 0) ws_stream<NTN, KSUB, 0>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else if (mt_act == 1) ws_stream<NTN, KSUB, 1>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else ws_stream<NTN, KSUB, 2>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
 
     // Epilogue.
     if constexpr (EPI == WS_EPI_LM_STATS) {
@@ -372,12 +411,12 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
   switch (epi) {
-    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM><<<grid, NT, 0, s>>>(a); break;
     default: break;
   }
 }

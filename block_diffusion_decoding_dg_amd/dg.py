@@ -9,7 +9,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdg.so")
+# DG_LIBRARY selects another build of the same library (e.g. one compiled with
+# different tile parameters); the default is the in-tree build.
+LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_PKG, "libdg.so")
 
 DG_OK, DG_ERR_INVALID_ARG, DG_ERR_WORKSPACE, DG_ERR_STATE, DG_ERR_CAPACITY, DG_ERR_HIP, DG_ERR_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5, -6
@@ -17,7 +19,7 @@ DG_F32, DG_BF16 = 0, 1
 
 EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "dg_commit_block", "dg_generate",
            "dg_destroy", "dg_last_error", "dg_get_request", "dg_get_canvas", "dg_set_canvas", "dg_set_committed",
-           "dg_last_step_rows", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
+           "dg_last_step_rows", "dg_last_step_router_logits", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
            "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read")
 
 KERNEL_FAMILIES = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "out_proj": 5, "router": 6, "permute": 7,
@@ -97,6 +99,7 @@ def load():
         "dg_set_canvas": [P, I32, P, P, I32, I32],
         "dg_set_committed": [P, I32, I32, U64],
         "dg_last_step_rows": [P, P, P, P, P, P, P],
+        "dg_last_step_router_logits": [P, P],
         "dg_last_step_logits": [P, P, I32, P],
         "dg_op_attention": [P, I32, I32, P, I32, I32, I32],
         "dg_op_moe": [P, I32, P, I32, P, P],
@@ -264,6 +267,12 @@ class Decoder:
         m = n.value
         return {"rows": m, "entropy": ent[:m], "lse": lse[:m], "argmax": am[:m],
                 "router_ids": rid[:L * m * k].reshape(L, m, k), "router_gates": rg[:L * m * k].reshape(L, m, k)}
+
+    def dg_last_step_router_logits(self, rows):
+        """[n_layers][rows][n_experts] fp32 router logits of the last step."""
+        out = np.zeros((self.cfg.n_layers, rows, self.cfg.n_experts), dtype=np.float32)
+        self._check(self.lib.dg_last_step_router_logits(self.ctx, _np_ptr(out)))
+        return out
 
     def dg_last_step_logits(self, rows):
         r = np.ascontiguousarray(rows, dtype=np.int32)

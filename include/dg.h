@@ -267,6 +267,13 @@ dg_status dg_last_step_rows(dg_ctx* ctx, int32_t* n_rows, float* entropy, float*
                             int32_t* argmax, int32_t* router_ids, float* router_gates);
 
 /*
+ * Router logits (fp32, before top-k) of every layer of the last
+ * dg_denoise_step: logits (host) receives [n_layers][rows][n_experts], rows as
+ * in dg_last_step_rows.  Errors: DG_ERR_STATE before the first step.
+ */
+dg_status dg_last_step_router_logits(dg_ctx* ctx, float* logits);
+
+/*
  * LM-head logits of the last step's final hidden rows: for each of the n
  * listed rows (indices as in dg_last_step_rows), vocab fp32 logits to
  * logits_dev (device, [n][vocab]).  Same normalisation and matrix-core path
