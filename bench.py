@@ -192,8 +192,17 @@ def main():
     log("bench: prefill %d x %d tokens" % (R, w.prompt_len))
     prefill_ms = prefill_all()
     log("bench: prefill %.1f ms; warmup %d steps" % (prefill_ms, W))
+    # Experts touched per layer, sampled on the untimed warmup steps (the routing
+    # of a canvas changes little from step to step) and on the last timed step.
+    touched_samples = []
+
+    def sample_touched():
+        rids = dec.dg_last_step_rows()["router_ids"]
+        touched_samples.append([int(np.unique(rids[l]).size) for l in range(w.n_layers)])
+
     for _ in range(W):
         dec.dg_denoise_step()
+        sample_touched()
     prefill_ms = prefill_all()  # reset to block 0, step 0
 
     dec.dg_kernel_timer(args.kernel)
@@ -223,10 +232,8 @@ def main():
     kt_ms, kt_n = dec.dg_kernel_timer_read()
     elapsed = t1 - t0
 
-    # touched experts per layer of the last step (random-init routers touch all of them)
-    rows_info = dec.dg_last_step_rows()
-    rids = rows_info["router_ids"]
-    touched = [int(np.unique(rids[l]).size) for l in range(w.n_layers)]
+    sample_touched()
+    touched = [float(np.mean([t[l] for t in touched_samples])) for l in range(w.n_layers)]
     dec.close()
 
     # Algorithmic bytes and FLOPs of every timed step, from its block and its open rows.
@@ -277,7 +284,8 @@ def main():
                      "launch_ms": launch_ms, "launches": kt_n, "bytes_per_launch": bpl},
         "step_roofline": {"bytes_per_step": mean_bytes, "flops_per_step": mean_flops,
                           "roofline_ms": roof_ms, "frac": roof_ms / ms_per_step,
-                          "touched_experts_per_layer": sum(touched) / len(touched)},
+                          "touched_experts_per_layer": sum(touched) / len(touched),
+                          "touched_sampled_steps": len(touched_samples)},
     }
     if args.kernel != DOMINANT:
         out["roofline"]["achieved"] = None

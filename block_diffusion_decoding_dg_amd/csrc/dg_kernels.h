@@ -118,7 +118,7 @@ struct WsArgs {
   const int32_t* offsets; // grouped: first position of each group in perm
   const int32_t* perm;    // grouped: pair index of each row; activation row = pair / kdiv, output row = pair
   int kdiv;
-  const int32_t* units;   // grouped: work list (group << 16 | n-block), length *n_units
+  const int32_t* units;   // grouped: work list (group << 24 | part << 16 | n-block), length *n_units
   const int32_t* n_units;
   void* out;
   int ldo;
@@ -129,7 +129,18 @@ struct WsArgs {
   DgSegs segs;
 };
 
+// Grouped launches: rows per unit of work (one pass of the kernel), and the
+// code of an empty slot of a work list.
+#define DG_WS_GROUP_ROWS 128
+#define DG_WS_UNIT_NONE 0xffffffffu
+// Slots of a grouped work list: parts * ceil8(nblk), where parts <= E +
+// rows * k / DG_WS_GROUP_ROWS bounds the number of (group, row part) pairs.
+inline int dg_ws_unit_slots(int E, int pairs, int nblk) {
+  return (E + (pairs + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS) * ((nblk + 7) & ~7);
+}
+
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);
-// Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b).
+// Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b);
+// each list needs dg_ws_unit_slots(E, rows * k, nblk) entries.
 void dg_launch_ws_units(const int32_t* counts, int E, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
                         int32_t* units_b, int32_t* n_b, hipStream_t s);

@@ -79,9 +79,10 @@ struct dg_ctx {
   int32_t* counts = nullptr;
   int32_t* offsets = nullptr;
   int32_t* perm = nullptr;
-  int32_t* units_up = nullptr;   // routed work lists (group << 16 | n-block)
+  int32_t* units_up = nullptr;   // routed work lists (group << 24 | part << 16 | n-block)
   int32_t* units_dn = nullptr;
   int32_t* n_units = nullptr;    // [2]: lengths of the two lists
+  int rows_cap = 0;              // rows of the largest forward pass (sizes the work lists)
   void* hbuf = nullptr;
   void* hs = nullptr;
   float* ybuf = nullptr;
@@ -206,6 +207,8 @@ const char* check_config(const dg_model_config* c) {
   if (c->max_ctx % 64) return "max_ctx must be a multiple of 64";
   if (c->max_ctx < c->canvas_len) return "max_ctx must hold at least one canvas";
   if (c->prefill_chunk < 0) return "prefill_chunk must be >= 0";
+  // a routed work unit names its row part of an expert in 8 bits (128 rows each)
+  if (c->prefill_chunk > 32768) return "prefill_chunk must be <= 32768";
   return nullptr;
 }
 
@@ -237,8 +240,9 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->counts = cv.take<int32_t>(E * 4);
   c->offsets = cv.take<int32_t>(E * 4);
   c->perm = cv.take<int32_t>(Tm * k * 4);
-  c->units_up = cv.take<int32_t>(E * ((m.expert_hidden + 31) / 32) * 4);
-  c->units_dn = cv.take<int32_t>(E * ((m.d_model + 63) / 64) * 4);
+  c->units_up = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.expert_hidden + 31) / 32) * 4);
+  c->units_dn = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.d_model + 63) / 64) * 4);
+  c->rows_cap = Tm;
   c->n_units = cv.take<int32_t>(2 * 4);
   c->hbuf = cv.take<void>(Tm * k * m.expert_hidden * es);
   c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
@@ -311,15 +315,17 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
 // Launch helpers.  bf16 models run the weight-streaming kernel (k_ws.hip); the
 // fp32 model keeps the plain matrix-core kernels.
 
-// Row ranges per weight tile for a dense launch with nblk tiles over M rows: enough
-// blocks to give every CU one (256), at least 16 rows per block.  The extra reads
-// of a tile come from L2 (see the row split in k_ws).
+// Row ranges per weight tile for a dense launch with nblk tiles over M rows: as
+// many blocks as fit one per CU (256), at least 16 rows per block.  The extra
+// reads of a tile come from L2 (see the row split in k_ws).
 #ifndef DG_DENSE_BLOCKS
 #define DG_DENSE_BLOCKS 256
 #endif
 int dense_msplit(int nblk, int M) {
+  // At most DG_DENSE_BLOCKS (one per CU) in all: a block streams its tile at a
+  // rate set by memory latency, and a CU that receives two blocks finishes last.
   const int padded = (nblk + 7) / 8 * 8;
-  int ms = (DG_DENSE_BLOCKS + padded - 1) / padded;
+  int ms = DG_DENSE_BLOCKS / padded;
   ms = std::min(ms, std::max(1, M / 16));
   return std::max(ms, 1);
 }
@@ -368,7 +374,7 @@ void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, c
   a.n_units = n_units;
   a.out = out;
   a.ldo = ldo;
-  dg_launch_ws(epi, a, c->cfg.n_experts * nblk, c->stream);
+  dg_launch_ws(epi, a, dg_ws_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, nblk), c->stream);
 }
 
 void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg) {

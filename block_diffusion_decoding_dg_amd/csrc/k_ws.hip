@@ -5,16 +5,19 @@
 // shared expert, the dense projections and the LM head.
 //
 // A block owns BN = 16 * NTN consecutive weight rows ("n-block") of one group and
-// every activation row of that group, up to 256 per pass over the weights (a group
-// with more rows takes several passes).  Each weight byte therefore crosses HBM
-// once per 256 rows, whatever the routing.  The weight tile streams through a
-// two-stage LDS buffer in chunks of 64 reduction elements (128 bytes per row), fed
-// by a four-deep register prefetch ring (NTN / 4 16-byte segments per thread per
-// chunk, four chunks in flight); the eight waves split the activation rows (m-tile
-// i goes to wave i % 8) and read their own activation fragments straight from
-// global memory one chunk ahead.  The LDS rows are XOR-swizzled in 16-byte units so
-// that both the cooperative stores and the fragment reads are free of bank
-// conflicts.
+// a range of that group's activation rows: a grouped launch cuts each group into
+// parts of at most DG_WS_GROUP_ROWS rows, one unit of work per (group, part,
+// n-block), so that an expert that receives most of the rows does not serialise
+// the launch; a dense launch splits its rows over msplit blocks per n-block.  The
+// blocks that share a weight tile run on the same XCD at the same time, so the
+// tile crosses HBM once and the others read it from that XCD's L2.  The weight tile streams through four
+// LDS stages in chunks of KSUB x 64 reduction elements (128 bytes per row per
+// sub-chunk), fed by a four-slot register ring; each chunk is stored two
+// iterations before it is used (see ws_stream).  The eight waves split the
+// activation rows (m-tile i goes to wave i % 8) and read their own activation
+// fragments straight from global memory three chunks ahead.  The LDS rows are
+// XOR-swizzled in 16-byte units so that both the cooperative stores and the
+// fragment reads are free of bank conflicts.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16): lane l supplies activation row
 // l % 16 and weight row l % 16, each with reduction elements 8 (l / 16) .. +7 of a
@@ -31,17 +34,13 @@ namespace {
 #endif
 constexpr int NWAVE = 8;  // waves per block
 constexpr int NT = 64 * NWAVE;
-constexpr int MTW = 2;    // m-tiles per wave per pass
-constexpr int PASS_ROWS = NWAVE * MTW * 16;
+// MT (template parameter): m-tiles per wave per pass, so a pass covers
+// NWAVE * MT * 16 activation rows.
 // A chunk is KSUB sub-chunks of 64 reduction elements (128 bytes of each weight
-// row per sub-chunk); one barrier per chunk.  ring_depth(KSUB) chunks are in
-// flight per thread.
+// row per sub-chunk); one barrier per chunk (see ws_stream for the pipeline).
 constexpr int KSUB_PROJ = DG_WS_KSUB;  // projections and experts
 constexpr int KSUB_LM = DG_WS_KSUB < 2 ? DG_WS_KSUB : 2;  // LM head (128 weight rows per block)
-#ifndef DG_WS_RING1
-#define DG_WS_RING1 4
-#endif
-constexpr int ring_depth(int ksub) { return ksub == 1 ? DG_WS_RING1 : 2; }
+
 
 // LDS slot (16-byte units) of segment `seg` (0 .. 8 KSUB - 1) of weight row `row`:
 // XOR swizzle of the segment within each 128-byte sub-row.
@@ -54,6 +53,20 @@ template <int N>
 struct Segs {
   uint4 v[N];
 };
+
+// Activation fragments of four consecutive chunks (chunk c in buffer c % 4),
+// selected by a compile-time index.
+template <int MT, int KSUB>
+struct AFrags {
+  v8s b0[MT][2 * KSUB], b1[MT][2 * KSUB], b2[MT][2 * KSUB], b3[MT][2 * KSUB];
+};
+template <int I, int MT, int KSUB>
+__device__ __forceinline__ v8s (&abuf(AFrags<MT, KSUB>& F))[MT][2 * KSUB] {
+  if constexpr (I == 0) return F.b0;
+  else if constexpr (I == 1) return F.b1;
+  else if constexpr (I == 2) return F.b2;
+  else return F.b3;
+}
 
 // Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue.
 template <int EPI, int NTN>
@@ -89,22 +102,35 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
 }
 
 // Streams the weight tile of one pass through LDS and accumulates this wave's MA
-// active m-tiles (0, 1 or 2).  The loop body is branch-free: the chunk count is
-// padded to a multiple of the ring depth, sub-chunks past the end put zeros in
-// LDS (their products add nothing) and every load address is clamped to valid
-// memory, so the number of loads in flight is the same in every iteration and the
-// compiler can wait for exactly the oldest one.  All variants execute the same
-// barriers.
-template <int NTN, int KSUB, int MA>
+// active m-tiles (0 .. MT).
+//
+// Pipeline, with NSTAGE = 4 LDS stages and a ring of 4 register slots.  In
+// iteration c the wave
+//   1. fetches its activation fragments of chunk c + 3 (into buffer (c + 3) % 4),
+//   2. stores weight chunk c + 2 (fetched four iterations earlier) into stage
+//      (c + 2) % 4 and refills that ring slot with chunk c + 6,
+//   3. computes chunk c from stage c % 4 (stored two iterations earlier) and
+//      activation buffer c % 4,
+//   4. meets the block at one barrier.
+// The hardware retires vector loads in issue order, so a wait for one load is a
+// wait for every older load.  Fetching the activations three chunks ahead, before
+// the weight refill of the same iteration, means that the wait for chunk c's
+// activations only covers weight loads that were already needed by earlier
+// stores, and the four-chunk weight prefetch stays four chunks deep.  A stage is
+// rewritten two barriers after its last reader.
+//
+// The loop body is branch-free: the chunk count is padded to a multiple of 4,
+// chunks past the end are stored as zeros (their products add nothing) and every
+// load address is clamped to valid memory, so the number of loads in flight is
+// the same in every iteration and the compiler can wait for exactly the load it
+// needs.  All variants execute the same barriers.
+template <int NTN, int KSUB, int MT, int MA>
 __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], const char* const (&gsrc)[NTN * KSUB / 4],
                                           const int (&slot)[NTN * KSUB / 4], const int (&sub)[NTN * KSUB / 4],
-                                          const char* const (&ap)[MTW], int nk64, int lane, v4f (&acc)[MTW][NTN]) {
+                                          const char* const (&ap)[MT], int nk64, int lane, v4f (&acc)[MT][NTN]) {
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte weight segments per thread per chunk
-  constexpr int RING = ring_depth(KSUB);
   const int nchunk = (nk64 + KSUB - 1) / KSUB;
-  // Ring slots; slot q holds chunk c with c % RING == q.
-  static_assert(RING == 2 || RING == 4 || RING == 8, "ring depth");
-  Segs<NSEG> R0, R1, R2, R3, R4, R5, R6, R7;
+  Segs<NSEG> R0, R1, R2, R3;
   auto fetch = [&](Segs<NSEG>& R, int c) {
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
@@ -112,21 +138,18 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
       R.v[i] = *(const uint4*)(gsrc[i] + kc * 128);
     }
   };
-  fetch(R0, 0);
-  fetch(R1, 1);
-  if constexpr (RING >= 4) {
-    fetch(R2, 2);
-    fetch(R3, 3);
-  }
-  if constexpr (RING == 8) {
-    fetch(R4, 4);
-    fetch(R5, 5);
-    fetch(R6, 6);
-    fetch(R7, 7);
-  }
-  // Activation fragments, double-buffered by chunk parity.
-  v8s af0[MTW][2 * KSUB], af1[MTW][2 * KSUB];
-  auto fetch_a = [&](v8s (&A)[MTW][2 * KSUB], int c) {
+  // Stores chunk c from R into its stage; sub-chunks past the end store zeros (a
+  // mask on the values: a conditional between two lvalues would make the compiler
+  // select between their addresses and keep the ring in scratch memory).
+  auto store = [&](uint4* stage, const Segs<NSEG>& R, int c) {
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      const uint32_t live = c * KSUB + sub[i] < nk64 ? 0xffffffffu : 0u;
+      stage[slot[i]] = make_uint4(R.v[i].x & live, R.v[i].y & live, R.v[i].z & live, R.v[i].w & live);
+    }
+  };
+  AFrags<MT, KSUB> F;
+  auto fetch_a = [&](v8s (&A)[MT][2 * KSUB], int c) {
 #pragma unroll
     for (int j = 0; j < MA; ++j)
 #pragma unroll
@@ -135,30 +158,32 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
         A[j][q] = *(const v8s*)(ap[j] + kc * 128 + (q & 1) * 64);
       }
   };
-  fetch_a(af0, 0);
+  fetch(R0, 0);
+  fetch(R1, 1);
+  fetch(R2, 2);
+  fetch(R3, 3);
+  fetch_a(abuf<0>(F), 0);
+  fetch_a(abuf<1>(F), 1);
+  fetch_a(abuf<2>(F), 2);
+  store(sW[0], R0, 0);
+  store(sW[1], R1, 1);
+  fetch(R0, 4);
+  fetch(R1, 5);
+  __syncthreads();
   auto chunk = [&](auto JR, Segs<NSEG>& R, int c) {
-    constexpr int jr = decltype(JR)::value;
-    constexpr int st = jr & 1;  // LDS stage == c & 1 (c0 is a multiple of RING, which is even)
-    v8s(&acur)[MTW][2 * KSUB] = (jr & 1) ? af1 : af0;
-    v8s(&anxt)[MTW][2 * KSUB] = (jr & 1) ? af0 : af1;
-    // Sub-chunks past the end store zeros: a mask on the values (a conditional
-    // between two lvalues would make the compiler select between their addresses
-    // and keep the ring in scratch memory).
-#pragma unroll
-    for (int i = 0; i < NSEG; ++i) {
-      const uint32_t live = c * KSUB + sub[i] < nk64 ? 0xffffffffu : 0u;
-      sW[st][slot[i]] = make_uint4(R.v[i].x & live, R.v[i].y & live, R.v[i].z & live, R.v[i].w & live);
-    }
-    __syncthreads();
-    fetch(R, c + RING);
-    fetch_a(anxt, c + 1);
+    constexpr int jr = decltype(JR)::value;   // == c % 4 (c0 is a multiple of 4)
+    constexpr int ahead = (jr + 2) & 3;       // stage and ring slot of chunk c + 2
+    fetch_a(abuf<(jr + 3) & 3>(F), c + 3);
+    store(sW[ahead], R, c + 2);
+    fetch(R, c + 6);
     if constexpr (MA > 0) {
+      v8s(&acur)[MT][2 * KSUB] = abuf<jr>(F);
 #pragma unroll
       for (int q = 0; q < 2 * KSUB; ++q) {
         v8s wf[NTN];
 #pragma unroll
         for (int n = 0; n < NTN; ++n) {
-          const uint4 u = sW[st][lds_slot<KSUB>(n * 16 + (lane & 15), q * 4 + (lane >> 4))];
+          const uint4 u = sW[jr][lds_slot<KSUB>(n * 16 + (lane & 15), q * 4 + (lane >> 4))];
           wf[n] = *reinterpret_cast<const v8s*>(&u);
         }
 #pragma unroll
@@ -168,35 +193,32 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
             acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[j][q], wf[n], acc[j][n], 0, 0, 0);
       }
     }
+    __syncthreads();
   };
-  for (int c0 = 0; c0 < nchunk; c0 += RING) {
-    chunk(std::integral_constant<int, 0>{}, R0, c0);
-    chunk(std::integral_constant<int, 1>{}, R1, c0 + 1);
-    if constexpr (RING >= 4) {
-      chunk(std::integral_constant<int, 2>{}, R2, c0 + 2);
-      chunk(std::integral_constant<int, 3>{}, R3, c0 + 3);
-    }
-    if constexpr (RING == 8) {
-      chunk(std::integral_constant<int, 4>{}, R4, c0 + 4);
-      chunk(std::integral_constant<int, 5>{}, R5, c0 + 5);
-      chunk(std::integral_constant<int, 6>{}, R6, c0 + 6);
-      chunk(std::integral_constant<int, 7>{}, R7, c0 + 7);
-    }
+  for (int c0 = 0; c0 < nchunk; c0 += 4) {
+    chunk(std::integral_constant<int, 0>{}, R2, c0);      // slot 2 holds chunk c0 + 2
+    chunk(std::integral_constant<int, 1>{}, R3, c0 + 1);  // slot 3 holds chunk c0 + 3
+    chunk(std::integral_constant<int, 2>{}, R0, c0 + 2);  // slot 0 holds chunk c0 + 4
+    chunk(std::integral_constant<int, 3>{}, R1, c0 + 3);  // slot 1 holds chunk c0 + 5
   }
 }
 
-template <int EPI, int NTN, int KSUB>
+template <int EPI, int NTN, int KSUB, int MT>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   constexpr int BN = 16 * NTN;
+  constexpr int PASS_ROWS = NWAVE * MT * 16;
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte segments per thread per chunk
-  __shared__ uint4 sW[2][BN * 8 * KSUB];
+  __shared__ uint4 sW[4][BN * 8 * KSUB];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int g = 0, nb = blockIdx.x, ms = 0;
+  int part = -1;
   if (a.units) {
     if ((int)blockIdx.x >= *a.n_units) return;
-    const int code = a.units[blockIdx.x];
-    g = code >> 16;
-    nb = code & 0xffff;
+    const uint32_t code = (uint32_t)a.units[blockIdx.x];
+    if (code == DG_WS_UNIT_NONE) return;  // padding of the work list
+    g = (int)(code >> 24);
+    part = (int)((code >> 16) & 0xff);
+    nb = (int)(code & 0xffff);
   } else if (a.msplit > 1) {
     // Row split of a dense launch.  Work-groups are dealt to the 8 XCDs in turn
     // (block b runs on XCD b % 8), so tile nb is given to XCD nb % 8 and its
@@ -210,7 +232,11 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   }
   int cnt = a.counts ? a.counts[g] : (a.M_dev ? *a.M_dev : a.M);
   int row0 = 0;
-  if (a.msplit > 1 && !a.counts) {
+  if (part >= 0) {
+    // Grouped launch: rows part * DG_WS_GROUP_ROWS .. + DG_WS_GROUP_ROWS - 1 of the group.
+    row0 = part * DG_WS_GROUP_ROWS;
+    cnt = min(cnt - row0, DG_WS_GROUP_ROWS);
+  } else if (a.msplit > 1) {
     const int per = ((cnt + a.msplit - 1) / a.msplit + 15) / 16 * 16;
     row0 = ms * per;
     cnt = min(cnt - row0, per);
@@ -237,9 +263,9 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
     const int pbase = pass * PASS_ROWS;
     // Activation rows of this wave's m-tiles (rows row0 + pbase + ... of the group).
     int mt_act = 0;
-    const char* ap[MTW];
+    const char* ap[MT];
 #pragma unroll
-    for (int j = 0; j < MTW; ++j) {
+    for (int j = 0; j < MT; ++j) {
       const int t0 = pbase + (wave + NWAVE * j) * 16;
       if (t0 < cnt) mt_act = j + 1;
       const int r = row0 + min(t0 + (lane & 15), cnt - 1);
@@ -249,15 +275,15 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
       ap[j] = (const char*)((const bf16_t*)a.A + (size_t)arow * a.lda) + (lane >> 4) * 16;
     }
 
-    v4f acc[MTW][NTN];
+    v4f acc[MT][NTN];
 #pragma unroll
-    for (int j = 0; j < MTW; ++j)
+    for (int j = 0; j < MT; ++j)
 #pragma unroll
       for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (mt_act == 0) ws_stream<NTN, KSUB, 0>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else if (mt_act == 1) ws_stream<NTN, KSUB, 1>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else ws_stream<NTN, KSUB, 2>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else if (MT == 1 || mt_act == 1) ws_stream<NTN, KSUB, MT, 1>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else ws_stream<NTN, KSUB, MT, MT>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
 
     // Epilogue.
     if constexpr (EPI == WS_EPI_LM_STATS) {
@@ -265,7 +291,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
       // sum exp(z - max) (z - max), and the argmax (lowest column among equal
       // maxima).  Lane holds columns n * 16 + lane % 16 of rows 4 (lane / 16) + i.
 #pragma unroll
-      for (int j = 0; j < MTW; ++j) {
+      for (int j = 0; j < MT; ++j) {
         if (j >= mt_act) break;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -310,7 +336,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < MTW; ++j) {
+      for (int j = 0; j < MT; ++j) {
         if (j >= mt_act) break;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -378,16 +404,31 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   }
 }
 
-// Work list of the grouped launches: every (group, n-block) of the groups that
-// received rows, groups in increasing order.  One block; E <= 256.
+// Work lists of two grouped launches over the same groups.  A group with c rows
+// is cut into ceil(c / DG_WS_GROUP_ROWS) row parts (one pass of the kernel each),
+// and every (group, part, n-block) is one unit: group << 24 | part << 16 | n-block.
+// The list holds, for each part in group order, ceil8(nblk) slots, n-blocks in
+// order and DG_WS_UNIT_NONE in the padding.  Work-groups are dealt to the 8 XCDs
+// in turn (block u runs on XCD u % 8), so every part of n-block b of a group runs
+// on XCD b % 8 and the parts after the first find that weight tile in its L2.
+// One block; E <= 256.
+__device__ __forceinline__ void ws_fill_units(int32_t* __restrict__ units, int first, int parts, int e, int nblk) {
+  const int stride = (nblk + 7) & ~7;
+  for (int p = 0; p < parts; ++p)
+    for (int b = 0; b < stride; ++b)
+      units[(first + p) * stride + b] = b < nblk ? (int32_t)(((uint32_t)e << 24) | ((uint32_t)p << 16) | (uint32_t)b)
+                                                 : (int32_t)DG_WS_UNIT_NONE;
+}
+
 __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ counts, int E, int nblk_a,
                                                   int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                   int nblk_b, int32_t* __restrict__ units_b,
                                                   int32_t* __restrict__ n_b) {
   __shared__ int s_scan[256];
   const int e = threadIdx.x;
-  const int touched = (e < E && counts[e] > 0) ? 1 : 0;
-  s_scan[e] = touched;
+  const int c = e < E ? counts[e] : 0;
+  const int parts = (c + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+  s_scan[e] = parts;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
     const int v = e >= o ? s_scan[e - o] : 0;
@@ -395,14 +436,12 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
     s_scan[e] += v;
     __syncthreads();
   }
-  const int before = s_scan[e] - touched;  // exclusive prefix
-  if (touched) {
-    for (int b = 0; b < nblk_a; ++b) units_a[before * nblk_a + b] = (e << 16) | b;
-    for (int b = 0; b < nblk_b; ++b) units_b[before * nblk_b + b] = (e << 16) | b;
-  }
+  const int before = s_scan[e] - parts;  // exclusive prefix
+  ws_fill_units(units_a, before, parts, e, nblk_a);
+  ws_fill_units(units_b, before, parts, e, nblk_b);
   if (e == 255) {
-    *n_a = s_scan[255] * nblk_a;
-    *n_b = s_scan[255] * nblk_b;
+    *n_a = s_scan[255] * ((nblk_a + 7) & ~7);
+    *n_b = s_scan[255] * ((nblk_b + 7) & ~7);
   }
 }
 
@@ -411,12 +450,14 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
   switch (epi) {
-    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
+    // The LM head keeps two m-tiles per wave: up to 256 rows in one pass, so the
+    // embedding crosses HBM once per step.
+    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2><<<grid, NT, 0, s>>>(a); break;
     default: break;
   }
 }

@@ -70,7 +70,7 @@ typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  * d_model and expert_hidden multiples of 64; n_q_heads*head_dim and
  * shared_hidden multiples of 64 (bf16) or 16 (f32); vocab a multiple of 128;
  * top_k <= 16; n_experts <= 256; max_requests <= 16; max_ctx a multiple of 64;
- * canvas_len == 256.
+ * canvas_len == 256; prefill_chunk <= 32768.
  */
 typedef struct dg_model_config {
   int32_t vocab;
