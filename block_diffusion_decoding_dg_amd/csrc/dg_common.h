@@ -8,6 +8,7 @@ typedef uint16_t bf16_t;  // raw bf16 bits
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 #define DG_WAVE 64
 

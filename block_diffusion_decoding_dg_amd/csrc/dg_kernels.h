@@ -23,6 +23,8 @@ struct DgShape {
   int32_t d, hq, hkv, hd, max_ctx, vocab;
 };
 
+#define DG_MAX_TOPK 16  // routed experts per token, at most
+
 // dtype: 0 = f32, 1 = bf16 (weights, activations and cache).
 void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, int vocab, float* x,
                      hipStream_t s);
@@ -47,6 +49,11 @@ void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, f
 // Permutation: counts[E], offsets[E], perm[rows*k] (pair index t*k + j, token order per expert).
 void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
                        hipStream_t s);
+// Router top-k, histogram, offsets, permutation and both grouped work lists
+// (dg_launch_ws_units); everything after the top-k in one block for rows <= 2048.
+void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
+                     int32_t* units_b, int32_t* n_b, hipStream_t s);
 // Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
 void dg_launch_expert_up(int dtype, const void* b, int rows, int d, int E, int k, int eh, const void* w1,
                          const void* w3, const int32_t* counts, const int32_t* offsets, const int32_t* perm, void* h,
@@ -55,7 +62,10 @@ void dg_launch_expert_down(int dtype, const void* h, int rows, int d, int E, int
                            const int32_t* counts, const int32_t* offsets, const int32_t* perm, float* y,
                            hipStream_t s);
 // x[t] += sum_j gates[t][j] * y[t*k + j]
-void dg_launch_combine(float* x, const float* y, const float* gates, int rows, int d, int k, hipStream_t s);
+// x[t] += sum_j gates[t][j] y[t k + j] for every row, then (gain given) the
+// RMSNorm of the updated rows into out (model dtype).  d <= 16384, k <= 16.
+void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
+                            const void* gain, float eps, void* out, hipStream_t s);
 // LM head over rows of hn [n][d] (dtype), n from n_dev (<= max_rows): partials then merge.
 void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_rows, int d, const void* embed,
                        int vocab, float* part, int32_t* part_arg, float* ent, float* lse, int32_t* amax,
@@ -137,6 +147,16 @@ struct WsArgs {
 // rows * k / DG_WS_GROUP_ROWS bounds the number of (group, row part) pairs.
 inline int dg_ws_unit_slots(int E, int pairs, int nblk) {
   return (E + (pairs + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS) * ((nblk + 7) & ~7);
+}
+
+// Writes the work-list entries of group e's `parts` row parts, starting at part
+// slot `first`: ceil8(nblk) entries per part, n-blocks in order, then padding.
+__device__ __forceinline__ void dg_fill_units(int32_t* __restrict__ units, int first, int parts, int e, int nblk) {
+  const int stride = (nblk + 7) & ~7;
+  for (int p = 0; p < parts; ++p)
+    for (int b = 0; b < stride; ++b)
+      units[(first + p) * stride + b] = b < nblk ? (int32_t)(((uint32_t)e << 24) | ((uint32_t)p << 16) | (uint32_t)b)
+                                                 : (int32_t)DG_WS_UNIT_NONE;
 }
 
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);

@@ -198,6 +198,7 @@ const char* check_config(const dg_model_config* c) {
     return "bf16: n_q_heads * head_dim and shared_hidden must be multiples of 64";
   if (((c->n_q_heads + 2 * c->n_kv_heads) * hd / 2) % 16) return "(Hq + 2 Hkv) * head_dim / 2 must be a multiple of 16";
   if (c->d_model % 64 || c->d_model % kc) return "d_model must be a multiple of 64";
+  if (c->d_model > 16384) return "d_model must be <= 16384";
   if ((c->n_q_heads * hd) % kc) return "n_q_heads * head_dim must be a multiple of the k-chunk";
   if (c->expert_hidden % 64) return "expert_hidden must be a multiple of 64";
   if (c->shared_hidden % 16 || c->shared_hidden % kc) return "shared_hidden must be a multiple of 16 and the k-chunk";
@@ -436,13 +437,17 @@ void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t
 }
 
 // Attention half of layer l over `rows` rows in c->x.
-void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal) {
+// norm_done: c->xn already holds the normalised rows (fused into the previous
+// layer's combine).
+void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal, bool norm_done = false) {
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
   const DgShape sh = shape_of(c);
   const DgSegs sg = make_segs(c, slots, l, causal);
-  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, s));
+  if (!norm_done)
+    KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps,
+                                           c->xn, s));
   KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
   const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
@@ -456,8 +461,9 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
 }
 
 // FFN half of layer l over `rows` rows in c->x; routing written to ids/gates,
-// router logits to rlog ([rows][E] fp32).
-void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlog) {
+// router logits to rlog ([rows][E] fp32).  next_gain: the RMSNorm gain of the
+// next layer's attention, applied to the updated rows into c->xn by the combine.
+void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlog, const void* next_gain = nullptr) {
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
@@ -474,12 +480,10 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KT(c, DG_KF_SHARED_DOWN, dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s));
   } else {
     KT(c, DG_KF_ROUTER, launch_dense(c, WS_EPI_STORE_F32, c->xn, rows, m.d_model, w.router, nullptr, m.n_experts, rlog,
-                                     m.n_experts);
-                            dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s));
+                                     m.n_experts));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
-    KT(c, DG_KF_PERMUTE, dg_launch_permute(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm, s);
-                             dg_launch_ws_units(c->counts, m.n_experts, nb_up, c->units_up, c->n_units, nb_dn, c->units_dn,
-                                                c->n_units + 1, s));
+    KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
+                                         nb_up, c->units_up, c->n_units, nb_dn, c->units_dn, c->n_units + 1, s));
     KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xn, m.d_model, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
                                          m.d_model, m.expert_hidden, m.top_k, c->units_up, c->n_units, nb_up, c->hbuf,
                                          m.expert_hidden));
@@ -491,28 +495,33 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KT(c, DG_KF_SHARED_DOWN, launch_dense(c, WS_EPI_ADD_F32, c->hs, rows, m.shared_hidden, w.sw2, nullptr, m.d_model, c->x,
                                           m.d_model));
   }
-  KT(c, DG_KF_COMBINE, dg_launch_combine(c->x, c->ybuf, gates, rows, m.d_model, m.top_k, s));
+  KT(c, DG_KF_COMBINE, dg_launch_combine_norm(c->dtype, c->x, c->ybuf, gates, rows, m.d_model, m.top_k, next_gain,
+                                              m.rms_eps, c->xn, s));
 }
 
 // Forward of the rows in c->x through all layers.  kv_only: the last layer only
 // writes its K/V (commit and prefill need nothing else from it).
 void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool causal, bool kv_only, bool tap) {
   const dg_model_config& m = c->cfg;
+  bool xn_ready = false;  // c->xn holds layer l's attention-normalised rows
   for (int l = 0; l < m.n_layers; ++l) {
     const bool last = l == m.n_layers - 1;
     if (last && kv_only) {
-      const DgShape sh = shape_of(c);
       const DgSegs sg = make_segs(c, slots, l, causal);
       const dg_layer_weights& w = c->layers[l];
-      KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps, c->xn, c->stream));
+      if (!xn_ready)
+        KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm,
+                                               m.rms_eps, c->xn, c->stream));
       KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
       break;
     }
-    attn_half(c, l, slots, rows, causal);
+    attn_half(c, l, slots, rows, causal, xn_ready);
     int32_t* ids = tap ? c->tap_ids + (size_t)l * c->rows_step * m.top_k : c->rids;
     float* gates = tap ? c->tap_gates + (size_t)l * c->rows_step * m.top_k : c->rgates;
     float* rlog = tap ? c->tap_logits + (size_t)l * c->rows_step * m.n_experts : c->rlogits;
-    ffn_half(c, l, rows, ids, gates, rlog);
+    const void* next_gain = last ? nullptr : c->layers[l + 1].attn_norm;
+    ffn_half(c, l, rows, ids, gates, rlog, next_gain);
+    xn_ready = next_gain != nullptr;
   }
 }
 

@@ -201,6 +201,14 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
   }
 }
 
+// Two bf16 values (low half first) to two fp16 values: exact over fp16's normal
+// range (bf16 has 8 significant bits); the conversion rounds toward zero, which
+// only touches magnitudes below that range and clamps those above it to 65504.
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+  return *reinterpret_cast<const uint32_t*>(&h);
+}
+
 // bf16 attention with the K and V^T tiles of 32 keys staged in LDS once per
 // block and shared by its four waves (the kernel above reads them once per wave).
 // The next tile is prefetched into registers while the current one is used, and
@@ -211,6 +219,13 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
 // is one conflict-free 16-byte LDS load.  All waves of a block walk the same
 // key tiles; the key range is cut at the largest position among the block's
 // rows when the mask is causal.
+//
+// The probabilities P enter the P V product as fp16 (11 significant bits, round
+// to nearest even) against V converted to fp16 when its tile is staged: a bf16
+// value has 8 significant bits, so the conversion is exact over fp16's normal
+// range; magnitudes below it keep an absolute error under 2^-25 and magnitudes
+// above 65504 are clamped to it.  The running output is rescaled only when some
+// row's maximum moved, and full tiles of a bidirectional step skip the mask.
 template <int HD>
 __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
                                                      int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
@@ -303,8 +318,8 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
     for (int i = 0; i < LV; ++i) {
       const int sid = tid + 256 * i, d = sid >> 2, s4 = sid & 3;
       const int kt = s4 >> 1, g0 = (s4 & 1) * 2, sw = (d >> 1) & 3;
-      v8[d * 8 + (g0 ^ sw) * 2 + kt] = make_uint2(rv[i].x, rv[i].y);        // keys 8 s4 .. +3
-      v8[d * 8 + ((g0 + 1) ^ sw) * 2 + kt] = make_uint2(rv[i].z, rv[i].w);  // keys 8 s4 + 4 .. +7
+      v8[d * 8 + (g0 ^ sw) * 2 + kt] = make_uint2(bf2_to_h2(rv[i].x), bf2_to_h2(rv[i].y));        // keys 8 s4 .. +3
+      v8[d * 8 + ((g0 + 1) ^ sw) * 2 + kt] = make_uint2(bf2_to_h2(rv[i].z), bf2_to_h2(rv[i].w));  // keys 8 s4 + 4 .. +7
     }
   };
 
@@ -338,6 +353,8 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
         }
       }
       float p[2][2][4];
+      // no key of a full tile is masked in a bidirectional step (block-uniform)
+      const bool full = !sg.causal && kb + 32 <= k_hi;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         float tmax = -INFINITY;
@@ -347,50 +364,47 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
           for (int i = 0; i < 4; ++i) {
             const int key = kb + kt * 16 + g4 * 4 + i;
             float sc = st[kt][qt][i] * scale;
-            if (key >= k_hi || (sg.causal && key > qpos[qt])) sc = -INFINITY;
+            if (!full && (key >= k_hi || (sg.causal && key > qpos[qt]))) sc = -INFINITY;
             p[kt][qt][i] = sc;
             tmax = fmaxf(tmax, sc);
           }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mnew = fmaxf(mrun[qt], tmax);
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun[qt] - mnew);
+        // with every score of the row masked so far (mnew = -inf) the exponentials
+        // below are 0 and the (zero) running sums stay 0
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2f(mrun[qt] - mref);
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = (mnew == -INFINITY) ? 0.f : exp2f(p[kt][qt][i] - mnew);
+            const float e = exp2f(p[kt][qt][i] - mref);
             p[kt][qt][i] = e;
             psum += e;
           }
         lrun[qt] = lrun[qt] * alpha + psum;
         mrun[qt] = mnew;
+        if (__any(alpha != 1.f)) {  // some row's maximum moved
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] *= alpha;
+          for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] *= alpha;
+        }
       }
-      // P as bf16 high + low parts (see k_attn).
-      F pf[2], pl[2];
+      v8h pf[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = p[kt][qt][i];
-            const bf16_t hb = f2bf(v);
-            pf[qt][kt * 4 + i] = (short)hb;
-            pl[qt][kt * 4 + i] = (short)f2bf(v - bf2f(hb));
-          }
+          for (int i = 0; i < 4; ++i) pf[qt][kt * 4 + i] = (_Float16)p[kt][qt][i];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         const int d = ht * 16 + c16;
         const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
-        const F vf = *reinterpret_cast<const F*>(&u);
-        oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], oacc[ht][0], 0, 0, 0);
-        oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], oacc[ht][1], 0, 0, 0);
-        oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[0], oacc[ht][0], 0, 0, 0);
-        oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[1], oacc[ht][1], 0, 0, 0);
+        const v8h vf = *reinterpret_cast<const v8h*>(&u);
+        oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[0], oacc[ht][0], 0, 0, 0);
+        oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[1], oacc[ht][1], 0, 0, 0);
       }
     }
     store_tile(stg ^ 1, rk, rv);

@@ -50,18 +50,80 @@ void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, 
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm: out[i] = x[src(i)] / sqrt(mean(x^2) + eps) * g, written in the model dtype.
-// src(i) = row_idx[i] if given; rows with i >= *n_dev (if given) are skipped.
+// Row kernel over the fp32 residual stream: one block of 256 threads per row, the
+// row held in registers as float4 (NV per thread, d <= 1024 NV).
+//   combine (y given): x[t] += sum_j gates[t][j] y[t k + j], written back (the
+//     gate-weighted sum of the routed experts' outputs, j in increasing order);
+//   RMSNorm (g given): out[i] = x[t] / sqrt(mean(x[t]^2) + eps) * g in the model
+//     dtype.
+// t = row_idx[i] if given, else i; rows with i >= *n_dev (if given) are skipped.
 template <typename T>
-__global__ void __launch_bounds__(256) k_rmsnorm(const float* __restrict__ x, const int32_t* __restrict__ row_idx,
-                                                 const int32_t* __restrict__ n_dev, int d, const T* __restrict__ g,
-                                                 float eps, T* __restrict__ out) {
+__device__ __forceinline__ void store4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
+  const uint32_t lo = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  const uint32_t hi = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <typename T, int NV>
+__global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const int32_t* __restrict__ row_idx,
+                                                  const int32_t* __restrict__ n_dev, int d,
+                                                  const float* __restrict__ y, const float* __restrict__ gates, int k,
+                                                  const T* __restrict__ g, float eps, T* __restrict__ out) {
   const int i = blockIdx.x;
   if (n_dev && i >= *n_dev) return;
-  const int src = row_idx ? row_idx[i] : i;
-  const float* xr = x + (size_t)src * d;
+  const int t = row_idx ? row_idx[i] : i;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)t * d);
+  const int nv = d >> 2;
+  float4 v[NV];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) ss += xr[c] * xr[c];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nv) {
+      float4 a = xr[c];
+      if (y) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < DG_MAX_TOPK; ++j) {
+          if (j < k) {
+            const float gj = gates[(size_t)t * k + j];
+            const float4 yy = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * d)[c];
+            acc.x += gj * yy.x;
+            acc.y += gj * yy.y;
+            acc.z += gj * yy.z;
+            acc.w += gj * yy.w;
+          }
+        }
+        a.x += acc.x;
+        a.y += acc.y;
+        a.z += acc.z;
+        a.w += acc.w;
+        xr[c] = a;
+      }
+      v[u] = a;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+  }
+  if (!g) return;  // uniform over the block
   ss = wave_sum(ss);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -69,16 +131,50 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* __restrict__ x, co
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
   T* o = out + (size_t)i * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = from_f<T>(xr[c] * inv * to_f(g[c]));
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    if (c < nv) {
+      const float4 gg = load4<T>(g + 4 * c);
+      store4<T>(o + 4 * c, make_float4(v[u].x * inv * gg.x, v[u].y * inv * gg.y, v[u].z * inv * gg.z,
+                                       v[u].w * inv * gg.w));
+    }
+  }
+}
+
+template <typename T>
+void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d, const float* y,
+                     const float* gates, int k, const T* g, float eps, T* out, hipStream_t s) {
+  const int nv = (d / 4 + 255) / 256;
+#define DG_ROW_NORM(NVV) k_row_norm<T, NVV><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, y, gates, k, g, eps, out)
+  if (nv <= 1) DG_ROW_NORM(1);
+  else if (nv <= 2) DG_ROW_NORM(2);
+  else if (nv <= 3) DG_ROW_NORM(3);
+  else if (nv <= 4) DG_ROW_NORM(4);
+  else if (nv <= 8) DG_ROW_NORM(8);
+  else DG_ROW_NORM(16);  // d <= 16384 (checked at creation)
+#undef DG_ROW_NORM
 }
 
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
                        const void* gain, float eps, void* out, hipStream_t s) {
   if (rows <= 0) return;
+  // x is only read: the combine part is off (y == nullptr)
   if (dtype == 1)
-    k_rmsnorm<bf16_t><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, (const bf16_t*)gain, eps, (bf16_t*)out);
+    launch_row_norm<bf16_t>(const_cast<float*>(x), row_idx, n_dev, rows, d, nullptr, nullptr, 0,
+                            (const bf16_t*)gain, eps, (bf16_t*)out, s);
   else
-    k_rmsnorm<float><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, (const float*)gain, eps, (float*)out);
+    launch_row_norm<float>(const_cast<float*>(x), row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const float*)gain,
+                           eps, (float*)out, s);
+}
+
+void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
+                            const void* gain, float eps, void* out, hipStream_t s) {
+  if (rows <= 0) return;
+  if (dtype == 1)
+    launch_row_norm<bf16_t>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps, (bf16_t*)out, s);
+  else
+    launch_row_norm<float>(x, nullptr, nullptr, rows, d, y, gates, k, (const float*)gain, eps, (float*)out, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,21 +401,6 @@ void dg_launch_swiglu(int dtype, const void* A, int M, int K, const void* w1, co
 
 // ---------------------------------------------------------------------------
 // MoE combine: x[t] += sum_j gates[t][j] * y[t*k + j], slots in fixed order.
-__global__ void __launch_bounds__(256) k_combine(float* __restrict__ x, const float* __restrict__ y,
-                                                 const float* __restrict__ gates, int d, int k) {
-  const int t = blockIdx.x;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += gates[t * k + j] * y[((size_t)t * k + j) * d + c];
-    x[(size_t)t * d + c] += acc;
-  }
-}
-
-void dg_launch_combine(float* x, const float* y, const float* gates, int rows, int d, int k, hipStream_t s) {
-  if (rows <= 0) return;
-  k_combine<<<rows, 256, 0, s>>>(x, y, gates, d, k);
-}
-
 __global__ void k_gather_rows(const float* __restrict__ x, const int32_t* __restrict__ idx, int d,
                               float* __restrict__ out) {
   const int i = blockIdx.x;

@@ -12,56 +12,55 @@
 #include "gemm_core.h"
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per row.  The k largest logits (ties to the lower expert id),
-// gates = softmax over the k kept logits.
+// Top-k: one block per row.  The k largest logits, ties to the lower expert id (a
+// NaN logit ranks lowest): the rank of logit e is the number of logits that beat
+// it under that order, and the entries of rank < k are the selection, in rank
+// order.  The E x E comparisons are spread over the block as (logit, slice of 32
+// logits) items and the partial ranks are summed in LDS.  gates = softmax over the k kept logits, summed in
+// rank order.
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int rows, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ gates) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
-  if (r >= rows) return;
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    const float x = e < E ? logits[(size_t)r * E + e] : -INFINITY;
-    v[i] = x == x ? x : -INFINITY;  // a NaN logit ranks lowest
+  __shared__ float s_v[256];
+  __shared__ int s_rank[256];
+  __shared__ float s_sel[DG_MAX_TOPK];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* lrow = logits + (size_t)r * E;
+  if (tid < E) {
+    const float x = lrow[tid];
+    s_v[tid] = x == x ? x : -INFINITY;
   }
-  float sel[16];
-  int sid[16];
-  unsigned taken = 0;  // entries of this lane already selected
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+  s_rank[tid] = 0;
+  __syncthreads();
+  // work items (e, slice): E logits x ceil(E / 32) slices of 32 comparisons
+  const int nsl = (E + 31) / 32;
+  for (int it = tid; it < E * nsl; it += 256) {
+    const int e = it % E, sl = it / E;
+    const float v = s_v[e];
+    const int j0 = sl * 32, j1 = min(j0 + 32, E);
+    int cnt = 0;
+    for (int j = j0; j < j1; ++j) {
+      const float w = s_v[j];
+      cnt += (w > v || (w == v && j < e)) ? 1 : 0;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    sel[j] = bv;
-    sid[j] = bi;  // k <= E: some untaken entry always exists, so bi is a real expert
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == bi) taken |= 1u << i;
+    if (cnt) atomicAdd(&s_rank[e], cnt);
   }
-  if (lane == 0) {
+  __syncthreads();
+  if (tid < E && s_rank[tid] < k) {
+    ids[(size_t)r * k + s_rank[tid]] = tid;
+    s_sel[s_rank[tid]] = s_v[tid];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float m = s_sel[0];
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s += __expf(sel[j] - sel[0]);
-    for (int j = 0; j < k; ++j) {
-      ids[(size_t)r * k + j] = sid[j];
-      gates[(size_t)r * k + j] = __expf(sel[j] - sel[0]) / s;
-    }
+    for (int j = 0; j < k; ++j) s += __expf(s_sel[j] - m);
+    for (int j = 0; j < k; ++j) gates[(size_t)r * k + j] = __expf(s_sel[j] - m) / s;
   }
 }
 
 void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s) {
   if (rows <= 0) return;
-  k_topk<<<(rows + 3) / 4, 256, 0, s>>>(logits, rows, E, k, ids, gates);
+  k_topk<<<rows, 256, 0, s>>>(logits, rows, E, k, ids, gates);
 }
 
 // ---------------------------------------------------------------------------
@@ -118,6 +117,89 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
                        hipStream_t s) {
   if (rows <= 0) return;
   k_permute<<<E, 256, 0, s>>>(ids, rows * k, counts, offsets, perm);
+}
+
+// ---------------------------------------------------------------------------
+// Everything after the top-k in one block of 16 waves: the expert histogram and
+// offsets, the token permutation (as k_permute: the pairs of an expert in
+// increasing pair index) and the two grouped work lists (as k_ws_units).  Expert
+// e's rows are a bitmap over tokens; a token picks an expert at most once, so the
+// rank of pair (t, e) among e's pairs is the number of e's tokens below t.
+// rows <= DG_ROUTE_MAX_ROWS, E <= 256.
+#define DG_ROUTE_MAX_ROWS 2048
+__global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__ ids, int rows, int E, int k,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm, int nblk_a,
+                                                     int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
+                                                     int nblk_b, int32_t* __restrict__ units_b,
+                                                     int32_t* __restrict__ n_b) {
+  constexpr int WPE = DG_ROUTE_MAX_ROWS / 32;  // bitmap words per expert
+  __shared__ uint32_t s_bits[256][WPE];
+  __shared__ int s_off[256], s_part[256];
+  const int tid = threadIdx.x;
+  const int nw = (rows + 31) / 32;
+  for (int i = tid; i < 256 * nw; i += 1024) s_bits[i / nw][i % nw] = 0u;
+  __syncthreads();
+  const int npairs = rows * k;
+  for (int p = tid; p < npairs; p += 1024) {
+    const int t = p / k;
+    atomicOr(&s_bits[ids[p]][t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  int cnt = 0, parts = 0;
+  if (tid < 256) {
+    if (tid < E)
+      for (int w = 0; w < nw; ++w) cnt += __popc(s_bits[tid][w]);
+    parts = (cnt + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+    s_off[tid] = cnt;
+    s_part[tid] = parts;
+  }
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive scans over the experts
+    int a = 0, b = 0;
+    if (tid < 256 && tid >= o) {
+      a = s_off[tid - o];
+      b = s_part[tid - o];
+    }
+    __syncthreads();
+    if (tid < 256) {
+      s_off[tid] += a;
+      s_part[tid] += b;
+    }
+    __syncthreads();
+  }
+  if (tid < 256) s_off[tid] -= cnt;  // exclusive: first position of expert tid
+  __syncthreads();
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = s_off[tid];
+    const int before = s_part[tid] - parts;
+    dg_fill_units(units_a, before, parts, tid, nblk_a);
+    dg_fill_units(units_b, before, parts, tid, nblk_b);
+  }
+  if (tid == 0) {
+    *n_a = s_part[255] * ((nblk_a + 7) & ~7);
+    *n_b = s_part[255] * ((nblk_b + 7) & ~7);
+  }
+  for (int p = tid; p < npairs; p += 1024) {
+    const int e = ids[p], t = p / k, tw = t >> 5;
+    int rank = __popc(s_bits[e][tw] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < tw; ++w) rank += __popc(s_bits[e][w]);
+    perm[s_off[e] + rank] = p;
+  }
+}
+
+void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
+                     int32_t* units_b, int32_t* n_b, hipStream_t s) {
+  dg_launch_topk(logits, rows, E, k, ids, gates, s);
+  if (rows <= DG_ROUTE_MAX_ROWS && E <= 256) {
+    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, nblk_a, units_a, n_a, nblk_b, units_b,
+                                    n_b);
+    return;
+  }
+  dg_launch_permute(ids, rows, E, k, counts, offsets, perm, s);
+  dg_launch_ws_units(counts, E, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -412,14 +412,6 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 // in turn (block u runs on XCD u % 8), so every part of n-block b of a group runs
 // on XCD b % 8 and the parts after the first find that weight tile in its L2.
 // One block; E <= 256.
-__device__ __forceinline__ void ws_fill_units(int32_t* __restrict__ units, int first, int parts, int e, int nblk) {
-  const int stride = (nblk + 7) & ~7;
-  for (int p = 0; p < parts; ++p)
-    for (int b = 0; b < stride; ++b)
-      units[(first + p) * stride + b] = b < nblk ? (int32_t)(((uint32_t)e << 24) | ((uint32_t)p << 16) | (uint32_t)b)
-                                                 : (int32_t)DG_WS_UNIT_NONE;
-}
-
 __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ counts, int E, int nblk_a,
                                                   int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                   int nblk_b, int32_t* __restrict__ units_b,
@@ -437,8 +429,8 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
     __syncthreads();
   }
   const int before = s_scan[e] - parts;  // exclusive prefix
-  ws_fill_units(units_a, before, parts, e, nblk_a);
-  ws_fill_units(units_b, before, parts, e, nblk_b);
+  dg_fill_units(units_a, before, parts, e, nblk_a);
+  dg_fill_units(units_b, before, parts, e, nblk_b);
   if (e == 255) {
     *n_a = s_scan[255] * ((nblk_a + 7) & ~7);
     *n_b = s_scan[255] * ((nblk_b + 7) & ~7);

@@ -67,7 +67,7 @@ typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  * with weight 1.  The embedding is not scaled and serves as the LM head (tied).
  *
  * Supported shapes: head_dim 16, 32, 64, 128 or 256 (bf16: at least 64);
- * d_model and expert_hidden multiples of 64; n_q_heads*head_dim and
+ * d_model (at most 16384) and expert_hidden multiples of 64; n_q_heads*head_dim and
  * shared_hidden multiples of 64 (bf16) or 16 (f32); vocab a multiple of 128;
  * top_k <= 16; n_experts <= 256; max_requests <= 16; max_ctx a multiple of 64;
  * canvas_len == 256; prefill_chunk <= 32768.
@@ -341,7 +341,7 @@ dg_status dg_philox_tokens(uint64_t seed, int32_t block, int32_t step, int32_t n
  * Kernel families of a denoising step.  The timer brackets every launch of one
  * family with a pair of HIP events on the context's stream; a family made of
  * two launches (the LM head and its tile merge, attention and its split merge,
- * router logits and top-k) is timed as one unit.
+ * router logits and top-k in the fp32 model) is timed as one unit.
  */
 typedef enum dg_kernel_family {
   DG_KF_NONE = 0,
@@ -350,13 +350,15 @@ typedef enum dg_kernel_family {
   DG_KF_QKV = 3,          /* q/k/v projection + RoPE + K/V cache write */
   DG_KF_ATTENTION = 4,    /* split-KV attention + merge */
   DG_KF_OUT_PROJ = 5,     /* output projection + residual */
-  DG_KF_ROUTER = 6,       /* router logits + top-k gates */
-  DG_KF_PERMUTE = 7,      /* expert histogram, offsets, token permutation */
+  DG_KF_ROUTER = 6,       /* router logits (+ top-k gates in the fp32 model) */
+  DG_KF_PERMUTE = 7,      /* (top-k gates,) expert histogram, offsets, token
+                             permutation, routed work lists */
   DG_KF_EXPERT_UP = 8,    /* routed experts, W1/W3 with SwiGLU */
   DG_KF_EXPERT_DOWN = 9,  /* routed experts, W2 */
   DG_KF_SHARED_UP = 10,   /* shared expert, W1/W3 with SwiGLU */
   DG_KF_SHARED_DOWN = 11, /* shared expert, W2 + residual */
-  DG_KF_COMBINE = 12,     /* gate-weighted sum of the routed outputs + residual */
+  DG_KF_COMBINE = 12,     /* gate-weighted sum of the routed outputs + residual,
+                             with the next layer's attention RMSNorm */
   DG_KF_LM_HEAD = 13,     /* fused LM head + softmax statistics + tile merge */
   DG_KF_SAMPLE = 14,      /* entropy-bound sampler */
   DG_KF_COUNT = 15
