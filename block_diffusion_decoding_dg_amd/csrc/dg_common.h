@@ -10,6 +10,16 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
+// Fragment-major ("FM") layout of a bf16 activation matrix with K columns (K a
+// multiple of 64) and rows padded to a multiple of 16: the 16-row x 32-column
+// blocks are stored one after another, row tiles outer, and inside a block lane
+// L = 16 g + i of the matrix core's operand layout owns the 16 bytes of row i,
+// columns 8 g .. 8 g + 7.  A wave's operand fragment is then one contiguous 1 KB
+// load.  Element index of (r, k):
+__device__ __forceinline__ size_t fm_index(int r, int k, int K) {
+  return ((size_t)(r >> 4) * (K >> 5) + (k >> 5)) * 512 + (((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 #define DG_WAVE 64
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }

@@ -30,8 +30,12 @@ void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed,
                      hipStream_t s);
 struct DgSampleArgs;
 void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, int d, float* x, hipStream_t s);
+// fm: bf16 output in the fragment-major layout (fm_index) instead of row-major.
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, hipStream_t s);
+                       const void* gain, float eps, void* out, bool fm, hipStream_t s);
+// Expert-sorted fragment-major copy: dst row spos[i] = src row perm[i] / kdiv, i < n.
+void dg_launch_gather_fm(const void* src, int K, const int32_t* perm, const int32_t* spos, int kdiv, int n, void* dst,
+                         hipStream_t s);
 // y = A W^T; mode 0: store in dtype, 1: store fp32, 2: add into fp32 out.
 void dg_launch_gemm(int dtype, int mode, const void* A, int M, int K, const void* W, int N, void* out, int ldo,
                     hipStream_t s);
@@ -49,11 +53,15 @@ void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, f
 // Permutation: counts[E], offsets[E], perm[rows*k] (pair index t*k + j, token order per expert).
 void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
                        hipStream_t s);
-// Router top-k, histogram, offsets, permutation and both grouped work lists
-// (dg_launch_ws_units); everything after the top-k in one block for rows <= 2048.
+// Router top-k, histogram, offsets, permutation, the expert-sorted row layout
+// (offsets16[e]: first row of expert e, 16-aligned; spos[i]: row of sorted pair i)
+// and both grouped work lists (dg_launch_ws_units); everything after the top-k in
+// one block for rows <= 2048.
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
-                     int32_t* offsets, int32_t* perm, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
-                     int32_t* units_b, int32_t* n_b, hipStream_t s);
+                     int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* spos, int nblk_a,
+                     int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s);
+// Rows of the expert-sorted layout: pairs + 16 per expert.
+inline int dg_sorted_rows(int E, int pairs) { return pairs + 16 * E; }
 // Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
 void dg_launch_expert_up(int dtype, const void* b, int rows, int d, int E, int k, int eh, const void* w1,
                          const void* w3, const int32_t* counts, const int32_t* offsets, const int32_t* perm, void* h,
@@ -65,7 +73,7 @@ void dg_launch_expert_down(int dtype, const void* h, int rows, int d, int E, int
 // x[t] += sum_j gates[t][j] y[t k + j] for every row, then (gain given) the
 // RMSNorm of the updated rows into out (model dtype).  d <= 16384, k <= 16.
 void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
-                            const void* gain, float eps, void* out, hipStream_t s);
+                            const void* gain, float eps, void* out, bool fm, hipStream_t s);
 // LM head over rows of hn [n][d] (dtype), n from n_dev (<= max_rows): partials then merge.
 void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_rows, int d, const void* embed,
                        int vocab, float* part, int32_t* part_arg, float* ent, float* lse, int32_t* amax,
@@ -112,8 +120,7 @@ enum {
 };
 
 struct WsArgs {
-  const void* A;          // activation rows, bf16, row stride lda elements
-  int lda;
+  const void* A;          // activation rows, bf16, fragment-major with K columns (fm_index)
   const void* W0;         // weight matrices, row-major [rows][K]
   const void* W1;
   const void* W2;
@@ -126,8 +133,8 @@ struct WsArgs {
   int nblk;               // dense launches: number of n-blocks
   const int32_t* counts;  // grouped: rows per group
   const int32_t* offsets; // grouped: first position of each group in perm
-  const int32_t* perm;    // grouped: pair index of each row; activation row = pair / kdiv, output row = pair
-  int kdiv;
+  const int32_t* perm;    // grouped: pair index of each sorted row (the output row of a fp32 store)
+  const int32_t* offsets16;  // grouped: first row of each group in A (and a SwiGLU output), 16-aligned
   const int32_t* units;   // grouped: work list (group << 24 | part << 16 | n-block), length *n_units
   const int32_t* n_units;
   void* out;

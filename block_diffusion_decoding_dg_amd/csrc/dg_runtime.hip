@@ -79,6 +79,9 @@ struct dg_ctx {
   int32_t* counts = nullptr;
   int32_t* offsets = nullptr;
   int32_t* perm = nullptr;
+  int32_t* offsets16 = nullptr;  // expert-sorted layout: first row of each expert (16-aligned)
+  int32_t* spos = nullptr;       // expert-sorted layout: row of each sorted pair
+  void* xs = nullptr;            // expert-sorted copy of the normalised rows (bf16, fragment-major)
   int32_t* units_up = nullptr;   // routed work lists (group << 24 | part << 16 | n-block)
   int32_t* units_dn = nullptr;
   int32_t* n_units = nullptr;    // [2]: lengths of the two lists
@@ -224,7 +227,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   const int C = m.canvas_len;
   const int Rs = m.max_requests * C;
   const int pc = m.prefill_chunk > 0 ? m.prefill_chunk : 2048;
-  const int Tm = std::max(Rs, pc);
+  const int Tm = (std::max(Rs, pc) + 15) / 16 * 16;  // fragment-major buffers hold whole 16-row tiles
   const size_t d = m.d_model, qd = (size_t)m.n_q_heads * m.head_dim;
   const size_t k = m.top_k, E = m.n_experts;
   const size_t attn_cap = std::max((size_t)32 * Rs, (size_t)4 * Tm);
@@ -241,11 +244,15 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->counts = cv.take<int32_t>(E * 4);
   c->offsets = cv.take<int32_t>(E * 4);
   c->perm = cv.take<int32_t>(Tm * k * 4);
+  c->offsets16 = cv.take<int32_t>(E * 4);
+  c->spos = cv.take<int32_t>(Tm * k * 4);
+  const size_t srows = (size_t)dg_sorted_rows((int)E, (int)(Tm * k));  // expert-sorted rows
+  c->xs = cv.take<void>(srows * d * es);
   c->units_up = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.expert_hidden + 31) / 32) * 4);
   c->units_dn = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.d_model + 63) / 64) * 4);
   c->rows_cap = Tm;
   c->n_units = cv.take<int32_t>(2 * 4);
-  c->hbuf = cv.take<void>(Tm * k * m.expert_hidden * es);
+  c->hbuf = cv.take<void>(srows * m.expert_hidden * es);
   c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
   c->ybuf = cv.take<float>(Tm * k * d * 4);
   c->hn = cv.take<void>(Rs * d * es);
@@ -340,13 +347,11 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
-  a.lda = K;
   a.W0 = W0;
   a.W1 = W1;
   a.K = K;
   a.N = N;
   a.M = M;
-  a.kdiv = 1;
   a.out = out;
   a.ldo = ldo;
   const int nblk = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
@@ -355,13 +360,14 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), c->stream);
 }
 
-void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, const void* W1, size_t wgs, int K, int N,
-                   int kdiv, const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo) {
+// Grouped launch over the expert-sorted rows: A is the expert-sorted
+// fragment-major copy of the group's input rows (c->offsets16 layout).
+void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void* W1, size_t wgs, int K, int N,
+                   const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
-  a.lda = lda;
   a.W0 = W0;
   a.W1 = W1;
   a.wgs = wgs;
@@ -370,7 +376,7 @@ void launch_routed(dg_ctx* c, int epi, const void* A, int lda, const void* W0, c
   a.counts = c->counts;
   a.offsets = c->offsets;
   a.perm = c->perm;
-  a.kdiv = kdiv;
+  a.offsets16 = c->offsets16;
   a.units = units;
   a.n_units = n_units;
   a.out = out;
@@ -387,14 +393,12 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = c->xn;
-  a.lda = m.d_model;
   a.W0 = w.wq;
   a.W1 = w.wk;
   a.W2 = w.wv;
   a.K = m.d_model;
   a.N = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim;
   a.M = rows;
-  a.kdiv = 1;
   a.out = c->q;
   a.ldo = m.n_q_heads * m.head_dim;
   a.hd = m.head_dim;
@@ -422,13 +426,11 @@ void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = c->hn;
-  a.lda = m.d_model;
   a.W0 = c->embed;
   a.K = m.d_model;
   a.N = m.vocab;
   a.M = max_rows;
   a.M_dev = n_dev;
-  a.kdiv = 1;
   a.out = c->lpart;
   a.ldo = c->lm_tiles;
   a.part_arg = c->lpart_arg;
@@ -447,7 +449,7 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
   const DgSegs sg = make_segs(c, slots, l, causal);
   if (!norm_done)
     KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm, m.rms_eps,
-                                           c->xn, s));
+                                           c->xn, c->dtype == DG_BF16, s));
   KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
   const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
@@ -467,7 +469,7 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
-  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, s));
+  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, c->dtype == DG_BF16, s));
   if (c->dtype == DG_F32) {
     KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, rlog, m.n_experts, s);
                             dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s));
@@ -483,20 +485,25 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
                                      m.n_experts));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
     KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
-                                         nb_up, c->units_up, c->n_units, nb_dn, c->units_dn, c->n_units + 1, s));
-    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xn, m.d_model, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
-                                         m.d_model, m.expert_hidden, m.top_k, c->units_up, c->n_units, nb_up, c->hbuf,
+                                         c->offsets16, c->spos, nb_up, c->units_up, c->n_units, nb_dn, c->units_dn,
+                                         c->n_units + 1, s);
+                             dg_launch_gather_fm(c->xn, m.d_model, c->perm, c->spos, m.top_k, rows * m.top_k, c->xs, s));
+    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU from the sorted
+    // copy of the normalised rows into c->hbuf (same sorted rows), W2 from there
+    // into c->ybuf at each row's pair index
+    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xs, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
+                                         m.d_model, m.expert_hidden, c->units_up, c->n_units, nb_up, c->hbuf,
                                          m.expert_hidden));
-    KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, m.expert_hidden, w.w2, nullptr,
-                                           (size_t)m.d_model * m.expert_hidden, m.expert_hidden, m.d_model, 1, c->units_dn,
-                                           c->n_units + 1, nb_dn, c->ybuf, m.d_model));
+    KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, (size_t)m.d_model * m.expert_hidden,
+                                           m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,
+                                           m.d_model));
     KT(c, DG_KF_SHARED_UP, launch_dense(c, WS_EPI_SWIGLU, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs,
                                         m.shared_hidden));
     KT(c, DG_KF_SHARED_DOWN, launch_dense(c, WS_EPI_ADD_F32, c->hs, rows, m.shared_hidden, w.sw2, nullptr, m.d_model, c->x,
                                           m.d_model));
   }
   KT(c, DG_KF_COMBINE, dg_launch_combine_norm(c->dtype, c->x, c->ybuf, gates, rows, m.d_model, m.top_k, next_gain,
-                                              m.rms_eps, c->xn, s));
+                                              m.rms_eps, c->xn, c->dtype == DG_BF16, s));
 }
 
 // Forward of the rows in c->x through all layers.  kv_only: the last layer only
@@ -511,7 +518,7 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
       const dg_layer_weights& w = c->layers[l];
       if (!xn_ready)
         KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.attn_norm,
-                                               m.rms_eps, c->xn, c->stream));
+                                               m.rms_eps, c->xn, c->dtype == DG_BF16, c->stream));
       KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
       break;
     }
@@ -704,7 +711,7 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
   KT(c, DG_KF_EMBED, dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s));
   forward_layers(c, slots, rows, false, false, true);
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
-                                         c->cfg.rms_eps, c->hn, s));
+                                         c->cfg.rms_eps, c->hn, c->dtype == DG_BF16, s));
   KT(c, DG_KF_LM_HEAD, launch_lm_head(c, c->n_open_rows, rows, c->open_rows, c->ent, c->lse, c->amax));
   KT(c, DG_KF_SAMPLE, dg_launch_sample(a, c->ent, c->amax, c->info_dev, nullptr, nullptr, s));
   LAUNCHCK(c);
@@ -897,7 +904,7 @@ dg_status dg_last_step_logits(dg_ctx* c, const int32_t* rows_list, int32_t n, fl
     if (rows_list[i] < 0 || rows_list[i] >= c->last_rows) return fail(c, DG_ERR_INVALID_ARG, "row out of range");
   hipStream_t s = c->stream;
   HIPCK(c, hipMemcpyAsync(c->ids_stage, rows_list, n * 4, hipMemcpyHostToDevice, s));
-  dg_launch_rmsnorm(c->dtype, c->x, c->ids_stage, nullptr, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn, s);
+  dg_launch_rmsnorm(c->dtype, c->x, c->ids_stage, nullptr, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn, false, s);
   dg_launch_gemm(c->dtype, 1, c->hn, n, c->cfg.d_model, c->embed, c->cfg.vocab, logits_dev, c->cfg.vocab, s);
   LAUNCHCK(c);
   HIPCK(c, hipStreamSynchronize(s));
@@ -944,7 +951,7 @@ dg_status dg_op_lm_head(dg_ctx* c, const float* h_dev, int32_t n, float* entropy
     return fail(c, DG_ERR_INVALID_ARG, "bad arguments");
   hipStream_t s = c->stream;
   HIPCK(c, hipMemcpyAsync(c->n_open_rows, &n, 4, hipMemcpyHostToDevice, s));
-  dg_launch_rmsnorm(c->dtype, h_dev, nullptr, c->n_open_rows, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn,
+  dg_launch_rmsnorm(c->dtype, h_dev, nullptr, c->n_open_rows, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps, c->hn, c->dtype == DG_BF16,
                     s);
   launch_lm_head(c, c->n_open_rows, n, nullptr, entropy_dev, lse_dev, argmax_dev);
   LAUNCHCK(c);

@@ -429,8 +429,9 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   }
 }
 
-// Merge the splits of each (row, q-head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <typename T>
+// Merge the splits of each (row, q-head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// written row-major or (FM, bf16) fragment-major with hq * hd columns (fm_index).
+template <typename T, bool FM>
 __global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opart, const float* __restrict__ mlpart,
                                                    int nsplit, int rows_total, int hq, int hd, T* __restrict__ o) {
   const size_t qi = blockIdx.x;  // row * hq + qhead
@@ -442,13 +443,26 @@ __global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opa
     if (ml[1] > 0.f) L += exp2f(ml[0] - M) * ml[1];
   }
   const float invL = 1.f / L;
-  for (int c = threadIdx.x; c < hd; c += 64) {
-    float acc = 0.f;
+  const int row = (int)(qi / hq), col0 = (int)(qi % hq) * hd;
+  for (int c = 4 * threadIdx.x; c < hd; c += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < nsplit; ++s) {
-      const float* ml = mlpart + ((size_t)s * rows_total * hq + qi) * 2;
-      if (ml[1] > 0.f) acc += exp2f(ml[0] - M) * opart[((size_t)s * rows_total * hq + qi) * hd + c];
+      const size_t base = (size_t)s * rows_total * hq + qi;
+      const float* ml = mlpart + base * 2;
+      if (ml[1] > 0.f) {
+        const float w = exp2f(ml[0] - M);
+        const float4 v = *reinterpret_cast<const float4*>(opart + base * hd + c);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+      }
     }
-    o[qi * hd + c] = from_f<T>(acc * invL);
+    T* dst = o + (FM ? fm_index(row, col0 + c, hq * hd) : qi * hd + c);
+    dst[0] = from_f<T>(acc.x * invL);
+    dst[1] = from_f<T>(acc.y * invL);
+    dst[2] = from_f<T>(acc.z * invL);
+    dst[3] = from_f<T>(acc.w * invL);
   }
 }
 
@@ -479,10 +493,10 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
   const int blocks = segs.count * sh.hkv * nqb * nsplit;
 #define DG_ATTN(TT, HDV)                                                                                     \
   k_attn<TT, HDV><<<blocks, 256, 0, s>>>((const TT*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);         \
-  k_attn_merge<TT><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (TT*)o)
+  k_attn_merge<TT, sizeof(TT) == 2><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (TT*)o)
 #define DG_ATTN_LDS(HDV)                                                                                    \
   k_attn_lds<HDV><<<blocks, 256, 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);        \
-  k_attn_merge<bf16_t><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (bf16_t*)o)
+  k_attn_merge<bf16_t, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (bf16_t*)o)
   if (dtype == 1) {
     if (sh.hd == 256) { DG_ATTN_LDS(256); }
     else if (sh.hd == 128) { DG_ATTN_LDS(128); }

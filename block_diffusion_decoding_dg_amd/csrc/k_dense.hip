@@ -55,7 +55,7 @@ void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, 
 //   combine (y given): x[t] += sum_j gates[t][j] y[t k + j], written back (the
 //     gate-weighted sum of the routed experts' outputs, j in increasing order);
 //   RMSNorm (g given): out[i] = x[t] / sqrt(mean(x[t]^2) + eps) * g in the model
-//     dtype.
+//     dtype, row-major or (FM) fragment-major (fm_index).
 // t = row_idx[i] if given, else i; rows with i >= *n_dev (if given) are skipped.
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float4 v);
@@ -82,7 +82,7 @@ __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
                      __uint_as_float(u.y & 0xffff0000u));
 }
 
-template <typename T, int NV>
+template <typename T, int NV, bool FM>
 __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const int32_t* __restrict__ row_idx,
                                                   const int32_t* __restrict__ n_dev, int d,
                                                   const float* __restrict__ y, const float* __restrict__ gates, int k,
@@ -130,23 +130,22 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  T* o = out + (size_t)i * d;
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     const int c = threadIdx.x + 256 * u;
     if (c < nv) {
       const float4 gg = load4<T>(g + 4 * c);
-      store4<T>(o + 4 * c, make_float4(v[u].x * inv * gg.x, v[u].y * inv * gg.y, v[u].z * inv * gg.z,
-                                       v[u].w * inv * gg.w));
+      T* o = out + (FM ? fm_index(i, 4 * c, d) : (size_t)i * d + 4 * c);
+      store4<T>(o, make_float4(v[u].x * inv * gg.x, v[u].y * inv * gg.y, v[u].z * inv * gg.z, v[u].w * inv * gg.w));
     }
   }
 }
 
-template <typename T>
+template <typename T, bool FM>
 void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d, const float* y,
                      const float* gates, int k, const T* g, float eps, T* out, hipStream_t s) {
   const int nv = (d / 4 + 255) / 256;
-#define DG_ROW_NORM(NVV) k_row_norm<T, NVV><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, y, gates, k, g, eps, out)
+#define DG_ROW_NORM(NVV) k_row_norm<T, NVV, FM><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, y, gates, k, g, eps, out)
   if (nv <= 1) DG_ROW_NORM(1);
   else if (nv <= 2) DG_ROW_NORM(2);
   else if (nv <= 3) DG_ROW_NORM(3);
@@ -157,24 +156,51 @@ void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int
 }
 
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, hipStream_t s) {
+                       const void* gain, float eps, void* out, bool fm, hipStream_t s) {
   if (rows <= 0) return;
   // x is only read: the combine part is off (y == nullptr)
-  if (dtype == 1)
-    launch_row_norm<bf16_t>(const_cast<float*>(x), row_idx, n_dev, rows, d, nullptr, nullptr, 0,
-                            (const bf16_t*)gain, eps, (bf16_t*)out, s);
+  float* xm = const_cast<float*>(x);
+  if (dtype == 1 && fm)
+    launch_row_norm<bf16_t, true>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
+                                  (bf16_t*)out, s);
+  else if (dtype == 1)
+    launch_row_norm<bf16_t, false>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
+                                   (bf16_t*)out, s);
   else
-    launch_row_norm<float>(const_cast<float*>(x), row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const float*)gain,
-                           eps, (float*)out, s);
+    launch_row_norm<float, false>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const float*)gain, eps,
+                                  (float*)out, s);
 }
 
 void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
-                            const void* gain, float eps, void* out, hipStream_t s) {
+                            const void* gain, float eps, void* out, bool fm, hipStream_t s) {
   if (rows <= 0) return;
-  if (dtype == 1)
-    launch_row_norm<bf16_t>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps, (bf16_t*)out, s);
+  if (dtype == 1 && fm)
+    launch_row_norm<bf16_t, true>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps,
+                                  (bf16_t*)out, s);
+  else if (dtype == 1)
+    launch_row_norm<bf16_t, false>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps,
+                                   (bf16_t*)out, s);
   else
-    launch_row_norm<float>(x, nullptr, nullptr, rows, d, y, gates, k, (const float*)gain, eps, (float*)out, s);
+    launch_row_norm<float, false>(x, nullptr, nullptr, rows, d, y, gates, k, (const float*)gain, eps, (float*)out,
+                                  s);
+}
+
+// Expert-sorted copy of fragment-major activation rows: dst row spos[i] = src row
+// perm[i] / kdiv, i = 0 .. n-1 (the pairs in expert order; spos starts every
+// expert on a 16-row tile).  One block per row, 16 bytes per thread.
+__global__ void __launch_bounds__(256) k_gather_fm(const bf16_t* __restrict__ src, int K,
+                                                   const int32_t* __restrict__ perm, const int32_t* __restrict__ spos,
+                                                   int kdiv, bf16_t* __restrict__ dst) {
+  const int i = blockIdx.x;
+  const int t = perm[i] / kdiv, r = spos[i];
+  for (int c = threadIdx.x; c < K / 8; c += 256)
+    *reinterpret_cast<uint4*>(dst + fm_index(r, 8 * c, K)) = *reinterpret_cast<const uint4*>(src + fm_index(t, 8 * c, K));
+}
+
+void dg_launch_gather_fm(const void* src, int K, const int32_t* perm, const int32_t* spos, int kdiv, int n, void* dst,
+                         hipStream_t s) {
+  if (n <= 0) return;
+  k_gather_fm<<<n, 256, 0, s>>>((const bf16_t*)src, K, perm, spos, kdiv, (bf16_t*)dst);
 }
 
 // ---------------------------------------------------------------------------

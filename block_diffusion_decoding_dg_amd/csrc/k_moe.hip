@@ -124,18 +124,21 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
 // offsets, the token permutation (as k_permute: the pairs of an expert in
 // increasing pair index) and the two grouped work lists (as k_ws_units).  Expert
 // e's rows are a bitmap over tokens; a token picks an expert at most once, so the
-// rank of pair (t, e) among e's pairs is the number of e's tokens below t.
-// rows <= DG_ROUTE_MAX_ROWS, E <= 256.
+// rank of pair (t, e) among e's pairs is the number of e's tokens below t.  Also
+// the expert-sorted row layout of the grouped launches: expert e's rows start at
+// offsets16[e] (its predecessors' counts rounded up to 16), sorted pair i sits at
+// row spos[i].  rows <= DG_ROUTE_MAX_ROWS, E <= 256.
 #define DG_ROUTE_MAX_ROWS 2048
 __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__ ids, int rows, int E, int k,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm, int nblk_a,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ offsets16,
+                                                     int32_t* __restrict__ spos, int nblk_a,
                                                      int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                      int nblk_b, int32_t* __restrict__ units_b,
                                                      int32_t* __restrict__ n_b) {
   constexpr int WPE = DG_ROUTE_MAX_ROWS / 32;  // bitmap words per expert
   __shared__ uint32_t s_bits[256][WPE];
-  __shared__ int s_off[256], s_part[256];
+  __shared__ int s_off[256], s_part[256], s_off16[256];
   const int tid = threadIdx.x;
   const int nw = (rows + 31) / 32;
   for (int i = tid; i < 256 * nw; i += 1024) s_bits[i / nw][i % nw] = 0u;
@@ -153,26 +156,33 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
     parts = (cnt + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
     s_off[tid] = cnt;
     s_part[tid] = parts;
+    s_off16[tid] = (cnt + 15) & ~15;
   }
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {  // inclusive scans over the experts
-    int a = 0, b = 0;
+    int a = 0, b = 0, c = 0;
     if (tid < 256 && tid >= o) {
       a = s_off[tid - o];
       b = s_part[tid - o];
+      c = s_off16[tid - o];
     }
     __syncthreads();
     if (tid < 256) {
       s_off[tid] += a;
       s_part[tid] += b;
+      s_off16[tid] += c;
     }
     __syncthreads();
   }
-  if (tid < 256) s_off[tid] -= cnt;  // exclusive: first position of expert tid
+  if (tid < 256) {  // exclusive: first position of expert tid
+    s_off[tid] -= cnt;
+    s_off16[tid] -= (cnt + 15) & ~15;
+  }
   __syncthreads();
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = s_off[tid];
+    offsets16[tid] = s_off16[tid];
     const int before = s_part[tid] - parts;
     dg_fill_units(units_a, before, parts, tid, nblk_a);
     dg_fill_units(units_b, before, parts, tid, nblk_b);
@@ -186,19 +196,44 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
     int rank = __popc(s_bits[e][tw] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < tw; ++w) rank += __popc(s_bits[e][w]);
     perm[s_off[e] + rank] = p;
+    spos[s_off[e] + rank] = s_off16[e] + rank;
+  }
+}
+
+// The expert-sorted row layout for the multi-kernel routing path (more rows than
+// k_route_tail takes), from counts and offsets: one block, E <= 256.
+__global__ void __launch_bounds__(256) k_sorted_layout(const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ offsets, int E,
+                                                       int32_t* __restrict__ offsets16, int32_t* __restrict__ spos) {
+  __shared__ int s_off16[256];
+  const int e = threadIdx.x;
+  const int cnt = e < E ? counts[e] : 0, pad = (cnt + 15) & ~15;
+  s_off16[e] = pad;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = e >= o ? s_off16[e - o] : 0;
+    __syncthreads();
+    s_off16[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int first = s_off16[e] - pad, off = offsets[e];
+    offsets16[e] = first;
+    for (int r = 0; r < cnt; ++r) spos[off + r] = first + r;
   }
 }
 
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
-                     int32_t* offsets, int32_t* perm, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
-                     int32_t* units_b, int32_t* n_b, hipStream_t s) {
+                     int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* spos, int nblk_a,
+                     int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s) {
   dg_launch_topk(logits, rows, E, k, ids, gates, s);
   if (rows <= DG_ROUTE_MAX_ROWS && E <= 256) {
-    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, nblk_a, units_a, n_a, nblk_b, units_b,
-                                    n_b);
+    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, spos, nblk_a, units_a, n_a,
+                                    nblk_b, units_b, n_b);
     return;
   }
   dg_launch_permute(ids, rows, E, k, counts, offsets, perm, s);
+  k_sorted_layout<<<1, 256, 0, s>>>(counts, offsets, E, offsets16, spos);
   dg_launch_ws_units(counts, E, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
 }
 

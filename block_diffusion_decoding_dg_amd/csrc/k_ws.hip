@@ -15,7 +15,10 @@
 // sub-chunk), fed by a four-slot register ring; each chunk is stored two
 // iterations before it is used (see ws_stream).  The eight waves split the
 // activation rows (m-tile i goes to wave i % 8) and read their own activation
-// fragments straight from global memory three chunks ahead.  The LDS rows are
+// fragments straight from global memory three chunks ahead.  Activations are in
+// the fragment-major layout (fm_index), so each fragment is one contiguous 1 KB
+// load; a grouped launch reads them from an expert-sorted copy in which every
+// expert's rows start on a 16-row tile.  The LDS rows are
 // XOR-swizzled in 16-byte units so that both the cooperative stores and the
 // fragment reads are free of bank conflicts.
 //
@@ -155,7 +158,7 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
 #pragma unroll
       for (int q = 0; q < 2 * KSUB; ++q) {
         const int kc = min(c * KSUB + q / 2, nk64 - 1);
-        A[j][q] = *(const v8s*)(ap[j] + kc * 128 + (q & 1) * 64);
+        A[j][q] = *(const v8s*)(ap[j] + (2 * kc + (q & 1)) * 1024);
       }
   };
   fetch(R0, 0);
@@ -243,6 +246,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   }
   if (cnt <= 0) return;  // uniform over the block
   const int off = a.counts ? a.offsets[g] : 0;
+  const int arow0 = a.counts ? a.offsets16[g] : 0;  // group's first row in the A matrix
   const int nk64 = a.K / 64;  // 64-element sub-chunks of the reduction
 
   // This thread's 16-byte segments of every weight chunk: segment id
@@ -268,11 +272,10 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
     for (int j = 0; j < MT; ++j) {
       const int t0 = pbase + (wave + NWAVE * j) * 16;
       if (t0 < cnt) mt_act = j + 1;
-      const int r = row0 + min(t0 + (lane & 15), cnt - 1);
-      int arow;
-      if (a.counts) arow = a.perm[off + r] / a.kdiv;
-      else arow = r;
-      ap[j] = (const char*)((const bf16_t*)a.A + (size_t)arow * a.lda) + (lane >> 4) * 16;
+      // first row of this m-tile in the A matrix (a multiple of 16); a tile past
+      // the end is read from the last one, which holds valid rows
+      const int tr = arow0 + row0 + min(t0, (cnt - 1) & ~15);
+      ap[j] = (const char*)a.A + (size_t)(tr >> 4) * (a.K >> 5) * 1024 + lane * 16;
     }
 
     v4f acc[MT][NTN];
@@ -343,13 +346,14 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
           const int rl = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
           if (rl >= cnt) continue;
           const int r = row0 + rl;
-          const int orow = a.counts ? a.perm[off + r] : r;
           if constexpr (EPI == WS_EPI_SWIGLU) {
+            // fragment-major output with N columns, at the input's row (the
+            // expert-sorted row for a grouped launch)
+            const int frow = arow0 + r;
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
               const int col = nb * 32 + n * 16 + (lane & 15);
-              if (col < a.N)
-                ((bf16_t*)a.out)[(size_t)orow * a.ldo + col] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + 2][i]);
+              if (col < a.N) ((bf16_t*)a.out)[fm_index(frow, col, a.N)] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + 2][i]);
             }
           } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
             const int half = a.hd / 2, per_head = half / 32;
@@ -387,6 +391,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
               }
             }
           } else {
+            const int orow = a.counts ? a.perm[off + r] : r;
 #pragma unroll
             for (int n = 0; n < NTN; ++n) {
               const int col = nb * BN + n * 16 + (lane & 15);
