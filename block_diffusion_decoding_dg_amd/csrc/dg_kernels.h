@@ -30,12 +30,11 @@ void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed,
                      hipStream_t s);
 struct DgSampleArgs;
 void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, int d, float* x, hipStream_t s);
-// fm: bf16 output in the fragment-major layout (fm_index) instead of row-major.
+// fm: bf16 output in the fragment-major layout (fm_index) instead of row-major;
+// out_rm (optional, bf16): a second, row-major copy.
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, bool fm, hipStream_t s);
-// Expert-sorted fragment-major copy: dst row spos[i] = src row perm[i] / kdiv, i < n.
-void dg_launch_gather_fm(const void* src, int K, const int32_t* perm, const int32_t* spos, int kdiv, int n, void* dst,
-                         hipStream_t s);
+                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm = nullptr);
+
 // y = A W^T; mode 0: store in dtype, 1: store fp32, 2: add into fp32 out.
 void dg_launch_gemm(int dtype, int mode, const void* A, int M, int K, const void* W, int N, void* out, int ldo,
                     hipStream_t s);
@@ -54,12 +53,13 @@ void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, f
 void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
                        hipStream_t s);
 // Router top-k, histogram, offsets, permutation, the expert-sorted row layout
-// (offsets16[e]: first row of expert e, 16-aligned; spos[i]: row of sorted pair i)
-// and both grouped work lists (dg_launch_ws_units); everything after the top-k in
-// one block for rows <= 2048.
+// (offsets16[e]: first row of expert e, 16-aligned; rowsrc[r]: token of sorted row
+// r, -1 on padding rows, for r < *n_srows) and both grouped work lists
+// (dg_launch_ws_units); everything after the top-k in one block for rows <= 2048.
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
-                     int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* spos, int nblk_a,
-                     int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s);
+                     int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
+                     int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b,
+                     hipStream_t s);
 // Rows of the expert-sorted layout: pairs + 16 per expert.
 inline int dg_sorted_rows(int E, int pairs) { return pairs + 16 * E; }
 // Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
@@ -135,6 +135,7 @@ struct WsArgs {
   const int32_t* offsets; // grouped: first position of each group in perm
   const int32_t* perm;    // grouped: pair index of each sorted row (the output row of a fp32 store)
   const int32_t* offsets16;  // grouped: first row of each group in A (and a SwiGLU output), 16-aligned
+  const int32_t* rowsrc;  // grouped, optional: A is row-major and sorted row r reads A row rowsrc[r]
   const int32_t* units;   // grouped: work list (group << 24 | part << 16 | n-block), length *n_units
   const int32_t* n_units;
   void* out;

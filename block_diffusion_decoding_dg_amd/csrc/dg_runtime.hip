@@ -69,6 +69,7 @@ struct dg_ctx {
   // scratch
   float* x = nullptr;
   void* xn = nullptr;
+  void* xr = nullptr;  // bf16: row-major copy of the FFN-normalised rows
   void* q = nullptr;
   void* ao = nullptr;
   float* opart = nullptr;
@@ -80,11 +81,10 @@ struct dg_ctx {
   int32_t* offsets = nullptr;
   int32_t* perm = nullptr;
   int32_t* offsets16 = nullptr;  // expert-sorted layout: first row of each expert (16-aligned)
-  int32_t* spos = nullptr;       // expert-sorted layout: row of each sorted pair
-  void* xs = nullptr;            // expert-sorted copy of the normalised rows (bf16, fragment-major)
+  int32_t* rowsrc = nullptr;     // expert-sorted layout: token of each row (-1: padding)
   int32_t* units_up = nullptr;   // routed work lists (group << 24 | part << 16 | n-block)
   int32_t* units_dn = nullptr;
-  int32_t* n_units = nullptr;    // [2]: lengths of the two lists
+  int32_t* n_units = nullptr;    // [3]: lengths of the two lists, rows of the expert-sorted layout
   int rows_cap = 0;              // rows of the largest forward pass (sizes the work lists)
   void* hbuf = nullptr;
   void* hs = nullptr;
@@ -234,6 +234,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   const int tiles = dg_lm_head_tiles(m.vocab);
   c->x = cv.take<float>(Tm * d * 4);
   c->xn = cv.take<void>(Tm * d * es);
+  c->xr = cv.take<void>(Tm * d * es);
   c->q = cv.take<void>(Tm * qd * es);
   c->ao = cv.take<void>(Tm * qd * es);
   c->opart = cv.take<float>(attn_cap * m.n_q_heads * m.head_dim * 4);
@@ -245,13 +246,12 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->offsets = cv.take<int32_t>(E * 4);
   c->perm = cv.take<int32_t>(Tm * k * 4);
   c->offsets16 = cv.take<int32_t>(E * 4);
-  c->spos = cv.take<int32_t>(Tm * k * 4);
   const size_t srows = (size_t)dg_sorted_rows((int)E, (int)(Tm * k));  // expert-sorted rows
-  c->xs = cv.take<void>(srows * d * es);
+  c->rowsrc = cv.take<int32_t>(srows * 4);
   c->units_up = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.expert_hidden + 31) / 32) * 4);
   c->units_dn = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.d_model + 63) / 64) * 4);
   c->rows_cap = Tm;
-  c->n_units = cv.take<int32_t>(2 * 4);
+  c->n_units = cv.take<int32_t>(3 * 4);  // up list, down list, expert-sorted rows
   c->hbuf = cv.take<void>(srows * m.expert_hidden * es);
   c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
   c->ybuf = cv.take<float>(Tm * k * d * 4);
@@ -360,10 +360,12 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), c->stream);
 }
 
-// Grouped launch over the expert-sorted rows: A is the expert-sorted
-// fragment-major copy of the group's input rows (c->offsets16 layout).
+// Grouped launch over the expert-sorted rows: A is fragment-major in the
+// expert-sorted layout (c->offsets16), or row-major with rowsrc mapping each
+// sorted row to its row of A.
 void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void* W1, size_t wgs, int K, int N,
-                   const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo) {
+                   const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo,
+                   const int32_t* rowsrc = nullptr) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel
   WsArgs a;
   memset(&a, 0, sizeof a);
@@ -377,6 +379,7 @@ void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void
   a.offsets = c->offsets;
   a.perm = c->perm;
   a.offsets16 = c->offsets16;
+  a.rowsrc = rowsrc;
   a.units = units;
   a.n_units = n_units;
   a.out = out;
@@ -469,7 +472,10 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
-  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn, c->dtype == DG_BF16, s));
+  // bf16: fragment-major for the dense projections, and a row-major copy that the
+  // expert-sorted gather reads
+  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps,
+                                         c->xn, c->dtype == DG_BF16, s, c->dtype == DG_BF16 ? c->xr : nullptr));
   if (c->dtype == DG_F32) {
     KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, rlog, m.n_experts, s);
                             dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s));
@@ -485,15 +491,14 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
                                      m.n_experts));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
     KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
-                                         c->offsets16, c->spos, nb_up, c->units_up, c->n_units, nb_dn, c->units_dn,
-                                         c->n_units + 1, s);
-                             dg_launch_gather_fm(c->xn, m.d_model, c->perm, c->spos, m.top_k, rows * m.top_k, c->xs, s));
-    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU from the sorted
-    // copy of the normalised rows into c->hbuf (same sorted rows), W2 from there
-    // into c->ybuf at each row's pair index
-    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xs, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
+                                         c->offsets16, c->rowsrc, c->n_units + 2, nb_up, c->units_up, c->n_units, nb_dn,
+                                         c->units_dn, c->n_units + 1, s));
+    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU gathering the
+    // row-major normalised rows into c->hbuf (fragment-major, sorted rows), W2
+    // from there into c->ybuf at each row's pair index
+    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
                                          m.d_model, m.expert_hidden, c->units_up, c->n_units, nb_up, c->hbuf,
-                                         m.expert_hidden));
+                                         m.expert_hidden, c->rowsrc));
     KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, (size_t)m.d_model * m.expert_hidden,
                                            m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,
                                            m.d_model));

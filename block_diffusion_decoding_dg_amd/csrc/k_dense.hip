@@ -57,6 +57,7 @@ void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, 
 //   RMSNorm (g given): out[i] = x[t] / sqrt(mean(x[t]^2) + eps) * g in the model
 //     dtype, row-major or (FM) fragment-major (fm_index).
 // t = row_idx[i] if given, else i; rows with i >= *n_dev (if given) are skipped.
+// out_rm (optional): a second, row-major copy of the normalised rows.
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float4 v);
 template <>
@@ -86,7 +87,8 @@ template <typename T, int NV, bool FM>
 __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const int32_t* __restrict__ row_idx,
                                                   const int32_t* __restrict__ n_dev, int d,
                                                   const float* __restrict__ y, const float* __restrict__ gates, int k,
-                                                  const T* __restrict__ g, float eps, T* __restrict__ out) {
+                                                  const T* __restrict__ g, float eps, T* __restrict__ out,
+                                                  T* __restrict__ out_rm) {
   const int i = blockIdx.x;
   if (n_dev && i >= *n_dev) return;
   const int t = row_idx ? row_idx[i] : i;
@@ -102,15 +104,21 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
       float4 a = xr[c];
       if (y) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+          // the (up to) eight expert rows' loads first, then their sum in order
+          float4 yy[8];
 #pragma unroll
-        for (int j = 0; j < DG_MAX_TOPK; ++j) {
-          if (j < k) {
-            const float gj = gates[(size_t)t * k + j];
-            const float4 yy = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * d)[c];
-            acc.x += gj * yy.x;
-            acc.y += gj * yy.y;
-            acc.z += gj * yy.z;
-            acc.w += gj * yy.w;
+          for (int jj = 0; jj < 8; ++jj)
+            if (j0 + jj < k) yy[jj] = reinterpret_cast<const float4*>(y + ((size_t)t * k + j0 + jj) * d)[c];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            if (j0 + jj < k) {
+              const float gj = gates[(size_t)t * k + j0 + jj];
+              acc.x += gj * yy[jj].x;
+              acc.y += gj * yy[jj].y;
+              acc.z += gj * yy[jj].z;
+              acc.w += gj * yy[jj].w;
+            }
           }
         }
         a.x += acc.x;
@@ -135,17 +143,19 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
     const int c = threadIdx.x + 256 * u;
     if (c < nv) {
       const float4 gg = load4<T>(g + 4 * c);
-      T* o = out + (FM ? fm_index(i, 4 * c, d) : (size_t)i * d + 4 * c);
-      store4<T>(o, make_float4(v[u].x * inv * gg.x, v[u].y * inv * gg.y, v[u].z * inv * gg.z, v[u].w * inv * gg.w));
+      const float4 r = make_float4(v[u].x * inv * gg.x, v[u].y * inv * gg.y, v[u].z * inv * gg.z, v[u].w * inv * gg.w);
+      store4<T>(out + (FM ? fm_index(i, 4 * c, d) : (size_t)i * d + 4 * c), r);
+      if (out_rm) store4<T>(out_rm + (size_t)i * d + 4 * c, r);
     }
   }
 }
 
 template <typename T, bool FM>
 void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d, const float* y,
-                     const float* gates, int k, const T* g, float eps, T* out, hipStream_t s) {
+                     const float* gates, int k, const T* g, float eps, T* out, hipStream_t s, T* out_rm = nullptr) {
   const int nv = (d / 4 + 255) / 256;
-#define DG_ROW_NORM(NVV) k_row_norm<T, NVV, FM><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, y, gates, k, g, eps, out)
+#define DG_ROW_NORM(NVV) \
+  k_row_norm<T, NVV, FM><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, y, gates, k, g, eps, out, out_rm)
   if (nv <= 1) DG_ROW_NORM(1);
   else if (nv <= 2) DG_ROW_NORM(2);
   else if (nv <= 3) DG_ROW_NORM(3);
@@ -156,13 +166,13 @@ void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int
 }
 
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, bool fm, hipStream_t s) {
+                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm) {
   if (rows <= 0) return;
   // x is only read: the combine part is off (y == nullptr)
   float* xm = const_cast<float*>(x);
   if (dtype == 1 && fm)
     launch_row_norm<bf16_t, true>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
-                                  (bf16_t*)out, s);
+                                  (bf16_t*)out, s, (bf16_t*)out_rm);
   else if (dtype == 1)
     launch_row_norm<bf16_t, false>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
                                    (bf16_t*)out, s);
@@ -185,23 +195,6 @@ void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* ga
                                   s);
 }
 
-// Expert-sorted copy of fragment-major activation rows: dst row spos[i] = src row
-// perm[i] / kdiv, i = 0 .. n-1 (the pairs in expert order; spos starts every
-// expert on a 16-row tile).  One block per row, 16 bytes per thread.
-__global__ void __launch_bounds__(256) k_gather_fm(const bf16_t* __restrict__ src, int K,
-                                                   const int32_t* __restrict__ perm, const int32_t* __restrict__ spos,
-                                                   int kdiv, bf16_t* __restrict__ dst) {
-  const int i = blockIdx.x;
-  const int t = perm[i] / kdiv, r = spos[i];
-  for (int c = threadIdx.x; c < K / 8; c += 256)
-    *reinterpret_cast<uint4*>(dst + fm_index(r, 8 * c, K)) = *reinterpret_cast<const uint4*>(src + fm_index(t, 8 * c, K));
-}
-
-void dg_launch_gather_fm(const void* src, int K, const int32_t* perm, const int32_t* spos, int kdiv, int n, void* dst,
-                         hipStream_t s) {
-  if (n <= 0) return;
-  k_gather_fm<<<n, 256, 0, s>>>((const bf16_t*)src, K, perm, spos, kdiv, (bf16_t*)dst);
-}
 
 // ---------------------------------------------------------------------------
 // Plain projection out = A W^T.  Block = WM waves stacked along rows, each wave

@@ -126,13 +126,15 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
 // e's rows are a bitmap over tokens; a token picks an expert at most once, so the
 // rank of pair (t, e) among e's pairs is the number of e's tokens below t.  Also
 // the expert-sorted row layout of the grouped launches: expert e's rows start at
-// offsets16[e] (its predecessors' counts rounded up to 16), sorted pair i sits at
-// row spos[i].  rows <= DG_ROUTE_MAX_ROWS, E <= 256.
+// offsets16[e] (its predecessors' counts rounded up to 16); rowsrc[r] is the token
+// of sorted row r (-1 on the padding rows), r < *n_srows.  rows <=
+// DG_ROUTE_MAX_ROWS, E <= 256.
 #define DG_ROUTE_MAX_ROWS 2048
 __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__ ids, int rows, int E, int k,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ offsets16,
-                                                     int32_t* __restrict__ spos, int nblk_a,
+                                                     int32_t* __restrict__ rowsrc, int32_t* __restrict__ n_srows,
+                                                     int nblk_a,
                                                      int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                      int nblk_b, int32_t* __restrict__ units_b,
                                                      int32_t* __restrict__ n_b) {
@@ -174,6 +176,8 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
     }
     __syncthreads();
   }
+  const int tot_parts = s_part[255], tot_rows16 = s_off16[255];
+  __syncthreads();
   if (tid < 256) {  // exclusive: first position of expert tid
     s_off[tid] -= cnt;
     s_off16[tid] -= (cnt + 15) & ~15;
@@ -183,28 +187,48 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
     counts[tid] = cnt;
     offsets[tid] = s_off[tid];
     offsets16[tid] = s_off16[tid];
-    const int before = s_part[tid] - parts;
-    dg_fill_units(units_a, before, parts, tid, nblk_a);
-    dg_fill_units(units_b, before, parts, tid, nblk_b);
+    for (int r = cnt; r < ((cnt + 15) & ~15); ++r) rowsrc[s_off16[tid] + r] = -1;  // padding rows
   }
+  const int sa = (nblk_a + 7) & ~7, sb = (nblk_b + 7) & ~7;
   if (tid == 0) {
-    *n_a = s_part[255] * ((nblk_a + 7) & ~7);
-    *n_b = s_part[255] * ((nblk_b + 7) & ~7);
+    *n_a = tot_parts * sa;
+    *n_b = tot_parts * sb;
+    *n_srows = tot_rows16;
+  }
+  // Work lists (as k_ws_units): part slot q belongs to the expert e with
+  // s_part[e - 1] <= q < s_part[e] (inclusive scan).
+  for (int u = tid; u < tot_parts * (sa + sb); u += 1024) {
+    const bool first = u < tot_parts * sa;
+    const int v = first ? u : u - tot_parts * sa, st = first ? sa : sb, nb = first ? nblk_a : nblk_b;
+    const int q = v / st, b = v - q * st;
+    int lo = 0, hi = 255;  // smallest e with s_part[e] > q
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_part[mid] > q) hi = mid;
+      else lo = mid + 1;
+    }
+    const int pe = q - (lo > 0 ? s_part[lo - 1] : 0);
+    const int32_t code = b < nb ? (int32_t)(((uint32_t)lo << 24) | ((uint32_t)pe << 16) | (uint32_t)b)
+                                : (int32_t)DG_WS_UNIT_NONE;
+    if (first) units_a[v] = code;
+    else units_b[v] = code;
   }
   for (int p = tid; p < npairs; p += 1024) {
     const int e = ids[p], t = p / k, tw = t >> 5;
     int rank = __popc(s_bits[e][tw] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < tw; ++w) rank += __popc(s_bits[e][w]);
     perm[s_off[e] + rank] = p;
-    spos[s_off[e] + rank] = s_off16[e] + rank;
+    rowsrc[s_off16[e] + rank] = t;
   }
 }
 
 // The expert-sorted row layout for the multi-kernel routing path (more rows than
-// k_route_tail takes), from counts and offsets: one block, E <= 256.
+// k_route_tail takes), from counts, offsets and perm: one block, E <= 256.
 __global__ void __launch_bounds__(256) k_sorted_layout(const int32_t* __restrict__ counts,
-                                                       const int32_t* __restrict__ offsets, int E,
-                                                       int32_t* __restrict__ offsets16, int32_t* __restrict__ spos) {
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ perm, int E, int k,
+                                                       int32_t* __restrict__ offsets16, int32_t* __restrict__ rowsrc,
+                                                       int32_t* __restrict__ n_srows) {
   __shared__ int s_off16[256];
   const int e = threadIdx.x;
   const int cnt = e < E ? counts[e] : 0, pad = (cnt + 15) & ~15;
@@ -216,24 +240,26 @@ __global__ void __launch_bounds__(256) k_sorted_layout(const int32_t* __restrict
     s_off16[e] += v;
     __syncthreads();
   }
+  if (e == 255) *n_srows = s_off16[255];
   if (e < E) {
     const int first = s_off16[e] - pad, off = offsets[e];
     offsets16[e] = first;
-    for (int r = 0; r < cnt; ++r) spos[off + r] = first + r;
+    for (int r = 0; r < pad; ++r) rowsrc[first + r] = r < cnt ? perm[off + r] / k : -1;
   }
 }
 
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
-                     int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* spos, int nblk_a,
-                     int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s) {
+                     int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
+                     int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b,
+                     hipStream_t s) {
   dg_launch_topk(logits, rows, E, k, ids, gates, s);
   if (rows <= DG_ROUTE_MAX_ROWS && E <= 256) {
-    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, spos, nblk_a, units_a, n_a,
-                                    nblk_b, units_b, n_b);
+    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, rowsrc, n_srows, nblk_a,
+                                    units_a, n_a, nblk_b, units_b, n_b);
     return;
   }
   dg_launch_permute(ids, rows, E, k, counts, offsets, perm, s);
-  k_sorted_layout<<<1, 256, 0, s>>>(counts, offsets, E, offsets16, spos);
+  k_sorted_layout<<<1, 256, 0, s>>>(counts, offsets, perm, E, k, offsets16, rowsrc, n_srows);
   dg_launch_ws_units(counts, E, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
 }
 

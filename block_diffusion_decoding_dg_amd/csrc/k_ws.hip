@@ -17,8 +17,10 @@
 // activation rows (m-tile i goes to wave i % 8) and read their own activation
 // fragments straight from global memory three chunks ahead.  Activations are in
 // the fragment-major layout (fm_index), so each fragment is one contiguous 1 KB
-// load; a grouped launch reads them from an expert-sorted copy in which every
-// expert's rows start on a 16-row tile.  The LDS rows are
+// load; the routed down projection reads them in an expert-sorted layout in
+// which every expert's rows start on a 16-row tile.  The routed W1/W3 launch
+// instead gathers its rows from the row-major normalised rows through the
+// sorted-row -> token map (a sorted copy would cost more than it saves).  The LDS rows are
 // XOR-swizzled in 16-byte units so that both the cooperative stores and the
 // fragment reads are free of bank conflicts.
 //
@@ -28,6 +30,7 @@
 #include "dg_common.h"
 #include "dg_kernels.h"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace {
@@ -75,9 +78,11 @@ __device__ __forceinline__ v8s (&abuf(AFrags<MT, KSUB>& F))[MT][2 * KSUB] {
 template <int EPI, int NTN>
 __device__ __forceinline__ const bf16_t* weight_row(const WsArgs& a, int g, int nb, int r) {
   if constexpr (EPI == WS_EPI_SWIGLU) {
-    // rows 0..31: W1 rows, rows 32..63: W3 rows, of the same 32 hidden columns
-    const bf16_t* W = (const bf16_t*)(r < 32 ? a.W0 : a.W1) + (size_t)g * a.wgs;
-    const int n = nb * 32 + (r & 31);
+    // rows 0 .. 8 NTN - 1: W1 rows, rows 8 NTN .. 16 NTN - 1: W3 rows, of the same
+    // 8 NTN hidden columns
+    constexpr int HALF = 8 * NTN;
+    const bf16_t* W = (const bf16_t*)(r < HALF ? a.W0 : a.W1) + (size_t)g * a.wgs;
+    const int n = nb * HALF + (r % HALF);
     return W + (size_t)min(n, a.N - 1) * a.K;
   } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
     // rows 0..31: columns j0 .. j0+31 of one head's first half, rows 32..63: the
@@ -127,7 +132,7 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
 // load address is clamped to valid memory, so the number of loads in flight is
 // the same in every iteration and the compiler can wait for exactly the load it
 // needs.  All variants execute the same barriers.
-template <int NTN, int KSUB, int MT, int MA>
+template <int NTN, int KSUB, int MT, int MA, bool GATHER>
 __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], const char* const (&gsrc)[NTN * KSUB / 4],
                                           const int (&slot)[NTN * KSUB / 4], const int (&sub)[NTN * KSUB / 4],
                                           const char* const (&ap)[MT], int nk64, int lane, v4f (&acc)[MT][NTN]) {
@@ -158,7 +163,8 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
 #pragma unroll
       for (int q = 0; q < 2 * KSUB; ++q) {
         const int kc = min(c * KSUB + q / 2, nk64 - 1);
-        A[j][q] = *(const v8s*)(ap[j] + (2 * kc + (q & 1)) * 1024);
+        if constexpr (GATHER) A[j][q] = *(const v8s*)(ap[j] + kc * 128 + (q & 1) * 64);  // row-major source row
+        else A[j][q] = *(const v8s*)(ap[j] + (2 * kc + (q & 1)) * 1024);               // fragment-major block
       }
   };
   fetch(R0, 0);
@@ -206,7 +212,7 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
   }
 }
 
-template <int EPI, int NTN, int KSUB, int MT>
+template <int EPI, int NTN, int KSUB, int MT, bool GATHER>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   constexpr int BN = 16 * NTN;
   constexpr int PASS_ROWS = NWAVE * MT * 16;
@@ -272,10 +278,17 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
     for (int j = 0; j < MT; ++j) {
       const int t0 = pbase + (wave + NWAVE * j) * 16;
       if (t0 < cnt) mt_act = j + 1;
-      // first row of this m-tile in the A matrix (a multiple of 16); a tile past
-      // the end is read from the last one, which holds valid rows
-      const int tr = arow0 + row0 + min(t0, (cnt - 1) & ~15);
-      ap[j] = (const char*)a.A + (size_t)(tr >> 4) * (a.K >> 5) * 1024 + lane * 16;
+      if constexpr (GATHER) {
+        // row-major source rows: lane l reads the token of sorted row (clamped to
+        // the group's rows) l % 16 of the m-tile
+        const int r = arow0 + row0 + min(t0 + (lane & 15), cnt - 1);
+        ap[j] = (const char*)((const bf16_t*)a.A + (size_t)a.rowsrc[r] * a.K) + (lane >> 4) * 16;
+      } else {
+        // first row of this m-tile in the A matrix (a multiple of 16); a tile past
+        // the end is read from the last one, which holds valid rows
+        const int tr = arow0 + row0 + min(t0, (cnt - 1) & ~15);
+        ap[j] = (const char*)a.A + (size_t)(tr >> 4) * (a.K >> 5) * 1024 + lane * 16;
+      }
     }
 
     v4f acc[MT][NTN];
@@ -284,9 +297,9 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
       for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else if (MT == 1 || mt_act == 1) ws_stream<NTN, KSUB, MT, 1>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else ws_stream<NTN, KSUB, MT, MT>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else if (MT == 1 || mt_act == 1) ws_stream<NTN, KSUB, MT, 1, GATHER>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else ws_stream<NTN, KSUB, MT, MT, GATHER>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
 
     // Epilogue.
     if constexpr (EPI == WS_EPI_LM_STATS) {
@@ -351,9 +364,10 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
             // expert-sorted row for a grouped launch)
             const int frow = arow0 + r;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-              const int col = nb * 32 + n * 16 + (lane & 15);
-              if (col < a.N) ((bf16_t*)a.out)[fm_index(frow, col, a.N)] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + 2][i]);
+            for (int n = 0; n < NTN / 2; ++n) {
+              const int col = nb * (8 * NTN) + n * 16 + (lane & 15);
+              if (col < a.N)
+                ((bf16_t*)a.out)[fm_index(frow, col, a.N)] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + NTN / 2][i]);
             }
           } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
             const int half = a.hd / 2, per_head = half / 32;
@@ -446,15 +460,20 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
+  if (a.rowsrc) {  // routed W1/W3: activation rows gathered from the row-major rows
+    if (epi != WS_EPI_SWIGLU) abort();
+    k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true><<<grid, NT, 0, s>>>(a);
+    return;
+  }
   switch (epi) {
-    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
     // The LM head keeps two m-tiles per wave: up to 256 rows in one pass, so the
     // embedding crosses HBM once per step.
-    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2, false><<<grid, NT, 0, s>>>(a); break;
     default: break;
   }
 }
