@@ -16,7 +16,9 @@ The JSON line carries:
   ms_per_step  timed ms / steps;
   roofline     the dominant kernel (routed-expert W1/W3 projection) measured
                with HIP events on the library's stream: algorithmic bytes per
-               launch / mean launch time against 8 TB/s;
+               launch / mean launch time against 8 TB/s; "traffic" is the HBM
+               bytes per launch that rocprofv3's counters measured for this
+               kernel source (profiles/ws_hbm_traffic.md), null once it changed;
   step_roofline  the whole step: algorithmic bytes and FLOPs per step against
                max(bytes / 8 TB/s, FLOPs / 2.5 PFLOP/s);
   cpu_baseline the CPU oracle on a bounded sample (one layer + LM head),
@@ -78,6 +80,24 @@ def step_flops(w, P, rows, n_open):
     f += 4 * w.n_layers * w.n_q_heads * hd * rows * (P + rows)
     f += 2 * n_open * d * w.vocab
     return f
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "ws_hbm_traffic.md")
+    src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", "k_ws.hip")
+    try:
+        fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and l.split(": ", 1)[0]
+                      in ("expert_up_traffic_bytes_per_launch", "k_ws_source_sha256"))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("k_ws_source_sha256", "").strip() != sha:
+        return None
+    return int(fields["expert_up_traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, tokens_per_step):
@@ -280,7 +300,8 @@ def main():
         "prefill_ms": prefill_ms,
         "roofline": {"bound": "hbm", "kernel": args.kernel,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                     "traffic": measured_traffic() if args.kernel == DOMINANT else None,
                      "launch_ms": launch_ms, "launches": kt_n, "bytes_per_launch": bpl},
         "step_roofline": {"bytes_per_step": mean_bytes, "flops_per_step": mean_flops,
                           "roofline_ms": roof_ms, "frac": roof_ms / ms_per_step,

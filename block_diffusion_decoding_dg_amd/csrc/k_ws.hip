@@ -60,6 +60,24 @@ struct Segs {
   uint4 v[N];
 };
 
+// Register ring of up to eight weight chunks, selected by a compile-time index
+// (a runtime index would put the ring in scratch memory).
+template <int N>
+struct Ring8 {
+  Segs<N> r0, r1, r2, r3, r4, r5, r6, r7;
+};
+template <int I, int N>
+__device__ __forceinline__ Segs<N>& ring(Ring8<N>& R) {
+  if constexpr (I == 0) return R.r0;
+  else if constexpr (I == 1) return R.r1;
+  else if constexpr (I == 2) return R.r2;
+  else if constexpr (I == 3) return R.r3;
+  else if constexpr (I == 4) return R.r4;
+  else if constexpr (I == 5) return R.r5;
+  else if constexpr (I == 6) return R.r6;
+  else return R.r7;
+}
+
 // Activation fragments of four consecutive chunks (chunk c in buffer c % 4),
 // selected by a compile-time index.
 template <int MT, int KSUB>
@@ -132,28 +150,29 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
 // load address is clamped to valid memory, so the number of loads in flight is
 // the same in every iteration and the compiler can wait for exactly the load it
 // needs.  All variants execute the same barriers.
-template <int NTN, int KSUB, int MT, int MA, bool GATHER>
+template <int NTN, int KSUB, int MT, int MA, bool GATHER, int RING>
 __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], const char* const (&gsrc)[NTN * KSUB / 4],
                                           const int (&slot)[NTN * KSUB / 4], const int (&sub)[NTN * KSUB / 4],
                                           const char* const (&ap)[MT], int nk64, int lane, v4f (&acc)[MT][NTN]) {
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte weight segments per thread per chunk
+  static_assert(RING == 4 || RING == 8, "ring of 4 or 8 chunks");
   const int nchunk = (nk64 + KSUB - 1) / KSUB;
-  Segs<NSEG> R0, R1, R2, R3;
-  auto fetch = [&](Segs<NSEG>& R, int c) {
+  Ring8<NSEG> R;
+  auto fetch = [&](Segs<NSEG>& S, int c) {
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       const int kc = min(c * KSUB + sub[i], nk64 - 1);
-      R.v[i] = *(const uint4*)(gsrc[i] + kc * 128);
+      S.v[i] = *(const uint4*)(gsrc[i] + kc * 128);
     }
   };
-  // Stores chunk c from R into its stage; sub-chunks past the end store zeros (a
+  // Stores chunk c from S into its stage; sub-chunks past the end store zeros (a
   // mask on the values: a conditional between two lvalues would make the compiler
   // select between their addresses and keep the ring in scratch memory).
-  auto store = [&](uint4* stage, const Segs<NSEG>& R, int c) {
+  auto store = [&](uint4* stage, const Segs<NSEG>& S, int c) {
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       const uint32_t live = c * KSUB + sub[i] < nk64 ? 0xffffffffu : 0u;
-      stage[slot[i]] = make_uint4(R.v[i].x & live, R.v[i].y & live, R.v[i].z & live, R.v[i].w & live);
+      stage[slot[i]] = make_uint4(S.v[i].x & live, S.v[i].y & live, S.v[i].z & live, S.v[i].w & live);
     }
   };
   AFrags<MT, KSUB> F;
@@ -167,24 +186,33 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
         else A[j][q] = *(const v8s*)(ap[j] + (2 * kc + (q & 1)) * 1024);               // fragment-major block
       }
   };
-  fetch(R0, 0);
-  fetch(R1, 1);
-  fetch(R2, 2);
-  fetch(R3, 3);
+  fetch(ring<0>(R), 0);
+  fetch(ring<1>(R), 1);
+  fetch(ring<2>(R), 2);
+  fetch(ring<3>(R), 3);
+  if constexpr (RING == 8) {
+    fetch(ring<4>(R), 4);
+    fetch(ring<5>(R), 5);
+    fetch(ring<6>(R), 6);
+    fetch(ring<7>(R), 7);
+  }
   fetch_a(abuf<0>(F), 0);
   fetch_a(abuf<1>(F), 1);
   fetch_a(abuf<2>(F), 2);
-  store(sW[0], R0, 0);
-  store(sW[1], R1, 1);
-  fetch(R0, 4);
-  fetch(R1, 5);
+  store(sW[0], ring<0>(R), 0);
+  store(sW[1], ring<1>(R), 1);
+  fetch(ring<0>(R), RING);
+  fetch(ring<1>(R), RING + 1);
   __syncthreads();
-  auto chunk = [&](auto JR, Segs<NSEG>& R, int c) {
-    constexpr int jr = decltype(JR)::value;   // == c % 4 (c0 is a multiple of 4)
-    constexpr int ahead = (jr + 2) & 3;       // stage and ring slot of chunk c + 2
+  // Chunk c at position J = c % RING of the unrolled loop (c0 a multiple of RING).
+  auto chunk = [&](auto JJ, int c) {
+    constexpr int J = decltype(JJ)::value;
+    constexpr int jr = J & 3;                  // LDS stage of chunk c (and its activation buffer)
+    constexpr int ahead = (jr + 2) & 3;        // stage of chunk c + 2
+    constexpr int rs = (J + 2) % RING;         // ring slot holding chunk c + 2
     fetch_a(abuf<(jr + 3) & 3>(F), c + 3);
-    store(sW[ahead], R, c + 2);
-    fetch(R, c + 6);
+    store(sW[ahead], ring<rs>(R), c + 2);
+    fetch(ring<rs>(R), c + 2 + RING);
     if constexpr (MA > 0) {
       v8s(&acur)[MT][2 * KSUB] = abuf<jr>(F);
 #pragma unroll
@@ -204,15 +232,22 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
     }
     __syncthreads();
   };
-  for (int c0 = 0; c0 < nchunk; c0 += 4) {
-    chunk(std::integral_constant<int, 0>{}, R2, c0);      // slot 2 holds chunk c0 + 2
-    chunk(std::integral_constant<int, 1>{}, R3, c0 + 1);  // slot 3 holds chunk c0 + 3
-    chunk(std::integral_constant<int, 2>{}, R0, c0 + 2);  // slot 0 holds chunk c0 + 4
-    chunk(std::integral_constant<int, 3>{}, R1, c0 + 3);  // slot 1 holds chunk c0 + 5
+  for (int c0 = 0; c0 < nchunk; c0 += RING) {
+    chunk(std::integral_constant<int, 0>{}, c0);
+    chunk(std::integral_constant<int, 1>{}, c0 + 1);
+    chunk(std::integral_constant<int, 2>{}, c0 + 2);
+    chunk(std::integral_constant<int, 3>{}, c0 + 3);
+    if constexpr (RING == 8) {
+      if (c0 + 4 >= nchunk) break;  // uniform; saves up to four padded chunks
+      chunk(std::integral_constant<int, 4>{}, c0 + 4);
+      chunk(std::integral_constant<int, 5>{}, c0 + 5);
+      chunk(std::integral_constant<int, 6>{}, c0 + 6);
+      chunk(std::integral_constant<int, 7>{}, c0 + 7);
+    }
   }
 }
 
-template <int EPI, int NTN, int KSUB, int MT, bool GATHER>
+template <int EPI, int NTN, int KSUB, int MT, bool GATHER, int RING>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   constexpr int BN = 16 * NTN;
   constexpr int PASS_ROWS = NWAVE * MT * 16;
@@ -297,9 +332,9 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
       for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else if (MT == 1 || mt_act == 1) ws_stream<NTN, KSUB, MT, 1, GATHER>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else ws_stream<NTN, KSUB, MT, MT, GATHER>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER, RING>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else if (MT == 1 || mt_act == 1) ws_stream<NTN, KSUB, MT, 1, GATHER, RING>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else ws_stream<NTN, KSUB, MT, MT, GATHER, RING>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
 
     // Epilogue.
     if constexpr (EPI == WS_EPI_LM_STATS) {
@@ -458,22 +493,34 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 
 }  // namespace
 
+// Register ring depth (chunks in flight per block).  Eight measured slower than
+// four for every launch of the denoising step: the blocks are bound by the
+// L2-to-CU traffic of their tiles, not by memory latency.
+#ifndef DG_WS_RING_DENSE
+#define DG_WS_RING_DENSE 4
+#endif
+#ifndef DG_WS_RING_ROUTED
+#define DG_WS_RING_ROUTED 4
+#endif
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
-  if (a.rowsrc) {  // routed W1/W3: activation rows gathered from the row-major rows
-    if (epi != WS_EPI_SWIGLU) abort();
-    k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true><<<grid, NT, 0, s>>>(a);
+  constexpr int RD = DG_WS_RING_DENSE, RR = DG_WS_RING_ROUTED;
+  if (a.counts) {  // grouped (routed experts)
+    if (a.rowsrc && epi == WS_EPI_SWIGLU) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, RR><<<grid, NT, 0, s>>>(a);
+    else if (!a.rowsrc && epi == WS_EPI_STORE_F32)
+      k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RR><<<grid, NT, 0, s>>>(a);
+    else abort();
     return;
   }
   switch (epi) {
-    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1, false><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     // The LM head keeps two m-tiles per wave: up to 256 rows in one pass, so the
     // embedding crosses HBM once per step.
-    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2, false><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2, false, 4><<<grid, NT, 0, s>>>(a); break;
     default: break;
   }
 }
