@@ -18,6 +18,8 @@
 #include "dg_common.h"
 #include "dg_kernels.h"
 
+#include <type_traits>
+
 #define ATTN_QROWS 128  // query rows per block (4 waves x 32)
 
 template <typename T, int HD>
@@ -224,8 +226,9 @@ __device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u) {
 // to nearest even) against V converted to fp16 when its tile is staged: a bf16
 // value has 8 significant bits, so the conversion is exact over fp16's normal
 // range; magnitudes below it keep an absolute error under 2^-25 and magnitudes
-// above 65504 are clamped to it.  The running output is rescaled only when some
-// row's maximum moved, and full tiles of a bidirectional step skip the mask.
+// above 65504 are clamped to it.  A row's reference maximum moves only when a
+// tile's maximum exceeds it by more than 2^8 (so P <= 256), which keeps the
+// rescaling of the running output rare.
 template <int HD>
 __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
                                                      int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
@@ -335,78 +338,96 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   }
   __syncthreads();
   int stg = 0;
+  // The reference maximum of a row (mrun) moves only when a tile's maximum
+  // exceeds it by more than RESCALE_TH (log2 units): P = 2^(s - mrun) then stays
+  // at most 2^RESCALE_TH, well inside fp16, and the running output and sum are
+  // rescaled rarely instead of on almost every tile.  The split's (mrun, lrun)
+  // pair is reported with its output, so the merge stays exact.
+  constexpr float RESCALE_TH = 8.f;
+  // Keys at or beyond klim[qt] are masked for row qt: the end of the range, and
+  // with a causal mask the row's own position + 1.
+  int klim[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) klim[qt] = sg.causal ? min(k_hi, qpos[qt] + 1) : k_hi;
+  // One tile: scores, softmax update, P V.
+  auto tile = [&](int kb) {
+    v4f st[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      st[kt][0] = st[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+      const int key = kt * 16 + c16;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & 7))];
+        const F kf = *reinterpret_cast<const F*>(&u);
+        st[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], st[kt][0], 0, 0, 0);
+        st[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], st[kt][1], 0, 0, 0);
+      }
+    }
+    float p[2][2][4];
+    bool grow = false;
+    float alpha[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + kt * 16 + g4 * 4 + i;
+          const float sc = key < klim[qt] ? st[kt][qt][i] * scale : -INFINITY;
+          p[kt][qt][i] = sc;
+          tmax = fmaxf(tmax, sc);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // a row's reference moves to its tile maximum when that exceeds it by more
+      // than the threshold (always on the row's first unmasked tile)
+      const bool move = tmax > mrun[qt] + RESCALE_TH;
+      const float mnew = move ? tmax : mrun[qt];
+      alpha[qt] = move ? __builtin_amdgcn_exp2f(mrun[qt] - mnew) : 1.f;  // 2^-inf = 0 on the first move
+      grow |= move;
+      mrun[qt] = mnew;
+      // rows with every score masked so far keep mrun = -inf: their P is 0
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(p[kt][qt][i] - mref);
+          p[kt][qt][i] = e;
+          psum += e;
+        }
+      lrun[qt] = lrun[qt] * alpha[qt] + psum;
+    }
+    if (__any(grow)) {  // wave-uniform; rare after the first tile
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        oacc[ht][0] *= alpha[0];
+        oacc[ht][1] *= alpha[1];
+      }
+    }
+    v8h pf[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf[qt][kt * 4 + i] = (_Float16)p[kt][qt][i];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int d = ht * 16 + c16;
+      const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
+      const v8h vf = *reinterpret_cast<const v8h*>(&u);
+      oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[0], oacc[ht][0], 0, 0, 0);
+      oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[1], oacc[ht][1], 0, 0, 0);
+    }
+  };
   for (int kb = k_lo; kb < k_hi; kb += 32) {
     const bool more = kb + 32 < k_hi;
     load_tile(more ? kb + 32 : kb, rk, rv);
-    if (wave_active) {
-      v4f st[2][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        st[kt][0] = st[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
-        const int key = kt * 16 + c16;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & 7))];
-          const F kf = *reinterpret_cast<const F*>(&u);
-          st[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], st[kt][0], 0, 0, 0);
-          st[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], st[kt][1], 0, 0, 0);
-        }
-      }
-      float p[2][2][4];
-      // no key of a full tile is masked in a bidirectional step (block-uniform)
-      const bool full = !sg.causal && kb + 32 <= k_hi;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb + kt * 16 + g4 * 4 + i;
-            float sc = st[kt][qt][i] * scale;
-            if (!full && (key >= k_hi || (sg.causal && key > qpos[qt]))) sc = -INFINITY;
-            p[kt][qt][i] = sc;
-            tmax = fmaxf(tmax, sc);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(mrun[qt], tmax);
-        // with every score of the row masked so far (mnew = -inf) the exponentials
-        // below are 0 and the (zero) running sums stay 0
-        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(mrun[qt] - mref);
-        float psum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = exp2f(p[kt][qt][i] - mref);
-            p[kt][qt][i] = e;
-            psum += e;
-          }
-        lrun[qt] = lrun[qt] * alpha + psum;
-        mrun[qt] = mnew;
-        if (__any(alpha != 1.f)) {  // some row's maximum moved
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] *= alpha;
-        }
-      }
-      v8h pf[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pf[qt][kt * 4 + i] = (_Float16)p[kt][qt][i];
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        const int d = ht * 16 + c16;
-        const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
-        const v8h vf = *reinterpret_cast<const v8h*>(&u);
-        oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[0], oacc[ht][0], 0, 0, 0);
-        oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[1], oacc[ht][1], 0, 0, 0);
-      }
-    }
+    if (wave_active) tile(kb);
     store_tile(stg ^ 1, rk, rv);
     __syncthreads();
     stg ^= 1;
