@@ -229,8 +229,8 @@ __device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u) {
 // above 65504 are clamped to it.  A row's reference maximum moves only when a
 // tile's maximum exceeds it by more than 2^8 (so P <= 256), which keeps the
 // rescaling of the running output rare.
-template <int HD>
-__global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
+template <int HD, int QT>
+__global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
                                                      int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
                                                      int rows_total) {
   typedef v8s F;
@@ -239,8 +239,9 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   constexpr int KSEG = HD / 8;            // 16-byte segments per key row
   constexpr int SEGS_K = 32 * KSEG;       // per tile
   constexpr int SEGS_V = HD * 4;          // per tile (HD rows of 32 keys)
-  constexpr int LK = SEGS_K / 256, LV = SEGS_V / 256;
-  static_assert(LK >= 1 && LV >= 1, "head_dim >= 64");
+  constexpr int NTHR = 512 / QT;         // 128 query rows per block, QT m-tiles per wave
+  constexpr int LK = SEGS_K / NTHR, LV = SEGS_V / NTHR;
+  static_assert(LK >= 1 && LV >= 1, "tile staging: head_dim too small for this wave count");
   __shared__ uint4 sK[2][SEGS_K];
   __shared__ uint4 sV[2][SEGS_V];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -258,13 +259,13 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   const int G = sh.hq / sh.hkv;
   const int nq = G * seg.n;
   if (qb * ATTN_QROWS >= nq) return;  // uniform over the block
-  const int qr0 = qb * ATTN_QROWS + wave * 32;
+  const int qr0 = qb * ATTN_QROWS + wave * 16 * QT;
   const bool wave_active = qr0 < nq;
 
-  int qhead[2], trow[2], qpos[2];
-  bool qvalid[2];
+  int qhead[QT], trow[QT], qpos[QT];
+  bool qvalid[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int qr = qr0 + qt * 16 + c16;
     qvalid[qt] = qr < nq;
     const int qrc = qvalid[qt] ? qr : nq - 1;
@@ -284,9 +285,9 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
     k_hi = min(k_hi, seg.pos0 + max_i + 1);
   }
 
-  F qf[2][NKK];
+  F qf[QT][NKK];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const char* qp = (const char*)(q + (size_t)trow[qt] * (sh.hq * HD) + qhead[qt] * HD) + g4 * 16;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[qt][kk] = *(const F*)(qp + kk * 64);
@@ -300,36 +301,41 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   auto load_tile = [&](int kb, uint4 (&rk)[LK], uint4 (&rv)[LV]) {
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int sid = tid + 256 * i, key = sid / KSEG, sgi = sid % KSEG;
+      const int sid = tid + NTHR * i, key = sid / KSEG, sgi = sid % KSEG;
       const int gk = min(kb + key, nkeys - 1);
       rk[i] = *(const uint4*)(kbase + (size_t)gk * HD + sgi * 8);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int sid = tid + 256 * i, d = sid >> 2, s4 = sid & 3;
+      const int sid = tid + NTHR * i, d = sid >> 2, s4 = sid & 3;
       rv[i] = *(const uint4*)(vbase + (size_t)d * sh.max_ctx + kb + s4 * 8);
     }
   };
   auto store_tile = [&](int stg, const uint4 (&rk)[LK], const uint4 (&rv)[LV]) {
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int sid = tid + 256 * i, key = sid / KSEG, sgi = sid % KSEG;
+      const int sid = tid + NTHR * i, key = sid / KSEG, sgi = sid % KSEG;
       sK[stg][key * KSEG + (sgi ^ (key & 7))] = rk[i];
     }
     uint2* v8 = reinterpret_cast<uint2*>(sV[stg]);
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int sid = tid + 256 * i, d = sid >> 2, s4 = sid & 3;
+      const int sid = tid + NTHR * i, d = sid >> 2, s4 = sid & 3;
       const int kt = s4 >> 1, g0 = (s4 & 1) * 2, sw = (d >> 1) & 3;
       v8[d * 8 + (g0 ^ sw) * 2 + kt] = make_uint2(bf2_to_h2(rv[i].x), bf2_to_h2(rv[i].y));        // keys 8 s4 .. +3
       v8[d * 8 + ((g0 + 1) ^ sw) * 2 + kt] = make_uint2(bf2_to_h2(rv[i].z), bf2_to_h2(rv[i].w));  // keys 8 s4 + 4 .. +7
     }
   };
 
-  v4f oacc[NHT][2];
+  v4f oacc[NHT][QT];
+  float mrun[QT], lrun[QT];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) oacc[ht][0] = oacc[ht][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) oacc[ht][qt] = v4f{0.f, 0.f, 0.f, 0.f};
+    mrun[qt] = -INFINITY;
+    lrun[qt] = 0.f;
+  }
 
   uint4 rk[LK], rv[LV];
   if (k_lo < k_hi) {
@@ -346,29 +352,31 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   constexpr float RESCALE_TH = 8.f;
   // Keys at or beyond klim[qt] are masked for row qt: the end of the range, and
   // with a causal mask the row's own position + 1.
-  int klim[2];
+  int klim[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) klim[qt] = sg.causal ? min(k_hi, qpos[qt] + 1) : k_hi;
+  for (int qt = 0; qt < QT; ++qt) klim[qt] = sg.causal ? min(k_hi, qpos[qt] + 1) : k_hi;
   // One tile: scores, softmax update, P V.
   auto tile = [&](int kb) {
-    v4f st[2][2];
+    v4f st[2][QT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      st[kt][0] = st[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) st[kt][qt] = v4f{0.f, 0.f, 0.f, 0.f};
       const int key = kt * 16 + c16;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & 7))];
         const F kf = *reinterpret_cast<const F*>(&u);
-        st[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], st[kt][0], 0, 0, 0);
-        st[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], st[kt][1], 0, 0, 0);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          st[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][kk], st[kt][qt], 0, 0, 0);
       }
     }
-    float p[2][2][4];
+    float p[2][QT][4];
     bool grow = false;
-    float alpha[2];
+    float alpha[QT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -403,14 +411,13 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
     }
     if (__any(grow)) {  // wave-uniform; rare after the first tile
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        oacc[ht][0] *= alpha[0];
-        oacc[ht][1] *= alpha[1];
-      }
-    }
-    v8h pf[2];
+      for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < QT; ++qt) oacc[ht][qt] *= alpha[qt];
+    }
+    v8h pf[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -420,8 +427,9 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
       const int d = ht * 16 + c16;
       const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
       const v8h vf = *reinterpret_cast<const v8h*>(&u);
-      oacc[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[0], oacc[ht][0], 0, 0, 0);
-      oacc[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[1], oacc[ht][1], 0, 0, 0);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qt], oacc[ht][qt], 0, 0, 0);
     }
   };
   for (int kb = k_lo; kb < k_hi; kb += 32) {
@@ -434,7 +442,7 @@ __global__ void __launch_bounds__(256, 1) k_attn_lds(const bf16_t* __restrict__ 
   }
   if (!wave_active) return;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
     lrun[qt] += __shfl_xor(lrun[qt], 32, 64);
     if (!qvalid[qt]) continue;
@@ -515,8 +523,12 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #define DG_ATTN(TT, HDV)                                                                                     \
   k_attn<TT, HDV><<<blocks, 256, 0, s>>>((const TT*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);         \
   k_attn_merge<TT, sizeof(TT) == 2><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (TT*)o)
+// m-tiles (16 query rows) per wave: one at head_dim >= 128 (eight waves, two per
+// SIMD, half the registers each), two at 64 (the tile staging needs 256 threads)
+#define DG_ATTN_QT(HDV) ((HDV) >= 128 ? 1 : 2)
 #define DG_ATTN_LDS(HDV)                                                                                    \
-  k_attn_lds<HDV><<<blocks, 256, 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);        \
+  k_attn_lds<HDV, DG_ATTN_QT(HDV)><<<blocks, 512 / DG_ATTN_QT(HDV), 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit,    \
+                                                                           opart, mlpart, rows);                   \
   k_attn_merge<bf16_t, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (bf16_t*)o)
   if (dtype == 1) {
     if (sh.hd == 256) { DG_ATTN_LDS(256); }
@@ -532,4 +544,5 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
   }
 #undef DG_ATTN
 #undef DG_ATTN_LDS
+#undef DG_ATTN_QT
 }
