@@ -30,10 +30,19 @@ void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed,
                      hipStream_t s);
 struct DgSampleArgs;
 void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, int d, float* x, hipStream_t s);
+// Pending partial sums of a split-reduction add projection: n ranges of
+// [rows][d] fp32, range k at p + k * stride; folded into x by the next row kernel.
+struct DgParts {
+  const float* p = nullptr;
+  int n = 0;
+  size_t stride = 0;
+};
 // fm: bf16 output in the fragment-major layout (fm_index) instead of row-major;
-// out_rm (optional, bf16): a second, row-major copy.
+// out_rm (optional, bf16): a second, row-major copy; parts: folded into x first
+// (x is then written back).
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm = nullptr);
+                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm = nullptr,
+                       const DgParts& parts = DgParts{});
 
 // y = A W^T; mode 0: store in dtype, 1: store fp32, 2: add into fp32 out.
 void dg_launch_gemm(int dtype, int mode, const void* A, int M, int K, const void* W, int N, void* out, int ldo,
@@ -73,7 +82,8 @@ void dg_launch_expert_down(int dtype, const void* h, int rows, int d, int E, int
 // x[t] += sum_j gates[t][j] y[t k + j] for every row, then (gain given) the
 // RMSNorm of the updated rows into out (model dtype).  d <= 16384, k <= 16.
 void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
-                            const void* gain, float eps, void* out, bool fm, hipStream_t s);
+                            const void* gain, float eps, void* out, bool fm, hipStream_t s,
+                            const DgParts& parts = DgParts{});
 // LM head over rows of hn [n][d] (dtype), n from n_dev (<= max_rows): partials then merge.
 void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_rows, int d, const void* embed,
                        int vocab, float* part, int32_t* part_arg, float* ent, float* lse, int32_t* amax,
@@ -129,7 +139,12 @@ struct WsArgs {
   int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it
   int M;                  // rows of the single group when counts is null
   const int32_t* M_dev;   // if set (and counts null): the row count, read on the device
-  int msplit;             // dense launches: row ranges per n-block (grid = nblk * msplit); 0 or 1 = none
+  int msplit;             // dense launches: row ranges per n-block; 0 or 1 = none
+  int ksplit;             // dense add launches: reduction ranges per n-block (partial sums); 0 or 1 = none
+  int kchunks;            // with ksplit: 64-element chunks of the reduction per range
+  float* part_out;        // with ksplit: partial sums [ksplit][rows][ldo] (fp32), range k at part_out + k * part_stride
+  size_t part_stride;
+  int wide;               // add launches: 128 output columns per block instead of 64
   int nblk;               // dense launches: number of n-blocks
   const int32_t* counts;  // grouped: rows per group
   const int32_t* offsets; // grouped: first position of each group in perm

@@ -20,6 +20,12 @@
 #include "dg.h"
 #include "dg_kernels.h"
 
+// Reduction ranges of a split-reduction add projection, at most (partial-sum
+// buffer: DG_MAX_KSPLIT x max_requests x canvas_len rows of d_model fp32).
+#ifndef DG_MAX_KSPLIT
+#define DG_MAX_KSPLIT 8
+#endif
+
 namespace {
 
 thread_local std::string g_create_error;
@@ -70,6 +76,8 @@ struct dg_ctx {
   float* x = nullptr;
   void* xn = nullptr;
   void* xr = nullptr;  // bf16: row-major copy of the FFN-normalised rows
+  float* parts = nullptr;  // partial sums of split-reduction add projections [ksplit][parts_rows][d]
+  int parts_rows = 0;
   void* q = nullptr;
   void* ao = nullptr;
   float* opart = nullptr;
@@ -235,6 +243,8 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->x = cv.take<float>(Tm * d * 4);
   c->xn = cv.take<void>(Tm * d * es);
   c->xr = cv.take<void>(Tm * d * es);
+  c->parts = cv.take<float>((size_t)DG_MAX_KSPLIT * Rs * d * 4);
+  c->parts_rows = Rs;
   c->q = cv.take<void>(Tm * qd * es);
   c->ao = cv.take<void>(Tm * qd * es);
   c->opart = cv.take<float>(attn_cap * m.n_q_heads * m.head_dim * 4);
@@ -363,6 +373,47 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 // Grouped launch over the expert-sorted rows: A is fragment-major in the
 // expert-sorted layout (c->offsets16), or row-major with rowsrc mapping each
 // sorted row to its row of A.
+// Output projection / shared-expert W2: out (fp32 [M][N], row-major) += A W^T.
+// 128 output columns per block and at most 128 rows (one pass), and when that
+// leaves CUs idle the reduction is split too: each range then stores its partial
+// sums into c->parts, and the returned DgParts must be folded into out by the
+// next row kernel (in range order, so the result is deterministic).
+DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, int N, float* out) {
+  if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = A;
+  a.W0 = W;
+  a.K = K;
+  a.N = N;
+  a.M = M;
+  a.out = out;
+  a.ldo = N;
+  a.wide = 1;
+  const int nblk = (N + 127) / 128, padded = (nblk + 7) / 8 * 8;
+  a.nblk = nblk;
+  a.msplit = std::max(1, (M + 127) / 128);
+  int ks = 1;
+  if (M <= c->parts_rows && N == c->cfg.d_model)
+    ks = std::min(DG_MAX_KSPLIT, std::max(1, DG_DENSE_BLOCKS / (padded * a.msplit)));
+  const int nk = K / 64;
+  const int kchunks = (nk + ks - 1) / ks;
+  ks = (nk + kchunks - 1) / kchunks;  // every range non-empty
+  DgParts pend;
+  if (ks > 1) {
+    a.ksplit = ks;
+    a.kchunks = kchunks;
+    a.part_out = c->parts;
+    a.part_stride = (size_t)c->parts_rows * N;
+    pend.p = c->parts;
+    pend.n = ks;
+    pend.stride = a.part_stride;
+  }
+  const int grid = (a.msplit > 1 || ks > 1) ? padded * a.msplit * ks : nblk;
+  dg_launch_ws(WS_EPI_ADD_F32, a, grid, c->stream);
+  return pend;
+}
+
 void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void* W1, size_t wgs, int K, int N,
                    const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo,
                    const int32_t* rowsrc = nullptr) {
@@ -444,7 +495,9 @@ void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t
 // Attention half of layer l over `rows` rows in c->x.
 // norm_done: c->xn already holds the normalised rows (fused into the previous
 // layer's combine).
-void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal, bool norm_done = false) {
+// Returns the output projection's pending partial sums (bf16 model), which the
+// caller folds into c->x with its next row kernel.
+DgParts attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bool causal, bool norm_done = false) {
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
@@ -457,25 +510,29 @@ void attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows, bo
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
   const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
   KT(c, DG_KF_ATTENTION, dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s));
+  DgParts pend;
   if (c->dtype == DG_F32)
     KT(c, DG_KF_OUT_PROJ, dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x,
                                          m.d_model, s));
   else
-    KT(c, DG_KF_OUT_PROJ, launch_dense(c, WS_EPI_ADD_F32, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, nullptr,
-                                       m.d_model, c->x, m.d_model));
+    KT(c, DG_KF_OUT_PROJ, pend = launch_dense_add(c, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x));
+  return pend;
 }
 
 // FFN half of layer l over `rows` rows in c->x; routing written to ids/gates,
 // router logits to rlog ([rows][E] fp32).  next_gain: the RMSNorm gain of the
 // next layer's attention, applied to the updated rows into c->xn by the combine.
-void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlog, const void* next_gain = nullptr) {
+// pend: the output projection's partial sums, folded into c->x by the FFN norm.
+void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlog, const void* next_gain = nullptr,
+              const DgParts& pend = DgParts{}) {
   const dg_model_config& m = c->cfg;
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
   // bf16: fragment-major for the dense projections, and a row-major copy that the
   // expert-sorted gather reads
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps,
-                                         c->xn, c->dtype == DG_BF16, s, c->dtype == DG_BF16 ? c->xr : nullptr));
+                                         c->xn, c->dtype == DG_BF16, s, c->dtype == DG_BF16 ? c->xr : nullptr, pend));
+  DgParts pend2;  // the shared expert's W2 partial sums, folded by the combine
   if (c->dtype == DG_F32) {
     KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, rlog, m.n_experts, s);
                             dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s));
@@ -504,11 +561,10 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
                                            m.d_model));
     KT(c, DG_KF_SHARED_UP, launch_dense(c, WS_EPI_SWIGLU, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs,
                                         m.shared_hidden));
-    KT(c, DG_KF_SHARED_DOWN, launch_dense(c, WS_EPI_ADD_F32, c->hs, rows, m.shared_hidden, w.sw2, nullptr, m.d_model, c->x,
-                                          m.d_model));
+    KT(c, DG_KF_SHARED_DOWN, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x));
   }
   KT(c, DG_KF_COMBINE, dg_launch_combine_norm(c->dtype, c->x, c->ybuf, gates, rows, m.d_model, m.top_k, next_gain,
-                                              m.rms_eps, c->xn, c->dtype == DG_BF16, s));
+                                              m.rms_eps, c->xn, c->dtype == DG_BF16, s, pend2));
 }
 
 // Forward of the rows in c->x through all layers.  kv_only: the last layer only
@@ -527,12 +583,12 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
       KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
       break;
     }
-    attn_half(c, l, slots, rows, causal, xn_ready);
+    const DgParts pend = attn_half(c, l, slots, rows, causal, xn_ready);
     int32_t* ids = tap ? c->tap_ids + (size_t)l * c->rows_step * m.top_k : c->rids;
     float* gates = tap ? c->tap_gates + (size_t)l * c->rows_step * m.top_k : c->rgates;
     float* rlog = tap ? c->tap_logits + (size_t)l * c->rows_step * m.n_experts : c->rlogits;
     const void* next_gain = last ? nullptr : c->layers[l + 1].attn_norm;
-    ffn_half(c, l, rows, ids, gates, rlog, next_gain);
+    ffn_half(c, l, rows, ids, gates, rlog, next_gain, pend);
     xn_ready = next_gain != nullptr;
   }
 }
@@ -926,7 +982,11 @@ dg_status dg_op_attention(dg_ctx* c, int32_t req, int32_t layer, float* x_dev, i
   const size_t bytes = (size_t)t * c->cfg.d_model * 4;
   HIPCK(c, hipMemcpyAsync(c->x, x_dev, bytes, hipMemcpyDeviceToDevice, c->stream));
   std::vector<SlotRow> slots{{req, pos0, t}};
-  attn_half(c, layer, slots, t, causal != 0);
+  const DgParts pend = attn_half(c, layer, slots, t, causal != 0);
+  // fold the output projection's partial sums into x (no norm follows here)
+  if (pend.n > 0)
+    dg_launch_combine_norm(c->dtype, c->x, nullptr, nullptr, t, c->cfg.d_model, 0, nullptr, c->cfg.rms_eps, nullptr,
+                           true, c->stream, pend);
   LAUNCHCK(c);
   HIPCK(c, hipMemcpyAsync(x_dev, c->x, bytes, hipMemcpyDeviceToDevice, c->stream));
   HIPCK(c, hipStreamSynchronize(c->stream));

@@ -52,6 +52,8 @@ void dg_launch_embed_slots(int dtype, const DgSampleArgs& a, const void* embed, 
 // ---------------------------------------------------------------------------
 // Row kernel over the fp32 residual stream: one block of 256 threads per row, the
 // row held in registers as float4 (NV per thread, d <= 1024 NV).
+//   partials (nparts > 0): x[t] += sum_s parts[s][t], the partial sums of a
+//     projection whose reduction was split, in range order, written back;
 //   combine (y given): x[t] += sum_j gates[t][j] y[t k + j], written back (the
 //     gate-weighted sum of the routed experts' outputs, j in increasing order);
 //   RMSNorm (g given): out[i] = x[t] / sqrt(mean(x[t]^2) + eps) * g in the model
@@ -86,6 +88,7 @@ __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
 template <typename T, int NV, bool FM>
 __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const int32_t* __restrict__ row_idx,
                                                   const int32_t* __restrict__ n_dev, int d,
+                                                  const float* __restrict__ parts, int nparts, size_t part_stride,
                                                   const float* __restrict__ y, const float* __restrict__ gates, int k,
                                                   const T* __restrict__ g, float eps, T* __restrict__ out,
                                                   T* __restrict__ out_rm) {
@@ -102,6 +105,14 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
     v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < nv) {
       float4 a = xr[c];
+      // pending partial sums of a split-reduction projection, in range order
+      for (int sp = 0; sp < nparts; ++sp) {
+        const float4 pp = reinterpret_cast<const float4*>(parts + sp * part_stride + (size_t)t * d)[c];
+        a.x += pp.x;
+        a.y += pp.y;
+        a.z += pp.z;
+        a.w += pp.w;
+      }
       if (y) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int j0 = 0; j0 < k; j0 += 8) {
@@ -125,8 +136,8 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
         a.y += acc.y;
         a.z += acc.z;
         a.w += acc.w;
-        xr[c] = a;
       }
+      if (y || nparts) xr[c] = a;
       v[u] = a;
       ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
     }
@@ -152,10 +163,12 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
 
 template <typename T, bool FM>
 void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d, const float* y,
-                     const float* gates, int k, const T* g, float eps, T* out, hipStream_t s, T* out_rm = nullptr) {
+                     const float* gates, int k, const T* g, float eps, T* out, hipStream_t s, T* out_rm = nullptr,
+                     const DgParts& pp = DgParts{}) {
   const int nv = (d / 4 + 255) / 256;
-#define DG_ROW_NORM(NVV) \
-  k_row_norm<T, NVV, FM><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, y, gates, k, g, eps, out, out_rm)
+#define DG_ROW_NORM(NVV)                                                                                     \
+  k_row_norm<T, NVV, FM><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, pp.p, pp.n, pp.stride, y, gates, k, g, eps, out, \
+                                              out_rm)
   if (nv <= 1) DG_ROW_NORM(1);
   else if (nv <= 2) DG_ROW_NORM(2);
   else if (nv <= 3) DG_ROW_NORM(3);
@@ -166,13 +179,15 @@ void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int
 }
 
 void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm) {
+                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm,
+                       const DgParts& parts) {
   if (rows <= 0) return;
-  // x is only read: the combine part is off (y == nullptr)
+  // x is only read unless partial sums are folded in (the combine part is off)
   float* xm = const_cast<float*>(x);
   if (dtype == 1 && fm)
     launch_row_norm<bf16_t, true>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
-                                  (bf16_t*)out, s, (bf16_t*)out_rm);
+                                  (bf16_t*)out, s, (bf16_t*)out_rm, parts);
+  else if (parts.n > 0) abort();  // partial sums come only from the bf16 streaming kernel
   else if (dtype == 1)
     launch_row_norm<bf16_t, false>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
                                    (bf16_t*)out, s);
@@ -182,11 +197,12 @@ void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const 
 }
 
 void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
-                            const void* gain, float eps, void* out, bool fm, hipStream_t s) {
+                            const void* gain, float eps, void* out, bool fm, hipStream_t s, const DgParts& parts) {
   if (rows <= 0) return;
   if (dtype == 1 && fm)
     launch_row_norm<bf16_t, true>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps,
-                                  (bf16_t*)out, s);
+                                  (bf16_t*)out, s, nullptr, parts);
+  else if (parts.n > 0) abort();  // partial sums come only from the bf16 streaming kernel
   else if (dtype == 1)
     launch_row_norm<bf16_t, false>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps,
                                    (bf16_t*)out, s);

@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte segments per thread per chunk
   __shared__ uint4 sW[4][BN * 8 * KSUB];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int g = 0, nb = blockIdx.x, ms = 0;
+  int g = 0, nb = blockIdx.x, ms = 0, ks = 0;
   int part = -1;
   if (a.units) {
     if ((int)blockIdx.x >= *a.n_units) return;
@@ -263,15 +263,20 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
     g = (int)(code >> 24);
     part = (int)((code >> 16) & 0xff);
     nb = (int)(code & 0xffff);
-  } else if (a.msplit > 1) {
-    // Row split of a dense launch.  Work-groups are dealt to the 8 XCDs in turn
-    // (block b runs on XCD b % 8), so tile nb is given to XCD nb % 8 and its
-    // msplit row ranges to consecutive slots of that XCD: they start together and
-    // share that XCD's L2, and the tile crosses HBM once.  The grid is padded to
-    // 8 * ceil(nblk / 8) * msplit; padding blocks exit at once.
-    const int b = blockIdx.x, x = b % 8, j = b / 8;
-    ms = j % a.msplit;
-    nb = x + 8 * (j / a.msplit);
+  } else if (a.msplit > 1 || a.ksplit > 1) {
+    // Row and reduction split of a dense launch.  Work-groups are dealt to the 8
+    // XCDs in turn (block b runs on XCD b % 8), so tile nb is given to XCD nb % 8
+    // and its msplit x ksplit parts to consecutive slots of that XCD: the row
+    // parts of one reduction range start together and share that XCD's L2, and
+    // the tile crosses HBM once.  The grid is padded to 8 * ceil(nblk / 8) *
+    // msplit * ksplit; padding blocks exit at once.
+    // (an unset split count, 0, means 1)
+    const int msp = max(a.msplit, 1), ksp = max(a.ksplit, 1);
+    const int b = blockIdx.x, x = b % 8, j = b / 8, nsub = msp * ksp;
+    const int sub = j % nsub;
+    ks = sub / msp;
+    ms = sub % msp;
+    nb = x + 8 * (j / nsub);
     if (nb >= a.nblk) return;
   }
   int cnt = a.counts ? a.counts[g] : (a.M_dev ? *a.M_dev : a.M);
@@ -288,7 +293,10 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   if (cnt <= 0) return;  // uniform over the block
   const int off = a.counts ? a.offsets[g] : 0;
   const int arow0 = a.counts ? a.offsets16[g] : 0;  // group's first row in the A matrix
-  const int nk64 = a.K / 64;  // 64-element sub-chunks of the reduction
+  // 64-element sub-chunks of the reduction: this block's range of them
+  const int kc0 = ks * a.kchunks;
+  const int nk64 = a.ksplit > 1 ? min(a.K / 64 - kc0, a.kchunks) : a.K / 64;
+  if (nk64 <= 0) return;  // uniform over the block
 
   // This thread's 16-byte segments of every weight chunk: segment id
   // tid + NT i -> weight row id / (8 KSUB), segment id % (8 KSUB) within the
@@ -298,7 +306,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
   for (int i = 0; i < NSEG; ++i) {
     const int sid = tid + NT * i, wr = sid / (8 * KSUB), sg = sid % (8 * KSUB);
-    gsrc[i] = (const char*)weight_row<EPI, NTN>(a, g, nb, wr) + (sg & 7) * 16;
+    gsrc[i] = (const char*)(weight_row<EPI, NTN>(a, g, nb, wr) + kc0 * 64) + (sg & 7) * 16;
     slot[i] = lds_slot<KSUB>(wr, sg);
     sub[i] = sg >> 3;
   }
@@ -317,12 +325,12 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
         // row-major source rows: lane l reads the token of sorted row (clamped to
         // the group's rows) l % 16 of the m-tile
         const int r = arow0 + row0 + min(t0 + (lane & 15), cnt - 1);
-        ap[j] = (const char*)((const bf16_t*)a.A + (size_t)a.rowsrc[r] * a.K) + (lane >> 4) * 16;
+        ap[j] = (const char*)((const bf16_t*)a.A + (size_t)a.rowsrc[r] * a.K + kc0 * 64) + (lane >> 4) * 16;
       } else {
         // first row of this m-tile in the A matrix (a multiple of 16); a tile past
         // the end is read from the last one, which holds valid rows
         const int tr = arow0 + row0 + min(t0, (cnt - 1) & ~15);
-        ap[j] = (const char*)a.A + (size_t)(tr >> 4) * (a.K >> 5) * 1024 + lane * 16;
+        ap[j] = (const char*)a.A + ((size_t)(tr >> 4) * (a.K >> 5) + 2 * kc0) * 1024 + lane * 16;
       }
     }
 
@@ -448,6 +456,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
               const size_t o = (size_t)orow * a.ldo + col;
               if constexpr (EPI == WS_EPI_STORE_BF16) ((bf16_t*)a.out)[o] = f2bf(acc[j][n][i]);
               else if constexpr (EPI == WS_EPI_STORE_F32) ((float*)a.out)[o] = acc[j][n][i];
+              else if (a.ksplit > 1) a.part_out[(size_t)ks * a.part_stride + o] = acc[j][n][i];  // partial sum
               else ((float*)a.out)[o] += acc[j][n][i];
             }
           }
@@ -515,7 +524,11 @@ void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   switch (epi) {
     case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32:
+      // 128 output columns per block (half the activation re-reads of 64)
+      if (a.wide) k_ws<WS_EPI_ADD_F32, 8, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
+      else k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
+      break;
     case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     // The LM head keeps two m-tiles per wave: up to 256 rows in one pass, so the
