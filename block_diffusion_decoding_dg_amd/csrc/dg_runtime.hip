@@ -65,6 +65,9 @@ struct dg_ctx {
   std::vector<dg_layer_weights> layers;
   char* kv = nullptr;
   hipStream_t stream = nullptr;
+  hipStream_t side = nullptr;              // second stream: the shared expert overlaps the routed ones
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipError_t sticky = hipSuccess;          // first failed stream call of a void helper
   int C = 256;
   int rows_step = 0;   // max_requests * C
   int rows_max = 0;    // max(rows_step, prefill_chunk)
@@ -77,6 +80,7 @@ struct dg_ctx {
   void* xn = nullptr;
   void* xr = nullptr;  // bf16: row-major copy of the FFN-normalised rows
   float* parts = nullptr;  // partial sums of split-reduction add projections [ksplit][parts_rows][d]
+  float* parts2 = nullptr;  // the same for the shared expert's W2 (side stream)
   int parts_rows = 0;
   void* q = nullptr;
   void* ao = nullptr;
@@ -149,26 +153,34 @@ dg_status fail(dg_ctx* c, dg_status st, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));     \
   } while (0)
 
+// Launch errors, and the first error of a stream call inside a void helper
+// (recorded by HIPCK_V), are reported by the next LAUNCHCK of the entry point.
 #define LAUNCHCK(ctx)                                                                                  \
   do {                                                                                                 \
-    hipError_t e_ = hipGetLastError();                                                                 \
+    hipError_t e_ = (ctx)->sticky != hipSuccess ? (ctx)->sticky : hipGetLastError();                  \
+    (ctx)->sticky = hipSuccess;                                                                        \
     if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+#define HIPCK_V(call)                                              \
+  do {                                                             \
+    hipError_t e_ = (call);                                        \
+    if (e_ != hipSuccess && c->sticky == hipSuccess) c->sticky = e_; \
   } while (0)
 
 // Kernel timer.  kt_begin/kt_end bracket one launch of family f; the events are
 // read back (and the pairs reused) by kt_collect after the stream has synchronised.
-void kt_begin(dg_ctx* c, int f) {
+void kt_begin(dg_ctx* c, int f, hipStream_t s) {
   if (c->kt_family != f) return;
   while (c->kt_ev.size() < c->kt_used + 2) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) { c->kt_family = 0; return; }
     c->kt_ev.push_back(e);
   }
-  hipEventRecord(c->kt_ev[c->kt_used], c->stream);
+  hipEventRecord(c->kt_ev[c->kt_used], s);
 }
-void kt_end(dg_ctx* c, int f) {
+void kt_end(dg_ctx* c, int f, hipStream_t s) {
   if (c->kt_family != f) return;
-  hipEventRecord(c->kt_ev[c->kt_used + 1], c->stream);
+  hipEventRecord(c->kt_ev[c->kt_used + 1], s);
   c->kt_used += 2;
 }
 void kt_collect(dg_ctx* c) {
@@ -181,11 +193,18 @@ void kt_collect(dg_ctx* c) {
   }
   c->kt_used = 0;
 }
-#define KT(c, fam, launch) \
-  do {                     \
-    kt_begin((c), (fam));  \
-    launch;                \
-    kt_end((c), (fam));    \
+#define KT(c, fam, launch)           \
+  do {                               \
+    kt_begin((c), (fam), (c)->stream); \
+    launch;                          \
+    kt_end((c), (fam), (c)->stream);   \
+  } while (0)
+// The same for a launch on stream st.
+#define KTS(c, fam, st, launch) \
+  do {                          \
+    kt_begin((c), (fam), (st)); \
+    launch;                     \
+    kt_end((c), (fam), (st));   \
   } while (0)
 
 int kc_of(int dtype) { return dtype == DG_BF16 ? 32 : 16; }
@@ -244,6 +263,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->xn = cv.take<void>(Tm * d * es);
   c->xr = cv.take<void>(Tm * d * es);
   c->parts = cv.take<float>((size_t)DG_MAX_KSPLIT * Rs * d * 4);
+  c->parts2 = cv.take<float>((size_t)DG_MAX_KSPLIT * Rs * d * 4);
   c->parts_rows = Rs;
   c->q = cv.take<void>(Tm * qd * es);
   c->ao = cv.take<void>(Tm * qd * es);
@@ -352,7 +372,7 @@ int dense_msplit(int nblk, int M) {
 // 8 (see k_ws), so the tile count is padded to a multiple of 8.
 int dense_grid(int nblk, int msplit) { return msplit > 1 ? (nblk + 7) / 8 * 8 * msplit : nblk; }
 void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W0, const void* W1, int N, void* out,
-                  int ldo) {
+                  int ldo, hipStream_t st = nullptr) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
   WsArgs a;
   memset(&a, 0, sizeof a);
@@ -367,7 +387,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   const int nblk = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, M);
-  dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), c->stream);
+  dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), st ? st : c->stream);
 }
 
 // Grouped launch over the expert-sorted rows: A is fragment-major in the
@@ -378,7 +398,9 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 // leaves CUs idle the reduction is split too: each range then stores its partial
 // sums into c->parts, and the returned DgParts must be folded into out by the
 // next row kernel (in range order, so the result is deterministic).
-DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, int N, float* out) {
+DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, int N, float* out,
+                         hipStream_t st = nullptr, float* parts = nullptr) {
+  if (!parts) parts = c->parts;
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
   WsArgs a;
   memset(&a, 0, sizeof a);
@@ -403,14 +425,14 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   if (ks > 1) {
     a.ksplit = ks;
     a.kchunks = kchunks;
-    a.part_out = c->parts;
+    a.part_out = parts;
     a.part_stride = (size_t)c->parts_rows * N;
-    pend.p = c->parts;
+    pend.p = parts;
     pend.n = ks;
     pend.stride = a.part_stride;
   }
   const int grid = (a.msplit > 1 || ks > 1) ? padded * a.msplit * ks : nblk;
-  dg_launch_ws(WS_EPI_ADD_F32, a, grid, c->stream);
+  dg_launch_ws(WS_EPI_ADD_F32, a, grid, st ? st : c->stream);
   return pend;
 }
 
@@ -544,6 +566,17 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KT(c, DG_KF_SHARED_UP, dg_launch_swiglu(c->dtype, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs, s));
     KT(c, DG_KF_SHARED_DOWN, dg_launch_gemm(c->dtype, 2, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x, m.d_model, s));
   } else {
+    // The shared expert depends only on the normalised rows: it runs on the side
+    // stream beside the router, the routing and the routed launches, filling the
+    // GPU while those small or draining launches leave it idle.  (Forking later,
+    // beside the routed launches alone, measured slower: they then share HBM.)
+    HIPCK_V(hipEventRecord(c->ev_fork, s));
+    HIPCK_V(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+    KTS(c, DG_KF_SHARED_UP, c->side, launch_dense(c, WS_EPI_SWIGLU, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden,
+                                                  c->hs, m.shared_hidden, c->side));
+    KTS(c, DG_KF_SHARED_DOWN, c->side, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x,
+                                                                c->side, c->parts2));
+    HIPCK_V(hipEventRecord(c->ev_join, c->side));
     KT(c, DG_KF_ROUTER, launch_dense(c, WS_EPI_STORE_F32, c->xn, rows, m.d_model, w.router, nullptr, m.n_experts, rlog,
                                      m.n_experts));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
@@ -559,10 +592,8 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, (size_t)m.d_model * m.expert_hidden,
                                            m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,
                                            m.d_model));
-    KT(c, DG_KF_SHARED_UP, launch_dense(c, WS_EPI_SWIGLU, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden, c->hs,
-                                        m.shared_hidden));
-    KT(c, DG_KF_SHARED_DOWN, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x));
   }
+  if (c->dtype == DG_BF16) HIPCK_V(hipStreamWaitEvent(s, c->ev_join, 0));  // the shared expert is done
   KT(c, DG_KF_COMBINE, dg_launch_combine_norm(c->dtype, c->x, c->ybuf, gates, rows, m.d_model, m.top_k, next_gain,
                                               m.rms_eps, c->xn, c->dtype == DG_BF16, s, pend2));
 }
@@ -691,10 +722,16 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   if (e == hipSuccess) e = hipMemsetAsync(c->kv, 0, need_kv, c->stream);
   if (e == hipSuccess) e = hipMemsetAsync(c->canvas_acc, 1, c->rows_step, c->stream);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->info_host, m.max_requests * 4 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);  // default priority
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) {
     fail(nullptr, DG_ERR_HIP, "create: %s", hipGetErrorString(e));
     if (c->info_host) hipHostFree(c->info_host);
+    if (c->ev_fork) hipEventDestroy(c->ev_fork);
+    if (c->ev_join) hipEventDestroy(c->ev_join);
+    if (c->side) hipStreamDestroy(c->side);
     delete c;
     return DG_ERR_HIP;
   }
@@ -705,7 +742,11 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
 void dg_destroy(dg_ctx* ctx) {
   if (!ctx) return;
   hipStreamSynchronize(ctx->stream);
+  if (ctx->side) hipStreamSynchronize(ctx->side);
   for (hipEvent_t e : ctx->kt_ev) hipEventDestroy(e);
+  if (ctx->ev_fork) hipEventDestroy(ctx->ev_fork);
+  if (ctx->ev_join) hipEventDestroy(ctx->ev_join);
+  if (ctx->side) hipStreamDestroy(ctx->side);
   if (ctx->info_host) hipHostFree(ctx->info_host);
   delete ctx;
 }

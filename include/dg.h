@@ -158,9 +158,12 @@ dg_status dg_workspace_size(const dg_model_config* cfg, size_t* kv_bytes, size_t
 /*
  * Create a context.  Validates the configuration, carves the scratch buffer and
  * records the weight pointers (not copied: they must outlive the context).
- * stream is a hipStream_t (NULL: the null stream).  On success *out receives
- * the context; on failure *out is set to NULL and the message is available
- * from dg_last_error(NULL).
+ * stream is a hipStream_t (NULL: the null stream).  The context also creates
+ * one stream of its own (default priority) on which the bf16 model's shared
+ * expert runs beside the routed experts; it is joined back into `stream` with
+ * events inside every call, so each call's work is still ordered on `stream`.
+ * On success *out receives the context; on failure *out is set to NULL and the
+ * message is available from dg_last_error(NULL).
  */
 dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg,
                     const dg_weights* weights, void* kv_dev, size_t kv_bytes, void* scratch_dev,
