@@ -18,4 +18,4 @@ from .model import (ModelConfig, LayerWeights, Weights, Precision, round_bf16, r
                     attention, silu, topk_select, route, moe, layer_forward, lm_head_stats)
 from .philox import philox4x64_10, draw_tokens
 from .decode import (SamplerConfig, RequestState, StepResult, new_request, prefill, start_canvas,
-                     canvas_forward, sampler_decide, denoise_step, commit_block, generate)
+                     canvas_forward, sampler_decide, entropy_fixed, budget_decide, denoise_step, commit_block, generate)

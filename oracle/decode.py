@@ -17,15 +17,31 @@ generation changes the bottleneck":
 5. a finished block is committed to the KV cache and the next canvas is
    conditioned on it; nothing of the canvas enters the cache before that.
 
-The pages leave the acceptance rule open (the budget sampler of the second
-page is described only in words).  Rule implemented, a stated reading: the
-candidate is the argmax token; among open positions, accept those whose
-softmax entropy is strictly below tau, and always the single open position of
-lowest entropy (ties to the lower position); accepted positions never change.
-At the step cap every position still open is forced to its argmax.  The
+Two accept rules, both with the argmax token as the candidate, accepted
+positions never changing and every open position forced to its argmax at the
+step cap:
+
+* "threshold" (a stated reading where the pages leave the rule open): among
+  open positions accept those whose softmax entropy is strictly below tau, and
+  always the single open position of lowest entropy (ties to the lower
+  position).
+* "budget", the default sampler of "DiffusionGemma hits ~1,500 TPS on one
+  H100", section "How the sampler actually works" (budget 0.1, stop threshold
+  0.005), which the pages describe in words only.  Readings taken: open
+  positions are taken in order of rising entropy (ties to the lower position)
+  while the running sum of their entropies, this one included, stays within
+  the budget, and the first of them always (so that every step makes
+  progress); the block stops early when the argmax canvas (accepted positions
+  at their token, open ones at this step's argmax) equals the previous step's
+  and the mean entropy of the open positions is below the stop threshold: then
+  every open position is forced to its argmax, as at the cap.  The sums and
+  the mean are taken exactly on entropies in 64-bit fixed point (2^-40 nat
+  units, see `entropy_fixed`), so that their decisions do not depend on the
+  order of summation.  The
 committed K/V of a block are those of one more forward over the final canvas.
 Prompt positions attend causally (the parent model is autoregressive).
 """
+import math
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -39,6 +55,9 @@ from .philox import draw_tokens
 class SamplerConfig:
     tau: float
     max_steps: int  # step cap per block
+    mode: str = "threshold"      # or "budget"
+    budget: float = 0.1          # entropy budget per step ("budget" mode)
+    stop_entropy: float = 0.005  # early-stop mean entropy ("budget" mode)
 
 
 @dataclass
@@ -53,6 +72,7 @@ class RequestState:
     active: bool = False
     ids: Optional[np.ndarray] = None       # [C] int64 canvas token ids
     accepted: Optional[np.ndarray] = None  # [C] bool
+    prev_argmax: Optional[np.ndarray] = None  # [C] argmax canvas of the previous step of this block
 
 
 @dataclass
@@ -72,6 +92,7 @@ class StepResult:
     layers: list             # per-layer LayerTrace (router decisions etc.)
     logits: Optional[np.ndarray] = None
     hidden: Optional[np.ndarray] = None
+    stopped: bool = False    # "budget" mode: the early stop fired this step
 
 
 def new_request(cfg: ModelConfig, seed: int, max_ctx: int) -> RequestState:
@@ -114,6 +135,7 @@ def start_canvas(st: RequestState, cfg: ModelConfig):
     c = cfg.canvas_len
     st.ids = draw_tokens(st.seed, st.block, 0, np.arange(c), cfg.vocab)
     st.accepted = np.zeros(c, dtype=bool)
+    st.prev_argmax = None
     st.step = 0
     st.active = True
 
@@ -155,6 +177,52 @@ def sampler_decide(entropy, argmax, accepted, tau, step, max_steps):
     return acc, forced
 
 
+FIX_FRAC_BITS = 40   # fixed-point entropies: units of 2^-40 nat
+FIX_MAX_NATS = 64.0  # clamp; NaN counts as this (least confident)
+
+
+def entropy_fixed(h) -> int:
+    """Entropy (taken as float32) in fixed point: floor(clamp(h, 0, 64) * 2^40).
+
+    Every float32 in [0, 64] times 2^40 is exact in float64, so the floor is
+    exact and so are sums of up to 2^16 such values in 64 bits."""
+    h = float(np.float32(h))
+    if not h >= 0.0:
+        h = 0.0 if h < 0.0 else FIX_MAX_NATS
+    h = min(h, FIX_MAX_NATS)
+    return int(math.floor(h * 2.0 ** FIX_FRAC_BITS))
+
+
+def budget_decide(entropy, argmax, accepted, argmax_canvas, prev_argmax, budget, stop_entropy, step,
+                  max_steps):
+    """Entropy-budget accept rule on one canvas (pure function).
+
+    entropy, argmax: per position (entries of accepted positions unused);
+    accepted: mask before the step; argmax_canvas: this step's argmax canvas;
+    prev_argmax: the previous step's, or None at the first step of a block;
+    step: 1-based.  Returns (accept_budget, accept_forced, stopped)."""
+    accepted = np.asarray(accepted, dtype=bool)
+    n = len(accepted)
+    open_pos = [i for i in range(n) if not accepted[i]]
+    q = {i: entropy_fixed(entropy[i]) for i in open_pos}
+    limit = entropy_fixed(budget)
+    acc = np.zeros(n, dtype=bool)
+    spent = 0
+    for rank, i in enumerate(sorted(open_pos, key=lambda i: (q[i], i))):
+        spent += q[i]
+        if rank > 0 and spent > limit:
+            break
+        acc[i] = True
+    stable = prev_argmax is not None and np.array_equal(np.asarray(argmax_canvas), np.asarray(prev_argmax))
+    low = bool(open_pos) and sum(q.values()) < len(open_pos) * entropy_fixed(stop_entropy)
+    stopped = stable and low
+    forced = np.zeros(n, dtype=bool)
+    if stopped or step >= max_steps:
+        forced[open_pos] = True
+        forced &= ~acc
+    return acc, forced, stopped
+
+
 def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Weights,
                  prec: Precision, keep_logits=False) -> StepResult:
     if not st.active:
@@ -164,8 +232,17 @@ def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Wei
     s = st.step + 1
     ids_before = st.ids.copy()
     acc_before = st.accepted.copy()
-    acc_e, acc_f = sampler_decide(stats["entropy"], stats["argmax"], st.accepted, scfg.tau, s,
-                                  scfg.max_steps)
+    argmax_canvas = np.where(st.accepted, st.ids, stats["argmax"])
+    if scfg.mode == "budget":
+        acc_e, acc_f, stopped = budget_decide(stats["entropy"], stats["argmax"], st.accepted, argmax_canvas,
+                                        st.prev_argmax, scfg.budget, scfg.stop_entropy, s, scfg.max_steps)
+    elif scfg.mode == "threshold":
+        stopped = False
+        acc_e, acc_f = sampler_decide(stats["entropy"], stats["argmax"], st.accepted, scfg.tau, s,
+                                      scfg.max_steps)
+    else:
+        raise ValueError("unknown sampler mode %r" % scfg.mode)
+    st.prev_argmax = argmax_canvas
     take = acc_e | acc_f
     ids = st.ids.copy()
     ids[take] = stats["argmax"][take]
@@ -181,7 +258,7 @@ def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Wei
                       ids_before=ids_before, accepted_before=acc_before,
                       ids_after=ids.copy(), accepted_after=accepted.copy(),
                       n_open=n_open, done=(n_open == 0), layers=traces,
-                      logits=stats.get("logits"), hidden=x)
+                      logits=stats.get("logits"), hidden=x, stopped=stopped)
 
 
 def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision, keep_traces=False):
@@ -200,6 +277,7 @@ def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision
     st.active = False
     st.ids = None
     st.accepted = None
+    st.prev_argmax = None
     return (out, traces) if keep_traces else out
 
 

@@ -357,6 +357,132 @@ def test_sampler_strict_threshold_and_cap():
     assert list(np.nonzero(forced)[0]) == [1, 3, 4]
 
 
+# ------------------------------------------------ entropy-budget sampler ----
+
+def test_entropy_fixed_point_values():
+    f = oracle.entropy_fixed
+    assert f(0.0) == 0 and f(1.0) == 2 ** 40 and f(0.5) == 2 ** 39
+    assert f(2.0 ** -41) == 0 and f(3 * 2.0 ** -41) == 1     # floor
+    assert f(-1e-7) == 0                                     # rounding below zero clamps to zero
+    assert f(float("nan")) == 64 * 2 ** 40 and f(1e9) == 64 * 2 ** 40
+    x = np.float32(0.1)                                      # taken as float32, not float64
+    assert f(0.1) == f(x) == math.floor(float(x) * 2 ** 40)
+
+
+def _budget(H, accepted=None, budget=0.1, prev=None, canvas=None, step=1, cap=64, stop=0.005):
+    n = len(H)
+    accepted = np.zeros(n, bool) if accepted is None else np.asarray(accepted, bool)
+    canvas = np.zeros(n, int) if canvas is None else canvas
+    return oracle.budget_decide(np.asarray(H, np.float32), np.zeros(n, int), accepted, canvas, prev, budget, stop,
+                                step, cap)
+
+
+def test_budget_worked_example():
+    # by hand: order 0.02 (pos 1), 0.03 (3), 0.04 (4), 0.05 (0), 0.5 (2); running sums
+    # 0.02, 0.05, 0.09 stay within 0.1, 0.14 does not.
+    acc, forced, stopped = _budget([0.05, 0.02, 0.5, 0.03, 0.04])
+    assert list(np.nonzero(acc)[0]) == [1, 3, 4] and not forced.any() and not stopped
+    # binary-exact values: a running sum equal to the budget is within it
+    H = [0.0625, 0.03125, 0.03125, 0.5]
+    assert list(np.nonzero(_budget(H, budget=0.125)[0])[0]) == [0, 1, 2]
+    assert list(np.nonzero(_budget(H, budget=0.124)[0])[0]) == [1, 2]
+    # ties in entropy go to the lower position
+    assert list(np.nonzero(_budget([0.09, 0.09, 0.09], budget=0.1)[0])[0]) == [0]
+    # the most confident position is taken even when it alone exceeds the budget
+    assert list(np.nonzero(_budget([3.0, 2.0, 2.5], budget=0.1)[0])[0]) == [1]
+    # already accepted positions are neither counted nor taken
+    acc, _, _ = _budget([0.0, 0.06, 0.05, 0.01], accepted=[1, 0, 0, 0])
+    assert list(np.nonzero(acc)[0]) == [2, 3]
+    # a canvas of certain predictions is accepted whole
+    assert _budget(np.zeros(256))[0].all()
+
+
+def _budget_by_prefixes(H, accepted, budget):
+    """Independent formulation with exact rationals: sort the open positions by
+    (float32 entropy, position); take the longest prefix whose exact sum is <=
+    the float32 budget, and at least one position."""
+    from fractions import Fraction
+    open_pos = sorted((i for i in range(len(H)) if not accepted[i]), key=lambda i: (np.float32(H[i]), i))
+    b = Fraction(float(np.float32(budget)))
+    best = 1 if open_pos else 0
+    for k in range(1, len(open_pos) + 1):
+        if sum(Fraction(float(np.float32(H[i]))) for i in open_pos[:k]) <= b:
+            best = max(best, k)
+    return set(open_pos[:best])
+
+
+def test_budget_matches_prefix_formulation():
+    rng = np.random.default_rng(23)
+    for trial in range(400):
+        n = int(rng.integers(1, 12))
+        H = rng.integers(0, 12, n) / 64.0           # multiples of 2^-6: exact in fixed point, many ties
+        accepted = rng.random(n) < 0.3
+        budget = float(rng.integers(0, 16)) / 64.0  # includes 0 and sums landing exactly on it
+        acc, _, _ = _budget(H, accepted, budget)
+        assert set(np.nonzero(acc)[0]) == _budget_by_prefixes(H, accepted, budget), (H, accepted, budget)
+
+
+def test_budget_fixed_point_agrees_with_exact_sums_off_the_boundary():
+    rng = np.random.default_rng(29)
+    for trial in range(200):
+        n = 40
+        H = rng.exponential(0.01, n).astype(np.float32)
+        acc, _, _ = _budget(H, budget=0.1)
+        want = _budget_by_prefixes(H, np.zeros(n, bool), 0.1)
+        if set(np.nonzero(acc)[0]) != want:
+            # only a running sum within n * 2^-40 of the budget may decide differently
+            order = sorted(range(n), key=lambda i: (H[i], i))
+            sums = np.cumsum([float(H[i]) for i in order])
+            assert np.min(np.abs(sums - float(np.float32(0.1)))) < n * 2.0 ** -40
+
+
+def test_budget_invariants():
+    rng = np.random.default_rng(31)
+    for trial in range(200):
+        n = 64
+        H = rng.exponential(rng.choice([0.003, 0.03, 1.0]), n).astype(np.float32)
+        accepted = rng.random(n) < 0.5
+        a1, _, _ = _budget(H, accepted, 0.05)
+        a2, _, _ = _budget(H, accepted, 0.2)
+        open_ = ~accepted
+        assert not (a1 & accepted).any() and (a1.sum() >= 1) == open_.any()
+        assert not (a1 & ~a2).any()                           # monotone in the budget
+        rej = open_ & ~a2
+        if a2.any() and rej.any():
+            assert H[a2].max() <= H[rej].min()                # accepted never less confident than rejected
+        if a2.sum() > 1:
+            assert sum(oracle.entropy_fixed(h) for h in H[a2]) <= oracle.entropy_fixed(0.2)
+
+
+def test_budget_stop_rule():
+    n = 8
+    low = np.full(n, 0.001)
+    canvas = np.arange(n) * 3
+    # first step of a block: no previous canvas, no stop
+    acc, forced, stopped = _budget(low, prev=None, canvas=canvas, budget=0.0)
+    assert not stopped and acc.sum() == 1 and not forced.any()
+    # stable and confident: every open position not accepted is forced
+    acc, forced, stopped = _budget(low, prev=canvas.copy(), canvas=canvas, budget=0.0)
+    assert stopped and acc.sum() == 1 and forced.sum() == n - 1 and not (acc & forced).any()
+    # one position changed: no stop
+    prev = canvas.copy()
+    prev[5] += 1
+    assert not _budget(low, prev=prev, canvas=canvas, budget=0.0)[2]
+    # mean entropy at the threshold is not below it; just under it is
+    at = np.full(n, 0.005, np.float32)
+    assert not _budget(at, prev=canvas, canvas=canvas, budget=0.0)[2]
+    under = at.copy()
+    under[0] = np.nextafter(np.float32(0.005), np.float32(0))
+    assert _budget(under, prev=canvas, canvas=canvas, budget=0.0)[2]
+    # the mean is over open positions only
+    mixed = np.array([5.0, 0.001, 0.001, 0.001, 0.001, 0.001, 0.001, 0.001])
+    assert _budget(mixed, accepted=[1, 0, 0, 0, 0, 0, 0, 0], prev=canvas, canvas=canvas, budget=0.0)[2]
+    assert not _budget(mixed, prev=canvas, canvas=canvas, budget=0.0)[2]
+    # the cap forces regardless of stability
+    acc, forced, stopped = _budget(np.full(n, 3.0), prev=None, canvas=canvas, step=64, cap=64)
+    assert not stopped and acc.sum() + forced.sum() == n
+
+
 def _tiny_setup(seed=0, **kw):
     w = helpers.small_workload(**kw)
     tw = synth.make_weights(w, seed=seed)
@@ -398,6 +524,29 @@ def test_generation_deterministic_and_seeded():
     b, _, _ = oracle.generate(prompt, 256, 5, cfg, scfg, ow, oracle.Precision())
     c, _, _ = oracle.generate(prompt, 256, 6, cfg, scfg, ow, oracle.Precision())
     assert np.array_equal(a, b) and not np.array_equal(a, c)
+
+
+def test_budget_generation_tiny():
+    """Random weights: entropies far above the budget, so one position per step
+    and the rest forced at the cap; the stop rule never fires (mean entropy
+    ~6 nats).  A model made certain (embedding scaled up) finishes in one step."""
+    w, cfg, ow = _tiny_setup(n_out=256, max_steps=16)
+    scfg = oracle.SamplerConfig(tau=w.tau, max_steps=16, mode="budget")
+    prompt = synth.make_prompt(w, seed=1)
+    rec = []
+
+    def on_step(b, n, r, st):
+        rec.append(r)
+        new = r.accepted_after & ~r.accepted_before
+        assert np.array_equal(r.ids_after[new], r.argmax[new])
+        assert np.array_equal(r.ids_after[r.accepted_before], r.ids_before[r.accepted_before])
+
+    out, steps, st = oracle.generate(prompt, 256, 3, cfg, scfg, ow, oracle.Precision(), on_step=on_step)
+    assert steps == [16] and all(r.accept_entropy.sum() == 1 for r in rec)
+    assert rec[-1].accept_forced.sum() == 256 - 16
+    sure = oracle.Weights(embed=ow.embed * 400.0, final_norm=ow.final_norm, layers=ow.layers)
+    out, steps, st = oracle.generate(prompt, 256, 3, cfg, scfg, sure, oracle.Precision())
+    assert steps == [1]
 
 
 # ---------------------------------------------------- residual structure ----
