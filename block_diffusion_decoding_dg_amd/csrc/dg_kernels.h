@@ -96,6 +96,7 @@ void dg_launch_lm_merge(const float* part, const int32_t* part_arg, const int32_
 struct DgSampleSlot {
   int32_t* ids;       // canvas ids [C]
   uint8_t* accepted;  // [C]
+  int32_t* prev;      // argmax canvas of the block's previous step [C]; -1 = none
   uint64_t seed;
   int32_t block, step, row0;
 };
@@ -103,6 +104,8 @@ struct DgSampleArgs {
   DgSampleSlot s[DG_MAX_SEGS];
   int32_t count, C, vocab, max_steps;
   float tau;
+  int32_t mode;               // DG_SAMPLER_THRESHOLD / DG_SAMPLER_BUDGET
+  uint64_t budget_q, stop_q;  // fixed-point budget and stop threshold (2^-40 nat units)
 };
 // ent/amax indexed by batch row (slot * C + pos).  info [count][4]: accepted, forced, open, done.
 // open_rows/n_open_rows: compacted list of batch rows still open after the step.

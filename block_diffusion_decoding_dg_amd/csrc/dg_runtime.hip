@@ -111,6 +111,7 @@ struct dg_ctx {
   int32_t* n_open_rows = nullptr;
   int32_t* canvas_ids = nullptr;
   uint8_t* canvas_acc = nullptr;
+  int32_t* canvas_prev = nullptr;  // argmax canvas of each request's previous step (-1: none)
   int32_t* info_dev = nullptr;
   int32_t* tap_ids = nullptr;
   float* tap_gates = nullptr;
@@ -295,6 +296,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->n_open_rows = cv.take<int32_t>(4);
   c->canvas_ids = cv.take<int32_t>(Rs * 4);
   c->canvas_acc = cv.take<uint8_t>(Rs);
+  c->canvas_prev = cv.take<int32_t>(Rs * 4);
   c->info_dev = cv.take<int32_t>(m.max_requests * 4 * 4);
   c->tap_ids = cv.take<int32_t>((size_t)m.n_layers * Rs * k * 4);
   c->tap_gates = cv.take<float>((size_t)m.n_layers * Rs * k * 4);
@@ -624,6 +626,13 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
   }
 }
 
+// Sampler threshold in fixed point: floor(clamp(h, 0, 64) * 2^40), NaN as 64
+// (the kernel converts entropies the same way; every product is exact in double).
+uint64_t entropy_fixed(float h) {
+  h = h >= 0.f ? std::min(h, 64.f) : (h < 0.f ? 0.f : 64.f);
+  return (uint64_t)((double)h * 1099511627776.0);
+}
+
 DgSampleArgs sample_args(const dg_ctx* c, const std::vector<int>& slot_req) {
   DgSampleArgs a;
   memset(&a, 0, sizeof a);
@@ -631,6 +640,7 @@ DgSampleArgs sample_args(const dg_ctx* c, const std::vector<int>& slot_req) {
     const int r = slot_req[i];
     a.s[i].ids = c->canvas_ids + (size_t)r * c->C;
     a.s[i].accepted = c->canvas_acc + (size_t)r * c->C;
+    a.s[i].prev = c->canvas_prev + (size_t)r * c->C;
     a.s[i].seed = c->req[r].seed;
     a.s[i].block = c->req[r].block;
     a.s[i].step = c->req[r].step + 1;
@@ -641,6 +651,9 @@ DgSampleArgs sample_args(const dg_ctx* c, const std::vector<int>& slot_req) {
   a.vocab = c->cfg.vocab;
   a.max_steps = c->scfg.max_steps > 0 ? c->scfg.max_steps : c->C;
   a.tau = c->scfg.tau;
+  a.mode = c->scfg.mode;
+  a.budget_q = entropy_fixed(c->scfg.budget);
+  a.stop_q = entropy_fixed(c->scfg.stop_entropy);
   return a;
 }
 
@@ -679,6 +692,11 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   if (msg) return fail(nullptr, DG_ERR_INVALID_ARG, "%s", msg);
   if (!scfg) return fail(nullptr, DG_ERR_INVALID_ARG, "null sampler config");
   if (!(scfg->tau >= 0.f)) return fail(nullptr, DG_ERR_INVALID_ARG, "tau must be >= 0");
+  if (scfg->mode != DG_SAMPLER_THRESHOLD && scfg->mode != DG_SAMPLER_BUDGET)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "unknown sampler mode %d", scfg->mode);
+  if (scfg->mode == DG_SAMPLER_BUDGET &&
+      !(scfg->budget >= 0.f && scfg->budget <= 64.f && scfg->stop_entropy >= 0.f && scfg->stop_entropy <= 64.f))
+    return fail(nullptr, DG_ERR_INVALID_ARG, "budget and stop_entropy must lie in [0, 64]");
   if (!weights || !weights->embed || !weights->final_norm || !weights->layers)
     return fail(nullptr, DG_ERR_INVALID_ARG, "null weights");
   for (int l = 0; l < cfg->n_layers; ++l) {
@@ -944,6 +962,7 @@ dg_status dg_set_canvas(dg_ctx* c, int32_t req, const int32_t* ids, const uint8_
   }
   HIPCK(c, hipMemcpyAsync(c->canvas_ids + (size_t)req * c->C, ids, c->C * 4, hipMemcpyHostToDevice, c->stream));
   HIPCK(c, hipMemcpyAsync(c->canvas_acc + (size_t)req * c->C, accepted, c->C, hipMemcpyHostToDevice, c->stream));
+  HIPCK(c, hipMemsetAsync(c->canvas_prev + (size_t)req * c->C, 0xff, c->C * 4, c->stream));  // -1: no previous step
   HIPCK(c, hipStreamSynchronize(c->stream));
   q.active = true;
   q.done = open == 0;

@@ -40,8 +40,12 @@ class ModelConfig(ctypes.Structure):
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
 
 
+SAMPLER_MODES = {"threshold": 0, "budget": 1}
+
+
 class SamplerConfig(ctypes.Structure):
-    _fields_ = [("tau", ctypes.c_float), ("max_steps", ctypes.c_int32)]
+    _fields_ = [("tau", ctypes.c_float), ("max_steps", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("budget", ctypes.c_float), ("stop_entropy", ctypes.c_float)]
 
 
 _LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router", "w1", "w3", "w2", "sw1", "sw3", "sw2")
@@ -166,7 +170,8 @@ class Decoder:
     weights: {"embed", "final_norm", "layers": [ {name: tensor} ]} on the GPU in
     the model dtype (see synth.make_weights)."""
 
-    def __init__(self, cfg: ModelConfig, tau, max_steps, weights, device="cuda"):
+    def __init__(self, cfg: ModelConfig, tau, max_steps, weights, device="cuda", sampler="threshold",
+                 budget=0.1, stop_entropy=0.005):
         self.lib = load()
         self.cfg = cfg
         kv_bytes, sc_bytes = dg_workspace_size(cfg)
@@ -180,7 +185,10 @@ class Decoder:
                 setattr(self._layers[l], n, lt[n].data_ptr())
         self._w = Weights(embed=weights["embed"].data_ptr(), final_norm=weights["final_norm"].data_ptr(),
                           layers=self._layers)
-        self.scfg = SamplerConfig(tau=tau, max_steps=max_steps)
+        if sampler not in SAMPLER_MODES:
+            raise ValueError("unknown sampler %r" % (sampler,))
+        self.scfg = SamplerConfig(tau=tau, max_steps=max_steps, mode=SAMPLER_MODES[sampler], budget=budget,
+                                  stop_entropy=stop_entropy)
         self.ctx = ctypes.c_void_p()
         st = self.lib.dg_create(ctypes.byref(cfg), ctypes.byref(self.scfg), ctypes.byref(self._w),
                                 _ptr(self.kv), kv_bytes, _ptr(self.scratch), sc_bytes, _stream_handle(),

@@ -93,18 +93,39 @@ typedef struct dg_model_config {
 } dg_model_config;
 
 /*
- * Entropy-bound sampler.  Reading of "How the sampler actually works" taken
- * here: the candidate at every open position is the argmax token (ties to the
- * lower id); accepted this step are the open positions whose softmax entropy
+ * Entropy-bound sampler.  In both modes the candidate at every open position
+ * is its argmax token (ties to the lower id), accepted positions never change,
+ * every open position not accepted is re-drawn (see dg_denoise_step), and at
+ * step max_steps of a block every position still open is set to its argmax and
+ * accepted (the step cap; max_steps <= 0 selects canvas_len).
+ *
+ * DG_SAMPLER_THRESHOLD (0): "How the sampler actually works" leaves the rule
+ * open; the reading taken accepts the open positions whose softmax entropy
  * (nats, fp32) is strictly below tau, plus always the single open position of
- * lowest entropy (ties to the lower position); accepted positions never change;
- * every other open position is re-drawn (see dg_denoise_step).  At step
- * max_steps of a block every position still open is set to its argmax and
- * accepted (the step cap).  max_steps <= 0 selects canvas_len.
+ * lowest entropy (ties to the lower position).
+ *
+ * DG_SAMPLER_BUDGET (1): the default sampler of "DiffusionGemma hits ~1,500 TPS
+ * on one H100", section "How the sampler actually works" (budget 0.1, stop
+ * threshold 0.005 there), described in words only.  Readings taken: open
+ * positions are taken in order of rising entropy (ties to the lower position)
+ * while the running sum of their entropies, the position's own included, is
+ * at most `budget`, and the first of them always; the block ends early when
+ * the argmax canvas (accepted positions at their token, open ones at this
+ * step's argmax) equals that of the block's previous step and the mean
+ * entropy of the open positions is below `stop_entropy`: every open position
+ * not taken is then set to its argmax and accepted, as at the cap.  Sums and
+ * the mean compare exactly in 64-bit fixed point: each fp32 entropy h counts
+ * floor(clamp(h, 0, 64) * 2^40) (NaN as 64), budget and stop_entropy the same.
+ * The previous argmax canvas is forgotten by dg_set_canvas.  tau is unused.
  */
+#define DG_SAMPLER_THRESHOLD 0
+#define DG_SAMPLER_BUDGET 1
 typedef struct dg_sampler_config {
   float tau;
   int32_t max_steps;
+  int32_t mode;        /* DG_SAMPLER_THRESHOLD or DG_SAMPLER_BUDGET */
+  float budget;        /* >= 0, finite; DG_SAMPLER_BUDGET only */
+  float stop_entropy;  /* >= 0, finite; DG_SAMPLER_BUDGET only */
 } dg_sampler_config;
 
 /*

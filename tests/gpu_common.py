@@ -30,9 +30,11 @@ def to_gpu(tw):
             "layers": [{k: v.cuda() for k, v in lt.items()} for lt in tw["layers"]]}
 
 
-def make_decoder(w, tw_gpu, max_requests=None, max_ctx=None, prefill_chunk=0, tau=None, max_steps=None):
+def make_decoder(w, tw_gpu, max_requests=None, max_ctx=None, prefill_chunk=0, tau=None, max_steps=None,
+                 sampler="threshold", budget=0.1, stop_entropy=0.005):
     cfg = dg.model_config(w, max_requests=max_requests, max_ctx=max_ctx, prefill_chunk=prefill_chunk)
-    return dg.Decoder(cfg, w.tau if tau is None else tau, w.max_steps if max_steps is None else max_steps, tw_gpu)
+    return dg.Decoder(cfg, w.tau if tau is None else tau, w.max_steps if max_steps is None else max_steps, tw_gpu,
+                      sampler=sampler, budget=budget, stop_entropy=stop_entropy)
 
 
 def normwise(a, b):
@@ -109,8 +111,28 @@ def rule_on(H, accepted, tau, step, cap):
     return take
 
 
+def _budget_diff_explained(i, Ho, Hg, open_b, acc_o, budget, flipped):
+    """Whether position i may legitimately be decided differently by the budget
+    rule on the GPU's entropies than on the oracle's: a routing flip, an order
+    swap with an open position of the other decision whose oracle entropy lies
+    within twice the measured error, or a running sum through i (in the
+    oracle's order) within the accumulated entropy error of the budget."""
+    if flipped[i]:
+        return True
+    idx = np.nonzero(open_b)[0]
+    err = np.abs(Hg.astype(np.float64) - Ho)
+    eps = float(err[idx].max())
+    other = idx[acc_o[idx] != acc_o[i]]
+    if other.size and np.min(np.abs(Ho[other] - Ho[i])) <= 2 * eps + 1e-12:
+        return True
+    order = sorted(idx, key=lambda j: (np.float32(Ho[j]), j))
+    k = order.index(i)
+    run = float(np.sum(Ho[order[:k + 1]]))
+    return abs(run - float(np.float32(budget))) <= float(np.sum(err[order[:k + 2]])) + 1e-12
+
+
 def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows=8, check_router=True,
-               req=0, rng=None, stats=None, band=GAP):
+               req=0, rng=None, stats=None, band=GAP, gstate=None):
     """Run one GPU step and the oracle step from the same state; compare.
 
     Continuous values (entropy, log-sum-exp, sampled logits) are compared on the
@@ -125,6 +147,12 @@ def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows
         minimum, the only way an error that small can move that choice;
       * Philox re-draws: bit-exact.
     After a permitted difference the GPU is re-synchronised to the oracle's state.
+    With the budget sampler (scfg.mode == "budget") the GPU's decision is checked
+    against the rule on its own entropies, argmax canvas and previous argmax
+    canvas (kept in `gstate`, a dict the caller passes from step to step);
+    differences from the oracle must be explained by _budget_diff_explained or,
+    for the early stop, by a mean entropy within the error of the threshold or
+    an argmax near-tie.
     Returns (oracle StepResult, resynced, GPU step info)."""
     ids_g0, acc_g0 = dec.dg_get_canvas(req) if dec.dg_get_request(req)["active"] else (None, None)
     if ids_g0 is not None and st.active:
@@ -170,7 +198,15 @@ def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows
     # sampler: the GPU's accept set is the rule applied to its own (H, argmax)
     ids_g, acc_g = dec.dg_get_canvas(req)
     Hg_all = rows["entropy"][row0:row0 + C]
-    take_g = rule_on(Hg_all, r.accepted_before, scfg.tau, st.step, scfg.max_steps)
+    budget = getattr(scfg, "mode", "threshold") == "budget"
+    if budget:
+        canvas_g = np.where(r.accepted_before, r.ids_before, am_g)
+        te, tf, stop_g = oracle.budget_decide(Hg_all, am_g, r.accepted_before, canvas_g, gstate.get("prev"),
+                                              scfg.budget, scfg.stop_entropy, st.step, scfg.max_steps)
+        take_g = te | tf
+        gstate["prev"] = canvas_g
+    else:
+        take_g = rule_on(Hg_all, r.accepted_before, scfg.tau, st.step, scfg.max_steps)
     assert np.array_equal(acc_g, r.accepted_before | take_g), "GPU accept set is not the rule on its own entropies"
     exp_ids = r.ids_before.copy()
     exp_ids[take_g] = am_g[take_g]
@@ -184,7 +220,19 @@ def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows
         newly_g = acc_g & ~r.accepted_before
         eps = float(np.max(np.abs(Hg_all[open_b].astype(np.float64) - r.entropy[open_b])))
         h_o_min = float(np.min(r.entropy[open_b]))
-        for i in np.nonzero(newly_o != newly_g)[0]:
+        if budget:
+            stop_o = r.stopped
+            if stop_o != bool(stop_g):
+                mean_o = float(np.mean(r.entropy[open_b]))
+                near_mean = abs(mean_o - scfg.stop_entropy) <= eps + 1e-12
+                near_tie = bool(np.any(open_b & (am_g != r.argmax) & (gap < band)))
+                assert near_mean or near_tie or flipped[open_b].any(), ("early stop differs", mean_o, eps)
+            else:
+                acc_o = r.accept_entropy | r.accepted_before
+                for i in np.nonzero(r.accept_entropy != te)[0]:
+                    assert _budget_diff_explained(i, r.entropy, Hg_all, open_b, acc_o, scfg.budget, flipped), (
+                        "budget decision differs outside the bands", int(i), eps)
+        for i in np.nonzero(newly_o != newly_g)[0] if not budget else []:
             near_tau = abs(r.entropy[i] - scfg.tau) < TAU_BAND
             lowest_choice = r.entropy[i] - h_o_min <= 2 * eps + 1e-12
             assert near_tau or lowest_choice or flipped[i], ("accept decision differs outside the bands", int(i),
@@ -192,6 +240,9 @@ def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows
         for i in np.nonzero(newly_o & newly_g & (ids_g != r.ids_after))[0]:
             assert gap[i] < band or flipped[i], ("accepted token differs outside the argmax band", int(i))
         dec.dg_set_canvas(req, st.ids, st.accepted, st.step, st.block)
+        if budget:   # the library forgets the previous argmax canvas on a set; so does the oracle here
+            st.prev_argmax = None
+            gstate["prev"] = None
         resync = True
         log("  resync at block %d step %d" % (st.block, st.step))
     assert info["step"] == st.step

@@ -78,10 +78,15 @@ def test_create_validates_before_device_work(lib):
     st = lib.dg_create(ctypes.byref(cfg), ctypes.byref(scfg), ctypes.byref(w), ctypes.c_void_p(0x1000), kv - 1,
                        ctypes.c_void_p(0x1000), sc, None, ctypes.byref(out))
     assert st == dg.DG_ERR_WORKSPACE
-    bad_tau = dg.SamplerConfig(tau=-1.0, max_steps=64)
-    st = lib.dg_create(ctypes.byref(cfg), ctypes.byref(bad_tau), ctypes.byref(w), ctypes.c_void_p(0x1000), kv,
-                       ctypes.c_void_p(0x1000), sc, None, ctypes.byref(out))
-    assert st == dg.DG_ERR_INVALID_ARG
+    bad = [dg.SamplerConfig(tau=-1.0, max_steps=64),
+           dg.SamplerConfig(tau=0.5, max_steps=64, mode=2),
+           dg.SamplerConfig(tau=0.5, max_steps=64, mode=1, budget=-0.1, stop_entropy=0.005),
+           dg.SamplerConfig(tau=0.5, max_steps=64, mode=1, budget=float("nan"), stop_entropy=0.005),
+           dg.SamplerConfig(tau=0.5, max_steps=64, mode=1, budget=0.1, stop_entropy=float("inf"))]
+    for b in bad:
+        st = lib.dg_create(ctypes.byref(cfg), ctypes.byref(b), ctypes.byref(w), ctypes.c_void_p(0x1000), kv,
+                           ctypes.c_void_p(0x1000), sc, None, ctypes.byref(out))
+        assert st == dg.DG_ERR_INVALID_ARG and not out.value, (b.mode, b.budget, b.stop_entropy)
 
 
 def test_null_context_calls_fail_cleanly(lib):

@@ -236,3 +236,128 @@ def test_tiny_sampler_crafted(setup, trial):
     assert np.array_equal(ids_g, ids_o)
     assert info["n_accepted"] == acc_e.sum() and info["n_forced"] == acc_f.sum()
     assert info["n_open"] == still.sum() and info["done"] == int(still.sum() == 0)
+
+
+# ------------------------------------------------ entropy-budget sampler ----
+
+def _budget_ref(H, am, ids, acc, prev, step, seed, block, budget, stop, cap):
+    """The oracle's budget rule applied to one call of the sampler op."""
+    canvas = np.where(acc, ids, am)
+    e, f, stopped = oracle.budget_decide(H, am, acc, canvas, prev, budget, stop, step, cap)
+    take = e | f
+    ids2 = ids.copy()
+    ids2[take] = am[take]
+    still = ~(acc | take)
+    pos = np.nonzero(still)[0]
+    ids2[pos] = philox.draw_tokens(seed, block, step, pos, W.vocab)
+    return ids2, acc | take, e, f, still, canvas, stopped
+
+
+@pytest.mark.parametrize("trial", range(8))
+def test_tiny_sampler_budget_crafted(setup, trial):
+    """Budget rule through the sampler op, three successive calls per case (the
+    second and third see the previous argmax canvas): spread entropies, sums
+    landing exactly on the budget, ties, zeros, NaN / inf / negative inputs, the
+    cap and the early stop.  Bit-exact with the oracle."""
+    tw, twg, ocfg, ow = setup
+    rng = np.random.default_rng(100 + trial)
+    C = 256
+    budget, stop, cap = 0.1, 0.005, W.max_steps
+    if trial == 1:
+        budget = 0.125
+        H = (rng.integers(0, 9, C) / 256.0).astype(np.float32)     # binary-exact; sums land on 0.125
+    elif trial == 2:
+        H = np.zeros(C, np.float32)
+    elif trial == 3:
+        H = np.full(C, 0.03, np.float32)
+    elif trial == 4:
+        H = rng.uniform(1, 5, C).astype(np.float32)
+    elif trial == 5:
+        H = rng.exponential(0.02, C).astype(np.float32)
+        H[rng.choice(C, 12, replace=False)] = [np.nan, np.inf, -1e-7, -0.0, 0.0, 64.0, 65.0, 1e-30, np.nan,
+                                               -np.inf, 3e-45, 0.1]
+    elif trial in (6, 7):
+        budget = 0.0
+        H = rng.uniform(0, 0.008, C).astype(np.float32)             # mean below 0.005
+    else:
+        H = rng.exponential(0.01, C).astype(np.float32)
+    seed = 500 + trial
+    dec = make_decoder(W, twg, sampler="budget", budget=budget, stop_entropy=stop)
+    dec.dg_set_committed(0, 64, seed)
+    am = rng.integers(0, W.vocab, C).astype(np.int32)
+    acc = rng.random(C) < (0.0 if trial in (2, 3, 6, 7) else 0.3)
+    ids = rng.integers(0, W.vocab, C).astype(np.int32)
+    block = trial
+    step0 = cap - 2 if trial == 4 else 1
+    dec.dg_set_canvas(0, ids, acc, step0 - 1, block)
+    prev = None
+    for call in range(3):
+        step = step0 + call
+        if trial == 7 and call == 1:
+            am = am.copy()
+            am[np.nonzero(~acc)[0][-1]] ^= 1                         # one open argmax moves: no stop yet
+        info = dec.dg_op_sample(0, torch.from_numpy(H).cuda(), torch.from_numpy(am).cuda(), step)
+        ids_g, acc_g = dec.dg_get_canvas(0)
+        ids_o, acc_o, e, f, still, prev, stopped = _budget_ref(H, am, ids, acc, prev, step, seed, block, budget,
+                                                               stop, cap)
+        log("budget trial %d call %d: %d by budget, %d forced, %d open, stop %s"
+            % (trial, call, e.sum(), f.sum(), still.sum(), stopped))
+        assert np.array_equal(acc_g, acc_o), (trial, call)
+        assert np.array_equal(ids_g, ids_o), (trial, call)
+        assert info["n_accepted"] == e.sum() and info["n_forced"] == f.sum()
+        assert info["n_open"] == still.sum() and info["done"] == int(still.sum() == 0)
+        if trial == 6:
+            assert stopped == (call == 1)
+        if trial == 7:
+            assert stopped == (call == 2)
+        ids, acc = ids_o, acc_o
+        if still.sum() == 0:
+            break
+
+
+def _scaled_embed(tw, scale):
+    """Tiny weights with the embedding (and so the tied LM head) scaled, which
+    sharpens the predictions into the range the budget sampler works in."""
+    tws = dict(tw)
+    tws["embed"] = tw["embed"] * scale
+    return to_gpu(tws), helpers.oracle_weights(W, tws)
+
+
+def test_tiny_budget_block_free_running(setup):
+    tw, _, ocfg, _ = setup
+    twg, ow = _scaled_embed(tw, 10.0)
+    prompt = synth.make_prompt(W, seed=0)
+    seed = 4321
+    dec = make_decoder(W, twg, sampler="budget")
+    dec.dg_prefill(0, prompt, seed)
+    st = oracle.new_request(ocfg, seed, W.max_ctx)
+    oracle.prefill(st, prompt, ocfg, ow, oracle.Precision())
+    scfg = oracle.SamplerConfig(W.tau, W.max_steps, mode="budget")
+    gstate, steps, n_resync, per_step = {}, 0, 0, []
+    while True:
+        r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, oracle.Precision(), _fp32_ent_tol, _fp32_logit_tol,
+                                     gstate=gstate)
+        steps += 1
+        n_resync += resync
+        per_step.append(int(r.accept_entropy.sum()))
+        assert info["n_open"] == r.n_open
+        if r.done:
+            break
+    log("tiny budget: %d steps, accepted per step %s, %d resyncs" % (steps, per_step, n_resync))
+    assert 1 < steps < W.max_steps and max(per_step) > 1
+    ids_g = dec.dg_commit_block(0)
+    ids_o = oracle.commit_block(st, ocfg, ow, oracle.Precision())
+    assert np.array_equal(ids_g, ids_o)
+
+
+def test_tiny_budget_generate_matches_oracle(setup):
+    tw, _, ocfg, _ = setup
+    twg, ow = _scaled_embed(tw, 12.0)
+    prompt = synth.make_prompt(W, seed=6, length=80)
+    dec = make_decoder(W, twg, max_ctx=640, sampler="budget")
+    outs, stats = dec.dg_generate([prompt], 400, [91])
+    ref, steps, _ = oracle.generate(prompt, 400, 91, ocfg, oracle.SamplerConfig(W.tau, W.max_steps, mode="budget"),
+                                    ow, oracle.Precision())
+    log("tiny budget generate: steps %s, stats %s" % (steps, stats))
+    assert np.array_equal(outs[0], ref)
+    assert stats["steps"] == sum(steps) and sum(steps) < 2 * W.max_steps
