@@ -47,11 +47,19 @@ def esize(w):
     return 2 if w.dtype == "bf16" else 4
 
 
+def expert_matrix_bytes(w, rows, cols):
+    """Bytes of one routed expert matrix [rows, cols]: the model dtype, or one byte
+    per E4M3 code plus a float32 scale per row."""
+    if w.expert_format == "fp8":
+        return rows * cols + 4 * rows
+    return rows * cols * esize(w)
+
+
 def expert_up_bytes(w, touched, rows):
     """Algorithmic HBM bytes of one routed W1/W3 launch: the touched experts' W1 and
     W3 once, the normalised rows once, the SwiGLU output once."""
     es = esize(w)
-    return (touched * 2 * w.expert_hidden * w.d_model * es + rows * w.d_model * es
+    return (touched * 2 * expert_matrix_bytes(w, w.expert_hidden, w.d_model) + rows * w.d_model * es
             + rows * w.top_k * w.expert_hidden * es)
 
 
@@ -64,8 +72,9 @@ def step_bytes(w, P, rows, touched_per_layer):
     dense = ((w.n_q_heads + 2 * w.n_kv_heads) * hd * d + w.n_q_heads * hd * d + w.n_experts * d
              + 3 * d * w.shared_hidden)
     total = 0
+    per_expert = 2 * expert_matrix_bytes(w, w.expert_hidden, d) + expert_matrix_bytes(w, d, w.expert_hidden)
     for t in touched_per_layer:
-        total += (dense + t * 3 * d * w.expert_hidden) * es
+        total += dense * es + t * per_expert
     kv = w.n_layers * 2 * w.n_kv_heads * hd * es
     total += P * kv + rows * kv          # prefix read + canvas K/V write
     total += w.vocab * d * es            # LM head
@@ -82,22 +91,25 @@ def step_flops(w, P, rows, n_open):
     return f
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
-    kernel source has changed since the counters were taken."""
+def measured_traffic(w):
+    """HBM bytes per launch of the dominant kernel (bf16 or FP8 experts, per the
+    workload) from the committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, copy-calibrated), or None when the kernel source has changed
+    since the counters were taken or the summary has no figure for it."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "ws_hbm_traffic.md")
     src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", "k_ws.hip")
     try:
+        key = "expert_up_fp8_traffic_bytes_per_launch" if w.expert_format == "fp8" else \
+            "expert_up_traffic_bytes_per_launch"
         fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and l.split(": ", 1)[0]
-                      in ("expert_up_traffic_bytes_per_launch", "k_ws_source_sha256"))
+                      in (key, "k_ws_source_sha256"))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if fields.get("k_ws_source_sha256", "").strip() != sha:
+    if fields.get("k_ws_source_sha256", "").strip() != sha or key not in fields:
         return None
-    return int(fields["expert_up_traffic_bytes_per_launch"])
+    return int(fields[key])
 
 
 def cpu_baseline(w, tokens_per_step):
@@ -150,57 +162,31 @@ def cpu_baseline(w, tokens_per_step):
             "ms_per_step": step_s * 1e3}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="full")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel", default=DOMINANT, help="kernel family timed with HIP events")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only copy a MIB-sized device buffer 8 times (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE "
-                         "against a kernel of known traffic) and exit")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        n = args.copy_calibration * (1 << 20)
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(8):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "copies": 8}))
-        return
+def describe(w, K):
+    C = w.canvas_len
+    return ("%s: vocab %d, d_model %d, %d layers, %d/%d heads x %d, %d experts top-%d + 1 shared, expert hidden "
+            "%d, shared hidden %d%s; %d requests x %d-token prompt, %d timed steps (%d canvases of %d)" % (
+                w.name, w.vocab, w.d_model, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_experts,
+                w.top_k, w.expert_hidden, w.shared_hidden,
+                ", routed experts in FP8 E4M3 with row scales" if w.expert_format == "fp8" else "",
+                w.n_requests, w.prompt_len, K, max(1, -(-K // C)), C))
 
-    if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (no sharding, no collectives); --gpus %d is not "
-              "supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
 
+def timed_run(w, tw, K, W, kernel, seed, log):
+    """Prefill, W untimed warm-up steps, prefill again, then K timed steps with
+    the block commits that fall inside them.  Returns the measured figures."""
     import numpy as np
     import torch
-    from block_diffusion_decoding_dg_amd import dg, synth
-
-    if not torch.cuda.is_available():
-        print("bench.py: needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    w = synth.WORKLOADS[args.workload]
+    from block_diffusion_decoding_dg_amd import dg
+    from block_diffusion_decoding_dg_amd import synth
     C = w.canvas_len
     R = w.n_requests
-    K, W = args.steps, args.warmup
     n_blocks = max(1, -(-K // C))
     max_ctx = w.prompt_len + n_blocks * C
-    log = lambda *a: print(*a, file=sys.stderr, flush=True)
-
-    log("bench: generating %s weights on the GPU" % w.name)
-    tw = synth.make_weights(w, seed=args.seed, device="cuda")
-    torch.cuda.synchronize()
     cfg = dg.model_config(w, max_ctx=max_ctx)
     dec = dg.Decoder(cfg, w.tau, w.max_steps, tw)
-    prompts = [synth.make_prompt(w, seed=args.seed + r) for r in range(R)]
-    seeds = [args.seed + r for r in range(R)]
+    prompts = [synth.make_prompt(w, seed=seed + r) for r in range(R)]
+    seeds = [seed + r for r in range(R)]
 
     def prefill_all():
         t0 = time.perf_counter()
@@ -209,7 +195,7 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3
 
-    log("bench: prefill %d x %d tokens" % (R, w.prompt_len))
+    log("bench: %s: prefill %d x %d tokens" % (w.name, R, w.prompt_len))
     prefill_ms = prefill_all()
     log("bench: prefill %.1f ms; warmup %d steps" % (prefill_ms, W))
     # Experts touched per layer, sampled on the untimed warmup steps (the routing
@@ -225,10 +211,10 @@ def main():
         sample_touched()
     prefill_ms = prefill_all()  # reset to block 0, step 0
 
-    dec.dg_kernel_timer(args.kernel)
+    dec.dg_kernel_timer(kernel)
     torch.cuda.synchronize()
     log("bench: timing %d steps" % K)
-    trace = []  # (P, open rows before the step) per request per step
+    trace = []  # (block, step, tokens) per request per step
     tokens = 0
     commits = 0
     t0 = time.perf_counter()
@@ -261,61 +247,121 @@ def main():
     tot_flops = 0
     for blk, step, _ in trace:
         P = w.prompt_len + blk * C
-        n_open = C - (step - 1)  # one acceptance per step before this one (checked below)
+        n_open = C - (step - 1)  # one acceptance per step before this one (random weights)
         tot_bytes += step_bytes(w, P, C, touched)
         tot_flops += step_flops(w, P, C, n_open)
     mean_bytes = tot_bytes / max(1, len(trace)) * R
     mean_flops = tot_flops / max(1, len(trace)) * R
     ms_per_step = elapsed * 1e3 / K
     roof_ms = max(mean_bytes / (HBM_PEAK_GBS * 1e9), mean_flops / (MFMA_BF16_TFLOPS * 1e12)) * 1e3
-    tok_per_step = tokens / K
 
     launch_ms = kt_ms / max(1, kt_n)
-    rows_step = R * C
-    bpl = expert_up_bytes(w, sum(touched) / len(touched), rows_step)
-    achieved = bpl / (launch_ms * 1e-3) / 1e9 if kt_n else None
-
-    out = {
-        "metric": "output tok/s at bs=1, 4096-in/1024-out; ms per 256-token denoise step",
-        "value": tokens / elapsed,
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic: random N(0,0.02) weights, uniform random prompt ids",
-        "config": {"workload": "%s: vocab %d, d_model %d, %d layers, %d/%d heads x %d, %d experts top-%d + 1 "
-                               "shared, expert hidden %d, shared hidden %d; %d requests x %d-token prompt, "
-                               "%d timed steps (%d canvases of %d)" % (
-                                   w.name, w.vocab, w.d_model, w.n_layers, w.n_q_heads, w.n_kv_heads,
-                                   w.head_dim, w.n_experts, w.top_k, w.expert_hidden, w.shared_hidden, R,
-                                   w.prompt_len, K, n_blocks, C),
-                   "global_batch": R, "seq_len": w.prompt_len, "parallelism": "none"},
-        "tokens_per_step": tok_per_step,
-        "commits": commits,
-        "prefill_ms": prefill_ms,
-        "roofline": {"bound": "hbm", "kernel": args.kernel,
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                     "traffic": measured_traffic() if args.kernel == DOMINANT else None,
+    bpl = expert_up_bytes(w, sum(touched) / len(touched), R * C)
+    achieved = bpl / (launch_ms * 1e-3) / 1e9 if (kt_n and kernel == DOMINANT) else None
+    return {
+        "value": tokens / elapsed, "ms_per_step": ms_per_step, "tokens_per_step": tokens / K,
+        "commits": commits, "prefill_ms": prefill_ms,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
                      "launch_ms": launch_ms, "launches": kt_n, "bytes_per_launch": bpl},
         "step_roofline": {"bytes_per_step": mean_bytes, "flops_per_step": mean_flops,
                           "roofline_ms": roof_ms, "frac": roof_ms / ms_per_step,
                           "touched_experts_per_layer": sum(touched) / len(touched),
                           "touched_sampled_steps": len(touched_samples)},
     }
-    if args.kernel != DOMINANT:
-        out["roofline"]["achieved"] = None
-        out["roofline"]["frac"] = None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", default=DOMINANT, help="kernel family timed with HIP events")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--fp8-steps", type=int, default=256,
+                    help="steps timed again with the routed experts in FP8 (full workload only; 0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer 8 times (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE "
+                         "against a kernel of known traffic) and exit")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 8}))
+        return
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no sharding, no collectives); --gpus %d is not "
+              "supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from block_diffusion_decoding_dg_amd import dg, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log("bench: generating %s weights on the GPU" % w.name)
+    tw = synth.make_weights(w, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    res = timed_run(w, tw, args.steps, args.warmup, args.kernel, args.seed, log)
+    K, W, R, C = args.steps, args.warmup, w.n_requests, w.canvas_len
+    out = {
+        "metric": "output tok/s at bs=1, 4096-in/1024-out; ms per 256-token denoise step",
+        "value": res["value"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: random N(0,0.02) weights, uniform random prompt ids",
+        "config": {"workload": describe(w, K),
+                   "global_batch": R, "seq_len": w.prompt_len, "parallelism": "none"},
+        "tokens_per_step": res["tokens_per_step"],
+        "commits": res["commits"],
+        "prefill_ms": res["prefill_ms"],
+        "roofline": res["roofline"],
+        "step_roofline": res["step_roofline"],
+    }
+    if w.expert_format == "fp8":
+        out["dtype"] = "bf16, fp8 (e4m3) routed-expert weights"
+    if args.kernel == DOMINANT:
+        out["roofline"]["traffic"] = measured_traffic(w)
+    if args.fp8_steps > 0 and w.name == "full":
+        # The same model with its routed experts quantized to E4M3 + row scales
+        # (the pages' FP8 checkpoint, as read here), timed on its own.
+        w8 = synth.WORKLOADS["full_fp8"]
+        log("bench: quantizing the routed experts to FP8")
+        for lt in tw["layers"]:
+            for n in ("w1", "w3", "w2"):
+                lt[n], lt[n + "_scale"] = synth.quantize_rows_e4m3(lt[n])
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        r8 = timed_run(w8, tw, args.fp8_steps, args.warmup, args.kernel, args.seed, log)
+        if args.kernel == DOMINANT:
+            r8["roofline"]["traffic"] = measured_traffic(w8)
+        out["fp8_experts"] = {"workload": describe(w8, args.fp8_steps), "steps": args.fp8_steps,
+                              "value": r8["value"], "unit": "tok/s", "ms_per_step": r8["ms_per_step"],
+                              "roofline": r8["roofline"], "step_roofline": r8["step_roofline"]}
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         del tw
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(w, tok_per_step)
+        out["cpu_baseline"] = cpu_baseline(w, res["tokens_per_step"])
     print(json.dumps(out), flush=True)
 
 

@@ -137,6 +137,9 @@ struct WsArgs {
   const void* W0;         // weight matrices, row-major [rows][K]
   const void* W1;
   const void* W2;
+  int w8;                 // grouped launches: W0 / W1 hold E4M3 codes (one byte per weight) ...
+  const float* wsc0;      // ... with float32 scales per weight row, [groups][N], for W0
+  const float* wsc1;      // and W1
   size_t wgs;             // elements between the matrices of consecutive groups
   int K;                  // reduction length, multiple of 64
   int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it

@@ -214,6 +214,9 @@ int kc_of(int dtype) { return dtype == DG_BF16 ? 32 : 16; }
 const char* check_config(const dg_model_config* c) {
   if (!c) return "null config";
   if (c->dtype != DG_F32 && c->dtype != DG_BF16) return "dtype must be DG_F32 or DG_BF16";
+  if (c->expert_format != DG_EXPERTS_NATIVE && c->expert_format != DG_EXPERTS_FP8)
+    return "expert_format must be DG_EXPERTS_NATIVE or DG_EXPERTS_FP8";
+  if (c->expert_format == DG_EXPERTS_FP8 && c->dtype != DG_BF16) return "FP8 experts need a bf16 model";
   if (c->vocab <= 0 || c->d_model <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
       c->head_dim <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->expert_hidden <= 0 || c->shared_hidden <= 0 ||
       c->max_ctx <= 0 || c->max_requests <= 0)
@@ -438,15 +441,20 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   return pend;
 }
 
-void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void* W1, size_t wgs, int K, int N,
-                   const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo,
-                   const int32_t* rowsrc = nullptr) {
+// Routed launch over the expert work list; with FP8 experts W0 / W1 hold E4M3
+// codes and s0 / s1 their per-row scales ([E][N] each).
+void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void* W1, const float* s0,
+                   const float* s1, size_t wgs, int K, int N, const int32_t* units, const int32_t* n_units, int nblk,
+                   void* out, int ldo, const int32_t* rowsrc = nullptr) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
   a.W0 = W0;
   a.W1 = W1;
+  a.w8 = c->cfg.expert_format == DG_EXPERTS_FP8;
+  a.wsc0 = s0;
+  a.wsc1 = s1;
   a.wgs = wgs;
   a.K = K;
   a.N = N;
@@ -588,10 +596,12 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     // routed experts over the expert-sorted rows: W1/W3 + SwiGLU gathering the
     // row-major normalised rows into c->hbuf (fragment-major, sorted rows), W2
     // from there into c->ybuf at each row's pair index
-    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, (size_t)m.expert_hidden * m.d_model,
+    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, w.w1_scale, w.w3_scale,
+                                         (size_t)m.expert_hidden * m.d_model,
                                          m.d_model, m.expert_hidden, c->units_up, c->n_units, nb_up, c->hbuf,
                                          m.expert_hidden, c->rowsrc));
-    KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, (size_t)m.d_model * m.expert_hidden,
+    KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, w.w2_scale, nullptr,
+                                           (size_t)m.d_model * m.expert_hidden,
                                            m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,
                                            m.d_model));
   }
@@ -704,6 +714,8 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
     const void* ps[] = {w.attn_norm, w.wq, w.wk, w.wv, w.wo, w.ffn_norm, w.router, w.w1, w.w3, w.w2, w.sw1, w.sw3, w.sw2};
     for (const void* p : ps)
       if (!p) return fail(nullptr, DG_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
+    if (cfg->expert_format == DG_EXPERTS_FP8 && (!w.w1_scale || !w.w3_scale || !w.w2_scale))
+      return fail(nullptr, DG_ERR_INVALID_ARG, "null expert scale pointer in layer %d", l);
   }
   if (!kv_dev || !scratch_dev) return fail(nullptr, DG_ERR_INVALID_ARG, "null kv or scratch buffer");
   dg_model_config m = *cfg;

@@ -55,19 +55,21 @@ __device__ __forceinline__ int lds_slot(int row, int seg) {
   return row * (8 * KSUB) + (seg & ~7) + ((seg & 7) ^ (row & 7));
 }
 
-template <int N>
+// A thread's share of one weight chunk: N segments of 16 bytes of bf16 (T = uint4)
+// or of the 8 bytes of E4M3 codes they are widened from (T = uint2).
+template <int N, typename T>
 struct Segs {
-  uint4 v[N];
+  T v[N];
 };
 
 // Register ring of up to eight weight chunks, selected by a compile-time index
 // (a runtime index would put the ring in scratch memory).
-template <int N>
+template <int N, typename T>
 struct Ring8 {
-  Segs<N> r0, r1, r2, r3, r4, r5, r6, r7;
+  Segs<N, T> r0, r1, r2, r3, r4, r5, r6, r7;
 };
-template <int I, int N>
-__device__ __forceinline__ Segs<N>& ring(Ring8<N>& R) {
+template <int I, int N, typename T>
+__device__ __forceinline__ Segs<N, T>& ring(Ring8<N, T>& R) {
   if constexpr (I == 0) return R.r0;
   else if constexpr (I == 1) return R.r1;
   else if constexpr (I == 2) return R.r2;
@@ -92,16 +94,29 @@ __device__ __forceinline__ v8s (&abuf(AFrags<MT, KSUB>& F))[MT][2 * KSUB] {
   else return F.b3;
 }
 
-// Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue.
-template <int EPI, int NTN>
-__device__ __forceinline__ const bf16_t* weight_row(const WsArgs& a, int g, int nb, int r) {
+// Eight E4M3 codes (little-endian bytes, in reduction order) widened to eight
+// bf16 values: exact, since an E4M3 value has a 4-bit significand and an
+// exponent inside bf16's range.  The conversion reads the OCP E4M3 encoding.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
+// Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue, as a byte
+// address; ES = bytes per weight (2: bf16, 1: E4M3 codes).
+template <int EPI, int NTN, int ES = 2>
+__device__ __forceinline__ const char* weight_row(const WsArgs& a, int g, int nb, int r) {
   if constexpr (EPI == WS_EPI_SWIGLU) {
     // rows 0 .. 8 NTN - 1: W1 rows, rows 8 NTN .. 16 NTN - 1: W3 rows, of the same
     // 8 NTN hidden columns
     constexpr int HALF = 8 * NTN;
-    const bf16_t* W = (const bf16_t*)(r < HALF ? a.W0 : a.W1) + (size_t)g * a.wgs;
+    const char* W = (const char*)(r < HALF ? a.W0 : a.W1) + (size_t)g * a.wgs * ES;
     const int n = nb * HALF + (r % HALF);
-    return W + (size_t)min(n, a.N - 1) * a.K;
+    return W + (size_t)min(n, a.N - 1) * a.K * ES;
   } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
     // rows 0..31: columns j0 .. j0+31 of one head's first half, rows 32..63: the
     // matching columns of its second half (RoPE pairs j, j + hd/2)
@@ -112,11 +127,11 @@ __device__ __forceinline__ const bf16_t* weight_row(const WsArgs& a, int g, int 
     if (head < a.hq) { W = (const bf16_t*)a.W0; hl = head; }
     else if (head < a.hq + a.hkv) { W = (const bf16_t*)a.W1; hl = head - a.hq; }
     else { W = (const bf16_t*)a.W2; hl = head - a.hq - a.hkv; }
-    return W + (size_t)(hl * a.hd + j) * a.K;
+    return (const char*)(W + (size_t)(hl * a.hd + j) * a.K);
   } else {
-    const bf16_t* W = (const bf16_t*)a.W0 + (size_t)g * a.wgs;
+    const char* W = (const char*)a.W0 + (size_t)g * a.wgs * ES;
     const int n = nb * (16 * NTN) + r;
-    return W + (size_t)min(n, a.N - 1) * a.K;
+    return W + (size_t)min(n, a.N - 1) * a.K * ES;
   }
 }
 
@@ -150,29 +165,33 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
 // load address is clamped to valid memory, so the number of loads in flight is
 // the same in every iteration and the compiler can wait for exactly the load it
 // needs.  All variants execute the same barriers.
-template <int NTN, int KSUB, int MT, int MA, bool GATHER, int RING>
+template <int NTN, int KSUB, int MT, int MA, bool GATHER, int RING, bool W8>
 __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], const char* const (&gsrc)[NTN * KSUB / 4],
                                           const int (&slot)[NTN * KSUB / 4], const int (&sub)[NTN * KSUB / 4],
                                           const char* const (&ap)[MT], int nk64, int lane, v4f (&acc)[MT][NTN]) {
-  constexpr int NSEG = NTN * KSUB / 4;  // 16-byte weight segments per thread per chunk
+  constexpr int NSEG = NTN * KSUB / 4;  // 16-byte LDS segments (8 weights) per thread per chunk
+  using SegT = std::conditional_t<W8, uint2, uint4>;
+  constexpr int SUBB = W8 ? 64 : 128;   // bytes of a weight row per 64-element sub-chunk
   static_assert(RING == 4 || RING == 8, "ring of 4 or 8 chunks");
   const int nchunk = (nk64 + KSUB - 1) / KSUB;
-  Ring8<NSEG> R;
-  auto fetch = [&](Segs<NSEG>& S, int c) {
+  Ring8<NSEG, SegT> R;
+  auto fetch = [&](Segs<NSEG, SegT>& S, int c) {
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       const int kc = min(c * KSUB + sub[i], nk64 - 1);
-      S.v[i] = *(const uint4*)(gsrc[i] + kc * 128);
+      S.v[i] = *(const SegT*)(gsrc[i] + kc * SUBB);
     }
   };
-  // Stores chunk c from S into its stage; sub-chunks past the end store zeros (a
-  // mask on the values: a conditional between two lvalues would make the compiler
-  // select between their addresses and keep the ring in scratch memory).
-  auto store = [&](uint4* stage, const Segs<NSEG>& S, int c) {
+  // Stores chunk c from S into its stage (E4M3 codes widened to bf16 on the way);
+  // sub-chunks past the end store zeros (a mask on the values: a conditional
+  // between two lvalues would make the compiler select between their addresses
+  // and keep the ring in scratch memory).
+  auto store = [&](uint4* stage, const Segs<NSEG, SegT>& S, int c) {
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       const uint32_t live = c * KSUB + sub[i] < nk64 ? 0xffffffffu : 0u;
-      stage[slot[i]] = make_uint4(S.v[i].x & live, S.v[i].y & live, S.v[i].z & live, S.v[i].w & live);
+      if constexpr (W8) stage[slot[i]] = e4m3x8_to_bf16(S.v[i].x & live, S.v[i].y & live);
+      else stage[slot[i]] = make_uint4(S.v[i].x & live, S.v[i].y & live, S.v[i].z & live, S.v[i].w & live);
     }
   };
   AFrags<MT, KSUB> F;
@@ -247,8 +266,9 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
   }
 }
 
-template <int EPI, int NTN, int KSUB, int MT, bool GATHER, int RING>
+template <int EPI, int NTN, int KSUB, int MT, bool GATHER, int RING, bool W8 = false>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
+  static_assert(!W8 || EPI == WS_EPI_SWIGLU || EPI == WS_EPI_STORE_F32, "E4M3 weights: routed experts only");
   constexpr int BN = 16 * NTN;
   constexpr int PASS_ROWS = NWAVE * MT * 16;
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte segments per thread per chunk
@@ -306,7 +326,8 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
   for (int i = 0; i < NSEG; ++i) {
     const int sid = tid + NT * i, wr = sid / (8 * KSUB), sg = sid % (8 * KSUB);
-    gsrc[i] = (const char*)(weight_row<EPI, NTN>(a, g, nb, wr) + kc0 * 64) + (sg & 7) * 16;
+    if constexpr (W8) gsrc[i] = weight_row<EPI, NTN, 1>(a, g, nb, wr) + kc0 * 64 + (sg & 7) * 8;
+    else gsrc[i] = weight_row<EPI, NTN>(a, g, nb, wr) + kc0 * 128 + (sg & 7) * 16;
     slot[i] = lds_slot<KSUB>(wr, sg);
     sub[i] = sg >> 3;
   }
@@ -340,9 +361,10 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
       for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER, RING>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else if (MT == 1 || mt_act == 1) ws_stream<NTN, KSUB, MT, 1, GATHER, RING>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else ws_stream<NTN, KSUB, MT, MT, GATHER, RING>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER, RING, W8>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else if (MT == 1 || mt_act == 1)
+      ws_stream<NTN, KSUB, MT, 1, GATHER, RING, W8>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    else ws_stream<NTN, KSUB, MT, MT, GATHER, RING, W8>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
 
     // Epilogue.
     if constexpr (EPI == WS_EPI_LM_STATS) {
@@ -409,8 +431,13 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
             for (int n = 0; n < NTN / 2; ++n) {
               const int col = nb * (8 * NTN) + n * 16 + (lane & 15);
-              if (col < a.N)
-                ((bf16_t*)a.out)[fm_index(frow, col, a.N)] = f2bf(silu_f(acc[j][n][i]) * acc[j][n + NTN / 2][i]);
+              if (col >= a.N) continue;
+              float u = acc[j][n][i], v = acc[j][n + NTN / 2][i];
+              if constexpr (W8) {  // row scales of the W1 and W3 codes
+                u *= a.wsc0[(size_t)g * a.N + col];
+                v *= a.wsc1[(size_t)g * a.N + col];
+              }
+              ((bf16_t*)a.out)[fm_index(frow, col, a.N)] = f2bf(silu_f(u) * v);
             }
           } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
             const int half = a.hd / 2, per_head = half / 32;
@@ -455,7 +482,8 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
               if (col >= a.N) continue;
               const size_t o = (size_t)orow * a.ldo + col;
               if constexpr (EPI == WS_EPI_STORE_BF16) ((bf16_t*)a.out)[o] = f2bf(acc[j][n][i]);
-              else if constexpr (EPI == WS_EPI_STORE_F32) ((float*)a.out)[o] = acc[j][n][i];
+              else if constexpr (EPI == WS_EPI_STORE_F32)
+                ((float*)a.out)[o] = W8 ? acc[j][n][i] * a.wsc0[(size_t)g * a.N + col] : acc[j][n][i];
               else if (a.ksplit > 1) a.part_out[(size_t)ks * a.part_stride + o] = acc[j][n][i];  // partial sum
               else ((float*)a.out)[o] += acc[j][n][i];
             }
@@ -511,16 +539,25 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 #ifndef DG_WS_RING_ROUTED
 #define DG_WS_RING_ROUTED 4
 #endif
+// E4M3 weights: a ring of 8 (the same bytes in flight as bf16's 4) needs more
+// registers than two blocks per CU allow and measured slower.
+#ifndef DG_WS_RING_FP8
+#define DG_WS_RING_FP8 4
+#endif
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
-  constexpr int RD = DG_WS_RING_DENSE, RR = DG_WS_RING_ROUTED;
+  constexpr int RD = DG_WS_RING_DENSE, RR = DG_WS_RING_ROUTED, R8 = DG_WS_RING_FP8;
   if (a.counts) {  // grouped (routed experts)
-    if (a.rowsrc && epi == WS_EPI_SWIGLU) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, RR><<<grid, NT, 0, s>>>(a);
-    else if (!a.rowsrc && epi == WS_EPI_STORE_F32)
-      k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RR><<<grid, NT, 0, s>>>(a);
-    else abort();
+    if (a.rowsrc && epi == WS_EPI_SWIGLU) {
+      if (a.w8) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, R8, true><<<grid, NT, 0, s>>>(a);
+      else k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, RR><<<grid, NT, 0, s>>>(a);
+    } else if (!a.rowsrc && epi == WS_EPI_STORE_F32) {
+      if (a.w8) k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, R8, true><<<grid, NT, 0, s>>>(a);
+      else k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RR><<<grid, NT, 0, s>>>(a);
+    } else abort();
     return;
   }
+  if (a.w8) abort();  // E4M3 weights: routed experts only
   switch (epi) {
     case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;

@@ -37,7 +37,8 @@ class ModelConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "vocab", "d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
         "expert_hidden", "shared_hidden", "canvas_len", "max_ctx", "max_requests", "prefill_chunk")] + [
-        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("expert_format", ctypes.c_int32)]
 
 
 SAMPLER_MODES = {"threshold": 0, "budget": 1}
@@ -48,7 +49,10 @@ class SamplerConfig(ctypes.Structure):
                 ("budget", ctypes.c_float), ("stop_entropy", ctypes.c_float)]
 
 
-_LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router", "w1", "w3", "w2", "sw1", "sw3", "sw2")
+_LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router", "w1", "w3", "w2", "sw1", "sw3", "sw2",
+                 "w1_scale", "w3_scale", "w2_scale")
+_SCALE_FIELDS = ("w1_scale", "w3_scale", "w2_scale")
+DG_EXPERTS_NATIVE, DG_EXPERTS_FP8 = 0, 1
 
 
 class LayerWeights(ctypes.Structure):
@@ -145,7 +149,8 @@ def model_config(w, max_requests=None, max_ctx=None, prefill_chunk=0):
                        expert_hidden=w.expert_hidden, shared_hidden=w.shared_hidden, canvas_len=w.canvas_len,
                        max_ctx=w.max_ctx if max_ctx is None else max_ctx,
                        max_requests=w.n_requests if max_requests is None else max_requests,
-                       prefill_chunk=prefill_chunk, rope_theta=w.rope_theta, rms_eps=w.rms_eps, dtype=dtype)
+                       prefill_chunk=prefill_chunk, rope_theta=w.rope_theta, rms_eps=w.rms_eps, dtype=dtype,
+                       expert_format=DG_EXPERTS_FP8 if w.expert_format == "fp8" else DG_EXPERTS_NATIVE)
 
 
 def dg_workspace_size(cfg):
@@ -182,6 +187,8 @@ class Decoder:
         self._layers = (LayerWeights * L)()
         for l, lt in enumerate(weights["layers"]):
             for n in _LAYER_FIELDS:
+                if n in _SCALE_FIELDS and n not in lt:
+                    continue  # bf16 experts: no scales
                 setattr(self._layers[l], n, lt[n].data_ptr())
         self._w = Weights(embed=weights["embed"].data_ptr(), final_norm=weights["final_norm"].data_ptr(),
                           layers=self._layers)

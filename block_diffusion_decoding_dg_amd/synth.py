@@ -16,7 +16,7 @@ Generators: torch's seeded normal generator (CPU or GPU device) per tensor,
 seed = hash of (workload seed, tensor index); fp32 then round-to-nearest-even
 bf16 for the bf16 workloads.  Prompts: numpy PCG64 uniform integers.
 """
-from dataclasses import dataclass, asdict
+from dataclasses import dataclass, asdict, replace
 from typing import List, Optional
 
 import numpy as np
@@ -46,6 +46,7 @@ class Workload:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
     init_std: float = 0.02
+    expert_format: str = "native"   # or "fp8": routed experts as E4M3 codes + row scales
 
     @property
     def n_blocks(self):
@@ -102,6 +103,10 @@ WORKLOADS = {
                           n_requests=1, tau=1.0, max_steps=256),
 }
 
+# The mid-size and full-size shapes with FP8 (E4M3) routed experts.
+WORKLOADS["mid_fp8"] = replace(WORKLOADS["mid"], name="mid_fp8", expert_format="fp8")
+WORKLOADS["full_fp8"] = replace(WORKLOADS["full"], name="full_fp8", expert_format="fp8")
+
 LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router",
                  "w1", "w3", "w2", "sw1", "sw3", "sw2")
 
@@ -153,8 +158,23 @@ def make_weights(w: Workload, seed: int = 0, device="cpu", layers: Optional[List
                 lt[name] = torch.ones(shapes[name], device=device, dtype=dt)
             else:
                 lt[name] = _normal(shapes[name], w.init_std, seed, 1 + l * 64 + i, device, dt)
+        if w.expert_format == "fp8":
+            for name in ("w1", "w3", "w2"):
+                lt[name], lt[name + "_scale"] = quantize_rows_e4m3(lt[name])
         out["layers"].append(lt)
     return out
+
+
+def quantize_rows_e4m3(w: torch.Tensor):
+    """Stand-in for an FP8 checkpoint of a weight tensor [..., out, in]: per output
+    row a float32 scale max|w| / 448 (1 for a zero row) and the E4M3 codes of
+    w / scale (torch's round-to-nearest-even cast), as uint8.  The random bf16
+    weights are drawn first, so the FP8 model is the bf16 one quantized."""
+    wf = w.float()
+    amax = wf.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (wf / scale[..., None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
 
 
 def make_prompt(w: Workload, seed: int = 0, length: Optional[int] = None):

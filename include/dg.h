@@ -56,6 +56,22 @@ typedef enum dg_status {
 typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
 
 /*
+ * Storage of the routed experts' weights.  The pages name FP8 checkpoints
+ * ("Google open-sources DiffusionGemma: H100 reaches 1000 TPS", section
+ * "Hardware requirements"; "DiffusionGemma hits ~1,500 TPS on one H100",
+ * section "Serve it with vLLM") without their layout; the format taken:
+ *   DG_EXPERTS_NATIVE: the model dtype, like every other weight;
+ *   DG_EXPERTS_FP8: one byte per weight in the OCP FP8 E4M3 encoding (bias 7,
+ *     subnormals at exponent 0, 0x7F / 0xFF NaN, largest finite 448) plus one
+ *     float32 scale per output row (dg_layer_weights.w1_scale, ...):
+ *     W[e][n][k] = scale[e][n] * e4m3(code[e][n][k]).  The kernels widen the
+ *     codes to bf16 (exact) and apply the scale to the fp32 row sum.  bf16
+ *     models only (DG_ERR_INVALID_ARG otherwise).  Code arrays must not hold
+ *     NaN codes.
+ */
+typedef enum dg_expert_format { DG_EXPERTS_NATIVE = 0, DG_EXPERTS_FP8 = 1 } dg_expert_format;
+
+/*
  * Model shape.  Pre-norm decoder blocks: RMSNorm (gain per channel, eps under
  * the root), grouped-query attention with rotate-half RoPE at absolute
  * positions (pairs j, j + head_dim/2; angle pos * rope_theta^(-2j/head_dim);
@@ -90,6 +106,7 @@ typedef struct dg_model_config {
   float rope_theta;      /* 10000 */
   float rms_eps;         /* 1e-6 */
   int32_t dtype;         /* dg_dtype of weights, KV cache and activations */
+  int32_t expert_format; /* dg_expert_format of the routed experts' w1, w3, w2 */
 } dg_model_config;
 
 /*
@@ -132,10 +149,14 @@ typedef struct dg_sampler_config {
  * Device weights of one layer, dtype of the model, row-major [out, in]:
  *   attn_norm, ffn_norm [d]; wq [Hq*hd, d]; wk, wv [Hkv*hd, d]; wo [d, Hq*hd];
  *   router [E, d]; w1, w3 [E, eh, d]; w2 [E, d, eh]; sw1, sw3 [sh, d]; sw2 [d, sh].
+ * With expert_format DG_EXPERTS_FP8, w1, w3 and w2 hold E4M3 codes (uint8, same
+ * shapes) and w1_scale, w3_scale [E, eh] and w2_scale [E, d] their float32 row
+ * scales; otherwise the scale pointers are ignored.
  */
 typedef struct dg_layer_weights {
   const void *attn_norm, *wq, *wk, *wv, *wo;
   const void *ffn_norm, *router, *w1, *w3, *w2, *sw1, *sw3, *sw2;
+  const float *w1_scale, *w3_scale, *w2_scale;
 } dg_layer_weights;
 
 typedef struct dg_weights {

@@ -10,12 +10,14 @@ Parity pins (see tests/test_oracle_*.py): Philox against numpy's own
 Philox4x64-10; attention and RoPE against closed forms; the MoE against a
 dense all-experts evaluation with a gate mask; entropy against scipy and
 closed forms; the sampler against its invariants and brute-force
-enumeration; the commit against a one-shot forward under the block mask.
+enumeration; the commit against a one-shot forward under the block mask; the
+E4M3 decoding against torch's float8_e4m3fn and the format's closed forms.
 Logit values of a whole random-weight model have no printed worked example in
 the pages: beyond those pins they are "parity unpinned".
 """
 from .model import (ModelConfig, LayerWeights, Weights, Precision, round_bf16, rmsnorm, rope,
                     attention, silu, topk_select, route, moe, layer_forward, lm_head_stats)
 from .philox import philox4x64_10, draw_tokens
+from .quant import decode_e4m3, dequantize_rows, E4M3_MAX
 from .decode import (SamplerConfig, RequestState, StepResult, new_request, prefill, start_canvas,
                      canvas_forward, sampler_decide, entropy_fixed, budget_decide, denoise_step, commit_block, generate)

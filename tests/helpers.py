@@ -22,7 +22,11 @@ def oracle_weights(w: synth.Workload, tw) -> oracle.Weights:
         if lt is None:
             layers.append(None)
             continue
-        layers.append(oracle.LayerWeights(**{k: to_f64(v) for k, v in lt.items()}))
+        d = {k: to_f64(v) for k, v in lt.items() if not k.endswith("_scale")}
+        if "w1_scale" in lt:   # FP8 experts: the oracle's own decoding of the codes
+            for n in ("w1", "w3", "w2"):
+                d[n] = oracle.dequantize_rows(lt[n].cpu().numpy(), lt[n + "_scale"].cpu().numpy())
+        layers.append(oracle.LayerWeights(**d))
     return oracle.Weights(embed=to_f64(tw["embed"]), final_norm=to_f64(tw["final_norm"]),
                           layers=layers)
 

@@ -131,6 +131,45 @@ def test_full_moe_op(layer0, t, skew):
     dec.close()
 
 
+@pytest.mark.parametrize("t,skew", [(256, 0.0), (256, 4.0), (2048, 4.0)])
+def test_full_moe_op_fp8(layer0, t, skew):
+    """MoE half with FP8 (E4M3 + row scale) routed experts: layer 0's experts
+    quantized; the oracle decodes the same codes itself."""
+    tw, cfg, lw, _, _, prec = layer0
+    W8 = synth.WORKLOADS["full_fp8"]
+    l8 = dict(tw["layers"][0])
+    for n in ("w1", "w3", "w2"):
+        l8[n], l8[n + "_scale"] = synth.quantize_rows_e4m3(tw["layers"][0][n])
+    tw8 = dict(tw, layers=[l8] * W.n_layers)
+    lw8 = oracle.LayerWeights(**{**lw.__dict__, **{n: oracle.dequantize_rows(l8[n].cpu().numpy(),
+                                                                              l8[n + "_scale"].cpu().numpy())
+                                                    for n in ("w1", "w3", "w2")}})
+    dec = make_decoder(W8, tw8, max_requests=t // 256)
+    x = synth.make_normal((t, W.d_model), seed=t + int(skew), std=1.0, device="cuda")
+    if skew:
+        x = x + skew * synth.make_normal((1, W.d_model), seed=99, std=1.0, device="cuda")
+    xg = x.contiguous().clone()
+    ids = torch.empty((t, W.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((t, W.top_k), dtype=torch.float32, device="cuda")
+    log("full fp8 moe t=%d skew %.0f" % (t, skew))
+    dec.dg_op_moe(0, xg, ids, gates)
+    xo = x.cpu().numpy().astype(np.float64)
+    b = oracle.round_bf16(oracle.rmsnorm(xo, lw8.ffn_norm, cfg.rms_eps))
+    f, r, oids, ogates = oracle.moe(b, lw8, cfg, prec)
+    tr = oracle.model.LayerTrace(router_logits=r, ids=oids, gates=ogates)
+    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 2e-2)
+    keep = np.setdiff1d(np.arange(t), flips)
+    got = xg.cpu().numpy().astype(np.float64)
+    worst = max(rel_l2(got[i] - xo[i], f[i]) for i in keep)
+    # the quantized experts differ from the bf16 ones by the E4M3 rounding (~2^-4 relative)
+    fb, _, _, _ = oracle.moe(b[:8], lw, cfg, prec)
+    qerr = max(rel_l2(f[i], fb[i]) for i in range(8))
+    log("full fp8 moe t=%d skew %.0f: %d router flips, worst rel L2 %.2e (fp8 vs bf16 model: %.2e)"
+        % (t, skew, len(flips), worst, qerr))
+    assert worst <= RL2 and qerr > 4 * worst
+    dec.close()
+
+
 def test_full_lm_head_op(layer0):
     tw, cfg, _, embed, fnorm, prec = layer0
     dec = make_decoder(W, tw)

@@ -49,13 +49,19 @@ def _logit_tol(g, o):
         assert e <= LOGIT_RL2, ("logits rel L2", i, e)
 
 
-@pytest.fixture(scope="module")
-def setup():
-    log("mid: generating weights on the GPU")
-    tw_gpu = synth.make_weights(W, seed=0, device="cuda")
+@pytest.fixture(scope="module", params=["mid", "mid_fp8"])
+def setup(request):
+    """The mid-size model with bf16 routed experts, and the same model with its
+    routed experts quantized to FP8 (E4M3 codes + row scales; the oracle decodes
+    the codes itself)."""
+    w = synth.WORKLOADS[request.param]
+    log("%s: generating weights on the GPU" % w.name)
+    tw_gpu = synth.make_weights(w, seed=0, device="cuda")
     torch.cuda.synchronize()
-    ow = helpers.oracle_weights(W, tw_gpu)
-    return tw_gpu, helpers.oracle_config(W), ow, helpers.oracle_precision(W)
+    ow = helpers.oracle_weights(w, tw_gpu)
+    yield w, tw_gpu, helpers.oracle_config(w), ow, helpers.oracle_precision(w)
+    del tw_gpu
+    torch.cuda.empty_cache()
 
 
 def _cache_rows(dec, st, ocfg, lo, hi, req=0):
@@ -101,7 +107,7 @@ def _check_cache(dec, st, ocfg, lo, hi, what, traces=None):
 
 
 def test_mid_prefill_steps_commit(setup):
-    tw, ocfg, ow, prec = setup
+    W, tw, ocfg, ow, prec = setup
     prompt = synth.make_prompt(W, seed=0)
     seed = 42
     dec = make_decoder(W, tw)

@@ -624,3 +624,40 @@ def test_commit_before_done_is_rejected():
     oracle.denoise_step(st, cfg, oracle.SamplerConfig(0.5, 4), ow, oracle.Precision())
     with pytest.raises(ValueError):
         oracle.commit_block(st, cfg, ow, oracle.Precision())
+
+
+# ------------------------------------------------------ FP8 expert weights ----
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))   # -0.0 at 0x80
+
+
+def test_e4m3_closed_forms():
+    d = oracle.decode_e4m3
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0                    # exponent field 7 = bias
+    assert d(0x7E) == oracle.E4M3_MAX == 448.0                   # 2^8 * 1.75
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9     # subnormals m * 2^-9
+    assert d(0x08) == 2.0 ** -6                                  # smallest normal
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    pos = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)                              # codes 0..126 increase strictly
+
+
+def test_dequantize_rows_scales_each_output_row():
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 256, (3, 5, 7)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                         # no NaN codes
+    s = rng.uniform(0.5, 2.0, (3, 5)).astype(np.float32)
+    w = oracle.dequantize_rows(codes, s)
+    for e in range(3):
+        for n in range(5):
+            assert np.array_equal(w[e, n], float(s[e, n]) * oracle.decode_e4m3(codes[e, n]))
+    x = rng.standard_normal(7)
+    # a row scale commutes with the reduction (the kernel applies it after the sum)
+    assert np.allclose(w[1] @ x, s[1].astype(np.float64) * (oracle.decode_e4m3(codes[1]) @ x), rtol=1e-14)
