@@ -41,6 +41,7 @@ MFMA_F32_TFLOPS = 157.3
 # Routed-expert W1/W3 kernel: the largest single kernel of the step (2/3 of the
 # routed expert bytes, which are ~89% of the step's bytes at the full shape).
 DOMINANT = "expert_up"
+TIMER_EVERY = 8  # the dominant kernel is timed on one timed step in this many
 
 
 def esize(w):
@@ -212,6 +213,9 @@ def timed_run(w, tw, K, W, kernel, seed, log):
     prefill_ms = prefill_all()  # reset to block 0, step 0
 
     dec.dg_kernel_timer(kernel)
+    # HIP events on every 8th step only: each event pair holds the stream for a
+    # few microseconds, which timing every launch would add to the step time
+    dec.dg_kernel_timer_every(TIMER_EVERY)
     torch.cuda.synchronize()
     log("bench: timing %d steps" % K)
     trace = []  # (block, step, tokens) per request per step

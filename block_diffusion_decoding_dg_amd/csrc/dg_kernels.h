@@ -58,6 +58,8 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
                          float* mlpart, void* o, int rows, hipStream_t s);
 // Router top-k: logits [rows][E] fp32 -> ids [rows][k], gates [rows][k].
 void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s);
+// bf16 router logits [rows][E] fp32 from the fragment-major normalised rows (d a multiple of 64).
+void dg_launch_router(const void* b_fm, int rows, int d, const void* wg, int E, float* logits, hipStream_t s);
 // Permutation: counts[E], offsets[E], perm[rows*k] (pair index t*k + j, token order per expert).
 void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
                        hipStream_t s);

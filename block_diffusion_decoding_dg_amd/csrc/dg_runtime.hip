@@ -124,6 +124,9 @@ struct dg_ctx {
 
   // Kernel timer: HIP event pairs around every launch of one kernel family.
   int kt_family = 0;
+  int kt_every = 1;       // time every kt_every-th step or commit
+  int64_t kt_calls = 0;   // steps and commits since dg_kernel_timer_every
+  bool kt_on = true;      // the current step or commit is timed
   std::vector<hipEvent_t> kt_ev;  // 2 per recorded launch
   size_t kt_used = 0;
   double kt_ms = 0.0;
@@ -171,7 +174,7 @@ dg_status fail(dg_ctx* c, dg_status st, const char* fmt, ...) {
 // Kernel timer.  kt_begin/kt_end bracket one launch of family f; the events are
 // read back (and the pairs reused) by kt_collect after the stream has synchronised.
 void kt_begin(dg_ctx* c, int f, hipStream_t s) {
-  if (c->kt_family != f) return;
+  if (c->kt_family != f || !c->kt_on) return;
   while (c->kt_ev.size() < c->kt_used + 2) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) { c->kt_family = 0; return; }
@@ -180,7 +183,7 @@ void kt_begin(dg_ctx* c, int f, hipStream_t s) {
   hipEventRecord(c->kt_ev[c->kt_used], s);
 }
 void kt_end(dg_ctx* c, int f, hipStream_t s) {
-  if (c->kt_family != f) return;
+  if (c->kt_family != f || !c->kt_on) return;
   hipEventRecord(c->kt_ev[c->kt_used + 1], s);
   c->kt_used += 2;
 }
@@ -587,8 +590,7 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KTS(c, DG_KF_SHARED_DOWN, c->side, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x,
                                                                 c->side, c->parts2));
     HIPCK_V(hipEventRecord(c->ev_join, c->side));
-    KT(c, DG_KF_ROUTER, launch_dense(c, WS_EPI_STORE_F32, c->xn, rows, m.d_model, w.router, nullptr, m.n_experts, rlog,
-                                     m.n_experts));
+    KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
     KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
                                          c->offsets16, c->rowsrc, c->n_units + 2, nb_up, c->units_up, c->n_units, nb_dn,
@@ -825,6 +827,7 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
     if (!q.active) fresh.push_back(r);
   }
   if (slot_req.empty()) return fail(c, DG_ERR_STATE, "no request can take a denoising step");
+  c->kt_on = c->kt_calls++ % c->kt_every == 0;
   hipStream_t s = c->stream;
   if (!fresh.empty()) {
     for (int r : fresh) {
@@ -868,6 +871,7 @@ dg_status dg_commit_block(dg_ctx* c, int32_t req, int32_t* out_ids) {
   if (st != DG_OK) return st;
   Request& q = c->req[req];
   if (!q.active || !q.done) return fail(c, DG_ERR_STATE, "request %d has no finished canvas", req);
+  c->kt_on = c->kt_calls++ % c->kt_every == 0;
   hipStream_t s = c->stream;
   std::vector<int> one{req};
   const DgSampleArgs a = sample_args(c, one);
@@ -1136,6 +1140,14 @@ dg_status dg_kernel_timer(dg_ctx* c, int32_t family) {
   c->kt_family = family;
   c->kt_ms = 0.0;
   c->kt_launches = 0;
+  return DG_OK;
+}
+
+dg_status dg_kernel_timer_every(dg_ctx* c, int32_t every) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (every < 1) return fail(c, DG_ERR_INVALID_ARG, "every must be >= 1");
+  c->kt_every = every;
+  c->kt_calls = 0;
   return DG_OK;
 }
 

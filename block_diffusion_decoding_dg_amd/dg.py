@@ -20,7 +20,7 @@ DG_F32, DG_BF16 = 0, 1
 EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "dg_commit_block", "dg_generate",
            "dg_destroy", "dg_last_error", "dg_get_request", "dg_get_canvas", "dg_set_canvas", "dg_set_committed",
            "dg_last_step_rows", "dg_last_step_router_logits", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
-           "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read")
+           "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read", "dg_kernel_timer_every")
 
 KERNEL_FAMILIES = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "out_proj": 5, "router": 6, "permute": 7,
                    "expert_up": 8, "expert_down": 9, "shared_up": 10, "shared_down": 11, "combine": 12,
@@ -116,6 +116,7 @@ def load():
         "dg_philox_tokens": [U64, I32, I32, I32, I32, P, P],
         "dg_kernel_timer": [P, I32],
         "dg_kernel_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+        "dg_kernel_timer_every": [P, ctypes.c_int32],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -321,6 +322,9 @@ class Decoder:
     def dg_kernel_timer(self, family):
         f = KERNEL_FAMILIES[family] if isinstance(family, str) else int(family)
         self._check(self.lib.dg_kernel_timer(self.ctx, f))
+
+    def dg_kernel_timer_every(self, every):
+        self._check(self.lib.dg_kernel_timer_every(self.ctx, every))
 
     def dg_kernel_timer_read(self):
         ms, n = ctypes.c_double(), ctypes.c_int64()

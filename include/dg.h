@@ -418,6 +418,12 @@ dg_status dg_kernel_timer(dg_ctx* ctx, int32_t family);
  * dg_kernel_timer.  Synchronizes the stream. */
 dg_status dg_kernel_timer_read(dg_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* Bracket the timed family's launches only in every `every`-th denoising step or
+ * block commit from now on (1, the default: all).  Each event pair costs a few
+ * microseconds of stream time, so sampling keeps the timer from slowing the
+ * steps it measures.  Errors: DG_ERR_INVALID_ARG if every < 1. */
+dg_status dg_kernel_timer_every(dg_ctx* ctx, int32_t every);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,7 @@ def test_create_validates_before_device_work(lib):
 def test_null_context_calls_fail_cleanly(lib):
     info = (dg.StepInfo * 1)()
     assert lib.dg_denoise_step(None, info) == dg.DG_ERR_INVALID_ARG
+    assert lib.dg_kernel_timer_every(None, 1) == dg.DG_ERR_INVALID_ARG
     assert lib.dg_prefill(None, 0, None, 0, 0) == dg.DG_ERR_INVALID_ARG
     assert lib.dg_commit_block(None, 0, None) == dg.DG_ERR_INVALID_ARG
     assert lib.dg_philox_tokens(0, -1, 0, 4, 10, None, None) == dg.DG_ERR_INVALID_ARG
