@@ -407,7 +407,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 // sums into c->parts, and the returned DgParts must be folded into out by the
 // next row kernel (in range order, so the result is deterministic).
 DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, int N, float* out,
-                         hipStream_t st = nullptr, float* parts = nullptr) {
+                         hipStream_t st = nullptr, float* parts = nullptr, int max_ksplit = DG_MAX_KSPLIT) {
   if (!parts) parts = c->parts;
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
   WsArgs a;
@@ -425,7 +425,7 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   a.msplit = std::max(1, (M + 127) / 128);
   int ks = 1;
   if (M <= c->parts_rows && N == c->cfg.d_model)
-    ks = std::min(DG_MAX_KSPLIT, std::max(1, DG_DENSE_BLOCKS / (padded * a.msplit)));
+    ks = std::min(max_ksplit, std::max(1, DG_DENSE_BLOCKS / (padded * a.msplit)));
   const int nk = K / 64;
   const int kchunks = (nk + ks - 1) / ks;
   ks = (nk + kchunks - 1) / kchunks;  // every range non-empty
@@ -587,8 +587,11 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     HIPCK_V(hipStreamWaitEvent(c->side, c->ev_fork, 0));
     KTS(c, DG_KF_SHARED_UP, c->side, launch_dense(c, WS_EPI_SWIGLU, c->xn, rows, m.d_model, w.sw1, w.sw3, m.shared_hidden,
                                                   c->hs, m.shared_hidden, c->side));
+    // W2 adds straight into the residual: off the critical path, a split
+    // reduction would only add its partial sums to the combine's reads.  Nothing
+    // on the main stream touches c->x between the fork and the join.
     KTS(c, DG_KF_SHARED_DOWN, c->side, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x,
-                                                                c->side, c->parts2));
+                                                                c->side, c->parts2, 1));
     HIPCK_V(hipEventRecord(c->ev_join, c->side));
     KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;

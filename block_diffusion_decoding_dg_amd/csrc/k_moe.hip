@@ -12,83 +12,95 @@
 #include "gemm_core.h"
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per row, four rows per block.  The k largest logits, ties to
-// the lower expert id (a NaN logit ranks lowest): the rank of logit e is the
-// number of logits that beat it under that order, and the entries of rank < k
-// are the selection, in rank order.  Each lane ranks its logits against the
-// row's E logits, read from LDS (the same address for the whole wave).
-// gates = softmax over the k kept logits, summed in rank order.
+// Top-k: one block per row.  The k largest logits, ties to the lower expert id (a
+// NaN logit ranks lowest): the rank of logit e is the number of logits that beat
+// it under that order, and the entries of rank < k are the selection, in rank
+// order.  The E x E comparisons are spread over the block as (logit, slice of 32
+// logits) items and the partial ranks are summed in LDS.  gates = softmax over the k kept logits, summed in
+// rank order.
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int rows, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ gates) {
-  __shared__ float s_v[4][256];
-  __shared__ float s_sel[4][DG_MAX_TOPK];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
-  const bool live = r < rows;  // the block's barriers need every wave
-  for (int e = lane; e < E; e += 64) {
-    const float x = live ? logits[(size_t)r * E + e] : 0.f;
-    s_v[wave][e] = x == x ? x : -INFINITY;
+  __shared__ float s_v[256];
+  __shared__ int s_rank[256];
+  __shared__ float s_sel[DG_MAX_TOPK];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* lrow = logits + (size_t)r * E;
+  if (tid < E) {
+    const float x = lrow[tid];
+    s_v[tid] = x == x ? x : -INFINITY;
+  }
+  s_rank[tid] = 0;
+  __syncthreads();
+  // work items (e, slice): E logits x ceil(E / 32) slices of 32 comparisons
+  const int nsl = (E + 31) / 32;
+  for (int it = tid; it < E * nsl; it += 256) {
+    const int e = it % E, sl = it / E;
+    const float v = s_v[e];
+    const int j0 = sl * 32, j1 = min(j0 + 32, E);
+    int cnt = 0;
+    for (int j = j0; j < j1; ++j) {
+      const float w = s_v[j];
+      cnt += (w > v || (w == v && j < e)) ? 1 : 0;
+    }
+    if (cnt) atomicAdd(&s_rank[e], cnt);
   }
   __syncthreads();
-  for (int e = lane; e < E; e += 64) {
-    const float v = s_v[wave][e];
-    int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const float w = s_v[wave][j];
-      rank += (w > v || (w == v && j < e)) ? 1 : 0;
-    }
-    if (rank < k) {
-      if (live) ids[(size_t)r * k + rank] = e;
-      s_sel[wave][rank] = v;
-    }
+  if (tid < E && s_rank[tid] < k) {
+    ids[(size_t)r * k + s_rank[tid]] = tid;
+    s_sel[s_rank[tid]] = s_v[tid];
   }
   __syncthreads();
-  if (lane == 0 && live) {
-    const float m = s_sel[wave][0];
+  if (tid == 0) {
+    const float m = s_sel[0];
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s += __expf(s_sel[wave][j] - m);
-    for (int j = 0; j < k; ++j) gates[(size_t)r * k + j] = __expf(s_sel[wave][j] - m) / s;
+    for (int j = 0; j < k; ++j) s += __expf(s_sel[j] - m);
+    for (int j = 0; j < k; ++j) gates[(size_t)r * k + j] = __expf(s_sel[j] - m) / s;
   }
 }
 
 void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s) {
   if (rows <= 0) return;
-  k_topk<<<(rows + 3) / 4, 256, 0, s>>>(logits, rows, E, k, ids, gates);
+  k_topk<<<rows, 256, 0, s>>>(logits, rows, E, k, ids, gates);
 }
 
 // ---------------------------------------------------------------------------
 // Router logits of the bf16 model: logits[r][e] = b[r] . Wg[e] in fp32 on the
-// matrix cores.  A block computes one 16-row x 16-expert tile; its four waves
-// take a quarter of the reduction each (two accumulators in alternation, so
-// that consecutive matrix-core operations are independent) and the partial
-// tiles are summed in LDS in wave order.  b is fragment-major (fm_index),
-// Wg row-major [E][d]; d is a multiple of 64.
-__global__ void __launch_bounds__(256) k_router(const bf16_t* __restrict__ b, int rows, int d,
+// matrix cores.  A block computes one 16-row x 16-expert tile; its eight waves
+// take an eighth of the reduction each, issue the loads of up to eight steps
+// before their products (the steps are few, so their latency is what counts),
+// alternate two accumulators, and the partial tiles are summed in LDS in wave
+// order.  b is fragment-major (fm_index), Wg row-major [E][d]; d is a multiple
+// of 64.
+__global__ void __launch_bounds__(512) k_router(const bf16_t* __restrict__ b, int rows, int d,
                                                 const bf16_t* __restrict__ wg, int E, float* __restrict__ logits) {
-  __shared__ v4f s_part[4][64];
+  __shared__ v4f s_part[8][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int net = (E + 15) >> 4;
   const int rt = blockIdx.x / net, et = blockIdx.x % net;
   const int nk = d >> 5;  // 32-element reduction steps
-  const int k0 = wave * nk / 4, k1 = (wave + 1) * nk / 4;
+  const int k0 = wave * nk / 8, k1 = (wave + 1) * nk / 8;
   const char* ap = (const char*)b + (size_t)rt * nk * 1024 + lane * 16;
   const int e = min(et * 16 + (lane & 15), E - 1);
   const char* bp = (const char*)(wg + (size_t)e * d) + (lane >> 4) * 16;
-  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  int kc = k0;
-  for (; kc + 1 < k1; kc += 2) {
-    const v8s a0 = *(const v8s*)(ap + (size_t)kc * 1024), a1 = *(const v8s*)(ap + (size_t)(kc + 1) * 1024);
-    const v8s w0 = *(const v8s*)(bp + kc * 64), w1 = *(const v8s*)(bp + (kc + 1) * 64);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w1, acc1, 0, 0, 0);
+  v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  for (int kg = k0; kg < k1; kg += 8) {
+    v8s a[8], w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kc = min(kg + j, k1 - 1);  // steps past the range are loaded but not used
+      a[j] = *(const v8s*)(ap + (size_t)kc * 1024);
+      w[j] = *(const v8s*)(bp + kc * 64);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (kg + j < k1) acc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], w[j], acc[j & 1], 0, 0, 0);
   }
-  if (kc < k1)
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const v8s*)(ap + (size_t)kc * 1024), *(const v8s*)(bp + kc * 64),
-                                                   acc0, 0, 0, 0);
-  s_part[wave][lane] = acc0 + acc1;
+  s_part[wave][lane] = acc[0] + acc[1];
   __syncthreads();
   if (wave == 0) {
-    const v4f t = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+    v4f t = s_part[0][lane];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) t += s_part[q][lane];
     // lane holds rows 4 (lane / 16) + i, expert et * 16 + lane % 16
     const int col = et * 16 + (lane & 15);
 #pragma unroll
@@ -101,7 +113,7 @@ __global__ void __launch_bounds__(256) k_router(const bf16_t* __restrict__ b, in
 
 void dg_launch_router(const void* b_fm, int rows, int d, const void* wg, int E, float* logits, hipStream_t s) {
   if (rows <= 0) return;
-  k_router<<<((rows + 15) / 16) * ((E + 15) / 16), 256, 0, s>>>((const bf16_t*)b_fm, rows, d, (const bf16_t*)wg, E,
+  k_router<<<((rows + 15) / 16) * ((E + 15) / 16), 512, 0, s>>>((const bf16_t*)b_fm, rows, d, (const bf16_t*)wg, E,
                                                               logits);
 }
 
