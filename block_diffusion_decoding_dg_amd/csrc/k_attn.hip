@@ -441,15 +441,26 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
     stg ^= 1;
   }
   if (!wave_active) return;
+  // The split's output leaves normalised (O / l, at most max |v| in size) as
+  // fp16, half the bytes of fp32 to write and to merge; 11 significant bits
+  // are far below the bf16 rounding of the merged output.  The merge weighs it
+  // by l 2^(m - M).
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
     lrun[qt] += __shfl_xor(lrun[qt], 32, 64);
     if (!qvalid[qt]) continue;
     const size_t qi = (size_t)trow[qt] * sh.hq + qhead[qt];
-    float* op = opart + ((size_t)split * rows_total * sh.hq + qi) * HD;
+    const float inv = lrun[qt] > 0.f ? 1.f / lrun[qt] : 0.f;
+    _Float16* op = reinterpret_cast<_Float16*>(opart) + ((size_t)split * rows_total * sh.hq + qi) * HD;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) *(v4f*)(op + ht * 16 + g4 * 4) = oacc[ht][qt];
+    for (int ht = 0; ht < NHT; ++ht) {
+      typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+      v4h hv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = (_Float16)fminf(fmaxf(oacc[ht][qt][i] * inv, -65504.f), 65504.f);
+      *(v4h*)(op + ht * 16 + g4 * 4) = hv;
+    }
     if (g4 == 0) {
       float* ml = mlpart + ((size_t)split * rows_total * sh.hq + qi) * 2;
       ml[0] = mrun[qt];
@@ -460,32 +471,51 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
 
 // Merge the splits of each (row, q-head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // written row-major or (FM, bf16) fragment-major with hq * hd columns (fm_index).
-template <typename T, bool FM>
-__global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opart, const float* __restrict__ mlpart,
+// P: element type of the split outputs; NORM: they hold O_s / l_s (weighed by l_s).
+template <typename T, bool FM, typename P = float, bool NORM = false>
+__global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opart_f, const float* __restrict__ mlpart,
                                                    int nsplit, int rows_total, int hq, int hd, T* __restrict__ o) {
+  // One wave per (row, q-head).  Lane s reads split s's (m, l) (nsplit <= 64),
+  // the wave reduces M and L, and each lane keeps its split's weight; then
+  // every lane merges four columns, the loads of all splits in flight at once.
+  const P* opart = reinterpret_cast<const P*>(opart_f);
   const size_t qi = blockIdx.x;  // row * hq + qhead
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mlpart[((size_t)s * rows_total * hq + qi) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ml = mlpart + ((size_t)s * rows_total * hq + qi) * 2;
-    if (ml[1] > 0.f) L += exp2f(ml[0] - M) * ml[1];
+  const int lane = threadIdx.x;
+  const size_t sstride = (size_t)rows_total * hq;
+  float m = -INFINITY, l = 0.f;
+  if (lane < nsplit) {
+    const float2 ml = *reinterpret_cast<const float2*>(mlpart + ((size_t)lane * sstride + qi) * 2);
+    m = ml.x;
+    l = ml.y;
   }
+  float M = m;
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+  const float e = l > 0.f ? exp2f(m - M) : 0.f;
+  const float w_own = NORM ? e * l : e;
+  float L = e * l;
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) L += __shfl_xor(L, o2, 64);
   const float invL = 1.f / L;
   const int row = (int)(qi / hq), col0 = (int)(qi % hq) * hd;
-  for (int c = 4 * threadIdx.x; c < hd; c += 256) {
+  for (int c = 4 * lane; c < hd; c += 256) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t base = (size_t)s * rows_total * hq + qi;
-      const float* ml = mlpart + base * 2;
-      if (ml[1] > 0.f) {
-        const float w = exp2f(ml[0] - M);
-        const float4 v = *reinterpret_cast<const float4*>(opart + base * hd + c);
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
+#pragma unroll 8
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float w = __shfl(w_own, sp, 64);
+      const P* src = opart + ((size_t)sp * sstride + qi) * hd + c;
+      float4 v;
+      if constexpr (sizeof(P) == 2) {
+        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+        const v4h h = *reinterpret_cast<const v4h*>(src);
+        v = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+      } else {
+        v = *reinterpret_cast<const float4*>(src);
       }
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
     }
     T* dst = o + (FM ? fm_index(row, col0 + c, hq * hd) : qi * hd + c);
     dst[0] = from_f<T>(acc.x * invL);
@@ -529,7 +559,8 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #define DG_ATTN_LDS(HDV)                                                                                    \
   k_attn_lds<HDV, DG_ATTN_QT(HDV)><<<blocks, 512 / DG_ATTN_QT(HDV), 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit,    \
                                                                            opart, mlpart, rows);                   \
-  k_attn_merge<bf16_t, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (bf16_t*)o)
+  k_attn_merge<bf16_t, true, _Float16, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV,  \
+                                                                          (bf16_t*)o)
   if (dtype == 1) {
     if (sh.hd == 256) { DG_ATTN_LDS(256); }
     else if (sh.hd == 128) { DG_ATTN_LDS(128); }
