@@ -367,6 +367,12 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
 #ifndef DG_DENSE_BLOCKS
 #define DG_DENSE_BLOCKS 256
 #endif
+// Rows per block of the shared expert's W2 (no split reduction).  It overlaps
+// the routed W1/W3 launch; few large blocks slow that launch least (measured:
+// 128-row parts 11.02 ms/step, 32-row 11.17, 16-row 11.44).
+#ifndef DG_SHARED_W2_ROWS
+#define DG_SHARED_W2_ROWS 128
+#endif
 int dense_msplit(int nblk, int M) {
   // At most DG_DENSE_BLOCKS (one per CU) in all: a block streams its tile at a
   // rate set by memory latency, and a CU that receives two blocks finishes last.
@@ -407,7 +413,8 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 // sums into c->parts, and the returned DgParts must be folded into out by the
 // next row kernel (in range order, so the result is deterministic).
 DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, int N, float* out,
-                         hipStream_t st = nullptr, float* parts = nullptr, int max_ksplit = DG_MAX_KSPLIT) {
+                         hipStream_t st = nullptr, float* parts = nullptr, int max_ksplit = DG_MAX_KSPLIT,
+                         int part_rows = 128) {
   if (!parts) parts = c->parts;
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
   WsArgs a;
@@ -422,7 +429,7 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   a.wide = 1;
   const int nblk = (N + 127) / 128, padded = (nblk + 7) / 8 * 8;
   a.nblk = nblk;
-  a.msplit = std::max(1, (M + 127) / 128);
+  a.msplit = std::max(1, (M + part_rows - 1) / part_rows);
   int ks = 1;
   if (M <= c->parts_rows && N == c->cfg.d_model)
     ks = std::min(max_ksplit, std::max(1, DG_DENSE_BLOCKS / (padded * a.msplit)));
@@ -591,7 +598,7 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     // reduction would only add its partial sums to the combine's reads.  Nothing
     // on the main stream touches c->x between the fork and the join.
     KTS(c, DG_KF_SHARED_DOWN, c->side, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x,
-                                                                c->side, c->parts2, 1));
+                                                                c->side, c->parts2, 1, DG_SHARED_W2_ROWS));
     HIPCK_V(hipEventRecord(c->ev_join, c->side));
     KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
