@@ -349,3 +349,51 @@ def test_full_chunked_prefill_sampled_rows(full_model):
         # layer 1 rows may legitimately differ after a router near-tie in layer 0
         assert all(layer == 1 and gap[i] < 1e-2 for i in bad), (layer, S[bad].tolist(), errs[bad])
     dec.close()
+
+
+def test_full_budget_sampler_and_fp8_steps(full_model):
+    """Whole steps at the full shape with the pages' budget sampler, on the bf16
+    model and on the same model with FP8 routed experts: each step's accept set
+    is the budget rule applied to the GPU's own entropies, argmax canvas and
+    previous argmax canvas; accepted tokens never change; open positions hold
+    their Philox draws."""
+    tw = full_model
+    prompt = synth.make_prompt(W, seed=3)
+    for fmt in ("bf16", "fp8"):
+        if fmt == "fp8":
+            W8 = synth.WORKLOADS["full_fp8"]
+            layers = []
+            for lt in tw["layers"]:
+                l8 = dict(lt)
+                for n in ("w1", "w3", "w2"):
+                    l8[n], l8[n + "_scale"] = synth.quantize_rows_e4m3(lt[n])
+                layers.append(l8)
+            tws, ws = dict(tw, layers=layers), W8
+        else:
+            tws, ws = tw, W
+        dec = make_decoder(ws, tws, max_requests=1, max_ctx=4096 + 512, sampler="budget")
+        dec.dg_prefill(0, prompt, 9)
+        ids = philox.draw_tokens(9, 0, 0, np.arange(256), W.vocab).astype(np.int32)
+        acc = np.zeros(256, bool)
+        prev = None
+        for s in range(3):
+            info = dec.dg_denoise_step()[0]
+            rows = dec.dg_last_step_rows()
+            H, am = rows["entropy"][:256], rows["argmax"][:256]
+            canvas = np.where(acc, ids, am)
+            e, f, stopped = oracle.budget_decide(H, am, acc, canvas, prev, 0.1, 0.005, s + 1, W.max_steps)
+            ids_g, acc_g = dec.dg_get_canvas(0)
+            assert np.array_equal(acc_g, acc | e | f), (fmt, s)
+            assert np.array_equal(ids_g[acc], ids[acc]), (fmt, s, "an accepted token changed")
+            take = e | f
+            assert np.array_equal(ids_g[take], am[take])
+            still = ~acc_g
+            assert np.array_equal(ids_g[still], philox.draw_tokens(9, 0, s + 1, np.nonzero(still)[0], W.vocab))
+            assert info["n_accepted"] == e.sum() and info["n_forced"] == f.sum()
+            log("full %s budget step %d: %d accepted, mean open entropy %.2f" % (fmt, s + 1, e.sum(),
+                                                                                 float(np.mean(H[~acc]))))
+            ids, acc, prev = ids_g, acc_g, canvas
+        dec.close()
+        if fmt == "fp8":
+            del tws, layers
+            torch.cuda.empty_cache()
