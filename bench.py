@@ -49,10 +49,13 @@ def esize(w):
 
 
 def expert_matrix_bytes(w, rows, cols):
-    """Bytes of one routed expert matrix [rows, cols]: the model dtype, or one byte
-    per E4M3 code plus a float32 scale per row."""
+    """Bytes of one routed expert matrix [rows, cols]: the model dtype, one byte
+    per E4M3 code plus a float32 scale per row, or half a byte per E2M1 code plus
+    one E8M0 byte per 32 weights."""
     if w.expert_format == "fp8":
         return rows * cols + 4 * rows
+    if w.expert_format == "mxfp4":
+        return rows * cols // 2 + rows * cols // 32
     return rows * cols * esize(w)
 
 
@@ -93,7 +96,7 @@ def step_flops(w, P, rows, n_open):
 
 
 def measured_traffic(w):
-    """HBM bytes per launch of the dominant kernel (bf16 or FP8 experts, per the
+    """HBM bytes per launch of the dominant kernel (bf16, FP8 or MXFP4 experts, per the
     workload) from the committed rocprofv3 counter summary (FETCH_SIZE +
     WRITE_SIZE, copy-calibrated), or None when the kernel source has changed
     since the counters were taken or the summary has no figure for it."""
@@ -101,8 +104,9 @@ def measured_traffic(w):
     prof = os.path.join(ROOT, "profiles", "ws_hbm_traffic.md")
     src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", "k_ws.hip")
     try:
-        key = "expert_up_fp8_traffic_bytes_per_launch" if w.expert_format == "fp8" else \
-            "expert_up_traffic_bytes_per_launch"
+        key = {"fp8": "expert_up_fp8_traffic_bytes_per_launch",
+               "mxfp4": "expert_up_mxfp4_traffic_bytes_per_launch"}.get(w.expert_format,
+                                                                         "expert_up_traffic_bytes_per_launch")
         fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and l.split(": ", 1)[0]
                       in (key, "k_ws_source_sha256"))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -169,7 +173,8 @@ def describe(w, K):
             "%d, shared hidden %d%s; %d requests x %d-token prompt, %d timed steps (%d canvases of %d)" % (
                 w.name, w.vocab, w.d_model, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_experts,
                 w.top_k, w.expert_hidden, w.shared_hidden,
-                ", routed experts in FP8 E4M3 with row scales" if w.expert_format == "fp8" else "",
+                {"fp8": ", routed experts in FP8 E4M3 with row scales",
+                 "mxfp4": ", routed experts in MXFP4 (E2M1, E8M0 scale per 32 weights)"}.get(w.expert_format, ""),
                 w.n_requests, w.prompt_len, K, max(1, -(-K // C)), C))
 
 
@@ -286,6 +291,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--fp8-steps", type=int, default=256,
                     help="steps timed again with the routed experts in FP8 (full workload only; 0 = skip)")
+    ap.add_argument("--mxfp4-steps", type=int, default=256,
+                    help="steps timed again with the routed experts in MXFP4 (full workload only; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 8 times (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE "
                          "against a kernel of known traffic) and exit")
@@ -343,24 +350,35 @@ def main():
     }
     if w.expert_format == "fp8":
         out["dtype"] = "bf16, fp8 (e4m3) routed-expert weights"
+    elif w.expert_format == "mxfp4":
+        out["dtype"] = "bf16, mxfp4 (e2m1 + e8m0 block scales) routed-expert weights"
     if args.kernel == DOMINANT:
         out["roofline"]["traffic"] = measured_traffic(w)
-    if args.fp8_steps > 0 and w.name == "full":
-        # The same model with its routed experts quantized to E4M3 + row scales
-        # (the pages' FP8 checkpoint, as read here), timed on its own.
-        w8 = synth.WORKLOADS["full_fp8"]
-        log("bench: quantizing the routed experts to FP8")
+    # The same model with its routed experts quantized to E4M3 + row scales (the
+    # pages' FP8 checkpoint, as read here) and to MXFP4, each timed on its own.
+    legs = (("fp8", args.fp8_steps, synth.quantize_rows_e4m3, "_scale"),
+            ("mxfp4", args.mxfp4_steps, synth.quantize_blocks_mxfp4, "_mx_scale"))
+    for fmt, steps, quant, suffix in legs:
+        if steps <= 0 or w.name != "full":
+            continue
+        wq = synth.WORKLOADS["full_" + fmt]
+        log("bench: quantizing the routed experts to %s" % fmt)
+        layers = []
         for lt in tw["layers"]:
+            lq = dict(lt)
             for n in ("w1", "w3", "w2"):
-                lt[n], lt[n + "_scale"] = synth.quantize_rows_e4m3(lt[n])
+                lq[n], lq[n + suffix] = quant(lt[n])
+            layers.append(lq)
+        tq = dict(tw, layers=layers)
         torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        r8 = timed_run(w8, tw, args.fp8_steps, args.warmup, args.kernel, args.seed, log)
+        rq = timed_run(wq, tq, steps, args.warmup, args.kernel, args.seed, log)
         if args.kernel == DOMINANT:
-            r8["roofline"]["traffic"] = measured_traffic(w8)
-        out["fp8_experts"] = {"workload": describe(w8, args.fp8_steps), "steps": args.fp8_steps,
-                              "value": r8["value"], "unit": "tok/s", "ms_per_step": r8["ms_per_step"],
-                              "roofline": r8["roofline"], "step_roofline": r8["step_roofline"]}
+            rq["roofline"]["traffic"] = measured_traffic(wq)
+        out[fmt + "_experts"] = {"workload": describe(wq, steps), "steps": steps,
+                                 "value": rq["value"], "unit": "tok/s", "ms_per_step": rq["ms_per_step"],
+                                 "roofline": rq["roofline"], "step_roofline": rq["step_roofline"]}
+        del tq, layers
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         del tw

@@ -134,14 +134,24 @@ enum {
                           // fp32 [rows][ldo][3] and the argmax to part_arg [rows][ldo] (ldo = vocab / 128)
 };
 
+// Storage of grouped (routed-expert) weights.
+enum {
+  DG_WS_W_BF16 = 0,   // bf16, two bytes per weight
+  DG_WS_W_E4M3 = 1,   // OCP E4M3 codes, one byte per weight, with a float32 scale per weight row
+  DG_WS_W_MXFP4 = 2   // OCP MX FP4 (E2M1) codes, two per byte (lower k in the low nibble), with an
+                      // E8M0 scale per 32 consecutive weights of a row
+};
+
 struct WsArgs {
   const void* A;          // activation rows, bf16, fragment-major with K columns (fm_index)
   const void* W0;         // weight matrices, row-major [rows][K]
   const void* W1;
   const void* W2;
-  int w8;                 // grouped launches: W0 / W1 hold E4M3 codes (one byte per weight) ...
-  const float* wsc0;      // ... with float32 scales per weight row, [groups][N], for W0
-  const float* wsc1;      // and W1
+  int wfmt;               // grouped launches: DG_WS_W_* storage of W0 / W1
+  const float* wsc0;      // DG_WS_W_E4M3: float32 scales per weight row, [groups][N], of W0
+  const float* wsc1;      // and of W1
+  const uint8_t* wbs0;    // DG_WS_W_MXFP4: E8M0 scales per 32 weights, [groups][N][K / 32], of W0
+  const uint8_t* wbs1;    // and of W1
   size_t wgs;             // elements between the matrices of consecutive groups
   int K;                  // reduction length, multiple of 64
   int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it

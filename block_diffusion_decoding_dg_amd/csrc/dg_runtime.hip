@@ -217,9 +217,11 @@ int kc_of(int dtype) { return dtype == DG_BF16 ? 32 : 16; }
 const char* check_config(const dg_model_config* c) {
   if (!c) return "null config";
   if (c->dtype != DG_F32 && c->dtype != DG_BF16) return "dtype must be DG_F32 or DG_BF16";
-  if (c->expert_format != DG_EXPERTS_NATIVE && c->expert_format != DG_EXPERTS_FP8)
-    return "expert_format must be DG_EXPERTS_NATIVE or DG_EXPERTS_FP8";
+  if (c->expert_format != DG_EXPERTS_NATIVE && c->expert_format != DG_EXPERTS_FP8 &&
+      c->expert_format != DG_EXPERTS_MXFP4)
+    return "expert_format must be DG_EXPERTS_NATIVE, DG_EXPERTS_FP8 or DG_EXPERTS_MXFP4";
   if (c->expert_format == DG_EXPERTS_FP8 && c->dtype != DG_BF16) return "FP8 experts need a bf16 model";
+  if (c->expert_format == DG_EXPERTS_MXFP4 && c->dtype != DG_BF16) return "MXFP4 experts need a bf16 model";
   if (c->vocab <= 0 || c->d_model <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
       c->head_dim <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->expert_hidden <= 0 || c->shared_hidden <= 0 ||
       c->max_ctx <= 0 || c->max_requests <= 0)
@@ -452,19 +454,25 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
 }
 
 // Routed launch over the expert work list; with FP8 experts W0 / W1 hold E4M3
-// codes and s0 / s1 their per-row scales ([E][N] each).
+// codes and s0 / s1 their per-row scales ([E][N] each), with MXFP4 experts
+// packed E2M1 codes and b0 / b1 their E8M0 block scales ([E][N][K / 32] each).
 void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void* W1, const float* s0,
-                   const float* s1, size_t wgs, int K, int N, const int32_t* units, const int32_t* n_units, int nblk,
-                   void* out, int ldo, const int32_t* rowsrc = nullptr) {
+                   const float* s1, const uint8_t* b0, const uint8_t* b1, size_t wgs, int K, int N,
+                   const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo,
+                   const int32_t* rowsrc = nullptr) {
   if (c->dtype != DG_BF16) abort();  // bf16-only kernel
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
   a.W0 = W0;
   a.W1 = W1;
-  a.w8 = c->cfg.expert_format == DG_EXPERTS_FP8;
+  a.wfmt = c->cfg.expert_format == DG_EXPERTS_FP8     ? DG_WS_W_E4M3
+           : c->cfg.expert_format == DG_EXPERTS_MXFP4 ? DG_WS_W_MXFP4
+                                                      : DG_WS_W_BF16;
   a.wsc0 = s0;
   a.wsc1 = s1;
+  a.wbs0 = b0;
+  a.wbs1 = b1;
   a.wgs = wgs;
   a.K = K;
   a.N = N;
@@ -609,11 +617,11 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     // row-major normalised rows into c->hbuf (fragment-major, sorted rows), W2
     // from there into c->ybuf at each row's pair index
     KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, w.w1_scale, w.w3_scale,
-                                         (size_t)m.expert_hidden * m.d_model,
+                                         w.w1_mx_scale, w.w3_mx_scale, (size_t)m.expert_hidden * m.d_model,
                                          m.d_model, m.expert_hidden, c->units_up, c->n_units, nb_up, c->hbuf,
                                          m.expert_hidden, c->rowsrc));
     KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, w.w2_scale, nullptr,
-                                           (size_t)m.d_model * m.expert_hidden,
+                                           w.w2_mx_scale, nullptr, (size_t)m.d_model * m.expert_hidden,
                                            m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,
                                            m.d_model));
   }
@@ -728,6 +736,8 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
       if (!p) return fail(nullptr, DG_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
     if (cfg->expert_format == DG_EXPERTS_FP8 && (!w.w1_scale || !w.w3_scale || !w.w2_scale))
       return fail(nullptr, DG_ERR_INVALID_ARG, "null expert scale pointer in layer %d", l);
+    if (cfg->expert_format == DG_EXPERTS_MXFP4 && (!w.w1_mx_scale || !w.w3_mx_scale || !w.w2_mx_scale))
+      return fail(nullptr, DG_ERR_INVALID_ARG, "null expert block-scale pointer in layer %d", l);
   }
   if (!kv_dev || !scratch_dev) return fail(nullptr, DG_ERR_INVALID_ARG, "null kv or scratch buffer");
   dg_model_config m = *cfg;

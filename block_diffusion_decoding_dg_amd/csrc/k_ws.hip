@@ -55,8 +55,9 @@ __device__ __forceinline__ int lds_slot(int row, int seg) {
   return row * (8 * KSUB) + (seg & ~7) + ((seg & 7) ^ (row & 7));
 }
 
-// A thread's share of one weight chunk: N segments of 16 bytes of bf16 (T = uint4)
-// or of the 8 bytes of E4M3 codes they are widened from (T = uint2).
+// A thread's share of one weight chunk: N segments of 16 bytes of bf16 (T = uint4),
+// or the codes they are widened from (T = uint2): 8 bytes of E4M3 codes, or 4
+// bytes of MXFP4 codes (.x) and their E8M0 scale byte (.y).
 template <int N, typename T>
 struct Segs {
   T v[N];
@@ -106,17 +107,35 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
 }
 
+// Eight MXFP4 (E2M1) codes, two per byte with the lower reduction index in the
+// low nibble, widened to bf16 and multiplied by their block's E8M0 scale
+// 2^(sb - 127), passed to the conversion as the float with that exponent field.
+// A two-bit significand times a power of two: exact for scale bytes 1 .. 252
+// (a GPU check over every code byte and byte select matched the exact value
+// rounded to bf16, subnormals included, at scale bytes 1, 2, 120, 127 and 252;
+// from 253 the largest codes overflow bf16; byte 0 reads as a zero scale and
+// 255 as infinity).
+__device__ __forceinline__ uint4 mxfp4x8_to_bf16(uint32_t codes, uint32_t sb) {
+  const float sc = __uint_as_float(sb << 23);
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 // Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue, as a byte
-// address; ES = bytes per weight (2: bf16, 1: E4M3 codes).
-template <int EPI, int NTN, int ES = 2>
+// address; EB = bits per weight (16: bf16, 8: E4M3 codes, 4: MXFP4 codes).
+template <int EPI, int NTN, int EB = 16>
 __device__ __forceinline__ const char* weight_row(const WsArgs& a, int g, int nb, int r) {
   if constexpr (EPI == WS_EPI_SWIGLU) {
     // rows 0 .. 8 NTN - 1: W1 rows, rows 8 NTN .. 16 NTN - 1: W3 rows, of the same
     // 8 NTN hidden columns
     constexpr int HALF = 8 * NTN;
-    const char* W = (const char*)(r < HALF ? a.W0 : a.W1) + (size_t)g * a.wgs * ES;
+    const char* W = (const char*)(r < HALF ? a.W0 : a.W1) + (size_t)g * a.wgs * EB / 8;
     const int n = nb * HALF + (r % HALF);
-    return W + (size_t)min(n, a.N - 1) * a.K * ES;
+    return W + (size_t)min(n, a.N - 1) * a.K * EB / 8;
   } else if constexpr (EPI == WS_EPI_ROPE_QKV) {
     // rows 0..31: columns j0 .. j0+31 of one head's first half, rows 32..63: the
     // matching columns of its second half (RoPE pairs j, j + hd/2)
@@ -129,9 +148,24 @@ __device__ __forceinline__ const char* weight_row(const WsArgs& a, int g, int nb
     else { W = (const bf16_t*)a.W2; hl = head - a.hq - a.hkv; }
     return (const char*)(W + (size_t)(hl * a.hd + j) * a.K);
   } else {
-    const char* W = (const char*)a.W0 + (size_t)g * a.wgs * ES;
+    const char* W = (const char*)a.W0 + (size_t)g * a.wgs * EB / 8;
     const int n = nb * (16 * NTN) + r;
-    return W + (size_t)min(n, a.N - 1) * a.K * ES;
+    return W + (size_t)min(n, a.N - 1) * a.K * EB / 8;
+  }
+}
+
+// E8M0 block scales (K / 32 bytes per weight row) of the MXFP4 weight row that
+// weight_row names, for the grouped epilogues.
+template <int EPI, int NTN>
+__device__ __forceinline__ const uint8_t* scale_row(const WsArgs& a, int g, int nb, int r) {
+  static_assert(EPI == WS_EPI_SWIGLU || EPI == WS_EPI_STORE_F32, "MXFP4 weights: routed experts only");
+  if constexpr (EPI == WS_EPI_SWIGLU) {
+    constexpr int HALF = 8 * NTN;
+    const int n = nb * HALF + (r % HALF);
+    return (r < HALF ? a.wbs0 : a.wbs1) + (size_t)g * (a.wgs / 32) + (size_t)min(n, a.N - 1) * (a.K / 32);
+  } else {
+    const int n = nb * (16 * NTN) + r;
+    return a.wbs0 + (size_t)g * (a.wgs / 32) + (size_t)min(n, a.N - 1) * (a.K / 32);
   }
 }
 
@@ -165,13 +199,15 @@ __device__ __forceinline__ int seg_index(const DgSegs& sg, int r) {
 // load address is clamped to valid memory, so the number of loads in flight is
 // the same in every iteration and the compiler can wait for exactly the load it
 // needs.  All variants execute the same barriers.
-template <int NTN, int KSUB, int MT, int MA, bool GATHER, int RING, bool W8>
+template <int NTN, int KSUB, int MT, int MA, bool GATHER, int RING, int WF>
 __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], const char* const (&gsrc)[NTN * KSUB / 4],
+                                          const uint8_t* const (&gsc)[NTN * KSUB / 4],
                                           const int (&slot)[NTN * KSUB / 4], const int (&sub)[NTN * KSUB / 4],
                                           const char* const (&ap)[MT], int nk64, int lane, v4f (&acc)[MT][NTN]) {
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte LDS segments (8 weights) per thread per chunk
-  using SegT = std::conditional_t<W8, uint2, uint4>;
-  constexpr int SUBB = W8 ? 64 : 128;   // bytes of a weight row per 64-element sub-chunk
+  using SegT = std::conditional_t<WF == DG_WS_W_BF16, uint4, uint2>;
+  // bytes of a weight row per 64-element sub-chunk
+  constexpr int SUBB = WF == DG_WS_W_BF16 ? 128 : WF == DG_WS_W_E4M3 ? 64 : 32;
   static_assert(RING == 4 || RING == 8, "ring of 4 or 8 chunks");
   const int nchunk = (nk64 + KSUB - 1) / KSUB;
   Ring8<NSEG, SegT> R;
@@ -179,10 +215,13 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       const int kc = min(c * KSUB + sub[i], nk64 - 1);
-      S.v[i] = *(const SegT*)(gsrc[i] + kc * SUBB);
+      if constexpr (WF == DG_WS_W_MXFP4)
+        S.v[i] = make_uint2(*(const uint32_t*)(gsrc[i] + kc * SUBB), *(const uint8_t*)(gsc[i] + kc * 2));
+      else S.v[i] = *(const SegT*)(gsrc[i] + kc * SUBB);
     }
   };
-  // Stores chunk c from S into its stage (E4M3 codes widened to bf16 on the way);
+  // Stores chunk c from S into its stage (E4M3 or MXFP4 codes widened to bf16 on
+  // the way; zero codes widen to zeros);
   // sub-chunks past the end store zeros (a mask on the values: a conditional
   // between two lvalues would make the compiler select between their addresses
   // and keep the ring in scratch memory).
@@ -190,7 +229,8 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
       const uint32_t live = c * KSUB + sub[i] < nk64 ? 0xffffffffu : 0u;
-      if constexpr (W8) stage[slot[i]] = e4m3x8_to_bf16(S.v[i].x & live, S.v[i].y & live);
+      if constexpr (WF == DG_WS_W_E4M3) stage[slot[i]] = e4m3x8_to_bf16(S.v[i].x & live, S.v[i].y & live);
+      else if constexpr (WF == DG_WS_W_MXFP4) stage[slot[i]] = mxfp4x8_to_bf16(S.v[i].x & live, S.v[i].y);
       else stage[slot[i]] = make_uint4(S.v[i].x & live, S.v[i].y & live, S.v[i].z & live, S.v[i].w & live);
     }
   };
@@ -266,9 +306,10 @@ __device__ __forceinline__ void ws_stream(uint4 (*sW)[16 * NTN * 8 * KSUB], cons
   }
 }
 
-template <int EPI, int NTN, int KSUB, int MT, bool GATHER, int RING, bool W8 = false>
+template <int EPI, int NTN, int KSUB, int MT, bool GATHER, int RING, int WF = DG_WS_W_BF16>
 __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
-  static_assert(!W8 || EPI == WS_EPI_SWIGLU || EPI == WS_EPI_STORE_F32, "E4M3 weights: routed experts only");
+  static_assert(WF == DG_WS_W_BF16 || EPI == WS_EPI_SWIGLU || EPI == WS_EPI_STORE_F32,
+                "E4M3 / MXFP4 weights: routed experts only");
   constexpr int BN = 16 * NTN;
   constexpr int PASS_ROWS = NWAVE * MT * 16;
   constexpr int NSEG = NTN * KSUB / 4;  // 16-byte segments per thread per chunk
@@ -322,12 +363,16 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
   // tid + NT i -> weight row id / (8 KSUB), segment id % (8 KSUB) within the
   // chunk's KSUB * 128 bytes of that row (sub-chunk segment / 8).
   const char* gsrc[NSEG];
+  const uint8_t* gsc[NSEG];  // MXFP4: the segment's scale byte (a segment is 8 weights of one 32-block)
   int slot[NSEG], sub[NSEG];
 #pragma unroll
   for (int i = 0; i < NSEG; ++i) {
     const int sid = tid + NT * i, wr = sid / (8 * KSUB), sg = sid % (8 * KSUB);
-    if constexpr (W8) gsrc[i] = weight_row<EPI, NTN, 1>(a, g, nb, wr) + kc0 * 64 + (sg & 7) * 8;
+    if constexpr (WF == DG_WS_W_E4M3) gsrc[i] = weight_row<EPI, NTN, 8>(a, g, nb, wr) + kc0 * 64 + (sg & 7) * 8;
+    else if constexpr (WF == DG_WS_W_MXFP4) gsrc[i] = weight_row<EPI, NTN, 4>(a, g, nb, wr) + kc0 * 32 + (sg & 7) * 4;
     else gsrc[i] = weight_row<EPI, NTN>(a, g, nb, wr) + kc0 * 128 + (sg & 7) * 16;
+    if constexpr (WF == DG_WS_W_MXFP4) gsc[i] = scale_row<EPI, NTN>(a, g, nb, wr) + kc0 * 2 + (sg & 7) / 4;
+    else gsc[i] = nullptr;
     slot[i] = lds_slot<KSUB>(wr, sg);
     sub[i] = sg >> 3;
   }
@@ -361,10 +406,10 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
       for (int n = 0; n < NTN; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER, RING, W8>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+    if (mt_act == 0) ws_stream<NTN, KSUB, MT, 0, GATHER, RING, WF>(sW, gsrc, gsc, slot, sub, ap, nk64, lane, acc);
     else if (MT == 1 || mt_act == 1)
-      ws_stream<NTN, KSUB, MT, 1, GATHER, RING, W8>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
-    else ws_stream<NTN, KSUB, MT, MT, GATHER, RING, W8>(sW, gsrc, slot, sub, ap, nk64, lane, acc);
+      ws_stream<NTN, KSUB, MT, 1, GATHER, RING, WF>(sW, gsrc, gsc, slot, sub, ap, nk64, lane, acc);
+    else ws_stream<NTN, KSUB, MT, MT, GATHER, RING, WF>(sW, gsrc, gsc, slot, sub, ap, nk64, lane, acc);
 
     // Epilogue.
     if constexpr (EPI == WS_EPI_LM_STATS) {
@@ -433,7 +478,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
               const int col = nb * (8 * NTN) + n * 16 + (lane & 15);
               if (col >= a.N) continue;
               float u = acc[j][n][i], v = acc[j][n + NTN / 2][i];
-              if constexpr (W8) {  // row scales of the W1 and W3 codes
+              if constexpr (WF == DG_WS_W_E4M3) {  // row scales of the W1 and W3 codes
                 u *= a.wsc0[(size_t)g * a.N + col];
                 v *= a.wsc1[(size_t)g * a.N + col];
               }
@@ -483,7 +528,8 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
               const size_t o = (size_t)orow * a.ldo + col;
               if constexpr (EPI == WS_EPI_STORE_BF16) ((bf16_t*)a.out)[o] = f2bf(acc[j][n][i]);
               else if constexpr (EPI == WS_EPI_STORE_F32)
-                ((float*)a.out)[o] = W8 ? acc[j][n][i] * a.wsc0[(size_t)g * a.N + col] : acc[j][n][i];
+                ((float*)a.out)[o] =
+                    WF == DG_WS_W_E4M3 ? acc[j][n][i] * a.wsc0[(size_t)g * a.N + col] : acc[j][n][i];
               else if (a.ksplit > 1) a.part_out[(size_t)ks * a.part_stride + o] = acc[j][n][i];  // partial sum
               else ((float*)a.out)[o] += acc[j][n][i];
             }
@@ -540,24 +586,32 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 #define DG_WS_RING_ROUTED 4
 #endif
 // E4M3 weights: a ring of 8 (the same bytes in flight as bf16's 4) needs more
-// registers than two blocks per CU allow and measured slower.
+// registers than two blocks per CU allow and measured slower.  MXFP4 keeps 4 too.
 #ifndef DG_WS_RING_FP8
 #define DG_WS_RING_FP8 4
 #endif
+#ifndef DG_WS_RING_FP4
+#define DG_WS_RING_FP4 4
+#endif
 void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
-  constexpr int RD = DG_WS_RING_DENSE, RR = DG_WS_RING_ROUTED, R8 = DG_WS_RING_FP8;
+  constexpr int RD = DG_WS_RING_DENSE, RR = DG_WS_RING_ROUTED, R8 = DG_WS_RING_FP8, R4 = DG_WS_RING_FP4;
+  constexpr int E8 = DG_WS_W_E4M3, F4 = DG_WS_W_MXFP4;
   if (a.counts) {  // grouped (routed experts)
+    if (a.wfmt != DG_WS_W_BF16 && a.wfmt != E8 && a.wfmt != F4) abort();
+    if (a.wfmt == F4 && a.K % 64) abort();  // whole 32-blocks per 64-element sub-chunk
     if (a.rowsrc && epi == WS_EPI_SWIGLU) {
-      if (a.w8) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, R8, true><<<grid, NT, 0, s>>>(a);
+      if (a.wfmt == E8) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, R8, E8><<<grid, NT, 0, s>>>(a);
+      else if (a.wfmt == F4) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, R4, F4><<<grid, NT, 0, s>>>(a);
       else k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, RR><<<grid, NT, 0, s>>>(a);
     } else if (!a.rowsrc && epi == WS_EPI_STORE_F32) {
-      if (a.w8) k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, R8, true><<<grid, NT, 0, s>>>(a);
+      if (a.wfmt == E8) k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, R8, E8><<<grid, NT, 0, s>>>(a);
+      else if (a.wfmt == F4) k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, R4, F4><<<grid, NT, 0, s>>>(a);
       else k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RR><<<grid, NT, 0, s>>>(a);
     } else abort();
     return;
   }
-  if (a.w8) abort();  // E4M3 weights: routed experts only
+  if (a.wfmt != DG_WS_W_BF16) abort();  // E4M3 / MXFP4 weights: routed experts only
   switch (epi) {
     case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;

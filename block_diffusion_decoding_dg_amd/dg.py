@@ -50,9 +50,10 @@ class SamplerConfig(ctypes.Structure):
 
 
 _LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router", "w1", "w3", "w2", "sw1", "sw3", "sw2",
-                 "w1_scale", "w3_scale", "w2_scale")
-_SCALE_FIELDS = ("w1_scale", "w3_scale", "w2_scale")
-DG_EXPERTS_NATIVE, DG_EXPERTS_FP8 = 0, 1
+                 "w1_scale", "w3_scale", "w2_scale", "w1_mx_scale", "w3_mx_scale", "w2_mx_scale")
+_SCALE_FIELDS = ("w1_scale", "w3_scale", "w2_scale", "w1_mx_scale", "w3_mx_scale", "w2_mx_scale")
+DG_EXPERTS_NATIVE, DG_EXPERTS_FP8, DG_EXPERTS_MXFP4 = 0, 1, 2
+EXPERT_FORMATS = {"native": DG_EXPERTS_NATIVE, "fp8": DG_EXPERTS_FP8, "mxfp4": DG_EXPERTS_MXFP4}
 
 
 class LayerWeights(ctypes.Structure):
@@ -151,7 +152,7 @@ def model_config(w, max_requests=None, max_ctx=None, prefill_chunk=0):
                        max_ctx=w.max_ctx if max_ctx is None else max_ctx,
                        max_requests=w.n_requests if max_requests is None else max_requests,
                        prefill_chunk=prefill_chunk, rope_theta=w.rope_theta, rms_eps=w.rms_eps, dtype=dtype,
-                       expert_format=DG_EXPERTS_FP8 if w.expert_format == "fp8" else DG_EXPERTS_NATIVE)
+                       expert_format=EXPERT_FORMATS[w.expert_format])
 
 
 def dg_workspace_size(cfg):
@@ -189,7 +190,7 @@ class Decoder:
         for l, lt in enumerate(weights["layers"]):
             for n in _LAYER_FIELDS:
                 if n in _SCALE_FIELDS and n not in lt:
-                    continue  # bf16 experts: no scales
+                    continue  # scales of another expert format
                 setattr(self._layers[l], n, lt[n].data_ptr())
         self._w = Weights(embed=weights["embed"].data_ptr(), final_norm=weights["final_norm"].data_ptr(),
                           layers=self._layers)

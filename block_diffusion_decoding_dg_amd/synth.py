@@ -106,6 +106,9 @@ WORKLOADS = {
 # The mid-size and full-size shapes with FP8 (E4M3) routed experts.
 WORKLOADS["mid_fp8"] = replace(WORKLOADS["mid"], name="mid_fp8", expert_format="fp8")
 WORKLOADS["full_fp8"] = replace(WORKLOADS["full"], name="full_fp8", expert_format="fp8")
+# ... and with MXFP4 (E2M1 + E8M0 block scales) routed experts.
+WORKLOADS["mid_mxfp4"] = replace(WORKLOADS["mid"], name="mid_mxfp4", expert_format="mxfp4")
+WORKLOADS["full_mxfp4"] = replace(WORKLOADS["full"], name="full_mxfp4", expert_format="mxfp4")
 
 LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router",
                  "w1", "w3", "w2", "sw1", "sw3", "sw2")
@@ -161,6 +164,9 @@ def make_weights(w: Workload, seed: int = 0, device="cpu", layers: Optional[List
         if w.expert_format == "fp8":
             for name in ("w1", "w3", "w2"):
                 lt[name], lt[name + "_scale"] = quantize_rows_e4m3(lt[name])
+        elif w.expert_format == "mxfp4":
+            for name in ("w1", "w3", "w2"):
+                lt[name], lt[name + "_mx_scale"] = quantize_blocks_mxfp4(lt[name])
         out["layers"].append(lt)
     return out
 
@@ -175,6 +181,37 @@ def quantize_rows_e4m3(w: torch.Tensor):
     scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
     codes = (wf / scale[..., None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes.contiguous(), scale.contiguous()
+
+
+# E2M1 magnitudes by code (index = code & 7) and the midpoints between neighbours.
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def quantize_blocks_mxfp4(w: torch.Tensor):
+    """Stand-in for an MXFP4 checkpoint of a weight tensor [..., out, in] (in a
+    multiple of 32), following the OCP MX conversion: per block of 32 weights of
+    a row the shared exponent X = floor(log2 max|w|) - 2 (2 = E2M1's largest
+    exponent; X = 0 for an all-zero block, clamped to [-126, 127]), scale byte
+    X + 127, and the E2M1 codes of w / 2^X rounded to nearest, ties to the even
+    code, saturating at 6.  Returns (packed codes uint8 [..., out, in / 2], lower
+    index in the low nibble; scale bytes uint8 [..., out, in / 32])."""
+    wf = w.float()
+    shape = wf.shape
+    blocks = wf.reshape(*shape[:-1], shape[-1] // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)  # amax = f * 2^e with f in [0.5, 1): floor(log2 amax) = e - 1
+    x = torch.where(amax > 0, e - 3, torch.zeros_like(e)).clamp_(-126, 127)
+    y = blocks / torch.ldexp(torch.ones_like(amax), x)[..., None]  # exact: a power of two
+    a = y.abs()
+    idx = torch.zeros(a.shape, dtype=torch.uint8, device=a.device)
+    for j, m in enumerate(_E2M1_MIDS):
+        # at a midpoint the tie goes to the even neighbour: up when the lower one is odd
+        idx += ((a > m) | ((a == m) & (j % 2 == 1))).to(torch.uint8)
+    del a
+    code = (idx | ((y < 0).to(torch.uint8) << 3)).reshape(shape)
+    del idx, y
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), (x + 127).to(torch.uint8).contiguous()
 
 
 def make_prompt(w: Workload, seed: int = 0, length: Optional[int] = None):

@@ -68,8 +68,26 @@ typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  *     codes to bf16 (exact) and apply the scale to the fp32 row sum.  bf16
  *     models only (DG_ERR_INVALID_ARG otherwise).  Code arrays must not hold
  *     NaN codes.
+ *   DG_EXPERTS_MXFP4: the OCP Microscaling (MX) FP4 format: E2M1 codes (sign,
+ *     two exponent bits with bias 1, one mantissa bit; magnitudes 0, 0.5, 1,
+ *     1.5, 2, 3, 4, 6), two per byte with the lower reduction index k in the
+ *     low nibble, plus one E8M0 scale byte per 32 consecutive weights of a row
+ *     (dg_layer_weights.w1_mx_scale, ...):
+ *     W[e][n][k] = 2^(s[e][n][k / 32] - 127) * e2m1(code of k).  The kernels
+ *     widen the codes to bf16 times the block scale (exact).  bf16 models
+ *     only; the reduction length of each matrix (d_model for w1 / w3,
+ *     expert_hidden for w2) is a multiple of 64, as for every format.  Scale
+ *     bytes must lie in 1 .. 252 (2^-126 .. 2^125, where every code times the
+ *     scale is a bf16 value): byte 0 (2^-127) reads as a zero scale, 253 and
+ *     254 overflow bf16 for the largest codes and 255 (NaN) is not implemented.
+ *   The pages also name NVFP4 checkpoints; MXFP4 is CDNA4's native 4-bit
+ *   format and the one built.
  */
-typedef enum dg_expert_format { DG_EXPERTS_NATIVE = 0, DG_EXPERTS_FP8 = 1 } dg_expert_format;
+typedef enum dg_expert_format {
+  DG_EXPERTS_NATIVE = 0,
+  DG_EXPERTS_FP8 = 1,
+  DG_EXPERTS_MXFP4 = 2
+} dg_expert_format;
 
 /*
  * Model shape.  Pre-norm decoder blocks: RMSNorm (gain per channel, eps under
@@ -151,12 +169,16 @@ typedef struct dg_sampler_config {
  *   router [E, d]; w1, w3 [E, eh, d]; w2 [E, d, eh]; sw1, sw3 [sh, d]; sw2 [d, sh].
  * With expert_format DG_EXPERTS_FP8, w1, w3 and w2 hold E4M3 codes (uint8, same
  * shapes) and w1_scale, w3_scale [E, eh] and w2_scale [E, d] their float32 row
- * scales; otherwise the scale pointers are ignored.
+ * scales.  With DG_EXPERTS_MXFP4 they hold packed E2M1 codes (uint8 [E, eh, d/2]
+ * and [E, d, eh/2]) and w1_mx_scale, w3_mx_scale [E, eh, d/32] and w2_mx_scale
+ * [E, d, eh/32] their E8M0 block scales.  Scale pointers of the other formats
+ * are ignored.
  */
 typedef struct dg_layer_weights {
   const void *attn_norm, *wq, *wk, *wv, *wo;
   const void *ffn_norm, *router, *w1, *w3, *w2, *sw1, *sw3, *sw2;
   const float *w1_scale, *w3_scale, *w2_scale;
+  const uint8_t *w1_mx_scale, *w3_mx_scale, *w2_mx_scale;
 } dg_layer_weights;
 
 typedef struct dg_weights {

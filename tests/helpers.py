@@ -26,6 +26,9 @@ def oracle_weights(w: synth.Workload, tw) -> oracle.Weights:
         if "w1_scale" in lt:   # FP8 experts: the oracle's own decoding of the codes
             for n in ("w1", "w3", "w2"):
                 d[n] = oracle.dequantize_rows(lt[n].cpu().numpy(), lt[n + "_scale"].cpu().numpy())
+        if "w1_mx_scale" in lt:   # MXFP4 experts: likewise
+            for n in ("w1", "w3", "w2"):
+                d[n] = oracle.dequantize_mxfp4(lt[n].cpu().numpy(), lt[n + "_mx_scale"].cpu().numpy())
         layers.append(oracle.LayerWeights(**d))
     return oracle.Weights(embed=to_f64(tw["embed"]), final_norm=to_f64(tw["final_norm"]),
                           layers=layers)

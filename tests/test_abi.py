@@ -52,7 +52,9 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("bad", [dict(canvas_len=128), dict(head_dim=24), dict(vocab=500), dict(max_ctx=300),
                                  dict(n_q_heads=3), dict(top_k=17), dict(max_requests=17), dict(dtype=7),
-                                 dict(d_model=0), dict(expert_hidden=100), dict(n_experts=300)])
+                                 dict(d_model=0), dict(expert_hidden=100), dict(n_experts=300),
+                                 # quantized experts need a bf16 model; 3 is no format
+                                 dict(expert_format=1), dict(expert_format=2), dict(expert_format=3)])
 def test_bad_configs_rejected(bad):
     with pytest.raises(dg.DgError) as e:
         dg.dg_workspace_size(_cfg(**bad))

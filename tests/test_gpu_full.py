@@ -170,6 +170,45 @@ def test_full_moe_op_fp8(layer0, t, skew):
     dec.close()
 
 
+@pytest.mark.parametrize("t,skew", [(256, 0.0), (256, 4.0), (2048, 4.0)])
+def test_full_moe_op_mxfp4(layer0, t, skew):
+    """MoE half with MXFP4 (E2M1 codes, E8M0 scale per 32 weights) routed
+    experts: layer 0's experts quantized; the oracle decodes the same codes."""
+    tw, cfg, lw, _, _, prec = layer0
+    W4 = synth.WORKLOADS["full_mxfp4"]
+    l4 = dict(tw["layers"][0])
+    for n in ("w1", "w3", "w2"):
+        l4[n], l4[n + "_mx_scale"] = synth.quantize_blocks_mxfp4(tw["layers"][0][n])
+    tw4 = dict(tw, layers=[l4] * W.n_layers)
+    lw4 = oracle.LayerWeights(**{**lw.__dict__, **{n: oracle.dequantize_mxfp4(l4[n].cpu().numpy(),
+                                                                              l4[n + "_mx_scale"].cpu().numpy())
+                                                    for n in ("w1", "w3", "w2")}})
+    dec = make_decoder(W4, tw4, max_requests=t // 256)
+    x = synth.make_normal((t, W.d_model), seed=t + int(skew), std=1.0, device="cuda")
+    if skew:
+        x = x + skew * synth.make_normal((1, W.d_model), seed=99, std=1.0, device="cuda")
+    xg = x.contiguous().clone()
+    ids = torch.empty((t, W.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((t, W.top_k), dtype=torch.float32, device="cuda")
+    log("full mxfp4 moe t=%d skew %.0f" % (t, skew))
+    dec.dg_op_moe(0, xg, ids, gates)
+    xo = x.cpu().numpy().astype(np.float64)
+    b = oracle.round_bf16(oracle.rmsnorm(xo, lw4.ffn_norm, cfg.rms_eps))
+    f, r, oids, ogates = oracle.moe(b, lw4, cfg, prec)
+    tr = oracle.model.LayerTrace(router_logits=r, ids=oids, gates=ogates)
+    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 2e-2)
+    keep = np.setdiff1d(np.arange(t), flips)
+    got = xg.cpu().numpy().astype(np.float64)
+    worst = max(rel_l2(got[i] - xo[i], f[i]) for i in keep)
+    # the quantized experts differ from the bf16 ones by the E2M1 rounding
+    fb, _, _, _ = oracle.moe(b[:8], lw, cfg, prec)
+    qerr = max(rel_l2(f[i], fb[i]) for i in range(8))
+    log("full mxfp4 moe t=%d skew %.0f: %d router flips, worst rel L2 %.2e (mxfp4 vs bf16 model: %.2e)"
+        % (t, skew, len(flips), worst, qerr))
+    assert worst <= RL2 and qerr > 4 * worst
+    dec.close()
+
+
 def test_full_lm_head_op(layer0):
     tw, cfg, _, embed, fnorm, prec = layer0
     dec = make_decoder(W, tw)
@@ -351,24 +390,25 @@ def test_full_chunked_prefill_sampled_rows(full_model):
     dec.close()
 
 
-def test_full_budget_sampler_and_fp8_steps(full_model):
+def test_full_budget_sampler_and_quantized_steps(full_model):
     """Whole steps at the full shape with the pages' budget sampler, on the bf16
-    model and on the same model with FP8 routed experts: each step's accept set
+    model and on the same model with FP8 or MXFP4 routed experts: each step's accept set
     is the budget rule applied to the GPU's own entropies, argmax canvas and
     previous argmax canvas; accepted tokens never change; open positions hold
     their Philox draws."""
     tw = full_model
     prompt = synth.make_prompt(W, seed=3)
-    for fmt in ("bf16", "fp8"):
-        if fmt == "fp8":
-            W8 = synth.WORKLOADS["full_fp8"]
+    for fmt in ("bf16", "fp8", "mxfp4"):
+        if fmt != "bf16":
+            quant = synth.quantize_rows_e4m3 if fmt == "fp8" else synth.quantize_blocks_mxfp4
+            suffix = "_scale" if fmt == "fp8" else "_mx_scale"
             layers = []
             for lt in tw["layers"]:
-                l8 = dict(lt)
+                lq = dict(lt)
                 for n in ("w1", "w3", "w2"):
-                    l8[n], l8[n + "_scale"] = synth.quantize_rows_e4m3(lt[n])
-                layers.append(l8)
-            tws, ws = dict(tw, layers=layers), W8
+                    lq[n], lq[n + suffix] = quant(lt[n])
+                layers.append(lq)
+            tws, ws = dict(tw, layers=layers), synth.WORKLOADS["full_" + fmt]
         else:
             tws, ws = tw, W
         dec = make_decoder(ws, tws, max_requests=1, max_ctx=4096 + 512, sampler="budget")
@@ -394,6 +434,6 @@ def test_full_budget_sampler_and_fp8_steps(full_model):
                                                                                  float(np.mean(H[~acc]))))
             ids, acc, prev = ids_g, acc_g, canvas
         dec.close()
-        if fmt == "fp8":
+        if fmt != "bf16":
             del tws, layers
             torch.cuda.empty_cache()

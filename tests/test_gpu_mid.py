@@ -49,11 +49,11 @@ def _logit_tol(g, o):
         assert e <= LOGIT_RL2, ("logits rel L2", i, e)
 
 
-@pytest.fixture(scope="module", params=["mid", "mid_fp8"])
+@pytest.fixture(scope="module", params=["mid", "mid_fp8", "mid_mxfp4"])
 def setup(request):
     """The mid-size model with bf16 routed experts, and the same model with its
-    routed experts quantized to FP8 (E4M3 codes + row scales; the oracle decodes
-    the codes itself)."""
+    routed experts quantized to FP8 (E4M3 codes + row scales) or to MXFP4 (E2M1
+    codes + E8M0 scales per 32 weights); the oracle decodes the codes itself."""
     w = synth.WORKLOADS[request.param]
     log("%s: generating weights on the GPU" % w.name)
     tw_gpu = synth.make_weights(w, seed=0, device="cuda")

@@ -661,3 +661,110 @@ def test_dequantize_rows_scales_each_output_row():
     x = rng.standard_normal(7)
     # a row scale commutes with the reduction (the kernel applies it after the sum)
     assert np.allclose(w[1] @ x, s[1].astype(np.float64) * (oracle.decode_e4m3(codes[1]) @ x), rtol=1e-14)
+
+
+# ---------------------------------------------------- MXFP4 expert weights ----
+
+def _minifloat(code, e_bits, m_bits, bias):
+    """Generic sign / exponent / mantissa decoding (IEEE-style, subnormals at
+    exponent 0, no special values), written once for any field widths; checked
+    against torch's E4M3 below, then evaluated at E2M1's widths."""
+    s = (code >> (e_bits + m_bits)) & 1
+    e = (code >> m_bits) & ((1 << e_bits) - 1)
+    m = code & ((1 << m_bits) - 1)
+    from fractions import Fraction
+    frac = Fraction(m, 1 << m_bits)
+    v = (frac if e == 0 else 1 + frac) * Fraction(2) ** ((1 if e == 0 else e) - bias)
+    return float(-v if s else v)
+
+
+def test_generic_minifloat_reproduces_torch_e4m3():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue                                             # E4M3's NaN codes
+        assert _minifloat(c, 4, 3, 7) == ref[c], c
+
+
+def test_e2m1_decode_matches_generic_minifloat_on_every_code():
+    got = oracle.decode_e2m1(np.arange(16))
+    ref = np.array([_minifloat(c, 2, 1, 1) for c in range(16)])
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.arange(16) >= 8)  # -0.0 at code 8
+
+
+def test_e2m1_closed_forms():
+    d = oracle.decode_e2m1
+    assert d(1) == 0.5                                           # the only subnormal: half the smallest normal
+    assert d(2) == 1.0                                           # exponent field 1 = bias
+    assert d(7) == oracle.E2M1_MAX == 6.0                        # 2^2 * 1.5
+    assert d(15) == -6.0 and d(9) == -0.5
+    mags = d(np.arange(8))
+    assert np.all(np.diff(mags) > 0) and len(set(mags)) == 8
+    assert np.array_equal(d(np.arange(8) | 8), -mags)
+    # every E2M1 value is an E4M3 value (torch round-trips it exactly)
+    assert np.array_equal(torch.tensor(mags).to(torch.float8_e4m3fn).double().numpy(), mags)
+    with pytest.raises(ValueError):
+        d(16)
+
+
+def test_e8m0_decode_matches_torch_on_every_byte():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = oracle.decode_e8m0(b)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[128] == 2.0 and got[126] == 0.5
+
+
+def test_unpack_fp4_low_nibble_first():
+    assert oracle.unpack_fp4(np.array([[0x21, 0xF0]], dtype=np.uint8)).tolist() == [[1, 2, 0, 15]]
+
+
+def test_dequantize_mxfp4_scales_each_block_of_32():
+    rng = np.random.default_rng(43)
+    packed = rng.integers(0, 256, (2, 3, 48)).astype(np.uint8)   # K = 96: three blocks per row
+    sb = rng.integers(100, 140, (2, 3, 3)).astype(np.uint8)
+    w = oracle.dequantize_mxfp4(packed, sb)
+    assert w.shape == (2, 3, 96)
+    vals = oracle.decode_e2m1(oracle.unpack_fp4(packed))
+    for e in range(2):
+        for n in range(3):
+            for b in range(3):
+                sc = torch.tensor([int(sb[e, n, b])], dtype=torch.uint8).view(torch.float8_e8m0fnu).double().item()
+                assert np.array_equal(w[e, n, 32 * b:32 * b + 32], sc * vals[e, n, 32 * b:32 * b + 32])
+    # one scale byte up by one doubles exactly its own 32 weights
+    sb2 = sb.copy()
+    sb2[1, 2, 1] += 1
+    w2 = oracle.dequantize_mxfp4(packed, sb2)
+    diff = w2 != w
+    assert np.array_equal(w2[1, 2, 32:64], 2 * w[1, 2, 32:64])
+    diff[1, 2, 32:64] = False
+    assert not diff.any()
+    with pytest.raises(ValueError):
+        oracle.dequantize_mxfp4(packed, sb[..., :2])
+
+
+def test_mxfp4_stand_in_quantizer_rounds_to_nearest_even():
+    # scale byte from the block maximum; values on the grid, at midpoints and past 6
+    row = np.zeros(64, dtype=np.float32)
+    row[:10] = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.9, -0.74]   # block max 7.9: X = 2 - 2 = 0
+    row[32:36] = [0.5, -0.125, 0.21875, 0.0]                            # block max 0.5: X = -1 - 2 = -3
+    packed, sb = synth.quantize_blocks_mxfp4(torch.from_numpy(row).reshape(1, 64))
+    assert sb.tolist() == [[127, 124]]
+    w = oracle.dequantize_mxfp4(packed.numpy(), sb.numpy())[0]
+    # ties: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4; 7.9 saturates at 6
+    assert w[:10].tolist() == [4.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, -0.5]
+    assert w[10:32].tolist() == [0.0] * 22
+    assert w[32:36].tolist() == [0.5, -0.125, 0.25, 0.0]               # 1.75 * 2^-3 ties up to 2 * 2^-3
+    # random bf16 weights: error within half a grid step, or the saturation at 6 scales
+    wt = (torch.randn(4, 8, 256, generator=torch.Generator().manual_seed(5)) * 0.02).to(torch.bfloat16)
+    p, s = synth.quantize_blocks_mxfp4(wt)
+    deq = oracle.dequantize_mxfp4(p.numpy(), s.numpy())
+    ref = wt.float().numpy().astype(np.float64)
+    sc = np.repeat(oracle.decode_e8m0(s.numpy()), 32, axis=-1)
+    y = np.abs(ref) / sc
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    err = np.abs(deq - ref) / sc
+    assert np.all((err <= step / 2) | ((y > 6) & (np.abs(deq) / sc == 6)))
