@@ -47,6 +47,7 @@ class Workload:
     rms_eps: float = 1e-6
     init_std: float = 0.02
     expert_format: str = "native"   # or "fp8": routed experts as E4M3 codes + row scales
+    self_cond_hidden: int = 0       # width of the self-conditioning MLP (0: none)
 
     @property
     def n_blocks(self):
@@ -58,7 +59,8 @@ class Workload:
 
     def model_dict(self):
         keys = ("vocab", "d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "n_experts",
-                "top_k", "expert_hidden", "shared_hidden", "canvas_len", "rope_theta", "rms_eps")
+                "top_k", "expert_hidden", "shared_hidden", "canvas_len", "rope_theta", "rms_eps",
+                "self_cond_hidden")
         return {k: getattr(self, k) for k in keys}
 
     def param_count(self):
@@ -109,6 +111,9 @@ WORKLOADS["full_fp8"] = replace(WORKLOADS["full"], name="full_fp8", expert_forma
 # ... and with MXFP4 (E2M1 + E8M0 block scales) routed experts.
 WORKLOADS["mid_mxfp4"] = replace(WORKLOADS["mid"], name="mid_mxfp4", expert_format="mxfp4")
 WORKLOADS["full_mxfp4"] = replace(WORKLOADS["full"], name="full_mxfp4", expert_format="mxfp4")
+# ... and with self-conditioning through a gated MLP of width 256.
+WORKLOADS["mid_sc"] = replace(WORKLOADS["mid"], name="mid_sc", self_cond_hidden=256)
+WORKLOADS["full_sc"] = replace(WORKLOADS["full"], name="full_sc", self_cond_hidden=256)
 
 LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "router",
                  "w1", "w3", "w2", "sw1", "sw3", "sw2")
@@ -168,6 +173,10 @@ def make_weights(w: Workload, seed: int = 0, device="cpu", layers: Optional[List
             for name in ("w1", "w3", "w2"):
                 lt[name], lt[name + "_mx_scale"] = quantize_blocks_mxfp4(lt[name])
         out["layers"].append(lt)
+    if w.self_cond_hidden > 0:
+        m, d = w.self_cond_hidden, w.d_model
+        for i, (name, shape) in enumerate((("sc_w1", (m, d)), ("sc_w3", (m, d)), ("sc_w2", (d, m)))):
+            out[name] = _normal(shape, w.init_std, seed, 1 + w.n_layers * 64 + i, device, dt)
     return out
 
 

@@ -16,7 +16,8 @@ Logit values of a whole random-weight model have no printed worked example in
 the pages: beyond those pins they are "parity unpinned".
 """
 from .model import (ModelConfig, LayerWeights, Weights, Precision, round_bf16, rmsnorm, rope,
-                    attention, silu, topk_select, route, moe, layer_forward, lm_head_stats)
+                    attention, silu, topk_select, route, moe, layer_forward, lm_head_stats,
+                    self_cond_input, self_cond_embedding)
 from .philox import philox4x64_10, draw_tokens
 from .quant import (decode_e4m3, dequantize_rows, E4M3_MAX, decode_e2m1, decode_e8m0, unpack_fp4,
                     dequantize_mxfp4, MX_BLOCK, E2M1_MAX)

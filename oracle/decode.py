@@ -47,7 +47,8 @@ from typing import List, Optional
 
 import numpy as np
 
-from .model import (ModelConfig, Weights, Precision, layer_forward, lm_head_stats)
+from .model import (ModelConfig, Weights, Precision, layer_forward, lm_head_stats, self_cond_input,
+                    self_cond_embedding)
 from .philox import draw_tokens
 
 
@@ -73,6 +74,7 @@ class RequestState:
     ids: Optional[np.ndarray] = None       # [C] int64 canvas token ids
     accepted: Optional[np.ndarray] = None  # [C] bool
     prev_argmax: Optional[np.ndarray] = None  # [C] argmax canvas of the previous step of this block
+    sc_state: Optional[np.ndarray] = None     # [C, d] self-conditioning state (cfg.self_cond_hidden > 0)
 
 
 @dataclass
@@ -136,6 +138,7 @@ def start_canvas(st: RequestState, cfg: ModelConfig):
     st.ids = draw_tokens(st.seed, st.block, 0, np.arange(c), cfg.vocab)
     st.accepted = np.zeros(c, dtype=bool)
     st.prev_argmax = None
+    st.sc_state = np.zeros((c, cfg.d_model)) if cfg.self_cond_hidden > 0 else None
     st.step = 0
     st.active = True
 
@@ -148,6 +151,8 @@ def canvas_forward(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precisi
     if P + c > st.max_ctx:
         raise ValueError("canvas does not fit in max_ctx")
     x = w.embed[st.ids]
+    if cfg.self_cond_hidden > 0:
+        x = x + self_cond_embedding(st.sc_state, w, prec)
     pos = P + np.arange(c)
     traces = []
     for l, lw in enumerate(w.layers):
@@ -228,7 +233,13 @@ def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Wei
     if not st.active:
         start_canvas(st, cfg)
     x, traces = canvas_forward(st, cfg, w, prec)
-    stats = lm_head_stats(x, w.embed, w.final_norm, cfg, prec, keep_logits=keep_logits)
+    sc = cfg.self_cond_hidden > 0
+    stats = lm_head_stats(x, w.embed, w.final_norm, cfg, prec, keep_logits=keep_logits or sc)
+    if sc:
+        # positions open at the start of the step take this step's softmax
+        open_ = ~st.accepted
+        st.sc_state = st.sc_state.copy()
+        st.sc_state[open_] = self_cond_input(stats["logits"][open_], stats["lse"][open_], w.embed, prec)
     s = st.step + 1
     ids_before = st.ids.copy()
     acc_before = st.accepted.copy()
@@ -258,7 +269,7 @@ def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Wei
                       ids_before=ids_before, accepted_before=acc_before,
                       ids_after=ids.copy(), accepted_after=accepted.copy(),
                       n_open=n_open, done=(n_open == 0), layers=traces,
-                      logits=stats.get("logits"), hidden=x, stopped=stopped)
+                      logits=stats.get("logits") if keep_logits else None, hidden=x, stopped=stopped)
 
 
 def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision, keep_traces=False):
@@ -278,6 +289,7 @@ def commit_block(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precision
     st.ids = None
     st.accepted = None
     st.prev_argmax = None
+    st.sc_state = None
     return (out, traces) if keep_traces else out
 
 

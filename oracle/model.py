@@ -19,7 +19,14 @@ below is the plainest reading, listed with the rest in the design notes:
 * router logits r = b Wg^T; the k largest (ties to the lower expert id) are
   kept and their gates are the softmax over those k logits; the shared expert
   is added with weight 1; each expert is the SwiGLU FFN W2 (silu(W1 b) * W3 b);
-* embedding without scaling; the LM head is the embedding matrix (tied).
+* embedding without scaling; the LM head is the embedding matrix (tied);
+* self-conditioning (optional; "DiffusionGemma hits ~1,500 TPS on one H100",
+  section "How the sampler actually works", says only that the previous
+  step's softmax goes back in through a small gated MLP): every canvas
+  position keeps the expectation u = sum_v p_v E_v of the embedding under its
+  softmax from the last step at which it was open (zero when the canvas
+  starts), and each forward over the canvas adds W2 (silu(W1 u) * W3 u) to the
+  token's embedding.
 
 Arithmetic: float64 everywhere.  `Precision.bf16_points` optionally rounds
 the operands that the bf16 GPU path feeds to its matrix cores (normalised
@@ -49,6 +56,7 @@ class ModelConfig:
     canvas_len: int = 256
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
+    self_cond_hidden: int = 0   # width of the self-conditioning MLP; 0 = no self-conditioning
 
 
 @dataclass
@@ -73,6 +81,9 @@ class Weights:
     embed: np.ndarray       # [V, d]; also the LM head
     final_norm: np.ndarray  # [d]
     layers: List[LayerWeights]
+    sc_w1: Optional[np.ndarray] = None   # [m, d] self-conditioning MLP (gate)
+    sc_w3: Optional[np.ndarray] = None   # [m, d] (up)
+    sc_w2: Optional[np.ndarray] = None   # [d, m] (down)
 
 
 @dataclass
@@ -229,6 +240,21 @@ def layer_forward(x, positions, lw: LayerWeights, cfg: ModelConfig, prec: Precis
     f, r, ids, gates = moe(b, lw, cfg, prec)
     tr.ffn_in, tr.router_logits, tr.ids, tr.gates = b, r, ids, gates
     return x + f, tr
+
+
+def self_cond_input(z, lse, embed, prec: Precision):
+    """Self-conditioning input of rows with logits z [R, V] and log-sum-exp lse
+    [R]: the expectation of the embedding under the row's softmax, sum_v p_v E_v.
+    The GPU rounds p to bf16 before the product (bf16 models)."""
+    p = np.exp(z - np.asarray(lse)[:, None])
+    return _maybe_bf16(p, prec) @ embed
+
+
+def self_cond_embedding(u, w: Weights, prec: Precision):
+    """Term added to the token embedding of canvas rows with self-conditioning
+    state u [R, d]: the gated MLP W2 (silu(W1 u) * (W3 u)), u in bf16 on bf16
+    models.  Zero for u = 0."""
+    return swiglu_ffn(_maybe_bf16(u, prec), w.sc_w1, w.sc_w3, w.sc_w2, prec)
 
 
 def lm_head_stats(h, embed, final_norm, cfg: ModelConfig, prec: Precision, keep_logits=False):

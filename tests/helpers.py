@@ -31,7 +31,8 @@ def oracle_weights(w: synth.Workload, tw) -> oracle.Weights:
                 d[n] = oracle.dequantize_mxfp4(lt[n].cpu().numpy(), lt[n + "_mx_scale"].cpu().numpy())
         layers.append(oracle.LayerWeights(**d))
     return oracle.Weights(embed=to_f64(tw["embed"]), final_norm=to_f64(tw["final_norm"]),
-                          layers=layers)
+                          layers=layers, sc_w1=to_f64(tw.get("sc_w1")), sc_w3=to_f64(tw.get("sc_w3")),
+                          sc_w2=to_f64(tw.get("sc_w2")))
 
 
 def oracle_precision(w: synth.Workload, bf16_points=True) -> oracle.Precision:

@@ -768,3 +768,92 @@ def test_mxfp4_stand_in_quantizer_rounds_to_nearest_even():
     step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
     err = np.abs(deq - ref) / sc
     assert np.all((err <= step / 2) | ((y > 6) & (np.abs(deq) / sc == 6)))
+
+
+# ------------------------------------------------------- self-conditioning ----
+
+def test_self_cond_input_is_the_gradient_of_log_sum_exp():
+    # sum_v softmax(h E^T)_v E_v is d/dh log sum_v exp(h . E_v): central differences
+    rng = np.random.default_rng(7)
+    E = rng.standard_normal((37, 6))
+    h = rng.standard_normal((3, 6))
+    z = h @ E.T
+    lse = scipy.special.logsumexp(z, axis=1)
+    u = oracle.self_cond_input(z, lse, E, oracle.Precision())
+    eps = 1e-6
+    for r in range(3):
+        for j in range(6):
+            hp, hm = h[r].copy(), h[r].copy()
+            hp[j] += eps
+            hm[j] -= eps
+            g = (scipy.special.logsumexp(hp @ E.T) - scipy.special.logsumexp(hm @ E.T)) / (2 * eps)
+            assert abs(u[r, j] - g) < 1e-8
+
+
+def test_self_cond_input_special_cases():
+    rng = np.random.default_rng(8)
+    E = rng.standard_normal((50, 4))
+    z = np.zeros((1, 50))                                        # uniform softmax: the mean embedding
+    u = oracle.self_cond_input(z, scipy.special.logsumexp(z, axis=1), E, oracle.Precision())
+    assert np.allclose(u[0], E.mean(axis=0), rtol=1e-13, atol=1e-15)
+    z = np.full((1, 50), -1e3)
+    z[0, 17] = 0.0                                               # one dominant token: its embedding
+    u = oracle.self_cond_input(z, scipy.special.logsumexp(z, axis=1), E, oracle.Precision())
+    assert np.allclose(u[0], E[17], rtol=0, atol=1e-12)
+
+
+def test_self_cond_mlp_of_zero_is_zero_and_matches_a_swiglu():
+    w, cfg, ow = _tiny_setup(self_cond_hidden=32)
+    assert oracle.self_cond_embedding(np.zeros((3, w.d_model)), ow, oracle.Precision()).tolist() == \
+        np.zeros((3, w.d_model)).tolist()
+    u = np.random.default_rng(9).standard_normal((2, w.d_model))
+    g, up = u @ ow.sc_w1.T, u @ ow.sc_w3.T
+    ref = (g / (1 + np.exp(-g)) * up) @ ow.sc_w2.T
+    assert np.allclose(oracle.self_cond_embedding(u, ow, oracle.Precision()), ref, rtol=1e-12, atol=1e-15)
+
+
+def test_self_cond_steps_against_the_plain_model():
+    """First step of a canvas: state zero, so the step equals the plain model's.
+    Later steps differ; accepted positions keep their state; open positions
+    take the step's softmax expectation; a new canvas starts from zero."""
+    w, cfg, ow = _tiny_setup(self_cond_hidden=32)
+    # N(0, 0.02) weights give a near-uniform softmax and a term of ~1e-10: larger MLP weights make it visible
+    ow.sc_w1, ow.sc_w3, ow.sc_w2 = 100 * ow.sc_w1, 100 * ow.sc_w3, 100 * ow.sc_w2
+    w0, cfg0, ow0 = _tiny_setup(self_cond_hidden=0)
+    prec = oracle.Precision()
+    scfg = oracle.SamplerConfig(tau=w.tau, max_steps=w.max_steps)
+    prompt = synth.make_prompt(w, seed=1)
+    st = oracle.new_request(cfg, seed=5, max_ctx=w.prompt_len + 512)
+    st0 = oracle.new_request(cfg0, seed=5, max_ctx=w.prompt_len + 512)
+    oracle.prefill(st, prompt, cfg, ow, prec)
+    oracle.prefill(st0, prompt, cfg0, ow0, prec)
+    r = oracle.denoise_step(st, cfg, scfg, ow, prec, keep_logits=True)
+    r0 = oracle.denoise_step(st0, cfg0, scfg, ow0, prec)
+    assert np.array_equal(r.entropy, r0.entropy) and np.array_equal(r.ids_after, r0.ids_after)
+    # the state of the rows open in step 1 is their softmax expectation
+    open1 = ~r.accepted_before
+    assert open1.all()
+    assert np.allclose(st.sc_state, oracle.self_cond_input(r.logits, r.lse, ow.embed, prec), rtol=1e-12)
+    s1 = st.sc_state.copy()
+    r2 = oracle.denoise_step(st, cfg, scfg, ow, prec)
+    r20 = oracle.denoise_step(st0, cfg0, scfg, ow0, prec)
+    assert np.max(np.abs(r2.entropy - r20.entropy)) > 1e-6      # the MLP term reaches the output
+    acc = r2.accepted_before
+    assert acc.any() and np.array_equal(st.sc_state[acc], s1[acc])
+    assert not np.allclose(st.sc_state[~acc], s1[~acc])
+    while not st.accepted.all():
+        oracle.denoise_step(st, cfg, scfg, ow, prec)
+    oracle.commit_block(st, cfg, ow, prec)
+    oracle.denoise_step(st, cfg, scfg, ow, prec)
+    assert st.step == 1
+
+
+def test_self_cond_with_zero_mlp_weights_is_the_plain_model():
+    w, cfg, ow = _tiny_setup(self_cond_hidden=32)
+    ow.sc_w2 = np.zeros_like(ow.sc_w2)
+    w0, cfg0, ow0 = _tiny_setup(self_cond_hidden=0)
+    scfg = oracle.SamplerConfig(tau=w.tau, max_steps=w.max_steps)
+    prompt = synth.make_prompt(w, seed=2)
+    out = oracle.generate(prompt, 256, 3, cfg, scfg, ow, oracle.Precision())
+    out0 = oracle.generate(prompt, 256, 3, cfg0, scfg, ow0, oracle.Precision())
+    assert np.array_equal(out[0], out0[0])
