@@ -82,6 +82,11 @@ def step_bytes(w, P, rows, touched_per_layer):
     kv = w.n_layers * 2 * w.n_kv_heads * hd * es
     total += P * kv + rows * kv          # prefix read + canvas K/V write
     total += w.vocab * d * es            # LM head
+    m = getattr(w, "self_cond_hidden", 0)
+    if m:
+        # self-conditioning: the transposed embedding once, the open rows' logits
+        # (fp32) and softmax (bf16) written and read once, the MLP weights once
+        total += w.vocab * d * es + rows * w.vocab * 2 * (4 + 2) + 3 * d * m * es
     return total
 
 
@@ -92,6 +97,9 @@ def step_flops(w, P, rows, n_open):
     f = 2 * rows * w.n_layers * per_tok
     f += 4 * w.n_layers * w.n_q_heads * hd * rows * (P + rows)
     f += 2 * n_open * d * w.vocab
+    m = getattr(w, "self_cond_hidden", 0)
+    if m:
+        f += 2 * n_open * d * w.vocab + 2 * rows * 3 * d * m  # softmax x embedding; the MLP
     return f
 
 
@@ -174,7 +182,8 @@ def describe(w, K):
                 w.name, w.vocab, w.d_model, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_experts,
                 w.top_k, w.expert_hidden, w.shared_hidden,
                 {"fp8": ", routed experts in FP8 E4M3 with row scales",
-                 "mxfp4": ", routed experts in MXFP4 (E2M1, E8M0 scale per 32 weights)"}.get(w.expert_format, ""),
+                 "mxfp4": ", routed experts in MXFP4 (E2M1, E8M0 scale per 32 weights)"}.get(w.expert_format, "")
+                + (", self-conditioning MLP of width %d" % w.self_cond_hidden if w.self_cond_hidden else ""),
                 w.n_requests, w.prompt_len, K, max(1, -(-K // C)), C))
 
 
@@ -293,6 +302,8 @@ def main():
                     help="steps timed again with the routed experts in FP8 (full workload only; 0 = skip)")
     ap.add_argument("--mxfp4-steps", type=int, default=256,
                     help="steps timed again with the routed experts in MXFP4 (full workload only; 0 = skip)")
+    ap.add_argument("--sc-steps", type=int, default=256,
+                    help="steps timed again with a self-conditioning MLP of width 256 (full workload only; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 8 times (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE "
                          "against a kernel of known traffic) and exit")
@@ -378,6 +389,24 @@ def main():
                                  "value": rq["value"], "unit": "tok/s", "ms_per_step": rq["ms_per_step"],
                                  "roofline": rq["roofline"], "step_roofline": rq["step_roofline"]}
         del tq, layers
+        torch.cuda.empty_cache()
+    # The same model with self-conditioning (an MLP of width 256 on the previous
+    # step's softmax expectation of the embedding), its kernels timed as a family.
+    if args.sc_steps > 0 and w.name == "full":
+        ws = synth.WORKLOADS["full_sc"]
+        log("bench: self-conditioning leg")
+        tsc = dict(tw, **synth.make_self_cond_weights(ws, seed=args.seed, device="cuda"))
+        torch.cuda.synchronize()
+        rs = timed_run(ws, tsc, args.sc_steps, args.warmup, "self_cond", args.seed, log)
+        out["self_cond"] = {"workload": describe(ws, args.sc_steps), "steps": args.sc_steps, "value": rs["value"],
+                            "unit": "tok/s", "ms_per_step": rs["ms_per_step"],
+                            "self_cond_kernels_ms_per_launch": rs["roofline"]["launch_ms"],
+                            "self_cond_launches_timed": rs["roofline"]["launches"],
+                            "note": "two timed units per step: the MLP term added to the embedding, and the state "
+                                    "update after the LM head (logits to bf16 softmax, split-vocabulary product with "
+                                    "the transposed embedding, fold)",
+                            "step_roofline": rs["step_roofline"]}
+        del tsc
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")

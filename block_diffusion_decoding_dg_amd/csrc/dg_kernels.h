@@ -122,6 +122,27 @@ void dg_launch_philox_tokens(uint64_t seed, int block, int step, int n, int voca
 void dg_launch_gather_rows(const float* x, const int32_t* idx, int n, int d, float* out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Self-conditioning (bf16 models).  DgScSlots: the state rows ([C][d] fp32) of
+// the request in each slot of the step.
+struct DgScSlots {
+  float* state[DG_MAX_SEGS];
+};
+// ET [d][V] = E^T for E [V][d] bf16 (V, d multiples of 64).
+void dg_launch_transpose_bf16(const void* E, int V, int d, void* ET, hipStream_t s);
+// P (bf16, fragment-major [rows][V]) = exp(z - lse[row_idx[r]]) for rows r < *n_dev of z (fp32 [rows][V]).
+void dg_launch_sc_probs(const float* z, const float* lse, const int32_t* row_idx, const int32_t* n_dev,
+                        int max_rows, int V, void* P, hipStream_t s);
+// State rows of compacted rows r < *n_dev (canvas row row_idx[r]) = sum over the nks
+// ranges of parts ([nks][rows][d] fp32, range k at parts + k * stride).
+void dg_launch_sc_fold(const float* parts, int nks, size_t stride, int d, const int32_t* row_idx,
+                       const int32_t* n_dev, int max_rows, const DgScSlots& sl, int C, hipStream_t s);
+// b (bf16, fragment-major [rows][d]) = the state of canvas row t = slot * C + position.
+void dg_launch_sc_gather(const DgScSlots& sl, int rows, int C, int d, void* b, hipStream_t s);
+// b (bf16, fragment-major [n][d]) = u (fp32 row-major [n][d]).
+void dg_launch_rows_to_fm(const float* u, int n, int d, void* b, hipStream_t s);
+void dg_launch_fill_zero(float* p, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Weight-streaming GEMM (bf16 only): out = A W^T per group, 64 weight rows per
 // block and every activation row of the group (256 per pass over the weights).
 enum {
@@ -174,6 +195,7 @@ struct WsArgs {
   void* out;
   int ldo;
   int32_t* part_arg;      // LM-head argmax partials
+  float* zout;            // LM head, optional: the logits, fp32 [rows][N] (compacted rows)
   // q/k/v epilogue
   int hd, hq, hkv, max_ctx;
   const double* inv_freq;

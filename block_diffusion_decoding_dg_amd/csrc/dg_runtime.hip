@@ -25,6 +25,10 @@
 #ifndef DG_MAX_KSPLIT
 #define DG_MAX_KSPLIT 8
 #endif
+// Vocabulary ranges of the self-conditioning product, at most.
+#ifndef DG_SC_KSPLIT
+#define DG_SC_KSPLIT 16
+#endif
 
 namespace {
 
@@ -121,6 +125,16 @@ struct dg_ctx {
   float* xg = nullptr;  // gathered rows for the logits tap [rows_step][d]
 
   int32_t* info_host = nullptr;  // pinned [max_requests][4]
+
+  // Self-conditioning (cfg.self_cond_hidden > 0)
+  const void *sc_w1 = nullptr, *sc_w3 = nullptr, *sc_w2 = nullptr;
+  void* embed_t = nullptr;   // the embedding transposed, [d][V] bf16
+  float* sc_z = nullptr;     // logits of the LM head's open rows [rows_step][V]
+  void* sc_p = nullptr;      // their softmax, bf16 fragment-major [rows_step][V]
+  float* sc_parts = nullptr; // split-vocabulary partial sums [DG_SC_KSPLIT][rows_step][d]
+  float* sc_state = nullptr; // per request and position [max_requests][C][d]
+  void* sc_b = nullptr;      // MLP input, bf16 fragment-major [rows_step][d]
+  void* sc_h = nullptr;      // MLP hidden, bf16 fragment-major [rows_step][m]
 
   // Kernel timer: HIP event pairs around every launch of one kernel family.
   int kt_family = 0;
@@ -249,6 +263,9 @@ const char* check_config(const dg_model_config* c) {
   if (c->prefill_chunk < 0) return "prefill_chunk must be >= 0";
   // a routed work unit names its row part of an expert in 8 bits (128 rows each)
   if (c->prefill_chunk > 32768) return "prefill_chunk must be <= 32768";
+  if (c->self_cond_hidden < 0 || c->self_cond_hidden % 64 || c->self_cond_hidden > 4096)
+    return "self_cond_hidden must be a multiple of 64 in [0, 4096]";
+  if (c->self_cond_hidden > 0 && c->dtype != DG_BF16) return "self-conditioning needs a bf16 model";
   return nullptr;
 }
 
@@ -313,6 +330,16 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->ids_stage = cv.take<int32_t>(Tm * 4);
   c->xg = cv.take<float>(Rs * d * 4);
   c->attn_cap = attn_cap;
+  if (m.self_cond_hidden > 0) {
+    const size_t V = m.vocab;
+    c->embed_t = cv.take<void>(V * d * es);
+    c->sc_z = cv.take<float>((size_t)Rs * V * 4);
+    c->sc_p = cv.take<void>((size_t)Rs * V * es);
+    c->sc_parts = cv.take<float>((size_t)DG_SC_KSPLIT * Rs * d * 4);
+    c->sc_state = cv.take<float>((size_t)Rs * d * 4);
+    c->sc_b = cv.take<void>((size_t)Rs * d * es);
+    c->sc_h = cv.take<void>((size_t)Rs * m.self_cond_hidden * es);
+  }
   return align_up(cv.off, 256);
 }
 
@@ -520,7 +547,7 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
 // Fused LM head over the rows of c->hn (count *n_dev <= max_rows): per-row
 // softmax statistics and argmax written at row_idx[row] (or row).
 void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t* row_idx, float* ent, float* lse,
-                    int32_t* amax) {
+                    int32_t* amax, float* zout = nullptr) {
   const dg_model_config& m = c->cfg;
   if (c->dtype == DG_F32) {
     dg_launch_lm_head(c->dtype, c->hn, n_dev, max_rows, m.d_model, c->embed, m.vocab, c->lpart, c->lpart_arg, ent, lse,
@@ -538,8 +565,72 @@ void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t
   a.out = c->lpart;
   a.ldo = c->lm_tiles;
   a.part_arg = c->lpart_arg;
+  a.zout = zout;
   dg_launch_ws(WS_EPI_LM_STATS, a, c->lm_tiles, c->stream);
   dg_launch_lm_merge(c->lpart, c->lpart_arg, n_dev, max_rows, c->lm_tiles, row_idx, ent, lse, amax, c->stream);
+}
+
+// Self-conditioning state rows of the requests in the step's slots.
+DgScSlots sc_slots(const dg_ctx* c, const std::vector<int>& slot_req) {
+  DgScSlots sl;
+  memset(&sl, 0, sizeof sl);
+  for (size_t i = 0; i < slot_req.size(); ++i)
+    sl.state[i] = c->sc_state + (size_t)slot_req[i] * c->C * c->cfg.d_model;
+  return sl;
+}
+
+// The MLP term of the state rows in c->sc_b (bf16, fragment-major, `rows` rows)
+// added to x: W2 (silu(W1 b) * (W3 b)).  K of the W2 product is the MLP width,
+// a few 64-element chunks, so it is not split.
+void sc_mlp_add(dg_ctx* c, int rows, float* x) {
+  const dg_model_config& m = c->cfg;
+  launch_dense(c, WS_EPI_SWIGLU, c->sc_b, rows, m.d_model, c->sc_w1, c->sc_w3, m.self_cond_hidden, c->sc_h,
+               m.self_cond_hidden);
+  launch_dense_add(c, c->sc_h, rows, m.self_cond_hidden, c->sc_w2, m.d_model, x, nullptr, nullptr, 1);
+}
+
+// Embedding term of the canvas rows of the step's slots (rows = slots x C).
+void sc_embed(dg_ctx* c, const std::vector<int>& slot_req, int rows) {
+  if (c->cfg.self_cond_hidden <= 0) return;
+  KT(c, DG_KF_SELF_COND, dg_launch_sc_gather(sc_slots(c, slot_req), rows, c->C, c->cfg.d_model, c->sc_b, c->stream);
+                         sc_mlp_add(c, rows, c->x));
+}
+
+// State update after the LM head, whose logits of the open rows (compacted,
+// count *c->n_open_rows, canvas rows c->open_rows) are in c->sc_z and
+// log-sum-exp in c->lse: softmax in bf16, its product with the embedding over
+// vocabulary ranges (streaming GEMM against the transposed embedding, partial
+// sums per range), and the fold into the state rows.
+void sc_update(dg_ctx* c, const std::vector<int>& slot_req, int max_rows) {
+  const dg_model_config& m = c->cfg;
+  hipStream_t s = c->stream;
+  dg_launch_sc_probs(c->sc_z, c->lse, c->open_rows, c->n_open_rows, max_rows, m.vocab, c->sc_p, s);
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = c->sc_p;
+  a.W0 = c->embed_t;
+  a.K = m.vocab;
+  a.N = m.d_model;
+  a.M = max_rows;
+  a.M_dev = c->n_open_rows;
+  a.ldo = m.d_model;
+  a.wide = 1;  // 128 output columns per block
+  const int nblk = (m.d_model + 127) / 128, padded = (nblk + 7) / 8 * 8;
+  a.nblk = nblk;
+  a.msplit = std::max(1, (max_rows + 127) / 128);  // one pass of 128 rows per block
+  // Vocabulary ranges: enough blocks for about three per CU, at least two ranges
+  // (the partial-sum path), every range non-empty.
+  const int nk = m.vocab / 64;
+  int ks = std::min(DG_SC_KSPLIT, std::max(2, 3 * DG_DENSE_BLOCKS / (padded * a.msplit)));
+  const int kchunks = (nk + ks - 1) / ks;
+  ks = (nk + kchunks - 1) / kchunks;
+  a.ksplit = ks;
+  a.kchunks = kchunks;
+  a.part_out = c->sc_parts;
+  a.part_stride = (size_t)c->rows_step * m.d_model;
+  dg_launch_ws(WS_EPI_ADD_F32, a, padded * a.msplit * ks, s);
+  dg_launch_sc_fold(c->sc_parts, ks, a.part_stride, m.d_model, c->open_rows, c->n_open_rows, max_rows,
+                    sc_slots(c, slot_req), c->C, s);
 }
 
 // Attention half of layer l over `rows` rows in c->x.
@@ -739,6 +830,8 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
     if (cfg->expert_format == DG_EXPERTS_MXFP4 && (!w.w1_mx_scale || !w.w3_mx_scale || !w.w2_mx_scale))
       return fail(nullptr, DG_ERR_INVALID_ARG, "null expert block-scale pointer in layer %d", l);
   }
+  if (cfg->self_cond_hidden > 0 && (!weights->sc_w1 || !weights->sc_w3 || !weights->sc_w2))
+    return fail(nullptr, DG_ERR_INVALID_ARG, "null self-conditioning weight pointer");
   if (!kv_dev || !scratch_dev) return fail(nullptr, DG_ERR_INVALID_ARG, "null kv or scratch buffer");
   dg_model_config m = *cfg;
   if (m.prefill_chunk == 0) m.prefill_chunk = 2048;
@@ -756,6 +849,11 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   c->embed = weights->embed;
   c->final_norm = weights->final_norm;
   c->layers.assign(weights->layers, weights->layers + m.n_layers);
+  if (m.self_cond_hidden > 0) {
+    c->sc_w1 = weights->sc_w1;
+    c->sc_w3 = weights->sc_w3;
+    c->sc_w2 = weights->sc_w2;
+  }
   c->kv = (char*)kv_dev;
   c->stream = (hipStream_t)stream;
   c->C = m.canvas_len;
@@ -773,6 +871,11 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   // tiles; zeroing the cache once keeps those reads finite.
   if (e == hipSuccess) e = hipMemsetAsync(c->kv, 0, need_kv, c->stream);
   if (e == hipSuccess) e = hipMemsetAsync(c->canvas_acc, 1, c->rows_step, c->stream);
+  if (e == hipSuccess && m.self_cond_hidden > 0) {
+    dg_launch_transpose_bf16(c->embed, m.vocab, m.d_model, c->embed_t, c->stream);
+    dg_launch_fill_zero(c->sc_state, (size_t)c->rows_step * m.d_model, c->stream);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->info_host, m.max_requests * 4 * sizeof(int32_t));
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);  // default priority
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
@@ -857,6 +960,9 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
     }
     DgSampleArgs ia = sample_args(c, fresh);
     dg_launch_canvas_init(ia, c->open_rows, c->n_open_rows, s);
+    if (c->cfg.self_cond_hidden > 0)  // a new canvas starts with a zero state
+      for (int r : fresh)
+        dg_launch_fill_zero(c->sc_state + (size_t)r * c->C * c->cfg.d_model, (size_t)c->C * c->cfg.d_model, s);
   }
   const DgSampleArgs a = sample_args(c, slot_req);
   const int rows = a.count * c->C;
@@ -864,10 +970,15 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
   for (int r : slot_req) slots.push_back({r, c->req[r].P, c->C});
   dg_launch_open_rows(a, c->open_rows, c->n_open_rows, s);
   KT(c, DG_KF_EMBED, dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s));
+  sc_embed(c, slot_req, rows);
   forward_layers(c, slots, rows, false, false, true);
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
                                          c->cfg.rms_eps, c->hn, c->dtype == DG_BF16, s));
-  KT(c, DG_KF_LM_HEAD, launch_lm_head(c, c->n_open_rows, rows, c->open_rows, c->ent, c->lse, c->amax));
+  const bool sc = c->cfg.self_cond_hidden > 0;
+  KT(c, DG_KF_LM_HEAD, launch_lm_head(c, c->n_open_rows, rows, c->open_rows, c->ent, c->lse, c->amax,
+                                      sc ? c->sc_z : nullptr));
+  // the positions open at the start of the step take this step's softmax
+  if (sc) KT(c, DG_KF_SELF_COND, sc_update(c, slot_req, rows));
   KT(c, DG_KF_SAMPLE, dg_launch_sample(a, c->ent, c->amax, c->info_dev, nullptr, nullptr, s));
   LAUNCHCK(c);
   HIPCK(c, hipMemcpyAsync(c->info_host, c->info_dev, a.count * 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
@@ -896,6 +1007,7 @@ dg_status dg_commit_block(dg_ctx* c, int32_t req, int32_t* out_ids) {
   std::vector<int> one{req};
   const DgSampleArgs a = sample_args(c, one);
   dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s);
+  sc_embed(c, one, c->C);
   std::vector<SlotRow> slots{{req, q.P, c->C}};
   forward_layers(c, slots, c->C, false, true, false);
   LAUNCHCK(c);
@@ -1117,6 +1229,48 @@ dg_status dg_op_lm_head(dg_ctx* c, const float* h_dev, int32_t n, float* entropy
   launch_lm_head(c, c->n_open_rows, n, nullptr, entropy_dev, lse_dev, argmax_dev);
   LAUNCHCK(c);
   HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_op_self_cond(dg_ctx* c, const float* u_dev, int32_t n, float* out_dev) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (c->cfg.self_cond_hidden <= 0) return fail(c, DG_ERR_UNSUPPORTED, "the model has no self-conditioning");
+  if (!u_dev || !out_dev || n <= 0 || n > c->rows_step) return fail(c, DG_ERR_INVALID_ARG, "bad arguments");
+  hipStream_t s = c->stream;
+  dg_launch_fill_zero(out_dev, (size_t)n * c->cfg.d_model, s);
+  dg_launch_rows_to_fm(u_dev, n, c->cfg.d_model, c->sc_b, s);
+  sc_mlp_add(c, n, out_dev);
+  LAUNCHCK(c);
+  HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+namespace {
+dg_status sc_state_check(dg_ctx* c, int32_t req, const void* state) {
+  dg_status st = check_req(c, req);
+  if (st != DG_OK) return st;
+  if (c->cfg.self_cond_hidden <= 0) return fail(c, DG_ERR_UNSUPPORTED, "the model has no self-conditioning");
+  if (!state) return fail(c, DG_ERR_INVALID_ARG, "null state");
+  if (!c->req[req].active) return fail(c, DG_ERR_STATE, "request %d has no canvas", req);
+  return DG_OK;
+}
+}  // namespace
+
+dg_status dg_get_self_cond(dg_ctx* c, int32_t req, float* state) {
+  dg_status st = sc_state_check(c, req, state);
+  if (st != DG_OK) return st;
+  const size_t n = (size_t)c->C * c->cfg.d_model;
+  HIPCK(c, hipMemcpyAsync(state, c->sc_state + (size_t)req * n, n * 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
+  return DG_OK;
+}
+
+dg_status dg_set_self_cond(dg_ctx* c, int32_t req, const float* state) {
+  dg_status st = sc_state_check(c, req, state);
+  if (st != DG_OK) return st;
+  const size_t n = (size_t)c->C * c->cfg.d_model;
+  HIPCK(c, hipMemcpyAsync(c->sc_state + (size_t)req * n, state, n * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCK(c, hipStreamSynchronize(c->stream));
   return DG_OK;
 }
 

@@ -450,6 +450,11 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
           }
           const int rl = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
           const int r = row0 + rl;
+          if (a.zout && rl < cnt) {  // the logits themselves (self-conditioning)
+            float* zr = a.zout + (size_t)r * a.N + nb * BN + (lane & 15);
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) zr[n * 16] = acc[j][n][i];
+          }
           if ((lane & 15) == 0 && rl < cnt) {
             const size_t pi = (size_t)r * a.ldo + nb;  // ldo = number of vocabulary tiles
             float* pp = (float*)a.out + pi * 3;

@@ -20,11 +20,12 @@ DG_F32, DG_BF16 = 0, 1
 EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "dg_commit_block", "dg_generate",
            "dg_destroy", "dg_last_error", "dg_get_request", "dg_get_canvas", "dg_set_canvas", "dg_set_committed",
            "dg_last_step_rows", "dg_last_step_router_logits", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
-           "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read", "dg_kernel_timer_every")
+           "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read", "dg_kernel_timer_every",
+           "dg_get_self_cond", "dg_set_self_cond", "dg_op_self_cond")
 
 KERNEL_FAMILIES = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "out_proj": 5, "router": 6, "permute": 7,
                    "expert_up": 8, "expert_down": 9, "shared_up": 10, "shared_down": 11, "combine": 12,
-                   "lm_head": 13, "sample": 14}
+                   "lm_head": 13, "sample": 14, "self_cond": 15}
 
 
 class DgError(RuntimeError):
@@ -38,7 +39,7 @@ class ModelConfig(ctypes.Structure):
         "vocab", "d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
         "expert_hidden", "shared_hidden", "canvas_len", "max_ctx", "max_requests", "prefill_chunk")] + [
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("expert_format", ctypes.c_int32)]
+        ("expert_format", ctypes.c_int32), ("self_cond_hidden", ctypes.c_int32)]
 
 
 SAMPLER_MODES = {"threshold": 0, "budget": 1}
@@ -62,7 +63,8 @@ class LayerWeights(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
-                ("layers", ctypes.POINTER(LayerWeights))]
+                ("layers", ctypes.POINTER(LayerWeights)), ("sc_w1", ctypes.c_void_p), ("sc_w3", ctypes.c_void_p),
+                ("sc_w2", ctypes.c_void_p)]
 
 
 class StepInfo(ctypes.Structure):
@@ -110,6 +112,9 @@ def load():
         "dg_last_step_rows": [P, P, P, P, P, P, P],
         "dg_last_step_router_logits": [P, P],
         "dg_last_step_logits": [P, P, I32, P],
+        "dg_get_self_cond": [P, I32, P],
+        "dg_set_self_cond": [P, I32, P],
+        "dg_op_self_cond": [P, P, I32, P],
         "dg_op_attention": [P, I32, I32, P, I32, I32, I32],
         "dg_op_moe": [P, I32, P, I32, P, P],
         "dg_op_lm_head": [P, P, I32, P, P, P],
@@ -152,7 +157,8 @@ def model_config(w, max_requests=None, max_ctx=None, prefill_chunk=0):
                        max_ctx=w.max_ctx if max_ctx is None else max_ctx,
                        max_requests=w.n_requests if max_requests is None else max_requests,
                        prefill_chunk=prefill_chunk, rope_theta=w.rope_theta, rms_eps=w.rms_eps, dtype=dtype,
-                       expert_format=EXPERT_FORMATS[w.expert_format])
+                       expert_format=EXPERT_FORMATS[w.expert_format],
+                       self_cond_hidden=getattr(w, "self_cond_hidden", 0))
 
 
 def dg_workspace_size(cfg):
@@ -192,8 +198,9 @@ class Decoder:
                 if n in _SCALE_FIELDS and n not in lt:
                     continue  # scales of another expert format
                 setattr(self._layers[l], n, lt[n].data_ptr())
+        sc = {n: (weights[n].data_ptr() if n in weights else None) for n in ("sc_w1", "sc_w3", "sc_w2")}
         self._w = Weights(embed=weights["embed"].data_ptr(), final_norm=weights["final_norm"].data_ptr(),
-                          layers=self._layers)
+                          layers=self._layers, **sc)
         if sampler not in SAMPLER_MODES:
             raise ValueError("unknown sampler %r" % (sampler,))
         self.scfg = SamplerConfig(tau=tau, max_steps=max_steps, mode=SAMPLER_MODES[sampler], budget=budget,
@@ -297,6 +304,17 @@ class Decoder:
         self._check(self.lib.dg_last_step_logits(self.ctx, _np_ptr(r), len(r), _ptr(out)))
         return out
 
+    def dg_get_self_cond(self, req):
+        """Self-conditioning state of request req's canvas, fp32 [canvas_len][d_model]."""
+        out = np.zeros((self.C, self.cfg.d_model), dtype=np.float32)
+        self._check(self.lib.dg_get_self_cond(self.ctx, req, _np_ptr(out)))
+        return out
+
+    def dg_set_self_cond(self, req, state):
+        st = np.ascontiguousarray(state, dtype=np.float32)
+        assert st.shape == (self.C, self.cfg.d_model)
+        self._check(self.lib.dg_set_self_cond(self.ctx, req, _np_ptr(st)))
+
     # --- single operations -------------------------------------------------
     def dg_op_attention(self, req, layer, x, pos0, causal):
         assert x.dtype == torch.float32 and x.is_contiguous()
@@ -313,6 +331,13 @@ class Decoder:
         am = torch.empty(n, dtype=torch.int32, device=h.device)
         self._check(self.lib.dg_op_lm_head(self.ctx, _ptr(h), n, _ptr(ent), _ptr(lse), _ptr(am)))
         return ent, lse, am
+
+    def dg_op_self_cond(self, u):
+        """Self-conditioning MLP term of the rows of u (fp32 [n][d_model], device)."""
+        assert u.dtype == torch.float32 and u.is_contiguous()
+        out = torch.empty_like(u)
+        self._check(self.lib.dg_op_self_cond(self.ctx, _ptr(u), u.shape[0], _ptr(out)))
+        return out
 
     def dg_op_sample(self, req, entropy, argmax, step):
         info = StepInfo()

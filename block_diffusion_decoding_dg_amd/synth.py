@@ -173,7 +173,16 @@ def make_weights(w: Workload, seed: int = 0, device="cpu", layers: Optional[List
             for name in ("w1", "w3", "w2"):
                 lt[name], lt[name + "_mx_scale"] = quantize_blocks_mxfp4(lt[name])
         out["layers"].append(lt)
+    out.update(make_self_cond_weights(w, seed, device))
+    return out
+
+
+def make_self_cond_weights(w: Workload, seed: int = 0, device="cpu"):
+    """The self-conditioning MLP's weights of make_weights alone ({} without
+    self-conditioning): sc_w1, sc_w3 [m, d] and sc_w2 [d, m] in the workload dtype."""
+    out = {}
     if w.self_cond_hidden > 0:
+        dt = torch_dtype(w)
         m, d = w.self_cond_hidden, w.d_model
         for i, (name, shape) in enumerate((("sc_w1", (m, d)), ("sc_w3", (m, d)), ("sc_w2", (d, m)))):
             out[name] = _normal(shape, w.init_std, seed, 1 + w.n_layers * 64 + i, device, dt)

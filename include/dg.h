@@ -105,6 +105,17 @@ typedef enum dg_expert_format {
  * shared_hidden multiples of 64 (bf16) or 16 (f32); vocab a multiple of 128;
  * top_k <= 16; n_experts <= 256; max_requests <= 16; max_ctx a multiple of 64;
  * canvas_len == 256; prefill_chunk <= 32768.
+ *
+ * Self-conditioning ("DiffusionGemma hits ~1,500 TPS on one H100", section "How
+ * the sampler actually works": the previous step's softmax is fed back through
+ * a small gated MLP; the pages give no structure).  With self_cond_hidden m > 0
+ * every canvas position keeps a state u in R^d: zero when the canvas starts,
+ * and after each denoising step, at the positions that were open when the step
+ * began, u = sum_v softmax(z)_v E[v] (the expectation of the tied embedding
+ * under that step's logits z; softmax rounded to bf16 before the product).
+ * Every forward over the canvas (denoising steps and the block commit) adds
+ * sc_w2 (silu(sc_w1 u) * (sc_w3 u)) to the token embedding, u rounded to
+ * bf16.  bf16 models only; m a multiple of 64 and at most 4096.
  */
 typedef struct dg_model_config {
   int32_t vocab;
@@ -125,6 +136,7 @@ typedef struct dg_model_config {
   float rms_eps;         /* 1e-6 */
   int32_t dtype;         /* dg_dtype of weights, KV cache and activations */
   int32_t expert_format; /* dg_expert_format of the routed experts' w1, w3, w2 */
+  int32_t self_cond_hidden; /* width m of the self-conditioning MLP; 0 = none */
 } dg_model_config;
 
 /*
@@ -185,6 +197,9 @@ typedef struct dg_weights {
   const void* embed;              /* [V, d] device; also the LM head */
   const void* final_norm;         /* [d] device */
   const dg_layer_weights* layers; /* host array of n_layers entries (copied by dg_create) */
+  /* self-conditioning MLP (self_cond_hidden m > 0, else ignored), device, bf16:
+   * sc_w1, sc_w3 [m, d]; sc_w2 [d, m] */
+  const void *sc_w1, *sc_w3, *sc_w2;
 } dg_weights;
 
 /* Result of one denoising step for one request. */
@@ -348,6 +363,22 @@ dg_status dg_last_step_router_logits(dg_ctx* ctx, float* logits);
  */
 dg_status dg_last_step_logits(dg_ctx* ctx, const int32_t* rows, int32_t n, float* logits_dev);
 
+/*
+ * Self-conditioning state of request req's canvas (see dg_model_config):
+ * state (host, fp32 [canvas_len][d_model]) receives u of every position.
+ * Errors: DG_ERR_UNSUPPORTED without self-conditioning, DG_ERR_STATE if the
+ * request has no active canvas.
+ */
+dg_status dg_get_self_cond(dg_ctx* ctx, int32_t req, float* state);
+
+/*
+ * Replace request req's self-conditioning state (host, fp32
+ * [canvas_len][d_model]); used with dg_set_canvas to start both
+ * implementations of a step from the same state.  Same errors as
+ * dg_get_self_cond.
+ */
+dg_status dg_set_self_cond(dg_ctx* ctx, int32_t req, const float* state);
+
 /* ------------------------------------------------------------------------ */
 /* Single operations of the step, on the context's weights and scratch.      */
 /* Inputs and outputs are device pointers; each call runs on the context's   */
@@ -393,6 +424,14 @@ dg_status dg_op_sample(dg_ctx* ctx, int32_t req, const float* entropy_dev,
                        const int32_t* argmax_dev, int32_t step, dg_step_info* info);
 
 /*
+ * Self-conditioning term of n rows: out_dev (fp32 [n][d]) = sc_w2 (silu(sc_w1 b)
+ * * (sc_w3 b)) with b = bf16(u_dev) (u_dev fp32 [n][d]), by the kernels the
+ * step runs on the canvas.  n <= max_requests * canvas_len.  Errors:
+ * DG_ERR_UNSUPPORTED without self-conditioning.
+ */
+dg_status dg_op_self_cond(dg_ctx* ctx, const float* u_dev, int32_t n, float* out_dev);
+
+/*
  * Context-free: n uniform tokens in [0, vocab) for positions 0..n-1 of
  * (seed, block, step), as drawn by the sampler, to out_dev (int32).  stream as
  * in dg_create.  Synchronizes.
@@ -428,7 +467,9 @@ typedef enum dg_kernel_family {
                              with the next layer's attention RMSNorm */
   DG_KF_LM_HEAD = 13,     /* fused LM head + softmax statistics + tile merge */
   DG_KF_SAMPLE = 14,      /* entropy-bound sampler */
-  DG_KF_COUNT = 15
+  DG_KF_SELF_COND = 15,   /* self-conditioning: MLP term added to the embedding,
+                             and the state update after the LM head */
+  DG_KF_COUNT = 16
 } dg_kernel_family;
 
 /* Start timing `family` (DG_KF_NONE stops) on every later denoising step and

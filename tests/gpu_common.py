@@ -26,8 +26,12 @@ def log(*a):
 
 
 def to_gpu(tw):
-    return {"embed": tw["embed"].cuda(), "final_norm": tw["final_norm"].cuda(),
-            "layers": [{k: v.cuda() for k, v in lt.items()} for lt in tw["layers"]]}
+    out = {"embed": tw["embed"].cuda(), "final_norm": tw["final_norm"].cuda(),
+           "layers": [{k: v.cuda() for k, v in lt.items()} for lt in tw["layers"]]}
+    for n in ("sc_w1", "sc_w3", "sc_w2"):
+        if n in tw:
+            out[n] = tw[n].cuda()
+    return out
 
 
 def make_decoder(w, tw_gpu, max_requests=None, max_ctx=None, prefill_chunk=0, tau=None, max_steps=None,
@@ -207,6 +211,7 @@ def check_step(w, dec, st, ocfg, scfg, ow, prec, ent_tol, logit_tol, sample_rows
         stats.setdefault("ent_err", []).append(float(err_h.max()) if err_h.size else 0.0)
         stats.setdefault("router_flip_rows", []).append(int(flipped.sum()))
         stats.setdefault("argmax_flips", []).append(int(len(am_diff)))
+        stats["flipped"] = flipped  # rows whose routing differed in some layer (this step)
     # sampler: the GPU's accept set is the rule applied to its own (H, argmax)
     ids_g, acc_g = dec.dg_get_canvas(req)
     Hg_all = rows["entropy"][row0:row0 + C]

@@ -437,3 +437,48 @@ def test_full_budget_sampler_and_quantized_steps(full_model):
         if fmt != "bf16":
             del tws, layers
             torch.cuda.empty_cache()
+
+
+def test_full_self_cond_steps(full_model):
+    """Self-conditioning at the full shape (the full model plus an MLP of width
+    256): after each step, the GPU's state at sampled open positions against the
+    oracle's definition sum_v softmax(z)_v E[v] on the GPU's own logits and
+    log-sum-exp (the split-vocabulary product in its full-size launch shape); the
+    MLP op on unit-scale rows against the oracle; and, after a unit-scale state is
+    injected, the step's accept set against the rule on its own entropies,
+    accepted positions' state kept."""
+    tw = full_model
+    ws = synth.WORKLOADS["full_sc"]
+    tws = dict(tw, **synth.make_self_cond_weights(ws, seed=0, device="cuda"))
+    dec = make_decoder(ws, tws, max_requests=1, max_ctx=4096 + 512)
+    E = tw["embed"].float().cpu().numpy().astype(np.float64)
+    osc = oracle.Weights(embed=E, final_norm=None, layers=[],
+                         **{n: tws[n].float().cpu().numpy().astype(np.float64) for n in ("sc_w1", "sc_w3", "sc_w2")})
+    prec = oracle.Precision(bf16_points=True)
+    u = np.random.default_rng(11).standard_normal((37, ws.d_model)).astype(np.float32)
+    g = dec.dg_op_self_cond(torch.from_numpy(u).cuda()).cpu().numpy()
+    o = oracle.self_cond_embedding(u.astype(np.float64), osc, prec)
+    err = max(rel_l2(g[i], o[i]) for i in range(len(u)))
+    log("full_sc: MLP op worst row rel L2 %.2e" % err)
+    assert err <= 1e-2
+    prompt = synth.make_prompt(W, seed=4)
+    dec.dg_prefill(0, prompt, 21)
+    ids = philox.draw_tokens(21, 0, 0, np.arange(256), W.vocab).astype(np.int32)
+    acc = np.zeros(256, bool)
+    for s in range(3):
+        if s == 1:
+            dec.dg_set_self_cond(0, np.random.default_rng(12).standard_normal((256, ws.d_model)).astype(np.float32))
+        before = dec.dg_get_self_cond(0) if s > 0 else np.zeros((256, ws.d_model), np.float32)
+        dec.dg_denoise_step()
+        _check_step_properties(dec, 0, ids, acc, 21, W.vocab)
+        state = dec.dg_get_self_cond(0)
+        assert np.array_equal(state[acc], before[acc]), "state of accepted positions changed"
+        rows = dec.dg_last_step_rows()
+        pick = np.nonzero(~acc)[0][[0, 57, 128, -1]]
+        lg = dec.dg_last_step_logits(pick).cpu().numpy().astype(np.float64)
+        u_def = oracle.self_cond_input(lg, rows["lse"][pick].astype(np.float64), E, prec)
+        e = max(rel_l2(state[i], u_def[n]) for n, i in enumerate(pick))
+        log("full_sc: step %d: state vs definition on GPU logits %.2e" % (s + 1, e))
+        assert e <= 2e-3
+        ids, acc = dec.dg_get_canvas(0)
+    dec.close()

@@ -139,3 +139,117 @@ def test_mid_prefill_steps_commit(setup):
                                  band=STEP_BAND)
     assert info["block"] == 1 and info["step"] == 1
     dec.close()
+
+
+# ------------------------------------------------------------ self-conditioning
+# The mid-size model with a self-conditioning MLP of width 256.  With random
+# weights the softmax is nearly uniform and the state u = sum_v p_v E[v] is tiny
+# (~0.02 / sqrt(V)), so its MLP term barely moves the step; the tests therefore
+# check the state itself against the oracle's definition, the MLP op on
+# unit-scale inputs, and whole steps and a commit after a unit-scale state has
+# been injected on both sides, where the MLP term is as large as the embedding.
+SC_RL2 = 1e-2
+# The state against the oracle's own state (each side from its own forward):
+# u moves with the logits' error divided by the relative spread of p, about
+# 0.6 here (p is proportional to exp(z) with z of standard deviation ~0.64), so
+# the state is held to twice the logits' relative L2 bound.
+SC_STATE_RL2 = 2 * LOGIT_RL2
+
+
+@pytest.fixture(scope="module")
+def sc_setup():
+    w = synth.WORKLOADS["mid_sc"]
+    log("%s: generating weights on the GPU" % w.name)
+    tw_gpu = synth.make_weights(w, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    ow = helpers.oracle_weights(w, tw_gpu)
+    yield w, tw_gpu, helpers.oracle_config(w), ow, helpers.oracle_precision(w)
+    del tw_gpu
+    torch.cuda.empty_cache()
+
+
+def _rows_rel_l2(g, o):
+    return max(rel_l2(g[i], o[i]) for i in range(len(g))) if len(g) else 0.0
+
+
+def test_mid_self_cond_mlp_op(sc_setup):
+    """dg_op_self_cond on unit-scale rows (a ragged count: 200 rows, not a
+    multiple of the 16-row tile) against the oracle's W2 (silu(W1 u) * W3 u)."""
+    W, tw, ocfg, ow, prec = sc_setup
+    dec = make_decoder(W, tw)
+    u = np.random.default_rng(3).standard_normal((200, W.d_model)).astype(np.float32)
+    g = dec.dg_op_self_cond(torch.from_numpy(u).cuda()).cpu().numpy()
+    o = oracle.self_cond_embedding(u.astype(np.float64), ow, prec)
+    err = _rows_rel_l2(g, o)
+    log("mid_sc: MLP op worst row rel L2 %.2e (|out| rms %.3f)" % (err, float(np.sqrt(np.mean(o ** 2)))))
+    assert err <= SC_RL2
+    dec.close()
+
+
+def _check_state(dec, st, r, ow, prec, what, flipped):
+    """The GPU's state after a step: at the positions open when the step began,
+    (1) against the oracle's own state (same canvas, independent arithmetic), on
+    the rows whose routing agreed in every layer (a row whose expert set flipped
+    at a near-tie carries a legitimately different hidden state), and (2)
+    against the oracle's definition applied to the GPU's own logits and
+    log-sum-exp of a sample of the open rows (isolates the state update from the
+    forward's bf16 error)."""
+    g = dec.dg_get_self_cond(0)
+    open_b = ~r.accepted_before
+    idx = np.nonzero(open_b)[0]
+    cmp = np.nonzero(open_b & ~flipped)[0]
+    e1 = _rows_rel_l2(g[cmp], st.sc_state[cmp])
+    rows = dec.dg_last_step_rows()
+    pick = idx[np.linspace(0, len(idx) - 1, min(16, len(idx))).astype(int)]
+    lg = dec.dg_last_step_logits(pick).cpu().numpy().astype(np.float64)
+    u_def = oracle.self_cond_input(lg, rows["lse"][pick].astype(np.float64), ow.embed, prec)
+    e2 = _rows_rel_l2(g[pick], u_def)
+    log("mid_sc: %s: state vs oracle state %.2e (%d rows, %d routing flips left out), vs definition on GPU "
+        "logits %.2e" % (what, e1, len(cmp), len(idx) - len(cmp), e2))
+    assert e1 <= SC_STATE_RL2 and e2 <= 2e-3, (e1, e2)
+    return g
+
+
+def test_mid_self_cond_steps_commit(sc_setup):
+    W, tw, ocfg, ow, prec = sc_setup
+    prompt = synth.make_prompt(W, seed=0)
+    seed = 42
+    dec = make_decoder(W, tw)
+    dec.dg_prefill(0, prompt, seed)
+    st = oracle.new_request(ocfg, seed, W.max_ctx)
+    oracle.prefill(st, prompt, ocfg, ow, prec)
+    scfg = oracle.SamplerConfig(W.tau, W.max_steps)
+    # step 1: zero state, the plain model's step
+    stats = {}
+    r, _, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16, band=STEP_BAND,
+                         stats=stats)
+    g = _check_state(dec, st, r, ow, prec, "step 1", stats["flipped"])
+    # a unit-scale state on both sides (the GPU's bytes, so both start equal)
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal((256, W.d_model)).astype(np.float32)
+    dec.dg_set_self_cond(0, u)
+    st.sc_state = u.astype(np.float64)
+    assert np.array_equal(dec.dg_get_self_cond(0), u)
+    for s in (2, 3):
+        before = dec.dg_get_self_cond(0)
+        r, resync, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16,
+                                  band=STEP_BAND, stats=stats)
+        g = _check_state(dec, st, r, ow, prec, "step %d" % s, stats["flipped"])
+        keep = r.accepted_before
+        assert np.array_equal(g[keep], before[keep]), "state of accepted positions changed"
+        log("mid_sc: step %d ok (resync %s)" % (s, resync))
+    # commit with the state of the last step in the embedding term
+    st.accepted[:] = True
+    dec.dg_set_canvas(0, st.ids, st.accepted, st.step, st.block)
+    st.sc_state = dec.dg_get_self_cond(0).astype(np.float64)
+    P = st.P
+    ids_g = dec.dg_commit_block(0)
+    ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
+    assert np.array_equal(ids_g, ids_o)
+    _check_cache(dec, st, ocfg, P, P + 256, "commit", ctraces)
+    # the next canvas starts from a zero state again
+    r, _, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16, band=STEP_BAND,
+                            stats=stats)
+    assert info["block"] == 1 and info["step"] == 1
+    _check_state(dec, st, r, ow, prec, "block 1 step 1", stats["flipped"])
+    dec.close()
