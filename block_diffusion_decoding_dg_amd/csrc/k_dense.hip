@@ -85,8 +85,11 @@ __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
                      __uint_as_float(u.y & 0xffff0000u));
 }
 
-template <typename T, int NV, bool FM>
-__global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const int32_t* __restrict__ row_idx,
+// NTH threads per row (a multiple of 64): enough that a full-width row takes
+// one float4 per thread, so that every load of the row is in flight at once
+// (one block per row and a few hundred rows leave one block per CU).
+template <typename T, int NV, bool FM, int NTH>
+__global__ void __launch_bounds__(NTH) k_row_norm(float* __restrict__ x, const int32_t* __restrict__ row_idx,
                                                   const int32_t* __restrict__ n_dev, int d,
                                                   const float* __restrict__ parts, int nparts, size_t part_stride,
                                                   const float* __restrict__ y, const float* __restrict__ gates, int k,
@@ -101,7 +104,7 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
   float ss = 0.f;
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
-    const int c = threadIdx.x + 256 * u;
+    const int c = threadIdx.x + NTH * u;
     v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < nv) {
       float4 a = xr[c];
@@ -144,14 +147,16 @@ __global__ void __launch_bounds__(256) k_row_norm(float* __restrict__ x, const i
   }
   if (!g) return;  // uniform over the block
   ss = wave_sum(ss);
-  __shared__ float red[4];
+  __shared__ float red[NTH / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
-    const int c = threadIdx.x + 256 * u;
+    const int c = threadIdx.x + NTH * u;
     if (c < nv) {
       const float4 gg = load4<T>(g + 4 * c);
       const float4 r = make_float4(v[u].x * inv * gg.x, v[u].y * inv * gg.y, v[u].z * inv * gg.z, v[u].w * inv * gg.w);
@@ -165,16 +170,15 @@ template <typename T, bool FM>
 void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d, const float* y,
                      const float* gates, int k, const T* g, float eps, T* out, hipStream_t s, T* out_rm = nullptr,
                      const DgParts& pp = DgParts{}) {
-  const int nv = (d / 4 + 255) / 256;
-#define DG_ROW_NORM(NVV)                                                                                     \
-  k_row_norm<T, NVV, FM><<<rows, 256, 0, s>>>(x, row_idx, n_dev, d, pp.p, pp.n, pp.stride, y, gates, k, g, eps, out, \
-                                              out_rm)
-  if (nv <= 1) DG_ROW_NORM(1);
-  else if (nv <= 2) DG_ROW_NORM(2);
-  else if (nv <= 3) DG_ROW_NORM(3);
-  else if (nv <= 4) DG_ROW_NORM(4);
-  else if (nv <= 8) DG_ROW_NORM(8);
-  else DG_ROW_NORM(16);  // d <= 16384 (checked at creation)
+  const int nv4 = d / 4;  // float4s per row
+#define DG_ROW_NORM(NVV, NTHR)                                                                                    \
+  k_row_norm<T, NVV, FM, NTHR><<<rows, NTHR, 0, s>>>(x, row_idx, n_dev, d, pp.p, pp.n, pp.stride, y, gates, k, g, \
+                                                     eps, out, out_rm)
+  if (nv4 <= 256) DG_ROW_NORM(1, 256);
+  else if (nv4 <= 768) DG_ROW_NORM(1, 768);
+  else if (nv4 <= 1024) DG_ROW_NORM(1, 1024);
+  else if (nv4 <= 2048) DG_ROW_NORM(2, 1024);
+  else DG_ROW_NORM(4, 1024);  // d <= 16384 (checked at creation)
 #undef DG_ROW_NORM
 }
 
