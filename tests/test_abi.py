@@ -54,7 +54,9 @@ def _cfg(**kw):
                                  dict(n_q_heads=3), dict(top_k=17), dict(max_requests=17), dict(dtype=7),
                                  dict(d_model=0), dict(expert_hidden=100), dict(n_experts=300),
                                  # quantized experts need a bf16 model; 3 is no format
-                                 dict(expert_format=1), dict(expert_format=2), dict(expert_format=3)])
+                                 dict(expert_format=1), dict(expert_format=2), dict(expert_format=3),
+                                 # self-conditioning: bf16 models only, width a multiple of 64, at most 4096
+                                 dict(self_cond_hidden=64), dict(self_cond_hidden=-64)])
 def test_bad_configs_rejected(bad):
     with pytest.raises(dg.DgError) as e:
         dg.dg_workspace_size(_cfg(**bad))
@@ -99,3 +101,24 @@ def test_null_context_calls_fail_cleanly(lib):
     assert lib.dg_commit_block(None, 0, None) == dg.DG_ERR_INVALID_ARG
     assert lib.dg_philox_tokens(0, -1, 0, 4, 10, None, None) == dg.DG_ERR_INVALID_ARG
     lib.dg_destroy(None)
+
+
+def test_self_cond_workspace():
+    """Self-conditioning adds to the scratch exactly: the transposed embedding,
+    the open rows' logits (fp32) and softmax (bf16), the split partial sums, the
+    state, and the MLP's input and hidden rows (each carved on 256-byte
+    boundaries); the KV cache is unchanged.  A width that is not a multiple of 64
+    or above 4096 is rejected."""
+    w, ws = synth.WORKLOADS["mid"], synth.WORKLOADS["mid_sc"]
+    kv0, sc0 = dg.dg_workspace_size(dg.model_config(w))
+    kv1, sc1 = dg.dg_workspace_size(dg.model_config(ws))
+    assert kv1 == kv0
+    rows, V, d, m = w.n_requests * w.canvas_len, w.vocab, w.d_model, ws.self_cond_hidden
+    parts = [V * d * 2, rows * V * 4, rows * V * 2, 16 * rows * d * 4, rows * d * 4, rows * d * 2, rows * m * 2]
+    assert sc1 - sc0 == sum((p + 255) // 256 * 256 for p in parts)
+    for bad in (100, 8192):
+        c = dg.model_config(ws)
+        c.self_cond_hidden = bad
+        with pytest.raises(dg.DgError) as e:
+            dg.dg_workspace_size(c)
+        assert e.value.status == dg.DG_ERR_INVALID_ARG
