@@ -67,20 +67,24 @@ def expert_up_bytes(w, touched, rows):
             + rows * w.top_k * w.expert_hidden * es)
 
 
-def step_bytes(w, P, rows, touched_per_layer):
+def step_bytes(w, P, rows, touched_per_layer, weights=True):
     """Algorithmic HBM bytes of one denoising step over `rows` canvas rows whose
     request has committed length P: every weight the step needs once (routed
-    experts: only those touched), the KV prefix once, the canvas K/V written once."""
+    experts: only those touched), the KV prefix once, the canvas K/V written once.
+    weights=False: the request's own bytes only (its KV), for the second and later
+    requests of a step that denoises several canvases against the same weights."""
     es = esize(w)
     d, hd = w.d_model, w.head_dim
     dense = ((w.n_q_heads + 2 * w.n_kv_heads) * hd * d + w.n_q_heads * hd * d + w.n_experts * d
              + 3 * d * w.shared_hidden)
     total = 0
     per_expert = 2 * expert_matrix_bytes(w, w.expert_hidden, d) + expert_matrix_bytes(w, d, w.expert_hidden)
-    for t in touched_per_layer:
-        total += dense * es + t * per_expert
     kv = w.n_layers * 2 * w.n_kv_heads * hd * es
     total += P * kv + rows * kv          # prefix read + canvas K/V write
+    if not weights:
+        return total
+    for t in touched_per_layer:
+        total += dense * es + t * per_expert
     total += w.vocab * d * es            # LM head
     m = getattr(w, "self_cond_hidden", 0)
     if m:
@@ -121,6 +125,8 @@ def measured_traffic(w):
     except OSError:
         return None
     if fields.get("k_ws_source_sha256", "").strip() != sha or key not in fields:
+        return None
+    if w.n_requests != 1 or w.prompt_len != 4096:  # the counters were taken on the one-request workload
         return None
     return int(fields[key])
 
@@ -232,18 +238,20 @@ def timed_run(w, tw, K, W, kernel, seed, log):
     dec.dg_kernel_timer_every(TIMER_EVERY)
     torch.cuda.synchronize()
     log("bench: timing %d steps" % K)
-    trace = []  # (block, step, tokens) per request per step
+    trace = []  # (block, step, first active request of its step) per request per step
     tokens = 0
     commits = 0
     t0 = time.perf_counter()
     for i in range(K):
         infos = dec.dg_denoise_step()
+        first = True  # the step's first active request carries the weight bytes
         for r in range(R):
             inf = infos[r]
             if not inf["active"]:
                 continue
             tokens += inf["n_accepted"] + inf["n_forced"]
-            trace.append((inf["block"], inf["step"], inf["n_accepted"] + inf["n_forced"]))
+            trace.append((inf["block"], inf["step"], first))
+            first = False
         if all(infos[r]["done"] or not infos[r]["active"] for r in range(R)):
             for r in range(R):
                 if infos[r]["active"] and infos[r]["done"]:
@@ -263,10 +271,12 @@ def timed_run(w, tw, K, W, kernel, seed, log):
     # Algorithmic bytes and FLOPs of every timed step, from its block and its open rows.
     tot_bytes = 0
     tot_flops = 0
-    for blk, step, _ in trace:
+    # With R concurrent requests a step reads the weights once (touched experts
+    # as sampled for the whole batch) and each request's KV.
+    for blk, step, first in trace:
         P = w.prompt_len + blk * C
         n_open = C - (step - 1)  # one acceptance per step before this one (random weights)
-        tot_bytes += step_bytes(w, P, C, touched)
+        tot_bytes += step_bytes(w, P, C, touched, weights=first)
         tot_flops += step_flops(w, P, C, n_open)
     mean_bytes = tot_bytes / max(1, len(trace)) * R
     mean_flops = tot_flops / max(1, len(trace)) * R

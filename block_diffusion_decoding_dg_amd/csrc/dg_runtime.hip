@@ -1111,6 +1111,10 @@ dg_status dg_set_canvas(dg_ctx* c, int32_t req, const int32_t* ids, const uint8_
   HIPCK(c, hipMemcpyAsync(c->canvas_ids + (size_t)req * c->C, ids, c->C * 4, hipMemcpyHostToDevice, c->stream));
   HIPCK(c, hipMemcpyAsync(c->canvas_acc + (size_t)req * c->C, accepted, c->C, hipMemcpyHostToDevice, c->stream));
   HIPCK(c, hipMemsetAsync(c->canvas_prev + (size_t)req * c->C, 0xff, c->C * 4, c->stream));  // -1: no previous step
+  if (!q.active && c->cfg.self_cond_hidden > 0) {  // a new canvas starts from a zero self-conditioning state
+    dg_launch_fill_zero(c->sc_state + (size_t)req * c->C * c->cfg.d_model, (size_t)c->C * c->cfg.d_model, c->stream);
+    LAUNCHCK(c);
+  }
   HIPCK(c, hipStreamSynchronize(c->stream));
   q.active = true;
   q.done = open == 0;

@@ -329,6 +329,9 @@ dg_status dg_get_canvas(dg_ctx* ctx, int32_t req, int32_t* ids, uint8_t* accepte
  * the number of steps already taken in the block, and the block index.  The
  * request must be prefilled; committed length is kept.  Makes the canvas
  * active.  Used to start both implementations of a step from the same state.
+ * With self-conditioning, a request that had no active canvas gets a zero
+ * state (as a canvas started by dg_denoise_step); an active request keeps its
+ * state (dg_set_self_cond replaces it).
  */
 dg_status dg_set_canvas(dg_ctx* ctx, int32_t req, const int32_t* ids, const uint8_t* accepted,
                         int32_t step, int32_t block);

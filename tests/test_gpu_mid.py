@@ -253,3 +253,45 @@ def test_mid_self_cond_steps_commit(sc_setup):
     assert info["block"] == 1 and info["step"] == 1
     _check_state(dec, st, r, ow, prec, "block 1 step 1", stats["flipped"])
     dec.close()
+
+
+def test_mid_self_cond_two_requests(sc_setup):
+    """Two requests denoised together with self-conditioning: each request's
+    state rows hold the definition applied to its own rows' logits (canvas row =
+    slot * 256 + position), after a step from a zero state and after a step from
+    a unit-scale state injected into request 1 only (request 0 must not see it)."""
+    W, tw, ocfg, ow, prec = sc_setup
+    dec = make_decoder(W, tw, max_requests=2)
+    for r in range(2):
+        dec.dg_prefill(r, synth.make_prompt(W, seed=10 + r), 30 + r)
+    for s in range(2):
+        if s == 1:
+            dec.dg_set_self_cond(1, np.random.default_rng(7).standard_normal((256, W.d_model)).astype(np.float32))
+        acc_before = [dec.dg_get_canvas(r)[1] if s else np.zeros(256, bool) for r in range(2)]
+        infos = dec.dg_denoise_step()
+        assert all(infos[r]["active"] for r in range(2))
+        rows = dec.dg_last_step_rows()
+        for r in range(2):
+            g = dec.dg_get_self_cond(r)
+            idx = np.nonzero(~acc_before[r])[0]
+            pick = idx[[0, 100, len(idx) - 1]]
+            lg = dec.dg_last_step_logits(pick + 256 * r).cpu().numpy().astype(np.float64)
+            u_def = oracle.self_cond_input(lg, rows["lse"][pick + 256 * r].astype(np.float64), ow.embed, prec)
+            e = _rows_rel_l2(g[pick], u_def)
+            log("mid_sc: two requests, step %d, request %d: state vs definition %.2e" % (s + 1, r, e))
+            assert e <= 2e-3
+        if s == 1:
+            H_batch = rows["entropy"][:256].copy()
+    dec.close()
+    # request 0 alone, same prompt, seed and steps: its entropies match the batch
+    # run's (request 1's injected state must not reach request 0's rows)
+    solo = make_decoder(W, tw, max_requests=1)
+    solo.dg_prefill(0, synth.make_prompt(W, seed=10), 30)
+    solo.dg_denoise_step()
+    acc = solo.dg_get_canvas(0)[1]
+    solo.dg_denoise_step()
+    H_solo = solo.dg_last_step_rows()["entropy"][:256]
+    dH = np.abs(H_batch - H_solo)[~acc]
+    log("mid_sc: request 0 batch vs alone: median |dH| %.2e, 90%% %.2e" % (np.median(dH), np.quantile(dH, 0.9)))
+    assert np.quantile(dH, 0.9) < 1e-3
+    solo.close()
