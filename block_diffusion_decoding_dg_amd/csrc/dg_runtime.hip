@@ -615,13 +615,14 @@ void sc_update(dg_ctx* c, const std::vector<int>& slot_req, int max_rows) {
   a.M_dev = c->n_open_rows;
   a.ldo = m.d_model;
   a.wide = 1;  // 128 output columns per block
+  a.mt2 = 1;   // 256 rows per pass: each block reads its tile of the transposed embedding once
   const int nblk = (m.d_model + 127) / 128, padded = (nblk + 7) / 8 * 8;
   a.nblk = nblk;
-  a.msplit = std::max(1, (max_rows + 127) / 128);  // one pass of 128 rows per block
-  // Vocabulary ranges: enough blocks for about three per CU, at least two ranges
-  // (the partial-sum path), every range non-empty.
+  a.msplit = std::max(1, (max_rows + 255) / 256);
+  // Vocabulary ranges: about one block per CU (the two-m-tile variant holds one
+  // block per CU), at least two ranges (the partial-sum path), every range non-empty.
   const int nk = m.vocab / 64;
-  int ks = std::min(DG_SC_KSPLIT, std::max(2, 3 * DG_DENSE_BLOCKS / (padded * a.msplit)));
+  int ks = std::min(DG_SC_KSPLIT, std::max(2, DG_DENSE_BLOCKS / (padded * a.msplit)));
   const int kchunks = (nk + ks - 1) / ks;
   ks = (nk + kchunks - 1) / kchunks;
   a.ksplit = ks;

@@ -622,7 +622,8 @@ void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
     case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     case WS_EPI_ADD_F32:
       // 128 output columns per block (half the activation re-reads of 64)
-      if (a.wide) k_ws<WS_EPI_ADD_F32, 8, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
+      if (a.wide && a.mt2) k_ws<WS_EPI_ADD_F32, 8, KSUB_PROJ, 2, false, RD><<<grid, NT, 0, s>>>(a);
+      else if (a.wide) k_ws<WS_EPI_ADD_F32, 8, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
       else k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
       break;
     case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
