@@ -295,3 +295,40 @@ def test_mid_self_cond_two_requests(sc_setup):
     log("mid_sc: request 0 batch vs alone: median |dH| %.2e, 90%% %.2e" % (np.median(dH), np.quantile(dH, 0.9)))
     assert np.quantile(dH, 0.9) < 1e-3
     solo.close()
+
+
+def test_mid_capped_block_free_running(setup):
+    """A whole block run on both sides with the step cap lowered to 12: every
+    step checked as above (re-synchronised after a permitted near-tie
+    difference), the cap step forcing the remaining 245 positions to their argmax
+    (bf16 argmax near-ties allowed only inside the band), then the commit of the
+    final canvas and the first two steps of the next block."""
+    W, tw, ocfg, ow, prec = setup
+    if W.expert_format != "native":
+        pytest.skip("the bf16 model covers the block protocol; the quantized experts change only the MoE")
+    cap = 12
+    prompt = synth.make_prompt(W, seed=2)
+    dec = make_decoder(W, tw, max_steps=cap)
+    dec.dg_prefill(0, prompt, 7)
+    st = oracle.new_request(ocfg, 7, W.max_ctx)
+    oracle.prefill(st, prompt, ocfg, ow, prec)
+    scfg = oracle.SamplerConfig(W.tau, cap)
+    resyncs = 0
+    for s in range(cap):
+        r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=8,
+                                     band=STEP_BAND)
+        resyncs += resync
+        if s < cap - 1:
+            assert info["n_accepted"] == 1 and not info["done"]
+    assert info["done"] and info["n_forced"] == 256 - cap and st.accepted.all()
+    log("mid: capped block done in %d steps, %d re-syncs" % (cap, resyncs))
+    P = st.P
+    ids_g = dec.dg_commit_block(0)
+    ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
+    assert np.array_equal(ids_g, ids_o)
+    _check_cache(dec, st, ocfg, P, P + 256, "capped commit", ctraces)
+    for s in range(2):
+        r, _, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=8,
+                                band=STEP_BAND)
+        assert info["block"] == 1 and info["step"] == s + 1
+    dec.close()
