@@ -215,7 +215,7 @@ __device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u) {
 // block and shared by its four waves (the kernel above reads them once per wave).
 // The next tile is prefetched into registers while the current one is used, and
 // written to the other of two LDS stages.  K rows are XOR-swizzled in 16-byte
-// units (key & 7); each V^T row holds its 32 keys in the order the score tiles
+// units (key & 15, or key & 7 at head_dim 64); each V^T row holds its 32 keys in the order the score tiles
 // deliver them (lane group g of the matrix core covers keys 4g..4g+3 and
 // 16+4g..16+4g+3) and is swizzled by ((row >> 1) & 3), so every fragment read
 // is one conflict-free 16-byte LDS load.  All waves of a block walk the same
@@ -237,6 +237,7 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
   constexpr int NKK = HD / 32;
   constexpr int NHT = HD / 16;
   constexpr int KSEG = HD / 8;            // 16-byte segments per key row
+  constexpr int KSW = KSEG >= 16 ? 15 : 7;  // K-row swizzle: XOR of the segment with the key's low bits
   constexpr int SEGS_K = 32 * KSEG;       // per tile
   constexpr int SEGS_V = HD * 4;          // per tile (HD rows of 32 keys)
   constexpr int NTHR = 512 / QT;         // 128 query rows per block, QT m-tiles per wave
@@ -315,7 +316,7 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int sid = tid + NTHR * i, key = sid / KSEG, sgi = sid % KSEG;
-      sK[stg][key * KSEG + (sgi ^ (key & 7))] = rk[i];
+      sK[stg][key * KSEG + (sgi ^ (key & KSW))] = rk[i];
     }
     uint2* v8 = reinterpret_cast<uint2*>(sV[stg]);
 #pragma unroll
@@ -365,7 +366,7 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
       const int key = kt * 16 + c16;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & 7))];
+        const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & KSW))];
         const F kf = *reinterpret_cast<const F*>(&u);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
