@@ -205,7 +205,9 @@ struct WsArgs {
 
 // Grouped launches: rows per unit of work (one pass of the kernel), and the
 // code of an empty slot of a work list.
+#ifndef DG_WS_GROUP_ROWS
 #define DG_WS_GROUP_ROWS 128
+#endif
 #define DG_WS_UNIT_NONE 0xffffffffu
 // Slots of a grouped work list: parts * ceil8(nblk), where parts <= E +
 // rows * k / DG_WS_GROUP_ROWS bounds the number of (group, row part) pairs.
