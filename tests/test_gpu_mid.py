@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from block_diffusion_decoding_dg_amd import synth
+from block_diffusion_decoding_dg_amd import dg, synth
 from tests import helpers
 from tests.gpu_common import check_step, log, make_decoder, rel_l2, topk_gap
 
@@ -332,3 +332,29 @@ def test_mid_capped_block_free_running(setup):
                                 band=STEP_BAND)
         assert info["block"] == 1 and info["step"] == s + 1
     dec.close()
+
+
+def test_mid_self_cond_errors(sc_setup):
+    """The self-conditioning calls fail cleanly: no canvas yet (state), a model
+    without self-conditioning (unsupported), bad arguments; nothing is queued."""
+    W, tw, ocfg, ow, prec = sc_setup
+    dec = make_decoder(W, tw)
+    dec.dg_prefill(0, synth.make_prompt(W, seed=1), 3)
+    with pytest.raises(dg.DgError) as e:
+        dec.dg_get_self_cond(0)
+    assert e.value.status == dg.DG_ERR_STATE
+    with pytest.raises(dg.DgError) as e:
+        dec.dg_set_self_cond(0, np.zeros((256, W.d_model), np.float32))
+    assert e.value.status == dg.DG_ERR_STATE
+    too_many = torch.zeros((W.n_requests * 256 + 1, W.d_model), dtype=torch.float32, device="cuda")
+    with pytest.raises(dg.DgError) as e:
+        dec.dg_op_self_cond(too_many)
+    assert e.value.status == dg.DG_ERR_INVALID_ARG
+    dec.dg_denoise_step()
+    assert dec.dg_get_self_cond(0).shape == (256, W.d_model)
+    dec.close()
+    plain = make_decoder(synth.WORKLOADS["mid"], {k: v for k, v in tw.items() if not k.startswith("sc_")})
+    with pytest.raises(dg.DgError) as e:
+        plain.dg_op_self_cond(torch.zeros((4, W.d_model), dtype=torch.float32, device="cuda"))
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED
+    plain.close()
