@@ -437,7 +437,8 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 // expert-sorted layout (c->offsets16), or row-major with rowsrc mapping each
 // sorted row to its row of A.
 // Output projection / shared-expert W2: out (fp32 [M][N], row-major) += A W^T.
-// 128 output columns per block and at most 128 rows (one pass), and when that
+// 128 output columns per block and at most 128 rows (one pass; 256 rows with two
+// m-tiles per wave when there are more than 256 rows), and when that
 // leaves CUs idle the reduction is split too: each range then stores its partial
 // sums into c->parts, and the returned DgParts must be folded into out by the
 // next row kernel (in range order, so the result is deterministic).
@@ -456,6 +457,12 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   a.out = out;
   a.ldo = N;
   a.wide = 1;
+  // More than 256 rows (prefill chunks, eight canvases): two m-tiles per wave and
+  // 256-row parts, so each weight tile is read by half as many blocks.
+  if (M > 256) {
+    a.mt2 = 1;
+    part_rows = std::max(part_rows, 256);
+  }
   const int nblk = (N + 127) / 128, padded = (nblk + 7) / 8 * 8;
   a.nblk = nblk;
   a.msplit = std::max(1, (M + part_rows - 1) / part_rows);
