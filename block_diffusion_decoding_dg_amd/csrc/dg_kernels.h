@@ -184,7 +184,7 @@ struct WsArgs {
   float* part_out;        // with ksplit: partial sums [ksplit][rows][ldo] (fp32), range k at part_out + k * part_stride
   size_t part_stride;
   int wide;               // add launches: 128 output columns per block instead of 64
-  int mt2;                // wide add launches: two m-tiles per wave (256 rows per pass, each weight tile read once)
+  int mt2;                // dense launches (wide add, SwiGLU, q/k/v): two m-tiles per wave (256 rows per pass)
   int nblk;               // dense launches: number of n-blocks
   const int32_t* counts;  // grouped: rows per group
   const int32_t* offsets; // grouped: first position of each group in perm

@@ -430,6 +430,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   const int nblk = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, M);
+  a.mt2 = epi == WS_EPI_SWIGLU && M > 256;  // 256 rows per pass for prefill chunks and eight canvases
   dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), st ? st : c->stream);
 }
 
@@ -548,6 +549,7 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   const int nblk = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64;
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, rows);
+  a.mt2 = rows > 256;  // 256 rows per pass for prefill chunks and eight canvases
   dg_launch_ws(WS_EPI_ROPE_QKV, a, dense_grid(nblk, a.msplit), c->stream);
 }
 

@@ -626,8 +626,15 @@ void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
       else if (a.wide) k_ws<WS_EPI_ADD_F32, 8, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
       else k_ws<WS_EPI_ADD_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
       break;
-    case WS_EPI_SWIGLU: k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
+    // mt2: two m-tiles per wave (256 rows per pass) for launches with many rows
+    case WS_EPI_SWIGLU:
+      if (a.mt2) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 2, false, RD><<<grid, NT, 0, s>>>(a);
+      else k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
+      break;
+    case WS_EPI_ROPE_QKV:
+      if (a.mt2) k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 2, false, RD><<<grid, NT, 0, s>>>(a);
+      else k_ws<WS_EPI_ROPE_QKV, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a);
+      break;
     // The LM head keeps two m-tiles per wave: up to 256 rows in one pass, so the
     // embedding crosses HBM once per step.
     case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2, false, 4><<<grid, NT, 0, s>>>(a); break;
