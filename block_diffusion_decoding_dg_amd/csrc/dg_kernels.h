@@ -39,10 +39,11 @@ struct DgParts {
 };
 // fm: bf16 output in the fragment-major layout (fm_index) instead of row-major;
 // out_rm (optional, bf16): a second, row-major copy; parts: folded into x first
-// (x is then written back).
-void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm = nullptr,
-                       const DgParts& parts = DgParts{});
+// (x is then written back).  Returns -1 (nothing launched) for partial sums
+// without the bf16 fragment-major output, else 0.
+int dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
+                      const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm = nullptr,
+                      const DgParts& parts = DgParts{});
 
 // y = A W^T; mode 0: store in dtype, 1: store fp32, 2: add into fp32 out.
 void dg_launch_gemm(int dtype, int mode, const void* A, int M, int K, const void* W, int N, void* out, int ldo,
@@ -69,8 +70,8 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
 // (dg_launch_ws_units); everything after the top-k in one block for rows <= 2048.
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
-                     int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b,
-                     hipStream_t s);
+                     int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b,
+                     int32_t* n_b, hipStream_t s);
 // Rows of the expert-sorted layout: pairs + 16 per expert.
 inline int dg_sorted_rows(int E, int pairs) { return pairs + 16 * E; }
 // Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
@@ -83,9 +84,11 @@ void dg_launch_expert_down(int dtype, const void* h, int rows, int d, int E, int
 // x[t] += sum_j gates[t][j] * y[t*k + j]
 // x[t] += sum_j gates[t][j] y[t k + j] for every row, then (gain given) the
 // RMSNorm of the updated rows into out (model dtype).  d <= 16384, k <= 16.
-void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
-                            const void* gain, float eps, void* out, bool fm, hipStream_t s,
-                            const DgParts& parts = DgParts{});
+// Returns -1 (nothing launched) for partial sums without the bf16
+// fragment-major output, else 0.
+int dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
+                           const void* gain, float eps, void* out, bool fm, hipStream_t s,
+                           const DgParts& parts = DgParts{});
 // LM head over rows of hn [n][d] (dtype), n from n_dev (<= max_rows): partials then merge.
 void dg_launch_lm_head(int dtype, const void* hn, const int32_t* n_dev, int max_rows, int d, const void* embed,
                        int vocab, float* part, int32_t* part_arg, float* ent, float* lse, int32_t* amax,
@@ -128,14 +131,16 @@ struct DgScSlots {
   float* state[DG_MAX_SEGS];
 };
 // ET [d][V] = E^T for E [V][d] bf16 (V, d multiples of 64).
-void dg_launch_transpose_bf16(const void* E, int V, int d, void* ET, hipStream_t s);
+// Returns -1 (nothing launched) unless V and d are multiples of 64.
+int dg_launch_transpose_bf16(const void* E, int V, int d, void* ET, hipStream_t s);
 // P (bf16, fragment-major [rows][V]) = exp(z - lse[row_idx[r]]) for rows r < *n_dev of z (fp32 [rows][V]).
 void dg_launch_sc_probs(const float* z, const float* lse, const int32_t* row_idx, const int32_t* n_dev,
                         int max_rows, int V, void* P, hipStream_t s);
 // State rows of compacted rows r < *n_dev (canvas row row_idx[r]) = sum over the nks
 // ranges of parts ([nks][rows][d] fp32, range k at parts + k * stride).
-void dg_launch_sc_fold(const float* parts, int nks, size_t stride, int d, const int32_t* row_idx,
-                       const int32_t* n_dev, int max_rows, const DgScSlots& sl, int C, hipStream_t s);
+// Returns -1 (nothing launched) unless d is a multiple of 4.
+int dg_launch_sc_fold(const float* parts, int nks, size_t stride, int d, const int32_t* row_idx,
+                      const int32_t* n_dev, int max_rows, const DgScSlots& sl, int C, hipStream_t s);
 // b (bf16, fragment-major [rows][d]) = the state of canvas row t = slot * C + position.
 void dg_launch_sc_gather(const DgScSlots& sl, int rows, int C, int d, void* b, hipStream_t s);
 // b (bf16, fragment-major [n][d]) = u (fp32 row-major [n][d]).
@@ -209,11 +214,6 @@ struct WsArgs {
 #define DG_WS_GROUP_ROWS 128
 #endif
 #define DG_WS_UNIT_NONE 0xffffffffu
-// Slots of a grouped work list: parts * ceil8(nblk), where parts <= E +
-// rows * k / DG_WS_GROUP_ROWS bounds the number of (group, row part) pairs.
-inline int dg_ws_unit_slots(int E, int pairs, int nblk) {
-  return (E + (pairs + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS) * ((nblk + 7) & ~7);
-}
 
 // Writes the work-list entries of group e's `parts` row parts, starting at part
 // slot `first`: ceil8(nblk) entries per part, n-blocks in order, then padding.
@@ -225,8 +225,15 @@ __device__ __forceinline__ void dg_fill_units(int32_t* __restrict__ units, int f
                                                  : (int32_t)DG_WS_UNIT_NONE;
 }
 
-void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);
+// Returns 0, or -1 for a configuration the kernels do not implement (nothing launched).
+int dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);
+
+// Slots of a grouped work list: parts * ceil8(nblk), where parts <= E +
+// pairs / part_rows bounds the number of (group, row part) pairs.
+inline int dg_unit_slots(int E, int pairs, int part_rows, int nblk) {
+  return (E + (pairs + part_rows - 1) / part_rows) * ((nblk + 7) & ~7);
+}
 // Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b);
-// each list needs dg_ws_unit_slots(E, rows * k, nblk) entries.
-void dg_launch_ws_units(const int32_t* counts, int E, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
-                        int32_t* units_b, int32_t* n_b, hipStream_t s);
+// each list needs dg_unit_slots(E, rows * k, part_rows, nblk) entries.
+void dg_launch_ws_units(const int32_t* counts, int E, int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a,
+                        int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s);

@@ -72,6 +72,7 @@ struct dg_ctx {
   hipStream_t side = nullptr;              // second stream: the shared expert overlaps the routed ones
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipError_t sticky = hipSuccess;          // first failed stream call of a void helper
+  const char* refused = nullptr;           // first launch a helper refused (shape outside the kernels)
   int C = 256;
   int rows_step = 0;   // max_requests * C
   int rows_max = 0;    // max(rows_step, prefill_chunk)
@@ -123,6 +124,12 @@ struct dg_ctx {
   double* inv_freq = nullptr;
   int32_t* ids_stage = nullptr;
   float* xg = nullptr;  // gathered rows for the logits tap [rows_step][d]
+  // Debug taps of the denoising step (caller-owned device buffer, fp32):
+  // [2 n_layers + 1][rows_step][d]: slot 2 l = input of layer l, slot 2 l + 1 =
+  // the rows after layer l's attention half, slot 2 n_layers = the final rows.
+  float* tap_buf = nullptr;
+  bool tap_on = false;  // the current forward is a denoising step with taps
+  bool tap_valid = false;  // the last denoising step filled the tap buffer
 
   int32_t* info_host = nullptr;  // pinned [max_requests][4]
 
@@ -177,7 +184,17 @@ dg_status fail(dg_ctx* c, dg_status st, const char* fmt, ...) {
   do {                                                                                                 \
     hipError_t e_ = (ctx)->sticky != hipSuccess ? (ctx)->sticky : hipGetLastError();                  \
     (ctx)->sticky = hipSuccess;                                                                        \
+    const char* r_ = (ctx)->refused;                                                                   \
+    (ctx)->refused = nullptr;                                                                          \
     if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
+    if (r_) return fail((ctx), DG_ERR_UNSUPPORTED, "launch refused: %s", r_);                         \
+  } while (0)
+// A launcher that returned -1 queued nothing: the entry point reports
+// DG_ERR_UNSUPPORTED at its next LAUNCHCK (later launches of the same call may
+// still be queued; their results are not used).
+#define REFUSE_IF(ctx, cond, what)                     \
+  do {                                                 \
+    if ((cond) && !(ctx)->refused) (ctx)->refused = (what); \
   } while (0)
 #define HIPCK_V(call)                                              \
   do {                                                             \
@@ -304,8 +321,8 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->offsets16 = cv.take<int32_t>(E * 4);
   const size_t srows = (size_t)dg_sorted_rows((int)E, (int)(Tm * k));  // expert-sorted rows
   c->rowsrc = cv.take<int32_t>(srows * 4);
-  c->units_up = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.expert_hidden + 31) / 32) * 4);
-  c->units_dn = cv.take<int32_t>((size_t)dg_ws_unit_slots(E, Tm * k, (m.d_model + 63) / 64) * 4);
+  c->units_up = cv.take<int32_t>((size_t)dg_unit_slots(E, Tm * k, DG_WS_GROUP_ROWS, (m.expert_hidden + 31) / 32) * 4);
+  c->units_dn = cv.take<int32_t>((size_t)dg_unit_slots(E, Tm * k, DG_WS_GROUP_ROWS, (m.d_model + 63) / 64) * 4);
   c->rows_cap = Tm;
   c->n_units = cv.take<int32_t>(3 * 4);  // up list, down list, expert-sorted rows
   c->hbuf = cv.take<void>(srows * m.expert_hidden * es);
@@ -364,6 +381,14 @@ void* kv_ptr(const dg_ctx* c, int r, int l, int which) {
   return c->kv + (((size_t)r * c->cfg.n_layers + l) * 2 + which) * per;
 }
 
+// Copies the rows of c->x into tap slot `slot` (denoising steps with a tap buffer).
+void tap_rows(dg_ctx* c, int slot, int rows) {
+  if (!c->tap_on) return;
+  const size_t per = (size_t)c->rows_step * c->cfg.d_model;
+  HIPCK_V(hipMemcpyAsync(c->tap_buf + slot * per, c->x, (size_t)rows * c->cfg.d_model * 4, hipMemcpyDeviceToDevice,
+                         c->stream));
+}
+
 // Segments (one per slot) for layer l.  rows of slot s: [s*n, (s+1)*n).
 struct SlotRow {
   int req, pos0, n;
@@ -416,7 +441,10 @@ int dense_msplit(int nblk, int M) {
 int dense_grid(int nblk, int msplit) { return msplit > 1 ? (nblk + 7) / 8 * 8 * msplit : nblk; }
 void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W0, const void* W1, int N, void* out,
                   int ldo, hipStream_t st = nullptr) {
-  if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
+  if (c->dtype != DG_BF16) {  // bf16-only kernel; the fp32 model has its own launches
+    REFUSE_IF(c, true, "bf16 streaming projection on a non-bf16 model");
+    return;
+  }
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
@@ -431,7 +459,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, M);
   a.mt2 = epi == WS_EPI_SWIGLU && M > 256;  // 256 rows per pass for prefill chunks and eight canvases
-  dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), st ? st : c->stream);
+  REFUSE_IF(c, dg_launch_ws(epi, a, dense_grid(nblk, a.msplit), st ? st : c->stream) != 0, "dense projection");
 }
 
 // Grouped launch over the expert-sorted rows: A is fragment-major in the
@@ -447,7 +475,10 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
                          hipStream_t st = nullptr, float* parts = nullptr, int max_ksplit = DG_MAX_KSPLIT,
                          int part_rows = 128) {
   if (!parts) parts = c->parts;
-  if (c->dtype != DG_BF16) abort();  // bf16-only kernel; the fp32 model has its own launches
+  if (c->dtype != DG_BF16) {  // bf16-only kernel; the fp32 model has its own launches
+    REFUSE_IF(c, true, "bf16 streaming add projection on a non-bf16 model");
+    return DgParts{};
+  }
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
@@ -484,7 +515,7 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
     pend.stride = a.part_stride;
   }
   const int grid = (a.msplit > 1 || ks > 1) ? padded * a.msplit * ks : nblk;
-  dg_launch_ws(WS_EPI_ADD_F32, a, grid, st ? st : c->stream);
+  REFUSE_IF(c, dg_launch_ws(WS_EPI_ADD_F32, a, grid, st ? st : c->stream) != 0, "add projection");
   return pend;
 }
 
@@ -495,7 +526,10 @@ void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void
                    const float* s1, const uint8_t* b0, const uint8_t* b1, size_t wgs, int K, int N,
                    const int32_t* units, const int32_t* n_units, int nblk, void* out, int ldo,
                    const int32_t* rowsrc = nullptr) {
-  if (c->dtype != DG_BF16) abort();  // bf16-only kernel
+  if (c->dtype != DG_BF16) {  // bf16-only kernels
+    REFUSE_IF(c, true, "routed streaming projection on a non-bf16 model");
+    return;
+  }
   WsArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
@@ -520,7 +554,8 @@ void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void
   a.n_units = n_units;
   a.out = out;
   a.ldo = ldo;
-  dg_launch_ws(epi, a, dg_ws_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, nblk), c->stream);
+  const int grid = dg_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, DG_WS_GROUP_ROWS, nblk);
+  REFUSE_IF(c, dg_launch_ws(epi, a, grid, c->stream) != 0, "routed projection");
 }
 
 void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg) {
@@ -550,7 +585,7 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, rows);
   a.mt2 = rows > 256;  // 256 rows per pass for prefill chunks and eight canvases
-  dg_launch_ws(WS_EPI_ROPE_QKV, a, dense_grid(nblk, a.msplit), c->stream);
+  REFUSE_IF(c, dg_launch_ws(WS_EPI_ROPE_QKV, a, dense_grid(nblk, a.msplit), c->stream) != 0, "q/k/v projection");
 }
 
 // Fused LM head over the rows of c->hn (count *n_dev <= max_rows): per-row
@@ -575,7 +610,7 @@ void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t
   a.ldo = c->lm_tiles;
   a.part_arg = c->lpart_arg;
   a.zout = zout;
-  dg_launch_ws(WS_EPI_LM_STATS, a, c->lm_tiles, c->stream);
+  REFUSE_IF(c, dg_launch_ws(WS_EPI_LM_STATS, a, c->lm_tiles, c->stream) != 0, "LM head");
   dg_launch_lm_merge(c->lpart, c->lpart_arg, n_dev, max_rows, c->lm_tiles, row_idx, ent, lse, amax, c->stream);
 }
 
@@ -638,9 +673,9 @@ void sc_update(dg_ctx* c, const std::vector<int>& slot_req, int max_rows) {
   a.kchunks = kchunks;
   a.part_out = c->sc_parts;
   a.part_stride = (size_t)c->rows_step * m.d_model;
-  dg_launch_ws(WS_EPI_ADD_F32, a, padded * a.msplit * ks, s);
-  dg_launch_sc_fold(c->sc_parts, ks, a.part_stride, m.d_model, c->open_rows, c->n_open_rows, max_rows,
-                    sc_slots(c, slot_req), c->C, s);
+  REFUSE_IF(c, dg_launch_ws(WS_EPI_ADD_F32, a, padded * a.msplit * ks, s) != 0, "self-conditioning product");
+  REFUSE_IF(c, dg_launch_sc_fold(c->sc_parts, ks, a.part_stride, m.d_model, c->open_rows, c->n_open_rows, max_rows,
+                                 sc_slots(c, slot_req), c->C, s) != 0, "self-conditioning fold");
 }
 
 // Attention half of layer l over `rows` rows in c->x.
@@ -681,8 +716,11 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
   hipStream_t s = c->stream;
   // bf16: fragment-major for the dense projections, and a row-major copy that the
   // expert-sorted gather reads
-  KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps,
-                                         c->xn, c->dtype == DG_BF16, s, c->dtype == DG_BF16 ? c->xr : nullptr, pend));
+  KT(c, DG_KF_RMSNORM,
+     REFUSE_IF(c, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn,
+                                    c->dtype == DG_BF16, s, c->dtype == DG_BF16 ? c->xr : nullptr, pend) != 0,
+               "FFN norm"));
+  tap_rows(c, 2 * l + 1, rows);  // x after the attention half (its partial sums are folded now)
   DgParts pend2;  // the shared expert's W2 partial sums, folded by the combine
   if (c->dtype == DG_F32) {
     KT(c, DG_KF_ROUTER, dg_launch_gemm(c->dtype, 1, c->xn, rows, m.d_model, w.router, m.n_experts, rlog, m.n_experts, s);
@@ -712,8 +750,8 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
     KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
-                                         c->offsets16, c->rowsrc, c->n_units + 2, nb_up, c->units_up, c->n_units, nb_dn,
-                                         c->units_dn, c->n_units + 1, s));
+                                         c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, nb_up, c->units_up,
+                                         c->n_units, nb_dn, c->units_dn, c->n_units + 1, s));
     // routed experts over the expert-sorted rows: W1/W3 + SwiGLU gathering the
     // row-major normalised rows into c->hbuf (fragment-major, sorted rows), W2
     // from there into c->ybuf at each row's pair index
@@ -727,8 +765,10 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
                                            m.d_model));
   }
   if (c->dtype == DG_BF16) HIPCK_V(hipStreamWaitEvent(s, c->ev_join, 0));  // the shared expert is done
-  KT(c, DG_KF_COMBINE, dg_launch_combine_norm(c->dtype, c->x, c->ybuf, gates, rows, m.d_model, m.top_k, next_gain,
-                                              m.rms_eps, c->xn, c->dtype == DG_BF16, s, pend2));
+  KT(c, DG_KF_COMBINE,
+     REFUSE_IF(c, dg_launch_combine_norm(c->dtype, c->x, c->ybuf, gates, rows, m.d_model, m.top_k, next_gain,
+                                         m.rms_eps, c->xn, c->dtype == DG_BF16, s, pend2) != 0,
+               "MoE combine"));
 }
 
 // Forward of the rows in c->x through all layers.  kv_only: the last layer only
@@ -747,6 +787,7 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
       KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
       break;
     }
+    tap_rows(c, 2 * l, rows);
     const DgParts pend = attn_half(c, l, slots, rows, causal, xn_ready);
     int32_t* ids = tap ? c->tap_ids + (size_t)l * c->rows_step * m.top_k : c->rids;
     float* gates = tap ? c->tap_gates + (size_t)l * c->rows_step * m.top_k : c->rgates;
@@ -755,6 +796,7 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
     ffn_half(c, l, rows, ids, gates, rlog, next_gain, pend);
     xn_ready = next_gain != nullptr;
   }
+  if (!kv_only) tap_rows(c, 2 * m.n_layers, rows);
 }
 
 // Sampler threshold in fixed point: floor(clamp(h, 0, 64) * 2^40), NaN as 64
@@ -882,9 +924,9 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   if (e == hipSuccess) e = hipMemsetAsync(c->kv, 0, need_kv, c->stream);
   if (e == hipSuccess) e = hipMemsetAsync(c->canvas_acc, 1, c->rows_step, c->stream);
   if (e == hipSuccess && m.self_cond_hidden > 0) {
-    dg_launch_transpose_bf16(c->embed, m.vocab, m.d_model, c->embed_t, c->stream);
+    if (dg_launch_transpose_bf16(c->embed, m.vocab, m.d_model, c->embed_t, c->stream) != 0) e = hipErrorInvalidValue;
     dg_launch_fill_zero(c->sc_state, (size_t)c->rows_step * m.d_model, c->stream);
-    e = hipGetLastError();
+    if (e == hipSuccess) e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->info_host, m.max_requests * 4 * sizeof(int32_t));
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);  // default priority
@@ -981,7 +1023,10 @@ dg_status dg_denoise_step(dg_ctx* c, dg_step_info* info) {
   dg_launch_open_rows(a, c->open_rows, c->n_open_rows, s);
   KT(c, DG_KF_EMBED, dg_launch_embed_slots(c->dtype, a, c->embed, c->cfg.d_model, c->x, s));
   sc_embed(c, slot_req, rows);
+  c->tap_on = c->tap_buf != nullptr;
+  c->tap_valid = c->tap_on;
   forward_layers(c, slots, rows, false, false, true);
+  c->tap_on = false;
   KT(c, DG_KF_RMSNORM, dg_launch_rmsnorm(c->dtype, c->x, c->open_rows, c->n_open_rows, rows, c->cfg.d_model, c->final_norm,
                                          c->cfg.rms_eps, c->hn, c->dtype == DG_BF16, s));
   const bool sc = c->cfg.self_cond_hidden > 0;
@@ -1179,6 +1224,62 @@ dg_status dg_last_step_router_logits(dg_ctx* c, float* logits) {
   return DG_OK;
 }
 
+dg_status dg_debug_tap_size(const dg_model_config* cfg, size_t* bytes) {
+  const char* msg = check_config(cfg);
+  if (msg) return fail(nullptr, DG_ERR_INVALID_ARG, "%s", msg);
+  if (!bytes) return fail(nullptr, DG_ERR_INVALID_ARG, "null output pointer");
+  *bytes = (size_t)(2 * cfg->n_layers + 1) * cfg->max_requests * cfg->canvas_len * cfg->d_model * 4;
+  return DG_OK;
+}
+
+dg_status dg_debug_set_tap_buffer(dg_ctx* c, void* tap_dev, size_t bytes) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (!tap_dev) {
+    c->tap_buf = nullptr;
+    return DG_OK;
+  }
+  size_t need = 0;
+  dg_debug_tap_size(&c->cfg, &need);
+  if (bytes < need) return fail(c, DG_ERR_WORKSPACE, "tap buffer of %zu bytes < %zu", bytes, need);
+  c->tap_buf = (float*)tap_dev;
+  c->last_rows = 0;  // taps of earlier steps (if any) are not in the buffer
+  return DG_OK;
+}
+
+dg_status dg_debug_tap(dg_ctx* c, int32_t which, int32_t layer, float* host_dst, size_t bytes) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (!host_dst) return fail(c, DG_ERR_INVALID_ARG, "null destination");
+  if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
+  const int L = c->cfg.n_layers;
+  const size_t rows = c->last_rows, d = c->cfg.d_model;
+  hipStream_t s = c->stream;
+  if (which == DG_TAP_ROUTER_LOGITS) {
+    if (layer < 0 || layer >= L) return fail(c, DG_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, L);
+    const size_t n = rows * c->cfg.n_experts * 4;
+    if (bytes < n) return fail(c, DG_ERR_INVALID_ARG, "destination of %zu bytes < %zu", bytes, n);
+    HIPCK(c, hipMemcpyAsync(host_dst, c->tap_logits + (size_t)layer * c->rows_step * c->cfg.n_experts, n,
+                            hipMemcpyDeviceToHost, s));
+    HIPCK(c, hipStreamSynchronize(s));
+    return DG_OK;
+  }
+  int slot;
+  if (which == DG_TAP_LAYER_INPUT) {
+    if (layer < 0 || layer > L) return fail(c, DG_ERR_INVALID_ARG, "layer %d outside [0, %d]", layer, L);
+    slot = 2 * layer;
+  } else if (which == DG_TAP_AFTER_ATTENTION) {
+    if (layer < 0 || layer >= L) return fail(c, DG_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, L);
+    slot = 2 * layer + 1;
+  } else {
+    return fail(c, DG_ERR_INVALID_ARG, "unknown tap %d", which);
+  }
+  if (!c->tap_buf || !c->tap_valid) return fail(c, DG_ERR_STATE, "the last step ran without a tap buffer");
+  const size_t n = rows * d * 4;
+  if (bytes < n) return fail(c, DG_ERR_INVALID_ARG, "destination of %zu bytes < %zu", bytes, n);
+  HIPCK(c, hipMemcpyAsync(host_dst, c->tap_buf + (size_t)slot * c->rows_step * d, n, hipMemcpyDeviceToHost, s));
+  HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
 dg_status dg_last_step_logits(dg_ctx* c, const int32_t* rows_list, int32_t n, float* logits_dev) {
   if (!c) return DG_ERR_INVALID_ARG;
   if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
@@ -1207,8 +1308,9 @@ dg_status dg_op_attention(dg_ctx* c, int32_t req, int32_t layer, float* x_dev, i
   const DgParts pend = attn_half(c, layer, slots, t, causal != 0);
   // fold the output projection's partial sums into x (no norm follows here)
   if (pend.n > 0)
-    dg_launch_combine_norm(c->dtype, c->x, nullptr, nullptr, t, c->cfg.d_model, 0, nullptr, c->cfg.rms_eps, nullptr,
-                           true, c->stream, pend);
+    REFUSE_IF(c, dg_launch_combine_norm(c->dtype, c->x, nullptr, nullptr, t, c->cfg.d_model, 0, nullptr,
+                                        c->cfg.rms_eps, nullptr, true, c->stream, pend) != 0,
+              "partial-sum fold");
   LAUNCHCK(c);
   HIPCK(c, hipMemcpyAsync(x_dev, c->x, bytes, hipMemcpyDeviceToDevice, c->stream));
   HIPCK(c, hipStreamSynchronize(c->stream));

@@ -222,13 +222,13 @@ __device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u) {
 // key tiles; the key range is cut at the largest position among the block's
 // rows when the mask is causal.
 //
-// The probabilities P enter the P V product as fp16 (11 significant bits, round
-// to nearest even) against V converted to fp16 when its tile is staged: a bf16
-// value has 8 significant bits, so the conversion is exact over fp16's normal
-// range; magnitudes below it keep an absolute error under 2^-25 and magnitudes
-// above 65504 are clamped to it.  A row's reference maximum moves only when a
-// tile's maximum exceeds it by more than 2^8 (so P <= 256), which keeps the
-// rescaling of the running output rare.
+// The probabilities P enter the P V product as an fp16 high part plus an fp16
+// remainder (two products) against V converted to fp16 when its tile is staged:
+// a bf16 value has 8 significant bits, so the conversion is exact over fp16's
+// normal range; magnitudes below it keep an absolute error under 2^-25 and
+// magnitudes above 65504 are clamped to it.  A row's reference maximum moves
+// only when a tile's maximum exceeds it by more than 2^8 (so P <= 256), which
+// keeps the rescaling of the running output rare.
 template <int HD, int QT>
 __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
                                                      int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
@@ -416,21 +416,33 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) oacc[ht][qt] *= alpha[qt];
     }
-    v8h pf[QT];
+    // P enters the matrix cores as an fp16 high part and an fp16 remainder
+    // (p = hi + lo to about 2^-22 relative), two products against the same V
+    // tile: one fp16 P would carry a relative error of up to 2^-12 into the
+    // output, enough to flip the output's bf16 rounding in about one element in
+    // eight, and those flips then move everything downstream of the layer.
+    v8h pf[QT], pl[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pf[qt][kt * 4 + i] = (_Float16)p[kt][qt][i];
+        for (int i = 0; i < 4; ++i) {
+          const float v = p[kt][qt][i];
+          const _Float16 hi = (_Float16)v;
+          pf[qt][kt * 4 + i] = hi;
+          pl[qt][kt * 4 + i] = (_Float16)(v - (float)hi);
+        }
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int d = ht * 16 + c16;
       const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
       const v8h vf = *reinterpret_cast<const v8h*>(&u);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+      for (int qt = 0; qt < QT; ++qt) {
         oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qt], oacc[ht][qt], 0, 0, 0);
+        oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], oacc[ht][qt], 0, 0, 0);
+      }
     }
   };
   for (int kb = k_lo; kb < k_hi; kb += 32) {
@@ -442,10 +454,10 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
     stg ^= 1;
   }
   if (!wave_active) return;
-  // The split's output leaves normalised (O / l, at most max |v| in size) as
-  // fp16, half the bytes of fp32 to write and to merge; 11 significant bits
-  // are far below the bf16 rounding of the merged output.  The merge weighs it
-  // by l 2^(m - M).
+  // The split's output leaves normalised (O / l, at most max |v| in size) in
+  // fp32: an fp16 copy would add a 2^-12 relative error ahead of the output's
+  // bf16 rounding (see the P product above).  The merge weighs it by
+  // l 2^(m - M).
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
@@ -453,15 +465,9 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
     if (!qvalid[qt]) continue;
     const size_t qi = (size_t)trow[qt] * sh.hq + qhead[qt];
     const float inv = lrun[qt] > 0.f ? 1.f / lrun[qt] : 0.f;
-    _Float16* op = reinterpret_cast<_Float16*>(opart) + ((size_t)split * rows_total * sh.hq + qi) * HD;
+    float* op = opart + ((size_t)split * rows_total * sh.hq + qi) * HD;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-      v4h hv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = (_Float16)fminf(fmaxf(oacc[ht][qt][i] * inv, -65504.f), 65504.f);
-      *(v4h*)(op + ht * 16 + g4 * 4) = hv;
-    }
+    for (int ht = 0; ht < NHT; ++ht) *(v4f*)(op + ht * 16 + g4 * 4) = oacc[ht][qt] * inv;
     if (g4 == 0) {
       float* ml = mlpart + ((size_t)split * rows_total * sh.hq + qi) * 2;
       ml[0] = mrun[qt];
@@ -560,8 +566,8 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #define DG_ATTN_LDS(HDV)                                                                                    \
   k_attn_lds<HDV, DG_ATTN_QT(HDV)><<<blocks, 512 / DG_ATTN_QT(HDV), 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit,    \
                                                                            opart, mlpart, rows);                   \
-  k_attn_merge<bf16_t, true, _Float16, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV,  \
-                                                                          (bf16_t*)o)
+  k_attn_merge<bf16_t, true, float, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV,     \
+                                                                       (bf16_t*)o)
   if (dtype == 1) {
     if (sh.hd == 256) { DG_ATTN_LDS(256); }
     else if (sh.hd == 128) { DG_ATTN_LDS(128); }

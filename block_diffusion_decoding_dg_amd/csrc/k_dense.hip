@@ -182,37 +182,39 @@ void launch_row_norm(float* x, const int32_t* row_idx, const int32_t* n_dev, int
 #undef DG_ROW_NORM
 }
 
-void dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
-                       const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm,
-                       const DgParts& parts) {
-  if (rows <= 0) return;
+int dg_launch_rmsnorm(int dtype, const float* x, const int32_t* row_idx, const int32_t* n_dev, int rows, int d,
+                      const void* gain, float eps, void* out, bool fm, hipStream_t s, void* out_rm,
+                      const DgParts& parts) {
+  if (rows <= 0) return 0;
+  if (parts.n > 0 && !(dtype == 1 && fm)) return -1;  // partial sums come only from the bf16 streaming kernel
   // x is only read unless partial sums are folded in (the combine part is off)
   float* xm = const_cast<float*>(x);
   if (dtype == 1 && fm)
     launch_row_norm<bf16_t, true>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
                                   (bf16_t*)out, s, (bf16_t*)out_rm, parts);
-  else if (parts.n > 0) abort();  // partial sums come only from the bf16 streaming kernel
   else if (dtype == 1)
     launch_row_norm<bf16_t, false>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const bf16_t*)gain, eps,
                                    (bf16_t*)out, s);
   else
     launch_row_norm<float, false>(xm, row_idx, n_dev, rows, d, nullptr, nullptr, 0, (const float*)gain, eps,
                                   (float*)out, s);
+  return 0;
 }
 
-void dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
-                            const void* gain, float eps, void* out, bool fm, hipStream_t s, const DgParts& parts) {
-  if (rows <= 0) return;
+int dg_launch_combine_norm(int dtype, float* x, const float* y, const float* gates, int rows, int d, int k,
+                           const void* gain, float eps, void* out, bool fm, hipStream_t s, const DgParts& parts) {
+  if (rows <= 0) return 0;
+  if (parts.n > 0 && !(dtype == 1 && fm)) return -1;  // partial sums come only from the bf16 streaming kernel
   if (dtype == 1 && fm)
     launch_row_norm<bf16_t, true>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps,
                                   (bf16_t*)out, s, nullptr, parts);
-  else if (parts.n > 0) abort();  // partial sums come only from the bf16 streaming kernel
   else if (dtype == 1)
     launch_row_norm<bf16_t, false>(x, nullptr, nullptr, rows, d, y, gates, k, (const bf16_t*)gain, eps,
                                    (bf16_t*)out, s);
   else
     launch_row_norm<float, false>(x, nullptr, nullptr, rows, d, y, gates, k, (const float*)gain, eps, (float*)out,
                                   s);
+  return 0;
 }
 
 

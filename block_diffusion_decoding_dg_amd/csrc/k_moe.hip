@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ offsets16,
                                                      int32_t* __restrict__ rowsrc, int32_t* __restrict__ n_srows,
-                                                     int nblk_a,
+                                                     int part_rows, int nblk_a,
                                                      int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                      int nblk_b, int32_t* __restrict__ units_b,
                                                      int32_t* __restrict__ n_b) {
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
   if (tid < 256) {
     if (tid < E)
       for (int w = 0; w < nw; ++w) cnt += __popc(s_bits[tid][w]);
-    parts = (cnt + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+    parts = (cnt + part_rows - 1) / part_rows;
     s_off[tid] = cnt;
     s_part[tid] = parts;
     s_off16[tid] = (cnt + 15) & ~15;
@@ -304,17 +304,17 @@ __global__ void __launch_bounds__(256) k_sorted_layout(const int32_t* __restrict
 
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
-                     int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b,
-                     hipStream_t s) {
+                     int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b,
+                     int32_t* n_b, hipStream_t s) {
   dg_launch_topk(logits, rows, E, k, ids, gates, s);
   if (rows <= DG_ROUTE_MAX_ROWS && E <= 256) {
-    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, rowsrc, n_srows, nblk_a,
-                                    units_a, n_a, nblk_b, units_b, n_b);
+    k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, rowsrc, n_srows, part_rows,
+                                    nblk_a, units_a, n_a, nblk_b, units_b, n_b);
     return;
   }
   dg_launch_permute(ids, rows, E, k, counts, offsets, perm, s);
   k_sorted_layout<<<1, 256, 0, s>>>(counts, offsets, perm, E, k, offsets16, rowsrc, n_srows);
-  dg_launch_ws_units(counts, E, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
+  dg_launch_ws_units(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
 }
 
 // ---------------------------------------------------------------------------

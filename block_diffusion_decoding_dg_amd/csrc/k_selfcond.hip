@@ -39,9 +39,10 @@ __global__ void __launch_bounds__(256) k_transpose_bf16(const bf16_t* __restrict
   }
 }
 
-void dg_launch_transpose_bf16(const void* E, int V, int d, void* ET, hipStream_t s) {
-  if (V % 64 || d % 64) abort();  // whole tiles only (the caller validates the shapes)
+int dg_launch_transpose_bf16(const void* E, int V, int d, void* ET, hipStream_t s) {
+  if (V % 64 || d % 64) return -1;  // whole tiles only
   k_transpose_bf16<<<(V / 64) * (d / 64), 256, 0, s>>>((const bf16_t*)E, V, d, (bf16_t*)ET);
+  return 0;
 }
 
 // Probabilities of the open rows: P[r][v] = bf16(exp(z[r][v] - lse[row_idx[r]]))
@@ -97,11 +98,12 @@ __global__ void __launch_bounds__(256) k_sc_fold(const float* __restrict__ parts
   }
 }
 
-void dg_launch_sc_fold(const float* parts, int nks, size_t stride, int d, const int32_t* row_idx,
-                       const int32_t* n_dev, int max_rows, const DgScSlots& sl, int C, hipStream_t s) {
-  if (max_rows <= 0) return;
-  if (d % 4) abort();  // float4 rows (d is a multiple of 64)
+int dg_launch_sc_fold(const float* parts, int nks, size_t stride, int d, const int32_t* row_idx,
+                      const int32_t* n_dev, int max_rows, const DgScSlots& sl, int C, hipStream_t s) {
+  if (max_rows <= 0) return 0;
+  if (d % 4) return -1;  // float4 rows
   k_sc_fold<<<max_rows, 256, 0, s>>>(parts, nks, stride, d, row_idx, n_dev, sl, C);
+  return 0;
 }
 
 // MLP input of the canvas rows: row t = slot * C + position (t < rows) of the

@@ -30,7 +30,6 @@
 #include "dg_common.h"
 #include "dg_kernels.h"
 
-#include <cstdlib>
 #include <type_traits>
 
 namespace {
@@ -554,14 +553,15 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 // in turn (block u runs on XCD u % 8), so every part of n-block b of a group runs
 // on XCD b % 8 and the parts after the first find that weight tile in its L2.
 // One block; E <= 256.
-__global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ counts, int E, int nblk_a,
+__global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ counts, int E, int part_rows,
+                                                  int nblk_a,
                                                   int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                   int nblk_b, int32_t* __restrict__ units_b,
                                                   int32_t* __restrict__ n_b) {
   __shared__ int s_scan[256];
   const int e = threadIdx.x;
   const int c = e < E ? counts[e] : 0;
-  const int parts = (c + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+  const int parts = (c + part_rows - 1) / part_rows;
   s_scan[e] = parts;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
@@ -598,13 +598,13 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
 #ifndef DG_WS_RING_FP4
 #define DG_WS_RING_FP4 4
 #endif
-void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
-  if (grid <= 0) return;
+int dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return 0;
   constexpr int RD = DG_WS_RING_DENSE, RR = DG_WS_RING_ROUTED, R8 = DG_WS_RING_FP8, R4 = DG_WS_RING_FP4;
   constexpr int E8 = DG_WS_W_E4M3, F4 = DG_WS_W_MXFP4;
   if (a.counts) {  // grouped (routed experts)
-    if (a.wfmt != DG_WS_W_BF16 && a.wfmt != E8 && a.wfmt != F4) abort();
-    if (a.wfmt == F4 && a.K % 64) abort();  // whole 32-blocks per 64-element sub-chunk
+    if (a.wfmt != DG_WS_W_BF16 && a.wfmt != E8 && a.wfmt != F4) return -1;
+    if (a.wfmt == F4 && a.K % 64) return -1;  // whole 32-blocks per 64-element sub-chunk
     if (a.rowsrc && epi == WS_EPI_SWIGLU) {
       if (a.wfmt == E8) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, R8, E8><<<grid, NT, 0, s>>>(a);
       else if (a.wfmt == F4) k_ws<WS_EPI_SWIGLU, 4, KSUB_PROJ, 1, true, R4, F4><<<grid, NT, 0, s>>>(a);
@@ -613,10 +613,10 @@ void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
       if (a.wfmt == E8) k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, R8, E8><<<grid, NT, 0, s>>>(a);
       else if (a.wfmt == F4) k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, R4, F4><<<grid, NT, 0, s>>>(a);
       else k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RR><<<grid, NT, 0, s>>>(a);
-    } else abort();
-    return;
+    } else return -1;
+    return 0;
   }
-  if (a.wfmt != DG_WS_W_BF16) abort();  // E4M3 / MXFP4 weights: routed experts only
+  if (a.wfmt != DG_WS_W_BF16) return -1;  // E4M3 / MXFP4 weights: routed experts only
   switch (epi) {
     case WS_EPI_STORE_BF16: k_ws<WS_EPI_STORE_BF16, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
     case WS_EPI_STORE_F32: k_ws<WS_EPI_STORE_F32, 4, KSUB_PROJ, 1, false, RD><<<grid, NT, 0, s>>>(a); break;
@@ -638,11 +638,12 @@ void dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
     // The LM head keeps two m-tiles per wave: up to 256 rows in one pass, so the
     // embedding crosses HBM once per step.
     case WS_EPI_LM_STATS: k_ws<WS_EPI_LM_STATS, 8, KSUB_LM, 2, false, 4><<<grid, NT, 0, s>>>(a); break;
-    default: break;
+    default: return -1;
   }
+  return 0;
 }
 
-void dg_launch_ws_units(const int32_t* counts, int E, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b,
-                        int32_t* units_b, int32_t* n_b, hipStream_t s) {
-  k_ws_units<<<1, 256, 0, s>>>(counts, E, nblk_a, units_a, n_a, nblk_b, units_b, n_b);
+void dg_launch_ws_units(const int32_t* counts, int E, int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a,
+                        int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s) {
+  k_ws_units<<<1, 256, 0, s>>>(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b);
 }

@@ -21,7 +21,10 @@ EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "d
            "dg_destroy", "dg_last_error", "dg_get_request", "dg_get_canvas", "dg_set_canvas", "dg_set_committed",
            "dg_last_step_rows", "dg_last_step_router_logits", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
            "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read", "dg_kernel_timer_every",
-           "dg_get_self_cond", "dg_set_self_cond", "dg_op_self_cond")
+           "dg_get_self_cond", "dg_set_self_cond", "dg_op_self_cond", "dg_debug_tap_size", "dg_debug_set_tap_buffer",
+           "dg_debug_tap")
+
+DG_TAP_LAYER_INPUT, DG_TAP_AFTER_ATTENTION, DG_TAP_ROUTER_LOGITS = 0, 1, 2
 
 KERNEL_FAMILIES = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "out_proj": 5, "router": 6, "permute": 7,
                    "expert_up": 8, "expert_down": 9, "shared_up": 10, "shared_down": 11, "combine": 12,
@@ -123,6 +126,9 @@ def load():
         "dg_kernel_timer": [P, I32],
         "dg_kernel_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
         "dg_kernel_timer_every": [P, ctypes.c_int32],
+        "dg_debug_tap_size": [ctypes.POINTER(ModelConfig), ctypes.POINTER(SZ)],
+        "dg_debug_set_tap_buffer": [P, P, SZ],
+        "dg_debug_tap": [P, I32, I32, P, SZ],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -296,6 +302,26 @@ class Decoder:
         """[n_layers][rows][n_experts] fp32 router logits of the last step."""
         out = np.zeros((self.cfg.n_layers, rows, self.cfg.n_experts), dtype=np.float32)
         self._check(self.lib.dg_last_step_router_logits(self.ctx, _np_ptr(out)))
+        return out
+
+    # --- debug taps ------------------------------------------------------------
+    def enable_taps(self, on=True):
+        """Register (or drop) a device tap buffer: later steps copy their hidden
+        rows at every layer into it (dg_debug_set_tap_buffer)."""
+        if not on:
+            self._check(self.lib.dg_debug_set_tap_buffer(self.ctx, None, 0))
+            self.tap_buf = None
+            return
+        n = ctypes.c_size_t()
+        self._check(self.lib.dg_debug_tap_size(ctypes.byref(self.cfg), ctypes.byref(n)))
+        self.tap_buf = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+        self._check(self.lib.dg_debug_set_tap_buffer(self.ctx, _ptr(self.tap_buf), n.value))
+
+    def dg_debug_tap(self, which, layer, rows):
+        """fp32 [rows][d_model] (router logits: [rows][n_experts]) of the last step."""
+        width = self.cfg.n_experts if which == DG_TAP_ROUTER_LOGITS else self.cfg.d_model
+        out = np.zeros((rows, width), dtype=np.float32)
+        self._check(self.lib.dg_debug_tap(self.ctx, which, layer, _np_ptr(out), out.nbytes))
         return out
 
     def dg_last_step_logits(self, rows):

@@ -238,6 +238,22 @@ def make_prompt(w: Workload, seed: int = 0, length: Optional[int] = None):
     return rng.integers(0, w.vocab, size=n, dtype=np.int64).astype(np.int32)
 
 
+def make_prefix_kv(w: Workload, P: int, layer: int, seed: int = 0, device="cpu"):
+    """A synthetic committed prefix for one layer of one request: post-RoPE keys
+    and values of positions [0, P), both [n_kv_heads, P, head_dim] in the
+    workload dtype, drawn N(0, s^2) with s = init_std * sqrt(d_model) -- the
+    spread of a unit-RMS row projected by N(0, init_std^2) weights, i.e. the
+    spread of the keys and values a prefill of the random-init model writes.
+    It stands in for the K/V of a long random prompt wherever running the
+    prompt's prefill on the CPU would be out of reach."""
+    std = w.init_std * float(np.sqrt(w.d_model))
+    shape = (w.n_kv_heads, P, w.head_dim)
+    dt = torch_dtype(w)
+    k = _normal(shape, std, seed, 0x100000 + 2 * layer, device, dt)
+    v = _normal(shape, std, seed, 0x100000 + 2 * layer + 1, device, dt)
+    return k, v
+
+
 def make_normal(shape, seed, std=1.0, device="cpu", dtype=torch.float32):
     """Seeded N(0, std) tensor for op-level test inputs (activations, caches)."""
     return _normal(shape, std, seed, 0x7FFF, device, dtype)

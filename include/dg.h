@@ -57,9 +57,10 @@ typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
 
 /*
  * Storage of the routed experts' weights.  The pages name FP8 checkpoints
- * ("Google open-sources DiffusionGemma: H100 reaches 1000 TPS", section
- * "Hardware requirements"; "DiffusionGemma hits ~1,500 TPS on one H100",
- * section "Serve it with vLLM") without their layout; the format taken:
+ * ("DiffusionGemma hits ~1,500 TPS on one H100", section "Serve it with
+ * vLLM") and a quantized model of about 18 GB ("Google open-sources
+ * DiffusionGemma: H100 reaches 1000 TPS", section "26B MoE Architecture, but
+ * Only 3.8B Activated") without their layout; the format taken:
  *   DG_EXPERTS_NATIVE: the model dtype, like every other weight;
  *   DG_EXPERTS_FP8: one byte per weight in the OCP FP8 E4M3 encoding (bias 7,
  *     subnormals at exponent 0, 0x7F / 0xFF NaN, largest finite 448) plus one
@@ -357,6 +358,32 @@ dg_status dg_last_step_rows(dg_ctx* ctx, int32_t* n_rows, float* entropy, float*
  * in dg_last_step_rows.  Errors: DG_ERR_STATE before the first step.
  */
 dg_status dg_last_step_router_logits(dg_ctx* ctx, float* logits);
+
+/*
+ * Debug taps of the denoising step (tests and tools; outside the five-call
+ * contract).  A caller that registers a device buffer of dg_debug_tap_size()
+ * bytes gets, on every later dg_denoise_step, the fp32 hidden rows of the
+ * step copied into it at three points of every layer; dg_debug_tap then reads
+ * one of them back for the last step.  Rows as in dg_last_step_rows.
+ *   DG_TAP_LAYER_INPUT     layer l's input rows x (layer = n_layers: the rows
+ *                          after the last layer, before the final norm)
+ *   DG_TAP_AFTER_ATTENTION x after layer l's attention half (residual added)
+ *   DG_TAP_ROUTER_LOGITS   layer l's fp32 router logits [rows][n_experts]
+ *                          (kept by every step, buffer or not)
+ * The copies cost device bandwidth (2 n_layers + 1 row copies per step); a
+ * NULL buffer turns them off.  The buffer is caller-owned and must outlive its
+ * use.  dg_debug_tap errors: DG_ERR_STATE before a step (or when the last step
+ * ran without a buffer), DG_ERR_INVALID_ARG for an unknown tap, a layer out of
+ * range or a destination smaller than rows * d_model * 4 bytes (rows *
+ * n_experts * 4 for the router logits).  dg_debug_set_tap_buffer:
+ * DG_ERR_WORKSPACE if bytes < dg_debug_tap_size().
+ */
+#define DG_TAP_LAYER_INPUT 0
+#define DG_TAP_AFTER_ATTENTION 1
+#define DG_TAP_ROUTER_LOGITS 2
+dg_status dg_debug_tap_size(const dg_model_config* cfg, size_t* bytes);
+dg_status dg_debug_set_tap_buffer(dg_ctx* ctx, void* tap_dev, size_t bytes);
+dg_status dg_debug_tap(dg_ctx* ctx, int32_t which, int32_t layer, float* host_dst, size_t bytes);
 
 /*
  * LM-head logits of the last step's final hidden rows: for each of the n

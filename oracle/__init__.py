@@ -22,4 +22,4 @@ from .philox import philox4x64_10, draw_tokens
 from .quant import (decode_e4m3, dequantize_rows, E4M3_MAX, decode_e2m1, decode_e8m0, unpack_fp4,
                     dequantize_mxfp4, MX_BLOCK, E2M1_MAX)
 from .decode import (SamplerConfig, RequestState, StepResult, new_request, prefill, start_canvas,
-                     canvas_forward, sampler_decide, entropy_fixed, budget_decide, denoise_step, commit_block, generate)
+                     canvas_forward, canvas_forward_batch, sampler_decide, entropy_fixed, budget_decide, denoise_step, denoise_step_batch, commit_block, generate)

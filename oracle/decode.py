@@ -163,6 +163,32 @@ def canvas_forward(st: RequestState, cfg: ModelConfig, w: Weights, prec: Precisi
     return x, traces
 
 
+def canvas_forward_batch(states, cfg: ModelConfig, w: Weights, prec: Precision):
+    """canvas_forward for several requests in one pass, layer after layer: every
+    request's rows go through layer l before any goes through layer l + 1, so
+    each layer's weights are touched once per step.  Requests never mix: each
+    canvas attends only to its own prefix and its own rows, and the other parts
+    of a layer act row by row, so the result is that of canvas_forward on each
+    request alone."""
+    c = cfg.canvas_len
+    xs, pos, traces = [], [], []
+    for st in states:
+        if st.P + c > st.max_ctx:
+            raise ValueError("canvas does not fit in max_ctx")
+        x = w.embed[st.ids]
+        if cfg.self_cond_hidden > 0:
+            x = x + self_cond_embedding(st.sc_state, w, prec)
+        xs.append(x)
+        pos.append(st.P + np.arange(c))
+        traces.append([])
+    for l, lw in enumerate(w.layers):
+        for i, st in enumerate(states):
+            xs[i], tr = layer_forward(xs[i], pos[i], lw, cfg, prec, st.cache_k[l][:st.P], st.cache_v[l][:st.P],
+                                      mask=None)
+            traces[i].append(tr)
+    return xs, traces
+
+
 def sampler_decide(entropy, argmax, accepted, tau, step, max_steps):
     """Entropy-bound accept rule on one canvas (pure function).
 
@@ -233,6 +259,25 @@ def denoise_step(st: RequestState, cfg: ModelConfig, scfg: SamplerConfig, w: Wei
     if not st.active:
         start_canvas(st, cfg)
     x, traces = canvas_forward(st, cfg, w, prec)
+    return _finish_step(st, x, traces, cfg, scfg, w, prec, keep_logits)
+
+
+def denoise_step_batch(states, cfg: ModelConfig, scfg: SamplerConfig, w: Weights, prec: Precision,
+                       keep_logits=False):
+    """One denoising step of several requests together (canvases started as in
+    denoise_step), their forwards taken layer by layer (canvas_forward_batch);
+    returns one StepResult per request, each what denoise_step gives alone."""
+    for st in states:
+        if not st.active:
+            start_canvas(st, cfg)
+    xs, traces = canvas_forward_batch(states, cfg, w, prec)
+    return [_finish_step(st, x, tr, cfg, scfg, w, prec, keep_logits) for st, x, tr in zip(states, xs, traces)]
+
+
+def _finish_step(st: RequestState, x, traces, cfg: ModelConfig, scfg: SamplerConfig, w: Weights,
+                 prec: Precision, keep_logits):
+    """LM head, self-conditioning update and sampler of one canvas whose forward
+    gave final rows x."""
     sc = cfg.self_cond_hidden > 0
     stats = lm_head_stats(x, w.embed, w.final_norm, cfg, prec, keep_logits=keep_logits or sc)
     if sc:

@@ -204,6 +204,8 @@ def moe(b, lw: LayerWeights, cfg: ModelConfig, prec: Precision):
 
 @dataclass
 class LayerTrace:
+    x_in: np.ndarray = None         # [T, d] rows entering the layer
+    x_attn: np.ndarray = None       # [T, d] rows after the attention half (residual added)
     k: np.ndarray = None            # [T, Hkv, hd] post-RoPE keys of the processed rows
     v: np.ndarray = None            # [T, Hkv, hd]
     ffn_in: np.ndarray = None       # [T, d] normalised FFN input
@@ -221,6 +223,7 @@ def layer_forward(x, positions, lw: LayerWeights, cfg: ModelConfig, prec: Precis
     Returns (x_out, trace)."""
     t = x.shape[0]
     hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    x_in = x
     a = _maybe_bf16(rmsnorm(x, lw.attn_norm, cfg.rms_eps), prec)
     q = (a @ lw.wq.T).reshape(t, hq, hd)
     k = (a @ lw.wk.T).reshape(t, hkv, hd)
@@ -233,7 +236,7 @@ def layer_forward(x, positions, lw: LayerWeights, cfg: ModelConfig, prec: Precis
     o = attention(q, keys, vals, mask)
     o = _maybe_bf16(o.reshape(t, hq * hd), prec)
     x = x + o @ lw.wo.T
-    tr = LayerTrace(k=k, v=v)
+    tr = LayerTrace(x_in=x_in, x_attn=x, k=k, v=v)
     if skip_ffn:
         return x, tr
     b = _maybe_bf16(rmsnorm(x, lw.ffn_norm, cfg.rms_eps), prec)

@@ -3,10 +3,11 @@
 Test infrastructure: only the tests, the package's smoke check and the bench's
 CPU-baseline leg use this module; the GPU library never imports or links it.
 
-The pages name FP8 and NVFP4 checkpoints of the model ("Google open-sources
-DiffusionGemma: H100 reaches 1000 TPS", section "Hardware requirements";
-"DiffusionGemma hits ~1,500 TPS on one H100", section "Serve it with vLLM") but
-not their layout.  Format taken (a stated reading): each routed expert matrix
+The pages name FP8 and NVFP4 checkpoints of the model ("DiffusionGemma hits
+~1,500 TPS on one H100", section "Serve it with vLLM") and a quantized model
+that fits in about 18 GB ("Google open-sources DiffusionGemma: H100 reaches 1000
+TPS", section "26B MoE Architecture, but Only 3.8B Activated") but not their
+layout.  Format taken (a stated reading): each routed expert matrix
 holds one byte per weight in the OCP FP8 E4M3 encoding (1 sign bit, 4 exponent
 bits with bias 7, 3 mantissa bits; exponent 0 is subnormal, m x 2^-9; the
 all-ones exponent and mantissa pattern is NaN; no infinities; largest finite

@@ -1,0 +1,318 @@
+"""Whole denoising steps of the GPU library against the oracle, at any workload
+shape: the harness shared by tests/test_gpu_step_parity.py.
+
+Both sides start from the same seeded inputs and neither takes a value from
+the other:
+  * weights: synth.make_weights on the GPU; the oracle reads host float64
+    copies of the same tensors, one layer at a time and each routed expert only
+    when some row is routed to it (LazyLayers), so that the full-size model
+    (50 GB of bf16 weights) never has to sit in host memory as float64;
+  * the committed prefix: synth.make_prefix_kv keys and values, written into
+    the library's cache and read, as float64, by the oracle (LazyPrefix);
+  * the canvas: Philox at step 0, drawn by each side itself.
+
+Two comparisons per step (the design doc lists the bands and why):
+  * teacher_forced(): layer by layer, the library's attention half and MoE half
+    (dg_op_attention, dg_op_moe: the kernels and launch shapes of the step) run
+    on the oracle's own input rows of that layer, so both sides take every
+    routing decision from the same values: expert sets bit-exact except where
+    the oracle's k-th - (k+1)-th router logit gap is below GAP (1e-3), gates
+    within GATE_TOL, each half's update within RL2 relative L2 per row;
+  * free_running(): the library's own dg_denoise_step against the oracle's
+    step, with the per-layer rows read back through the debug taps: routing
+    differences only where the oracle's gap is below STEP_GAP, hidden rows and
+    logits within RL2 per row, entropies within H_TOL, argmax equal except where
+    the oracle's top-1 - top-2 logit gap is below STEP_GAP, the accepted
+    position the oracle's except where its two lowest open entropies lie within
+    2 H_TOL, accepted tokens and Philox re-draws exact.
+"""
+import numpy as np
+import torch
+
+import oracle
+from oracle import philox
+from block_diffusion_decoding_dg_amd import synth
+from tests import helpers
+from tests.gpu_common import log, rel_l2, topk_gap
+
+GAP = 1e-3        # routing / argmax band where both sides see the same input
+STEP_GAP = 1e-2   # the same decisions inside a free-running step
+RL2 = 1e-2        # bf16: relative L2 per row
+GATE_TOL = 1e-4   # teacher-forced gates (same input, fp32 softmax of fp32 logits)
+H_TOL = 1e-3      # nats, entropies of a free-running bf16 step
+MAX_FLIP_FRAC = 0.02  # routing differences per layer in a free-running step, at most this share of rows
+
+
+def _f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+class _LazyExperts:
+    """Stacked expert matrices [E, out, in] of one layer; expert e is copied to
+    the host as float64 on first use."""
+
+    def __init__(self, t):
+        self.t = t
+        self.cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = _f64(self.t[e])
+        return self.cache[e]
+
+
+class LazyLayers:
+    """The oracle's per-layer weights, built from the GPU tensors of
+    synth.make_weights one layer at a time (the last layer used is kept)."""
+
+    def __init__(self, tw_gpu):
+        self.layers = tw_gpu["layers"]
+        self.cur, self.lw = -1, None
+
+    def __len__(self):
+        return len(self.layers)
+
+    def __getitem__(self, l):
+        if l != self.cur:
+            self.lw = None
+            lt = self.layers[l]
+            d = {}
+            for k, v in lt.items():
+                if k in ("w1", "w3", "w2"):
+                    d[k] = _LazyExperts(v)
+                elif not k.endswith("scale"):
+                    d[k] = _f64(v)
+            self.lw = oracle.LayerWeights(**d)
+            self.cur = l
+        return self.lw
+
+    def __iter__(self):
+        for l in range(len(self)):
+            yield self[l]
+
+
+def oracle_weights(tw_gpu):
+    return oracle.Weights(embed=_f64(tw_gpu["embed"]), final_norm=_f64(tw_gpu["final_norm"]),
+                          layers=LazyLayers(tw_gpu))
+
+
+class LazyPrefix:
+    """cache_k / cache_v of an oracle request whose committed prefix [0, P) is
+    synth.make_prefix_kv: layer l's rows are generated on first use (the last
+    layer is kept), as float64 [P, Hkv, hd]."""
+
+    def __init__(self, w, P, seed, which, shared):
+        self.w, self.P, self.seed, self.which, self.shared = w, P, seed, which, shared
+
+    def __len__(self):
+        return self.w.n_layers
+
+    def __getitem__(self, l):
+        sh = self.shared
+        if sh.get("layer") != l:
+            sh.clear()
+            k, v = synth.make_prefix_kv(self.w, self.P, l, self.seed, device="cuda")
+            sh["layer"] = l
+            sh["k"] = _f64(k.transpose(0, 1))
+            sh["v"] = _f64(v.transpose(0, 1))
+        return sh[self.which]
+
+
+def oracle_request(w, P, prefix_seed, seed):
+    """An oracle request whose committed length is P with the synthetic prefix."""
+    shared = {}
+    st = oracle.RequestState(seed=seed, max_ctx=P + w.canvas_len,
+                             cache_k=LazyPrefix(w, P, prefix_seed, "k", shared),
+                             cache_v=LazyPrefix(w, P, prefix_seed, "v", shared))
+    st.P = P
+    return st
+
+
+def fill_prefix(dec, w, req, P, prefix_seed):
+    """Write the synthetic prefix of request req into the library's cache and
+    set its committed length."""
+    for l in range(w.n_layers):
+        k, vt = dec.kv_views(req, l)
+        kk, vv = synth.make_prefix_kv(w, P, l, prefix_seed, device="cuda")
+        k[:, :P, :] = kk
+        vt[:, :, :P] = vv.transpose(1, 2)
+    torch.cuda.synchronize()
+
+
+def teacher_forced(dec, w, reqs, results, Ps, stats):
+    """Run the library's attention and MoE halves of every layer on the oracle's
+    inputs of that layer (results: the oracle's StepResults of the requests in
+    reqs, whose committed lengths are Ps) and compare."""
+    ocfg = helpers.oracle_config(w)
+    C, k = w.canvas_len, w.top_k
+    n_rows = C * len(reqs)
+    flips_total = 0
+    for l in range(w.n_layers):
+        # attention half, one request at a time (its own prefix and canvas)
+        x_attn_g = []
+        for i, (req, r) in enumerate(zip(reqs, results)):
+            tr = r.layers[l]
+            x = torch.from_numpy(tr.x_in.astype(np.float32)).cuda()
+            dec.dg_op_attention(req, l, x, Ps[i], False)
+            xg = x.cpu().numpy().astype(np.float64)
+            d_g, d_o = xg - tr.x_in.astype(np.float32), tr.x_attn - tr.x_in
+            errs = [rel_l2(d_g[t], d_o[t]) for t in range(C)]
+            stats.setdefault("attn_rl2", []).append(float(np.max(errs)))
+            stats.setdefault("attn_rl2_med", []).append(float(np.median(errs)))
+            assert max(errs) <= RL2, ("attention half", l, i, max(errs))
+            x_attn_g.append(xg)
+        # MoE half over all the step's rows at once (the step's launch shape)
+        xa = np.concatenate([r.layers[l].x_attn for r in results]).astype(np.float32)
+        x = torch.from_numpy(xa).cuda()
+        ids = torch.empty((n_rows, k), dtype=torch.int32, device="cuda")
+        gates = torch.empty((n_rows, k), dtype=torch.float32, device="cuda")
+        dec.dg_op_moe(l, x, ids, gates)
+        xg = x.cpu().numpy().astype(np.float64)
+        ids, gates = ids.cpu().numpy(), gates.cpu().numpy()
+        for i, r in enumerate(results):
+            tr = r.layers[l]
+            rows = slice(i * C, (i + 1) * C)
+            x_next = r.layers[l + 1].x_in if l + 1 < w.n_layers else r.hidden
+            gap = topk_gap(tr.router_logits.astype(np.float32), k)
+            d_g, d_o = xg[rows] - xa[rows], x_next - tr.x_attn
+            moe_errs = []
+            for t in range(C):
+                gi, gg = ids[rows][t], gates[rows][t]
+                if set(gi.tolist()) != set(tr.ids[t].tolist()):
+                    assert gap[t] < GAP, ("router set differs outside the band", l, i, t, gap[t])
+                    flips_total += 1
+                    continue
+                og = dict(zip(tr.ids[t].tolist(), tr.gates[t].tolist()))
+                for e, g in zip(gi.tolist(), gg.tolist()):
+                    assert abs(g - og[e]) <= GATE_TOL, ("gate", l, i, t, e, g, og[e])
+                e_ = rel_l2(d_g[t], d_o[t])
+                moe_errs.append(e_)
+                assert e_ <= RL2, ("MoE half", l, i, t, e_)
+            stats.setdefault("moe_rl2", []).append(float(max(moe_errs)))
+            stats.setdefault("moe_rl2_med", []).append(float(np.median(moe_errs)))
+        log("  teacher-forced layer %2d: attention update rel L2 median %.2e max %.2e; MoE update median %.2e "
+            "max %.2e" % (l, stats["attn_rl2_med"][-1], stats["attn_rl2"][-1], stats["moe_rl2_med"][-1],
+                          stats["moe_rl2"][-1]))
+    stats["tf_router_flips"] = flips_total
+    log("  teacher-forced: %d layers x %d rows; routing differences (all inside the %.0e band): %d; "
+        "max attention rel L2 %.2e, max MoE rel L2 %.2e" % (w.n_layers, n_rows, GAP, flips_total,
+                                                          max(stats["attn_rl2"]), max(stats["moe_rl2"])))
+
+
+def free_running(dec, w, reqs, results, states_before, stats, plain_results=None, n_logit_rows=8):
+    """The library's own last dg_denoise_step (run with the tap buffer set)
+    against the oracle's step from the same state.  Every measure is logged
+    before any is asserted."""
+    C, k, L = w.canvas_len, w.top_k, w.n_layers
+    rows = dec.dg_last_step_rows()
+    n_rows = rows["rows"]
+    assert n_rows == C * len(reqs)
+    taps = [dec.dg_debug_tap(0, l, n_rows) for l in range(L + 1)]
+    rlog = [dec.dg_debug_tap(2, l, n_rows) for l in range(L)]
+    flipped = np.zeros(n_rows, dtype=bool)
+    layer_err, flip_gaps, bad = [], [], []
+    for l in range(L):
+        n_flip, errs, dr = 0, [], 0.0
+        for i, r in enumerate(results):
+            tr = r.layers[l]
+            sl = slice(i * C, (i + 1) * C)
+            gap = topk_gap(tr.router_logits.astype(np.float32), k)
+            x_g = taps[l][sl].astype(np.float64)
+            for t in range(C):
+                row = i * C + t
+                if flipped[row]:
+                    continue
+                errs.append(rel_l2(x_g[t], tr.x_in[t]))
+                dr = max(dr, float(np.max(np.abs(rlog[l][row] - tr.router_logits[t]))))
+                if set(rows["router_ids"][l][row].tolist()) != set(tr.ids[t].tolist()):
+                    flip_gaps.append(float(gap[t]))
+                    if gap[t] >= STEP_GAP:
+                        bad.append(("router set differs outside the step band", l, i, t, float(gap[t])))
+                    flipped[row] = True
+                    n_flip += 1
+        if n_flip > MAX_FLIP_FRAC * n_rows:
+            bad.append(("too many routing differences", l, n_flip))
+        if max(errs) > RL2:
+            bad.append(("hidden rows entering layer", l, max(errs)))
+        layer_err.append((float(np.median(errs)), float(max(errs)), n_flip, dr))
+    stats["layer_err"] = layer_err
+    stats["flip_gaps"] = sorted(flip_gaps)
+    for l in range(L):
+        log("  free-running layer %2d: hidden rel L2 median %.2e max %.2e; routing differences %d; "
+            "max |router logit diff| on agreeing rows %.2e" % ((l,) + layer_err[l]))
+    log("  free-running: rows with a routing difference in some layer: %d of %d; their oracle gaps %s"
+        % (flipped.sum(), n_rows, ["%.1e" % g for g in stats["flip_gaps"]]))
+    # final rows, entropies, argmax, sampler, canvas
+    fin = taps[L]
+    for i, r in enumerate(results):
+        req = reqs[i]
+        sl = slice(i * C, (i + 1) * C)
+        open_b = ~r.accepted_before
+        cmp = open_b & ~flipped[sl]
+        e_fin = [rel_l2(fin[sl][t], r.hidden[t]) for t in np.nonzero(~flipped[sl])[0]]
+        if max(e_fin) > RL2:
+            bad.append(("final rows", i, max(e_fin)))
+        Hg = rows["entropy"][sl].astype(np.float64)
+        dH = np.abs(Hg - r.entropy)[cmp]
+        stats.setdefault("dH_max", []).append(float(dH.max()))
+        stats.setdefault("dH_median", []).append(float(np.median(dH)))
+        if dH.max() > H_TOL:
+            bad.append(("entropy", i, float(dH.max())))
+        am_g = rows["argmax"][sl]
+        lgap = topk_gap(r.logits.astype(np.float32), 1)
+        diff = np.nonzero(cmp & (am_g != r.argmax))[0]
+        for t in diff:
+            if lgap[t] >= STEP_GAP:
+                bad.append(("argmax differs outside the step band", i, int(t), float(lgap[t])))
+        stats.setdefault("argmax_diff_gaps", []).extend(float(lgap[t]) for t in diff)
+        # the sampler: the GPU's choice is the rule on its own entropies; the
+        # oracle's choice may differ only between near-equal lowest entropies
+        ids_g, acc_g = dec.dg_get_canvas(req)
+        idx = np.nonzero(open_b)[0]
+        Hg32 = rows["entropy"][sl].astype(np.float32)
+        take_g = np.zeros(C, bool)
+        take_g[idx[np.argmin(Hg32[idx])]] = True
+        take_g |= open_b & (Hg32 < np.float32(w.tau))
+        assert np.array_equal(acc_g, r.accepted_before | take_g), "accept set is not the rule on the GPU's entropies"
+        newly_o = r.accepted_after & ~r.accepted_before
+        h_sorted = np.sort(r.entropy[open_b])
+        stats.setdefault("lowest_two_gap", []).append(float(h_sorted[1] - h_sorted[0]))
+        if not np.array_equal(newly_o, take_g):
+            near = h_sorted[1] - h_sorted[0] < 2 * H_TOL
+            involved = np.nonzero(newly_o != take_g)[0]
+            if not (near or flipped[sl][involved].any()):
+                bad.append(("accepted position differs", i, float(h_sorted[1] - h_sorted[0])))
+            stats.setdefault("accept_diffs", []).append(i)
+        else:
+            for t in np.nonzero(newly_o)[0]:
+                assert ids_g[t] == am_g[t]
+                if ids_g[t] != r.ids_after[t] and not (lgap[t] < STEP_GAP or flipped[sl][t]):
+                    bad.append(("accepted token differs", i, int(t)))
+        still = ~acc_g
+        st = states_before[i]
+        assert np.array_equal(ids_g[still], philox.draw_tokens(st["seed"], st["block"], st["step"] + 1,
+                                                               np.nonzero(still)[0], w.vocab)), "Philox re-draws"
+        assert np.array_equal(ids_g[r.accepted_before], r.ids_before[r.accepted_before])
+        # logits of sampled rows, against the oracle and (if given) the plain-arithmetic oracle
+        cand = np.nonzero(cmp)[0]
+        pick = np.sort(np.random.default_rng(i).choice(cand, size=min(n_logit_rows, len(cand)), replace=False))
+        lg = dec.dg_last_step_logits(pick + i * C).cpu().numpy().astype(np.float64)
+        el = [rel_l2(lg[n], r.logits[t]) for n, t in enumerate(pick)]
+        stats.setdefault("logit_rl2", []).append(float(max(el)))
+        if max(el) > RL2:
+            bad.append(("logits", i, max(el)))
+        if plain_results is not None:
+            pr = plain_results[i]
+            ep = [rel_l2(lg[n], pr.logits[t]) for n, t in enumerate(pick)]
+            stats.setdefault("logit_rl2_plain", []).append(float(max(ep)))
+            stats.setdefault("dH_plain_max", []).append(float(np.max(np.abs(Hg - pr.entropy)[cmp])))
+    log("  free-running: |dH| max %.2e median %.2e; argmax differences at oracle gaps %s; accept differences %s "
+        "(lowest-two entropy gaps %s); logits rel L2 %.2e%s"
+        % (max(stats["dH_max"]), max(stats["dH_median"]), stats["argmax_diff_gaps"], stats.get("accept_diffs", []),
+           ["%.1e" % g for g in stats["lowest_two_gap"]], max(stats["logit_rl2"]),
+           "" if plain_results is None else
+           " (against the plain-arithmetic oracle: logits %.2e, |dH| max %.2e)"
+           % (max(stats["logit_rl2_plain"]), max(stats["dH_plain_max"]))))
+    assert not bad, bad[:10]
+    return flipped

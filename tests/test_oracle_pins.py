@@ -562,6 +562,113 @@ def test_zero_weights_layer_is_identity():
     assert np.array_equal(x, y)
 
 
+def _ffn_zero(lw):
+    """The layer with its FFN (router, routed and shared experts) zeroed: SwiGLU
+    of zero weights is exactly zero, so the FFN half adds nothing."""
+    d = dict(lw.__dict__)
+    for k in ("router", "w1", "w3", "w2", "sw1", "sw3", "sw2"):
+        d[k] = np.zeros_like(d[k])
+    return oracle.LayerWeights(**d)
+
+
+def _plain_rmsnorm(x, eps):
+    return x / np.sqrt((x ** 2).mean(axis=-1, keepdims=True) + eps)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_layer_wiring_uniform_attention_closed_form(causal):
+    """Wq = 0 makes every score zero, so each head's output is the plain mean of
+    the values it may see (GQA: q-head h reads kv-head h // (Hq / Hkv)), values
+    projected from the normalised rows WITHOUT RoPE, then added through Wo^T to
+    the residual.  Written out independently of oracle.attention / oracle.rope:
+    RoPE applied to v, a transposed Wo, a wrong GQA map or a lost residual all
+    change the result."""
+    w, cfg, ow = _tiny_setup(seed=3)
+    lw = _ffn_zero(ow.layers[0])
+    lw.wq = np.zeros_like(lw.wq)
+    rng = np.random.default_rng(21)
+    P, T = 7, 5
+    hkv, hd, hq = cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
+    kp = rng.standard_normal((P, hkv, hd))
+    vp = rng.standard_normal((P, hkv, hd))
+    x = rng.standard_normal((T, cfg.d_model))
+    pos = P + np.arange(T)
+    mask = None
+    if causal:  # key j visible to row i if j <= P + i (prefix fully, own rows causally)
+        mask = np.arange(P + T)[None, :] <= (P + np.arange(T))[:, None]
+    y, tr = oracle.layer_forward(x, pos, lw, cfg, oracle.Precision(), kp, vp, mask=mask)
+    a = _plain_rmsnorm(x, cfg.rms_eps)
+    v_own = (a @ lw.wv.T).reshape(T, hkv, hd)
+    vals = np.concatenate([vp, v_own], axis=0)
+    group = hq // hkv
+    o = np.zeros((T, hq, hd))
+    for i in range(T):
+        n_vis = P + i + 1 if causal else P + T
+        for h in range(hq):
+            o[i, h] = vals[:n_vis, h // group].mean(axis=0)
+    expect = x + o.reshape(T, hq * hd) @ lw.wo.T
+    np.testing.assert_allclose(y, expect, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(tr.v, v_own, rtol=1e-12, atol=1e-12)  # the cached values carry no rotation
+
+
+def test_layer_wiring_ffn_reads_post_attention_rows_and_zero_router_picks_first_experts():
+    """Router weights zero: every logit ties at 0, so the top-k are experts
+    0 .. k-1 (ties to the lower id) with gates 1/k each.  With Wq = 0 the
+    attention half is the closed form above, so the FFN input must be the
+    RMSNorm of the rows AFTER the attention residual, and the layer output
+    x_attn + (1/k) sum_{e<k} W2_e (silu(W1_e b) * W3_e b) + shared(b)."""
+    w, cfg, ow = _tiny_setup(seed=4)
+    src = ow.layers[1]
+    d = dict(src.__dict__)
+    d["wq"] = np.zeros_like(d["wq"])
+    d["router"] = np.zeros_like(d["router"])
+    lw = oracle.LayerWeights(**d)
+    rng = np.random.default_rng(22)
+    T = 6
+    x = rng.standard_normal((T, cfg.d_model))
+    empty = np.zeros((0, cfg.n_kv_heads, cfg.head_dim))
+    y, tr = oracle.layer_forward(x, np.arange(T), lw, cfg, oracle.Precision(), empty, empty)
+    # attention half, written out
+    a = _plain_rmsnorm(x, cfg.rms_eps)
+    v = (a @ lw.wv.T).reshape(T, cfg.n_kv_heads, cfg.head_dim)
+    group = cfg.n_q_heads // cfg.n_kv_heads
+    o = np.stack([v[:, h // group].mean(axis=0) for h in range(cfg.n_q_heads)])  # [Hq, hd], every row
+    x_attn = x + np.tile(o.reshape(1, -1), (T, 1)) @ lw.wo.T
+    b = _plain_rmsnorm(x_attn, cfg.rms_eps)
+    np.testing.assert_allclose(tr.ffn_in, b, rtol=1e-12, atol=1e-12)
+    k = cfg.top_k
+    assert np.array_equal(np.sort(tr.ids, axis=1), np.tile(np.arange(k), (T, 1)))
+    np.testing.assert_allclose(tr.gates, np.full((T, k), 1.0 / k), rtol=0, atol=1e-15)
+
+    def swiglu(b, w1, w3, w2):
+        g = b @ w1.T
+        return ((g / (1.0 + np.exp(-g))) * (b @ w3.T)) @ w2.T
+
+    f = sum(swiglu(b, lw.w1[e], lw.w3[e], lw.w2[e]) for e in range(k)) / k
+    f = f + swiglu(b, lw.sw1, lw.sw3, lw.sw2)
+    np.testing.assert_allclose(y, x_attn + f, rtol=1e-11, atol=1e-12)
+
+
+def test_step_wiring_identity_layers_unscaled_embedding_and_final_norm():
+    """With every layer zeroed (each layer the identity), a denoising step's
+    entropies, log-sum-exps and argmaxes are those of softmax(rmsnorm(E[id]) E^T)
+    at the canvas ids: the embedding enters unscaled and the tied LM head reads
+    the final RMSNorm of the last layer's rows.  Written with scipy's logsumexp."""
+    w, cfg, ow = _tiny_setup(seed=5)
+    zl = [oracle.LayerWeights(**{k: (np.ones_like(v) if k.endswith("norm") else np.zeros_like(v))
+                                 for k, v in lw.__dict__.items()}) for lw in ow.layers]
+    zw = oracle.Weights(embed=ow.embed, final_norm=ow.final_norm, layers=zl)
+    st = oracle.new_request(cfg, 9, 64 + cfg.canvas_len)
+    oracle.prefill(st, synth.make_prompt(w, seed=1), cfg, zw, oracle.Precision())
+    r = oracle.denoise_step(st, cfg, oracle.SamplerConfig(tau=w.tau, max_steps=w.max_steps), zw, oracle.Precision())
+    z = _plain_rmsnorm(ow.embed[r.ids_before], cfg.rms_eps) @ ow.embed.T
+    lse = scipy.special.logsumexp(z, axis=1)
+    p = np.exp(z - lse[:, None])
+    np.testing.assert_allclose(r.lse, lse, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r.entropy, -(p * np.log(p)).sum(axis=1), rtol=1e-10, atol=1e-12)
+    assert np.array_equal(r.argmax, np.argmax(z.astype(np.float32), axis=1))
+
+
 # ------------------------------------------------- cache / commit (block mask) ----
 
 def _block_mask(n_prompt, n_blocks, c):
@@ -857,3 +964,34 @@ def test_self_cond_with_zero_mlp_weights_is_the_plain_model():
     out = oracle.generate(prompt, 256, 3, cfg, scfg, ow, oracle.Precision())
     out0 = oracle.generate(prompt, 256, 3, cfg0, scfg, ow0, oracle.Precision())
     assert np.array_equal(out[0], out0[0])
+
+
+def test_batched_step_equals_each_request_alone():
+    """Two requests denoised together (layer-major) give exactly what each gives
+    alone: their rows never mix."""
+    w, cfg, ow = _tiny_setup(seed=6)
+    scfg = oracle.SamplerConfig(tau=w.tau, max_steps=w.max_steps)
+    prompts = [synth.make_prompt(w, seed=2), synth.make_prompt(w, seed=3, length=40)]
+
+    def fresh():
+        sts = []
+        for i, p in enumerate(prompts):
+            st = oracle.new_request(cfg, 11 + i, 64 + 2 * cfg.canvas_len)
+            oracle.prefill(st, p, cfg, ow, oracle.Precision())
+            sts.append(st)
+        return sts
+
+    alone, together = fresh(), fresh()
+    for _ in range(2):
+        ra = [oracle.denoise_step(st, cfg, scfg, ow, oracle.Precision()) for st in alone]
+        rb = oracle.denoise_step_batch(together, cfg, scfg, ow, oracle.Precision())
+        for a, b in zip(ra, rb):
+            assert np.array_equal(a.entropy, b.entropy) and np.array_equal(a.ids_after, b.ids_after)
+            assert np.array_equal(a.hidden, b.hidden)
+            for ta, tb in zip(a.layers, b.layers):
+                assert np.array_equal(ta.ids, tb.ids) and np.array_equal(ta.x_attn, tb.x_attn)
+    # the trace chains: layer l + 1 starts from layer l's output
+    for l in range(cfg.n_layers - 1):
+        x_next = rb[0].layers[l + 1].x_in
+        assert x_next.shape == (cfg.canvas_len, cfg.d_model)
+    assert np.array_equal(rb[0].layers[0].x_in, ow.embed[rb[0].ids_before])
