@@ -203,33 +203,60 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
   }
 }
 
-// Two bf16 values (low half first) to two fp16 values: exact over fp16's normal
-// range (bf16 has 8 significant bits); the conversion rounds toward zero, which
-// only touches magnitudes below that range and clamps those above it to 65504.
-__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
-  return *reinterpret_cast<const uint32_t*>(&h);
+// s_waitcnt with only the vector-memory counter: wait until at most n of this
+// wave's vector loads are outstanding (n <= 63).
+#define DG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// One global_load_lds_dwordx4: lane l copies 16 bytes from g (its own address)
+// to lds + 16 l (lds wave-uniform).  Issued from an asm statement with inputs
+// only (the LDS base goes to M0), so that the compiler adds no wait of its own
+// for it: the kernel's explicit vmcnt waits and barriers order these copies
+// against the LDS reads.  The statement writes no register.
+__device__ __forceinline__ void lds_dma16(const void* g, const uint4* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(a)), "v"(g)
+               : "memory", "m0");
 }
 
-// bf16 attention with the K and V^T tiles of 32 keys staged in LDS once per
-// block and shared by its four waves (the kernel above reads them once per wave).
-// The next tile is prefetched into registers while the current one is used, and
-// written to the other of two LDS stages.  K rows are XOR-swizzled in 16-byte
-// units (key & 15, or key & 7 at head_dim 64); each V^T row holds its 32 keys in the order the score tiles
-// deliver them (lane group g of the matrix core covers keys 4g..4g+3 and
-// 16+4g..16+4g+3) and is swizzled by ((row >> 1) & 3), so every fragment read
-// is one conflict-free 16-byte LDS load.  All waves of a block walk the same
-// key tiles; the key range is cut at the largest position among the block's
-// rows when the mask is causal.
+// bf16 attention with the K and V^T tiles of 32 keys brought from HBM straight
+// into LDS by the load unit (global_load_lds: lane l of a load instruction
+// writes its 16 bytes at offset 16 l of the instruction's 1 KB destination), in
+// a ring of NST stages, so that NST - 1 tiles are in flight while one is
+// computed and no register holds a tile on its way.  The loads bypass the
+// compiler's wait bookkeeping (lds_dma16), so the loop waits for them itself: every
+// thread issues the same LT loads per tile, so "tile t has landed" is "at most
+// (NST - 2) LT of this thread's loads are outstanding" followed by one barrier,
+// which also tells every wave that the stage about to be refilled (read in the
+// previous iteration) is free.  Tiles past the end of the key range reload the
+// last tile into the free stage, so every iteration issues the same loads.
 //
-// The probabilities P enter the P V product as an fp16 high part plus an fp16
-// remainder (two products) against V converted to fp16 when its tile is staged:
-// a bf16 value has 8 significant bits, so the conversion is exact over fp16's
-// normal range; magnitudes below it keep an absolute error under 2^-25 and
-// magnitudes above 65504 are clamped to it.  A row's reference maximum moves
-// only when a tile's maximum exceeds it by more than 2^8 (so P <= 256), which
-// keeps the rescaling of the running output rare.
-template <int HD, int QT>
+// Layouts, chosen on the load side (a lane picks the source of the LDS slot it
+// writes): a K row (one key, head_dim values) holds its 16-byte segments in the
+// order s ^ kswz(key); a V^T row (one dimension, 32 keys) its four 16-byte
+// segments in the order s ^ ((d >> 2) & 3).  Both make every fragment read one
+// conflict-free 16-byte LDS load.  The score tile kt (16 keys) takes keys
+// 8 (r >> 2) + 4 kt + (r & 3) for its row r, so that lane group g of the
+// matrix core ends up holding keys 8 g .. 8 g + 7 of P: the natural order of a
+// V^T row, read as one fragment.
+//
+// P enters the P V product as a bf16 high part and a bf16 remainder (p = hi + lo
+// to 2^-18 relative), two products against the bf16 V tile: a single bf16 P
+// would carry a relative error of up to 2^-9 into the output, enough to flip the
+// output's bf16 rounding in a large share of its elements, and those flips then
+// move everything downstream of the layer.  A row's reference maximum moves only
+// when a tile's maximum exceeds it by more than 2^8 (so P <= 256), which keeps
+// the rescaling of the running output rare.
+template <int HD>
+__device__ __forceinline__ int kswz(int key) {
+  // 16 distinct values over the 16 keys of a score tile (4 bits, or 3 bits plus
+  // the key's row parity at head_dim 64, where two key rows share 256 bytes)
+  if constexpr (HD >= 128) return (key & 3) | (((key >> 3) & 3) << 2);
+  else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);
+}
+
+template <int HD, int QT, int NST>
 __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
                                                      int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
                                                      int rows_total) {
@@ -237,14 +264,28 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
   constexpr int NKK = HD / 32;
   constexpr int NHT = HD / 16;
   constexpr int KSEG = HD / 8;            // 16-byte segments per key row
-  constexpr int KSW = KSEG >= 16 ? 15 : 7;  // K-row swizzle: XOR of the segment with the key's low bits
-  constexpr int SEGS_K = 32 * KSEG;       // per tile
-  constexpr int SEGS_V = HD * 4;          // per tile (HD rows of 32 keys)
-  constexpr int NTHR = 512 / QT;         // 128 query rows per block, QT m-tiles per wave
-  constexpr int LK = SEGS_K / NTHR, LV = SEGS_V / NTHR;
-  static_assert(LK >= 1 && LV >= 1, "tile staging: head_dim too small for this wave count");
-  __shared__ uint4 sK[2][SEGS_K];
-  __shared__ uint4 sV[2][SEGS_V];
+  constexpr int NTHR = 512 / QT;          // 128 query rows per block, QT m-tiles per wave
+  constexpr int NW = NTHR / 64;
+  constexpr int KB = 32 * HD * 2;         // bytes of a K tile (= bytes of a V^T tile)
+  constexpr int KI = KB / 1024;           // 1 KB load instructions per tile and matrix
+  static_assert(KI % NW == 0, "tile loads: whole instructions per wave");
+  constexpr int LK = KI / NW;             // per wave (and thread) and matrix
+  constexpr int LT = 2 * LK;              // loads per thread per tile
+  static_assert((NST - 2) * LT <= 63, "vmcnt range");
+  // One array per stage, every stage index a compile-time constant.
+  static_assert(NST == 4, "four stages");
+  __shared__ uint4 sK0[KB / 16], sK1[KB / 16], sK2[KB / 16], sK3[KB / 16];
+  __shared__ uint4 sV0[KB / 16], sV1[KB / 16], sV2[KB / 16], sV3[KB / 16];
+  auto stK = [&](auto J) __attribute__((always_inline)) -> uint4* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return sK0; else if constexpr (j == 1) return sK1; else if constexpr (j == 2) return sK2;
+    else return sK3;
+  };
+  auto stV = [&](auto J) __attribute__((always_inline)) -> uint4* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return sV0; else if constexpr (j == 1) return sV1; else if constexpr (j == 2) return sV2;
+    else return sV3;
+  };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
 
@@ -285,6 +326,7 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
     const int max_i = (first / seg.n == last / seg.n) ? last % seg.n : seg.n - 1;
     k_hi = min(k_hi, seg.pos0 + max_i + 1);
   }
+  const int ntiles = k_hi > k_lo ? (k_hi - k_lo + 31) / 32 : 0;
 
   F qf[QT][NKK];
 #pragma unroll
@@ -298,33 +340,26 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
   const bf16_t* vbase = (const bf16_t*)seg.vt + (size_t)h * HD * sh.max_ctx;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
-  // This thread's segments of a tile.
-  auto load_tile = [&](int kb, uint4 (&rk)[LK], uint4 (&rv)[LV]) {
+  // This thread's sources for tile t (clamped to the last tile of the range;
+  // keys past the last key re-read it), written to stage (sk, sv).
+  auto issue = [&](int t, uint4* sk, uint4* sv) __attribute__((always_inline)) {
+    const int kb = k_lo + 32 * min(t, ntiles - 1);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int sid = tid + NTHR * i, key = sid / KSEG, sgi = sid % KSEG;
+      const int ins = wave * LK + i;                 // 1 KB instruction within the tile
+      const int slot = ins * 64 + lane;              // 16-byte slot of the tile in LDS
+      const int key = slot / KSEG, ps = slot % KSEG;  // physical segment of that key row
+      const int sgi = ps ^ kswz<HD>(key);
       const int gk = min(kb + key, nkeys - 1);
-      rk[i] = *(const uint4*)(kbase + (size_t)gk * HD + sgi * 8);
+      lds_dma16(kbase + (size_t)gk * HD + sgi * 8, sk + ins * 64);
     }
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int sid = tid + NTHR * i, d = sid >> 2, s4 = sid & 3;
-      rv[i] = *(const uint4*)(vbase + (size_t)d * sh.max_ctx + kb + s4 * 8);
-    }
-  };
-  auto store_tile = [&](int stg, const uint4 (&rk)[LK], const uint4 (&rv)[LV]) {
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int sid = tid + NTHR * i, key = sid / KSEG, sgi = sid % KSEG;
-      sK[stg][key * KSEG + (sgi ^ (key & KSW))] = rk[i];
-    }
-    uint2* v8 = reinterpret_cast<uint2*>(sV[stg]);
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int sid = tid + NTHR * i, d = sid >> 2, s4 = sid & 3;
-      const int kt = s4 >> 1, g0 = (s4 & 1) * 2, sw = (d >> 1) & 3;
-      v8[d * 8 + (g0 ^ sw) * 2 + kt] = make_uint2(bf2_to_h2(rv[i].x), bf2_to_h2(rv[i].y));        // keys 8 s4 .. +3
-      v8[d * 8 + ((g0 + 1) ^ sw) * 2 + kt] = make_uint2(bf2_to_h2(rv[i].z), bf2_to_h2(rv[i].w));  // keys 8 s4 + 4 .. +7
+      const int ins = wave * LK + i;
+      const int slot = ins * 64 + lane;
+      const int d = slot >> 2, ps = slot & 3;
+      const int s4 = ps ^ ((d >> 2) & 3);
+      lds_dma16(vbase + (size_t)d * sh.max_ctx + kb + s4 * 8, sv + ins * 64);
     }
   };
 
@@ -337,42 +372,30 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
     mrun[qt] = -INFINITY;
     lrun[qt] = 0.f;
   }
-
-  uint4 rk[LK], rv[LV];
-  if (k_lo < k_hi) {
-    load_tile(k_lo, rk, rv);
-    store_tile(0, rk, rv);
-  }
-  __syncthreads();
-  int stg = 0;
-  // The reference maximum of a row (mrun) moves only when a tile's maximum
-  // exceeds it by more than RESCALE_TH (log2 units): P = 2^(s - mrun) then stays
-  // at most 2^RESCALE_TH, well inside fp16, and the running output and sum are
-  // rescaled rarely instead of on almost every tile.  The split's (mrun, lrun)
-  // pair is reported with its output, so the merge stays exact.
   constexpr float RESCALE_TH = 8.f;
-  // Keys at or beyond klim[qt] are masked for row qt: the end of the range, and
-  // with a causal mask the row's own position + 1.
   int klim[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) klim[qt] = sg.causal ? min(k_hi, qpos[qt] + 1) : k_hi;
-  // One tile: scores, softmax update, P V.
-  auto tile = [&](int kb) {
-    v4f st[2][QT];
+
+  // One tile from stage (sk, sv): scores, softmax update, P V.
+  auto tile = [&](int kb, const uint4* sk, const uint4* sv) __attribute__((always_inline)) {
+    v4f sc4[2][QT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st[kt][qt] = v4f{0.f, 0.f, 0.f, 0.f};
-      const int key = kt * 16 + c16;
+      for (int qt = 0; qt < QT; ++qt) sc4[kt][qt] = v4f{0.f, 0.f, 0.f, 0.f};
+      const int key = 8 * (c16 >> 2) + 4 * kt + (c16 & 3);  // this lane's key row of score tile kt
+      const int sw = kswz<HD>(key);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const uint4 u = sK[stg][key * KSEG + ((kk * 4 + g4) ^ (key & KSW))];
+        const uint4 u = sk[key * KSEG + ((kk * 4 + g4) ^ sw)];
         const F kf = *reinterpret_cast<const F*>(&u);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          st[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][kk], st[kt][qt], 0, 0, 0);
+          sc4[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][kk], sc4[kt][qt], 0, 0, 0);
       }
     }
+    // lane (g4, c16) holds, for query column c16, keys 8 g4 + 4 kt + i
     float p[2][QT][4];
     bool grow = false;
     float alpha[QT];
@@ -383,21 +406,18 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kb + kt * 16 + g4 * 4 + i;
-          const float sc = key < klim[qt] ? st[kt][qt][i] * scale : -INFINITY;
-          p[kt][qt][i] = sc;
-          tmax = fmaxf(tmax, sc);
+          const int key = kb + 8 * g4 + 4 * kt + i;
+          const float sv = key < klim[qt] ? sc4[kt][qt][i] * scale : -INFINITY;
+          p[kt][qt][i] = sv;
+          tmax = fmaxf(tmax, sv);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      // a row's reference moves to its tile maximum when that exceeds it by more
-      // than the threshold (always on the row's first unmasked tile)
       const bool move = tmax > mrun[qt] + RESCALE_TH;
       const float mnew = move ? tmax : mrun[qt];
       alpha[qt] = move ? __builtin_amdgcn_exp2f(mrun[qt] - mnew) : 1.f;  // 2^-inf = 0 on the first move
       grow |= move;
       mrun[qt] = mnew;
-      // rows with every score masked so far keep mrun = -inf: their P is 0
       const float mref = mnew == -INFINITY ? 0.f : mnew;
       float psum = 0.f;
 #pragma unroll
@@ -416,12 +436,7 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) oacc[ht][qt] *= alpha[qt];
     }
-    // P enters the matrix cores as an fp16 high part and an fp16 remainder
-    // (p = hi + lo to about 2^-22 relative), two products against the same V
-    // tile: one fp16 P would carry a relative error of up to 2^-12 into the
-    // output, enough to flip the output's bf16 rounding in about one element in
-    // eight, and those flips then move everything downstream of the layer.
-    v8h pf[QT], pl[QT];
+    F pf[QT], pl[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -429,35 +444,58 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = p[kt][qt][i];
-          const _Float16 hi = (_Float16)v;
-          pf[qt][kt * 4 + i] = hi;
-          pl[qt][kt * 4 + i] = (_Float16)(v - (float)hi);
+          const bf16_t hi = f2bf(v);
+          pf[qt][kt * 4 + i] = (short)hi;
+          pl[qt][kt * 4 + i] = (short)f2bf(v - bf2f(hi));
         }
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int d = ht * 16 + c16;
-      const uint4 u = sV[stg][d * 4 + (g4 ^ ((d >> 1) & 3))];
-      const v8h vf = *reinterpret_cast<const v8h*>(&u);
+      const uint4 u = sv[d * 4 + (g4 ^ ((d >> 2) & 3))];
+      const F vf = *reinterpret_cast<const F*>(&u);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qt], oacc[ht][qt], 0, 0, 0);
-        oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], oacc[ht][qt], 0, 0, 0);
+        oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], oacc[ht][qt], 0, 0, 0);
+        oacc[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qt], oacc[ht][qt], 0, 0, 0);
       }
     }
   };
-  for (int kb = k_lo; kb < k_hi; kb += 32) {
-    const bool more = kb + 32 < k_hi;
-    load_tile(more ? kb + 32 : kb, rk, rv);
-    if (wave_active) tile(kb);
-    store_tile(stg ^ 1, rk, rv);
-    __syncthreads();
-    stg ^= 1;
+
+  if (ntiles > 0) {
+    // The query fragments must have landed before the ring starts: the
+    // compiler's own wait for them would otherwise sit inside the loop, where
+    // (not knowing of the ring's loads) it would drain the ring every tile.
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[qt][kk]));
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    issue(0, stK(I0{}), stV(I0{}));
+    issue(1, stK(I1{}), stV(I1{}));
+    issue(2, stK(I2{}), stV(I2{}));
+    // Tile t sits in stage t % 4; its step refills stage (t + 3) % 4, read by
+    // the step before (every wave has passed the barrier since).
+    auto step = [&](int t, auto J, auto JN) __attribute__((always_inline)) {
+      if (t >= ntiles) return;        // block-uniform
+      DG_WAIT_VMCNT((NST - 2) * LT);  // this thread's loads of tile t have landed
+      __builtin_amdgcn_s_barrier();   // ... everyone's, and stage (t + 3) % 4 is free
+      issue(t + NST - 1, stK(JN), stV(JN));
+      if (wave_active) tile(k_lo + 32 * t, stK(J), stV(J));
+    };
+    for (int t0 = 0; t0 < ntiles; t0 += 4) {
+      step(t0, I0{}, I3{});
+      step(t0 + 1, I1{}, I0{});
+      step(t0 + 2, I2{}, I1{});
+      step(t0 + 3, I3{}, I2{});
+    }
+    DG_WAIT_VMCNT(0);  // the tail reloads have landed before the block leaves
   }
   if (!wave_active) return;
   // The split's output leaves normalised (O / l, at most max |v| in size) in
-  // fp32: an fp16 copy would add a 2^-12 relative error ahead of the output's
-  // bf16 rounding (see the P product above).  The merge weighs it by
-  // l 2^(m - M).
+  // fp32; the merge weighs it by l 2^(m - M).
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     lrun[qt] += __shfl_xor(lrun[qt], 16, 64);
@@ -560,12 +598,16 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #define DG_ATTN(TT, HDV)                                                                                     \
   k_attn<TT, HDV><<<blocks, 256, 0, s>>>((const TT*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);         \
   k_attn_merge<TT, sizeof(TT) == 2><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV, (TT*)o)
+// LDS stages of the tile ring (NST - 1 tiles in flight): 4 x 32 KB at head_dim 256.
+#ifndef DG_ATTN_NST
+#define DG_ATTN_NST 4
+#endif
 // m-tiles (16 query rows) per wave: one at head_dim >= 128 (eight waves, two per
 // SIMD, half the registers each), two at 64 (the tile staging needs 256 threads)
 #define DG_ATTN_QT(HDV) ((HDV) >= 128 ? 1 : 2)
 #define DG_ATTN_LDS(HDV)                                                                                    \
-  k_attn_lds<HDV, DG_ATTN_QT(HDV)><<<blocks, 512 / DG_ATTN_QT(HDV), 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit,    \
-                                                                           opart, mlpart, rows);                   \
+  k_attn_lds<HDV, DG_ATTN_QT(HDV), DG_ATTN_NST><<<blocks, 512 / DG_ATTN_QT(HDV), 0, s>>>(                            \
+      (const bf16_t*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);                                                \
   k_attn_merge<bf16_t, true, float, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV,     \
                                                                        (bf16_t*)o)
   if (dtype == 1) {

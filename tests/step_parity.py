@@ -19,12 +19,18 @@ Two comparisons per step (the design doc lists the bands and why):
     the oracle's k-th - (k+1)-th router logit gap is below GAP (1e-3), gates
     within GATE_TOL, each half's update within RL2 relative L2 per row;
   * free_running(): the library's own dg_denoise_step against the oracle's
-    step, with the per-layer rows read back through the debug taps: routing
-    differences only where the oracle's gap is below STEP_GAP, hidden rows and
-    logits within RL2 per row, entropies within H_TOL, argmax equal except where
-    the oracle's top-1 - top-2 logit gap is below STEP_GAP, the accepted
-    position the oracle's except where its two lowest open entropies lie within
-    2 H_TOL, accepted tokens and Philox re-draws exact.
+    step, with the per-layer rows read back through the debug taps.  Every bf16
+    rounding point turns a sub-ulp difference upstream into whole-ulp flips in a
+    few elements, so over many layers two correct bf16 implementations drift
+    apart by about an ulp; the bands are therefore the oracle's own spread
+    (oracle_spread: the bf16 model against exact arithmetic), never a measure
+    of the library's error: routing differences only at gaps no wider than the
+    widest the two oracles decide differently in that layer, hidden rows and
+    logits within the oracles' median and largest spread, entropies within the
+    entropy spread, argmax equal except at gaps no wider than the widest the two
+    oracles decide differently, the accepted position the oracle's except where
+    its two lowest open entropies lie within twice the entropy band; accepted
+    tokens and Philox re-draws exact.
 """
 import numpy as np
 import torch
@@ -36,11 +42,65 @@ from tests import helpers
 from tests.gpu_common import log, rel_l2, topk_gap
 
 GAP = 1e-3        # routing / argmax band where both sides see the same input
-STEP_GAP = 1e-2   # the same decisions inside a free-running step
-RL2 = 1e-2        # bf16: relative L2 per row
-GATE_TOL = 1e-4   # teacher-forced gates (same input, fp32 softmax of fp32 logits)
-H_TOL = 1e-3      # nats, entropies of a free-running bf16 step
-MAX_FLIP_FRAC = 0.02  # routing differences per layer in a free-running step, at most this share of rows
+RL2 = 1e-2        # bf16: relative L2 per row (updates of a layer half, logits)
+GATE_TOL = 1e-3   # teacher-forced gates: with equal inputs the router logits differ only where the fp32
+                  # norm rounds an element of the normalised row to the other bf16 neighbour
+H_TOL = 1e-3      # nats: entropy floor of the free-running bands
+# Free-running bands are SPREAD_MARGIN times the oracle spread: the library's
+# step and the bf16 oracle differ by a rounding-flip process of the same kind as
+# the one that separates the bf16 model from exact arithmetic, started by smaller
+# differences (measured 0.6 - 0.9 times the spread at the mid shape), so twice
+# the spread bounds it without following the library's own error.
+SPREAD_MARGIN = 2.0
+
+
+def oracle_spread(results, plain_results, k):
+    """How far the bf16 model itself (the oracle with its bf16 rounding points)
+    lies from exact arithmetic (the oracle without them) on the same step.
+    Oracle values only.  A free-running bf16 step is held to these: it may not
+    stray further from the bf16 model than the bf16 model strays from exact
+    arithmetic.  Per layer: the largest router gap that the two oracles decide
+    differently (the bf16 rounding can overturn gaps that wide), and the median
+    and largest relative L2 of the rows entering the layer, over the rows both
+    oracles have routed alike so far; at the end the same for the final rows
+    and the logits, the largest entropy difference, and the largest top-1 -
+    top-2 logit gap whose argmax the two oracles decide differently on such rows.
+    The router gaps are an envelope: the widest gap overturned in layers 0..l."""
+    L = len(results[0].layers)
+    sp = {"router_gap": np.zeros(L), "hidden_med": np.zeros(L + 1), "hidden_max": np.zeros(L + 1),
+          "router_flips": np.zeros(L, dtype=int)}
+    fin = dict(logit_med=0.0, logit_max=0.0, entropy=0.0, argmax_gap=0.0, argmax_flips=0)
+    hid = [[] for _ in range(L + 1)]
+    logit_e = []
+    for r, q in zip(results, plain_results):
+        C = len(r.hidden)
+        alike = np.ones(C, dtype=bool)
+        for l in range(L):
+            a, b = r.layers[l], q.layers[l]
+            hid[l].extend(rel_l2(a.x_in[t], b.x_in[t]) for t in np.nonzero(alike)[0])
+            gap = topk_gap(a.router_logits.astype(np.float32), k)
+            for t in range(C):
+                if alike[t] and set(a.ids[t].tolist()) != set(b.ids[t].tolist()):
+                    sp["router_gap"][l] = max(sp["router_gap"][l], float(gap[t]))
+                    sp["router_flips"][l] += 1
+                    alike[t] = False
+        hid[L].extend(rel_l2(r.hidden[t], q.hidden[t]) for t in np.nonzero(alike)[0])
+        open_ = ~r.accepted_before
+        logit_e.extend(rel_l2(r.logits[t], q.logits[t]) for t in np.nonzero(open_ & alike)[0])
+        fin["entropy"] = max(fin["entropy"], float(np.max(np.abs(r.entropy - q.entropy)[open_])))
+        lgap = topk_gap(r.logits.astype(np.float32), 1)
+        for t in np.nonzero(open_ & alike & (r.argmax != q.argmax))[0]:
+            fin["argmax_gap"] = max(fin["argmax_gap"], float(lgap[t]))
+            fin["argmax_flips"] += 1
+    for l in range(L + 1):
+        if hid[l]:
+            sp["hidden_med"][l], sp["hidden_max"][l] = float(np.median(hid[l])), float(np.max(hid[l]))
+    # the gaps the bf16 rounding overturns within the first l + 1 layers
+    sp["router_gap"] = np.maximum.accumulate(sp["router_gap"])
+    if logit_e:
+        fin["logit_med"], fin["logit_max"] = float(np.median(logit_e)), float(np.max(logit_e))
+    sp.update(fin)
+    return sp
 
 
 def _f64(t):
@@ -200,10 +260,10 @@ def teacher_forced(dec, w, reqs, results, Ps, stats):
                                                           max(stats["attn_rl2"]), max(stats["moe_rl2"])))
 
 
-def free_running(dec, w, reqs, results, states_before, stats, plain_results=None, n_logit_rows=8):
+def free_running(dec, w, reqs, results, states_before, stats, spread, plain_results=None, n_logit_rows=8):
     """The library's own last dg_denoise_step (run with the tap buffer set)
-    against the oracle's step from the same state.  Every measure is logged
-    before any is asserted."""
+    against the oracle's step from the same state, with the bands of `spread`
+    (oracle_spread).  Every measure is logged before any is asserted."""
     C, k, L = w.canvas_len, w.top_k, w.n_layers
     rows = dec.dg_last_step_rows()
     n_rows = rows["rows"]
@@ -214,6 +274,7 @@ def free_running(dec, w, reqs, results, states_before, stats, plain_results=None
     layer_err, flip_gaps, bad = [], [], []
     for l in range(L):
         n_flip, errs, dr = 0, [], 0.0
+        band = max(GAP, SPREAD_MARGIN * spread["router_gap"][l])
         for i, r in enumerate(results):
             tr = r.layers[l]
             sl = slice(i * C, (i + 1) * C)
@@ -227,20 +288,22 @@ def free_running(dec, w, reqs, results, states_before, stats, plain_results=None
                 dr = max(dr, float(np.max(np.abs(rlog[l][row] - tr.router_logits[t]))))
                 if set(rows["router_ids"][l][row].tolist()) != set(tr.ids[t].tolist()):
                     flip_gaps.append(float(gap[t]))
-                    if gap[t] >= STEP_GAP:
-                        bad.append(("router set differs outside the step band", l, i, t, float(gap[t])))
+                    if gap[t] >= band:
+                        bad.append(("router set differs outside the band", l, i, t, float(gap[t]), band))
                     flipped[row] = True
                     n_flip += 1
-        if n_flip > MAX_FLIP_FRAC * n_rows:
-            bad.append(("too many routing differences", l, n_flip))
-        if max(errs) > RL2:
-            bad.append(("hidden rows entering layer", l, max(errs)))
-        layer_err.append((float(np.median(errs)), float(max(errs)), n_flip, dr))
+        if (np.median(errs) > max(RL2, SPREAD_MARGIN * spread["hidden_med"][l])
+                or max(errs) > max(RL2, SPREAD_MARGIN * spread["hidden_max"][l])):
+            bad.append(("hidden rows entering layer", l, float(np.median(errs)), max(errs),
+                        spread["hidden_med"][l], spread["hidden_max"][l]))
+        layer_err.append((float(np.median(errs)), float(max(errs)), spread["hidden_med"][l], spread["hidden_max"][l],
+                          n_flip, int(spread["router_flips"][l]), dr, band))
     stats["layer_err"] = layer_err
     stats["flip_gaps"] = sorted(flip_gaps)
     for l in range(L):
-        log("  free-running layer %2d: hidden rel L2 median %.2e max %.2e; routing differences %d; "
-            "max |router logit diff| on agreeing rows %.2e" % ((l,) + layer_err[l]))
+        log("  free-running layer %2d: hidden rel L2 median %.2e max %.2e (oracle spread %.2e / %.2e); routing "
+            "differences %d (oracle vs oracle %d); router logits max diff %.2e; routing band %.1e"
+            % ((l,) + layer_err[l]))
     log("  free-running: rows with a routing difference in some layer: %d of %d; their oracle gaps %s"
         % (flipped.sum(), n_rows, ["%.1e" % g for g in stats["flip_gaps"]]))
     # final rows, entropies, argmax, sampler, canvas
@@ -251,20 +314,22 @@ def free_running(dec, w, reqs, results, states_before, stats, plain_results=None
         open_b = ~r.accepted_before
         cmp = open_b & ~flipped[sl]
         e_fin = [rel_l2(fin[sl][t], r.hidden[t]) for t in np.nonzero(~flipped[sl])[0]]
-        if max(e_fin) > RL2:
-            bad.append(("final rows", i, max(e_fin)))
+        if max(e_fin) > max(RL2, SPREAD_MARGIN * spread["hidden_max"][L]):
+            bad.append(("final rows", i, max(e_fin), spread["hidden_max"][L]))
         Hg = rows["entropy"][sl].astype(np.float64)
         dH = np.abs(Hg - r.entropy)[cmp]
         stats.setdefault("dH_max", []).append(float(dH.max()))
         stats.setdefault("dH_median", []).append(float(np.median(dH)))
-        if dH.max() > H_TOL:
-            bad.append(("entropy", i, float(dH.max())))
+        h_band = max(H_TOL, SPREAD_MARGIN * spread["entropy"])
+        if dH.max() > h_band:
+            bad.append(("entropy", i, float(dH.max()), h_band))
         am_g = rows["argmax"][sl]
         lgap = topk_gap(r.logits.astype(np.float32), 1)
         diff = np.nonzero(cmp & (am_g != r.argmax))[0]
+        z_band = max(GAP, SPREAD_MARGIN * spread["argmax_gap"])
         for t in diff:
-            if lgap[t] >= STEP_GAP:
-                bad.append(("argmax differs outside the step band", i, int(t), float(lgap[t])))
+            if lgap[t] >= z_band:
+                bad.append(("argmax differs outside the band", i, int(t), float(lgap[t]), z_band))
         stats.setdefault("argmax_diff_gaps", []).extend(float(lgap[t]) for t in diff)
         # the sampler: the GPU's choice is the rule on its own entropies; the
         # oracle's choice may differ only between near-equal lowest entropies
@@ -279,7 +344,7 @@ def free_running(dec, w, reqs, results, states_before, stats, plain_results=None
         h_sorted = np.sort(r.entropy[open_b])
         stats.setdefault("lowest_two_gap", []).append(float(h_sorted[1] - h_sorted[0]))
         if not np.array_equal(newly_o, take_g):
-            near = h_sorted[1] - h_sorted[0] < 2 * H_TOL
+            near = h_sorted[1] - h_sorted[0] < 2 * h_band
             involved = np.nonzero(newly_o != take_g)[0]
             if not (near or flipped[sl][involved].any()):
                 bad.append(("accepted position differs", i, float(h_sorted[1] - h_sorted[0])))
@@ -287,7 +352,7 @@ def free_running(dec, w, reqs, results, states_before, stats, plain_results=None
         else:
             for t in np.nonzero(newly_o)[0]:
                 assert ids_g[t] == am_g[t]
-                if ids_g[t] != r.ids_after[t] and not (lgap[t] < STEP_GAP or flipped[sl][t]):
+                if ids_g[t] != r.ids_after[t] and not (lgap[t] < z_band or flipped[sl][t]):
                     bad.append(("accepted token differs", i, int(t)))
         still = ~acc_g
         st = states_before[i]
@@ -300,17 +365,20 @@ def free_running(dec, w, reqs, results, states_before, stats, plain_results=None
         lg = dec.dg_last_step_logits(pick + i * C).cpu().numpy().astype(np.float64)
         el = [rel_l2(lg[n], r.logits[t]) for n, t in enumerate(pick)]
         stats.setdefault("logit_rl2", []).append(float(max(el)))
-        if max(el) > RL2:
-            bad.append(("logits", i, max(el)))
+        if max(el) > max(RL2, SPREAD_MARGIN * spread["logit_max"]):
+            bad.append(("logits", i, max(el), spread["logit_max"]))
         if plain_results is not None:
             pr = plain_results[i]
             ep = [rel_l2(lg[n], pr.logits[t]) for n, t in enumerate(pick)]
             stats.setdefault("logit_rl2_plain", []).append(float(max(ep)))
             stats.setdefault("dH_plain_max", []).append(float(np.max(np.abs(Hg - pr.entropy)[cmp])))
-    log("  free-running: |dH| max %.2e median %.2e; argmax differences at oracle gaps %s; accept differences %s "
-        "(lowest-two entropy gaps %s); logits rel L2 %.2e%s"
-        % (max(stats["dH_max"]), max(stats["dH_median"]), stats["argmax_diff_gaps"], stats.get("accept_diffs", []),
-           ["%.1e" % g for g in stats["lowest_two_gap"]], max(stats["logit_rl2"]),
+    log("  free-running: |dH| max %.2e median %.2e (oracle spread %.2e); argmax differences at oracle gaps %s "
+        "(band %.1e, oracle-vs-oracle differences %d); accept differences %s (lowest-two entropy gaps %s); logits "
+        "rel L2 %.2e (oracle spread median %.2e max %.2e)%s"
+        % (max(stats["dH_max"]), max(stats["dH_median"]), spread["entropy"], stats["argmax_diff_gaps"],
+           max(GAP, SPREAD_MARGIN * spread["argmax_gap"]), spread["argmax_flips"], stats.get("accept_diffs", []),
+           ["%.1e" % g for g in stats["lowest_two_gap"]], max(stats["logit_rl2"]), spread["logit_med"],
+           spread["logit_max"],
            "" if plain_results is None else
            " (against the plain-arithmetic oracle: logits %.2e, |dH| max %.2e)"
            % (max(stats["logit_rl2_plain"]), max(stats["dH_plain_max"]))))

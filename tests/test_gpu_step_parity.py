@@ -24,7 +24,9 @@ from tests.gpu_common import log, make_decoder
 pytestmark = pytest.mark.gpu
 
 
-def _run(wname, P, n_req, plain=False, logit_rows=8):
+def _run(wname, P, n_req, spread=None, logit_rows=8):
+    """One step of the workload on both sides.  spread: the free-running bands;
+    None computes them on this step with a second, plain-arithmetic oracle run."""
     w = synth.WORKLOADS[wname]
     log("%s: generating the model on the GPU (%d requests, %d-row prefixes)" % (wname, n_req, P))
     tw = synth.make_weights(w, seed=0, device="cuda")
@@ -46,17 +48,23 @@ def _run(wname, P, n_req, plain=False, logit_rows=8):
     states = [sp.oracle_request(w, P, 100 + r, seeds[r]) for r in range(n_req)]
     results = oracle.denoise_step_batch(states, ocfg, scfg, ow, prec, keep_logits=True)
     plain_results = None
-    if plain:
+    if spread is None:
         log("%s: plain-arithmetic oracle step" % wname)
         pst = [sp.oracle_request(w, P, 100 + r, seeds[r]) for r in range(n_req)]
         plain_results = oracle.denoise_step_batch(pst, ocfg, scfg, sp.oracle_weights(tw), oracle.Precision(False),
                                                   keep_logits=True)
+        spread = sp.oracle_spread(results, plain_results, w.top_k)
+        log("%s: oracle spread (bf16 model vs exact arithmetic): routing differences per layer %s, widest gap decided "
+            "differently %s; logits rel L2 median %.2e max %.2e; entropy %.2e; argmax differences %d (widest gap %.1e)"
+            % (wname, spread["router_flips"].tolist(), ["%.1e" % v for v in spread["router_gap"]], spread["logit_med"],
+               spread["logit_max"], spread["entropy"], spread["argmax_flips"], spread["argmax_gap"]))
     stats = {}
     # the free-running comparison reads the step's own taps and canvas first; the
     # teacher-forced ops then overwrite the canvas rows' cache entries
     err = None
     try:
-        sp.free_running(dec, w, list(range(n_req)), results, before, stats, plain_results, n_logit_rows=logit_rows)
+        sp.free_running(dec, w, list(range(n_req)), results, before, stats, spread, plain_results,
+                        n_logit_rows=logit_rows)
     except AssertionError as e:  # report after the teacher-forced check has run too
         err = e
     log("%s: teacher-forced layers" % wname)
@@ -66,19 +74,20 @@ def _run(wname, P, n_req, plain=False, logit_rows=8):
     dec.close()
     del tw
     torch.cuda.empty_cache()
+    stats["spread"] = spread
     return stats
 
 
 def test_mid_step_parity():
     """The mid-size model (8 layers, 32 experts top-4) over a 1024-row prefix."""
-    st = _run("mid", 1024, 1, plain=True)
+    st = _run("mid", 1024, 1)
     log("mid: %s" % {k: v for k, v in st.items() if k != "layer_err"})
 
 
 @pytest.mark.timeout(900)
 def test_full_step_parity_one_canvas():
     """The 4096-in workload: one canvas over a 4096-row prefix, all 30 layers."""
-    st = _run("full", 4096, 1, plain=True)
+    st = _run("full", 4096, 1)
     log("full: %s" % {k: v for k, v in st.items() if k != "layer_err"})
 
 
