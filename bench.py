@@ -21,8 +21,9 @@ The JSON line carries:
                kernel source (profiles/ws_hbm_traffic.md), null once it changed;
   step_roofline  the whole step: algorithmic bytes and FLOPs per step against
                max(bytes / 8 TB/s, FLOPs / 2.5 PFLOP/s);
-  cpu_baseline the CPU oracle on a bounded sample (one layer + LM head),
-               scaled to a whole step.
+  cpu_baseline the float64 oracle timed on the first step(s) of block 0 at full
+               size (all layers, LM head, sampler; optionally the commit),
+               with its BLAS thread count and the host's nproc / lscpu.
 """
 import argparse
 import json
@@ -131,54 +132,79 @@ def measured_traffic(w):
     return int(fields[key])
 
 
-def cpu_baseline(w, tokens_per_step):
-    """Time the CPU oracle on a bounded sample of one denoising step of the same
-    workload: layer 0 at its real shapes (256 canvas rows over a prompt-length KV
-    prefix) and the LM head over 128 rows (the mean number of open rows of a
-    block), scaled to n_layers layers."""
+def host_cpu():
+    """nproc and lscpu's model, sockets, cores and threads of this host."""
+    import subprocess
+    info = {"nproc": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        keys = {"Model name": "model", "Socket(s)": "sockets", "Core(s) per socket": "cores_per_socket",
+                "Thread(s) per core": "threads_per_core", "CPU(s)": "cpus"}
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in keys:
+                info[keys[k.strip()]] = v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return info
+
+
+def cpu_baseline(w, tw, n_steps=1, commit=False):
+    """Time the float64 oracle (numpy) on real denoising steps of the same
+    workload: the first n_steps steps of block 0 of one request -- each through
+    every layer, the LM head over the open rows and the sampler -- and, with
+    commit, the block commit's forward after them.  The request's committed prefix is
+    prompt_len rows of synthetic keys and values (synth.make_prefix_kv; the
+    oracle's own prefill of the prompt would take many times longer than the
+    steps).  The oracle reads the model's weights from the GPU one layer at a
+    time as float64 (oracle.stream): those copies are inside the timed region,
+    the embedding's is not."""
     import numpy as np
     import threadpoolctl
     import oracle
+    from oracle import stream
     from block_diffusion_decoding_dg_amd import synth
 
-    import torch
-    # The seeded generator runs on the GPU when there is one (much faster than
-    # torch's CPU generator); the values are copied to host memory for the oracle.
-    dev = "cuda" if torch.cuda.is_available() else "cpu"
-    tw = synth.make_weights(w, seed=0, device=dev, layers=[0])
-
-    def f64(t):
-        return t.float().cpu().numpy().astype(np.float64)
-
     cfg = oracle.ModelConfig(**w.model_dict())
-    lw = oracle.LayerWeights(**{k: f64(v) for k, v in tw["layers"][0].items()})
-    embed = f64(tw["embed"])
-    fnorm = f64(tw["final_norm"])
-    del tw
+    scfg = oracle.SamplerConfig(tau=w.tau, max_steps=w.max_steps)
     prec = oracle.Precision(bf16_points=(w.dtype == "bf16"))
-    C = w.canvas_len
     P = w.prompt_len
-    rng = np.random.default_rng(1)
-    kpre = rng.standard_normal((P, w.n_kv_heads, w.head_dim))
-    vpre = rng.standard_normal((P, w.n_kv_heads, w.head_dim))
-    ids = rng.integers(0, w.vocab, C)
-    x = embed[ids]
-    pos = P + np.arange(C)
-    n_open = C // 2
+    ow = stream.lazy_weights(tw)
+    st = stream.request_with_prefix(w.n_layers, P, w.canvas_len,
+                                    lambda l: synth.make_prefix_kv(w, P, l, seed=1, device=tw["embed"].device),
+                                    seed=0)
     info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    tokens, per_step, commit_s = 0, [], None
     t0 = time.perf_counter()
-    h, _ = oracle.layer_forward(x, pos, lw, cfg, prec, kpre, vpre)
-    t1 = time.perf_counter()
-    oracle.lm_head_stats(h[:n_open], embed, fnorm, cfg, prec)
-    t2 = time.perf_counter()
-    step_s = w.n_layers * (t1 - t0) + (t2 - t1)
-    return {"value": tokens_per_step / step_s, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": ("float64 numpy oracle, one layer (256 canvas rows over a %d-row KV prefix) timed at "
-                       "%.2f s and the LM head over %d rows at %.2f s, scaled to %d layers: %.1f s per step, "
-                       "at the GPU's %.2f tokens per step" % (P, t1 - t0, n_open, t2 - t1, w.n_layers, step_s,
-                                                              tokens_per_step)),
-            "ms_per_step": step_s * 1e3}
+    for _ in range(n_steps):
+        ts = time.perf_counter()
+        r = oracle.denoise_step(st, cfg, scfg, ow, prec)
+        per_step.append(time.perf_counter() - ts)
+        tokens += int(np.sum(r.accepted_after & ~r.accepted_before))
+        if r.done:
+            break
+    if commit:
+        # the commit's forward (every layer's K/V over the canvas, kv only); the
+        # canvas is not finished after a few steps, so it runs over the canvas
+        # as it stands, which costs the same
+        from oracle.decode import canvas_forward
+        tc = time.perf_counter()
+        canvas_forward(st, cfg, ow, prec, for_commit=True)
+        commit_s = time.perf_counter() - tc
+    elapsed = time.perf_counter() - t0
+    host = host_cpu()
+    return {"value": tokens / elapsed, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": ("float64 numpy oracle, the first %d step(s) of block 0%s of one request over a %d-row "
+                       "synthetic KV prefix, every layer at full size (weights copied from the GPU layer by layer "
+                       "inside the timed region): %.1f s per step%s, %d tokens accepted in %.1f s; %d BLAS threads "
+                       "on a host with nproc %s (%s, %s socket(s) x %s cores x %s threads)"
+                       % (len(per_step), " and the block commit" if commit else "", P,
+                          float(np.mean(per_step)), "" if commit_s is None else ", commit %.1f s" % commit_s,
+                          tokens, elapsed, threads, host.get("nproc"), host.get("model", "?"),
+                          host.get("sockets", "?"), host.get("cores_per_socket", "?"),
+                          host.get("threads_per_core", "?"))),
+            "ms_per_step": float(np.mean(per_step)) * 1e3, "host": host}
 
 
 def describe(w, K):
@@ -289,10 +315,13 @@ def timed_run(w, tw, K, W, kernel, seed, log):
     return {
         "value": tokens / elapsed, "ms_per_step": ms_per_step, "tokens_per_step": tokens / K,
         "commits": commits, "prefill_ms": prefill_ms,
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"scope": "one kernel: the step's dominant launch (routed-expert W1/W3 projection, one per "
+                              "layer); the whole step's fraction is step_roofline.frac",
+                     "bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
                      "launch_ms": launch_ms, "launches": kt_n, "bytes_per_launch": bpl},
-        "step_roofline": {"bytes_per_step": mean_bytes, "flops_per_step": mean_flops,
+        "step_roofline": {"scope": "the whole denoising step against max(bytes / 8 TB/s, FLOPs / 2.5 PFLOP/s)",
+                          "bytes_per_step": mean_bytes, "flops_per_step": mean_flops,
                           "roofline_ms": roof_ms, "frac": roof_ms / ms_per_step,
                           "touched_experts_per_layer": sum(touched) / len(touched),
                           "touched_sampled_steps": len(touched_samples)},
@@ -307,6 +336,9 @@ def main():
     ap.add_argument("--workload", default="full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", default=DOMINANT, help="kernel family timed with HIP events")
+    ap.add_argument("--cpu-steps", type=int, default=1,
+                    help="denoising steps of block 0 the CPU oracle baseline times (about 20 s each at full size)")
+    ap.add_argument("--cpu-commit", action="store_true", help="the CPU oracle baseline also times the block commit")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--fp8-steps", type=int, default=256,
                     help="steps timed again with the routed experts in FP8 (full workload only; 0 = skip)")
@@ -419,10 +451,8 @@ def main():
         del tsc
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("bench: CPU oracle baseline")
-        del tw
-        torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(w, res["tokens_per_step"])
+        log("bench: CPU oracle baseline (%d step(s)%s)" % (args.cpu_steps, " and a commit" if args.cpu_commit else ""))
+        out["cpu_baseline"] = cpu_baseline(w, tw, args.cpu_steps, args.cpu_commit)
     print(json.dumps(out), flush=True)
 
 

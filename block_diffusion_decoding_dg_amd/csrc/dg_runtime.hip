@@ -184,11 +184,20 @@ dg_status fail(dg_ctx* c, dg_status st, const char* fmt, ...) {
   do {                                                                                                 \
     hipError_t e_ = (ctx)->sticky != hipSuccess ? (ctx)->sticky : hipGetLastError();                  \
     (ctx)->sticky = hipSuccess;                                                                        \
-    const char* r_ = (ctx)->refused;                                                                   \
-    (ctx)->refused = nullptr;                                                                          \
-    if (e_ != hipSuccess) return fail((ctx), DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
-    if (r_) return fail((ctx), DG_ERR_UNSUPPORTED, "launch refused: %s", r_);                         \
+    if (e_ != hipSuccess) {                                                                            \
+      (ctx)->refused = nullptr;                                                                        \
+      return fail((ctx), DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_));                     \
+    }                                                                                                  \
+    const dg_status r_ = take_refusal(ctx);                                                            \
+    if (r_ != DG_OK) return r_;                                                                        \
   } while (0)
+// The refusal half of LAUNCHCK (host only): a launcher's -1, recorded by
+// REFUSE_IF, becomes DG_ERR_UNSUPPORTED with the launch's name.
+dg_status take_refusal(dg_ctx* c) {
+  const char* r = c->refused;
+  c->refused = nullptr;
+  return r ? fail(c, DG_ERR_UNSUPPORTED, "launch refused: %s", r) : DG_OK;
+}
 // A launcher that returned -1 queued nothing: the entry point reports
 // DG_ERR_UNSUPPORTED at its next LAUNCHCK (later launches of the same call may
 // still be queued; their results are not used).
@@ -1222,6 +1231,77 @@ dg_status dg_last_step_router_logits(dg_ctx* c, float* logits) {
                             hipMemcpyDeviceToHost, c->stream));
   HIPCK(c, hipStreamSynchronize(c->stream));
   return DG_OK;
+}
+
+// Each launcher's refusal path, reached on the host alone: the launcher is
+// called with arguments it must refuse, which it does before any HIP call, and
+// its -1 goes through REFUSE_IF and the refusal half of LAUNCHCK.
+int32_t dg_debug_refusal_count(void) { return 11; }
+
+dg_status dg_debug_refusal_case(int32_t i, char* msg, size_t msg_bytes) {
+  if (i < 0 || i >= dg_debug_refusal_count()) return DG_ERR_INVALID_ARG;
+  dg_ctx c;  // host-only stub: no stream, no device buffers
+  c.cfg.d_model = 64;
+  c.cfg.n_experts = 8;
+  c.cfg.top_k = 2;
+  c.rows_cap = 16;
+  c.dtype = (i < 3) ? DG_F32 : DG_BF16;
+  static int32_t dummy;  // a non-null work-list pointer the host never dereferences
+  WsArgs a;
+  memset(&a, 0, sizeof a);
+  a.K = 96;
+  a.N = 64;
+  a.M = 16;
+  DgParts parts;
+  parts.n = 2;
+  switch (i) {
+    case 0: launch_dense(&c, WS_EPI_STORE_BF16, nullptr, 16, 64, nullptr, nullptr, 64, nullptr, 64); break;
+    case 1: launch_dense_add(&c, nullptr, 16, 64, nullptr, 64, nullptr); break;
+    case 2:
+      launch_routed(&c, WS_EPI_SWIGLU, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 64, 64,
+                    nullptr, nullptr, 2, nullptr, 64);
+      break;
+    case 3:  // an epilogue the dense kernel does not have
+      launch_dense(&c, 99, nullptr, 16, 64, nullptr, nullptr, 64, nullptr, 64);
+      break;
+    case 4:  // a routed launch that neither gathers for SwiGLU nor stores fp32 rows
+      c.counts = &dummy;
+      launch_routed(&c, WS_EPI_ROPE_QKV, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 64, 64,
+                    &dummy, &dummy, 2, nullptr, 64, &dummy);
+      break;
+    case 5:  // MXFP4 weights with K not a multiple of 64
+      a.counts = &dummy;
+      a.wfmt = DG_WS_W_MXFP4;
+      REFUSE_IF(&c, dg_launch_ws(WS_EPI_STORE_F32, a, 1, nullptr) != 0, "routed projection");
+      break;
+    case 6:  // FP8 weights on a dense launch
+      a.wfmt = DG_WS_W_E4M3;
+      REFUSE_IF(&c, dg_launch_ws(WS_EPI_STORE_F32, a, 1, nullptr) != 0, "dense projection");
+      break;
+    case 7:  // partial sums without the bf16 fragment-major output
+      REFUSE_IF(&c, dg_launch_rmsnorm(DG_F32, nullptr, nullptr, nullptr, 16, 64, nullptr, 1e-6f, nullptr, false,
+                                      nullptr, nullptr, parts) != 0,
+                "FFN norm");
+      break;
+    case 8:
+      REFUSE_IF(&c, dg_launch_combine_norm(DG_F32, nullptr, nullptr, nullptr, 16, 64, 2, nullptr, 1e-6f, nullptr,
+                                           false, nullptr, parts) != 0,
+                "combine and norm");
+      break;
+    case 9:  // a vocabulary that is not whole 64-row tiles
+      REFUSE_IF(&c, dg_launch_transpose_bf16(nullptr, 100, 64, nullptr, nullptr) != 0, "embedding transpose");
+      break;
+    case 10: {  // rows that are not whole float4s
+      DgScSlots sl;
+      memset(&sl, 0, sizeof sl);
+      REFUSE_IF(&c, dg_launch_sc_fold(nullptr, 2, 0, 6, nullptr, nullptr, 16, sl, 256, nullptr) != 0,
+                "self-conditioning fold");
+      break;
+    }
+  }
+  const dg_status st = take_refusal(&c);
+  if (msg && msg_bytes) snprintf(msg, msg_bytes, "%s", c.err.c_str());
+  return st;
 }
 
 dg_status dg_debug_tap_size(const dg_model_config* cfg, size_t* bytes) {

@@ -22,7 +22,7 @@ EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "d
            "dg_last_step_rows", "dg_last_step_router_logits", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
            "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read", "dg_kernel_timer_every",
            "dg_get_self_cond", "dg_set_self_cond", "dg_op_self_cond", "dg_debug_tap_size", "dg_debug_set_tap_buffer",
-           "dg_debug_tap")
+           "dg_debug_tap", "dg_debug_refusal_count", "dg_debug_refusal_case")
 
 DG_TAP_LAYER_INPUT, DG_TAP_AFTER_ATTENTION, DG_TAP_ROUTER_LOGITS = 0, 1, 2
 
@@ -129,6 +129,8 @@ def load():
         "dg_debug_tap_size": [ctypes.POINTER(ModelConfig), ctypes.POINTER(SZ)],
         "dg_debug_set_tap_buffer": [P, P, SZ],
         "dg_debug_tap": [P, I32, I32, P, SZ],
+        "dg_debug_refusal_count": [],
+        "dg_debug_refusal_case": [I32, ctypes.c_char_p, SZ],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -174,6 +176,17 @@ def dg_workspace_size(cfg):
     if st != DG_OK:
         raise DgError(st, lib.dg_last_error(None).decode())
     return kv.value, sc.value
+
+
+def dg_debug_refusal_cases():
+    """(status, message) of every launcher refusal case (host only, no GPU)."""
+    lib = load()
+    out = []
+    for i in range(lib.dg_debug_refusal_count()):
+        buf = ctypes.create_string_buffer(512)
+        st = lib.dg_debug_refusal_case(i, buf, len(buf))
+        out.append((st, buf.value.decode()))
+    return out
 
 
 def dg_philox_tokens(seed, block, step, n, vocab, out):

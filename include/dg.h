@@ -386,6 +386,20 @@ dg_status dg_debug_set_tap_buffer(dg_ctx* ctx, void* tap_dev, size_t bytes);
 dg_status dg_debug_tap(dg_ctx* ctx, int32_t which, int32_t layer, float* host_dst, size_t bytes);
 
 /*
+ * Refusal self-test (host only; needs no GPU and makes no HIP call).  Every
+ * launcher returns -1 and queues nothing for arguments its kernels do not
+ * implement, and the entry point that called it then reports
+ * DG_ERR_UNSUPPORTED ("launch refused: <launch>").  Creation-time validation
+ * keeps a valid model from reaching these paths, so case i of
+ * dg_debug_refusal_count() calls one launcher with such arguments on a stub
+ * context and returns the status the entry point would return (the message,
+ * NUL-terminated, to msg when msg_bytes > 0).  DG_ERR_INVALID_ARG for i out of
+ * range.
+ */
+int32_t dg_debug_refusal_count(void);
+dg_status dg_debug_refusal_case(int32_t i, char* msg, size_t msg_bytes);
+
+/*
  * LM-head logits of the last step's final hidden rows: for each of the n
  * listed rows (indices as in dg_last_step_rows), vocab fp32 logits to
  * logits_dev (device, [n][vocab]).  Same normalisation and matrix-core path

@@ -17,7 +17,7 @@ def _declared():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             txt = open(os.path.join(ROOT, "include", fn)).read()
-            names |= set(re.findall(r"^\s*(?:dg_status|void|const char\*)\s+(dg_\w+)\s*\(", txt, re.M))
+            names |= set(re.findall(r"^\s*(?:dg_status|void|int32_t|const char\*)\s+(dg_\w+)\s*\(", txt, re.M))
     return names
 
 
@@ -101,6 +101,24 @@ def test_null_context_calls_fail_cleanly(lib):
     assert lib.dg_commit_block(None, 0, None) == dg.DG_ERR_INVALID_ARG
     assert lib.dg_philox_tokens(0, -1, 0, 4, 10, None, None) == dg.DG_ERR_INVALID_ARG
     lib.dg_destroy(None)
+
+
+def test_every_launch_refusal_reaches_the_caller_as_a_status(lib):
+    """Each launcher's refusal path (arguments its kernels do not implement):
+    the launcher queues nothing and the entry point returns DG_ERR_UNSUPPORTED
+    with the launch named, instead of stopping the process."""
+    cases = dg.dg_debug_refusal_cases()
+    assert len(cases) == 11
+    names = ["bf16 streaming projection on a non-bf16 model", "bf16 streaming add projection on a non-bf16 model",
+             "routed streaming projection on a non-bf16 model", "dense projection", "routed projection",
+             "routed projection", "dense projection", "FFN norm", "combine and norm", "embedding transpose",
+             "self-conditioning fold"]
+    for (st, msg), name in zip(cases, names):
+        assert st == dg.DG_ERR_UNSUPPORTED, (st, msg)
+        assert msg == "launch refused: " + name
+    buf = ctypes.create_string_buffer(8)
+    assert lib.dg_debug_refusal_case(len(cases), buf, len(buf)) == dg.DG_ERR_INVALID_ARG
+    assert lib.dg_debug_refusal_case(-1, None, 0) == dg.DG_ERR_INVALID_ARG
 
 
 def test_self_cond_workspace():
