@@ -120,7 +120,7 @@ def test_full_moe_op(layer0, t, skew):
     b = oracle.round_bf16(oracle.rmsnorm(xo, lw.ffn_norm, cfg.rms_eps))
     f, r, oids, ogates = oracle.moe(b, lw, cfg, prec)
     tr = oracle.model.LayerTrace(router_logits=r, ids=oids, gates=ogates)
-    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 2e-2)
+    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 1e-3)  # same input: gates apart by fp32 rounding
     u, c = np.unique(oids, return_counts=True)
     keep = np.setdiff1d(np.arange(t), flips)
     got = xg.cpu().numpy().astype(np.float64)
@@ -157,7 +157,7 @@ def test_full_moe_op_fp8(layer0, t, skew):
     b = oracle.round_bf16(oracle.rmsnorm(xo, lw8.ffn_norm, cfg.rms_eps))
     f, r, oids, ogates = oracle.moe(b, lw8, cfg, prec)
     tr = oracle.model.LayerTrace(router_logits=r, ids=oids, gates=ogates)
-    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 2e-2)
+    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 1e-3)  # same input: gates apart by fp32 rounding
     keep = np.setdiff1d(np.arange(t), flips)
     got = xg.cpu().numpy().astype(np.float64)
     worst = max(rel_l2(got[i] - xo[i], f[i]) for i in keep)
@@ -196,7 +196,7 @@ def test_full_moe_op_mxfp4(layer0, t, skew):
     b = oracle.round_bf16(oracle.rmsnorm(xo, lw4.ffn_norm, cfg.rms_eps))
     f, r, oids, ogates = oracle.moe(b, lw4, cfg, prec)
     tr = oracle.model.LayerTrace(router_logits=r, ids=oids, gates=ogates)
-    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 2e-2)
+    flips = compare_router(ids.cpu().numpy(), gates.cpu().numpy(), tr, cfg.top_k, 1e-3)  # same input: gates apart by fp32 rounding
     keep = np.setdiff1d(np.arange(t), flips)
     got = xg.cpu().numpy().astype(np.float64)
     worst = max(rel_l2(got[i] - xo[i], f[i]) for i in keep)

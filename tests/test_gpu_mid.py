@@ -12,23 +12,17 @@ import torch
 import oracle
 from block_diffusion_decoding_dg_amd import dg, synth
 from tests import helpers
-from tests.gpu_common import check_step, log, make_decoder, rel_l2, topk_gap
+from tests.gpu_common import PlainTwin, check_step, log, make_decoder, rel_l2, topk_gap
 
 pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS["mid"]
 STEPS = 4
 
-# bf16 tolerances: logits relative L2 <= 1e-2 per row against the float64
-# oracle; entropies and log-sum-exp within 1e-2 nats.
+# Steps are checked by gpu_common.check_step with bands of twice the spread
+# between the bf16 oracle and the exact-arithmetic oracle on the same step.
+# The self-conditioning state is held against the logits' relative L2 floor.
 LOGIT_RL2 = 1e-2
-ENT_ABS = 1e-2
-# Near-tie band of the step-level decisions (router sets, argmax).  The spec's
-# 1e-3 applies to a decision taken from the same input, which the op-level tests
-# check; here the step runs on the library's own prefill cache and eight layers,
-# so its inputs carry the saturated ~1-ulp bf16 difference and router logits of
-# size ~0.6 differ by a few 1e-3.  The band is set from that error.
-STEP_BAND = 1e-2
 # K/V cache rows after several layers.  Both sides round to bf16 at the same
 # points, but once their pre-rounding values differ by a fraction of an ulp some
 # roundings flip, and each flip seeds larger differences downstream: the
@@ -36,17 +30,12 @@ STEP_BAND = 1e-2
 # relative).  Rows are held to a median of 1e-2 and a 2e-2 tail (~5 ulp) for at
 # most 5% of rows; the step's own bound is on the logits.
 CACHE_ROW_TAIL = 2e-2
+# Router gaps within which a cache row's routing may have differed: fixed once
+# from the oracle's own spread at this shape (on a canvas step the bf16 model
+# overturns router gaps up to 1.2e-3 in layer 0, 5e-3 by layer 2 and 1.4e-2 by
+# layer 7 against exact arithmetic), so rows past a gap below 1e-2 in an earlier
+# layer may carry a different expert set.
 NEAR_TIE = 1e-2
-
-
-def _ent_tol(h):
-    return np.full_like(np.asarray(h, dtype=np.float64), ENT_ABS)
-
-
-def _logit_tol(g, o):
-    for i in range(g.shape[0]):
-        e = rel_l2(g[i], o[i])
-        assert e <= LOGIT_RL2, ("logits rel L2", i, e)
 
 
 @pytest.fixture(scope="module", params=["mid", "mid_fp8", "mid_mxfp4"])
@@ -115,28 +104,29 @@ def test_mid_prefill_steps_commit(setup):
     dec.dg_prefill(0, prompt, seed)
     st = oracle.new_request(ocfg, seed, W.max_ctx)
     _, traces = oracle.prefill(st, prompt, ocfg, ow, prec, keep_traces=True)
+    twin = PlainTwin(st, prompt, ocfg, ow)
     _check_cache(dec, st, ocfg, 0, len(prompt), "prefill", traces)
     scfg = oracle.SamplerConfig(W.tau, W.max_steps)
     stats = {}
     for s in range(STEPS):
-        r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16,
-                                     stats=stats, band=STEP_BAND)
+        r, resync, info, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=16, stats=stats, plain=twin)
         assert info["n_accepted"] == 1 and info["n_open"] == 255 - s   # random weights: H >> tau
         log("mid: step %d ok (resync %s)" % (s + 1, resync))
-    log("mid: per-step max entropy error %s, router-flip rows %s, argmax flips %s"
-        % (stats["ent_err"], stats["router_flip_rows"], stats["argmax_flips"]))
+    log("mid: per-step max entropy error %s, router-flip rows %s, argmax flips %s, decisions excused at gaps of "
+        "1e-3 or more: router %s, argmax %s" % (stats["ent_err"], stats["router_flip_rows"], stats["argmax_flips"],
+                                               stats["excused_router"], stats["excused_argmax"]))
     # Force the canvas done on both sides (the same ids, all accepted) and commit.
     st.accepted[:] = True
     dec.dg_set_canvas(0, st.ids, st.accepted, st.step, st.block)
     ids_g = dec.dg_commit_block(0)
     P = st.P
+    twin.commit(st)
     ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
     assert np.array_equal(ids_g, ids_o)
     _check_cache(dec, st, ocfg, P, P + 256, "commit", ctraces)
     assert dec.dg_get_request(0)["committed"] == P + 256
     # First step of block 1: a fresh canvas drawn at (seed, block 1, step 0).
-    r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16,
-                                 band=STEP_BAND)
+    r, resync, info, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=16, plain=twin)
     assert info["block"] == 1 and info["step"] == 1
     dec.close()
 
@@ -218,11 +208,11 @@ def test_mid_self_cond_steps_commit(sc_setup):
     dec.dg_prefill(0, prompt, seed)
     st = oracle.new_request(ocfg, seed, W.max_ctx)
     oracle.prefill(st, prompt, ocfg, ow, prec)
+    twin = PlainTwin(st, prompt, ocfg, ow)
     scfg = oracle.SamplerConfig(W.tau, W.max_steps)
     # step 1: zero state, the plain model's step
     stats = {}
-    r, _, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16, band=STEP_BAND,
-                         stats=stats)
+    r, _, _, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=16, stats=stats, plain=twin)
     g = _check_state(dec, st, r, ow, prec, "step 1", stats["flipped"])
     # a unit-scale state on both sides (the GPU's bytes, so both start equal)
     rng = np.random.default_rng(5)
@@ -232,8 +222,7 @@ def test_mid_self_cond_steps_commit(sc_setup):
     assert np.array_equal(dec.dg_get_self_cond(0), u)
     for s in (2, 3):
         before = dec.dg_get_self_cond(0)
-        r, resync, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16,
-                                  band=STEP_BAND, stats=stats)
+        r, resync, _, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=16, stats=stats, plain=twin)
         g = _check_state(dec, st, r, ow, prec, "step %d" % s, stats["flipped"])
         keep = r.accepted_before
         assert np.array_equal(g[keep], before[keep]), "state of accepted positions changed"
@@ -244,12 +233,12 @@ def test_mid_self_cond_steps_commit(sc_setup):
     st.sc_state = dec.dg_get_self_cond(0).astype(np.float64)
     P = st.P
     ids_g = dec.dg_commit_block(0)
+    twin.commit(st)
     ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
     assert np.array_equal(ids_g, ids_o)
     _check_cache(dec, st, ocfg, P, P + 256, "commit", ctraces)
     # the next canvas starts from a zero state again
-    r, _, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=16, band=STEP_BAND,
-                            stats=stats)
+    r, _, info, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=16, stats=stats, plain=twin)
     assert info["block"] == 1 and info["step"] == 1
     _check_state(dec, st, r, ow, prec, "block 1 step 1", stats["flipped"])
     dec.close()
@@ -304,19 +293,17 @@ def test_mid_capped_block_free_running(setup):
     (bf16 argmax near-ties allowed only inside the band), then the commit of the
     final canvas and the first two steps of the next block."""
     W, tw, ocfg, ow, prec = setup
-    if W.expert_format != "native":
-        pytest.skip("the bf16 model covers the block protocol; the quantized experts change only the MoE")
     cap = 12
     prompt = synth.make_prompt(W, seed=2)
     dec = make_decoder(W, tw, max_steps=cap)
     dec.dg_prefill(0, prompt, 7)
     st = oracle.new_request(ocfg, 7, W.max_ctx)
     oracle.prefill(st, prompt, ocfg, ow, prec)
+    twin = PlainTwin(st, prompt, ocfg, ow)
     scfg = oracle.SamplerConfig(W.tau, cap)
     resyncs = 0
     for s in range(cap):
-        r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=8,
-                                     band=STEP_BAND)
+        r, resync, info, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=8, plain=twin)
         resyncs += resync
         if s < cap - 1:
             assert info["n_accepted"] == 1 and not info["done"]
@@ -324,12 +311,12 @@ def test_mid_capped_block_free_running(setup):
     log("mid: capped block done in %d steps, %d re-syncs" % (cap, resyncs))
     P = st.P
     ids_g = dec.dg_commit_block(0)
+    twin.commit(st)
     ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
     assert np.array_equal(ids_g, ids_o)
     _check_cache(dec, st, ocfg, P, P + 256, "capped commit", ctraces)
     for s in range(2):
-        r, _, info = check_step(W, dec, st, ocfg, scfg, ow, prec, _ent_tol, _logit_tol, sample_rows=8,
-                                band=STEP_BAND)
+        r, _, info, _ = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=8, plain=twin)
         assert info["block"] == 1 and info["step"] == s + 1
     dec.close()
 
@@ -358,3 +345,51 @@ def test_mid_self_cond_errors(sc_setup):
         plain.dg_op_self_cond(torch.zeros((4, W.d_model), dtype=torch.float32, device="cuda"))
     assert e.value.status == dg.DG_ERR_UNSUPPORTED
     plain.close()
+
+
+@pytest.mark.timeout(1800)
+def test_mid_generation_two_canvases(setup):
+    """The mid-size workload's whole generation: a 1024-token prompt, then two
+    256-token canvases at tau 1.0 under the 256-step cap, block after block,
+    both sides running from their own state.  Every step is checked by
+    check_step, with the bands of each block fixed at its first step from the
+    oracle spread there; after a permitted near-tie difference the GPU takes the
+    oracle's canvas.  Both commits' cache rows are checked, and the output ids
+    of both blocks are the oracle's."""
+    import time
+    W, tw, ocfg, ow, prec = setup
+    if W.expert_format != "native":
+        pytest.skip("one whole generation, on the bf16 model; the quantized experts run the capped block above")
+    prompt = synth.make_prompt(W, seed=3)
+    seed = 11
+    dec = make_decoder(W, tw)
+    dec.dg_prefill(0, prompt, seed)
+    st = oracle.new_request(ocfg, seed, W.max_ctx)
+    oracle.prefill(st, prompt, ocfg, ow, prec)
+    twin = PlainTwin(st, prompt, ocfg, ow)
+    scfg = oracle.SamplerConfig(W.tau, W.max_steps)
+    t0 = time.time()
+    for b in range(W.n_out // W.canvas_len):
+        bands, stats, steps, resyncs = None, {}, 0, 0
+        while True:
+            r, resync, info, bands = check_step(W, dec, st, ocfg, scfg, ow, prec, sample_rows=4, stats=stats,
+                                                bands=bands, plain=twin)
+            steps += 1
+            resyncs += resync
+            if steps % 32 == 0:
+                log("mid generation: block %d, %d steps, %d re-syncs, %.0f s" % (b, steps, resyncs, time.time() - t0))
+            if r.done:
+                break
+        assert info["done"] and info["block"] == b and steps <= W.max_steps
+        log("mid generation: block %d done in %d steps, %d re-syncs; decisions excused at gaps of 1e-3 or more: "
+            "router %d, argmax %d; largest entropy error %.2e (band %.2e)"
+            % (b, steps, resyncs, sum(stats["excused_router"]), sum(stats["excused_argmax"]), max(stats["ent_err"]),
+               bands["entropy"]))
+        P = st.P
+        ids_g = dec.dg_commit_block(0)
+        twin.commit(st)
+        ids_o, ctraces = oracle.commit_block(st, ocfg, ow, prec, keep_traces=True)
+        assert np.array_equal(ids_g, ids_o)
+        _check_cache(dec, st, ocfg, P, P + 256, "generation block %d commit" % b, ctraces)
+    assert dec.dg_get_request(0)["committed"] == len(prompt) + W.n_out
+    dec.close()

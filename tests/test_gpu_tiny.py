@@ -44,14 +44,6 @@ def _cache_check(dec, st, ocfg, P, tol, req=0):
         assert normwise(vg.reshape(P, -1), st.cache_v[l][:P].reshape(P, -1)) < tol, ("V", l)
 
 
-def _fp32_logit_tol(g, o):
-    assert normwise(g, o) <= 1e-4, normwise(g, o)
-
-
-def _fp32_ent_tol(h):
-    return 1e-4 * np.maximum(np.abs(h), 1.0)
-
-
 def test_tiny_full_block_free_running(setup):
     tw, twg, ocfg, ow = setup
     prompt = synth.make_prompt(W, seed=0)
@@ -66,7 +58,7 @@ def test_tiny_full_block_free_running(setup):
     n_resync = 0
     steps = 0
     while True:
-        r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, oracle.Precision(), _fp32_ent_tol, _fp32_logit_tol)
+        r, resync, info, _ = check_step(W, dec, st, ocfg, scfg, ow, oracle.Precision())
         n_resync += resync
         steps += 1
         assert info["n_open"] == r.n_open
@@ -106,7 +98,7 @@ def test_tiny_prefill_chunked_and_empty_prompt(setup):
     st0 = oracle.new_request(ocfg, 3, 576)
     oracle.prefill(st0, np.zeros(0, np.int64), ocfg, ow, oracle.Precision())
     scfg = oracle.SamplerConfig(W.tau, W.max_steps)
-    check_step(W, dec, st0, ocfg, scfg, ow, oracle.Precision(), _fp32_ent_tol, _fp32_logit_tol)
+    check_step(W, dec, st0, ocfg, scfg, ow, oracle.Precision())
 
 
 @pytest.mark.parametrize("t,pos0,causal", [(256, 64, 0), (37, 300, 1), (5, 0, 0), (200, 17, 1)])
@@ -335,7 +327,7 @@ def test_tiny_budget_block_free_running(setup):
     scfg = oracle.SamplerConfig(W.tau, W.max_steps, mode="budget")
     gstate, steps, n_resync, per_step = {}, 0, 0, []
     while True:
-        r, resync, info = check_step(W, dec, st, ocfg, scfg, ow, oracle.Precision(), _fp32_ent_tol, _fp32_logit_tol,
+        r, resync, info, _ = check_step(W, dec, st, ocfg, scfg, ow, oracle.Precision(),
                                      gstate=gstate)
         steps += 1
         n_resync += resync
