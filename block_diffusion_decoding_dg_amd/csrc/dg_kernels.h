@@ -146,6 +146,8 @@ void dg_launch_sc_gather(const DgScSlots& sl, int rows, int C, int d, void* b, h
 // b (bf16, fragment-major [n][d]) = u (fp32 row-major [n][d]).
 void dg_launch_rows_to_fm(const float* u, int n, int d, void* b, hipStream_t s);
 void dg_launch_fill_zero(float* p, size_t n, hipStream_t s);
+// *p = v, written by a kernel on the stream.
+void dg_launch_set_i32(int32_t* p, int32_t v, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Weight-streaming GEMM (bf16 only): out = A W^T per group, 64 weight rows per

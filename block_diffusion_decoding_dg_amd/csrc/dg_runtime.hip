@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -30,6 +31,13 @@
 #define DG_SC_KSPLIT 16
 #endif
 
+// Static scratch of the allocation-free LM head (dg_op_lm_head_noalloc): every
+// GPU the library runs on holds one copy until the process ends.  Host code
+// never passes its name to a kernel; it uses the device address that
+// noalloc_scratch_ptr resolves for the current device.
+#define DG_NOALLOC_SCRATCH_BYTES (16u << 20)
+static __device__ __align__(256) unsigned char scratch[DG_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_create_error;
@@ -45,6 +53,28 @@ struct Request {
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Device address of `scratch` on the current device, resolved once per device
+// (each GPU holds its own copy at its own address).
+constexpr int DG_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[DG_MAX_DEVICES];
+
+hipError_t noalloc_scratch_ptr(void** p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= DG_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = q;
+  }
+  *p = g_scratch_dev[dev];
+  return hipSuccess;
+}
 
 struct Carve {
   char* base;
@@ -154,6 +184,8 @@ struct dg_ctx {
   int64_t kt_launches = 0;
 
   std::vector<Request> req;
+  void* noalloc_scratch = nullptr;  // this device's copy of `scratch` (dg_op_lm_head_noalloc)
+  std::string noalloc_err;          // why it could not be resolved
   std::vector<int> last_slots;  // request of each slot in the last step
   int last_rows = 0;
   std::string err;
@@ -599,28 +631,52 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
 
 // Fused LM head over the rows of c->hn (count *n_dev <= max_rows): per-row
 // softmax statistics and argmax written at row_idx[row] (or row).
+// hn, lpart, lpart_arg: the normalised rows and the per-tile partial statistics
+// (default: the context's scratch).
 void launch_lm_head(dg_ctx* c, const int32_t* n_dev, int max_rows, const int32_t* row_idx, float* ent, float* lse,
-                    int32_t* amax, float* zout = nullptr) {
+                    int32_t* amax, float* zout = nullptr, const void* hn = nullptr, float* lpart = nullptr,
+                    int32_t* lpart_arg = nullptr) {
   const dg_model_config& m = c->cfg;
+  if (!hn) hn = c->hn;
+  if (!lpart) lpart = c->lpart;
+  if (!lpart_arg) lpart_arg = c->lpart_arg;
   if (c->dtype == DG_F32) {
-    dg_launch_lm_head(c->dtype, c->hn, n_dev, max_rows, m.d_model, c->embed, m.vocab, c->lpart, c->lpart_arg, ent, lse,
-                      amax, row_idx, c->stream);
+    dg_launch_lm_head(c->dtype, hn, n_dev, max_rows, m.d_model, c->embed, m.vocab, lpart, lpart_arg, ent, lse, amax,
+                      row_idx, c->stream);
     return;
   }
   WsArgs a;
   memset(&a, 0, sizeof a);
-  a.A = c->hn;
+  a.A = hn;
   a.W0 = c->embed;
   a.K = m.d_model;
   a.N = m.vocab;
   a.M = max_rows;
   a.M_dev = n_dev;
-  a.out = c->lpart;
+  a.out = lpart;
   a.ldo = c->lm_tiles;
-  a.part_arg = c->lpart_arg;
+  a.part_arg = lpart_arg;
   a.zout = zout;
   REFUSE_IF(c, dg_launch_ws(WS_EPI_LM_STATS, a, c->lm_tiles, c->stream) != 0, "LM head");
-  dg_launch_lm_merge(c->lpart, c->lpart_arg, n_dev, max_rows, c->lm_tiles, row_idx, ent, lse, amax, c->stream);
+  dg_launch_lm_merge(lpart, lpart_arg, n_dev, max_rows, c->lm_tiles, row_idx, ent, lse, amax, c->stream);
+}
+
+// The static scratch of the allocation-free LM head for n rows: the row count,
+// the normalised rows (whole 16-row tiles) and the per-tile partial statistics.
+// Returns the bytes needed; with base, also the carved pointers.
+size_t noalloc_lm_carve(const dg_model_config& m, int n, char* base, int32_t** n_dev, void** hn, float** lpart,
+                        int32_t** lpart_arg) {
+  Carve cv{base};
+  const size_t n16 = (size_t)(n + 15) / 16 * 16, tiles = (size_t)dg_lm_head_tiles(m.vocab);
+  int32_t* nd = cv.take<int32_t>(4);
+  void* h = cv.take<void>(n16 * m.d_model * (m.dtype == DG_BF16 ? 2 : 4));
+  float* lp = cv.take<float>(n16 * tiles * 3 * 4);
+  int32_t* la = cv.take<int32_t>(n16 * tiles * 4);
+  if (n_dev) *n_dev = nd;
+  if (hn) *hn = h;
+  if (lpart) *lpart = lp;
+  if (lpart_arg) *lpart_arg = la;
+  return cv.off;
 }
 
 // Self-conditioning state rows of the requests in the step's slots.
@@ -924,6 +980,14 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   c->lm_tiles = dg_lm_head_tiles(m.vocab);
   c->req.resize(m.max_requests);
   carve(c, m, (char*)scratch_dev);
+  {  // the static scratch of dg_op_lm_head_noalloc on this device; only that call needs it
+    const hipError_t es = noalloc_scratch_ptr(&c->noalloc_scratch);
+    if (es != hipSuccess) {
+      c->noalloc_scratch = nullptr;
+      c->noalloc_err = hipGetErrorString(es);
+      (void)hipGetLastError();
+    }
+  }
 
   std::vector<double> inv(m.head_dim / 2);
   for (int j = 0; j < m.head_dim / 2; ++j) inv[j] = std::pow((double)m.rope_theta, -2.0 * j / m.head_dim);
@@ -1425,6 +1489,37 @@ dg_status dg_op_lm_head(dg_ctx* c, const float* h_dev, int32_t n, float* entropy
   launch_lm_head(c, c->n_open_rows, n, nullptr, entropy_dev, lse_dev, argmax_dev);
   LAUNCHCK(c);
   HIPCK(c, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_op_lm_head_noalloc(dg_ctx* c, const float* h_dev, int32_t n, float* entropy_dev, float* lse_dev,
+                                int32_t* argmax_dev) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (!h_dev || n <= 0 || !entropy_dev || !lse_dev || !argmax_dev) return fail(c, DG_ERR_INVALID_ARG, "bad arguments");
+  if (!c->noalloc_scratch)
+    return fail(c, DG_ERR_HIP, "the static scratch has no device address: %s", c->noalloc_err.c_str());
+  const size_t need = noalloc_lm_carve(c->cfg, n, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (need > DG_NOALLOC_SCRATCH_BYTES) {
+    int most = n;
+    while (most > 1 && noalloc_lm_carve(c->cfg, most, nullptr, nullptr, nullptr, nullptr, nullptr) >
+                           DG_NOALLOC_SCRATCH_BYTES)
+      most = most * 7 / 8;
+    return fail(c, DG_ERR_INVALID_ARG,
+                "%d rows need %zu bytes of static scratch, more than its %u (about %d rows fit this model)", n, need,
+                (unsigned)DG_NOALLOC_SCRATCH_BYTES, most);
+  }
+  int32_t* n_dev;
+  void* hn;
+  float* lpart;
+  int32_t* lpart_arg;
+  noalloc_lm_carve(c->cfg, n, (char*)c->noalloc_scratch, &n_dev, &hn, &lpart, &lpart_arg);
+  hipStream_t s = c->stream;
+  dg_launch_set_i32(n_dev, n, s);
+  REFUSE_IF(c, dg_launch_rmsnorm(c->dtype, h_dev, nullptr, n_dev, n, c->cfg.d_model, c->final_norm, c->cfg.rms_eps,
+                                 hn, c->dtype == DG_BF16, s) != 0,
+            "final norm");
+  launch_lm_head(c, n_dev, n, nullptr, entropy_dev, lse_dev, argmax_dev, nullptr, hn, lpart, lpart_arg);
+  LAUNCHCK(c);
   return DG_OK;
 }
 

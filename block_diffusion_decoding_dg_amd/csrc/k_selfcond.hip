@@ -154,6 +154,13 @@ __global__ void __launch_bounds__(256) k_fill_zero(float* __restrict__ p, size_t
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
+// One int32 set to v on the stream (no host copy).
+__global__ void k_set_i32(int32_t* __restrict__ p, int32_t v) {
+  if (threadIdx.x == 0) p[0] = v;
+}
+
+void dg_launch_set_i32(int32_t* p, int32_t v, hipStream_t s) { k_set_i32<<<1, 64, 0, s>>>(p, v); }
+
 void dg_launch_fill_zero(float* p, size_t n, hipStream_t s) {
   if (n == 0) return;
   const size_t blocks = std::min<size_t>((n + 255) / 256, 4096);

@@ -22,7 +22,7 @@ EXPORTS = ("dg_workspace_size", "dg_create", "dg_prefill", "dg_denoise_step", "d
            "dg_last_step_rows", "dg_last_step_router_logits", "dg_last_step_logits", "dg_op_attention", "dg_op_moe", "dg_op_lm_head",
            "dg_op_sample", "dg_philox_tokens", "dg_kernel_timer", "dg_kernel_timer_read", "dg_kernel_timer_every",
            "dg_get_self_cond", "dg_set_self_cond", "dg_op_self_cond", "dg_debug_tap_size", "dg_debug_set_tap_buffer",
-           "dg_debug_tap", "dg_debug_refusal_count", "dg_debug_refusal_case")
+           "dg_debug_tap", "dg_debug_refusal_count", "dg_debug_refusal_case", "dg_op_lm_head_noalloc")
 
 DG_TAP_LAYER_INPUT, DG_TAP_AFTER_ATTENTION, DG_TAP_ROUTER_LOGITS = 0, 1, 2
 
@@ -121,6 +121,7 @@ def load():
         "dg_op_attention": [P, I32, I32, P, I32, I32, I32],
         "dg_op_moe": [P, I32, P, I32, P, P],
         "dg_op_lm_head": [P, P, I32, P, P, P],
+        "dg_op_lm_head_noalloc": [P, P, I32, P, P, P],
         "dg_op_sample": [P, I32, P, P, I32, ctypes.POINTER(StepInfo)],
         "dg_philox_tokens": [U64, I32, I32, I32, I32, P, P],
         "dg_kernel_timer": [P, I32],
@@ -370,6 +371,11 @@ class Decoder:
         am = torch.empty(n, dtype=torch.int32, device=h.device)
         self._check(self.lib.dg_op_lm_head(self.ctx, _ptr(h), n, _ptr(ent), _ptr(lse), _ptr(am)))
         return ent, lse, am
+
+    def dg_op_lm_head_noalloc(self, h, ent, lse, am):
+        """dg_op_lm_head into caller-given outputs, with the library's static
+        scratch; asynchronous on the library's stream."""
+        self._check(self.lib.dg_op_lm_head_noalloc(self.ctx, _ptr(h), h.shape[0], _ptr(ent), _ptr(lse), _ptr(am)))
 
     def dg_op_self_cond(self, u):
         """Self-conditioning MLP term of the rows of u (fp32 [n][d_model], device)."""

@@ -459,6 +459,25 @@ dg_status dg_op_lm_head(dg_ctx* ctx, const float* h_dev, int32_t n, float* entro
                         float* lse_dev, int32_t* argmax_dev);
 
 /*
+ * dg_op_lm_head without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid it): the
+ * same kernels and results, but the normalised rows, the per-tile partial
+ * statistics and the row count live in the library's static device scratch
+ * (16 MiB, one copy per GPU, held until the process ends; its address on the
+ * current device is resolved by dg_create) instead of the context's
+ * workspace, and the call does not synchronise: the outputs are ready when
+ * the context's stream reaches this point.  It calls no allocator and no
+ * memset.  n may be any positive count whose buffers fit the 16 MiB (at most
+ * about 256 rows at vocab 262144 and d_model 2816); a larger n is rejected
+ * with DG_ERR_INVALID_ARG and a message giving the limit.  Every call on a GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (other streams,
+ * other contexts, other threads) race.  DG_ERR_HIP if the scratch has no
+ * device address.
+ */
+dg_status dg_op_lm_head_noalloc(dg_ctx* ctx, const float* h_dev, int32_t n, float* entropy_dev, float* lse_dev,
+                                int32_t* argmax_dev);
+
+/*
  * Sampler alone on request req's active canvas, given per-position entropy and
  * argmax (device, canvas_len each; entries of accepted positions are ignored)
  * as step `step` (1-based) of the current block.  Updates the canvas in place
