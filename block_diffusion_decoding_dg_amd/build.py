@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdg.so")
 
-SOURCES = ["k_dense.hip", "k_attn.hip", "k_moe.hip", "k_ws.hip", "k_sample.hip", "k_selfcond.hip", "dg_runtime.hip"]
+SOURCES = ["k_dense.hip", "k_attn.hip", "k_moe.hip", "k_ws.hip", "k_wsd.hip", "k_sample.hip", "k_selfcond.hip", "dg_runtime.hip"]
 ARCH = os.environ.get("DG_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 instructions are kept out of the generated code on purpose.

@@ -130,3 +130,20 @@ __device__ __forceinline__ int32_t draw_token(uint64_t seed, uint32_t block, uin
   philox4x64_10(c, seed, 0ull);
   return (int32_t)__umul64hi(c[0], (uint64_t)vocab);
 }
+
+// Wait until at most n of this wave's vector memory loads are outstanding
+// (vmcnt only; the lgkm and export counters are left at their maxima).
+#define DG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// One global_load_lds_dwordx4: lane l copies 16 bytes from g (its own address)
+// to lds + 16 l (lds wave-uniform).  Issued from an asm statement with inputs
+// only (the LDS base goes to M0), so that the compiler adds no wait of its own
+// for it: the kernel's explicit vmcnt waits and barriers order these copies
+// against the LDS reads.  The statement writes no register.
+__device__ __forceinline__ void lds_dma16(const void* g, const uint4* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(a)), "v"(g)
+               : "memory", "m0");
+}

@@ -74,6 +74,11 @@ void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, 
                      int32_t* n_b, hipStream_t s);
 // Rows of the expert-sorted layout: pairs + 16 per expert.
 inline int dg_sorted_rows(int E, int pairs) { return pairs + 16 * E; }
+// The expert-sorted rows (rowsrc, *n_srows <= srows_max, a multiple of 16) of the
+// row-major bf16 src ([rows][K]) copied into the fragment-major layout out
+// ([srows][K], fm_index), zeros on padding rows.
+void dg_launch_gather_fm(const void* src, const int32_t* rowsrc, const int32_t* n_srows, int srows_max, int K,
+                         void* out, hipStream_t s);
 // Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
 void dg_launch_expert_up(int dtype, const void* b, int rows, int d, int E, int k, int eh, const void* w1,
                          const void* w3, const int32_t* counts, const int32_t* offsets, const int32_t* perm, void* h,
@@ -235,6 +240,12 @@ int dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);
 inline int dg_unit_slots(int E, int pairs, int part_rows, int nblk) {
   return (E + (pairs + part_rows - 1) / part_rows) * ((nblk + 7) & ~7);
 }
+// Grouped launch of bf16 routed-expert weights with producer waves copying the
+// weight tiles straight into LDS and consumer waves on the matrix cores (k_wsd):
+// SwiGLU (W1 / W3) or an fp32 store (W2), A fragment-major over the
+// expert-sorted rows (no rowsrc), on the work list of a.units (DG_WS_GROUP_ROWS
+// rows per part).  Returns -1 (nothing launched) for any other combination.
+int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s);
 // Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b);
 // each list needs dg_unit_slots(E, rows * k, part_rows, nblk) entries.
 void dg_launch_ws_units(const int32_t* counts, int E, int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a,

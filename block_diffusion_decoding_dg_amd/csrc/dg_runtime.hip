@@ -26,6 +26,12 @@
 #ifndef DG_MAX_KSPLIT
 #define DG_MAX_KSPLIT 8
 #endif
+// Kernel of the bf16 routed experts: 1 producer / consumer waves with the
+// weight tiles copied straight into LDS and the rows gathered once into the
+// fragment-major layout (k_wsd), 0 the register-staged k_ws gathering rows.
+#ifndef DG_ROUTED_KERNEL
+#define DG_ROUTED_KERNEL 1
+#endif
 // Vocabulary ranges of the self-conditioning product, at most.
 #ifndef DG_SC_KSPLIT
 #define DG_SC_KSPLIT 16
@@ -134,6 +140,7 @@ struct dg_ctx {
   int32_t* n_units = nullptr;    // [3]: lengths of the two lists, rows of the expert-sorted layout
   int rows_cap = 0;              // rows of the largest forward pass (sizes the work lists)
   void* hbuf = nullptr;
+  void* xs = nullptr;  // bf16: the FFN-normalised rows in expert-sorted, fragment-major order
   void* hs = nullptr;
   float* ybuf = nullptr;
   void* hn = nullptr;
@@ -367,6 +374,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->rows_cap = Tm;
   c->n_units = cv.take<int32_t>(3 * 4);  // up list, down list, expert-sorted rows
   c->hbuf = cv.take<void>(srows * m.expert_hidden * es);
+  c->xs = cv.take<void>(m.dtype == DG_BF16 ? srows * d * es : 0);  // the sorted rows, fragment-major
   c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
   c->ybuf = cv.take<float>(Tm * k * d * 4);
   c->hn = cv.take<void>(Rs * d * es);
@@ -560,6 +568,12 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   return pend;
 }
 
+// Kernel of the routed launches: DG_ROUTED_KERNEL for bf16 experts, k_ws for
+// the codes that are widened on the way (E4M3, MXFP4).
+int routed_kernel(const dg_ctx* c) {
+  return c->dtype == DG_BF16 && c->cfg.expert_format == DG_EXPERTS_NATIVE ? DG_ROUTED_KERNEL : 0;
+}
+
 // Routed launch over the expert work list; with FP8 experts W0 / W1 hold E4M3
 // codes and s0 / s1 their per-row scales ([E][N] each), with MXFP4 experts
 // packed E2M1 codes and b0 / b1 their E8M0 block scales ([E][N][K / 32] each).
@@ -595,8 +609,10 @@ void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void
   a.n_units = n_units;
   a.out = out;
   a.ldo = ldo;
+  // bf16 experts: k_wsd; codes that are widened on the way (E4M3, MXFP4) keep k_ws
   const int grid = dg_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, DG_WS_GROUP_ROWS, nblk);
-  REFUSE_IF(c, dg_launch_ws(epi, a, grid, c->stream) != 0, "routed projection");
+  if (routed_kernel(c) == 1) REFUSE_IF(c, dg_launch_wsd(epi, a, grid, c->stream) != 0, "routed projection");
+  else REFUSE_IF(c, dg_launch_ws(epi, a, grid, c->stream) != 0, "routed projection");
 }
 
 void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg) {
@@ -817,13 +833,20 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
                                          c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, nb_up, c->units_up,
                                          c->n_units, nb_dn, c->units_dn, c->n_units + 1, s));
-    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU gathering the
-    // row-major normalised rows into c->hbuf (fragment-major, sorted rows), W2
-    // from there into c->ybuf at each row's pair index
-    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, w.w1_scale, w.w3_scale,
-                                         w.w1_mx_scale, w.w3_mx_scale, (size_t)m.expert_hidden * m.d_model,
-                                         m.d_model, m.expert_hidden, c->units_up, c->n_units, nb_up, c->hbuf,
-                                         m.expert_hidden, c->rowsrc));
+    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU into c->hbuf
+    // (fragment-major, sorted rows), W2 from there into c->ybuf at each row's
+    // pair index.  k_wsd reads the sorted rows gathered once into the
+    // fragment-major c->xs (contiguous 1 KB fragments instead of a 16-row
+    // gather per fragment and n-block); k_ws gathers from the row-major rows.
+    const bool sorted_copy = routed_kernel(c) == 1;
+    if (sorted_copy)
+      KT(c, DG_KF_PERMUTE, dg_launch_gather_fm(c->xr, c->rowsrc, c->n_units + 2,
+                                               dg_sorted_rows(m.n_experts, rows * m.top_k), m.d_model, c->xs, s));
+    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, sorted_copy ? c->xs : c->xr, w.w1, w.w3, w.w1_scale,
+                                         w.w3_scale, w.w1_mx_scale, w.w3_mx_scale,
+                                         (size_t)m.expert_hidden * m.d_model, m.d_model, m.expert_hidden,
+                                         c->units_up, c->n_units, nb_up, c->hbuf, m.expert_hidden,
+                                         sorted_copy ? nullptr : c->rowsrc));
     KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, w.w2_scale, nullptr,
                                            w.w2_mx_scale, nullptr, (size_t)m.d_model * m.expert_hidden,
                                            m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,

@@ -205,20 +205,6 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
 
 // s_waitcnt with only the vector-memory counter: wait until at most n of this
 // wave's vector loads are outstanding (n <= 63).
-#define DG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-
-// One global_load_lds_dwordx4: lane l copies 16 bytes from g (its own address)
-// to lds + 16 l (lds wave-uniform).  Issued from an asm statement with inputs
-// only (the LDS base goes to M0), so that the compiler adds no wait of its own
-// for it: the kernel's explicit vmcnt waits and barriers order these copies
-// against the LDS reads.  The statement writes no register.
-__device__ __forceinline__ void lds_dma16(const void* g, const uint4* lds) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(a)), "v"(g)
-               : "memory", "m0");
-}
 
 // bf16 attention with the K and V^T tiles of 32 keys brought from HBM straight
 // into LDS by the load unit (global_load_lds: lane l of a load instruction

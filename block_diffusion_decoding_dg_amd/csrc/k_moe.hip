@@ -317,6 +317,43 @@ void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, 
   dg_launch_ws_units(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
 }
 
+// The expert-sorted rows in the fragment-major layout (fm_index, K columns):
+// sorted row r < *n_srows is row rowsrc[r] of the row-major bf16 source (zero
+// on padding rows; K a multiple of 32 GF).  One wave per GF consecutive 1 KB
+// blocks of the layout (16 rows x 32 elements each, same rows): lane l copies
+// the 16 bytes of row l % 16 at elements 8 (l / 16) of each, so the writes are
+// contiguous, each row's reads are 64-byte runs, and GF loads are in flight
+// per lane.
+template <int GF>
+__global__ void __launch_bounds__(256) k_gather_fm(const bf16_t* __restrict__ src, const int32_t* __restrict__ rowsrc,
+                                                   const int32_t* __restrict__ n_srows, int K, int ngroups,
+                                                   uint4* __restrict__ out) {
+  const int grp = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (grp >= ngroups) return;
+  const int gpt = K / 32 / GF, tile = grp / gpt, kblk0 = (grp - tile * gpt) * GF;
+  if (tile * 16 >= *n_srows) return;  // uniform over the wave
+  const int t = rowsrc[tile * 16 + (lane & 15)];
+  const bf16_t* row = src + (size_t)max(t, 0) * K + kblk0 * 32 + (lane >> 4) * 8;
+  uint4 v[GF];
+#pragma unroll
+  for (int i = 0; i < GF; ++i) v[i] = t >= 0 ? *(const uint4*)(row + i * 32) : make_uint4(0u, 0u, 0u, 0u);
+  uint4* o = out + ((size_t)tile * (K / 32) + kblk0) * 64 + lane;
+#pragma unroll
+  for (int i = 0; i < GF; ++i) o[i * 64] = v[i];
+}
+
+void dg_launch_gather_fm(const void* src, const int32_t* rowsrc, const int32_t* n_srows, int srows_max, int K,
+                         void* out, hipStream_t s) {
+  // four blocks per wave where K allows it, else two (K is a multiple of 64)
+  const int gf = K % 128 == 0 ? 4 : 2;
+  const int ngroups = srows_max / 16 * (K / 32 / gf);
+  if (ngroups <= 0) return;
+  if (gf == 4)
+    k_gather_fm<4><<<(ngroups + 3) / 4, 256, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, ngroups, (uint4*)out);
+  else
+    k_gather_fm<2><<<(ngroups + 3) / 4, 256, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, ngroups, (uint4*)out);
+}
+
 // ---------------------------------------------------------------------------
 // Expert up-projection with SwiGLU: for expert e's rows (pairs p, token t = p / k),
 // h[p] = silu(W1_e b[t]) * (W3_e b[t]).  Block = (expert, 64 output columns); each
