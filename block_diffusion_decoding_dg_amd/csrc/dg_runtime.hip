@@ -1328,6 +1328,7 @@ int32_t dg_debug_refusal_count(void) { return 11; }
 dg_status dg_debug_refusal_case(int32_t i, char* msg, size_t msg_bytes) {
   if (i < 0 || i >= dg_debug_refusal_count()) return DG_ERR_INVALID_ARG;
   dg_ctx c;  // host-only stub: no stream, no device buffers
+  memset(&c.cfg, 0, sizeof c.cfg);  // bf16 experts in native format, every size zero but those below
   c.cfg.d_model = 64;
   c.cfg.n_experts = 8;
   c.cfg.top_k = 2;
