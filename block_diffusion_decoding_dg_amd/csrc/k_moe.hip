@@ -319,39 +319,36 @@ void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, 
 
 // The expert-sorted rows in the fragment-major layout (fm_index, K columns):
 // sorted row r < *n_srows is row rowsrc[r] of the row-major bf16 source (zero
-// on padding rows; K a multiple of 32 GF).  One wave per GF consecutive 1 KB
-// blocks of the layout (16 rows x 32 elements each, same rows): lane l copies
-// the 16 bytes of row l % 16 at elements 8 (l / 16) of each, so the writes are
-// contiguous, each row's reads are 64-byte runs, and GF loads are in flight
-// per lane.
-template <int GF>
-__global__ void __launch_bounds__(256) k_gather_fm(const bf16_t* __restrict__ src, const int32_t* __restrict__ rowsrc,
-                                                   const int32_t* __restrict__ n_srows, int K, int ngroups,
-                                                   uint4* __restrict__ out) {
-  const int grp = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (grp >= ngroups) return;
-  const int gpt = K / 32 / GF, tile = grp / gpt, kblk0 = (grp - tile * gpt) * GF;
-  if (tile * 16 >= *n_srows) return;  // uniform over the wave
-  const int t = rowsrc[tile * 16 + (lane & 15)];
-  const bf16_t* row = src + (size_t)max(t, 0) * K + kblk0 * 32 + (lane >> 4) * 8;
-  uint4 v[GF];
-#pragma unroll
-  for (int i = 0; i < GF; ++i) v[i] = t >= 0 ? *(const uint4*)(row + i * 32) : make_uint4(0u, 0u, 0u, 0u);
-  uint4* o = out + ((size_t)tile * (K / 32) + kblk0) * 64 + lane;
-#pragma unroll
-  for (int i = 0; i < GF; ++i) o[i * 64] = v[i];
+// on padding rows).  A block copies one 16-row tile x CG columns (CG / 32
+// blocks of 1 KB of the layout): it reads each of the 16 rows as a contiguous
+// run of 2 CG bytes into LDS (row stride padded by 16 bytes so the transposed
+// reads are free of bank conflicts) and writes the 1 KB blocks contiguously.
+template <int CG>
+__global__ void __launch_bounds__(CG * 2) k_gather_fm(const bf16_t* __restrict__ src,
+                                                      const int32_t* __restrict__ rowsrc,
+                                                      const int32_t* __restrict__ n_srows, int K,
+                                                      uint4* __restrict__ out) {
+  constexpr int SEGS = CG / 8;  // 16-byte segments per row
+  __shared__ uint4 s[16][SEGS + 1];
+  const int groups = K / CG, tile = blockIdx.x / groups, cg = blockIdx.x - tile * groups;
+  if (tile * 16 >= *n_srows) return;  // uniform over the block
+  const int t = threadIdx.x, row = t / SEGS, seg = t - row * SEGS;
+  const int srow = rowsrc[tile * 16 + row];
+  s[row][seg] = srow >= 0 ? *(const uint4*)(src + (size_t)srow * K + cg * CG + seg * 8) : make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  // 1 KB block b of the layout: lane l holds row l % 16, elements 8 (l / 16) of its 32
+  const int b = t / 64, l = t & 63;
+  out[((size_t)tile * (K / 32) + cg * (CG / 32) + b) * 64 + l] = s[l & 15][b * 4 + (l >> 4)];
 }
 
 void dg_launch_gather_fm(const void* src, const int32_t* rowsrc, const int32_t* n_srows, int srows_max, int K,
                          void* out, hipStream_t s) {
-  // four blocks per wave where K allows it, else two (K is a multiple of 64)
-  const int gf = K % 128 == 0 ? 4 : 2;
-  const int ngroups = srows_max / 16 * (K / 32 / gf);
-  if (ngroups <= 0) return;
-  if (gf == 4)
-    k_gather_fm<4><<<(ngroups + 3) / 4, 256, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, ngroups, (uint4*)out);
-  else
-    k_gather_fm<2><<<(ngroups + 3) / 4, 256, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, ngroups, (uint4*)out);
+  const int tiles = srows_max / 16;
+  if (tiles <= 0) return;
+  // 128 columns per block where K allows it, else 64 (K is a multiple of 64)
+  if (K % 128 == 0)
+    k_gather_fm<128><<<tiles * (K / 128), 256, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, (uint4*)out);
+  else k_gather_fm<64><<<tiles * (K / 64), 128, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, (uint4*)out);
 }
 
 // ---------------------------------------------------------------------------

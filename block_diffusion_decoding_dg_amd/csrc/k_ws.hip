@@ -468,6 +468,39 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         if (j >= mt_act) break;
+        if constexpr (EPI == WS_EPI_ROPE_QKV) {
+          // V into the transposed cache: a lane holds 4 consecutive rows (cache
+          // positions) of one column, so when they are valid, of one request
+          // and start at a position divisible by 4 the lane writes them as one
+          // 8-byte run (4 lanes: 32 contiguous bytes per column); else per row
+          const int per_head = a.hd / 64, head = nb / per_head;
+          if (head >= a.hq + a.hkv) {
+            const int rl0 = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4, r0 = row0 + rl0;
+            bool run = rl0 + 3 < cnt;
+            int si = 0, pos = 0;
+            if (run) {
+              si = seg_index(a.segs, r0);
+              pos = a.segs.s[si].pos0 + (r0 - a.segs.s[si].row0);
+              run = seg_index(a.segs, r0 + 3) == si && (pos & 3) == 0;
+            }
+            if (run) {
+              const int half = a.hd / 2, hl = head - a.hq - a.hkv;
+              bf16_t* vt = (bf16_t*)a.segs.s[si].vt + (size_t)hl * a.hd * a.max_ctx;
+#pragma unroll
+              for (int n = 0; n < 2; ++n) {
+                const int jj = (nb - head * per_head) * 32 + n * 16 + (lane & 15);
+                const uint2 lo = make_uint2((uint32_t)f2bf(acc[j][n][0]) | ((uint32_t)f2bf(acc[j][n][1]) << 16),
+                                            (uint32_t)f2bf(acc[j][n][2]) | ((uint32_t)f2bf(acc[j][n][3]) << 16));
+                const uint2 hi =
+                    make_uint2((uint32_t)f2bf(acc[j][n + 2][0]) | ((uint32_t)f2bf(acc[j][n + 2][1]) << 16),
+                               (uint32_t)f2bf(acc[j][n + 2][2]) | ((uint32_t)f2bf(acc[j][n + 2][3]) << 16));
+                *(uint2*)(vt + (size_t)jj * a.max_ctx + pos) = lo;
+                *(uint2*)(vt + (size_t)(jj + half) * a.max_ctx + pos) = hi;
+              }
+              continue;
+            }
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rl = pbase + (wave + NWAVE * j) * 16 + (lane >> 4) * 4 + i;
