@@ -111,21 +111,25 @@ def step_flops(w, P, rows, n_open):
 def measured_traffic(w):
     """HBM bytes per launch of the dominant kernel (bf16, FP8 or MXFP4 experts, per the
     workload) from the committed rocprofv3 counter summary (FETCH_SIZE +
-    WRITE_SIZE, copy-calibrated), or None when the kernel source has changed
-    since the counters were taken or the summary has no figure for it."""
+    WRITE_SIZE, copy-calibrated), or None when the kernel's source has changed
+    since the counters were taken or the summary has no figure for it.  The bf16
+    experts run on k_wsd, the FP8 and MXFP4 codes on k_ws."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "ws_hbm_traffic.md")
-    src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", "k_ws.hip")
+    src_name, sha_key = {"fp8": ("k_ws.hip", "k_ws_source_sha256"),
+                         "mxfp4": ("k_ws.hip", "k_ws_source_sha256")}.get(w.expert_format,
+                                                                         ("k_wsd.hip", "k_wsd_source_sha256"))
+    src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", src_name)
     try:
         key = {"fp8": "expert_up_fp8_traffic_bytes_per_launch",
                "mxfp4": "expert_up_mxfp4_traffic_bytes_per_launch"}.get(w.expert_format,
                                                                          "expert_up_traffic_bytes_per_launch")
         fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and l.split(": ", 1)[0]
-                      in (key, "k_ws_source_sha256"))
+                      in (key, sha_key))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if fields.get("k_ws_source_sha256", "").strip() != sha or key not in fields:
+    if fields.get(sha_key, "").strip() != sha or key not in fields:
         return None
     if w.n_requests != 1 or w.prompt_len != 4096:  # the counters were taken on the one-request workload
         return None
