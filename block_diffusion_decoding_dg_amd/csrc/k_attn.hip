@@ -203,9 +203,6 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
   }
 }
 
-// s_waitcnt with only the vector-memory counter: wait until at most n of this
-// wave's vector loads are outstanding (n <= 63).
-
 // bf16 attention with the K and V^T tiles of 32 keys brought from HBM straight
 // into LDS by the load unit (global_load_lds: lane l of a load instruction
 // writes its 16 bytes at offset 16 l of the instruction's 1 KB destination), in
