@@ -24,6 +24,7 @@ struct DgShape {
 };
 
 #define DG_MAX_TOPK 16  // routed experts per token, at most
+#define DG_ROUTE_MAX_ROWS 2048  // rows of the one-block routing tail and of the routing scatter, at most
 
 // dtype: 0 = f32, 1 = bf16 (weights, activations and cache).
 void dg_launch_embed(int dtype, const int32_t* ids, int rows, const void* embed, int d, int vocab, float* x,
@@ -67,18 +68,22 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
 // Router top-k, histogram, offsets, permutation, the expert-sorted row layout
 // (offsets16[e]: first row of expert e, 16-aligned; rowsrc[r]: token of sorted row
 // r, -1 on padding rows, for r < *n_srows) and both grouped work lists
-// (dg_launch_ws_units); everything after the top-k in one block for rows <= 2048.
+// (dg_launch_ws_units; lpt: longest-first lists for k_wsd); everything after
+// the top-k in one block for rows <= 2048.
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
                      int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b,
-                     int32_t* n_b, hipStream_t s);
+                     int32_t* n_b, hipStream_t s, int lpt = 0);
+// The routing after the top-k in one launch of parallel blocks (rows <= 2048,
+// E <= 256; as k_route_tail): counts, offsets, perm, the expert-sorted layout
+// (offsets16, rowsrc) and both work lists (lpt: longest first).  Returns -1
+// (nothing launched) outside those limits.
+int dg_launch_route_perm(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows, int part_rows, int nblk_a,
+                         int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b, int lpt,
+                         hipStream_t s);
 // Rows of the expert-sorted layout: pairs + 16 per expert.
 inline int dg_sorted_rows(int E, int pairs) { return pairs + 16 * E; }
-// The expert-sorted rows (rowsrc, *n_srows <= srows_max, a multiple of 16) of the
-// row-major bf16 src ([rows][K]) copied into the fragment-major layout out
-// ([srows][K], fm_index), zeros on padding rows.
-void dg_launch_gather_fm(const void* src, const int32_t* rowsrc, const int32_t* n_srows, int srows_max, int K,
-                         void* out, hipStream_t s);
 // Routed experts: up (SwiGLU) into h [rows*k][eh] (dtype), down into y [rows*k][d] fp32.
 void dg_launch_expert_up(int dtype, const void* b, int rows, int d, int E, int k, int eh, const void* w1,
                          const void* w3, const int32_t* counts, const int32_t* offsets, const int32_t* perm, void* h,
@@ -190,6 +195,7 @@ struct WsArgs {
   int N;                  // weight rows per group (SwiGLU: hidden width); stores are masked to it
   int M;                  // rows of the single group when counts is null
   const int32_t* M_dev;   // if set (and counts null): the row count, read on the device
+  int span;               // k_wsd: n-blocks per unit of the work list (0 = 1), swept in turn
   int msplit;             // dense launches: row ranges per n-block; 0 or 1 = none
   int ksplit;             // dense add launches: reduction ranges per n-block (partial sums); 0 or 1 = none
   int kchunks;            // with ksplit: 64-element chunks of the reduction per range
@@ -232,6 +238,115 @@ __device__ __forceinline__ void dg_fill_units(int32_t* __restrict__ units, int f
                                                  : (int32_t)DG_WS_UNIT_NONE;
 }
 
+// Longest-first work lists (k_wsd).  A block's time grows with the rows of its
+// part (more consumer waves load activations and run the matrix cores), and
+// blocks start in list order, so the list holds the parts in decreasing order
+// of their 16-row tiles (ties: expert order, then part order) and each part's
+// n-blocks (or spans of n-blocks) side by side: the last blocks to start are
+// the shortest, and the launch ends with fewer CUs idle.
+//
+// dg_sort_parts: called by every thread of a block of at least 256 threads;
+// thread e < 256 passes expert e's row count (0 for e >= E).  Writes part q of
+// the order to plist[q] as expert << 8 | part and returns the number of parts.
+// s_scan: 256 entries of LDS scratch; plist: LDS, room for E + pairs / part_rows.
+#define DG_WS_MAX_PARTS 512  // parts a longest-first list can hold (E + pairs / part_rows)
+__device__ __forceinline__ int dg_sort_parts(int e, int cnt, int part_rows, ulonglong2* s_scan, int32_t* plist) {
+  // per expert: parts with 8 tiles (full parts) and the tiles of a shorter
+  // last part, as 16-bit counts per tile class (classes 1..4 in x, 5..8 in y)
+  const int tiles_full = (part_rows + 15) / 16;
+  const int parts = cnt > 0 ? (cnt + part_rows - 1) / part_rows : 0;
+  const int rlast = cnt - (parts - 1) * part_rows, wl = min((rlast + 15) / 16, 8);
+  const int full = parts > 0 ? parts - 1 + (rlast == part_rows) : 0;
+  auto add = [](ulonglong2& v, int cls, unsigned long long n) {
+    if (cls <= 4) v.x += n << (16 * (cls - 1));
+    else v.y += n << (16 * (cls - 5));
+  };
+  auto get = [](const ulonglong2& v, int cls) -> int {
+    return (int)((cls <= 4 ? v.x >> (16 * (cls - 1)) : v.y >> (16 * (cls - 5))) & 0xffff);
+  };
+  ulonglong2 own = make_ulonglong2(0ull, 0ull);
+  if (e < 256) {
+    if (full) add(own, min(tiles_full, 8), (unsigned long long)full);
+    if (parts > 0 && rlast != part_rows) add(own, wl, 1ull);
+    s_scan[e] = own;
+  }
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive scan over the experts, field by field
+    ulonglong2 v = make_ulonglong2(0ull, 0ull);
+    if (e < 256 && e >= o) v = s_scan[e - o];
+    __syncthreads();
+    if (e < 256) {
+      s_scan[e].x += v.x;
+      s_scan[e].y += v.y;
+    }
+    __syncthreads();
+  }
+  const ulonglong2 tot = s_scan[255];
+  if (e < 256 && parts > 0) {
+    const ulonglong2 inc = s_scan[e];
+    const ulonglong2 exc = make_ulonglong2(inc.x - own.x, inc.y - own.y);
+    auto first_of = [&](int cls) {  // classes in decreasing order
+      int f = 0;
+      for (int k = 8; k > cls; --k) f += get(tot, k);
+      return f;
+    };
+    const int cf = min(tiles_full, 8);
+    for (int p = 0; p < full; ++p) plist[first_of(cf) + get(exc, cf) + p] = (e << 8) | p;
+    if (rlast != part_rows) plist[first_of(wl) + get(exc, wl) + (wl == cf ? full : 0)] = (e << 8) | (parts - 1);
+  }
+  int n = 0;
+  for (int k = 1; k <= 8; ++k) n += get(tot, k);
+  __syncthreads();
+  return n;
+}
+
+// Both grouped work lists from the experts' row counts, in one block of at least
+// 256 threads (thread e < 256 passes expert e's count, 0 for e >= E): longest first
+// (lpt, dg_sort_parts; unit u is n-block u % nblk of part u / nblk, no padding)
+// or in expert order with each part's units padded to ceil8(nblk)
+// (dg_fill_units).  Writes the list lengths to *n_a, *n_b.
+__device__ __forceinline__ void dg_build_lists(int e, int cnt, int part_rows, int nblk_a, int32_t* __restrict__ units_a,
+                                               int32_t* __restrict__ n_a, int nblk_b,
+                                               int32_t* __restrict__ units_b, int32_t* __restrict__ n_b, int lpt) {
+  __shared__ ulonglong2 s_sc[256];
+  __shared__ int32_t s_plist[DG_WS_MAX_PARTS];
+  if (lpt) {
+    const int np = dg_sort_parts(e, cnt, part_rows, s_sc, s_plist);
+    for (int u = e; u < np * (nblk_a + nblk_b); u += blockDim.x) {
+      const bool first = u < np * nblk_a;
+      const int v = first ? u : u - np * nblk_a, nb = first ? nblk_a : nblk_b;
+      const int q = v / nb, b = v - q * nb, ep = s_plist[q];
+      const int32_t code = (int32_t)(((uint32_t)(ep >> 8) << 24) | ((uint32_t)(ep & 0xff) << 16) | (uint32_t)b);
+      if (first) units_a[v] = code;
+      else units_b[v] = code;
+    }
+    if (e == 0) {
+      *n_a = np * nblk_a;
+      *n_b = np * nblk_b;
+    }
+    return;
+  }
+  int* s_scan = (int*)s_sc;  // 256 ints
+  const int parts = cnt > 0 ? (cnt + part_rows - 1) / part_rows : 0;
+  if (e < 256) s_scan[e] = parts;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = e < 256 && e >= o ? s_scan[e - o] : 0;
+    __syncthreads();
+    if (e < 256) s_scan[e] += v;
+    __syncthreads();
+  }
+  if (e < 256) {
+    const int before = s_scan[e] - parts;  // exclusive prefix
+    dg_fill_units(units_a, before, parts, e, nblk_a);
+    dg_fill_units(units_b, before, parts, e, nblk_b);
+  }
+  if (e == 255) {
+    *n_a = s_scan[255] * ((nblk_a + 7) & ~7);
+    *n_b = s_scan[255] * ((nblk_b + 7) & ~7);
+  }
+}
+
 // Returns 0, or -1 for a configuration the kernels do not implement (nothing launched).
 int dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s);
 
@@ -242,11 +357,15 @@ inline int dg_unit_slots(int E, int pairs, int part_rows, int nblk) {
 }
 // Grouped launch of bf16 routed-expert weights with producer waves copying the
 // weight tiles straight into LDS and consumer waves on the matrix cores (k_wsd):
-// SwiGLU (W1 / W3) or an fp32 store (W2), A fragment-major over the
-// expert-sorted rows (no rowsrc), on the work list of a.units (DG_WS_GROUP_ROWS
-// rows per part).  Returns -1 (nothing launched) for any other combination.
+// SwiGLU (W1 / W3; A row-major, its sorted rows read through rowsrc when set)
+// or an fp32 store (W2; A row-major at the expert-sorted rows), on the work list
+// of a.units (DG_WS_GROUP_ROWS rows per part, a.span n-blocks per unit).  The
+// SwiGLU output is row-major at the expert-sorted rows.  Returns -1 (nothing
+// launched) for any other combination.
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s);
-// Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b);
-// each list needs dg_unit_slots(E, rows * k, part_rows, nblk) entries.
+
+// Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b;
+// lpt: longest-first lists for k_wsd, nblk then counting spans); each list needs
+// dg_unit_slots(E, rows * k, part_rows, nblk) entries.
 void dg_launch_ws_units(const int32_t* counts, int E, int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a,
-                        int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s);
+                        int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s, int lpt = 0);

@@ -27,10 +27,25 @@
 #define DG_MAX_KSPLIT 8
 #endif
 // Kernel of the bf16 routed experts: 1 producer / consumer waves with the
-// weight tiles copied straight into LDS and the rows gathered once into the
-// fragment-major layout (k_wsd), 0 the register-staged k_ws gathering rows.
+// weight tiles copied straight into LDS (k_wsd, on longest-first work lists),
+// 0 the register-staged k_ws.  Both read the normalised rows through the
+// sorted-row -> token map.
 #ifndef DG_ROUTED_KERNEL
 #define DG_ROUTED_KERNEL 1
+#endif
+// n-blocks per k_wsd unit: W1/W3 (64 rows: 32 hidden columns of each) and W2
+// (64 output columns).  W2's reduction is the expert's hidden width, 11
+// chunks at the full size: a span of several keeps its weight stream from
+// ramping up and draining every 11 chunks.
+// Longest-first work lists for k_wsd (1) or lists in expert order (0).
+#ifndef DG_ROUTE_LPT
+#define DG_ROUTE_LPT 1
+#endif
+#ifndef DG_WSD_SPAN_UP
+#define DG_WSD_SPAN_UP 1
+#endif
+#ifndef DG_WSD_SPAN_DN
+#define DG_WSD_SPAN_DN 2
 #endif
 // Vocabulary ranges of the self-conditioning product, at most.
 #ifndef DG_SC_KSPLIT
@@ -140,7 +155,6 @@ struct dg_ctx {
   int32_t* n_units = nullptr;    // [3]: lengths of the two lists, rows of the expert-sorted layout
   int rows_cap = 0;              // rows of the largest forward pass (sizes the work lists)
   void* hbuf = nullptr;
-  void* xs = nullptr;  // bf16: the FFN-normalised rows in expert-sorted, fragment-major order
   void* hs = nullptr;
   float* ybuf = nullptr;
   void* hn = nullptr;
@@ -374,7 +388,6 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->rows_cap = Tm;
   c->n_units = cv.take<int32_t>(3 * 4);  // up list, down list, expert-sorted rows
   c->hbuf = cv.take<void>(srows * m.expert_hidden * es);
-  c->xs = cv.take<void>(m.dtype == DG_BF16 ? srows * d * es : 0);  // the sorted rows, fragment-major
   c->hs = cv.take<void>(Tm * (size_t)m.shared_hidden * es);
   c->ybuf = cv.take<float>(Tm * k * d * 4);
   c->hn = cv.take<void>(Rs * d * es);
@@ -573,6 +586,11 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
 int routed_kernel(const dg_ctx* c) {
   return c->dtype == DG_BF16 && c->cfg.expert_format == DG_EXPERTS_NATIVE ? DG_ROUTED_KERNEL : 0;
 }
+// n-blocks per unit of a k_wsd work list, and the units per row part.
+int wsd_span(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD_SPAN_DN; }
+int list_blocks(const dg_ctx* c, int epi, int nblk) {
+  return routed_kernel(c) == 1 ? (nblk + wsd_span(epi) - 1) / wsd_span(epi) : nblk;
+}
 
 // Routed launch over the expert work list; with FP8 experts W0 / W1 hold E4M3
 // codes and s0 / s1 their per-row scales ([E][N] each), with MXFP4 experts
@@ -610,9 +628,15 @@ void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void
   a.out = out;
   a.ldo = ldo;
   // bf16 experts: k_wsd; codes that are widened on the way (E4M3, MXFP4) keep k_ws
-  const int grid = dg_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, DG_WS_GROUP_ROWS, nblk);
-  if (routed_kernel(c) == 1) REFUSE_IF(c, dg_launch_wsd(epi, a, grid, c->stream) != 0, "routed projection");
-  else REFUSE_IF(c, dg_launch_ws(epi, a, grid, c->stream) != 0, "routed projection");
+  const int grid =
+      dg_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, DG_WS_GROUP_ROWS, list_blocks(c, epi, nblk));
+  if (routed_kernel(c) == 1) {
+    a.nblk = nblk;
+    a.span = wsd_span(epi);
+    REFUSE_IF(c, dg_launch_wsd(epi, a, grid, c->stream) != 0, "routed projection");
+  } else {
+    REFUSE_IF(c, dg_launch_ws(epi, a, grid, c->stream) != 0, "routed projection");
+  }
 }
 
 void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg) {
@@ -796,7 +820,7 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
   const dg_layer_weights& w = c->layers[l];
   hipStream_t s = c->stream;
   // bf16: fragment-major for the dense projections, and a row-major copy that the
-  // expert-sorted gather reads
+  // routed launches read through the sorted-row -> token map
   KT(c, DG_KF_RMSNORM,
      REFUSE_IF(c, dg_launch_rmsnorm(c->dtype, c->x, nullptr, nullptr, rows, m.d_model, w.ffn_norm, m.rms_eps, c->xn,
                                     c->dtype == DG_BF16, s, c->dtype == DG_BF16 ? c->xr : nullptr, pend) != 0,
@@ -830,23 +854,29 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     HIPCK_V(hipEventRecord(c->ev_join, c->side));
     KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
-    KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets, c->perm,
-                                         c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, nb_up, c->units_up,
-                                         c->n_units, nb_dn, c->units_dn, c->n_units + 1, s));
-    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU into c->hbuf
-    // (fragment-major, sorted rows), W2 from there into c->ybuf at each row's
-    // pair index.  k_wsd reads the sorted rows gathered once into the
-    // fragment-major c->xs (contiguous 1 KB fragments instead of a 16-row
-    // gather per fragment and n-block); k_ws gathers from the row-major rows.
-    const bool sorted_copy = routed_kernel(c) == 1;
-    if (sorted_copy)
-      KT(c, DG_KF_PERMUTE, dg_launch_gather_fm(c->xr, c->rowsrc, c->n_units + 2,
-                                               dg_sorted_rows(m.n_experts, rows * m.top_k), m.d_model, c->xs, s));
-    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, sorted_copy ? c->xs : c->xr, w.w1, w.w3, w.w1_scale,
-                                         w.w3_scale, w.w1_mx_scale, w.w3_mx_scale,
-                                         (size_t)m.expert_hidden * m.d_model, m.d_model, m.expert_hidden,
-                                         c->units_up, c->n_units, nb_up, c->hbuf, m.expert_hidden,
-                                         sorted_copy ? nullptr : c->rowsrc));
+    // routed experts over the expert-sorted rows: W1/W3 + SwiGLU into c->hbuf,
+    // W2 from there into c->ybuf at each row's pair index.  Both kernels read
+    // the normalised rows (row-major c->xr) through rowsrc; k_wsd keeps c->hbuf
+    // row-major, k_ws fragment-major.
+    const bool wsd = routed_kernel(c) == 1;
+    const int la = list_blocks(c, WS_EPI_SWIGLU, nb_up), lb = list_blocks(c, WS_EPI_STORE_F32, nb_dn);
+    if (wsd && rows <= DG_ROUTE_MAX_ROWS && m.n_experts <= 256 && 16 * m.top_k <= 256) {
+      // the permutation and the work lists in one launch of parallel blocks
+      KT(c, DG_KF_PERMUTE, dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s);
+         REFUSE_IF(c, dg_launch_route_perm(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm,
+                                           c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, la,
+                                           c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1,
+                                           DG_ROUTE_LPT, s) != 0,
+                   "routing"));
+    } else {
+      KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets,
+                                           c->perm, c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, la,
+                                           c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1, s, wsd));
+    }
+    KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, w.w1_scale, w.w3_scale, w.w1_mx_scale,
+                                         w.w3_mx_scale, (size_t)m.expert_hidden * m.d_model, m.d_model,
+                                         m.expert_hidden, c->units_up, c->n_units, nb_up, c->hbuf, m.expert_hidden,
+                                         c->rowsrc));
     KT(c, DG_KF_EXPERT_DOWN, launch_routed(c, WS_EPI_STORE_F32, c->hbuf, w.w2, nullptr, w.w2_scale, nullptr,
                                            w.w2_mx_scale, nullptr, (size_t)m.d_model * m.expert_hidden,
                                            m.expert_hidden, m.d_model, c->units_dn, c->n_units + 1, nb_dn, c->ybuf,

@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
     int cnt = 0;
     for (int j = j0; j < j1; ++j) {
       const float w = s_v[j];
-      cnt += (w > v || (w == v && j < e)) ? 1 : 0;
+      cnt += (int)(w > v) | ((int)(w == v) & (int)(j < e));  // bitwise: no short-circuit branches
     }
     if (cnt) atomicAdd(&s_rank[e], cnt);
   }
@@ -176,14 +176,13 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
 // ---------------------------------------------------------------------------
 // Everything after the top-k in one block of 16 waves: the expert histogram and
 // offsets, the token permutation (as k_permute: the pairs of an expert in
-// increasing pair index) and the two grouped work lists (as k_ws_units).  Expert
+// increasing pair index) and the two grouped work lists (dg_build_lists).  Expert
 // e's rows are a bitmap over tokens; a token picks an expert at most once, so the
 // rank of pair (t, e) among e's pairs is the number of e's tokens below t.  Also
 // the expert-sorted row layout of the grouped launches: expert e's rows start at
 // offsets16[e] (its predecessors' counts rounded up to 16); rowsrc[r] is the token
 // of sorted row r (-1 on the padding rows), r < *n_srows.  rows <=
 // DG_ROUTE_MAX_ROWS, E <= 256.
-#define DG_ROUTE_MAX_ROWS 2048
 __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__ ids, int rows, int E, int k,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ offsets16,
@@ -191,10 +190,10 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
                                                      int part_rows, int nblk_a,
                                                      int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                      int nblk_b, int32_t* __restrict__ units_b,
-                                                     int32_t* __restrict__ n_b) {
+                                                     int32_t* __restrict__ n_b, int lpt) {
   constexpr int WPE = DG_ROUTE_MAX_ROWS / 32;  // bitmap words per expert
   __shared__ uint32_t s_bits[256][WPE];
-  __shared__ int s_off[256], s_part[256], s_off16[256];
+  __shared__ int s_off[256], s_off16[256];
   const int tid = threadIdx.x;
   const int nw = (rows + 31) / 32;
   for (int i = tid; i < 256 * nw; i += 1024) s_bits[i / nw][i % nw] = 0u;
@@ -205,32 +204,28 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
     atomicOr(&s_bits[ids[p]][t >> 5], 1u << (t & 31));
   }
   __syncthreads();
-  int cnt = 0, parts = 0;
+  int cnt = 0;
   if (tid < 256) {
     if (tid < E)
       for (int w = 0; w < nw; ++w) cnt += __popc(s_bits[tid][w]);
-    parts = (cnt + part_rows - 1) / part_rows;
     s_off[tid] = cnt;
-    s_part[tid] = parts;
     s_off16[tid] = (cnt + 15) & ~15;
   }
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {  // inclusive scans over the experts
-    int a = 0, b = 0, c = 0;
+    int a = 0, c = 0;
     if (tid < 256 && tid >= o) {
       a = s_off[tid - o];
-      b = s_part[tid - o];
       c = s_off16[tid - o];
     }
     __syncthreads();
     if (tid < 256) {
       s_off[tid] += a;
-      s_part[tid] += b;
       s_off16[tid] += c;
     }
     __syncthreads();
   }
-  const int tot_parts = s_part[255], tot_rows16 = s_off16[255];
+  const int tot_rows16 = s_off16[255];
   __syncthreads();
   if (tid < 256) {  // exclusive: first position of expert tid
     s_off[tid] -= cnt;
@@ -243,30 +238,9 @@ __global__ void __launch_bounds__(1024) k_route_tail(const int32_t* __restrict__
     offsets16[tid] = s_off16[tid];
     for (int r = cnt; r < ((cnt + 15) & ~15); ++r) rowsrc[s_off16[tid] + r] = -1;  // padding rows
   }
-  const int sa = (nblk_a + 7) & ~7, sb = (nblk_b + 7) & ~7;
-  if (tid == 0) {
-    *n_a = tot_parts * sa;
-    *n_b = tot_parts * sb;
-    *n_srows = tot_rows16;
-  }
-  // Work lists (as k_ws_units): part slot q belongs to the expert e with
-  // s_part[e - 1] <= q < s_part[e] (inclusive scan).
-  for (int u = tid; u < tot_parts * (sa + sb); u += 1024) {
-    const bool first = u < tot_parts * sa;
-    const int v = first ? u : u - tot_parts * sa, st = first ? sa : sb, nb = first ? nblk_a : nblk_b;
-    const int q = v / st, b = v - q * st;
-    int lo = 0, hi = 255;  // smallest e with s_part[e] > q
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s_part[mid] > q) hi = mid;
-      else lo = mid + 1;
-    }
-    const int pe = q - (lo > 0 ? s_part[lo - 1] : 0);
-    const int32_t code = b < nb ? (int32_t)(((uint32_t)lo << 24) | ((uint32_t)pe << 16) | (uint32_t)b)
-                                : (int32_t)DG_WS_UNIT_NONE;
-    if (first) units_a[v] = code;
-    else units_b[v] = code;
-  }
+  if (tid == 0) *n_srows = tot_rows16;
+  // work lists (longest first for k_wsd, else in expert order, padded)
+  dg_build_lists(tid, cnt, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, lpt);
   for (int p = tid; p < npairs; p += 1024) {
     const int e = ids[p], t = p / k, tw = t >> 5;
     int rank = __popc(s_bits[e][tw] & ((1u << (t & 31)) - 1u));
@@ -305,51 +279,110 @@ __global__ void __launch_bounds__(256) k_sorted_layout(const int32_t* __restrict
 void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
                      int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b,
-                     int32_t* n_b, hipStream_t s) {
+                     int32_t* n_b, hipStream_t s, int lpt) {
   dg_launch_topk(logits, rows, E, k, ids, gates, s);
+  if (E + (rows * k + part_rows - 1) / part_rows > DG_WS_MAX_PARTS) lpt = 0;  // list order only
   if (rows <= DG_ROUTE_MAX_ROWS && E <= 256) {
     k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, rowsrc, n_srows, part_rows,
-                                    nblk_a, units_a, n_a, nblk_b, units_b, n_b);
+                                    nblk_a, units_a, n_a, nblk_b, units_b, n_b, lpt);
     return;
   }
   dg_launch_permute(ids, rows, E, k, counts, offsets, perm, s);
   k_sorted_layout<<<1, 256, 0, s>>>(counts, offsets, perm, E, k, offsets16, rowsrc, n_srows);
-  dg_launch_ws_units(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s);
+  dg_launch_ws_units(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, s, lpt);
 }
 
-// The expert-sorted rows in the fragment-major layout (fm_index, K columns):
-// sorted row r < *n_srows is row rowsrc[r] of the row-major bf16 source (zero
-// on padding rows).  A block copies one 16-row tile x CG columns (CG / 32
-// blocks of 1 KB of the layout): it reads each of the 16 rows as a contiguous
-// run of 2 CG bytes into LDS (row stride padded by 16 bytes so the transposed
-// reads are free of bank conflicts) and writes the 1 KB blocks contiguously.
-template <int CG>
-__global__ void __launch_bounds__(CG * 2) k_gather_fm(const bf16_t* __restrict__ src,
-                                                      const int32_t* __restrict__ rowsrc,
-                                                      const int32_t* __restrict__ n_srows, int K,
-                                                      uint4* __restrict__ out) {
-  constexpr int SEGS = CG / 8;  // 16-byte segments per row
-  __shared__ uint4 s[16][SEGS + 1];
-  const int groups = K / CG, tile = blockIdx.x / groups, cg = blockIdx.x - tile * groups;
-  if (tile * 16 >= *n_srows) return;  // uniform over the block
-  const int t = threadIdx.x, row = t / SEGS, seg = t - row * SEGS;
-  const int srow = rowsrc[tile * 16 + row];
-  s[row][seg] = srow >= 0 ? *(const uint4*)(src + (size_t)srow * K + cg * CG + seg * 8) : make_uint4(0u, 0u, 0u, 0u);
+// The routing after the top-k, for rows <= DG_ROUTE_MAX_ROWS and E <= 256, in
+// one launch with no global synchronisation (the one-block k_route_tail does
+// the same work in sequence): every block rebuilds the expert histogram from
+// all rows' expert ids (a bitmap over tokens per expert in LDS; the rank of
+// pair (t, e) among e's pairs is the number of e's tokens below t), so each
+// computes the same offsets on its own.  Block i < ceil(rows / 16) writes perm
+// and rowsrc for the pairs of rows 16 i .. 16 i + 15; the last block writes
+// counts, offsets, offsets16, rowsrc on the padding rows, *n_srows and both
+// work lists (dg_build_lists).  The bitmap is in dynamic LDS: E x ceil(rows /
+// 32) words.
+__global__ void __launch_bounds__(256) k_route_perm(const int32_t* __restrict__ ids, int rows, int E, int k,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm, int32_t* __restrict__ offsets16,
+                                                    int32_t* __restrict__ rowsrc, int32_t* __restrict__ n_srows,
+                                                    int part_rows, int nblk_a, int32_t* __restrict__ units_a,
+                                                    int32_t* __restrict__ n_a, int nblk_b,
+                                                    int32_t* __restrict__ units_b, int32_t* __restrict__ n_b,
+                                                    int lpt) {
+  extern __shared__ uint32_t s_bits[];  // [E][nw]
+  __shared__ int s_off[256], s_off16[256];
+  const int tid = threadIdx.x;
+  const int nw = (rows + 31) / 32;
+  for (int i = tid; i < E * nw; i += 256) s_bits[i] = 0u;
   __syncthreads();
-  // 1 KB block b of the layout: lane l holds row l % 16, elements 8 (l / 16) of its 32
-  const int b = t / 64, l = t & 63;
-  out[((size_t)tile * (K / 32) + cg * (CG / 32) + b) * 64 + l] = s[l & 15][b * 4 + (l >> 4)];
+  const int npairs = rows * k;
+  for (int p = tid; p < npairs; p += 256) {
+    const int t = p / k;
+    atomicOr(&s_bits[ids[p] * nw + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < nw; ++w) cnt += __popc(s_bits[tid * nw + w]);
+  s_off[tid] = cnt;
+  s_off16[tid] = (cnt + 15) & ~15;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive scans over the experts
+    int a = 0, c = 0;
+    if (tid >= o) {
+      a = s_off[tid - o];
+      c = s_off16[tid - o];
+    }
+    __syncthreads();
+    s_off[tid] += a;
+    s_off16[tid] += c;
+    __syncthreads();
+  }
+  const int tot16 = s_off16[255];
+  __syncthreads();
+  s_off[tid] -= cnt;  // exclusive: first position of expert tid
+  s_off16[tid] -= (cnt + 15) & ~15;
+  __syncthreads();
+
+  if ((int)blockIdx.x < (rows + 15) / 16) {
+    if (tid < 16 * k) {
+      const int i = tid / k, j = tid - i * k, t = blockIdx.x * 16 + i;
+      if (t < rows) {
+        const int e = ids[t * k + j], tw = t >> 5;
+        int rank = __popc(s_bits[e * nw + tw] & ((1u << (t & 31)) - 1u));
+        for (int w = 0; w < tw; ++w) rank += __popc(s_bits[e * nw + w]);
+        perm[s_off[e] + rank] = t * k + j;
+        rowsrc[s_off16[e] + rank] = t;
+      }
+    }
+    return;
+  }
+  // ---- the last block: counts, offsets, padding rows, work lists
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = s_off[tid];
+    offsets16[tid] = s_off16[tid];
+    for (int r = cnt; r < ((cnt + 15) & ~15); ++r) rowsrc[s_off16[tid] + r] = -1;  // padding rows
+  }
+  if (tid == 0) *n_srows = tot16;
+  dg_build_lists(tid, tid < E ? cnt : 0, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, lpt);
 }
 
-void dg_launch_gather_fm(const void* src, const int32_t* rowsrc, const int32_t* n_srows, int srows_max, int K,
-                         void* out, hipStream_t s) {
-  const int tiles = srows_max / 16;
-  if (tiles <= 0) return;
-  // 128 columns per block where K allows it, else 64 (K is a multiple of 64)
-  if (K % 128 == 0)
-    k_gather_fm<128><<<tiles * (K / 128), 256, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, (uint4*)out);
-  else k_gather_fm<64><<<tiles * (K / 64), 128, 0, s>>>((const bf16_t*)src, rowsrc, n_srows, K, (uint4*)out);
+int dg_launch_route_perm(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows, int part_rows, int nblk_a,
+                         int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b, int32_t* n_b, int lpt,
+                         hipStream_t s) {
+  if (rows <= 0) return 0;
+  if (rows > DG_ROUTE_MAX_ROWS || E > 256 || k > DG_MAX_TOPK || 16 * k > 256) return -1;
+  if (E + (rows * k + part_rows - 1) / part_rows > DG_WS_MAX_PARTS) lpt = 0;  // list order only
+  const size_t lds = (size_t)E * ((rows + 31) / 32) * 4;
+  k_route_perm<<<(rows + 15) / 16 + 1, 256, lds, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, rowsrc,
+                                                      n_srows, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b,
+                                                      lpt);
+  return 0;
 }
+
 
 // ---------------------------------------------------------------------------
 // Expert up-projection with SwiGLU: for expert e's rows (pairs p, token t = p / k),

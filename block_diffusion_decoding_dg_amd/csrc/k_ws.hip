@@ -581,7 +581,7 @@ __global__ void __launch_bounds__(NT) k_ws(WsArgs a) {
 // Work lists of two grouped launches over the same groups.  A group with c rows
 // is cut into ceil(c / DG_WS_GROUP_ROWS) row parts (one pass of the kernel each),
 // and every (group, part, n-block) is one unit: group << 24 | part << 16 | n-block.
-// The list holds, for each part in group order, ceil8(nblk) slots, n-blocks in
+// Longest-first lists (k_wsd) are described with dg_sort_parts.  Else the list holds, for each part in group order, ceil8(nblk) slots, n-blocks in
 // order and DG_WS_UNIT_NONE in the padding.  Work-groups are dealt to the 8 XCDs
 // in turn (block u runs on XCD u % 8), so every part of n-block b of a group runs
 // on XCD b % 8 and the parts after the first find that weight tile in its L2.
@@ -590,26 +590,9 @@ __global__ void __launch_bounds__(256) k_ws_units(const int32_t* __restrict__ co
                                                   int nblk_a,
                                                   int32_t* __restrict__ units_a, int32_t* __restrict__ n_a,
                                                   int nblk_b, int32_t* __restrict__ units_b,
-                                                  int32_t* __restrict__ n_b) {
-  __shared__ int s_scan[256];
+                                                  int32_t* __restrict__ n_b, int lpt) {
   const int e = threadIdx.x;
-  const int c = e < E ? counts[e] : 0;
-  const int parts = (c + part_rows - 1) / part_rows;
-  s_scan[e] = parts;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int v = e >= o ? s_scan[e - o] : 0;
-    __syncthreads();
-    s_scan[e] += v;
-    __syncthreads();
-  }
-  const int before = s_scan[e] - parts;  // exclusive prefix
-  dg_fill_units(units_a, before, parts, e, nblk_a);
-  dg_fill_units(units_b, before, parts, e, nblk_b);
-  if (e == 255) {
-    *n_a = s_scan[255] * ((nblk_a + 7) & ~7);
-    *n_b = s_scan[255] * ((nblk_b + 7) & ~7);
-  }
+  dg_build_lists(e, e < E ? counts[e] : 0, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, lpt);
 }
 
 }  // namespace
@@ -677,6 +660,6 @@ int dg_launch_ws(int epi, const WsArgs& a, int grid, hipStream_t s) {
 }
 
 void dg_launch_ws_units(const int32_t* counts, int E, int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a,
-                        int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s) {
-  k_ws_units<<<1, 256, 0, s>>>(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b);
+                        int nblk_b, int32_t* units_b, int32_t* n_b, hipStream_t s, int lpt) {
+  k_ws_units<<<1, 256, 0, s>>>(counts, E, part_rows, nblk_a, units_a, n_a, nblk_b, units_b, n_b, lpt);
 }
