@@ -55,7 +55,10 @@ void dg_launch_swiglu(int dtype, const void* A, int M, int K, const void* w1, co
                       hipStream_t s);
 // Attention: q [rows][hq*hd] (dtype), output o [rows][hq*hd] (dtype).  Uses the
 // split-KV partial buffers (fp32): opart [nsplit][rows*hq][hd], mlpart [nsplit][rows*hq][2].
-int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits);
+// Query rows per block of the attention kernel (dtype 1: bf16), and the key
+// splits for a launch (about one block per CU, at least 8 key tiles per split).
+int dg_attn_qrows(int dtype, int hd);
+int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits, int qrows);
 void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSegs& segs, int nsplit, float* opart,
                          float* mlpart, void* o, int rows, hipStream_t s);
 // Router top-k: logits [rows][E] fp32 -> ids [rows][k], gates [rows][k].
@@ -363,6 +366,13 @@ inline int dg_unit_slots(int E, int pairs, int part_rows, int nblk) {
 // SwiGLU output is row-major at the expert-sorted rows.  Returns -1 (nothing
 // launched) for any other combination.
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s);
+// Dense launch of k_wsd: one bf16 weight matrix (a.W0, q/k/v: a.W0..W2; SwiGLU:
+// W1 = a.W0, W3 = a.W1) on a.M fragment-major rows, a.nblk n-blocks of 64
+// weight rows, a.msplit parts of DG_WS_GROUP_ROWS rows (covering a.M), and for
+// WS_EPI_ADD_F32 optionally a.ksplit reduction ranges of a.kchunks chunks
+// (partial sums into a.part_out); the epilogues of k_ws.  Returns -1 (nothing
+// launched) for any other combination.
+int dg_launch_wsd_dense(int epi, const WsArgs& a, hipStream_t s);
 
 // Work lists of two grouped launches over the same groups (n-blocks per group nblk_a / nblk_b;
 // lpt: longest-first lists for k_wsd, nblk then counting spans); each list needs

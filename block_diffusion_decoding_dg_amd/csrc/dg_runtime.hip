@@ -37,6 +37,12 @@
 // (64 output columns).  W2's reduction is the expert's hidden width, 11
 // chunks at the full size: a span of several keeps its weight stream from
 // ramping up and draining every 11 chunks.
+// Kernel of the dense bf16 projections (q/k/v, output projection, shared
+// expert, self-conditioning MLP): 1 k_wsd's dense form (weight tiles copied
+// straight into LDS by producer waves), 0 the register-staged k_ws.
+#ifndef DG_DENSE_KERNEL
+#define DG_DENSE_KERNEL 1
+#endif
 // Longest-first work lists for k_wsd (1) or lists in expert order (0).
 #ifndef DG_ROUTE_LPT
 #define DG_ROUTE_LPT 1
@@ -518,6 +524,12 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
   a.out = out;
   a.ldo = ldo;
   const int nblk = epi == WS_EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
+  if (DG_DENSE_KERNEL == 1) {  // 64 weight rows per n-block (SwiGLU: 32 W1 + 32 W3), 128-row parts
+    a.nblk = nblk;
+    a.msplit = (M + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+    REFUSE_IF(c, dg_launch_wsd_dense(epi, a, st ? st : c->stream) != 0, "dense projection");
+    return;
+  }
   a.nblk = nblk;
   a.msplit = dense_msplit(nblk, M);
   a.mt2 = epi == WS_EPI_SWIGLU && M > 256;  // 256 rows per pass for prefill chunks and eight canvases
@@ -550,6 +562,31 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   a.M = M;
   a.out = out;
   a.ldo = N;
+  if (DG_DENSE_KERNEL == 1) {
+    // k_wsd: 64 output columns per n-block, 128-row parts; the reduction split
+    // into ranges (partial sums folded by the next row kernel) while that keeps
+    // the grid within one block per CU
+    const int nblk = (N + 63) / 64, padded = (nblk + 7) / 8 * 8;
+    a.nblk = nblk;
+    a.msplit = (M + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+    int ks = 1;
+    if (M <= c->parts_rows && N == c->cfg.d_model)
+      ks = std::min(max_ksplit, std::max(1, DG_DENSE_BLOCKS / (padded * a.msplit)));
+    const int nk = K / 64, kchunks = (nk + ks - 1) / ks;
+    ks = (nk + kchunks - 1) / kchunks;  // every range non-empty
+    DgParts pend;
+    if (ks > 1) {
+      a.ksplit = ks;
+      a.kchunks = kchunks;
+      a.part_out = parts;
+      a.part_stride = (size_t)c->parts_rows * N;
+      pend.p = parts;
+      pend.n = ks;
+      pend.stride = a.part_stride;
+    }
+    REFUSE_IF(c, dg_launch_wsd_dense(WS_EPI_ADD_F32, a, st ? st : c->stream) != 0, "add projection");
+    return pend;
+  }
   a.wide = 1;
   // More than 256 rows (prefill chunks, eight canvases): two m-tiles per wave and
   // 256-row parts, so each weight tile is read by half as many blocks.
@@ -664,6 +701,11 @@ void launch_qkv(dg_ctx* c, const dg_layer_weights& w, int rows, const DgSegs& sg
   a.segs = sg;
   const int nblk = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim / 64;
   a.nblk = nblk;
+  if (DG_DENSE_KERNEL == 1) {
+    a.msplit = (rows + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
+    REFUSE_IF(c, dg_launch_wsd_dense(WS_EPI_ROPE_QKV, a, c->stream) != 0, "q/k/v projection");
+    return;
+  }
   a.msplit = dense_msplit(nblk, rows);
   a.mt2 = rows > 256;  // 256 rows per pass for prefill chunks and eight canvases
   REFUSE_IF(c, dg_launch_ws(WS_EPI_ROPE_QKV, a, dense_grid(nblk, a.msplit), c->stream) != 0, "q/k/v projection");
@@ -799,7 +841,7 @@ DgParts attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows,
                                            c->xn, c->dtype == DG_BF16, s));
   KT(c, DG_KF_QKV, launch_qkv(c, w, rows, sg));
   const int max_splits = std::max(1, (int)(c->attn_cap / (size_t)rows));
-  const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64));
+  const int ns = dg_attn_splits(sg, sh, std::min(max_splits, 64), dg_attn_qrows(c->dtype, sh.hd));
   KT(c, DG_KF_ATTENTION, dg_launch_attention(c->dtype, c->q, sh, sg, ns, c->opart, c->mlpart, c->ao, rows, s));
   DgParts pend;
   if (c->dtype == DG_F32)

@@ -239,15 +239,15 @@ __device__ __forceinline__ int kswz(int key) {
   else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);
 }
 
-template <int HD, int QT, int NST>
-__global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
+template <int HD, int QT, int NST, int QR>
+__global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __restrict__ q, DgShape sh, DgSegs sg, int nqb,
                                                      int nsplit, float* __restrict__ opart, float* __restrict__ mlpart,
                                                      int rows_total) {
   typedef v8s F;
   constexpr int NKK = HD / 32;
   constexpr int NHT = HD / 16;
   constexpr int KSEG = HD / 8;            // 16-byte segments per key row
-  constexpr int NTHR = 512 / QT;          // 128 query rows per block, QT m-tiles per wave
+  constexpr int NTHR = QR * 4 / QT;       // QR query rows per block, QT m-tiles (16 rows) per wave
   constexpr int NW = NTHR / 64;
   constexpr int KB = 32 * HD * 2;         // bytes of a K tile (= bytes of a V^T tile)
   constexpr int KI = KB / 1024;           // 1 KB load instructions per tile and matrix
@@ -283,8 +283,8 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
   const DgSeg seg = sg.s[si];
   const int G = sh.hq / sh.hkv;
   const int nq = G * seg.n;
-  if (qb * ATTN_QROWS >= nq) return;  // uniform over the block
-  const int qr0 = qb * ATTN_QROWS + wave * 16 * QT;
+  if (qb * QR >= nq) return;  // uniform over the block
+  const int qr0 = qb * QR + wave * 16 * QT;
   const bool wave_active = qr0 < nq;
 
   int qhead[QT], trow[QT], qpos[QT];
@@ -305,7 +305,7 @@ __global__ void __launch_bounds__(512 / QT, 1) k_attn_lds(const bf16_t* __restri
   int k_hi = min(nkeys, k_lo + chunk);
   if (sg.causal) {
     // largest position among the block's rows (block-uniform)
-    const int first = qb * ATTN_QROWS, last = min(first + ATTN_QROWS, nq) - 1;
+    const int first = qb * QR, last = min(first + QR, nq) - 1;
     const int max_i = (first / seg.n == last / seg.n) ? last % seg.n : seg.n - 1;
     k_hi = min(k_hi, seg.pos0 + max_i + 1);
   }
@@ -553,11 +553,22 @@ __global__ void __launch_bounds__(64) k_attn_merge(const float* __restrict__ opa
   }
 }
 
-int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits) {
+// Query rows per block of the attention kernels (k_attn_lds for bf16).
+int dg_attn_qrows(int dtype, int hd) { return ATTN_QROWS; }
+// m-tiles per wave of k_attn_lds at head_dim 256: 1 (eight waves, two per SIMD)
+// or 2 (four waves, one per SIMD with its whole register file, every K and V^T
+// fragment read from LDS serving two m-tiles; measured slower: with one wave per
+// SIMD nothing hides the latencies -- 72 against 54 us per layer with the merge).
+// Two m-tiles with eight waves do not fit the 256 registers a wave then has.
+#ifndef DG_ATTN_QT256
+#define DG_ATTN_QT256 1
+#endif
+
+int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits, int qrows) {
   int base = 0, maxkeys = 0;
   const int G = sh.hq / sh.hkv;
   for (int i = 0; i < segs.count; ++i) {
-    base += sh.hkv * ((G * segs.s[i].n + ATTN_QROWS - 1) / ATTN_QROWS);
+    base += sh.hkv * ((G * segs.s[i].n + qrows - 1) / qrows);
     maxkeys = maxkeys > segs.s[i].nkeys ? maxkeys : segs.s[i].nkeys;
   }
   // One block per CU at the full head size: aim at 256 blocks, each split at
@@ -576,7 +587,8 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
   const int G = sh.hq / sh.hkv;
   int nmax = 0;
   for (int i = 0; i < segs.count; ++i) nmax = nmax > segs.s[i].n ? nmax : segs.s[i].n;
-  const int nqb = (G * nmax + ATTN_QROWS - 1) / ATTN_QROWS;
+  const int qrows = dg_attn_qrows(dtype, sh.hd);
+  const int nqb = (G * nmax + qrows - 1) / qrows;
   const int blocks = segs.count * sh.hkv * nqb * nsplit;
 #define DG_ATTN(TT, HDV)                                                                                     \
   k_attn<TT, HDV><<<blocks, 256, 0, s>>>((const TT*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);         \
@@ -585,12 +597,15 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #ifndef DG_ATTN_NST
 #define DG_ATTN_NST 4
 #endif
-// m-tiles (16 query rows) per wave: one at head_dim >= 128 (eight waves, two per
-// SIMD, half the registers each), two at 64 (the tile staging needs 256 threads)
-#define DG_ATTN_QT(HDV) ((HDV) >= 128 ? 1 : 2)
+// m-tiles (16 query rows) per wave: one at head_dim 128 (eight waves, two per
+// SIMD, half the registers each), two at 64 (the tile staging needs 256
+// threads), DG_ATTN_QT256 at 256
+#define DG_ATTN_QT(HDV) ((HDV) == 128 ? 1 : (HDV) == 256 ? DG_ATTN_QT256 : 2)
+#define DG_ATTN_QRT(HDV) ATTN_QROWS
 #define DG_ATTN_LDS(HDV)                                                                                    \
-  k_attn_lds<HDV, DG_ATTN_QT(HDV), DG_ATTN_NST><<<blocks, 512 / DG_ATTN_QT(HDV), 0, s>>>(                            \
-      (const bf16_t*)q, sh, segs, nqb, nsplit, opart, mlpart, rows);                                                \
+  k_attn_lds<HDV, DG_ATTN_QT(HDV), DG_ATTN_NST, DG_ATTN_QRT(HDV)>                                                   \
+      <<<blocks, DG_ATTN_QRT(HDV) * 4 / DG_ATTN_QT(HDV), 0, s>>>((const bf16_t*)q, sh, segs, nqb, nsplit, opart,    \
+                                                                  mlpart, rows);                                    \
   k_attn_merge<bf16_t, true, float, true><<<rows * sh.hq, 64, 0, s>>>(opart, mlpart, nsplit, rows, sh.hq, HDV,     \
                                                                        (bf16_t*)o)
   if (dtype == 1) {
@@ -608,4 +623,5 @@ void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSe
 #undef DG_ATTN
 #undef DG_ATTN_LDS
 #undef DG_ATTN_QT
+#undef DG_ATTN_QRT
 }

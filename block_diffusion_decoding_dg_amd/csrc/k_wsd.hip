@@ -43,6 +43,7 @@
 // span run side by side and share its weight tiles in that L2.
 #include "dg_common.h"
 #include "dg_kernels.h"
+#include "ws_common.h"
 
 namespace {
 
@@ -57,38 +58,28 @@ static_assert(WSD_NCW * 16 == DG_WS_GROUP_ROWS, "one m-tile per consumer wave co
 // LDS slot of 16-byte segment seg (0..7) of weight row `row` of a stage.
 __device__ __forceinline__ int wsd_slot(int row, int seg) { return row * 8 + (seg ^ (row & 7)); }
 
-// Byte address of weight row r (0..63) of n-block nb of expert g.  SwiGLU: rows
-// 0..31 are W1 rows and 32..63 the W3 rows of the same 32 hidden columns.
-template <int EPI>
-__device__ __forceinline__ const char* wsd_row(const WsArgs& a, int g, int nb, int r) {
-  if constexpr (EPI == WS_EPI_SWIGLU) {
-    const char* W = (const char*)(r < 32 ? a.W0 : a.W1) + (size_t)g * a.wgs * 2;
-    const int n = nb * 32 + (r & 31);
-    return W + (size_t)min(n, a.N - 1) * a.K * 2;
-  } else {
-    const char* W = (const char*)a.W0 + (size_t)g * a.wgs * 2;
-    const int n = nb * WSD_BN + r;
-    return W + (size_t)min(n, a.N - 1) * a.K * 2;
-  }
-}
-
-// A consumer wave's chunk loop over a span of nsub n-blocks (nsub x nk chunks):
-// fragments of the chunk three ahead loaded while a chunk is computed (ACT; an
-// idle wave only meets the barriers), one barrier per chunk, the weight
-// fragments read from stage c % NST.  The activation rows are the same for
-// every n-block of the span, so the fetch index wraps at nk; after the last
-// chunk of each n-block its results go to epi(acc, n-block of the span).  The
-// loop body covers whole groups of 4 chunks with no branch around a load (so
-// the compiler keeps exact waits for the activation loads); the last
-// (nsub nk) % 4 chunks follow it.
-template <bool ACT, int NST, typename Epi>
+// A consumer wave's chunk loop over a span of nsub n-blocks (nsub x nk chunks),
+// one barrier per chunk, the weight fragments read from stage c % NST; an idle
+// wave (ACT false) only meets the barriers.  The activation fragments of the
+// chunk three ahead are loaded while a chunk is computed (four register
+// buffers): from row-major rows (ap: the lane's row; step q of chunk c at
+// bytes 128 c + 64 q) or, AFM, from the fragment-major layout (ap: the m-tile's
+// first 1 KB block plus 16 bytes per lane; step q of chunk c is block 2 c + q).
+// The activation rows are the same for every n-block of the span, so the fetch
+// index wraps at nk; after the last chunk of each n-block its results go to
+// epi(acc, n-block of the span) -- inside the loop for spans (SPAN), else once
+// after it, so that a large epilogue is not repeated in the unrolled body.  The
+// loop body covers whole groups of 4 chunks with no branch around a load (so the
+// compiler keeps exact waits for them); the last (nsub nk) % 4 chunks follow it.
+template <bool ACT, int NST, bool AFM, bool SPAN, typename Epi>
 __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* ap, int nk, int nsub, int lane,
                                             Epi&& epi) {
   int fk = 0;  // chunk of the next activation fetch
   auto fetch_a = [&](v8s (&A)[2]) __attribute__((always_inline)) {
     if constexpr (ACT) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) A[q] = *(const v8s*)(ap + (size_t)fk * 128 + q * 64);
+      for (int q = 0; q < 2; ++q)
+        A[q] = *(const v8s*)(ap + (AFM ? (size_t)(2 * fk + q) * 1024 : (size_t)fk * 128 + q * 64));
       fk = fk + 1 == nk ? 0 : fk + 1;
     }
   };
@@ -118,7 +109,7 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, wf[n], acc[n], 0, 0, 0);
       }
-      if (++kc == nk) {  // the n-block is done (uniform)
+      if (SPAN && ++kc == nk) {  // the n-block is done (uniform)
         epi(acc, sub);
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -138,23 +129,24 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
   if (c < total) step(A0, A3, c);  // the last total % 4 chunks
   if (c + 1 < total) step(A1, A0, c + 1);
   if (c + 2 < total) step(A2, A1, c + 2);
+  if constexpr (ACT && !SPAN) epi(acc, 0);
 }
 
-// A consumer wave's results for rows t0 .. t0 + 15 of a part (rows row0 .. of
-// group g, cnt of them) and the 64 weight rows of n-block nb: lane holds
-// columns n * 16 + lane % 16 of rows 4 (lane / 16) + i.
+// A consumer wave's results for its m-tile (rows t0 .. t0 + 15 of a part with
+// cnt rows) and the 64 weight rows of n-block nb: lane holds columns n * 16 +
+// lane % 16 of rows 4 (lane / 16) + i.  orow[i]: the output row of the lane's
+// row i -- the expert-sorted row (SwiGLU) or the pair index (fp32 store) --
+// looked up before the chunk loop, so the epilogue issues stores only.
 template <int EPI>
-__device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4], int g, int nb, int row0, int cnt,
-                                             int t0, int lane) {
-  const int off = a.offsets[g], arow0 = a.offsets16[g];
+__device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4], int nb, int cnt, int t0, int lane,
+                                             const int (&orow)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = t0 + (lane >> 4) * 4 + i;
     if (rl >= cnt) continue;
-    const int r = row0 + rl;
     if constexpr (EPI == WS_EPI_SWIGLU) {
       // row-major hidden rows at the expert-sorted row
-      bf16_t* hrow = (bf16_t*)a.out + (size_t)(arow0 + r) * a.N;
+      bf16_t* hrow = (bf16_t*)a.out + (size_t)orow[i] * a.N;
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int col = nb * 32 + n * 16 + (lane & 15);
@@ -162,41 +154,69 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4
         hrow[col] = f2bf(silu_f(acc[n][i]) * acc[n + 2][i]);
       }
     } else {
-      const int orow = a.perm[off + r];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int col = nb * WSD_BN + n * 16 + (lane & 15);
         if (col >= a.N) continue;
-        ((float*)a.out)[(size_t)orow * a.ldo + col] = acc[n][i];
+        ((float*)a.out)[(size_t)orow[i] * a.ldo + col] = acc[n][i];
       }
     }
   }
 }
 
-template <int EPI, int NST>
+// One kernel for both kinds of launch:
+//   * grouped (DENSE false): routed experts on a work list, units (expert,
+//     row part, span of n-blocks); activations row-major (through rowsrc for
+//     W1/W3), wsd_epilogue;
+//   * dense (DENSE true): one weight matrix on M rows, units (n-block, row part
+//     of 128, reduction range) dealt as in k_ws: work-groups go to the 8 XCDs in
+//     turn (block b to XCD b % 8), so n-block nb goes to XCD nb % 8 and its
+//     parts x ranges to consecutive slots of that XCD -- the parts of one
+//     n-block run together and read its weight tile from that XCD's L2; the
+//     grid is 8 ceil(nblk / 8) x parts x ranges, padding blocks exit at once.
+//     Activations fragment-major; the epilogues of k_ws (ws_tile_epilogue).
+template <int EPI, int NST, bool DENSE>
 __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
   static_assert(NST >= 3 && (NST - 2) * WSD_INS <= 63, "ring depth within the vmcnt range");
   __shared__ uint4 sW[NST][WSD_SLOTS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if ((int)blockIdx.x >= *a.n_units) return;
-  const uint32_t code = (uint32_t)a.units[blockIdx.x];
-  if (code == DG_WS_UNIT_NONE) return;  // padding of the work list
-  const int g = (int)(code >> 24), part = (int)((code >> 16) & 0xff);
-  const int span = max(a.span, 1), nb0 = (int)(code & 0xffff) * span, nsub = min(span, a.nblk - nb0);
-  const int row0 = part * DG_WS_GROUP_ROWS;
-  const int cnt = min(a.counts[g] - row0, DG_WS_GROUP_ROWS);
-  if (cnt <= 0 || nsub <= 0) return;  // uniform over the block
-  const int nk = a.K / 64;
+  int g = 0, row0, cnt, nb0, nsub = 1, ks = 0, kc0 = 0, nk = a.K / 64;
+  if constexpr (DENSE) {
+    const int msp = max(a.msplit, 1), ksp = max(a.ksplit, 1);
+    const int b = blockIdx.x, x = b % 8, j = b / 8, nsubblk = msp * ksp, sub = j % nsubblk;
+    ks = sub / msp;
+    nb0 = x + 8 * (j / nsubblk);
+    if (nb0 >= a.nblk) return;  // padding of the grid
+    const int M = a.M_dev ? *a.M_dev : a.M;
+    row0 = (sub % msp) * DG_WS_GROUP_ROWS;
+    cnt = min(M - row0, DG_WS_GROUP_ROWS);
+    if (ksp > 1) {
+      kc0 = ks * a.kchunks;
+      nk = min(nk - kc0, a.kchunks);
+    }
+    if (cnt <= 0 || nk <= 0) return;  // uniform over the block
+  } else {
+    if ((int)blockIdx.x >= *a.n_units) return;
+    const uint32_t code = (uint32_t)a.units[blockIdx.x];
+    if (code == DG_WS_UNIT_NONE) return;  // padding of the work list
+    g = (int)(code >> 24);
+    const int part = (int)((code >> 16) & 0xff), span = max(a.span, 1);
+    nb0 = (int)(code & 0xffff) * span;
+    nsub = min(span, a.nblk - nb0);
+    row0 = part * DG_WS_GROUP_ROWS;
+    cnt = min(a.counts[g] - row0, DG_WS_GROUP_ROWS);
+    if (cnt <= 0 || nsub <= 0) return;  // uniform over the block
+  }
 
   if (wave >= WSD_NCW) {
-    // ---- producer: copies of the span's weight chunks into the LDS ring
+    // ---- producer: copies of the weight chunks (a span's n-blocks in turn) into the LDS ring
     const int p = wave - WSD_NCW;
     const char* src[WSD_INS];
     auto rows_of = [&](int nb) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < WSD_INS; ++i) {
         const int s = (p * WSD_INS + i) * 64 + lane, row = s >> 3, seg = (s & 7) ^ (row & 7);
-        src[i] = wsd_row<EPI>(a, g, nb, row) + seg * 16;
+        src[i] = weight_row<EPI, 4>(a, g, nb, row) + (size_t)kc0 * 128 + seg * 16;
       }
     };
     rows_of(nb0);
@@ -228,24 +248,43 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
 
   // ---- consumer: this wave's m-tile (rows t0 .. t0 + 15 of the part)
   const int t0 = wave * 16;
-  // lane's row (a row past the part's end reads its last row; only active
-  // waves load), through rowsrc when set, and its bytes of each 128-byte chunk
-  const int srow = a.offsets16[g] + row0 + min(t0 + (lane & 15), cnt - 1);
-  const int row = a.rowsrc ? a.rowsrc[srow] : srow;
-  const char* ap = (const char*)a.A + (size_t)row * a.K * 2 + (lane >> 4) * 16;
-  auto epi = [&](const v4f (&acc)[4], int sub) __attribute__((always_inline)) {
-    wsd_epilogue<EPI>(a, acc, g, nb0 + sub, row0, cnt, t0, lane);
-  };
-  // The active and the idle waves run separate loops (same barriers): a
-  // conditional load inside the loop makes the compiler's wait bookkeeping give
-  // up the three-chunk lead of the activation loads.
-  if (t0 < cnt) wsd_consume<true, NST>(sW, ap, nk, nsub, lane, epi);  // uniform over the wave
-  else wsd_consume<false, NST>(sW, ap, nk, nsub, lane, epi);
+  if constexpr (DENSE) {
+    // fragment-major rows: a tile past the part's rows reads the last one, which
+    // holds valid rows (only active waves load)
+    const int tr = row0 + min(t0, (cnt - 1) & ~15);
+    const char* ap = (const char*)a.A + ((size_t)(tr >> 4) * (a.K >> 5) + 2 * kc0) * 1024 + lane * 16;
+    auto epi = [&](const v4f (&acc)[4], int sub) __attribute__((always_inline)) {
+      ws_tile_epilogue<EPI, 4, DG_WS_W_BF16>(a, acc, 0, nb0 + sub, row0, t0, cnt, 0, 0, ks, lane);
+    };
+    if (t0 < cnt) wsd_consume<true, NST, true, false>(sW, ap, nk, 1, lane, epi);  // uniform over the wave
+    else wsd_consume<false, NST, true, false>(sW, ap, nk, 1, lane, epi);
+  } else {
+    // lane's row (a row past the part's end reads its last row; only active
+    // waves load), through rowsrc when set, and its bytes of each 128-byte chunk
+    const int srow = a.offsets16[g] + row0 + min(t0 + (lane & 15), cnt - 1);
+    const int row = a.rowsrc ? a.rowsrc[srow] : srow;
+    const char* ap = (const char*)a.A + (size_t)row * a.K * 2 + (lane >> 4) * 16;
+    int orow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = min(t0 + (lane >> 4) * 4 + i, cnt - 1);
+      if constexpr (EPI == WS_EPI_SWIGLU) orow[i] = a.offsets16[g] + row0 + rl;
+      else orow[i] = t0 < cnt ? a.perm[a.offsets[g] + row0 + rl] : 0;
+    }
+    auto epi = [&](const v4f (&acc)[4], int sub) __attribute__((always_inline)) {
+      wsd_epilogue<EPI>(a, acc, nb0 + sub, cnt, t0, lane, orow);
+    };
+    // The active and the idle waves run separate loops (same barriers): a
+    // conditional load inside the loop makes the compiler's wait bookkeeping
+    // give up the three-chunk lead of the activation loads.
+    if (t0 < cnt) wsd_consume<true, NST, false, true>(sW, ap, nk, nsub, lane, epi);  // uniform over the wave
+    else wsd_consume<false, NST, false, true>(sW, ap, nk, nsub, lane, epi);
+  }
 }
 
 }  // namespace
 
-// LDS ring depth (stages of 8 KB; two blocks per CU fit up to 10).
+// LDS ring depth (stages of 8 KB; a 64 KB ring allows one block per CU).
 #ifndef DG_WSD_NST
 #define DG_WSD_NST 8
 #endif
@@ -254,8 +293,25 @@ int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return 0;
   if (!a.counts || !a.units || !a.n_units || a.wfmt != DG_WS_W_BF16 || a.K % 64 || a.K < 64) return -1;
   if (a.nblk <= 0 || a.span > 0xffff || (a.rowsrc && epi != WS_EPI_SWIGLU)) return -1;
-  if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, DG_WSD_NST><<<grid, WSD_NT, 0, s>>>(a);
-  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, DG_WSD_NST><<<grid, WSD_NT, 0, s>>>(a);
+  if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, DG_WSD_NST, false><<<grid, WSD_NT, 0, s>>>(a);
+  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, DG_WSD_NST, false><<<grid, WSD_NT, 0, s>>>(a);
   else return -1;
+  return 0;
+}
+
+int dg_launch_wsd_dense(int epi, const WsArgs& a, hipStream_t s) {
+  if (a.counts || a.wfmt != DG_WS_W_BF16 || a.K % 64 || a.K < 64 || a.nblk <= 0 || a.span > 1) return -1;
+  if (a.ksplit > 1 && (epi != WS_EPI_ADD_F32 || !a.part_out || a.kchunks <= 0)) return -1;
+  const int M = a.M;  // with M_dev: the most rows the device count can hold
+  const int grid = (a.nblk + 7) / 8 * 8 * max(a.msplit, 1) * max(a.ksplit, 1);
+  if (M <= 0 || max(a.msplit, 1) * DG_WS_GROUP_ROWS < M) return -1;  // every row in a part
+  switch (epi) {
+    case WS_EPI_STORE_BF16: k_wsd<WS_EPI_STORE_BF16, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_wsd<WS_EPI_STORE_F32, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_wsd<WS_EPI_ADD_F32, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_wsd<WS_EPI_SWIGLU, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_wsd<WS_EPI_ROPE_QKV, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
+    default: return -1;
+  }
   return 0;
 }
