@@ -230,6 +230,8 @@ struct WsArgs {
 #define DG_WS_GROUP_ROWS 128
 #endif
 #define DG_WS_UNIT_NONE 0xffffffffu
+// Rows per part of the routed k_wsd launches (two m-tiles per consumer wave).
+#define DG_WSD_PART_ROWS 256
 
 // Writes the work-list entries of group e's `parts` row parts, starting at part
 // slot `first`: ceil8(nblk) entries per part, n-blocks in order, then padding.
@@ -244,7 +246,9 @@ __device__ __forceinline__ void dg_fill_units(int32_t* __restrict__ units, int f
 // Longest-first work lists (k_wsd).  A block's time grows with the rows of its
 // part (more consumer waves load activations and run the matrix cores), and
 // blocks start in list order, so the list holds the parts in decreasing order
-// of their 16-row tiles (ties: expert order, then part order) and each part's
+// of their tile class -- 16-row tiles, counted in pairs for parts of more than
+// 128 rows, so that 8 classes cover a part -- (ties: expert order, then part
+// order) and each part's
 // n-blocks (or spans of n-blocks) side by side: the last blocks to start are
 // the shortest, and the launch ends with fewer CUs idle.
 //
@@ -254,11 +258,11 @@ __device__ __forceinline__ void dg_fill_units(int32_t* __restrict__ units, int f
 // s_scan: 256 entries of LDS scratch; plist: LDS, room for E + pairs / part_rows.
 #define DG_WS_MAX_PARTS 512  // parts a longest-first list can hold (E + pairs / part_rows)
 __device__ __forceinline__ int dg_sort_parts(int e, int cnt, int part_rows, ulonglong2* s_scan, int32_t* plist) {
-  // per expert: parts with 8 tiles (full parts) and the tiles of a shorter
-  // last part, as 16-bit counts per tile class (classes 1..4 in x, 5..8 in y)
-  const int tiles_full = (part_rows + 15) / 16;
+  // per expert: full parts and a shorter last part, as 16-bit counts per tile
+  // class (classes 1..4 in x, 5..8 in y; tpc tiles per class)
+  const int tiles_full = (part_rows + 15) / 16, tpc = (tiles_full + 7) / 8;
   const int parts = cnt > 0 ? (cnt + part_rows - 1) / part_rows : 0;
-  const int rlast = cnt - (parts - 1) * part_rows, wl = min((rlast + 15) / 16, 8);
+  const int rlast = cnt - (parts - 1) * part_rows, wl = min(((rlast + 15) / 16 + tpc - 1) / tpc, 8);
   const int full = parts > 0 ? parts - 1 + (rlast == part_rows) : 0;
   auto add = [](ulonglong2& v, int cls, unsigned long long n) {
     if (cls <= 4) v.x += n << (16 * (cls - 1));
@@ -269,7 +273,7 @@ __device__ __forceinline__ int dg_sort_parts(int e, int cnt, int part_rows, ulon
   };
   ulonglong2 own = make_ulonglong2(0ull, 0ull);
   if (e < 256) {
-    if (full) add(own, min(tiles_full, 8), (unsigned long long)full);
+    if (full) add(own, min((tiles_full + tpc - 1) / tpc, 8), (unsigned long long)full);
     if (parts > 0 && rlast != part_rows) add(own, wl, 1ull);
     s_scan[e] = own;
   }
@@ -293,7 +297,7 @@ __device__ __forceinline__ int dg_sort_parts(int e, int cnt, int part_rows, ulon
       for (int k = 8; k > cls; --k) f += get(tot, k);
       return f;
     };
-    const int cf = min(tiles_full, 8);
+    const int cf = min((tiles_full + tpc - 1) / tpc, 8);
     for (int p = 0; p < full; ++p) plist[first_of(cf) + get(exc, cf) + p] = (e << 8) | p;
     if (rlast != part_rows) plist[first_of(wl) + get(exc, wl) + (wl == cf ? full : 0)] = (e << 8) | (parts - 1);
   }
@@ -361,9 +365,9 @@ inline int dg_unit_slots(int E, int pairs, int part_rows, int nblk) {
 // Grouped launch of bf16 routed-expert weights with producer waves copying the
 // weight tiles straight into LDS and consumer waves on the matrix cores (k_wsd):
 // SwiGLU (W1 / W3; A row-major, its sorted rows read through rowsrc when set)
-// or an fp32 store (W2; A row-major at the expert-sorted rows), on the work list
-// of a.units (DG_WS_GROUP_ROWS rows per part, a.span n-blocks per unit).  The
-// SwiGLU output is row-major at the expert-sorted rows.  Returns -1 (nothing
+// or an fp32 store (W2; A fragment-major at the expert-sorted rows), on the work list
+// of a.units (DG_WSD_PART_ROWS rows per part, a.span n-blocks per unit).  The
+// SwiGLU output is fragment-major at the expert-sorted rows.  Returns -1 (nothing
 // launched) for any other combination.
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s);
 // Dense launch of k_wsd: one bf16 weight matrix (a.W0, q/k/v: a.W0..W2; SwiGLU:

@@ -623,6 +623,9 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
 int routed_kernel(const dg_ctx* c) {
   return c->dtype == DG_BF16 && c->cfg.expert_format == DG_EXPERTS_NATIVE ? DG_ROUTED_KERNEL : 0;
 }
+// Rows per part of a routed work list: k_wsd takes up to 256 (two m-tiles per
+// consumer wave), so an expert's weights stream once for up to 256 rows.
+int routed_part_rows(const dg_ctx* c) { return routed_kernel(c) == 1 ? DG_WSD_PART_ROWS : DG_WS_GROUP_ROWS; }
 // n-blocks per unit of a k_wsd work list, and the units per row part.
 int wsd_span(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD_SPAN_DN; }
 int list_blocks(const dg_ctx* c, int epi, int nblk) {
@@ -665,8 +668,8 @@ void launch_routed(dg_ctx* c, int epi, const void* A, const void* W0, const void
   a.out = out;
   a.ldo = ldo;
   // bf16 experts: k_wsd; codes that are widened on the way (E4M3, MXFP4) keep k_ws
-  const int grid =
-      dg_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, DG_WS_GROUP_ROWS, list_blocks(c, epi, nblk));
+  const int grid = dg_unit_slots(c->cfg.n_experts, c->rows_cap * c->cfg.top_k, routed_part_rows(c),
+                                 list_blocks(c, epi, nblk));
   if (routed_kernel(c) == 1) {
     a.nblk = nblk;
     a.span = wsd_span(epi);
@@ -900,21 +903,21 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
     // routed experts over the expert-sorted rows: W1/W3 + SwiGLU into c->hbuf,
     // W2 from there into c->ybuf at each row's pair index.  Both kernels read
-    // the normalised rows (row-major c->xr) through rowsrc; k_wsd keeps c->hbuf
-    // row-major, k_ws fragment-major.
+    // the normalised rows (row-major c->xr) through rowsrc; c->hbuf is
+    // fragment-major.
     const bool wsd = routed_kernel(c) == 1;
     const int la = list_blocks(c, WS_EPI_SWIGLU, nb_up), lb = list_blocks(c, WS_EPI_STORE_F32, nb_dn);
     if (wsd && rows <= DG_ROUTE_MAX_ROWS && m.n_experts <= 256 && 16 * m.top_k <= 256) {
       // the permutation and the work lists in one launch of parallel blocks
       KT(c, DG_KF_PERMUTE, dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s);
          REFUSE_IF(c, dg_launch_route_perm(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm,
-                                           c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, la,
+                                           c->offsets16, c->rowsrc, c->n_units + 2, routed_part_rows(c), la,
                                            c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1,
                                            DG_ROUTE_LPT, s) != 0,
                    "routing"));
     } else {
       KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets,
-                                           c->perm, c->offsets16, c->rowsrc, c->n_units + 2, DG_WS_GROUP_ROWS, la,
+                                           c->perm, c->offsets16, c->rowsrc, c->n_units + 2, routed_part_rows(c), la,
                                            c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1, s, wsd));
     }
     KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, w.w1_scale, w.w3_scale, w.w1_mx_scale,

@@ -2,8 +2,10 @@
 // from HBM into LDS: the same work units, tiles and epilogues as the grouped
 // launches of k_ws, with the weight stream moved out of registers.
 //
-// A block owns one part of an expert's rows (at most DG_WS_GROUP_ROWS = 128, one
-// 16-row m-tile per consumer wave) and a span of S consecutive n-blocks of 64
+// A block owns one part of an expert's rows (at most DG_WSD_PART_ROWS = 256:
+// consumer wave w takes m-tiles w and w + 8, the second only where the part
+// has more than 128 rows, so an expert's weights stream once for up to 256
+// rows) and a span of S consecutive n-blocks of 64
 // weight rows, which it sweeps one after the other: the weight stream runs on
 // from one n-block into the next (the ring does not drain between them), and
 // the consumers store each n-block's results as it ends.  Its ten waves split
@@ -16,13 +18,16 @@
 //   * eight consumer waves load their m-tile's activation fragments with
 //     ordinary loads three chunks ahead (so the compiler's own waits for them
 //     stay exact: a consumer issues no copies), read the weight fragments of
-//     the chunk from LDS and run the matrix cores.  The activations are
-//     row-major rows: for W1/W3 the normalised token rows themselves, each
-//     sorted row read through rowsrc (no sorted copy is made: the few token
-//     rows stay in L2), for W2 the SwiGLU output, stored row-major at the
-//     expert-sorted rows.  Lane l holds row l % 16 and loads, for matrix-core
-//     step q of a chunk, the 16 bytes of reduction elements 32 q + 8 g .. + 7
-//     (g = l / 16): 64 contiguous bytes of each of 16 rows per load.
+//     the chunk from LDS and run the matrix cores.  For W1/W3 the activations
+//     are the normalised token rows themselves (row-major), each sorted row
+//     read through rowsrc (no sorted copy is made: the few token rows stay in
+//     L2): lane l holds row l % 16 and loads, for matrix-core step q of a
+//     chunk, the 16 bytes of reduction elements 32 q + 8 g .. + 7 (g = l / 16),
+//     64 contiguous bytes of each of 16 rows per load.  For W2 they are the
+//     SwiGLU output, which W1/W3 store fragment-major at the expert-sorted
+//     rows: one contiguous 1 KB load per step (whole cache lines, which the
+//     many-row parts, bound by their activation loads, read about twice as
+//     fast).
 // One barrier per chunk, passed by all ten waves: it publishes chunk c (every
 // producer has waited for its copies of c) and frees the stage that chunk c - 1
 // used (every consumer has read it), which the producers refill at once.  The
@@ -35,12 +40,11 @@
 // Copies of chunks past the end reload the last chunk into a free stage, so
 // every iteration issues the same copies and the waits stay constant.
 //
-// The work list (built with the routing) is cut into 8 contiguous slices in
-// the order expert, span, part, and slice x is laid out at list positions x,
-// x + 8, x + 16, ...: work-groups are dealt to the XCDs in turn, so XCD x runs
-// slice x in order.  An XCD then works on few experts at a time -- their rows
-// are fetched into its L2 once, not by all eight XCDs -- and the parts of one
-// span run side by side and share its weight tiles in that L2.
+// The work list (built with the routing) is longest first: the parts in
+// decreasing order of their 16-row tiles, each part's spans side by side, so
+// the blocks that start last are the shortest and the launch ends with few CUs
+// idle.  (A list cut into one slice per XCD, to keep each expert's rows in one
+// L2, measured no faster: the token rows are 1.4 MB and stay in every L2.)
 #include "dg_common.h"
 #include "dg_kernels.h"
 #include "ws_common.h"
@@ -53,45 +57,52 @@ constexpr int WSD_NT = 64 * (WSD_NCW + WSD_NPW);     // 640 threads
 constexpr int WSD_BN = 64;                           // weight rows per block
 constexpr int WSD_SLOTS = WSD_BN * 8;                // 16-byte LDS slots per stage (8 KB)
 constexpr int WSD_INS = WSD_SLOTS / 64 / WSD_NPW;    // copies per producer wave per chunk
-static_assert(WSD_NCW * 16 == DG_WS_GROUP_ROWS, "one m-tile per consumer wave covers a part");
+static_assert(WSD_NCW * 16 == DG_WS_GROUP_ROWS, "one m-tile per consumer wave covers a dense part");
+static_assert(2 * DG_WS_GROUP_ROWS == DG_WSD_PART_ROWS, "two m-tiles per consumer wave cover a routed part");
 
 // LDS slot of 16-byte segment seg (0..7) of weight row `row` of a stage.
 __device__ __forceinline__ int wsd_slot(int row, int seg) { return row * 8 + (seg ^ (row & 7)); }
 
 // A consumer wave's chunk loop over a span of nsub n-blocks (nsub x nk chunks),
-// one barrier per chunk, the weight fragments read from stage c % NST; an idle
-// wave (ACT false) only meets the barriers.  The activation fragments of the
-// chunk three ahead are loaded while a chunk is computed (four register
-// buffers): from row-major rows (ap: the lane's row; step q of chunk c at
-// bytes 128 c + 64 q) or, AFM, from the fragment-major layout (ap: the m-tile's
-// first 1 KB block plus 16 bytes per lane; step q of chunk c is block 2 c + q).
+// one barrier per chunk, the weight fragments read from stage c % NST and used
+// for each of the wave's MT m-tiles; an idle wave (ACT false) only meets the
+// barriers.  The activation fragments of the chunk three ahead are loaded
+// while a chunk is computed (four register buffers): from row-major rows
+// (ap[m]: the lane's row of m-tile m; step q of chunk c at bytes 128 c + 64 q)
+// or, AFM, from the fragment-major layout (ap[m]: the m-tile's first 1 KB block
+// plus 16 bytes per lane; step q of chunk c is block 2 c + q).
 // The activation rows are the same for every n-block of the span, so the fetch
 // index wraps at nk; after the last chunk of each n-block its results go to
 // epi(acc, n-block of the span) -- inside the loop for spans (SPAN), else once
-// after it, so that a large epilogue is not repeated in the unrolled body.  The
+// after it, so that a large epilogue is not repeated in the unrolled body
+// (epi(acc of m-tile m, n-block, m) for each m-tile).  The
 // loop body covers whole groups of 4 chunks with no branch around a load (so the
 // compiler keeps exact waits for them); the last (nsub nk) % 4 chunks follow it.
-template <bool ACT, int NST, bool AFM, bool SPAN, typename Epi>
-__device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* ap, int nk, int nsub, int lane,
-                                            Epi&& epi) {
+template <int MT, bool ACT, int NST, bool AFM, bool SPAN, typename Epi>
+__device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* const (&ap)[MT], int nk, int nsub,
+                                            int lane, Epi&& epi) {
   int fk = 0;  // chunk of the next activation fetch
-  auto fetch_a = [&](v8s (&A)[2]) __attribute__((always_inline)) {
+  auto fetch_a = [&](v8s (&A)[MT][2]) __attribute__((always_inline)) {
     if constexpr (ACT) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        A[q] = *(const v8s*)(ap + (AFM ? (size_t)(2 * fk + q) * 1024 : (size_t)fk * 128 + q * 64));
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          A[m][q] = *(const v8s*)(ap[m] + (AFM ? (size_t)(2 * fk + q) * 1024 : (size_t)fk * 128 + q * 64));
       fk = fk + 1 == nk ? 0 : fk + 1;
     }
   };
-  v4f acc[4];
+  v4f acc[MT][4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-  v8s A0[2], A1[2], A2[2], A3[2];
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8s A0[MT][2], A1[MT][2], A2[MT][2], A3[MT][2];
   fetch_a(A0);
   fetch_a(A1);
   fetch_a(A2);
   int kc = 0, sub = 0;  // chunk within the n-block, n-block of the span
-  auto step = [&](v8s (&Acur)[2], v8s (&Anext)[2], int c) __attribute__((always_inline)) {
+  auto step = [&](v8s (&Acur)[MT][2], v8s (&Anext)[MT][2], int c) __attribute__((always_inline)) {
     fetch_a(Anext);                // chunk c + 3 (past the end: the first chunks again)
     __builtin_amdgcn_s_barrier();  // chunk c is in its stage
     asm volatile("" ::: "memory");
@@ -99,7 +110,6 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
       const uint4* st = sW[c % NST];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const v8s am = Acur[q];
         v8s wf[4];
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
@@ -107,12 +117,18 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
           wf[n] = *reinterpret_cast<const v8s*>(&u);
         }
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, wf[n], acc[n], 0, 0, 0);
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n], 0, 0, 0);
       }
       if (SPAN && ++kc == nk) {  // the n-block is done (uniform)
-        epi(acc, sub);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < MT; ++m) {
+          epi(acc[m], sub, m);
+#pragma unroll
+          for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
         kc = 0;
         ++sub;
       }
@@ -129,14 +145,18 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
   if (c < total) step(A0, A3, c);  // the last total % 4 chunks
   if (c + 1 < total) step(A1, A0, c + 1);
   if (c + 2 < total) step(A2, A1, c + 2);
-  if constexpr (ACT && !SPAN) epi(acc, 0);
+  if constexpr (ACT && !SPAN) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) epi(acc[m], 0, m);
+  }
 }
 
 // A consumer wave's results for its m-tile (rows t0 .. t0 + 15 of a part with
 // cnt rows) and the 64 weight rows of n-block nb: lane holds columns n * 16 +
-// lane % 16 of rows 4 (lane / 16) + i.  orow[i]: the output row of the lane's
-// row i -- the expert-sorted row (SwiGLU) or the pair index (fp32 store) --
-// looked up before the chunk loop, so the epilogue issues stores only.
+// lane % 16 of rows 4 (lane / 16) + i.  orow[i]: where the lane's row i goes
+// -- the fragment-major offset of the expert-sorted row (SwiGLU) or the pair
+// index (fp32 store) -- looked up before the chunk loop, so the epilogue
+// issues stores only.
 template <int EPI>
 __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4], int nb, int cnt, int t0, int lane,
                                              const int (&orow)[4]) {
@@ -145,13 +165,15 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4
     const int rl = t0 + (lane >> 4) * 4 + i;
     if (rl >= cnt) continue;
     if constexpr (EPI == WS_EPI_SWIGLU) {
-      // row-major hidden rows at the expert-sorted row
-      bf16_t* hrow = (bf16_t*)a.out + (size_t)orow[i] * a.N;
+      // hidden rows at the expert-sorted row, fragment-major: the n-block's 32
+      // columns of an m-tile are one 1 KB block, orow[i] the row's element
+      // offset in its tile's first block (fm_index of column 0)
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int col = nb * 32 + n * 16 + (lane & 15);
         if (col >= a.N) continue;
-        hrow[col] = f2bf(silu_f(acc[n][i]) * acc[n + 2][i]);
+        ((bf16_t*)a.out)[(size_t)orow[i] + nb * 512 + (2 * n + ((lane >> 3) & 1)) * 128 + (lane & 7)] =
+            f2bf(silu_f(acc[n][i]) * acc[n + 2][i]);
       }
     } else {
 #pragma unroll
@@ -166,8 +188,8 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4
 
 // One kernel for both kinds of launch:
 //   * grouped (DENSE false): routed experts on a work list, units (expert,
-//     row part, span of n-blocks); activations row-major (through rowsrc for
-//     W1/W3), wsd_epilogue;
+//     row part, span of n-blocks); activations row-major through rowsrc
+//     (W1/W3) or fragment-major (W2), wsd_epilogue;
 //   * dense (DENSE true): one weight matrix on M rows, units (n-block, row part
 //     of 128, reduction range) dealt as in k_ws: work-groups go to the 8 XCDs in
 //     turn (block b to XCD b % 8), so n-block nb goes to XCD nb % 8 and its
@@ -203,8 +225,8 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
     const int part = (int)((code >> 16) & 0xff), span = max(a.span, 1);
     nb0 = (int)(code & 0xffff) * span;
     nsub = min(span, a.nblk - nb0);
-    row0 = part * DG_WS_GROUP_ROWS;
-    cnt = min(a.counts[g] - row0, DG_WS_GROUP_ROWS);
+    row0 = part * DG_WSD_PART_ROWS;
+    cnt = min(a.counts[g] - row0, DG_WSD_PART_ROWS);
     if (cnt <= 0 || nsub <= 0) return;  // uniform over the block
   }
 
@@ -252,33 +274,54 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
     // fragment-major rows: a tile past the part's rows reads the last one, which
     // holds valid rows (only active waves load)
     const int tr = row0 + min(t0, (cnt - 1) & ~15);
-    const char* ap = (const char*)a.A + ((size_t)(tr >> 4) * (a.K >> 5) + 2 * kc0) * 1024 + lane * 16;
-    auto epi = [&](const v4f (&acc)[4], int sub) __attribute__((always_inline)) {
+    const char* const ap[1] = {(const char*)a.A + ((size_t)(tr >> 4) * (a.K >> 5) + 2 * kc0) * 1024 + lane * 16};
+    auto epi = [&](const v4f (&acc)[4], int sub, int) __attribute__((always_inline)) {
       ws_tile_epilogue<EPI, 4, DG_WS_W_BF16>(a, acc, 0, nb0 + sub, row0, t0, cnt, 0, 0, ks, lane);
     };
-    if (t0 < cnt) wsd_consume<true, NST, true, false>(sW, ap, nk, 1, lane, epi);  // uniform over the wave
-    else wsd_consume<false, NST, true, false>(sW, ap, nk, 1, lane, epi);
+    if (t0 < cnt) wsd_consume<1, true, NST, true, false>(sW, ap, nk, 1, lane, epi);  // uniform over the wave
+    else wsd_consume<1, false, NST, true, false>(sW, ap, nk, 1, lane, epi);
   } else {
-    // lane's row (a row past the part's end reads its last row; only active
-    // waves load), through rowsrc when set, and its bytes of each 128-byte chunk
-    const int srow = a.offsets16[g] + row0 + min(t0 + (lane & 15), cnt - 1);
-    const int row = a.rowsrc ? a.rowsrc[srow] : srow;
-    const char* ap = (const char*)a.A + (size_t)row * a.K * 2 + (lane >> 4) * 16;
-    int orow[4];
+    // m-tiles t0 and t0 + 128 of the part.  W1/W3 (row-major token rows):
+    // lane's row of each (a row past the part's end reads its last row; only
+    // active waves load) through rowsrc, and its bytes of each 128-byte chunk;
+    // W2 (AFM: the fragment-major hidden rows at the expert-sorted rows): the
+    // m-tile's first 1 KB block.  The output rows of its results (orow[m][i])
+    // are looked up before the loop.
+    constexpr bool AFM = EPI != WS_EPI_SWIGLU;
+    const char* ap[2];
+    int orow[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rl = min(t0 + (lane >> 4) * 4 + i, cnt - 1);
-      if constexpr (EPI == WS_EPI_SWIGLU) orow[i] = a.offsets16[g] + row0 + rl;
-      else orow[i] = t0 < cnt ? a.perm[a.offsets[g] + row0 + rl] : 0;
+    for (int m = 0; m < 2; ++m) {
+      const int tm = t0 + m * DG_WS_GROUP_ROWS;
+      if constexpr (AFM) {
+        const int tile = (a.offsets16[g] + row0 + min(tm, (cnt - 1) & ~15)) >> 4;
+        ap[m] = (const char*)a.A + (size_t)tile * (a.K >> 5) * 1024 + lane * 16;
+      } else {
+        const int srow = a.offsets16[g] + row0 + min(tm + (lane & 15), cnt - 1);
+        const int row = a.rowsrc ? a.rowsrc[srow] : srow;
+        ap[m] = (const char*)a.A + (size_t)row * a.K * 2 + (lane >> 4) * 16;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = min(tm + (lane >> 4) * 4 + i, cnt - 1);
+        if constexpr (EPI == WS_EPI_SWIGLU) orow[m][i] = (int)fm_index(a.offsets16[g] + row0 + rl, 0, a.N);
+        else orow[m][i] = tm < cnt ? a.perm[a.offsets[g] + row0 + rl] : 0;
+      }
     }
-    auto epi = [&](const v4f (&acc)[4], int sub) __attribute__((always_inline)) {
-      wsd_epilogue<EPI>(a, acc, nb0 + sub, cnt, t0, lane, orow);
+    auto epi = [&](const v4f (&acc)[4], int sub, int m) __attribute__((always_inline)) {
+      wsd_epilogue<EPI>(a, acc, nb0 + sub, cnt, t0 + m * DG_WS_GROUP_ROWS, lane, orow[m]);
     };
-    // The active and the idle waves run separate loops (same barriers): a
-    // conditional load inside the loop makes the compiler's wait bookkeeping
+    // The waves with two, one or no m-tiles run separate loops (same barriers):
+    // a conditional load inside the loop makes the compiler's wait bookkeeping
     // give up the three-chunk lead of the activation loads.
-    if (t0 < cnt) wsd_consume<true, NST, false, true>(sW, ap, nk, nsub, lane, epi);  // uniform over the wave
-    else wsd_consume<false, NST, false, true>(sW, ap, nk, nsub, lane, epi);
+    if (t0 + DG_WS_GROUP_ROWS < cnt) {  // uniform over the wave
+      const char* const ap2[2] = {ap[0], ap[1]};
+      wsd_consume<2, true, NST, AFM, true>(sW, ap2, nk, nsub, lane, epi);
+    } else {
+      const char* const ap1[1] = {ap[0]};
+      if (t0 < cnt) wsd_consume<1, true, NST, AFM, true>(sW, ap1, nk, nsub, lane, epi);
+      else wsd_consume<1, false, NST, AFM, true>(sW, ap1, nk, nsub, lane, epi);
+    }
   }
 }
 
