@@ -370,6 +370,10 @@ inline int dg_unit_slots(int E, int pairs, int part_rows, int nblk) {
 // SwiGLU output is fragment-major at the expert-sorted rows.  Returns -1 (nothing
 // launched) for any other combination.
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s);
+// Weight rows per n-block of dg_launch_wsd for epilogue epi (64 or 128).
+int dg_wsd_bn(int epi);
+// n-blocks per unit of dg_launch_wsd for epilogue epi (a.span must not exceed it).
+int dg_wsd_span(int epi);
 // Dense launch of k_wsd: one bf16 weight matrix (a.W0, q/k/v: a.W0..W2; SwiGLU:
 // W1 = a.W0, W3 = a.W1) on a.M fragment-major rows, a.nblk n-blocks of 64
 // weight rows, a.msplit parts of DG_WS_GROUP_ROWS rows (covering a.M), and for

@@ -47,12 +47,6 @@
 #ifndef DG_ROUTE_LPT
 #define DG_ROUTE_LPT 1
 #endif
-#ifndef DG_WSD_SPAN_UP
-#define DG_WSD_SPAN_UP 1
-#endif
-#ifndef DG_WSD_SPAN_DN
-#define DG_WSD_SPAN_DN 2
-#endif
 // Vocabulary ranges of the self-conditioning product, at most.
 #ifndef DG_SC_KSPLIT
 #define DG_SC_KSPLIT 16
@@ -627,7 +621,7 @@ int routed_kernel(const dg_ctx* c) {
 // consumer wave), so an expert's weights stream once for up to 256 rows.
 int routed_part_rows(const dg_ctx* c) { return routed_kernel(c) == 1 ? DG_WSD_PART_ROWS : DG_WS_GROUP_ROWS; }
 // n-blocks per unit of a k_wsd work list, and the units per row part.
-int wsd_span(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD_SPAN_DN; }
+int wsd_span(int epi) { return dg_wsd_span(epi); }
 int list_blocks(const dg_ctx* c, int epi, int nblk) {
   return routed_kernel(c) == 1 ? (nblk + wsd_span(epi) - 1) / wsd_span(epi) : nblk;
 }
@@ -900,7 +894,11 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
                                                                 c->side, c->parts2, 1, DG_SHARED_W2_ROWS));
     HIPCK_V(hipEventRecord(c->ev_join, c->side));
     KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
-    const int nb_up = (m.expert_hidden + 31) / 32, nb_dn = (m.d_model + 63) / 64;
+    // n-blocks: k_wsd's width (dg_wsd_bn weight rows; SwiGLU: half of them W1),
+    // k_ws's 64 weight rows
+    const int bn_up = routed_kernel(c) == 1 ? dg_wsd_bn(WS_EPI_SWIGLU) : 64;
+    const int bn_dn = routed_kernel(c) == 1 ? dg_wsd_bn(WS_EPI_STORE_F32) : 64;
+    const int nb_up = (m.expert_hidden + bn_up / 2 - 1) / (bn_up / 2), nb_dn = (m.d_model + bn_dn - 1) / bn_dn;
     // routed experts over the expert-sorted rows: W1/W3 + SwiGLU into c->hbuf,
     // W2 from there into c->ybuf at each row's pair index.  Both kernels read
     // the normalised rows (row-major c->xr) through rowsrc; c->hbuf is

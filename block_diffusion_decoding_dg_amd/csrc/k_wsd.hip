@@ -5,18 +5,20 @@
 // A block owns one part of an expert's rows (at most DG_WSD_PART_ROWS = 256:
 // consumer wave w takes m-tiles w and w + 8, the second only where the part
 // has more than 128 rows, so an expert's weights stream once for up to 256
-// rows) and a span of S consecutive n-blocks of 64
-// weight rows, which it sweeps one after the other: the weight stream runs on
-// from one n-block into the next (the ring does not drain between them), and
-// the consumers store each n-block's results as it ends.  Its ten waves split
-// the work by role:
-//   * two producer waves copy each 8 KB weight chunk (64 rows x 64 reduction
-//     elements) into an LDS ring of NST stages with global_load_lds_dwordx4 --
-//     four copies per wave per chunk, NST - 1 chunks ahead of the consumers --
-//     and, since the compiler does not track these copies, wait for them
-//     themselves (DG_WAIT_VMCNT) before the chunk's barrier;
-//   * eight consumer waves load their m-tile's activation fragments with
-//     ordinary loads three chunks ahead (so the compiler's own waits for them
+// rows) and a span of S consecutive n-blocks of BN (64 or 128) weight rows,
+// which it sweeps one after the other: the weight stream runs on from one
+// n-block into the next (the ring does not drain between them), and the
+// consumers store each n-block's results as it ends.  Dense launches use
+// n-blocks of 64.  Its ten waves split the work by role:
+//   * two producer waves copy each weight chunk (BN rows x 64 reduction
+//     elements, 8 or 16 KB) into a 64 KB LDS ring of NST = 8 or 4 stages with
+//     global_load_lds_dwordx4 -- BN / 16 copies per wave per chunk, NST - 1
+//     chunks ahead of the consumers -- and, since the compiler does not track
+//     these copies, wait for them themselves (DG_WAIT_VMCNT) before the
+//     chunk's barrier;
+//   * eight consumer waves load their m-tiles' activation fragments with
+//     ordinary loads three chunks ahead (two for 16 KB chunks; so the
+//     compiler's own waits for them
 //     stay exact: a consumer issues no copies), read the weight fragments of
 //     the chunk from LDS and run the matrix cores.  For W1/W3 the activations
 //     are the normalised token rows themselves (row-major), each sorted row
@@ -31,8 +33,8 @@
 // One barrier per chunk, passed by all ten waves: it publishes chunk c (every
 // producer has waited for its copies of c) and frees the stage that chunk c - 1
 // used (every consumer has read it), which the producers refill at once.  The
-// ring holds NST stages, so the bytes in flight per block are (NST - 1) x 8 KB
-// instead of the four register slots of k_ws, and no register holds weights.
+// ring holds NST stages, so 56 or 48 KB are in flight per block instead of the
+// four register slots of k_ws, and no register holds weights.
 //
 // LDS rows are XOR-swizzled in 16-byte units exactly as in k_ws, so the
 // fragment reads are free of bank conflicts; the copies write each stage in
@@ -49,14 +51,43 @@
 #include "dg_kernels.h"
 #include "ws_common.h"
 
+// Weight rows per n-block of the routed launches (64 or 128; the 64 KB ring,
+// which allows one block per CU, holds 8 or 4 chunks).  128: the many-row
+// parts are bound by their activation loads, which every n-block repeats, so
+// twice the weight rows per n-block halves them (measured 10.38 -> 10.01 ms
+// per step, W1/W3 122 -> 116 us).
+#ifndef DG_WSD_BN_UP
+#define DG_WSD_BN_UP 128
+#endif
+#ifndef DG_WSD_BN_DN
+#define DG_WSD_BN_DN 128
+#endif
+static_assert((DG_WSD_BN_UP == 64 || DG_WSD_BN_UP == 128) && (DG_WSD_BN_DN == 64 || DG_WSD_BN_DN == 128),
+              "n-blocks of 64 or 128 weight rows");
+
+// n-blocks per unit of the routed launches (a span: the unit sweeps them with
+// the ring running on from one into the next).
+#ifndef DG_WSD_SPAN_UP
+#define DG_WSD_SPAN_UP 1
+#endif
+#ifndef DG_WSD_SPAN_DN
+#define DG_WSD_SPAN_DN 1
+#endif
+
 namespace {
 
 constexpr int WSD_NCW = 8;                           // consumer waves (m-tile = wave)
 constexpr int WSD_NPW = 2;                           // producer waves
 constexpr int WSD_NT = 64 * (WSD_NCW + WSD_NPW);     // 640 threads
-constexpr int WSD_BN = 64;                           // weight rows per block
-constexpr int WSD_SLOTS = WSD_BN * 8;                // 16-byte LDS slots per stage (8 KB)
-constexpr int WSD_INS = WSD_SLOTS / 64 / WSD_NPW;    // copies per producer wave per chunk
+constexpr int WSD_LDS_SLOTS = 4096;                 // 16-byte LDS slots of the ring (64 KB)
+// A block's n-block is BN weight rows (64 or 128: NT = BN / 16 n-tiles per
+// consumer wave); a chunk is BN rows x 64 reduction elements, BN * 8 slots, and
+// the ring holds WSD_LDS_SLOTS / (BN * 8) chunks.  ins: copies per producer
+// wave per chunk.
+template <int BN>
+struct WsdShape {
+  static constexpr int NT = BN / 16, SLOTS = BN * 8, NST = WSD_LDS_SLOTS / SLOTS, INS = SLOTS / 64 / WSD_NPW;
+};
 static_assert(WSD_NCW * 16 == DG_WS_GROUP_ROWS, "one m-tile per consumer wave covers a dense part");
 static_assert(2 * DG_WS_GROUP_ROWS == DG_WSD_PART_ROWS, "two m-tiles per consumer wave cover a routed part");
 
@@ -66,8 +97,8 @@ __device__ __forceinline__ int wsd_slot(int row, int seg) { return row * 8 + (se
 // A consumer wave's chunk loop over a span of nsub n-blocks (nsub x nk chunks),
 // one barrier per chunk, the weight fragments read from stage c % NST and used
 // for each of the wave's MT m-tiles; an idle wave (ACT false) only meets the
-// barriers.  The activation fragments of the chunk three ahead are loaded
-// while a chunk is computed (four register buffers): from row-major rows
+// barriers.  The activation fragments of the chunk PD ahead are loaded
+// while a chunk is computed (PD + 1 register buffers): from row-major rows
 // (ap[m]: the lane's row of m-tile m; step q of chunk c at bytes 128 c + 64 q)
 // or, AFM, from the fragment-major layout (ap[m]: the m-tile's first 1 KB block
 // plus 16 bytes per lane; step q of chunk c is block 2 c + q).
@@ -76,11 +107,13 @@ __device__ __forceinline__ int wsd_slot(int row, int seg) { return row * 8 + (se
 // epi(acc, n-block of the span) -- inside the loop for spans (SPAN), else once
 // after it, so that a large epilogue is not repeated in the unrolled body
 // (epi(acc of m-tile m, n-block, m) for each m-tile).  The
-// loop body covers whole groups of 4 chunks with no branch around a load (so the
-// compiler keeps exact waits for them); the last (nsub nk) % 4 chunks follow it.
-template <int MT, bool ACT, int NST, bool AFM, bool SPAN, typename Epi>
-__device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* const (&ap)[MT], int nk, int nsub,
+// loop body covers whole groups of PD + 1 chunks with no branch around a load
+// (so the compiler keeps exact waits for them); the remaining chunks follow it.
+template <int MT, int BN, bool ACT, bool AFM, bool SPAN, typename Epi>
+__device__ __forceinline__ void wsd_consume(const uint4* sW, const char* const (&ap)[MT], int nk, int nsub,
                                             int lane, Epi&& epi) {
+  using S = WsdShape<BN>;
+  constexpr int NT = S::NT;
   int fk = 0;  // chunk of the next activation fetch
   auto fetch_a = [&](v8s (&A)[MT][2]) __attribute__((always_inline)) {
     if constexpr (ACT) {
@@ -92,42 +125,49 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
       fk = fk + 1 == nk ? 0 : fk + 1;
     }
   };
-  v4f acc[MT][4];
+  v4f acc[MT][NT];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+  // activation prefetch depth in chunks: 3, or 2 for the twice as long chunks of
+  // 128-row n-blocks (fewer registers for their twice as many accumulators)
+  constexpr int PD = BN == 128 ? 2 : 3;
   v8s A0[MT][2], A1[MT][2], A2[MT][2], A3[MT][2];
   fetch_a(A0);
   fetch_a(A1);
-  fetch_a(A2);
+  if constexpr (PD == 3) fetch_a(A2);
   int kc = 0, sub = 0;  // chunk within the n-block, n-block of the span
   auto step = [&](v8s (&Acur)[MT][2], v8s (&Anext)[MT][2], int c) __attribute__((always_inline)) {
-    fetch_a(Anext);                // chunk c + 3 (past the end: the first chunks again)
+    fetch_a(Anext);                // chunk c + PD (past the end: the first chunks again)
     __builtin_amdgcn_s_barrier();  // chunk c is in its stage
     asm volatile("" ::: "memory");
     if constexpr (ACT) {
-      const uint4* st = sW[c % NST];
+      const uint4* st = sW + (c % S::NST) * S::SLOTS;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        v8s wf[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const uint4 u = st[wsd_slot(n * 16 + (lane & 15), q * 4 + (lane >> 4))];
-          wf[n] = *reinterpret_cast<const v8s*>(&u);
+        for (int n0 = 0; n0 < NT; n0 += 4) {  // weight fragments four n-tiles at a time
+          v8s wf[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const uint4 u = st[wsd_slot((n0 + n) * 16 + (lane & 15), q * 4 + (lane >> 4))];
+            wf[n] = *reinterpret_cast<const v8s*>(&u);
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              acc[m][n0 + n] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n0 + n], 0, 0, 0);
         }
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int n = 0; n < 4; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n], 0, 0, 0);
       }
       if (SPAN && ++kc == nk) {  // the n-block is done (uniform)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           epi(acc[m], sub, m);
 #pragma unroll
-          for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int n = 0; n < NT; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
         }
         kc = 0;
         ++sub;
@@ -136,15 +176,25 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
   };
   const int total = nsub * nk;
   int c = 0;
-  for (; c + 4 <= total; c += 4) {
-    step(A0, A3, c);
-    step(A1, A0, c + 1);
-    step(A2, A1, c + 2);
-    step(A3, A2, c + 3);
+  if constexpr (PD == 3) {
+    for (; c + 4 <= total; c += 4) {
+      step(A0, A3, c);
+      step(A1, A0, c + 1);
+      step(A2, A1, c + 2);
+      step(A3, A2, c + 3);
+    }
+    if (c < total) step(A0, A3, c);  // the last total % 4 chunks
+    if (c + 1 < total) step(A1, A0, c + 1);
+    if (c + 2 < total) step(A2, A1, c + 2);
+  } else {
+    for (; c + 3 <= total; c += 3) {
+      step(A0, A2, c);
+      step(A1, A0, c + 1);
+      step(A2, A1, c + 2);
+    }
+    if (c < total) step(A0, A2, c);  // the last total % 3 chunks
+    if (c + 1 < total) step(A1, A0, c + 1);
   }
-  if (c < total) step(A0, A3, c);  // the last total % 4 chunks
-  if (c + 1 < total) step(A1, A0, c + 1);
-  if (c + 2 < total) step(A2, A1, c + 2);
   if constexpr (ACT && !SPAN) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) epi(acc[m], 0, m);
@@ -152,33 +202,34 @@ __device__ __forceinline__ void wsd_consume(uint4 (*sW)[WSD_SLOTS], const char* 
 }
 
 // A consumer wave's results for its m-tile (rows t0 .. t0 + 15 of a part with
-// cnt rows) and the 64 weight rows of n-block nb: lane holds columns n * 16 +
+// cnt rows) and the 16 NT weight rows of n-block nb (SwiGLU: NT / 2 n-tiles of
+// W1 rows, then the matching NT / 2 of W3): lane holds columns n * 16 +
 // lane % 16 of rows 4 (lane / 16) + i.  orow[i]: where the lane's row i goes
 // -- the fragment-major offset of the expert-sorted row (SwiGLU) or the pair
 // index (fp32 store) -- looked up before the chunk loop, so the epilogue
 // issues stores only.
-template <int EPI>
-__device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4], int nb, int cnt, int t0, int lane,
+template <int EPI, int NT>
+__device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[NT], int nb, int cnt, int t0, int lane,
                                              const int (&orow)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = t0 + (lane >> 4) * 4 + i;
     if (rl >= cnt) continue;
     if constexpr (EPI == WS_EPI_SWIGLU) {
-      // hidden rows at the expert-sorted row, fragment-major: the n-block's 32
-      // columns of an m-tile are one 1 KB block, orow[i] the row's element
-      // offset in its tile's first block (fm_index of column 0)
+      // hidden rows at the expert-sorted row, fragment-major: each 32 columns
+      // of an m-tile are one 1 KB block, orow[i] the row's element offset in
+      // its tile's first block (fm_index of column 0)
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int col = nb * 32 + n * 16 + (lane & 15);
+      for (int n = 0; n < NT / 2; ++n) {
+        const int col = nb * 8 * NT + n * 16 + (lane & 15);
         if (col >= a.N) continue;
-        ((bf16_t*)a.out)[(size_t)orow[i] + nb * 512 + (2 * n + ((lane >> 3) & 1)) * 128 + (lane & 7)] =
-            f2bf(silu_f(acc[n][i]) * acc[n + 2][i]);
+        ((bf16_t*)a.out)[(size_t)orow[i] + (col >> 5) * 512 + ((col & 31) >> 3) * 128 + (lane & 7)] =
+            f2bf(silu_f(acc[n][i]) * acc[n + NT / 2][i]);
       }
     } else {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int col = nb * WSD_BN + n * 16 + (lane & 15);
+      for (int n = 0; n < NT; ++n) {
+        const int col = nb * 16 * NT + n * 16 + (lane & 15);
         if (col >= a.N) continue;
         ((float*)a.out)[(size_t)orow[i] * a.ldo + col] = acc[n][i];
       }
@@ -197,10 +248,12 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[4
 //     n-block run together and read its weight tile from that XCD's L2; the
 //     grid is 8 ceil(nblk / 8) x parts x ranges, padding blocks exit at once.
 //     Activations fragment-major; the epilogues of k_ws (ws_tile_epilogue).
-template <int EPI, int NST, bool DENSE>
+template <int EPI, bool DENSE, int BN>
 __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
-  static_assert(NST >= 3 && (NST - 2) * WSD_INS <= 63, "ring depth within the vmcnt range");
-  __shared__ uint4 sW[NST][WSD_SLOTS];
+  using S = WsdShape<BN>;
+  constexpr int NST = S::NST, INS = S::INS;
+  static_assert(NST >= 3 && (NST - 2) * INS <= 63, "ring depth within the vmcnt range");
+  __shared__ uint4 sW[WSD_LDS_SLOTS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int g = 0, row0, cnt, nb0, nsub = 1, ks = 0, kc0 = 0, nk = a.K / 64;
   if constexpr (DENSE) {
@@ -233,12 +286,12 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
   if (wave >= WSD_NCW) {
     // ---- producer: copies of the weight chunks (a span's n-blocks in turn) into the LDS ring
     const int p = wave - WSD_NCW;
-    const char* src[WSD_INS];
+    const char* src[INS];
     auto rows_of = [&](int nb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < WSD_INS; ++i) {
-        const int s = (p * WSD_INS + i) * 64 + lane, row = s >> 3, seg = (s & 7) ^ (row & 7);
-        src[i] = weight_row<EPI, 4>(a, g, nb, row) + (size_t)kc0 * 128 + seg * 16;
+      for (int i = 0; i < INS; ++i) {
+        const int s = (p * INS + i) * 64 + lane, row = s >> 3, seg = (s & 7) ^ (row & 7);
+        src[i] = weight_row<EPI, S::NT>(a, g, nb, row) + (size_t)kc0 * 128 + seg * 16;
       }
     };
     rows_of(nb0);
@@ -252,14 +305,14 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       }  // past the end: the last chunk again
       const size_t kb = (size_t)pk * 128;
 #pragma unroll
-      for (int i = 0; i < WSD_INS; ++i) lds_dma16(src[i] + kb, &sW[st][(p * WSD_INS + i) * 64]);
+      for (int i = 0; i < INS; ++i) lds_dma16(src[i] + kb, &sW[st * S::SLOTS + (p * INS + i) * 64]);
     };
     DG_WAIT_VMCNT(0);  // nothing of the compiler's own is outstanding from here on
 #pragma unroll
     for (int c = 0; c < NST - 1; ++c) issue(c);
     const int total = nsub * nk;
     for (int c = 0; c < total; ++c) {
-      DG_WAIT_VMCNT((NST - 2) * WSD_INS);  // this wave's copies of chunk c have landed
+      DG_WAIT_VMCNT((NST - 2) * INS);  // this wave's copies of chunk c have landed
       __builtin_amdgcn_s_barrier();        // ... and every wave's; stage (c - 1) % NST is free
       asm volatile("" ::: "memory");
       issue((c + NST - 1) % NST);
@@ -275,11 +328,11 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
     // holds valid rows (only active waves load)
     const int tr = row0 + min(t0, (cnt - 1) & ~15);
     const char* const ap[1] = {(const char*)a.A + ((size_t)(tr >> 4) * (a.K >> 5) + 2 * kc0) * 1024 + lane * 16};
-    auto epi = [&](const v4f (&acc)[4], int sub, int) __attribute__((always_inline)) {
-      ws_tile_epilogue<EPI, 4, DG_WS_W_BF16>(a, acc, 0, nb0 + sub, row0, t0, cnt, 0, 0, ks, lane);
+    auto epi = [&](const v4f (&acc)[S::NT], int sub, int) __attribute__((always_inline)) {
+      ws_tile_epilogue<EPI, S::NT, DG_WS_W_BF16>(a, acc, 0, nb0 + sub, row0, t0, cnt, 0, 0, ks, lane);
     };
-    if (t0 < cnt) wsd_consume<1, true, NST, true, false>(sW, ap, nk, 1, lane, epi);  // uniform over the wave
-    else wsd_consume<1, false, NST, true, false>(sW, ap, nk, 1, lane, epi);
+    if (t0 < cnt) wsd_consume<1, BN, true, true, false>(sW, ap, nk, 1, lane, epi);  // uniform over the wave
+    else wsd_consume<1, BN, false, true, false>(sW, ap, nk, 1, lane, epi);
   } else {
     // m-tiles t0 and t0 + 128 of the part.  W1/W3 (row-major token rows):
     // lane's row of each (a row past the part's end reads its last row; only
@@ -308,36 +361,37 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
         else orow[m][i] = tm < cnt ? a.perm[a.offsets[g] + row0 + rl] : 0;
       }
     }
-    auto epi = [&](const v4f (&acc)[4], int sub, int m) __attribute__((always_inline)) {
-      wsd_epilogue<EPI>(a, acc, nb0 + sub, cnt, t0 + m * DG_WS_GROUP_ROWS, lane, orow[m]);
+    auto epi = [&](const v4f (&acc)[S::NT], int sub, int m) __attribute__((always_inline)) {
+      wsd_epilogue<EPI, S::NT>(a, acc, nb0 + sub, cnt, t0 + m * DG_WS_GROUP_ROWS, lane, orow[m]);
     };
     // The waves with two, one or no m-tiles run separate loops (same barriers):
     // a conditional load inside the loop makes the compiler's wait bookkeeping
     // give up the three-chunk lead of the activation loads.
+    // units of one n-block run the epilogue once after the loop
+    constexpr bool SP = (EPI == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD_SPAN_DN) > 1;
     if (t0 + DG_WS_GROUP_ROWS < cnt) {  // uniform over the wave
       const char* const ap2[2] = {ap[0], ap[1]};
-      wsd_consume<2, true, NST, AFM, true>(sW, ap2, nk, nsub, lane, epi);
+      wsd_consume<2, BN, true, AFM, SP>(sW, ap2, nk, nsub, lane, epi);
     } else {
       const char* const ap1[1] = {ap[0]};
-      if (t0 < cnt) wsd_consume<1, true, NST, AFM, true>(sW, ap1, nk, nsub, lane, epi);
-      else wsd_consume<1, false, NST, AFM, true>(sW, ap1, nk, nsub, lane, epi);
+      if (t0 < cnt) wsd_consume<1, BN, true, AFM, SP>(sW, ap1, nk, nsub, lane, epi);
+      else wsd_consume<1, BN, false, AFM, SP>(sW, ap1, nk, nsub, lane, epi);
     }
   }
 }
 
 }  // namespace
 
-// LDS ring depth (stages of 8 KB; a 64 KB ring allows one block per CU).
-#ifndef DG_WSD_NST
-#define DG_WSD_NST 8
-#endif
+int dg_wsd_bn(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_BN_UP : DG_WSD_BN_DN; }
+int dg_wsd_span(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD_SPAN_DN; }
 
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return 0;
   if (!a.counts || !a.units || !a.n_units || a.wfmt != DG_WS_W_BF16 || a.K % 64 || a.K < 64) return -1;
   if (a.nblk <= 0 || a.span > 0xffff || (a.rowsrc && epi != WS_EPI_SWIGLU)) return -1;
-  if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, DG_WSD_NST, false><<<grid, WSD_NT, 0, s>>>(a);
-  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, DG_WSD_NST, false><<<grid, WSD_NT, 0, s>>>(a);
+  if (a.span > 1 && dg_wsd_span(epi) <= 1) return -1;  // that kernel stores one n-block per unit
+  if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP><<<grid, WSD_NT, 0, s>>>(a);
+  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN><<<grid, WSD_NT, 0, s>>>(a);
   else return -1;
   return 0;
 }
@@ -349,11 +403,11 @@ int dg_launch_wsd_dense(int epi, const WsArgs& a, hipStream_t s) {
   const int grid = (a.nblk + 7) / 8 * 8 * max(a.msplit, 1) * max(a.ksplit, 1);
   if (M <= 0 || max(a.msplit, 1) * DG_WS_GROUP_ROWS < M) return -1;  // every row in a part
   switch (epi) {
-    case WS_EPI_STORE_BF16: k_wsd<WS_EPI_STORE_BF16, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
-    case WS_EPI_STORE_F32: k_wsd<WS_EPI_STORE_F32, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
-    case WS_EPI_ADD_F32: k_wsd<WS_EPI_ADD_F32, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
-    case WS_EPI_SWIGLU: k_wsd<WS_EPI_SWIGLU, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
-    case WS_EPI_ROPE_QKV: k_wsd<WS_EPI_ROPE_QKV, DG_WSD_NST, true><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_BF16: k_wsd<WS_EPI_STORE_BF16, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_STORE_F32: k_wsd<WS_EPI_STORE_F32, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_ADD_F32: k_wsd<WS_EPI_ADD_F32, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_SWIGLU: k_wsd<WS_EPI_SWIGLU, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
+    case WS_EPI_ROPE_QKV: k_wsd<WS_EPI_ROPE_QKV, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
     default: return -1;
   }
   return 0;
