@@ -231,6 +231,14 @@ __global__ void __launch_bounds__(256) k_attn(const T* __restrict__ q, DgShape s
 // move everything downstream of the layer.  A row's reference maximum moves only
 // when a tile's maximum exceeds it by more than 2^8 (so P <= 256), which keeps
 // the rescaling of the running output rare.
+// Two floats rounded to bf16 (nearest even) and packed, a in the low half: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 template <int HD>
 __device__ __forceinline__ int kswz(int key) {
   // 16 distinct values over the 16 keys of a score tile (4 bits, or 3 bits plus
@@ -269,7 +277,7 @@ __global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __res
     if constexpr (j == 0) return sV0; else if constexpr (j == 1) return sV1; else if constexpr (j == 2) return sV2;
     else return sV3;
   };
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
 
   int bid = blockIdx.x;
@@ -378,24 +386,40 @@ __global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __res
           sc4[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][kk], sc4[kt][qt], 0, 0, 0);
       }
     }
-    // lane (g4, c16) holds, for query column c16, keys 8 g4 + 4 kt + i
+    // lane (g4, c16) holds, for query column c16, keys 8 g4 + 4 kt + i.  The
+    // maximum is taken on the raw scores (scale > 0, so it is the scaled
+    // maximum exactly once scaled) and the scale goes into the exponent's fma;
+    // tiles that lie below every row's key limit skip the mask.
     float p[2][QT][4];
     bool grow = false;
     float alpha[QT];
+    bool below = true;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) below &= kb + 32 <= klim[qt];
+    float tmx[QT];
+    auto scan = [&](auto MASK) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sv = sc4[kt][qt][i];
+            if constexpr (decltype(MASK)::value) p[kt][qt][i] = kb + 8 * g4 + 4 * kt + i < klim[qt] ? sv : -INFINITY;
+            else p[kt][qt][i] = sv;
+            tmax = fmaxf(tmax, p[kt][qt][i]);
+          }
+        tmx[qt] = tmax;
+      }
+    };
+    if (__all(below)) scan(std::false_type{});  // wave-uniform
+    else scan(std::true_type{});
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 8 * g4 + 4 * kt + i;
-          const float sv = key < klim[qt] ? sc4[kt][qt][i] * scale : -INFINITY;
-          p[kt][qt][i] = sv;
-          tmax = fmaxf(tmax, sv);
-        }
+      float tmax = tmx[qt];
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale;
       const bool move = tmax > mrun[qt] + RESCALE_TH;
       const float mnew = move ? tmax : mrun[qt];
       alpha[qt] = move ? __builtin_amdgcn_exp2f(mrun[qt] - mnew) : 1.f;  // 2^-inf = 0 on the first move
@@ -407,7 +431,7 @@ __global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __res
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(p[kt][qt][i] - mref);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(p[kt][qt][i], scale, -mref));
           p[kt][qt][i] = e;
           psum += e;
         }
@@ -419,18 +443,23 @@ __global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __res
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) oacc[ht][qt] *= alpha[qt];
     }
+    // P = hi + lo, both bf16 (round to nearest even, two values per
+    // conversion instruction)
     F pf[QT], pl[QT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
+    for (int qt = 0; qt < QT; ++qt) {
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = p[kt][qt][i];
-          const bf16_t hi = f2bf(v);
-          pf[qt][kt * 4 + i] = (short)hi;
-          pl[qt][kt * 4 + i] = (short)f2bf(v - bf2f(hi));
-        }
+      for (int j = 0; j < 4; ++j) {
+        const float v0 = p[j >> 1][qt][2 * (j & 1)], v1 = p[j >> 1][qt][2 * (j & 1) + 1];
+        const uint32_t h = bf16x2_rne(v0, v1);
+        hw[j] = h;
+        lw[j] = bf16x2_rne(v0 - __uint_as_float(h << 16), v1 - __uint_as_float(h & 0xffff0000u));
+      }
+      const uint4 hu = make_uint4(hw[0], hw[1], hw[2], hw[3]), lu = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      pf[qt] = *reinterpret_cast<const F*>(&hu);
+      pl[qt] = *reinterpret_cast<const F*>(&lu);
+    }
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int d = ht * 16 + c16;
