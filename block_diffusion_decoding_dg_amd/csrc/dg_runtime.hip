@@ -480,6 +480,12 @@ DgSegs make_segs(const dg_ctx* c, const std::vector<SlotRow>& slots, int l, bool
 // Row ranges per weight tile for a dense launch with nblk tiles over M rows: as
 // many blocks as fit one per CU (256), at least 16 rows per block.  The extra
 // reads of a tile come from L2 (see the row split in k_ws).
+// Output columns per n-block of the output projection (64 or 128: 128 halves
+// the activation reads per weight byte, and more reduction ranges keep the
+// grid near one block per CU).
+#ifndef DG_OUTPROJ_BN
+#define DG_OUTPROJ_BN 128
+#endif
 #ifndef DG_DENSE_BLOCKS
 #define DG_DENSE_BLOCKS 256
 #endif
@@ -541,7 +547,7 @@ void launch_dense(dg_ctx* c, int epi, const void* A, int M, int K, const void* W
 // next row kernel (in range order, so the result is deterministic).
 DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, int N, float* out,
                          hipStream_t st = nullptr, float* parts = nullptr, int max_ksplit = DG_MAX_KSPLIT,
-                         int part_rows = 128) {
+                         int part_rows = 128, int bn = 64) {
   if (!parts) parts = c->parts;
   if (c->dtype != DG_BF16) {  // bf16-only kernel; the fp32 model has its own launches
     REFUSE_IF(c, true, "bf16 streaming add projection on a non-bf16 model");
@@ -557,11 +563,12 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   a.out = out;
   a.ldo = N;
   if (DG_DENSE_KERNEL == 1) {
-    // k_wsd: 64 output columns per n-block, 128-row parts; the reduction split
-    // into ranges (partial sums folded by the next row kernel) while that keeps
-    // the grid within one block per CU
-    const int nblk = (N + 63) / 64, padded = (nblk + 7) / 8 * 8;
+    // k_wsd: bn (64 or 128) output columns per n-block, 128-row parts; the
+    // reduction split into ranges (partial sums folded by the next row kernel)
+    // while that keeps the grid within one block per CU
+    const int nblk = (N + bn - 1) / bn, padded = (nblk + 7) / 8 * 8;
     a.nblk = nblk;
+    a.wide = bn == 128;
     a.msplit = (M + DG_WS_GROUP_ROWS - 1) / DG_WS_GROUP_ROWS;
     int ks = 1;
     if (M <= c->parts_rows && N == c->cfg.d_model)
@@ -847,7 +854,8 @@ DgParts attn_half(dg_ctx* c, int l, const std::vector<SlotRow>& slots, int rows,
     KT(c, DG_KF_OUT_PROJ, dg_launch_gemm(c->dtype, 2, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x,
                                          m.d_model, s));
   else
-    KT(c, DG_KF_OUT_PROJ, pend = launch_dense_add(c, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x));
+    KT(c, DG_KF_OUT_PROJ, pend = launch_dense_add(c, c->ao, rows, m.n_q_heads * m.head_dim, w.wo, m.d_model, c->x,
+                                                  nullptr, nullptr, DG_MAX_KSPLIT, 128, DG_OUTPROJ_BN));
   return pend;
 }
 

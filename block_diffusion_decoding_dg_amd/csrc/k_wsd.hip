@@ -402,6 +402,11 @@ int dg_launch_wsd_dense(int epi, const WsArgs& a, hipStream_t s) {
   const int M = a.M;  // with M_dev: the most rows the device count can hold
   const int grid = (a.nblk + 7) / 8 * 8 * max(a.msplit, 1) * max(a.ksplit, 1);
   if (M <= 0 || max(a.msplit, 1) * DG_WS_GROUP_ROWS < M) return -1;  // every row in a part
+  if (a.wide) {  // n-blocks of 128 weight rows: the fp32 add only
+    if (epi != WS_EPI_ADD_F32) return -1;
+    k_wsd<WS_EPI_ADD_F32, true, 128><<<grid, WSD_NT, 0, s>>>(a);
+    return 0;
+  }
   switch (epi) {
     case WS_EPI_STORE_BF16: k_wsd<WS_EPI_STORE_BF16, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
     case WS_EPI_STORE_F32: k_wsd<WS_EPI_STORE_F32, true, 64><<<grid, WSD_NT, 0, s>>>(a); break;
