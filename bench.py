@@ -113,11 +113,10 @@ def measured_traffic(w):
     workload) from the committed rocprofv3 counter summary (FETCH_SIZE +
     WRITE_SIZE, copy-calibrated), or None when the kernel's source has changed
     since the counters were taken or the summary has no figure for it.  The bf16
-    experts run on k_wsd, the FP8 and MXFP4 codes on k_ws."""
+    and FP8 experts run on k_wsd, the MXFP4 codes on k_ws."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "ws_hbm_traffic.md")
-    src_name, sha_key = {"fp8": ("k_ws.hip", "k_ws_source_sha256"),
-                         "mxfp4": ("k_ws.hip", "k_ws_source_sha256")}.get(w.expert_format,
+    src_name, sha_key = {"mxfp4": ("k_ws.hip", "k_ws_source_sha256")}.get(w.expert_format,
                                                                          ("k_wsd.hip", "k_wsd_source_sha256"))
     src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", src_name)
     try:

@@ -619,14 +619,25 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   return pend;
 }
 
-// Kernel of the routed launches: DG_ROUTED_KERNEL for bf16 experts, k_ws for
-// the codes that are widened on the way (E4M3, MXFP4).
+// Kernel of the routed launches: DG_ROUTED_KERNEL (k_wsd) for bf16 experts and
+// for E4M3 codes (copied into LDS as codes, widened to bf16 in registers),
+// k_ws for MXFP4 codes (widened on the way into LDS).
+#ifndef DG_ROUTED_FP8_KERNEL
+#define DG_ROUTED_FP8_KERNEL 1
+#endif
 int routed_kernel(const dg_ctx* c) {
-  return c->dtype == DG_BF16 && c->cfg.expert_format == DG_EXPERTS_NATIVE ? DG_ROUTED_KERNEL : 0;
+  if (c->dtype != DG_BF16) return 0;
+  if (c->cfg.expert_format == DG_EXPERTS_NATIVE) return DG_ROUTED_KERNEL;
+  if (c->cfg.expert_format == DG_EXPERTS_FP8) return DG_ROUTED_FP8_KERNEL;
+  return 0;
 }
-// Rows per part of a routed work list: k_wsd takes up to 256 (two m-tiles per
-// consumer wave), so an expert's weights stream once for up to 256 rows.
-int routed_part_rows(const dg_ctx* c) { return routed_kernel(c) == 1 ? DG_WSD_PART_ROWS : DG_WS_GROUP_ROWS; }
+// Rows per part of a routed work list: k_wsd takes up to 256 for bf16 weights
+// (two m-tiles per consumer wave), so an expert's weights stream once for up to
+// 256 rows; 128 for E4M3 codes (registers for their widening).
+int routed_part_rows(const dg_ctx* c) {
+  if (routed_kernel(c) != 1) return DG_WS_GROUP_ROWS;
+  return c->cfg.expert_format == DG_EXPERTS_FP8 ? DG_WS_GROUP_ROWS : DG_WSD_PART_ROWS;
+}
 // n-blocks per unit of a k_wsd work list, and the units per row part.
 int wsd_span(int epi) { return dg_wsd_span(epi); }
 int list_blocks(const dg_ctx* c, int epi, int nblk) {

@@ -95,17 +95,6 @@ __device__ __forceinline__ v8s (&abuf(AFrags<MT, KSUB>& F))[MT][2 * KSUB] {
   else return F.b3;
 }
 
-// Eight E4M3 codes (little-endian bytes, in reduction order) widened to eight
-// bf16 values: exact, since an E4M3 value has a 4-bit significand and an
-// exponent inside bf16's range.  The conversion reads the OCP E4M3 encoding.
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
-}
 
 // Eight MXFP4 (E2M1) codes, two per byte with the lower reduction index in the
 // low nibble, widened to bf16 and multiplied by their block's E8M0 scale

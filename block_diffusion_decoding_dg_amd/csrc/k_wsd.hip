@@ -81,18 +81,27 @@ constexpr int WSD_NPW = 2;                           // producer waves
 constexpr int WSD_NT = 64 * (WSD_NCW + WSD_NPW);     // 640 threads
 constexpr int WSD_LDS_SLOTS = 4096;                 // 16-byte LDS slots of the ring (64 KB)
 // A block's n-block is BN weight rows (64 or 128: NT = BN / 16 n-tiles per
-// consumer wave); a chunk is BN rows x 64 reduction elements, BN * 8 slots, and
-// the ring holds WSD_LDS_SLOTS / (BN * 8) chunks.  ins: copies per producer
-// wave per chunk.
-template <int BN>
+// consumer wave); a chunk is BN rows x 64 reduction elements: SEG 16-byte
+// segments per row (8 for bf16 weights, 4 for E4M3 codes), SLOTS = BN SEG
+// 16-byte slots, and the ring holds WSD_LDS_SLOTS / SLOTS chunks.  INS: copies
+// per producer wave per chunk.
+template <int BN, int WF = DG_WS_W_BF16>
 struct WsdShape {
-  static constexpr int NT = BN / 16, SLOTS = BN * 8, NST = WSD_LDS_SLOTS / SLOTS, INS = SLOTS / 64 / WSD_NPW;
+  static constexpr int NT = BN / 16, SEG = WF == DG_WS_W_E4M3 ? 4 : 8, SLOTS = BN * SEG,
+                       NST = WSD_LDS_SLOTS / SLOTS, INS = SLOTS / 64 / WSD_NPW;
 };
 static_assert(WSD_NCW * 16 == DG_WS_GROUP_ROWS, "one m-tile per consumer wave covers a dense part");
 static_assert(2 * DG_WS_GROUP_ROWS == DG_WSD_PART_ROWS, "two m-tiles per consumer wave cover a routed part");
 
-// LDS slot of 16-byte segment seg (0..7) of weight row `row` of a stage.
-__device__ __forceinline__ int wsd_slot(int row, int seg) { return row * 8 + (seg ^ (row & 7)); }
+// LDS slot of 16-byte segment seg of weight row `row` of a stage: bf16 rows of
+// 8 segments XOR-swizzled by the row's low 3 bits, E4M3 rows of 4 segments by
+// bits 1-2 (eight consecutive lanes reading one segment of eight consecutive
+// rows then touch eight distinct 16-byte bank groups).
+template <int WF = DG_WS_W_BF16>
+__device__ __forceinline__ int wsd_slot(int row, int seg) {
+  if constexpr (WF == DG_WS_W_E4M3) return row * 4 + (seg ^ ((row >> 1) & 3));
+  else return row * 8 + (seg ^ (row & 7));
+}
 
 // A consumer wave's chunk loop over a span of nsub n-blocks (nsub x nk chunks),
 // one barrier per chunk, the weight fragments read from stage c % NST and used
@@ -109,19 +118,27 @@ __device__ __forceinline__ int wsd_slot(int row, int seg) { return row * 8 + (se
 // (epi(acc of m-tile m, n-block, m) for each m-tile).  The
 // loop body covers whole groups of PD + 1 chunks with no branch around a load
 // (so the compiler keeps exact waits for them); the remaining chunks follow it.
-template <int MT, int BN, bool ACT, bool AFM, bool SPAN, typename Epi>
+template <int MT, int BN, bool ACT, bool AFM, bool SPAN, int WF = DG_WS_W_BF16, typename Epi>
 __device__ __forceinline__ void wsd_consume(const uint4* sW, const char* const (&ap)[MT], int nk, int nsub,
                                             int lane, Epi&& epi) {
-  using S = WsdShape<BN>;
+  using S = WsdShape<BN, WF>;
   constexpr int NT = S::NT;
+  constexpr bool E8 = WF == DG_WS_W_E4M3;
+  // Activation step q of chunk fk: bf16 weights take reduction elements
+  // 32 q + 8 g .. + 7 of the chunk in lane group g; E4M3 weights 16 g + 8 q ..
+  // + 7, so that a lane's codes for both steps are one 16-byte segment (ap then
+  // already holds the lane group's offset of the permuted order).
+  auto a_off = [&](int f, int q) __attribute__((always_inline)) -> size_t {
+    if constexpr (AFM) return E8 ? (size_t)f * 2048 + q * 256 : (size_t)(2 * f + q) * 1024;
+    else return (size_t)f * 128 + q * (E8 ? 16 : 64);
+  };
   int fk = 0;  // chunk of the next activation fetch
   auto fetch_a = [&](v8s (&A)[MT][2]) __attribute__((always_inline)) {
     if constexpr (ACT) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          A[m][q] = *(const v8s*)(ap[m] + (AFM ? (size_t)(2 * fk + q) * 1024 : (size_t)fk * 128 + q * 64));
+        for (int q = 0; q < 2; ++q) A[m][q] = *(const v8s*)(ap[m] + a_off(fk, q));
       fk = fk + 1 == nk ? 0 : fk + 1;
     }
   };
@@ -144,22 +161,49 @@ __device__ __forceinline__ void wsd_consume(const uint4* sW, const char* const (
     asm volatile("" ::: "memory");
     if constexpr (ACT) {
       const uint4* st = sW + (c % S::NST) * S::SLOTS;
+      if constexpr (E8) {
+        // two n-tiles at a time (registers): one segment of 16 codes per lane
+        // and n-tile, widened to bf16 half by half (step 0: codes 0..7, step 1:
+        // codes 8..15)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+        for (int n0 = 0; n0 < NT; n0 += 2) {
+          uint4 raw[2];
 #pragma unroll
-        for (int n0 = 0; n0 < NT; n0 += 4) {  // weight fragments four n-tiles at a time
-          v8s wf[4];
+          for (int n = 0; n < 2; ++n) raw[n] = st[wsd_slot<WF>((n0 + n) * 16 + (lane & 15), lane >> 4)];
 #pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const uint4 u = st[wsd_slot((n0 + n) * 16 + (lane & 15), q * 4 + (lane >> 4))];
-            wf[n] = *reinterpret_cast<const v8s*>(&u);
+          for (int q = 0; q < 2; ++q) {
+            v8s wf[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              const uint4 u = q ? e4m3x8_to_bf16(raw[n].z, raw[n].w) : e4m3x8_to_bf16(raw[n].x, raw[n].y);
+              wf[n] = *reinterpret_cast<const v8s*>(&u);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int n = 0; n < 2; ++n)
+                acc[m][n0 + n] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n0 + n], 0, 0, 0);
           }
+        }
+      } else {
 #pragma unroll
-          for (int m = 0; m < MT; ++m)
+        for (int q = 0; q < 2; ++q) {
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-              acc[m][n0 + n] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n0 + n], 0, 0, 0);
+          for (int n0 = 0; n0 < NT; n0 += 4) {  // weight fragments four n-tiles at a time
+            v8s wf[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+              const uint4 u = st[wsd_slot((n0 + n) * 16 + (lane & 15), q * 4 + (lane >> 4))];
+              wf[n] = *reinterpret_cast<const v8s*>(&u);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int n = 0; n < 4; ++n)
+                acc[m][n0 + n] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n0 + n], 0, 0, 0);
+          }
         }
       }
       if (SPAN && ++kc == nk) {  // the n-block is done (uniform)
@@ -208,9 +252,12 @@ __device__ __forceinline__ void wsd_consume(const uint4* sW, const char* const (
 // -- the fragment-major offset of the expert-sorted row (SwiGLU) or the pair
 // index (fp32 store) -- looked up before the chunk loop, so the epilogue
 // issues stores only.
-template <int EPI, int NT>
-__device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[NT], int nb, int cnt, int t0, int lane,
-                                             const int (&orow)[4]) {
+template <int EPI, int NT, int WF = DG_WS_W_BF16>
+__device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[NT], int g, int nb, int cnt, int t0,
+                                             int lane, const int (&orow)[4]) {
+  // E4M3 weights: each weight row's scale multiplies its fp32 sum (SwiGLU: the
+  // W1 and W3 sums before the activation)
+  constexpr bool E8 = WF == DG_WS_W_E4M3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = t0 + (lane >> 4) * 4 + i;
@@ -223,15 +270,17 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[N
       for (int n = 0; n < NT / 2; ++n) {
         const int col = nb * 8 * NT + n * 16 + (lane & 15);
         if (col >= a.N) continue;
+        const float u = E8 ? acc[n][i] * a.wsc0[(size_t)g * a.N + col] : acc[n][i];
+        const float v = E8 ? acc[n + NT / 2][i] * a.wsc1[(size_t)g * a.N + col] : acc[n + NT / 2][i];
         ((bf16_t*)a.out)[(size_t)orow[i] + (col >> 5) * 512 + ((col & 31) >> 3) * 128 + (lane & 7)] =
-            f2bf(silu_f(acc[n][i]) * acc[n + NT / 2][i]);
+            f2bf(silu_f(u) * v);
       }
     } else {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const int col = nb * 16 * NT + n * 16 + (lane & 15);
         if (col >= a.N) continue;
-        ((float*)a.out)[(size_t)orow[i] * a.ldo + col] = acc[n][i];
+        ((float*)a.out)[(size_t)orow[i] * a.ldo + col] = E8 ? acc[n][i] * a.wsc0[(size_t)g * a.N + col] : acc[n][i];
       }
     }
   }
@@ -248,9 +297,11 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[N
 //     n-block run together and read its weight tile from that XCD's L2; the
 //     grid is 8 ceil(nblk / 8) x parts x ranges, padding blocks exit at once.
 //     Activations fragment-major; the epilogues of k_ws (ws_tile_epilogue).
-template <int EPI, bool DENSE, int BN>
+template <int EPI, bool DENSE, int BN, int WF = DG_WS_W_BF16>
 __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
-  using S = WsdShape<BN>;
+  using S = WsdShape<BN, WF>;
+  constexpr bool E8 = WF == DG_WS_W_E4M3;
+  static_assert(!E8 || !DENSE, "E4M3 weights: routed experts only");
   constexpr int NST = S::NST, INS = S::INS;
   static_assert(NST >= 3 && (NST - 2) * INS <= 63, "ring depth within the vmcnt range");
   __shared__ uint4 sW[WSD_LDS_SLOTS];
@@ -278,8 +329,11 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
     const int part = (int)((code >> 16) & 0xff), span = max(a.span, 1);
     nb0 = (int)(code & 0xffff) * span;
     nsub = min(span, a.nblk - nb0);
-    row0 = part * DG_WSD_PART_ROWS;
-    cnt = min(a.counts[g] - row0, DG_WSD_PART_ROWS);
+    // parts of DG_WSD_PART_ROWS rows (E4M3: DG_WS_GROUP_ROWS, one m-tile per
+    // wave, which leaves registers for the code widening)
+    constexpr int PR = E8 ? DG_WS_GROUP_ROWS : DG_WSD_PART_ROWS;
+    row0 = part * PR;
+    cnt = min(a.counts[g] - row0, PR);
     if (cnt <= 0 || nsub <= 0) return;  // uniform over the block
   }
 
@@ -290,8 +344,11 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
     auto rows_of = [&](int nb) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < INS; ++i) {
-        const int s = (p * INS + i) * 64 + lane, row = s >> 3, seg = (s & 7) ^ (row & 7);
-        src[i] = weight_row<EPI, S::NT>(a, g, nb, row) + (size_t)kc0 * 128 + seg * 16;
+        // slot s of the stage holds the global segment of its row that
+        // wsd_slot puts there
+        const int s = (p * INS + i) * 64 + lane, row = s / S::SEG;
+        const int seg = E8 ? (s & 3) ^ ((row >> 1) & 3) : (s & 7) ^ (row & 7);
+        src[i] = weight_row<EPI, S::NT, E8 ? 8 : 16>(a, g, nb, row) + (size_t)kc0 * S::SEG * 16 + seg * 16;
       }
     };
     rows_of(nb0);
@@ -303,7 +360,7 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
         pk = 0;
         rows_of(nb0 + ps);
       }  // past the end: the last chunk again
-      const size_t kb = (size_t)pk * 128;
+      const size_t kb = (size_t)pk * S::SEG * 16;
 #pragma unroll
       for (int i = 0; i < INS; ++i) lds_dma16(src[i] + kb, &sW[st * S::SLOTS + (p * INS + i) * 64]);
     };
@@ -348,11 +405,13 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       const int tm = t0 + m * DG_WS_GROUP_ROWS;
       if constexpr (AFM) {
         const int tile = (a.offsets16[g] + row0 + min(tm, (cnt - 1) & ~15)) >> 4;
-        ap[m] = (const char*)a.A + (size_t)tile * (a.K >> 5) * 1024 + lane * 16;
+        const int gq = lane >> 4;  // E4M3: the permuted reduction order of wsd_consume
+        ap[m] = (const char*)a.A + (size_t)tile * (a.K >> 5) * 1024 +
+                (E8 ? (gq >> 1) * 1024 + (32 * (gq & 1) + (lane & 15)) * 16 : lane * 16);
       } else {
         const int srow = a.offsets16[g] + row0 + min(tm + (lane & 15), cnt - 1);
         const int row = a.rowsrc ? a.rowsrc[srow] : srow;
-        ap[m] = (const char*)a.A + (size_t)row * a.K * 2 + (lane >> 4) * 16;
+        ap[m] = (const char*)a.A + (size_t)row * a.K * 2 + (lane >> 4) * (E8 ? 32 : 16);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -362,20 +421,22 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       }
     }
     auto epi = [&](const v4f (&acc)[S::NT], int sub, int m) __attribute__((always_inline)) {
-      wsd_epilogue<EPI, S::NT>(a, acc, nb0 + sub, cnt, t0 + m * DG_WS_GROUP_ROWS, lane, orow[m]);
+      wsd_epilogue<EPI, S::NT, WF>(a, acc, g, nb0 + sub, cnt, t0 + m * DG_WS_GROUP_ROWS, lane, orow[m]);
     };
     // The waves with two, one or no m-tiles run separate loops (same barriers):
     // a conditional load inside the loop makes the compiler's wait bookkeeping
     // give up the three-chunk lead of the activation loads.
     // units of one n-block run the epilogue once after the loop
     constexpr bool SP = (EPI == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD_SPAN_DN) > 1;
-    if (t0 + DG_WS_GROUP_ROWS < cnt) {  // uniform over the wave
-      const char* const ap2[2] = {ap[0], ap[1]};
-      wsd_consume<2, BN, true, AFM, SP>(sW, ap2, nk, nsub, lane, epi);
+    if (!E8 && t0 + DG_WS_GROUP_ROWS < cnt) {  // uniform over the wave
+      if constexpr (!E8) {
+        const char* const ap2[2] = {ap[0], ap[1]};
+        wsd_consume<2, BN, true, AFM, SP, WF>(sW, ap2, nk, nsub, lane, epi);
+      }
     } else {
       const char* const ap1[1] = {ap[0]};
-      if (t0 < cnt) wsd_consume<1, BN, true, AFM, SP>(sW, ap1, nk, nsub, lane, epi);
-      else wsd_consume<1, BN, false, AFM, SP>(sW, ap1, nk, nsub, lane, epi);
+      if (t0 < cnt) wsd_consume<1, BN, true, AFM, SP, WF>(sW, ap1, nk, nsub, lane, epi);
+      else wsd_consume<1, BN, false, AFM, SP, WF>(sW, ap1, nk, nsub, lane, epi);
     }
   }
 }
@@ -387,11 +448,15 @@ int dg_wsd_span(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD
 
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return 0;
-  if (!a.counts || !a.units || !a.n_units || a.wfmt != DG_WS_W_BF16 || a.K % 64 || a.K < 64) return -1;
+  if (!a.counts || !a.units || !a.n_units || a.K % 64 || a.K < 64) return -1;
+  if (a.wfmt != DG_WS_W_BF16 && (a.wfmt != DG_WS_W_E4M3 || !a.wsc0 || (epi == WS_EPI_SWIGLU && !a.wsc1))) return -1;
   if (a.nblk <= 0 || a.span > 0xffff || (a.rowsrc && epi != WS_EPI_SWIGLU)) return -1;
   if (a.span > 1 && dg_wsd_span(epi) <= 1) return -1;  // that kernel stores one n-block per unit
-  if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP><<<grid, WSD_NT, 0, s>>>(a);
-  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN><<<grid, WSD_NT, 0, s>>>(a);
+  const bool e8 = a.wfmt == DG_WS_W_E4M3;
+  if (epi == WS_EPI_SWIGLU && !e8) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP><<<grid, WSD_NT, 0, s>>>(a);
+  else if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP, DG_WS_W_E4M3><<<grid, WSD_NT, 0, s>>>(a);
+  else if (epi == WS_EPI_STORE_F32 && !e8) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN><<<grid, WSD_NT, 0, s>>>(a);
+  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN, DG_WS_W_E4M3><<<grid, WSD_NT, 0, s>>>(a);
   else return -1;
   return 0;
 }

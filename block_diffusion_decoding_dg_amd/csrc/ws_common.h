@@ -4,6 +4,18 @@
 #include "dg_common.h"
 #include "dg_kernels.h"
 
+// Eight E4M3 codes (little-endian bytes, in reduction order) widened to eight
+// bf16 values: exact, since an E4M3 value has a 4-bit significand and an
+// exponent inside bf16's range.  The conversion reads the OCP E4M3 encoding.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 // Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue, as a byte
 // address; EB = bits per weight (16: bf16, 8: E4M3 codes, 4: MXFP4 codes).
 template <int EPI, int NTN, int EB = 16>
