@@ -474,13 +474,6 @@ __global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __res
   };
 
   if (ntiles > 0) {
-    // The query fragments must have landed before the ring starts: the
-    // compiler's own wait for them would otherwise sit inside the loop, where
-    // (not knowing of the ring's loads) it would drain the ring every tile.
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[qt][kk]));
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -488,6 +481,15 @@ __global__ void __launch_bounds__(QR * 4 / QT, 1) k_attn_lds(const bf16_t* __res
     issue(0, stK(I0{}), stV(I0{}));
     issue(1, stK(I1{}), stV(I1{}));
     issue(2, stK(I2{}), stV(I2{}));
+    // The query fragments must have landed before the loop: the compiler's
+    // own wait for them would otherwise sit inside it, where (not knowing of
+    // the ring's loads) it would drain the ring every tile.  Waiting here, after
+    // the first three tiles' copies are issued, overlaps the two latencies
+    // (the wait covers those copies too).
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[qt][kk]));
     // Tile t sits in stage t % 4; its step refills stage (t + 3) % 4, read by
     // the step before (every wave has passed the barrier since).
     auto step = [&](int t, auto J, auto JN) __attribute__((always_inline)) {
