@@ -62,9 +62,14 @@ int dg_attn_splits(const DgSegs& segs, const DgShape& sh, int max_splits, int qr
 void dg_launch_attention(int dtype, const void* q, const DgShape& sh, const DgSegs& segs, int nsplit, float* opart,
                          float* mlpart, void* o, int rows, hipStream_t s);
 // Router top-k: logits [rows][E] fp32 -> ids [rows][k], gates [rows][k].
-void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s);
-// bf16 router logits [rows][E] fp32 from the fragment-major normalised rows (d a multiple of 64).
-void dg_launch_router(const void* b_fm, int rows, int d, const void* wg, int E, float* logits, hipStream_t s);
+// parts > 1: logits holds that many slabs [parts][rows][E] of partial sums,
+// added in slab order; their total is written over slab 0.
+void dg_launch_topk(float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s, int parts = 1);
+// bf16 router logits [rows][E] fp32 from the fragment-major normalised rows (d a multiple of 64); with
+// ksplit > 1 the reduction is split into that many ranges, slab ks of logits ([ksplit][rows][E]) holding
+// range ks's partial sums (dg_launch_topk adds them).
+void dg_launch_router(const void* b_fm, int rows, int d, const void* wg, int E, float* logits, hipStream_t s,
+                      int ksplit = 1);
 // Permutation: counts[E], offsets[E], perm[rows*k] (pair index t*k + j, token order per expert).
 void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
                        hipStream_t s);
@@ -73,10 +78,10 @@ void dg_launch_permute(const int32_t* ids, int rows, int E, int k, int32_t* coun
 // r, -1 on padding rows, for r < *n_srows) and both grouped work lists
 // (dg_launch_ws_units; lpt: longest-first lists for k_wsd); everything after
 // the top-k in one block for rows <= 2048.
-void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+void dg_launch_route(float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
                      int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b,
-                     int32_t* n_b, hipStream_t s, int lpt = 0);
+                     int32_t* n_b, hipStream_t s, int lpt = 0, int parts = 1);
 // The routing after the top-k in one launch of parallel blocks (rows <= 2048,
 // E <= 256; as k_route_tail): counts, offsets, perm, the expert-sorted layout
 // (offsets16, rowsrc) and both work lists (lpt: longest first).  Returns -1

@@ -23,6 +23,12 @@
 
 // Reduction ranges of a split-reduction add projection, at most (partial-sum
 // buffer: DG_MAX_KSPLIT x max_requests x canvas_len rows of d_model fp32).
+// Reduction ranges of the router logits (bf16 model): each a slab of partial
+// sums, added in range order by the top-k (twice the blocks for a 0.7 MB
+// weight that 128 blocks read at the per-CU L2 rate).
+#ifndef DG_ROUTER_KSPLIT
+#define DG_ROUTER_KSPLIT 2
+#endif
 #ifndef DG_MAX_KSPLIT
 #define DG_MAX_KSPLIT 8
 #endif
@@ -374,7 +380,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->ao = cv.take<void>(Tm * qd * es);
   c->opart = cv.take<float>(attn_cap * m.n_q_heads * m.head_dim * 4);
   c->mlpart = cv.take<float>(attn_cap * m.n_q_heads * 2 * 4);
-  c->rlogits = cv.take<float>(Tm * E * 4);
+  c->rlogits = cv.take<float>(Tm * E * 4 * DG_ROUTER_KSPLIT);  // a slab per router reduction range
   c->rids = cv.take<int32_t>(Tm * k * 4);
   c->rgates = cv.take<float>(Tm * k * 4);
   c->counts = cv.take<int32_t>(E * 4);
@@ -404,7 +410,7 @@ size_t carve(dg_ctx* c, const dg_model_config& m, char* base) {
   c->info_dev = cv.take<int32_t>(m.max_requests * 4 * 4);
   c->tap_ids = cv.take<int32_t>((size_t)m.n_layers * Rs * k * 4);
   c->tap_gates = cv.take<float>((size_t)m.n_layers * Rs * k * 4);
-  c->tap_logits = cv.take<float>((size_t)m.n_layers * Rs * E * 4);
+  c->tap_logits = cv.take<float>((size_t)m.n_layers * Rs * E * 4 * DG_ROUTER_KSPLIT);
   c->inv_freq = cv.take<double>(m.head_dim / 2 * 8);
   c->ids_stage = cv.take<int32_t>(Tm * 4);
   c->xg = cv.take<float>(Rs * d * 4);
@@ -618,6 +624,10 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
   REFUSE_IF(c, dg_launch_ws(WS_EPI_ADD_F32, a, grid, st ? st : c->stream) != 0, "add projection");
   return pend;
 }
+
+// Floats per layer of the router-logit taps: room for every reduction range's
+// slab (the top-k writes their total over the first).
+size_t tap_logit_stride(const dg_ctx* c) { return (size_t)DG_ROUTER_KSPLIT * c->rows_step * c->cfg.n_experts; }
 
 // Kernel of the routed launches: DG_ROUTED_KERNEL (k_wsd) for bf16 experts and
 // for E4M3 codes (copied into LDS as codes, widened to bf16 in registers),
@@ -912,7 +922,7 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     KTS(c, DG_KF_SHARED_DOWN, c->side, pend2 = launch_dense_add(c, c->hs, rows, m.shared_hidden, w.sw2, m.d_model, c->x,
                                                                 c->side, c->parts2, 1, DG_SHARED_W2_ROWS));
     HIPCK_V(hipEventRecord(c->ev_join, c->side));
-    KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s));
+    KT(c, DG_KF_ROUTER, dg_launch_router(c->xn, rows, m.d_model, w.router, m.n_experts, rlog, s, DG_ROUTER_KSPLIT));
     // n-blocks: k_wsd's width (dg_wsd_bn weight rows; SwiGLU: half of them W1),
     // k_ws's 64 weight rows
     const int bn_up = routed_kernel(c) == 1 ? dg_wsd_bn(WS_EPI_SWIGLU) : 64;
@@ -926,7 +936,7 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     const int la = list_blocks(c, WS_EPI_SWIGLU, nb_up), lb = list_blocks(c, WS_EPI_STORE_F32, nb_dn);
     if (wsd && rows <= DG_ROUTE_MAX_ROWS && m.n_experts <= 256 && 16 * m.top_k <= 256) {
       // the permutation and the work lists in one launch of parallel blocks
-      KT(c, DG_KF_PERMUTE, dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s);
+      KT(c, DG_KF_PERMUTE, dg_launch_topk(rlog, rows, m.n_experts, m.top_k, ids, gates, s, DG_ROUTER_KSPLIT);
          REFUSE_IF(c, dg_launch_route_perm(ids, rows, m.n_experts, m.top_k, c->counts, c->offsets, c->perm,
                                            c->offsets16, c->rowsrc, c->n_units + 2, routed_part_rows(c), la,
                                            c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1,
@@ -935,7 +945,8 @@ void ffn_half(dg_ctx* c, int l, int rows, int32_t* ids, float* gates, float* rlo
     } else {
       KT(c, DG_KF_PERMUTE, dg_launch_route(rlog, rows, m.n_experts, m.top_k, ids, gates, c->counts, c->offsets,
                                            c->perm, c->offsets16, c->rowsrc, c->n_units + 2, routed_part_rows(c), la,
-                                           c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1, s, wsd));
+                                           c->units_up, c->n_units, lb, c->units_dn, c->n_units + 1, s, wsd,
+                                           DG_ROUTER_KSPLIT));
     }
     KT(c, DG_KF_EXPERT_UP, launch_routed(c, WS_EPI_SWIGLU, c->xr, w.w1, w.w3, w.w1_scale, w.w3_scale, w.w1_mx_scale,
                                          w.w3_mx_scale, (size_t)m.expert_hidden * m.d_model, m.d_model,
@@ -973,7 +984,7 @@ void forward_layers(dg_ctx* c, const std::vector<SlotRow>& slots, int rows, bool
     const DgParts pend = attn_half(c, l, slots, rows, causal, xn_ready);
     int32_t* ids = tap ? c->tap_ids + (size_t)l * c->rows_step * m.top_k : c->rids;
     float* gates = tap ? c->tap_gates + (size_t)l * c->rows_step * m.top_k : c->rgates;
-    float* rlog = tap ? c->tap_logits + (size_t)l * c->rows_step * m.n_experts : c->rlogits;
+    float* rlog = tap ? c->tap_logits + (size_t)l * tap_logit_stride(c) : c->rlogits;
     const void* next_gain = last ? nullptr : c->layers[l + 1].attn_norm;
     ffn_half(c, l, rows, ids, gates, rlog, next_gain, pend);
     xn_ready = next_gain != nullptr;
@@ -1408,7 +1419,7 @@ dg_status dg_last_step_router_logits(dg_ctx* c, float* logits) {
   if (c->last_rows == 0) return fail(c, DG_ERR_STATE, "no step has run");
   const size_t per = (size_t)c->last_rows * c->cfg.n_experts;
   for (int l = 0; l < c->cfg.n_layers; ++l)
-    HIPCK(c, hipMemcpyAsync(logits + l * per, c->tap_logits + (size_t)l * c->rows_step * c->cfg.n_experts, per * 4,
+    HIPCK(c, hipMemcpyAsync(logits + l * per, c->tap_logits + (size_t)l * tap_logit_stride(c), per * 4,
                             hipMemcpyDeviceToHost, c->stream));
   HIPCK(c, hipStreamSynchronize(c->stream));
   return DG_OK;
@@ -1519,7 +1530,7 @@ dg_status dg_debug_tap(dg_ctx* c, int32_t which, int32_t layer, float* host_dst,
     if (layer < 0 || layer >= L) return fail(c, DG_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, L);
     const size_t n = rows * c->cfg.n_experts * 4;
     if (bytes < n) return fail(c, DG_ERR_INVALID_ARG, "destination of %zu bytes < %zu", bytes, n);
-    HIPCK(c, hipMemcpyAsync(host_dst, c->tap_logits + (size_t)layer * c->rows_step * c->cfg.n_experts, n,
+    HIPCK(c, hipMemcpyAsync(host_dst, c->tap_logits + (size_t)layer * tap_logit_stride(c), n,
                             hipMemcpyDeviceToHost, s));
     HIPCK(c, hipStreamSynchronize(s));
     return DG_OK;

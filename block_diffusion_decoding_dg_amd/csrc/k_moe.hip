@@ -18,15 +18,19 @@
 // order.  The E x E comparisons are spread over the block as (logit, slice of 32
 // logits) items and the partial ranks are summed in LDS.  gates = softmax over the k kept logits, summed in
 // rank order.
-__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int rows, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ gates) {
+__global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits, int rows, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ gates, int parts) {
   __shared__ float s_v[256];
   __shared__ int s_rank[256];
   __shared__ float s_sel[DG_MAX_TOPK];
   const int r = blockIdx.x, tid = threadIdx.x;
-  const float* lrow = logits + (size_t)r * E;
+  float* lrow = logits + (size_t)r * E;
   if (tid < E) {
-    const float x = lrow[tid];
+    // the router's partial sums over its reduction ranges, added in range
+    // order; the total replaces the first range's (what readers of the logits see)
+    float x = lrow[tid];
+    for (int p = 1; p < parts; ++p) x += lrow[(size_t)p * rows * E + tid];
+    if (parts > 1) lrow[tid] = x;
     s_v[tid] = x == x ? x : -INFINITY;
   }
   s_rank[tid] = 0;
@@ -58,9 +62,9 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
   }
 }
 
-void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s) {
+void dg_launch_topk(float* logits, int rows, int E, int k, int32_t* ids, float* gates, hipStream_t s, int parts) {
   if (rows <= 0) return;
-  k_topk<<<rows, 256, 0, s>>>(logits, rows, E, k, ids, gates);
+  k_topk<<<rows, 256, 0, s>>>(logits, rows, E, k, ids, gates, parts < 1 ? 1 : parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -72,13 +76,19 @@ void dg_launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, f
 // order.  b is fragment-major (fm_index), Wg row-major [E][d]; d is a multiple
 // of 64.
 __global__ void __launch_bounds__(512) k_router(const bf16_t* __restrict__ b, int rows, int d,
-                                                const bf16_t* __restrict__ wg, int E, float* __restrict__ logits) {
+                                                const bf16_t* __restrict__ wg, int E, float* __restrict__ logits,
+                                                int ksplit) {
   __shared__ v4f s_part[8][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int net = (E + 15) >> 4;
-  const int rt = blockIdx.x / net, et = blockIdx.x % net;
+  const int net = (E + 15) >> 4, ntile = ((rows + 15) >> 4) * net;
+  const int ks = blockIdx.x / ntile, tile = blockIdx.x % ntile;
+  const int rt = tile / net, et = tile % net;
   const int nk = d >> 5;  // 32-element reduction steps
-  const int k0 = wave * nk / 8, k1 = (wave + 1) * nk / 8;
+  // this block's reduction range (of ksplit), an eighth of it per wave; the
+  // range's partial sums go to slab ks of logits
+  const int r0 = ks * nk / ksplit, r1 = (ks + 1) * nk / ksplit;
+  const int k0 = r0 + wave * (r1 - r0) / 8, k1 = r0 + (wave + 1) * (r1 - r0) / 8;
+  logits += (size_t)ks * rows * E;
   const char* ap = (const char*)b + (size_t)rt * nk * 1024 + lane * 16;
   const int e = min(et * 16 + (lane & 15), E - 1);
   const char* bp = (const char*)(wg + (size_t)e * d) + (lane >> 4) * 16;
@@ -111,10 +121,12 @@ __global__ void __launch_bounds__(512) k_router(const bf16_t* __restrict__ b, in
   }
 }
 
-void dg_launch_router(const void* b_fm, int rows, int d, const void* wg, int E, float* logits, hipStream_t s) {
+void dg_launch_router(const void* b_fm, int rows, int d, const void* wg, int E, float* logits, hipStream_t s,
+                      int ksplit) {
   if (rows <= 0) return;
-  k_router<<<((rows + 15) / 16) * ((E + 15) / 16), 512, 0, s>>>((const bf16_t*)b_fm, rows, d, (const bf16_t*)wg, E,
-                                                              logits);
+  ksplit = ksplit < 1 ? 1 : ksplit;
+  k_router<<<((rows + 15) / 16) * ((E + 15) / 16) * ksplit, 512, 0, s>>>((const bf16_t*)b_fm, rows, d,
+                                                                         (const bf16_t*)wg, E, logits, ksplit);
 }
 
 // ---------------------------------------------------------------------------
@@ -276,11 +288,11 @@ __global__ void __launch_bounds__(256) k_sorted_layout(const int32_t* __restrict
   }
 }
 
-void dg_launch_route(const float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+void dg_launch_route(float* logits, int rows, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* offsets16, int32_t* rowsrc, int32_t* n_srows,
                      int part_rows, int nblk_a, int32_t* units_a, int32_t* n_a, int nblk_b, int32_t* units_b,
-                     int32_t* n_b, hipStream_t s, int lpt) {
-  dg_launch_topk(logits, rows, E, k, ids, gates, s);
+                     int32_t* n_b, hipStream_t s, int lpt, int parts) {
+  dg_launch_topk(logits, rows, E, k, ids, gates, s, parts);
   if (E + (rows * k + part_rows - 1) / part_rows > DG_WS_MAX_PARTS) lpt = 0;  // list order only
   if (rows <= DG_ROUTE_MAX_ROWS && E <= 256) {
     k_route_tail<<<1, 1024, 0, s>>>(ids, rows, E, k, counts, offsets, perm, offsets16, rowsrc, n_srows, part_rows,
