@@ -112,12 +112,11 @@ def measured_traffic(w):
     """HBM bytes per launch of the dominant kernel (bf16, FP8 or MXFP4 experts, per the
     workload) from the committed rocprofv3 counter summary (FETCH_SIZE +
     WRITE_SIZE, copy-calibrated), or None when the kernel's source has changed
-    since the counters were taken or the summary has no figure for it.  The bf16
-    and FP8 experts run on k_wsd, the MXFP4 codes on k_ws."""
+    since the counters were taken or the summary has no figure for it.  The bf16,
+    FP8 and MXFP4 experts run on k_wsd."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "ws_hbm_traffic.md")
-    src_name, sha_key = {"mxfp4": ("k_ws.hip", "k_ws_source_sha256")}.get(w.expert_format,
-                                                                         ("k_wsd.hip", "k_wsd_source_sha256"))
+    src_name, sha_key = "k_wsd.hip", "k_wsd_source_sha256"
     src = os.path.join(ROOT, "block_diffusion_decoding_dg_amd", "csrc", src_name)
     try:
         key = {"fp8": "expert_up_fp8_traffic_bytes_per_launch",

@@ -124,6 +124,7 @@ struct dg_ctx {
   const void* embed = nullptr;
   const void* final_norm = nullptr;
   std::vector<dg_layer_weights> layers;
+  bool mx_wsd = false;  // MXFP4 experts fit k_wsd (16-byte aligned scale rows, their unit copy in LDS)
   char* kv = nullptr;
   hipStream_t stream = nullptr;
   hipStream_t side = nullptr;              // second stream: the shared expert overlaps the routed ones
@@ -629,24 +630,29 @@ DgParts launch_dense_add(dg_ctx* c, const void* A, int M, int K, const void* W, 
 // slab (the top-k writes their total over the first).
 size_t tap_logit_stride(const dg_ctx* c) { return (size_t)DG_ROUTER_KSPLIT * c->rows_step * c->cfg.n_experts; }
 
-// Kernel of the routed launches: DG_ROUTED_KERNEL (k_wsd) for bf16 experts and
-// for E4M3 codes (copied into LDS as codes, widened to bf16 in registers),
-// k_ws for MXFP4 codes (widened on the way into LDS).
+// Kernel of the routed launches: DG_ROUTED_KERNEL (k_wsd) for bf16 experts, and
+// for E4M3 and MXFP4 codes (copied into LDS as codes, widened to bf16 in
+// registers); k_ws (widening on the way into LDS) for MXFP4 scale arrays that
+// k_wsd cannot copy (misaligned).
 #ifndef DG_ROUTED_FP8_KERNEL
 #define DG_ROUTED_FP8_KERNEL 1
+#endif
+#ifndef DG_ROUTED_MX_KERNEL
+#define DG_ROUTED_MX_KERNEL 1
 #endif
 int routed_kernel(const dg_ctx* c) {
   if (c->dtype != DG_BF16) return 0;
   if (c->cfg.expert_format == DG_EXPERTS_NATIVE) return DG_ROUTED_KERNEL;
   if (c->cfg.expert_format == DG_EXPERTS_FP8) return DG_ROUTED_FP8_KERNEL;
+  if (c->cfg.expert_format == DG_EXPERTS_MXFP4 && c->mx_wsd) return DG_ROUTED_MX_KERNEL;
   return 0;
 }
 // Rows per part of a routed work list: k_wsd takes up to 256 for bf16 weights
 // (two m-tiles per consumer wave), so an expert's weights stream once for up to
-// 256 rows; 128 for E4M3 codes (registers for their widening).
+// 256 rows; 128 for E4M3 and MXFP4 codes (registers for their widening).
 int routed_part_rows(const dg_ctx* c) {
   if (routed_kernel(c) != 1) return DG_WS_GROUP_ROWS;
-  return c->cfg.expert_format == DG_EXPERTS_FP8 ? DG_WS_GROUP_ROWS : DG_WSD_PART_ROWS;
+  return c->cfg.expert_format == DG_EXPERTS_NATIVE ? DG_WSD_PART_ROWS : DG_WS_GROUP_ROWS;
 }
 // n-blocks per unit of a k_wsd work list, and the units per row part.
 int wsd_span(int epi) { return dg_wsd_span(epi); }
@@ -1094,6 +1100,16 @@ dg_status dg_create(const dg_model_config* cfg, const dg_sampler_config* scfg, c
   c->embed = weights->embed;
   c->final_norm = weights->final_norm;
   c->layers.assign(weights->layers, weights->layers + m.n_layers);
+  if (m.expert_format == DG_EXPERTS_MXFP4) {
+    // k_wsd copies a unit's block scales into LDS in 16-byte pieces: every scale
+    // array 16-byte aligned, whole pieces per 64 rows, and 128 rows of K / 32
+    // bytes within its LDS copy
+    bool ok = m.expert_hidden % 8 == 0 && m.d_model % 8 == 0 && 128 * (m.d_model / 32) <= 16384 &&
+              128 * (m.expert_hidden / 32) <= 16384;
+    for (const dg_layer_weights& w : c->layers)
+      for (const void* p : {w.w1_mx_scale, w.w3_mx_scale, w.w2_mx_scale}) ok = ok && (uintptr_t)p % 16 == 0;
+    c->mx_wsd = ok;
+  }
   if (m.self_cond_hidden > 0) {
     c->sc_w1 = weights->sc_w1;
     c->sc_w3 = weights->sc_w3;

@@ -96,23 +96,6 @@ __device__ __forceinline__ v8s (&abuf(AFrags<MT, KSUB>& F))[MT][2 * KSUB] {
 }
 
 
-// Eight MXFP4 (E2M1) codes, two per byte with the lower reduction index in the
-// low nibble, widened to bf16 and multiplied by their block's E8M0 scale
-// 2^(sb - 127), passed to the conversion as the float with that exponent field.
-// A two-bit significand times a power of two: exact for scale bytes 1 .. 252
-// (a GPU check over every code byte and byte select matched the exact value
-// rounded to bf16, subnormals included, at scale bytes 1, 2, 120, 127 and 252;
-// from 253 the largest codes overflow bf16; byte 0 reads as a zero scale and
-// 255 as infinity).
-__device__ __forceinline__ uint4 mxfp4x8_to_bf16(uint32_t codes, uint32_t sb) {
-  const float sc = __uint_as_float(sb << 23);
-  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
-  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
-  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
-  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
-  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
-}
 
 // Streams the weight tile of one pass through LDS and accumulates this wave's MA
 // active m-tiles (0 .. MT).

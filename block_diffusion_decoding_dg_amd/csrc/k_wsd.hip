@@ -82,14 +82,17 @@ constexpr int WSD_NT = 64 * (WSD_NCW + WSD_NPW);     // 640 threads
 constexpr int WSD_LDS_SLOTS = 4096;                 // 16-byte LDS slots of the ring (64 KB)
 // A block's n-block is BN weight rows (64 or 128: NT = BN / 16 n-tiles per
 // consumer wave); a chunk is BN rows x 64 reduction elements: SEG 16-byte
-// segments per row (8 for bf16 weights, 4 for E4M3 codes), SLOTS = BN SEG
-// 16-byte slots, and the ring holds WSD_LDS_SLOTS / SLOTS chunks.  INS: copies
-// per producer wave per chunk.
+// segments per row (8 for bf16 weights, 4 for E4M3 codes, 2 for MXFP4 codes),
+// SLOTS = BN SEG 16-byte slots, and the ring holds WSD_LDS_SLOTS / SLOTS
+// chunks.  INS: copies per producer wave per chunk.
 template <int BN, int WF = DG_WS_W_BF16>
 struct WsdShape {
-  static constexpr int NT = BN / 16, SEG = WF == DG_WS_W_E4M3 ? 4 : 8, SLOTS = BN * SEG,
-                       NST = WSD_LDS_SLOTS / SLOTS, INS = SLOTS / 64 / WSD_NPW;
+  static constexpr int NT = BN / 16, SEG = WF == DG_WS_W_E4M3 ? 4 : WF == DG_WS_W_MXFP4 ? 2 : 8,
+                       SLOTS = BN * SEG, NST = WSD_LDS_SLOTS / SLOTS, INS = SLOTS / 64 / WSD_NPW;
 };
+// MXFP4: LDS bytes for the block scales of a unit's weight rows (BN x K / 32),
+// copied once per unit.
+constexpr int WSD_MX_SCALE_BYTES = 16384;
 static_assert(WSD_NCW * 16 == DG_WS_GROUP_ROWS, "one m-tile per consumer wave covers a dense part");
 static_assert(2 * DG_WS_GROUP_ROWS == DG_WSD_PART_ROWS, "two m-tiles per consumer wave cover a routed part");
 
@@ -97,9 +100,14 @@ static_assert(2 * DG_WS_GROUP_ROWS == DG_WSD_PART_ROWS, "two m-tiles per consume
 // 8 segments XOR-swizzled by the row's low 3 bits, E4M3 rows of 4 segments by
 // bits 1-2 (eight consecutive lanes reading one segment of eight consecutive
 // rows then touch eight distinct 16-byte bank groups).
+// MXFP4 rows of 2 segments, the lanes reading 8 bytes (one half of a segment)
+// each: the segments of rows 8..15 of every 16 are swapped, so that 16 lanes
+// reading one half of 16 rows touch 16 distinct 8-byte bank groups of a 256-byte
+// bank row.
 template <int WF = DG_WS_W_BF16>
 __device__ __forceinline__ int wsd_slot(int row, int seg) {
   if constexpr (WF == DG_WS_W_E4M3) return row * 4 + (seg ^ ((row >> 1) & 3));
+  else if constexpr (WF == DG_WS_W_MXFP4) return row * 2 + (seg ^ ((row >> 3) & 1));
   else return row * 8 + (seg ^ (row & 7));
 }
 
@@ -120,10 +128,12 @@ __device__ __forceinline__ int wsd_slot(int row, int seg) {
 // (so the compiler keeps exact waits for them); the remaining chunks follow it.
 template <int MT, int BN, bool ACT, bool AFM, bool SPAN, int WF = DG_WS_W_BF16, typename Epi>
 __device__ __forceinline__ void wsd_consume(const uint4* sW, const char* const (&ap)[MT], int nk, int nsub,
-                                            int lane, Epi&& epi) {
+                                            int lane, Epi&& epi, const uint8_t* sS = nullptr) {
   using S = WsdShape<BN, WF>;
   constexpr int NT = S::NT;
-  constexpr bool E8 = WF == DG_WS_W_E4M3;
+  constexpr bool MX = WF == DG_WS_W_MXFP4;
+  // E4M3 and MXFP4 codes take the reduction order below (E8: permuted)
+  constexpr bool E8 = WF == DG_WS_W_E4M3 || MX;
   // Activation step q of chunk fk: bf16 weights take reduction elements
   // 32 q + 8 g .. + 7 of the chunk in lane group g; E4M3 weights 16 g + 8 q ..
   // + 7, so that a lane's codes for both steps are one 16-byte segment (ap then
@@ -161,7 +171,39 @@ __device__ __forceinline__ void wsd_consume(const uint4* sW, const char* const (
     asm volatile("" ::: "memory");
     if constexpr (ACT) {
       const uint4* st = sW + (c % S::NST) * S::SLOTS;
-      if constexpr (E8) {
+      if constexpr (MX) {
+        // lane group u takes reduction elements 16 u .. 16 u + 15 of the chunk
+        // (the activations were loaded in the same order): 8 bytes of codes per
+        // n-tile, inside one MX block, whose scale byte the unit's copy holds
+        const int u = lane >> 4, kb32 = (nk * 64) >> 5;
+#pragma unroll
+        for (int n0 = 0; n0 < NT; n0 += 2) {
+          uint2 raw[2];
+          uint32_t sb[2];
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const int row = (n0 + n) * 16 + (lane & 15);
+            raw[n] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(st) +
+                                                     wsd_slot<WF>(row, u >> 1) * 16 + (u & 1) * 8);
+            sb[n] = sS[row * kb32 + 2 * (c % nk) + (u >> 1)];
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            v8s wf[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              const uint4 w4 = mxfp4x8_to_bf16(q ? raw[n].y : raw[n].x, sb[n]);
+              wf[n] = *reinterpret_cast<const v8s*>(&w4);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int n = 0; n < 2; ++n)
+                acc[m][n0 + n] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur[m][q], wf[n], acc[m][n0 + n], 0, 0, 0);
+          }
+        }
+      } else if constexpr (E8) {
         // two n-tiles at a time (registers): one segment of 16 codes per lane
         // and n-tile, widened to bf16 half by half (step 0: codes 0..7, step 1:
         // codes 8..15)
@@ -300,11 +342,15 @@ __device__ __forceinline__ void wsd_epilogue(const WsArgs& a, const v4f (&acc)[N
 template <int EPI, bool DENSE, int BN, int WF = DG_WS_W_BF16>
 __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
   using S = WsdShape<BN, WF>;
-  constexpr bool E8 = WF == DG_WS_W_E4M3;
-  static_assert(!E8 || !DENSE, "E4M3 weights: routed experts only");
+  constexpr bool MX = WF == DG_WS_W_MXFP4;
+  // E4M3 or MXFP4 codes: the permuted reduction order, 128-row parts
+  constexpr bool E8 = WF == DG_WS_W_E4M3 || MX;
+  static_assert(!E8 || !DENSE, "E4M3 / MXFP4 weights: routed experts only");
   constexpr int NST = S::NST, INS = S::INS;
   static_assert(NST >= 3 && (NST - 2) * INS <= 63, "ring depth within the vmcnt range");
   __shared__ uint4 sW[WSD_LDS_SLOTS];
+  __shared__ uint4 sS4[MX ? WSD_MX_SCALE_BYTES / 16 : 1];  // MXFP4: the unit's block scales
+  const uint8_t* sS = reinterpret_cast<const uint8_t*>(sS4);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int g = 0, row0, cnt, nb0, nsub = 1, ks = 0, kc0 = 0, nk = a.K / 64;
   if constexpr (DENSE) {
@@ -346,9 +392,16 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       for (int i = 0; i < INS; ++i) {
         // slot s of the stage holds the global segment of its row that
         // wsd_slot puts there
-        const int s = (p * INS + i) * 64 + lane, row = s / S::SEG;
-        const int seg = E8 ? (s & 3) ^ ((row >> 1) & 3) : (s & 7) ^ (row & 7);
-        src[i] = weight_row<EPI, S::NT, E8 ? 8 : 16>(a, g, nb, row) + (size_t)kc0 * S::SEG * 16 + seg * 16;
+        const int s = (p * INS + i) * 64 + lane;
+        int row, seg;
+        if constexpr (MX) {  // the inverse of wsd_slot<MXFP4>
+          row = s >> 1;
+          seg = (s & 1) ^ ((row >> 3) & 1);
+        } else {
+          row = s / S::SEG;
+          seg = WF == DG_WS_W_E4M3 ? (s & 3) ^ ((row >> 1) & 3) : (s & 7) ^ (row & 7);
+        }
+        src[i] = weight_row<EPI, S::NT, MX ? 4 : E8 ? 8 : 16>(a, g, nb, row) + (size_t)kc0 * S::SEG * 16 + seg * 16;
       }
     };
     rows_of(nb0);
@@ -365,6 +418,29 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       for (int i = 0; i < INS; ++i) lds_dma16(src[i] + kb, &sW[st * S::SLOTS + (p * INS + i) * 64]);
     };
     DG_WAIT_VMCNT(0);  // nothing of the compiler's own is outstanding from here on
+    if constexpr (MX) {
+      // The unit's block scales (one n-block: span 1), K / 32 bytes per weight
+      // row, copied once before the ring starts (SwiGLU: the W1 rows, then the
+      // W3 rows); rows past N are not copied.  The first chunk's wait below
+      // covers these copies too (loads complete in order).
+      const int kb32 = a.K >> 5;
+      auto copy_rows = [&](const uint8_t* base, int n0, int nrows, int lrow0) __attribute__((always_inline)) {
+        nrows = min(nrows, a.N - n0);
+        const int pieces = nrows > 0 ? nrows * kb32 / 16 : 0;
+        const uint8_t* src0 = base + (size_t)g * (a.wgs / 32) + (size_t)n0 * kb32;
+        for (int j = 0; j * 128 < pieces; ++j) {
+          const int q = j * 128 + p * 64 + lane;
+          uint4* dst = sS4 + lrow0 * kb32 / 16 + j * 128 + p * 64;  // wave-uniform: lane l writes dst[l]
+          if (q < pieces) lds_dma16(src0 + (size_t)q * 16, dst);
+        }
+      };
+      if constexpr (EPI == WS_EPI_SWIGLU) {
+        copy_rows(a.wbs0, nb0 * (BN / 2), BN / 2, 0);
+        copy_rows(a.wbs1, nb0 * (BN / 2), BN / 2, BN / 2);
+      } else {
+        copy_rows(a.wbs0, nb0 * BN, BN, 0);
+      }
+    }
 #pragma unroll
     for (int c = 0; c < NST - 1; ++c) issue(c);
     const int total = nsub * nk;
@@ -405,7 +481,7 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       const int tm = t0 + m * DG_WS_GROUP_ROWS;
       if constexpr (AFM) {
         const int tile = (a.offsets16[g] + row0 + min(tm, (cnt - 1) & ~15)) >> 4;
-        const int gq = lane >> 4;  // E4M3: the permuted reduction order of wsd_consume
+        const int gq = lane >> 4;  // E4M3, MXFP4: the permuted reduction order of wsd_consume
         ap[m] = (const char*)a.A + (size_t)tile * (a.K >> 5) * 1024 +
                 (E8 ? (gq >> 1) * 1024 + (32 * (gq & 1) + (lane & 15)) * 16 : lane * 16);
       } else {
@@ -435,8 +511,8 @@ __global__ void __launch_bounds__(WSD_NT) k_wsd(WsArgs a) {
       }
     } else {
       const char* const ap1[1] = {ap[0]};
-      if (t0 < cnt) wsd_consume<1, BN, true, AFM, SP, WF>(sW, ap1, nk, nsub, lane, epi);
-      else wsd_consume<1, BN, false, AFM, SP, WF>(sW, ap1, nk, nsub, lane, epi);
+      if (t0 < cnt) wsd_consume<1, BN, true, AFM, SP, WF>(sW, ap1, nk, nsub, lane, epi, sS);
+      else wsd_consume<1, BN, false, AFM, SP, WF>(sW, ap1, nk, nsub, lane, epi, sS);
     }
   }
 }
@@ -449,15 +525,27 @@ int dg_wsd_span(int epi) { return epi == WS_EPI_SWIGLU ? DG_WSD_SPAN_UP : DG_WSD
 int dg_launch_wsd(int epi, const WsArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return 0;
   if (!a.counts || !a.units || !a.n_units || a.K % 64 || a.K < 64) return -1;
-  if (a.wfmt != DG_WS_W_BF16 && (a.wfmt != DG_WS_W_E4M3 || !a.wsc0 || (epi == WS_EPI_SWIGLU && !a.wsc1))) return -1;
+  if (a.wfmt == DG_WS_W_E4M3 && (!a.wsc0 || (epi == WS_EPI_SWIGLU && !a.wsc1))) return -1;
+  if (a.wfmt == DG_WS_W_MXFP4) {  // scales of a unit in LDS: one n-block, whole 16-byte pieces
+    if (!a.wbs0 || (epi == WS_EPI_SWIGLU && !a.wbs1) || a.span > 1 || a.N % 8) return -1;
+    if ((size_t)(epi == WS_EPI_SWIGLU ? DG_WSD_BN_UP : DG_WSD_BN_DN) * (a.K / 32) > WSD_MX_SCALE_BYTES) return -1;
+  }
+  if (a.wfmt != DG_WS_W_BF16 && a.wfmt != DG_WS_W_E4M3 && a.wfmt != DG_WS_W_MXFP4) return -1;
   if (a.nblk <= 0 || a.span > 0xffff || (a.rowsrc && epi != WS_EPI_SWIGLU)) return -1;
   if (a.span > 1 && dg_wsd_span(epi) <= 1) return -1;  // that kernel stores one n-block per unit
-  const bool e8 = a.wfmt == DG_WS_W_E4M3;
-  if (epi == WS_EPI_SWIGLU && !e8) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP><<<grid, WSD_NT, 0, s>>>(a);
-  else if (epi == WS_EPI_SWIGLU) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP, DG_WS_W_E4M3><<<grid, WSD_NT, 0, s>>>(a);
-  else if (epi == WS_EPI_STORE_F32 && !e8) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN><<<grid, WSD_NT, 0, s>>>(a);
-  else if (epi == WS_EPI_STORE_F32) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN, DG_WS_W_E4M3><<<grid, WSD_NT, 0, s>>>(a);
-  else return -1;
+  const int f = a.wfmt;
+  constexpr int B = DG_WS_W_BF16, E8 = DG_WS_W_E4M3, F4 = DG_WS_W_MXFP4;
+  if (epi == WS_EPI_SWIGLU) {
+    if (f == B) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP><<<grid, WSD_NT, 0, s>>>(a);
+    else if (f == E8) k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP, E8><<<grid, WSD_NT, 0, s>>>(a);
+    else k_wsd<WS_EPI_SWIGLU, false, DG_WSD_BN_UP, F4><<<grid, WSD_NT, 0, s>>>(a);
+  } else if (epi == WS_EPI_STORE_F32) {
+    if (f == B) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN><<<grid, WSD_NT, 0, s>>>(a);
+    else if (f == E8) k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN, E8><<<grid, WSD_NT, 0, s>>>(a);
+    else k_wsd<WS_EPI_STORE_F32, false, DG_WSD_BN_DN, F4><<<grid, WSD_NT, 0, s>>>(a);
+  } else {
+    return -1;
+  }
   return 0;
 }
 

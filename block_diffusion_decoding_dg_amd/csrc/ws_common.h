@@ -16,6 +16,24 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
 }
 
+// Eight MXFP4 (E2M1) codes, two per byte with the lower reduction index in the
+// low nibble, widened to bf16 and multiplied by their block's E8M0 scale
+// 2^(sb - 127), passed to the conversion as the float with that exponent field.
+// A two-bit significand times a power of two: exact for scale bytes 1 .. 252
+// (a GPU check over every code byte and byte select matched the exact value
+// rounded to bf16, subnormals included, at scale bytes 1, 2, 120, 127 and 252;
+// from 253 the largest codes overflow bf16; byte 0 reads as a zero scale and
+// 255 as infinity).
+__device__ __forceinline__ uint4 mxfp4x8_to_bf16(uint32_t codes, uint32_t sb) {
+  const float sc = __uint_as_float(sb << 23);
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 // Weight row `r` (0 .. BN-1) of n-block nb of group g, per epilogue, as a byte
 // address; EB = bits per weight (16: bf16, 8: E4M3 codes, 4: MXFP4 codes).
 template <int EPI, int NTN, int EB = 16>
