@@ -147,3 +147,14 @@ __device__ __forceinline__ void lds_dma16(const void* g, const uint4* lds) {
                : "s"(__builtin_amdgcn_readfirstlane(a)), "v"(g)
                : "memory", "m0");
 }
+
+// The same copy with the non-temporal hint (nt): for data read once per launch
+// (streamed weights), which the L2 may then evict before the lines that many
+// blocks re-read (activation rows).
+__device__ __forceinline__ void lds_dma16_nt(const void* g, const uint4* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(a)), "v"(g)
+               : "memory", "m0");
+}
