@@ -283,16 +283,36 @@ __device__ __forceinline__ int dg_sort_parts(int e, int cnt, int part_rows, ulon
     s_scan[e] = own;
   }
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {  // inclusive scan over the experts, field by field
-    ulonglong2 v = make_ulonglong2(0ull, 0ull);
-    if (e < 256 && e >= o) v = s_scan[e - o];
-    __syncthreads();
-    if (e < 256) {
-      s_scan[e].x += v.x;
-      s_scan[e].y += v.y;
+  if (e < 64) {
+    // inclusive scan over the experts, field by field (no field carries into
+    // the next: each is at most the part count), by the first wave, four
+    // experts per lane
+    ulonglong2 v[4];
+    unsigned long long ax = 0ull, ay = 0ull;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = s_scan[4 * e + j];
+      ax += v[j].x;
+      ay += v[j].y;
     }
-    __syncthreads();
+    unsigned long long ix = ax, iy = ay;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long xx = __shfl_up(ix, o, 64), yy = __shfl_up(iy, o, 64);
+      if (e >= o) {
+        ix += xx;
+        iy += yy;
+      }
+    }
+    unsigned long long ex = ix - ax, ey = iy - ay;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ex += v[j].x;
+      ey += v[j].y;
+      s_scan[4 * e + j] = make_ulonglong2(ex, ey);
+    }
   }
+  __syncthreads();
   const ulonglong2 tot = s_scan[255];
   if (e < 256 && parts > 0) {
     const ulonglong2 inc = s_scan[e];
@@ -324,13 +344,11 @@ __device__ __forceinline__ void dg_build_lists(int e, int cnt, int part_rows, in
   __shared__ int32_t s_plist[DG_WS_MAX_PARTS];
   if (lpt) {
     const int np = dg_sort_parts(e, cnt, part_rows, s_sc, s_plist);
-    for (int u = e; u < np * (nblk_a + nblk_b); u += blockDim.x) {
-      const bool first = u < np * nblk_a;
-      const int v = first ? u : u - np * nblk_a, nb = first ? nblk_a : nblk_b;
-      const int q = v / nb, b = v - q * nb, ep = s_plist[q];
-      const int32_t code = (int32_t)(((uint32_t)(ep >> 8) << 24) | ((uint32_t)(ep & 0xff) << 16) | (uint32_t)b);
-      if (first) units_a[v] = code;
-      else units_b[v] = code;
+    for (int q = e; q < np; q += blockDim.x) {  // a thread per part: its n-blocks in both lists
+      const int ep = s_plist[q];
+      const uint32_t code = ((uint32_t)(ep >> 8) << 24) | ((uint32_t)(ep & 0xff) << 16);
+      for (int b = 0; b < nblk_a; ++b) units_a[q * nblk_a + b] = (int32_t)(code | (uint32_t)b);
+      for (int b = 0; b < nblk_b; ++b) units_b[q * nblk_b + b] = (int32_t)(code | (uint32_t)b);
     }
     if (e == 0) {
       *n_a = np * nblk_a;

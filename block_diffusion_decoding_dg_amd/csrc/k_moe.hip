@@ -17,7 +17,7 @@
 // it under that order, and the entries of rank < k are the selection, in rank
 // order.  The E x E comparisons are spread over the block as (logit, slice of 32
 // logits) items and the partial ranks are summed in LDS.  gates = softmax over the k kept logits, summed in
-// rank order.
+// rank order (lanes 0 .. k - 1 of the first wave take one exponential each).
 __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits, int rows, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ gates, int parts) {
   __shared__ float s_v[256];
@@ -27,9 +27,16 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits, int ro
   float* lrow = logits + (size_t)r * E;
   if (tid < E) {
     // the router's partial sums over its reduction ranges, added in range
-    // order; the total replaces the first range's (what readers of the logits see)
-    float x = lrow[tid];
-    for (int p = 1; p < parts; ++p) x += lrow[(size_t)p * rows * E + tid];
+    // order (the first four loaded together); the total replaces the first
+    // range's (what readers of the logits see)
+    float v[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) v[p] = p < parts ? lrow[(size_t)p * rows * E + tid] : 0.f;
+    float x = v[0];
+#pragma unroll
+    for (int p = 1; p < 4; ++p)
+      if (p < parts) x += v[p];
+    for (int p = 4; p < parts; ++p) x += lrow[(size_t)p * rows * E + tid];
     if (parts > 1) lrow[tid] = x;
     s_v[tid] = x == x ? x : -INFINITY;
   }
@@ -54,11 +61,12 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits, int ro
     s_sel[s_rank[tid]] = s_v[tid];
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {  // lane j < k: selected logit j's exponential; lane 0's order of the sum
     const float m = s_sel[0];
+    const float ej = tid < k ? __expf(s_sel[tid] - m) : 0.f;
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s += __expf(s_sel[j] - m);
-    for (int j = 0; j < k; ++j) gates[(size_t)r * k + j] = __expf(s_sel[j] - m) / s;
+    for (int j = 0; j < k; ++j) s += __shfl(ej, j, 64);
+    if (tid < k) gates[(size_t)r * k + tid] = ej / s;
   }
 }
 
@@ -323,39 +331,64 @@ __global__ void __launch_bounds__(256) k_route_perm(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ units_b, int32_t* __restrict__ n_b,
                                                     int lpt) {
   extern __shared__ uint32_t s_bits[];  // [E][nw]
-  __shared__ int s_off[256], s_off16[256];
+  __shared__ int s_cnt[256], s_off[256], s_off16[256], s_tot16;
   const int tid = threadIdx.x;
   const int nw = (rows + 31) / 32;
   for (int i = tid; i < E * nw; i += 256) s_bits[i] = 0u;
   __syncthreads();
   const int npairs = rows * k;
-  for (int p = tid; p < npairs; p += 256) {
-    const int t = p / k;
-    atomicOr(&s_bits[ids[p] * nw + (t >> 5)], 1u << (t & 31));
+  // eight ids per thread loaded before their bits are set (one memory round
+  // trip per eight pairs)
+  for (int p0 = 0; p0 < npairs; p0 += 8 * 256) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * 256 + tid;
+      ev[u] = p < npairs ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * 256 + tid, t = p / k;
+      if (ev[u] >= 0) atomicOr(&s_bits[ev[u] * nw + (t >> 5)], 1u << (t & 31));
+    }
   }
   __syncthreads();
   int cnt = 0;
   if (tid < E)
     for (int w = 0; w < nw; ++w) cnt += __popc(s_bits[tid * nw + w]);
-  s_off[tid] = cnt;
-  s_off16[tid] = (cnt + 15) & ~15;
+  s_cnt[tid] = cnt;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {  // inclusive scans over the experts
-    int a = 0, c = 0;
-    if (tid >= o) {
-      a = s_off[tid - o];
-      c = s_off16[tid - o];
+  if (tid < 64) {
+    // the first wave scans the experts, four per lane: exclusive offsets by
+    // pairs and by 16-row tiles
+    int c[4], a = 0, a16 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = s_cnt[4 * tid + j];
+      a += c[j];
+      a16 += (c[j] + 15) & ~15;
     }
-    __syncthreads();
-    s_off[tid] += a;
-    s_off16[tid] += c;
-    __syncthreads();
+    int ia = a, ia16 = a16;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int xa = __shfl_up(ia, o, 64), x16 = __shfl_up(ia16, o, 64);
+      if (tid >= o) {
+        ia += xa;
+        ia16 += x16;
+      }
+    }
+    int ea = ia - a, e16 = ia16 - a16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s_off[4 * tid + j] = ea;
+      s_off16[4 * tid + j] = e16;
+      ea += c[j];
+      e16 += (c[j] + 15) & ~15;
+    }
+    if (tid == 63) s_tot16 = ia16;
   }
-  const int tot16 = s_off16[255];
   __syncthreads();
-  s_off[tid] -= cnt;  // exclusive: first position of expert tid
-  s_off16[tid] -= (cnt + 15) & ~15;
-  __syncthreads();
+  const int tot16 = s_tot16;
 
   if ((int)blockIdx.x < (rows + 15) / 16) {
     if (tid < 16 * k) {
