@@ -20,7 +20,7 @@
 // rank order (lanes 0 .. k - 1 of the first wave take one exponential each).
 __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits, int rows, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ gates, int parts) {
-  __shared__ float s_v[256];
+  __shared__ __align__(16) float s_v[256];
   __shared__ int s_rank[256];
   __shared__ float s_sel[DG_MAX_TOPK];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -49,9 +49,24 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits, int ro
     const float v = s_v[e];
     const int j0 = sl * 32, j1 = min(j0 + 32, E);
     int cnt = 0;
-    for (int j = j0; j < j1; ++j) {
-      const float w = s_v[j];
-      cnt += (int)(w > v) | ((int)(w == v) & (int)(j < e));  // bitwise: no short-circuit branches
+    if (j1 - j0 == 32) {  // a whole slice: its 32 logits read as eight 16-byte loads before the comparisons
+      float4 w4[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w4[u] = reinterpret_cast<const float4*>(s_v + j0)[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float ww[4] = {w4[u].x, w4[u].y, w4[u].z, w4[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + 4 * u + q;
+          cnt += (int)(ww[q] > v) | ((int)(ww[q] == v) & (int)(j < e));  // bitwise: no short-circuit branches
+        }
+      }
+    } else {
+      for (int j = j0; j < j1; ++j) {
+        const float w = s_v[j];
+        cnt += (int)(w > v) | ((int)(w == v) & (int)(j < e));
+      }
     }
     if (cnt) atomicAdd(&s_rank[e], cnt);
   }
